@@ -1,0 +1,187 @@
+"""Benchmark: SubMConv3d ms/layer and effective TFLOP/s on one MI355X.
+
+Workload: SubMConv3d 3x3x3, batch 1, 128^3 grid, 209,715 uniform voxels (10 %
+occupancy), Cin = Cout = 128, fp16 features and weights, fp32 accumulation,
+no bias; the kernel map is built once and reused (warm cache), as in the
+"Performance" table of the trellis_sparse_mlx README.
+
+A step is one layer: weight preparation + the fused gather-GEMM forward,
+inputs resident in HBM. Effective TFLOP/s = 2 * active_pairs * Cin * Cout /
+time. The JSON line also carries the roofline of the forward kernel (HIP
+events around back-to-back forward launches on the launch stream), the
+kernel-map build time, and the CPU oracle (C twin, all host threads) timed on
+the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, TFLOP/s
+
+
+def algorithmic_bytes(n, cin, cout, ksize, has_order, has_bias):
+    """Compulsory HBM bytes of one forward launch: features read once, output
+    written once, the tap-major map read once (ksize 3), the processing order,
+    the prepared weights and the bias."""
+    K = 27 if ksize == 3 else 1
+    b = n * cin * 2 + n * cout * 2 + K * cin * cout * 2
+    if ksize == 3:
+        b += 27 * n * 4
+        if has_order:
+            b += n * 4
+    if has_bias:
+        b += cout * 4
+    return b
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c3_128_128")
+    ap.add_argument("--morton", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import submanifold_sparse_convolution_hash_amd as sc
+    import workloads
+
+    sc.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = workloads.make(args.config)
+    L = wl.layers[0]
+    coords = torch.from_numpy(wl.coords).to(dev)
+    feats = torch.from_numpy(wl.feats).to(dev)
+    W = torch.from_numpy(L.W).to(dev)
+    bias = None if L.bias is None else torch.from_numpy(L.bias).to(dev)
+    torch.cuda.synchronize()
+    print(f"[bench] {args.config}: N={wl.n} {L.cin}->{L.cout} ksize={L.ksize}", file=sys.stderr, flush=True)
+
+    # kernel-map build (cold, including allocation and the one host wait)
+    build_ms = []
+    km = None
+    for _ in range(5):
+        if km is not None:
+            km.free()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        km = sc.build_map(coords, wl.grid, wl.batch, morton=args.morton)
+        torch.cuda.synchronize()
+        build_ms.append((time.perf_counter() - t) * 1e3)
+    pairs = km.active_pairs(L.ksize)
+    flops = 2.0 * pairs * L.cin * L.cout
+
+    out = torch.empty((wl.n, L.cout), dtype=torch.float16, device=dev)
+
+    def step():
+        wp = sc.prepare_weights(W)
+        sc.forward(km, feats, bias=bias, prepared=wp, ksize=L.ksize, cout=L.cout, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t) * 1e3 / args.steps
+    ms_step = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] step {ms_step * 1e3:.1f} us (wall {wall_ms * 1e3:.1f} us)", file=sys.stderr, flush=True)
+
+    # forward kernel alone, back to back on the launch stream
+    wp = sc.prepare_weights(W)
+    for _ in range(args.warmup):
+        sc.forward(km, feats, bias=bias, prepared=wp, ksize=L.ksize, cout=L.cout, out=out)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        sc.forward(km, feats, bias=bias, prepared=wp, ksize=L.ksize, cout=L.cout, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    fwd_us = e0.elapsed_time(e1) / args.steps * 1e3
+    alg_bytes = algorithmic_bytes(wl.n, L.cin, L.cout, L.ksize, args.morton, bias is not None)
+    achieved_gbs = alg_bytes / (fwd_us * 1e-6) / 1e9
+    print(f"[bench] forward kernel {fwd_us:.1f} us, {achieved_gbs:.0f} GB/s algorithmic", file=sys.stderr, flush=True)
+
+    if args.calib_copy_mib > 0:
+        nb = args.calib_copy_mib * 1024 * 1024
+        a = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import cpu as oc
+        t = time.perf_counter()
+        kmap = oc.kernel_map(wl.coords, wl.grid, wl.batch, L.ksize)
+        map_s = time.perf_counter() - t
+        times = []
+        for _ in range(2):
+            t = time.perf_counter()
+            oc.submconv_rows(kmap, wl.feats, L.W, L.bias)
+            times.append(time.perf_counter() - t)
+        conv_s = min(times)
+        cpu = {"value": round(flops / conv_s / 1e12, 6), "unit": "TFLOP/s", "cores": oc.num_threads(),
+               "kind": "oracle",
+               "sample": f"full {args.config} layer, all {wl.n} rows: C oracle (fp64, sort+bsearch map, "
+                         f"naive loops, OpenMP); conv {conv_s * 1e3:.0f} ms (best of 2), "
+                         f"map {map_s * 1e3:.0f} ms"}
+        print(f"[bench] cpu oracle conv {conv_s:.2f} s", file=sys.stderr, flush=True)
+
+    rec = {
+        "metric": "SubMConv3d ms/layer + effective TFLOP/s (128^3 grid, C=128, 10% occ)",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 4),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: SubMConv3d {L.ksize}x{L.ksize}x{L.ksize}, grid {wl.grid[0]}^3, "
+                               f"batch {wl.batch}, N={wl.n}, Cin={L.cin}, Cout={L.cout}, warm kernel map",
+                   "active_pairs": pairs, "morton": bool(args.morton)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_fwd_mfma", "kernel_us": round(fwd_us, 2),
+                     "algorithmic_bytes": alg_bytes,
+                     "mfma_effective_frac": round(flops / (fwd_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
+        "map_build_ms": round(float(np.median(build_ms)), 3),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    km.free()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

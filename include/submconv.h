@@ -1,0 +1,164 @@
+/*
+ * submconv.h -- C ABI of libsubmconv.so: submanifold sparse 3D convolution
+ * (SubMConv3d, 3x3x3 and 1x1x1, stride 1) on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (trellis_sparse_mlx README, "What's in it" table, SubMConv3d
+ * and SparseTensor rows; "Performance" and "Correctness" sections):
+ *
+ *   A sparse tensor is a set of N distinct voxel sites coords[i] = (b,x,y,z)
+ *   with a feature row feats[i] of Cin values. A submanifold convolution
+ *   computes an output row only at the input sites:
+ *
+ *     out[i] = bias + sum over offsets d in {-1,0,1}^3 (or d = 0 for 1x1x1)
+ *              of feats[j] @ W[k(d)],  where coords[j] = coords[i] + d,
+ *
+ *   with the gather at c + d (cross-correlation), the same batch item b, and
+ *   absent neighbours (no site there, or outside the grid) contributing zero.
+ *   Tap index k(dx,dy,dz) = 9(dx+1) + 3(dy+1) + (dz+1), dx slowest; the
+ *   centre tap is k = 13. For a 1x1x1 kernel the single tap is k = 0.
+ *
+ * Work is split into a one-time kernel-map build per site set (a GPU hash of
+ * the sites and the [N,27] neighbour map; the cached, device-resident gather
+ * index of the README's "Performance" section) and a per-layer forward that
+ * reuses it.
+ *
+ * Conventions for every entry point:
+ *   - Tensor arguments are DEVICE pointers on the current HIP device unless
+ *     marked "host". The caller owns them; the library never frees them.
+ *   - fp16 data is passed as uint16_t holding IEEE-754 binary16 bit patterns.
+ *   - Row-major, densely packed layouts; feature and weight pointers must be
+ *     16-byte aligned.
+ *   - Work is enqueued on `stream` (0 = the null stream) and, unless stated,
+ *     returns without waiting for the device.
+ *   - Return value: SUBMCONV_OK (0) or a negative status; argument and shape
+ *     errors are detected before anything is enqueued. submconv_last_error()
+ *     gives a thread-local message for the last failure.
+ */
+#ifndef SUBMCONV_H_
+#define SUBMCONV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SUBMCONV_ABI_VERSION 1
+
+/* Status codes. */
+#define SUBMCONV_OK 0
+#define SUBMCONV_ERR_INVALID_ARG (-1)        /* NULL pointer, negative size, bad ksize */
+#define SUBMCONV_ERR_COORD_OUT_OF_RANGE (-2) /* a site outside [0,batch) x grid */
+#define SUBMCONV_ERR_DUPLICATE_COORD (-3)    /* the same site given twice */
+#define SUBMCONV_ERR_UNSUPPORTED_SHAPE (-4)  /* Cin/Cout not multiples of 8, too large, ... */
+#define SUBMCONV_ERR_HIP (-5)                /* a HIP runtime call or launch failed */
+#define SUBMCONV_ERR_OUT_OF_MEMORY (-6)      /* device allocation failed */
+
+/* Flags of submconv_build_map. */
+#define SUBMCONV_FLAG_MORTON 1u /* process output rows in Morton (Z-curve) order */
+
+/* Opaque kernel-map handle: library-owned device buffers, immutable after
+ * submconv_build_map returns, released by submconv_map_free. One handle may
+ * serve concurrent forwards on several streams of its device. */
+typedef struct submconv_map_s* submconv_map_t;
+
+/*
+ * submconv_build_map -- hash the sites and build the neighbour map.
+ *
+ * coords   [n,4] int32 (b,x,y,z), device. Sites must be distinct and satisfy
+ *          0 <= b < batch, 0 <= x < grid[0], 0 <= y < grid[1], 0 <= z < grid[2].
+ * n        number of sites (n = 0 gives an empty map).
+ * batch    number of batch items (>= 1).
+ * grid     host array of 3 positive extents.
+ * flags    0 or SUBMCONV_FLAG_MORTON (iteration order only; results are the
+ *          same bit for bit either way).
+ * out_map  receives the handle (host pointer).
+ *
+ * The map is built on `stream`; the function then waits for that stream once
+ * (to read back the validation flags and the active-pair count) and returns
+ * SUBMCONV_ERR_COORD_OUT_OF_RANGE or SUBMCONV_ERR_DUPLICATE_COORD, with no
+ * handle, when the sites are invalid. It allocates device memory
+ * (27*n*4 bytes for the map, plus temporaries freed before return).
+ */
+int submconv_build_map(const int32_t* coords, int64_t n, int32_t batch, const int32_t grid[3],
+                       uint32_t flags, hipStream_t stream, submconv_map_t* out_map);
+
+/* Number of sites of the map. */
+int64_t submconv_map_num_rows(submconv_map_t map);
+
+/* Number of (row, tap) pairs with a neighbour, the centre tap included
+ * (ksize 3), or n (ksize 1). Effective work of a forward is
+ * 2 * active_pairs * Cin * Cout flops. Negative on a bad argument. */
+int64_t submconv_map_active_pairs(submconv_map_t map, int32_t ksize);
+
+/*
+ * submconv_map_export -- write the neighbour map in the caller's row order.
+ * kmap [n,27] int32, device: kmap[i][k] = row j of the site coords[i] + d_k in
+ * the same batch item, or -1. Asynchronous on `stream`.
+ */
+int submconv_map_export(submconv_map_t map, int32_t* kmap, hipStream_t stream);
+
+/*
+ * submconv_map_order -- write the internal row processing order:
+ * order[t] = caller row processed t-th (identity without the Morton flag).
+ * order [n] int32, device. Asynchronous on `stream`.
+ */
+int submconv_map_order(submconv_map_t map, int32_t* order, hipStream_t stream);
+
+/* Release the map's device memory (waits for the device). NULL is a no-op. */
+int submconv_map_free(submconv_map_t map);
+
+/*
+ * submconv_prepared_weights_elems -- number of fp16 elements of the prepared
+ * weight buffer for a K x Cin x Cout kernel (K = 27 for ksize 3, 1 for 1).
+ * Negative for an unsupported shape.
+ */
+int64_t submconv_prepared_weights_elems(int32_t ksize, int32_t cin, int32_t cout);
+
+/*
+ * submconv_prepare_weights -- reorder weights into the forward kernel's layout.
+ * W   [K,Cin,Cout] fp16, device, out = feats @ W[k] per tap (k as above).
+ * Wp  device buffer of submconv_prepared_weights_elems(...) fp16 elements,
+ *     caller-allocated; its content is an opaque, shape-specific layout.
+ * Prepared weights stay valid for every forward with the same ksize, Cin and
+ * Cout. Asynchronous on `stream`; W and Wp must not overlap.
+ */
+int submconv_prepare_weights(const uint16_t* W, int32_t ksize, int32_t cin, int32_t cout,
+                             uint16_t* Wp, hipStream_t stream);
+
+/*
+ * submconv_forward -- one SubMConv3d layer on the sites of `map`.
+ *
+ * feats  [n,Cin] fp16, device, caller row order.
+ * Wp     prepared weights (submconv_prepare_weights) for (ksize, Cin, Cout).
+ * bias   [Cout] fp32, device, or NULL for no bias.
+ * out    [n,Cout] fp16, device, caller row order; must not overlap feats.
+ * ksize  3 (27 taps, uses the neighbour map) or 1 (centre tap only).
+ *
+ * Accumulates in fp32, adds the bias in fp32 and rounds once to fp16 (round to
+ * nearest even). Cin and Cout must be multiples of 8 and at most 1024.
+ * Enqueues on `stream`, allocates nothing and does not wait. Every output row
+ * is written by exactly one workgroup without atomics, so results are
+ * bitwise reproducible run to run.
+ */
+int submconv_forward(submconv_map_t map, const uint16_t* feats, const uint16_t* Wp,
+                     const float* bias, uint16_t* out, int32_t cin, int32_t cout, int32_t ksize,
+                     hipStream_t stream);
+
+/* Message for a status code (static string). */
+const char* submconv_status_string(int status);
+
+/* Thread-local detail message of the last failing call on this thread. */
+const char* submconv_last_error(void);
+
+/* SUBMCONV_ABI_VERSION of the built library. */
+int submconv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SUBMCONV_H_ */

@@ -1,0 +1,262 @@
+"""Submanifold sparse 3D convolution (SubMConv3d) on AMD Instinct MI355X.
+
+Thin Python binding of ``libsubmconv.so`` (C ABI in ``include/submconv.h``).
+It only marshals arguments: tensors are passed as device pointers together
+with PyTorch's current HIP stream; every step runs in the library's kernels.
+The library must be built (``python -m submanifold_sparse_convolution_hash_amd.build``
+or ``__graft_entry__.build()``); nothing here falls back to another
+implementation when it is missing.
+
+Operation (trellis_sparse_mlx README, "What's in it", "Performance",
+"Correctness"): for sites ``coords[N,4] = (b,x,y,z)`` and features
+``feats[N,Cin]``, ``out[i] = bias + sum_k feats[j_k(i)] @ W[k]`` where
+``j_k(i)`` is the site at ``coords[i] + d_k`` (same batch item), absent
+neighbours contributing zero; ``k = 9(dx+1)+3(dy+1)+(dz+1)`` for 3x3x3 and
+``k = 0`` for 1x1x1.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+__all__ = [
+    "SubmconvError", "KernelMap", "build_map", "prepare_weights", "forward", "SubMConv3d",
+    "library_path", "load_library", "abi_version", "FLAG_MORTON",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libsubmconv.so")
+FLAG_MORTON = 1
+_lib = None
+
+
+class SubmconvError(RuntimeError):
+    """A non-zero status returned by the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Loads ``libsubmconv.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is not built: run `python -m submanifold_sparse_convolution_hash_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64, U32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
+    sig = {
+        "submconv_build_map": ([P, I64, I32, P, U32, P, P], ctypes.c_int),
+        "submconv_map_num_rows": ([P], I64),
+        "submconv_map_active_pairs": ([P, I32], I64),
+        "submconv_map_export": ([P, P, P], ctypes.c_int),
+        "submconv_map_order": ([P, P, P], ctypes.c_int),
+        "submconv_map_free": ([P], ctypes.c_int),
+        "submconv_prepared_weights_elems": ([I32, I32, I32], I64),
+        "submconv_prepare_weights": ([P, I32, I32, I32, P, P], ctypes.c_int),
+        "submconv_forward": ([P, P, P, P, P, I32, I32, I32, P], ctypes.c_int),
+        "submconv_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "submconv_last_error": ([], ctypes.c_char_p),
+        "submconv_abi_version": ([], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return int(load_library().submconv_abi_version())
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        lib = load_library()
+        msg = lib.submconv_last_error().decode() or lib.submconv_status_string(status).decode()
+        raise SubmconvError(int(status), msg)
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[ctypes.c_void_p]:
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _require(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class KernelMap:
+    """Handle of a built neighbour map (library-owned device memory)."""
+
+    def __init__(self, handle: ctypes.c_void_p, device: torch.device, grid, batch: int, flags: int):
+        self._h = handle
+        self.device = device
+        self.grid = tuple(int(g) for g in grid)
+        self.batch = int(batch)
+        self.flags = int(flags)
+        lib = load_library()
+        self.num_rows = int(lib.submconv_map_num_rows(self._h))
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if self._h is None:
+            raise SubmconvError(-1, "map already freed")
+        return self._h
+
+    def active_pairs(self, ksize: int = 3) -> int:
+        v = int(load_library().submconv_map_active_pairs(self.handle, ksize))
+        if v < 0:
+            _check(v)
+        return v
+
+    def export(self) -> torch.Tensor:
+        """[N,27] int32 neighbour rows in the caller's order, -1 for none."""
+        out = torch.empty((self.num_rows, 27), dtype=torch.int32, device=self.device)
+        _check(load_library().submconv_map_export(self.handle, _ptr(out), _stream(self.device)))
+        return out
+
+    def order(self) -> torch.Tensor:
+        """[N] int32 processing order (caller row processed t-th)."""
+        out = torch.empty((self.num_rows,), dtype=torch.int32, device=self.device)
+        _check(load_library().submconv_map_order(self.handle, _ptr(out), _stream(self.device)))
+        return out
+
+    def free(self) -> None:
+        if self._h is not None and _lib is not None:
+            _check(_lib.submconv_map_free(self._h))
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def build_map(coords: torch.Tensor, grid: Sequence[int], batch: Optional[int] = None,
+              morton: bool = False) -> KernelMap:
+    """Hashes the sites ``coords`` ([N,4] int32 (b,x,y,z), device) and builds
+    their 3x3x3 neighbour map. Waits once for the stream (validation)."""
+    _require(coords, "coords", torch.int32, 2)
+    if coords.shape[1] != 4:
+        raise ValueError("coords must be [N,4]")
+    if batch is None:
+        batch = int(coords[:, 0].max().item()) + 1 if coords.shape[0] else 1
+    lib = load_library()
+    g = (ctypes.c_int32 * 3)(*[int(v) for v in grid])
+    h = ctypes.c_void_p()
+    flags = FLAG_MORTON if morton else 0
+    with torch.cuda.device(coords.device):
+        _check(lib.submconv_build_map(_ptr(coords), coords.shape[0], int(batch), g, flags,
+                                      _stream(coords.device), ctypes.byref(h)))
+    return KernelMap(h, coords.device, grid, batch, flags)
+
+
+def prepare_weights(W: torch.Tensor) -> torch.Tensor:
+    """Reorders weights [K,Cin,Cout] fp16 (K = 27 or 1) into the forward
+    kernel's layout (an opaque fp16 buffer of the same element count)."""
+    _require(W, "W", torch.float16, 3)
+    K, cin, cout = W.shape
+    if K not in (27, 1):
+        raise ValueError("W must be [27,Cin,Cout] or [1,Cin,Cout]")
+    ksize = 3 if K == 27 else 1
+    lib = load_library()
+    n = int(lib.submconv_prepared_weights_elems(ksize, cin, cout))
+    if n < 0:
+        _check(n)
+    wp = torch.empty((n,), dtype=torch.float16, device=W.device)
+    with torch.cuda.device(W.device):
+        _check(lib.submconv_prepare_weights(_ptr(W), ksize, cin, cout, _ptr(wp), _stream(W.device)))
+    return wp
+
+
+def forward(kmap: KernelMap, feats: torch.Tensor, W: Optional[torch.Tensor] = None,
+            bias: Optional[torch.Tensor] = None, *, prepared: Optional[torch.Tensor] = None,
+            ksize: Optional[int] = None, cout: Optional[int] = None,
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One SubMConv3d layer: ``out[N,Cout]`` fp16 in the caller's row order.
+
+    Pass either ``W`` ([K,Cin,Cout] fp16, prepared on the fly) or ``prepared``
+    (from :func:`prepare_weights`) together with ``ksize`` and ``cout``.
+    """
+    _require(feats, "feats", torch.float16, 2)
+    if feats.shape[0] != kmap.num_rows:
+        raise ValueError(f"feats has {feats.shape[0]} rows, the map {kmap.num_rows}")
+    cin = feats.shape[1]
+    if prepared is None:
+        if W is None:
+            raise ValueError("pass W or prepared")
+        if W.shape[1] != cin:
+            raise ValueError(f"W is {tuple(W.shape)} but feats has Cin = {cin}")
+        ksize = 3 if W.shape[0] == 27 else 1
+        cout = W.shape[2]
+        prepared = prepare_weights(W)
+    elif ksize is None or cout is None:
+        raise ValueError("with prepared weights, pass ksize and cout")
+    if bias is not None:
+        _require(bias, "bias", torch.float32, 1)
+        if bias.shape[0] != cout:
+            raise ValueError("bias must be [Cout]")
+    if out is None:
+        out = torch.empty((feats.shape[0], cout), dtype=torch.float16, device=feats.device)
+    else:
+        _require(out, "out", torch.float16, 2)
+        if tuple(out.shape) != (feats.shape[0], cout):
+            raise ValueError("out must be [N,Cout]")
+    with torch.cuda.device(feats.device):
+        _check(load_library().submconv_forward(kmap.handle, _ptr(feats), _ptr(prepared), _ptr(bias),
+                                               _ptr(out), cin, cout, int(ksize),
+                                               _stream(feats.device)))
+    return out
+
+
+class SubMConv3d(torch.nn.Module):
+    """Inference module: weight [K,Cin,Cout] fp16 (K = 27 or 1), optional fp32
+    bias; caches the prepared weights until the weight tensor changes."""
+
+    def __init__(self, cin: int, cout: int, ksize: int = 3, bias: bool = True,
+                 device=None, dtype=torch.float16):
+        super().__init__()
+        K = 27 if ksize == 3 else 1
+        self.ksize = ksize
+        self.weight = torch.nn.Parameter(torch.empty((K, cin, cout), device=device, dtype=dtype),
+                                         requires_grad=False)
+        self.bias = (torch.nn.Parameter(torch.zeros(cout, device=device, dtype=torch.float32),
+                                        requires_grad=False) if bias else None)
+        self._cache = None
+        self._cache_key = None
+
+    def prepared(self) -> torch.Tensor:
+        key = (self.weight.data_ptr(), self.weight._version)
+        if self._cache is None or self._cache_key != key:
+            self._cache = prepare_weights(self.weight)
+            self._cache_key = key
+        return self._cache
+
+    def forward(self, kmap: KernelMap, feats: torch.Tensor) -> torch.Tensor:
+        return forward(kmap, feats, bias=self.bias, prepared=self.prepared(), ksize=self.ksize,
+                       cout=self.weight.shape[2])

@@ -1,0 +1,406 @@
+// Kernel-map construction for SubMConv3d on gfx950.
+//
+// The map is the cached, device-resident gather index of the
+// trellis_sparse_mlx README ("Performance": the prepared gather index is
+// built once and reused; "What's in it": the indice-map cache of the sparse
+// tensor). Sites are packed injectively into one 64-bit key (the coordinate
+// packing of "Running TRELLIS.2 on a Mac (3/3)", section E), inserted into an
+// open-addressing hash table in HBM, and every site then probes its 27
+// neighbours c + d (cross-correlation, README "Correctness").
+//
+// Steps (one stream, one host wait at the end):
+//   pack     coords -> keys, range validation (error flag)
+//   insert   keys -> table, 64-bit compare-and-swap, linear probing; a key
+//            that is already present raises the duplicate flag
+//   order    optional Morton codes + radix sort -> processing order
+//   query    27 probes per site -> nbr[27][n] (tap-major), pair count
+//   readback flags + pair count (the single host wait)
+#include <rocprim/device/device_radix_sort.hpp>
+
+#include <cstdarg>
+#include <cstring>
+#include <vector>
+
+#include "submconv_internal.h"
+
+namespace submconv {
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr uint64_t kEmpty = ~0ull;
+constexpr uint32_t kErrRange = 1u;
+constexpr uint32_t kErrDuplicate = 2u;
+
+// MurmurHash3 64-bit finalizer (public domain, Austin Appleby): a bijective
+// mixer, so distinct keys stay distinct and nearby keys scatter.
+__device__ __forceinline__ uint64_t mix64(uint64_t k) {
+  k ^= k >> 33;
+  k *= 0xff51afd7ed558ccdull;
+  k ^= k >> 33;
+  k *= 0xc4ceb9fe1a85ec53ull;
+  k ^= k >> 33;
+  return k;
+}
+
+// key = ((b*G0 + x)*G1 + y)*G2 + z: injective for in-range sites.
+__device__ __forceinline__ uint64_t pack_key(int32_t b, int32_t x, int32_t y, int32_t z, int32_t g0,
+                                             int32_t g1, int32_t g2) {
+  return ((static_cast<uint64_t>(b) * g0 + static_cast<uint64_t>(x)) * g1 +
+          static_cast<uint64_t>(y)) *
+             g2 +
+         static_cast<uint64_t>(z);
+}
+
+// Spreads the low 21 bits of v so that bit i lands at bit 3i.
+__device__ __forceinline__ uint64_t spread3(uint64_t v) {
+  v &= 0x1fffffull;
+  v = (v | (v << 32)) & 0x1f00000000ffffull;
+  v = (v | (v << 16)) & 0x1f0000ff0000ffull;
+  v = (v | (v << 8)) & 0x100f00f00f00f00full;
+  v = (v | (v << 4)) & 0x10c30c30c30c30c3ull;
+  v = (v | (v << 2)) & 0x1249249249249249ull;
+  return v;
+}
+
+__global__ void k_pack(const int32_t* __restrict__ coords, int64_t n, int32_t batch, int32_t g0,
+                       int32_t g1, int32_t g2, uint64_t* __restrict__ keys,
+                       uint32_t* __restrict__ err, int morton_bits,
+                       uint64_t* __restrict__ mcode, int32_t* __restrict__ midx) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int32_t b = coords[4 * i + 0];
+  const int32_t x = coords[4 * i + 1];
+  const int32_t y = coords[4 * i + 2];
+  const int32_t z = coords[4 * i + 3];
+  const bool ok = b >= 0 && b < batch && x >= 0 && x < g0 && y >= 0 && y < g1 && z >= 0 && z < g2;
+  if (!ok) atomicOr(err, kErrRange);
+  keys[i] = ok ? pack_key(b, x, y, z, g0, g1, g2) : kEmpty;
+  if (mcode) {
+    uint64_t c = 0;
+    if (ok)
+      c = (static_cast<uint64_t>(b) << (3 * morton_bits)) |
+          (spread3(static_cast<uint64_t>(x)) << 2) | (spread3(static_cast<uint64_t>(y)) << 1) |
+          spread3(static_cast<uint64_t>(z));
+    mcode[i] = c;
+    midx[i] = static_cast<int32_t>(i);
+  }
+}
+
+__global__ void k_insert(const uint64_t* __restrict__ keys, int64_t n, uint64_t* tkeys,
+                         int32_t* __restrict__ tvals, uint64_t mask, uint32_t* __restrict__ err) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint64_t key = keys[i];
+  if (key == kEmpty) return;  // out-of-range site, already flagged
+  uint64_t h = mix64(key) & mask;
+  // The table holds at most n keys in >= 2n slots, so an empty slot exists.
+  while (true) {
+    const unsigned long long prev = atomicCAS(reinterpret_cast<unsigned long long*>(tkeys + h),
+                                              static_cast<unsigned long long>(kEmpty),
+                                              static_cast<unsigned long long>(key));
+    if (prev == kEmpty) {
+      tvals[h] = static_cast<int32_t>(i);
+      return;
+    }
+    if (prev == key) {
+      atomicOr(err, kErrDuplicate);
+      return;
+    }
+    h = (h + 1) & mask;
+  }
+}
+
+__global__ void k_query(const int32_t* __restrict__ coords, const int32_t* __restrict__ order,
+                        int64_t n, int32_t g0, int32_t g1, int32_t g2,
+                        const uint64_t* __restrict__ tkeys, const int32_t* __restrict__ tvals,
+                        uint64_t mask, int32_t* __restrict__ nbr,
+                        unsigned long long* __restrict__ pairs) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  int hits = 0;
+  if (t < n) {
+    const int64_t i = order ? order[t] : t;
+    const int32_t b = coords[4 * i + 0];
+    const int32_t x = coords[4 * i + 1];
+    const int32_t y = coords[4 * i + 2];
+    const int32_t z = coords[4 * i + 3];
+#pragma unroll 1
+    for (int k = 0; k < kTaps3; ++k) {
+      const int32_t nx = x + (k / 9) - 1;
+      const int32_t ny = y + ((k / 3) % 3) - 1;
+      const int32_t nz = z + (k % 3) - 1;
+      int32_t j = -1;
+      if (k == kCenterTap) {
+        j = static_cast<int32_t>(i);
+      } else if (nx >= 0 && nx < g0 && ny >= 0 && ny < g1 && nz >= 0 && nz < g2) {
+        const uint64_t key = pack_key(b, nx, ny, nz, g0, g1, g2);
+        uint64_t h = mix64(key) & mask;
+        while (true) {
+          const uint64_t s = tkeys[h];
+          if (s == key) {
+            j = tvals[h];
+            break;
+          }
+          if (s == kEmpty) break;
+          h = (h + 1) & mask;
+        }
+      }
+      nbr[static_cast<int64_t>(k) * n + t] = j;
+      hits += (j >= 0);
+    }
+  }
+  // wave-level sum, one atomic per wave
+  for (int off = 32; off > 0; off >>= 1) hits += __shfl_down(hits, off, 64);
+  if ((threadIdx.x & 63) == 0 && hits) atomicAdd(pairs, static_cast<unsigned long long>(hits));
+}
+
+__global__ void k_export(const int32_t* __restrict__ nbr, const int32_t* __restrict__ order,
+                         int64_t n, int32_t* __restrict__ kmap) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= n * kTaps3) return;
+  const int64_t k = idx / n;
+  const int64_t t = idx - k * n;
+  const int64_t i = order ? order[t] : t;
+  kmap[i * kTaps3 + k] = nbr[idx];
+}
+
+__global__ void k_order_out(const int32_t* __restrict__ order, int64_t n, int32_t* __restrict__ out) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t < n) out[t] = order ? order[t] : static_cast<int32_t>(t);
+}
+
+inline unsigned grid_for(int64_t n, int block) {
+  return static_cast<unsigned>((n + block - 1) / block);
+}
+
+int bits_for(int64_t extent) {  // smallest b with 2^b >= extent (at least 1)
+  int b = 1;
+  while ((int64_t{1} << b) < extent) ++b;
+  return b;
+}
+
+// Device buffers freed on scope exit (temporaries of one build).
+struct DevBuf {
+  void* p = nullptr;
+  ~DevBuf() {
+    if (p) (void)hipFree(p);
+  }
+};
+
+}  // namespace
+
+int set_error(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+const char* last_error_cstr() { return g_last_error.c_str(); }
+
+}  // namespace submconv
+
+using namespace submconv;
+
+extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batch,
+                                  const int32_t grid[3], uint32_t flags, hipStream_t stream,
+                                  submconv_map_t* out_map) {
+  clear_error();
+  if (!out_map) return set_error(SUBMCONV_ERR_INVALID_ARG, "out_map is NULL");
+  *out_map = nullptr;
+  if (!grid) return set_error(SUBMCONV_ERR_INVALID_ARG, "grid is NULL");
+  if (n < 0) return set_error(SUBMCONV_ERR_INVALID_ARG, "n = %lld is negative", (long long)n);
+  if (n > 0 && !coords) return set_error(SUBMCONV_ERR_INVALID_ARG, "coords is NULL");
+  if (batch < 1) return set_error(SUBMCONV_ERR_INVALID_ARG, "batch = %d < 1", batch);
+  if (flags & ~SUBMCONV_FLAG_MORTON)
+    return set_error(SUBMCONV_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  for (int a = 0; a < 3; ++a)
+    if (grid[a] < 1) return set_error(SUBMCONV_ERR_INVALID_ARG, "grid[%d] = %d < 1", a, grid[a]);
+  if (n > INT32_MAX - 1)
+    return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "n = %lld exceeds int32 row indices",
+                     (long long)n);
+  // the packed key must not overflow 63 bits: batch * G0 * G1 * G2 < 2^63
+  {
+    unsigned __int128 v = static_cast<unsigned __int128>(batch);
+    for (int a = 0; a < 3; ++a) v *= static_cast<unsigned __int128>(grid[a]);
+    if (v >= (static_cast<unsigned __int128>(1) << 63))
+      return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "batch*grid volume exceeds 2^63");
+  }
+  const bool morton = (flags & SUBMCONV_FLAG_MORTON) != 0;
+  int mbits = 0;
+  if (morton) {
+    mbits = bits_for(std::max(grid[0], std::max(grid[1], grid[2])));
+    const int bbits = batch > 1 ? bits_for(batch) : 0;
+    if (mbits > 21 || 3 * mbits + bbits > 64)
+      return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "grid too large for a 64-bit Morton code");
+  }
+
+  Map m;
+  SUBMCONV_HIP_CHECK(hipGetDevice(&m.device));
+  m.n = n;
+  m.batch = batch;
+  for (int a = 0; a < 3; ++a) m.grid[a] = grid[a];
+  m.flags = flags;
+  if (n == 0) {
+    *out_map = new submconv_map_s{m};
+    return SUBMCONV_OK;
+  }
+
+  int64_t cap = 64;
+  while (cap < 2 * n) cap <<= 1;
+  const uint64_t mask = static_cast<uint64_t>(cap - 1);
+
+  DevBuf keys, tkeys, tvals, small, mcode_in, mcode_out, midx, sort_tmp;
+  int32_t* nbr = nullptr;
+  int32_t* order = nullptr;
+  auto fail = [&](int status) {
+    if (nbr) (void)hipFree(nbr);
+    if (order) (void)hipFree(order);
+    return status;
+  };
+#define BUILD_CHECK(expr)                                                                 \
+  do {                                                                                    \
+    hipError_t e_ = (expr);                                                               \
+    if (e_ != hipSuccess)                                                                 \
+      return fail(set_error(e_ == hipErrorOutOfMemory ? SUBMCONV_ERR_OUT_OF_MEMORY        \
+                                                      : SUBMCONV_ERR_HIP,                 \
+                            "%s failed: %s", #expr, hipGetErrorString(e_)));             \
+  } while (0)
+
+  BUILD_CHECK(hipMalloc(&keys.p, sizeof(uint64_t) * n));
+  BUILD_CHECK(hipMalloc(&tkeys.p, sizeof(uint64_t) * cap));
+  BUILD_CHECK(hipMalloc(&tvals.p, sizeof(int32_t) * cap));
+  BUILD_CHECK(hipMalloc(&small.p, 64));
+  BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&nbr), sizeof(int32_t) * kTaps3 * n));
+  if (morton) {
+    BUILD_CHECK(hipMalloc(&mcode_in.p, sizeof(uint64_t) * n));
+    BUILD_CHECK(hipMalloc(&mcode_out.p, sizeof(uint64_t) * n));
+    BUILD_CHECK(hipMalloc(&midx.p, sizeof(int32_t) * n));
+    BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&order), sizeof(int32_t) * n));
+  }
+  uint32_t* err = static_cast<uint32_t*>(small.p);
+  unsigned long long* pairs = reinterpret_cast<unsigned long long*>(static_cast<char*>(small.p) + 8);
+
+  BUILD_CHECK(hipMemsetAsync(small.p, 0, 64, stream));
+  BUILD_CHECK(hipMemsetAsync(tkeys.p, 0xff, sizeof(uint64_t) * cap, stream));
+
+  const int B = 256;
+  k_pack<<<grid_for(n, B), B, 0, stream>>>(coords, n, batch, grid[0], grid[1], grid[2],
+                                           static_cast<uint64_t*>(keys.p), err, mbits,
+                                           static_cast<uint64_t*>(mcode_in.p),
+                                           static_cast<int32_t*>(midx.p));
+  BUILD_CHECK(hipGetLastError());
+  k_insert<<<grid_for(n, B), B, 0, stream>>>(static_cast<const uint64_t*>(keys.p), n,
+                                             static_cast<uint64_t*>(tkeys.p),
+                                             static_cast<int32_t*>(tvals.p), mask, err);
+  BUILD_CHECK(hipGetLastError());
+  if (morton) {
+    const int bbits = batch > 1 ? bits_for(batch) : 0;
+    const unsigned end_bit = static_cast<unsigned>(3 * mbits + bbits);
+    size_t tmp_bytes = 0;
+    BUILD_CHECK(rocprim::radix_sort_pairs(nullptr, tmp_bytes,
+                                          static_cast<const uint64_t*>(mcode_in.p),
+                                          static_cast<uint64_t*>(mcode_out.p),
+                                          static_cast<const int32_t*>(midx.p), order,
+                                          static_cast<size_t>(n), 0u, end_bit, stream));
+    BUILD_CHECK(hipMalloc(&sort_tmp.p, tmp_bytes > 0 ? tmp_bytes : 1));
+    BUILD_CHECK(rocprim::radix_sort_pairs(sort_tmp.p, tmp_bytes,
+                                          static_cast<const uint64_t*>(mcode_in.p),
+                                          static_cast<uint64_t*>(mcode_out.p),
+                                          static_cast<const int32_t*>(midx.p), order,
+                                          static_cast<size_t>(n), 0u, end_bit, stream));
+  }
+  k_query<<<grid_for(n, B), B, 0, stream>>>(coords, order, n, grid[0], grid[1], grid[2],
+                                            static_cast<const uint64_t*>(tkeys.p),
+                                            static_cast<const int32_t*>(tvals.p), mask, nbr,
+                                            pairs);
+  BUILD_CHECK(hipGetLastError());
+
+  uint64_t host_small[2] = {0, 0};
+  BUILD_CHECK(hipMemcpyAsync(host_small, small.p, 16, hipMemcpyDeviceToHost, stream));
+  BUILD_CHECK(hipStreamSynchronize(stream));
+  const uint32_t eflags = static_cast<uint32_t>(host_small[0]);
+  if (eflags & kErrRange)
+    return fail(set_error(SUBMCONV_ERR_COORD_OUT_OF_RANGE,
+                          "a site lies outside [0,%d) x [0,%d) x [0,%d) x [0,%d)", batch, grid[0],
+                          grid[1], grid[2]));
+  if (eflags & kErrDuplicate)
+    return fail(set_error(SUBMCONV_ERR_DUPLICATE_COORD, "a site occurs more than once"));
+  m.active_pairs = static_cast<int64_t>(host_small[1]);
+  m.nbr = nbr;
+  m.order = order;
+  *out_map = new submconv_map_s{m};
+  return SUBMCONV_OK;
+#undef BUILD_CHECK
+}
+
+extern "C" int64_t submconv_map_num_rows(submconv_map_t map) {
+  if (!map) return set_error(SUBMCONV_ERR_INVALID_ARG, "map is NULL");
+  return map->m.n;
+}
+
+extern "C" int64_t submconv_map_active_pairs(submconv_map_t map, int32_t ksize) {
+  if (!map) return set_error(SUBMCONV_ERR_INVALID_ARG, "map is NULL");
+  if (ksize == 1) return map->m.n;
+  if (ksize == 3) return map->m.active_pairs;
+  return set_error(SUBMCONV_ERR_INVALID_ARG, "ksize = %d is not 1 or 3", ksize);
+}
+
+extern "C" int submconv_map_export(submconv_map_t map, int32_t* kmap, hipStream_t stream) {
+  clear_error();
+  if (!map) return set_error(SUBMCONV_ERR_INVALID_ARG, "map is NULL");
+  const Map& m = map->m;
+  if (m.n == 0) return SUBMCONV_OK;
+  if (!kmap) return set_error(SUBMCONV_ERR_INVALID_ARG, "kmap is NULL");
+  const int B = 256;
+  k_export<<<grid_for(m.n * kTaps3, B), B, 0, stream>>>(m.nbr, m.order, m.n, kmap);
+  SUBMCONV_HIP_CHECK(hipGetLastError());
+  return SUBMCONV_OK;
+}
+
+extern "C" int submconv_map_order(submconv_map_t map, int32_t* order, hipStream_t stream) {
+  clear_error();
+  if (!map) return set_error(SUBMCONV_ERR_INVALID_ARG, "map is NULL");
+  const Map& m = map->m;
+  if (m.n == 0) return SUBMCONV_OK;
+  if (!order) return set_error(SUBMCONV_ERR_INVALID_ARG, "order is NULL");
+  const int B = 256;
+  k_order_out<<<grid_for(m.n, B), B, 0, stream>>>(m.order, m.n, order);
+  SUBMCONV_HIP_CHECK(hipGetLastError());
+  return SUBMCONV_OK;
+}
+
+extern "C" int submconv_map_free(submconv_map_t map) {
+  clear_error();
+  if (!map) return SUBMCONV_OK;
+  int status = SUBMCONV_OK;
+  if (map->m.nbr && hipFree(map->m.nbr) != hipSuccess)
+    status = set_error(SUBMCONV_ERR_HIP, "hipFree of the map failed");
+  if (map->m.order && hipFree(map->m.order) != hipSuccess)
+    status = set_error(SUBMCONV_ERR_HIP, "hipFree of the order failed");
+  delete map;
+  return status;
+}
+
+extern "C" const char* submconv_status_string(int status) {
+  switch (status) {
+    case SUBMCONV_OK: return "ok";
+    case SUBMCONV_ERR_INVALID_ARG: return "invalid argument";
+    case SUBMCONV_ERR_COORD_OUT_OF_RANGE: return "coordinate out of range";
+    case SUBMCONV_ERR_DUPLICATE_COORD: return "duplicate coordinate";
+    case SUBMCONV_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case SUBMCONV_ERR_HIP: return "HIP runtime error";
+    case SUBMCONV_ERR_OUT_OF_MEMORY: return "out of device memory";
+    default: return "unknown status";
+  }
+}
+
+extern "C" const char* submconv_last_error(void) { return submconv::last_error_cstr(); }
+
+extern "C" int submconv_abi_version(void) { return SUBMCONV_ABI_VERSION; }

@@ -1,0 +1,53 @@
+// Internal declarations shared by the map builder and the forward kernels of
+// libsubmconv.so. Not part of the public ABI (include/submconv.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/submconv.h"
+
+namespace submconv {
+
+// Number of taps of a 3x3x3 kernel and the centre tap, k = 9(dx+1)+3(dy+1)+(dz+1).
+constexpr int kTaps3 = 27;
+constexpr int kCenterTap = 13;
+
+// Kernel map: library-owned, immutable after the build.
+//  nbr   [27][n] int32, tap-major, rows in processing order t; each entry is
+//        the caller row of the neighbour at offset d_k, or -1.
+//  order [n] int32, processing order t -> caller row; nullptr = identity.
+struct Map {
+  int device = 0;
+  int64_t n = 0;
+  int32_t batch = 1;
+  int32_t grid[3] = {0, 0, 0};
+  uint32_t flags = 0;
+  int64_t active_pairs = 0;
+  int32_t* nbr = nullptr;
+  int32_t* order = nullptr;
+};
+
+// Records a thread-local message and returns `status`.
+int set_error(int status, const char* fmt, ...);
+void clear_error();
+const char* last_error_cstr();
+
+}  // namespace submconv
+
+struct submconv_map_s {
+  submconv::Map m;
+};
+
+#define SUBMCONV_HIP_CHECK(expr)                                                              \
+  do {                                                                                        \
+    hipError_t e_ = (expr);                                                                   \
+    if (e_ != hipSuccess)                                                                     \
+      return ::submconv::set_error(e_ == hipErrorOutOfMemory ? SUBMCONV_ERR_OUT_OF_MEMORY     \
+                                                             : SUBMCONV_ERR_HIP,              \
+                                   "%s failed: %s (%s:%d)", #expr, hipGetErrorString(e_),    \
+                                   __FILE__, __LINE__);                                       \
+  } while (0)

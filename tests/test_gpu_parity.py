@@ -1,0 +1,319 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Kernel map: bit for bit (caller row order, -1 sentinel), active pairs equal.
+Features: |gpu - oracle| <= 1e-3 + 1e-2 |oracle| per element, the tolerance
+fixed for this operation (fp16 inputs, fp32 accumulation, one fp16 rounding:
+the rounding alone is 2^-11 relative, well inside it).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import cpu as oc
+from oracle import oracle as op
+
+gpu = pytest.mark.gpu
+
+ATOL, RTOL = 1e-3, 1e-2
+
+
+def _sc():
+    import submanifold_sparse_convolution_hash_amd as sc
+    sc.load_library()
+    return sc
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _to(dev, a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def _assert_close(got, ref, what):
+    got = np.asarray(got, dtype=np.float64)
+    err = np.abs(got - ref)
+    bad = err > ATOL + RTOL * np.abs(ref)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} elements outside tolerance; "
+                             f"first {idx.tolist()} got {got[tuple(idx.T)]} ref {ref[tuple(idx.T)]}")
+
+
+def _run_map(sc, dev, wl, morton):
+    coords = _to(dev, wl.coords)
+    km = sc.build_map(coords, wl.grid, wl.batch, morton=morton)
+    return km
+
+
+def _check_map(km, wl, ref_map=None):
+    if ref_map is None:
+        ref_map = oc.kernel_map(wl.coords, wl.grid, wl.batch, 3)
+    got = km.export().cpu().numpy()
+    np.testing.assert_array_equal(got, ref_map)
+    assert km.active_pairs(3) == int((ref_map >= 0).sum())
+    assert km.active_pairs(1) == wl.n
+    order = km.order().cpu().numpy()
+    np.testing.assert_array_equal(np.sort(order), np.arange(wl.n))
+    return ref_map
+
+
+# ----------------------------------------------------------------------------
+# the named configurations
+# ----------------------------------------------------------------------------
+
+
+@gpu
+@pytest.mark.parametrize("morton", [False, True])
+@pytest.mark.parametrize("name", ["c1_16_8", "c2_64_64", "c3_128_128"])
+def test_uniform_configs_full(dev, name, morton):
+    sc = _sc()
+    wl = workloads.make(name)
+    _say(f"[{name} morton={morton}] N={wl.n}")
+    km = _run_map(sc, dev, wl, morton)
+    ref_map = _check_map(km, wl)
+    feats = _to(dev, wl.feats)
+    for li, L in enumerate(wl.layers):
+        _say(f"[{name}] layer {li} ksize={L.ksize} {L.cin}->{L.cout}")
+        out = sc.forward(km, feats, _to(dev, L.W), _to(dev, L.bias)).float().cpu().numpy()
+        km_l = ref_map if L.ksize == 3 else np.arange(wl.n, dtype=np.int32)[:, None]
+        ref = oc.submconv_rows(km_l, wl.feats, L.W, L.bias)
+        _assert_close(out, ref, f"{name} layer {li}")
+
+
+@gpu
+@pytest.mark.slow
+def test_c4_shell_256(dev):
+    sc = _sc()
+    wl = workloads.make("c4_256_shell")
+    _say(f"[c4] N={wl.n}")
+    km = _run_map(sc, dev, wl, False)
+    ref_map = _check_map(km, wl)
+    L = wl.layers[0]
+    out = sc.forward(km, _to(dev, wl.feats), _to(dev, L.W), None)
+    rows = np.random.default_rng(0).choice(wl.n, 1500, replace=False)
+    rows = np.concatenate([rows, [0, wl.n - 1]])
+    got = out[torch.from_numpy(rows).to(dev)].float().cpu().numpy()
+    ref = oc.submconv_rows(ref_map, wl.feats, L.W, None, rows)
+    _assert_close(got, ref, "c4 sampled rows")
+
+
+@gpu
+@pytest.mark.slow
+def test_c5_chain_512(dev):
+    sc = _sc()
+    wl = workloads.make("c5_512_chain")
+    _say(f"[c5] N={wl.n}")
+    km = _run_map(sc, dev, wl, True)
+    ref_map = _check_map(km, wl)
+    x = _to(dev, wl.feats)
+    rows = np.random.default_rng(1).choice(wl.n, 3000, replace=False)
+    rows_t = torch.from_numpy(rows).to(dev)
+    for li, L in enumerate(wl.layers):
+        _say(f"[c5] layer {li} ksize={L.ksize} {L.cin}->{L.cout}")
+        x_np = x.cpu().numpy()  # the oracle consumes the GPU's fp16 input of this layer
+        y = sc.forward(km, x, _to(dev, L.W), None)
+        km_l = ref_map if L.ksize == 3 else np.arange(wl.n, dtype=np.int32)[:, None]
+        ref = oc.submconv_rows(km_l, x_np, L.W, None, rows)
+        _assert_close(y[rows_t].float().cpu().numpy(), ref, f"c5 layer {li}")
+        x = y
+
+
+# ----------------------------------------------------------------------------
+# shapes, ragged tiles and edge cases
+# ----------------------------------------------------------------------------
+
+SHAPES = [(8, 8), (16, 24), (40, 48), (32, 16), (32, 32), (64, 32), (64, 64), (128, 64),
+          (128, 128), (256, 256), (32, 128), (128, 256)]
+
+
+@gpu
+@pytest.mark.parametrize("cin,cout", SHAPES)
+@pytest.mark.parametrize("ksize", [3, 1])
+def test_shapes_small(dev, cin, cout, ksize):
+    sc = _sc()
+    wl = workloads.random_small(1000 + cin + cout, G=14, occ=0.25, cin=cin, cout=cout, batch=2,
+                                ksize=ksize, bias=True)
+    _say(f"[shape {cin}->{cout} k{ksize}] N={wl.n}")
+    L = wl.layers[0]
+    km = _run_map(sc, dev, wl, False)
+    out = sc.forward(km, _to(dev, wl.feats), _to(dev, L.W), _to(dev, L.bias)).float().cpu().numpy()
+    kref = op.kernel_map(wl.coords, wl.grid, ksize, wl.batch)
+    ref = oc.submconv_rows(kref, wl.feats, L.W, L.bias)
+    _assert_close(out, ref, f"{cin}->{cout} k{ksize}")
+
+
+@gpu
+@pytest.mark.parametrize("n", [1, 2, 15, 16, 17, 63, 64, 65, 255, 256, 257, 511, 513, 1000])
+def test_ragged_row_counts(dev, n):
+    sc = _sc()
+    rng = np.random.default_rng(n)
+    G = 12
+    coords = workloads.uniform_coords(G, n, rng)
+    feats = workloads.normal_f16(rng, (n, 128))
+    W = workloads.normal_f16(rng, (27, 128, 128), std=0.05)
+    bias = rng.standard_normal(128).astype(np.float32)
+    _say(f"[ragged n={n}]")
+    km = sc.build_map(_to(dev, coords), (G, G, G), 1)
+    ref_map = oc.kernel_map(coords, (G, G, G), 1, 3)
+    np.testing.assert_array_equal(km.export().cpu().numpy(), ref_map)
+    out = sc.forward(km, _to(dev, feats), _to(dev, W), _to(dev, bias)).float().cpu().numpy()
+    ref = oc.submconv_rows(ref_map, feats, W, bias)
+    _assert_close(out, ref, f"ragged {n}")
+
+
+@gpu
+def test_empty_input(dev):
+    sc = _sc()
+    coords = torch.zeros((0, 4), dtype=torch.int32, device=dev)
+    km = sc.build_map(coords, (8, 8, 8), 1)
+    assert km.num_rows == 0 and km.active_pairs() == 0
+    assert km.export().shape == (0, 27)
+    out = sc.forward(km, torch.zeros((0, 32), dtype=torch.float16, device=dev),
+                     torch.zeros((27, 32, 32), dtype=torch.float16, device=dev))
+    assert out.shape == (0, 32)
+
+
+@gpu
+def test_dense_block_full_occupancy(dev):
+    """100 % occupancy: every interior site has all 27 neighbours."""
+    sc = _sc()
+    G = 9
+    lin = np.arange(G ** 3)
+    coords = np.stack([np.zeros_like(lin), lin // (G * G), (lin // G) % G, lin % G], 1).astype(np.int32)
+    rng = np.random.default_rng(5)
+    feats = workloads.normal_f16(rng, (len(lin), 64))
+    W = workloads.normal_f16(rng, (27, 64, 64), std=0.03)
+    km = sc.build_map(_to(dev, coords), (G, G, G), 1)
+    ref_map = oc.kernel_map(coords, (G, G, G), 1, 3)
+    np.testing.assert_array_equal(km.export().cpu().numpy(), ref_map)
+    out = sc.forward(km, _to(dev, feats), _to(dev, W)).float().cpu().numpy()
+    _assert_close(out, oc.submconv_rows(ref_map, feats, W, None), "dense block")
+
+
+@gpu
+def test_golden_hand_case_on_gpu(dev):
+    """The hand-derived four-site case, padded to Cin = Cout = 8 with zeros."""
+    sc = _sc()
+    coords = np.array([[0, 1, 1, 1], [0, 2, 1, 1], [0, 1, 2, 1], [0, 2, 2, 2]], dtype=np.int32)
+    feats = np.zeros((4, 8), dtype=np.float16)
+    feats[:, 0] = [1, 2, 3, 5]
+    W = np.zeros((27, 8, 8), dtype=np.float16)
+    W[:, 0, 0] = np.arange(1, 28)
+    bias = np.zeros(8, dtype=np.float32)
+    bias[0] = 0.5
+    km = sc.build_map(_to(dev, coords), (4, 4, 4), 1)
+    out = sc.forward(km, _to(dev, feats), _to(dev, W), _to(dev, bias)).float().cpu().numpy()
+    np.testing.assert_array_equal(out[:, 0], [246.5, 147.5, 213.5, 103.5])
+    np.testing.assert_array_equal(out[:, 1:], 0)
+
+
+# ----------------------------------------------------------------------------
+# properties: determinism, order independence, batch independence
+# ----------------------------------------------------------------------------
+
+
+@gpu
+def test_bitwise_determinism_and_morton_invariance(dev):
+    sc = _sc()
+    wl = workloads.make("c2_64_64")
+    L = wl.layers[0]
+    feats, W = _to(dev, wl.feats), _to(dev, L.W)
+    km0 = _run_map(sc, dev, wl, False)
+    km1 = _run_map(sc, dev, wl, True)
+    a = sc.forward(km0, feats, W)
+    b = sc.forward(km0, feats, W)
+    c = sc.forward(km1, feats, W)
+    assert torch.equal(a, b)
+    assert torch.equal(km0.export(), km1.export())
+    assert torch.equal(a, c)
+    assert not torch.equal(km1.order().cpu(), torch.arange(wl.n, dtype=torch.int32))
+
+
+@gpu
+def test_shuffled_rows_permute_outputs(dev):
+    sc = _sc()
+    wl = workloads.random_small(77, G=16, occ=0.2, cin=64, cout=64)
+    L = wl.layers[0]
+    perm = np.random.default_rng(3).permutation(wl.n)
+    km = sc.build_map(_to(dev, wl.coords), wl.grid, 1)
+    kp = sc.build_map(_to(dev, wl.coords[perm]), wl.grid, 1)
+    a = sc.forward(km, _to(dev, wl.feats), _to(dev, L.W), _to(dev, L.bias))
+    b = sc.forward(kp, _to(dev, wl.feats[perm]), _to(dev, L.W), _to(dev, L.bias))
+    assert torch.equal(a[torch.from_numpy(perm).to(dev)], b)
+
+
+@gpu
+def test_batch_items_are_independent(dev):
+    sc = _sc()
+    wl = workloads.random_small(78, G=12, occ=0.3, cin=32, cout=32)
+    two = np.concatenate([wl.coords, wl.coords])
+    two[wl.n:, 0] = 1
+    L = wl.layers[0]
+    km = sc.build_map(_to(dev, two), wl.grid, 2)
+    out = sc.forward(km, _to(dev, np.concatenate([wl.feats, wl.feats])), _to(dev, L.W), _to(dev, L.bias))
+    assert torch.equal(out[:wl.n], out[wl.n:])
+
+
+@gpu
+def test_prepared_weights_and_module(dev):
+    sc = _sc()
+    wl = workloads.random_small(79, G=12, occ=0.3, cin=64, cout=128)
+    L = wl.layers[0]
+    km = sc.build_map(_to(dev, wl.coords), wl.grid, 1)
+    feats = _to(dev, wl.feats)
+    ref = sc.forward(km, feats, _to(dev, L.W), _to(dev, L.bias))
+    wp = sc.prepare_weights(_to(dev, L.W))
+    again = sc.forward(km, feats, bias=_to(dev, L.bias), prepared=wp, ksize=3, cout=128)
+    assert torch.equal(ref, again)
+    mod = sc.SubMConv3d(64, 128, 3, bias=True, device=dev)
+    with torch.no_grad():
+        mod.weight.copy_(_to(dev, L.W))
+        mod.bias.copy_(_to(dev, L.bias))
+    assert torch.equal(mod(km, feats), ref)
+
+
+# ----------------------------------------------------------------------------
+# errors (forced from the host with bad inputs; every kernel exits normally)
+# ----------------------------------------------------------------------------
+
+
+@gpu
+def test_errors(dev):
+    sc = _sc()
+    dup = np.array([[0, 1, 1, 1], [0, 2, 2, 2], [0, 1, 1, 1]], dtype=np.int32)
+    with pytest.raises(sc.SubmconvError) as e:
+        sc.build_map(_to(dev, dup), (4, 4, 4), 1)
+    assert e.value.status == -3
+    oob = np.array([[0, 1, 1, 1], [0, 4, 0, 0]], dtype=np.int32)
+    with pytest.raises(sc.SubmconvError) as e:
+        sc.build_map(_to(dev, oob), (4, 4, 4), 1)
+    assert e.value.status == -2
+    neg = np.array([[0, 1, -1, 1]], dtype=np.int32)
+    with pytest.raises(sc.SubmconvError) as e:
+        sc.build_map(_to(dev, neg), (4, 4, 4), 1)
+    assert e.value.status == -2
+    bad_b = np.array([[1, 1, 1, 1]], dtype=np.int32)
+    with pytest.raises(sc.SubmconvError) as e:
+        sc.build_map(_to(dev, bad_b), (4, 4, 4), 1)
+    assert e.value.status == -2
+    ok = np.array([[0, 1, 1, 1], [0, 1, 1, 2]], dtype=np.int32)
+    km = sc.build_map(_to(dev, ok), (4, 4, 4), 1)
+    with pytest.raises(sc.SubmconvError) as e:
+        sc.forward(km, torch.zeros((2, 12), dtype=torch.float16, device=dev),
+                   torch.zeros((27, 12, 16), dtype=torch.float16, device=dev))
+    assert e.value.status == -4
+    with pytest.raises(sc.SubmconvError) as e:
+        sc.forward(km, torch.zeros((2, 16), dtype=torch.float16, device=dev),
+                   bias=None, prepared=torch.zeros(27 * 16 * 16, dtype=torch.float16, device=dev),
+                   ksize=2, cout=16)
+    assert e.value.status == -1
