@@ -8,25 +8,32 @@
 // issue #1 thread); the absent-neighbour skip generalises that thread's
 // skip-empty-V vote to single rows.
 //
-// Design of the MFMA kernel (one workgroup = one tile of M output rows x
+// Design of the MFMA kernel (one workgroup = one tile of 256 output rows x
 // COUT_T output columns; nothing is shared between workgroups, no atomics):
-//   1. Prologue: the tile's 27 x M neighbour entries are read once; a wave
-//      ballot per (tap, 64 rows) gives per-tap row masks, from which every
-//      tap gets a compacted list of the tile rows that have that neighbour
-//      (sentinel rows are dropped here, so no zero rows are ever multiplied
-//      beyond the padding of the last 16-row group of a tap).
-//   2. Main loop, per wave and without barriers: each wave owns COUT_T/NW
-//      output columns and walks all 16-row groups (centre tap first, then
-//      taps 0..26). For a group it gathers the 16 neighbour feature rows
-//      straight from HBM/L2 into MFMA B fragments (contiguous 16-byte loads),
-//      multiplies them with the tap's weight fragments on
-//      v_mfma_f32_16x16x32_f16 (fp32 accumulate), and adds the 16x16 results
-//      into an fp32 accumulator tile held in LDS. The centre tap initialises
-//      the accumulator (with the bias), every later tap read-modify-writes it;
-//      rows are unique within a tap and columns are private to a wave, so
-//      there are no conflicts and the order of additions is fixed.
-//   3. Epilogue: one rounding to fp16 (round to nearest even) and coalesced
-//      row stores at the caller's row index.
+//   * The map holds, per tile, the neighbours of every tap compacted into a
+//     list of {neighbour row, row in tile} (built once with the map), so
+//     absent neighbours cost nothing here: only the padding of the last
+//     16-row group of a tap is multiplied by zeros.
+//   * Each wave owns COUT_T/NW output columns and walks all 16-row groups of
+//     the tile (centre tap first, then taps 0..26, in list order). For a group
+//     it gathers the 16 feature rows straight into MFMA B fragments
+//     (contiguous 16-byte loads per lane), multiplies them with the tap's
+//     weight fragments on v_mfma_f32_16x16x32_f16 (fp32 accumulate) and adds
+//     the 16x16 results into an fp32 accumulator tile in LDS. The centre tap
+//     initialises the accumulator with the bias, later taps read-modify-write
+//     it; rows are unique within a tap and columns are private to a wave, so
+//     there are no conflicts and the order of additions is fixed.
+//   * The group loop is software-pipelined: list entries are fetched PIPE
+//     groups ahead, feature rows and weight fragments (when the tap
+//     changes) PIPE/2 groups ahead.
+//     Feature rows and entries go through buffer loads whose masked lanes
+//     use an out-of-range offset (zeros, no memory traffic) instead of
+//     branches; weight fragments are loaded only when the tap changes.
+//   * Epilogue: one rounding to fp16 (round to nearest even) and coalesced
+//     row stores at the caller's row index.
+#include <type_traits>
+#include <utility>
+
 #include "submconv_internal.h"
 
 namespace submconv {
@@ -36,10 +43,6 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxChannels = 1024;
-
-// Processing position p -> tap: the centre first (it initialises the
-// accumulator), then the other 26 taps in ascending order.
-__device__ __forceinline__ int tap_at(int p) { return p == 0 ? kCenterTap : (p <= kCenterTap ? p - 1 : p); }
 
 __device__ __forceinline__ int excl_scan_wave(int v, int lane) {
   int x = v;
@@ -51,35 +54,71 @@ __device__ __forceinline__ int excl_scan_wave(int v, int lane) {
   return x - v;
 }
 
+// Buffer resource over [base, base + bytes): loads at offsets >= bytes return
+// zeros without touching memory, which lets masked lanes and skipped loads
+// issue the same instructions as live ones (no branches, static wait counts).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+constexpr uint32_t kOob = 0x80000000u;  // an offset past every buffer (< 2 GiB)
+
+__device__ __forceinline__ half8 bload_h8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ int2 bload_i2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(int2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
 // ---------------------------------------------------------------------------
 // MFMA kernel
 // ---------------------------------------------------------------------------
 
-template <int CIN, int COUT_T, int M, int NW>
+template <int CIN, int COUT_T, int NW>
 struct Cfg {
+  static constexpr int M = kTileRows;      // output rows per tile
   static constexpr int S = CIN / 32;       // 32-channel MFMA K steps
   static constexpr int CW = COUT_T / NW;   // output columns per wave
   static constexpr int NB = CW / 16;       // 16-column MFMA blocks per wave
-  static constexpr int CHUNKS = M / 64;    // 64-row ballot chunks per tile
   static constexpr int NQ = COUT_T / 4;    // float4 chunks per accumulator row
-  static constexpr int MAXG = kTaps3 * M / 16;
   static_assert(CIN % 32 == 0 && CIN <= 256, "CIN");
   static_assert(CW % 16 == 0 && NB >= 1, "COUT_T/NW");
-  static_assert(M % 64 == 0 && M <= 256, "M");
   static_assert((NQ & (NQ - 1)) == 0, "NQ must be a power of two");
 };
 
-template <int CIN, int COUT_T, int M, int NW>
+// One 16-row group of the tile's schedule (uniform across the wave).
+struct Group {
+  int p;      // processing position (0 = centre tap)
+  int start;  // first entry of the group within the tile's list
+  int cnt;    // live rows in the group (<= 16; <= 0 past the end)
+};
+
+// Group g of the schedule whose per-position entry counts, entry offsets and
+// group offsets sit in lanes p = 0..26 (cnt_p, off_p, goff_p).
+__device__ __forceinline__ Group group_at(int g, int cnt_p, int off_p, int goff_p, int lane) {
+  const uint64_t m = __ballot(lane < kTaps3 && cnt_p > 0 && goff_p <= g);
+  const int p = m ? 63 - __clzll(m) : 0;
+  const int j = g - __builtin_amdgcn_readlane(goff_p, p);
+  Group gr;
+  gr.p = p;
+  gr.start = __builtin_amdgcn_readlane(off_p, p) + 16 * j;
+  const int left = __builtin_amdgcn_readlane(cnt_p, p) - 16 * j;
+  gr.cnt = m ? (left < 16 ? left : 16) : 0;
+  return gr;
+}
+
+template <int CIN, int COUT_T, int NW, bool K3, int PIPE>
 __global__ __launch_bounds__(64 * NW) void k_fwd_mfma(
-    const int32_t* __restrict__ nbr, const int32_t* __restrict__ order, int64_t n, int ksize,
+    const int2* __restrict__ ent, const int32_t* __restrict__ tile_off,
+    const uint16_t* __restrict__ tile_cnt, const int32_t* __restrict__ order, int64_t n,
     const _Float16* __restrict__ feats, const _Float16* __restrict__ wp,
     const float* __restrict__ bias, _Float16* __restrict__ out, int cout, int n_tiles, int n_ct,
     int tiles_per_xcd) {
-  using C = Cfg<CIN, COUT_T, M, NW>;
+  using C = Cfg<CIN, COUT_T, NW>;
+  constexpr int M = C::M;
+  constexpr int NB = C::NB;
+  constexpr int S = C::S;
   __shared__ float4v acc[M * C::NQ];
-  __shared__ uint8_t lrow[kTaps3 * M];
-  __shared__ uint64_t masks[kTaps3 * C::CHUNKS];
-  __shared__ uint32_t gtab[C::MAXG];
 
   // Workgroups are dealt to the 8 XCDs round robin; give each XCD a
   // contiguous run of row tiles (and all column tiles of a row tile) so that
@@ -99,130 +138,149 @@ __global__ __launch_bounds__(64 * NW) void k_fwd_mfma(
   const int rows_here = static_cast<int>(n - t0 < M ? n - t0 : M);
   const int c0 = ct * COUT_T;
 
-  // ---- 1. per-tap row masks ----
-  if (ksize == 3) {
-    for (int ch = w; ch < C::CHUNKS; ch += NW) {
-      const int r = ch * 64 + lane;
-      const bool valid = r < rows_here;
-      int32_t v[kTaps3];
-#pragma unroll
-      for (int k = 0; k < kTaps3; ++k) v[k] = valid ? nbr[static_cast<int64_t>(k) * n + t0 + r] : -1;
-#pragma unroll
-      for (int k = 0; k < kTaps3; ++k) {
-        const uint64_t m = __ballot(v[k] >= 0);
-        if (lane == 0) masks[k * C::CHUNKS + ch] = m;
-      }
-    }
-  }
-  __syncthreads();
-
-  // per-position counts and offsets (every wave computes them; lanes p < 27)
+  // ---- schedule: entries per processing position, in lanes p < 27 ----
   int cnt_p = 0;
-  if (ksize == 3) {
-    if (lane < kTaps3) {
-      const int k = tap_at(lane);
-#pragma unroll
-      for (int ch = 0; ch < C::CHUNKS; ++ch) cnt_p += __popcll(masks[k * C::CHUNKS + ch]);
-    }
+  int64_t ent0 = 0, ent1 = 0;
+  if (K3) {
+    if (lane < kTaps3) cnt_p = tile_cnt[static_cast<int64_t>(tile) * kTaps3 + lane];
+    ent0 = tile_off[tile];
+    ent1 = tile_off[tile + 1];
   } else {
     cnt_p = lane == 0 ? rows_here : 0;
   }
   const int ng_p = (cnt_p + 15) >> 4;
   const int off_p = excl_scan_wave(cnt_p, lane);
   const int goff_p = excl_scan_wave(ng_p, lane);
-  const int n_groups = __shfl(goff_p + ng_p, kTaps3 - 1, 64);
+  const int n_groups = __builtin_amdgcn_readlane(goff_p + ng_p, kTaps3 - 1);
 
-  // compacted row lists for the off-centre taps
-  if (ksize == 3) {
-    for (int ch = w; ch < C::CHUNKS; ch += NW) {
-      const int r = ch * 64 + lane;
-      const uint64_t below = (1ull << lane) - 1ull;
-      for (int p = 1; p < kTaps3; ++p) {
-        const int k = tap_at(p);
-        int base = __shfl(off_p, p, 64);
-        for (int c2 = 0; c2 < ch; ++c2) base += __popcll(masks[k * C::CHUNKS + c2]);
-        const uint64_t m = masks[k * C::CHUNKS + ch];
-        if ((m >> lane) & 1ull) lrow[base + __popcll(m & below)] = static_cast<uint8_t>(r);
+  const int s = lane & 15;   // slot (row of the group) this lane gathers
+  const int kg = lane >> 4;  // channel quarter this lane covers
+  const int cwb = c0 + w * C::CW;
+  const int qw = (w * C::CW) >> 2;
+
+  // bias of this lane's output columns, added once by the centre tap
+  float4v bias4[NB];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bias4[cb][i] = bias ? bias[cwb + cb * 16 + 4 * kg + i] : 0.f;
+
+  const __amdgpu_buffer_rsrc_t rf = make_rsrc(feats, static_cast<uint32_t>(n * CIN * 2));
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(wp, static_cast<uint32_t>((K3 ? kTaps3 : 1) * CIN * cout * 2));
+  const __amdgpu_buffer_rsrc_t re = make_rsrc(ent + ent0, static_cast<uint32_t>((ent1 - ent0) * 8));
+
+  auto sched = [&](int g) { return group_at(g, cnt_p, off_p, goff_p, lane); };
+  auto tap_of = [&](const Group& gr) { return K3 ? tap_at(gr.p) : 0; };
+  // entry {source row, row in tile} of this lane's slot in group gr
+  auto load_entry = [&](const Group& gr) -> int2 {
+    const bool live = s < gr.cnt;
+    if (K3) return bload_i2(re, live ? static_cast<uint32_t>(gr.start + s) * 8u : kOob);
+    int2 e;
+    e.x = static_cast<int>(t0) + gr.start + s;
+    e.y = gr.start + s;
+    return e;
+  };
+  auto load_b = [&](int2 e, bool live, half8 (&B)[S]) {
+    const uint32_t base = static_cast<uint32_t>(e.x) * (CIN * 2) + kg * (CIN / 2);
+#pragma unroll
+    for (int st = 0; st < S; ++st) B[st] = bload_h8(rf, live ? base + st * 16 : kOob);
+  };
+  auto load_a = [&](int tap, bool need, half8 (&A)[NB][S]) {
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+      const uint32_t base =
+          static_cast<uint32_t>(((tap * (cout / 16) + (cwb >> 4) + cb) * S) * 1024 + lane * 16);
+#pragma unroll
+      for (int st = 0; st < S; ++st)
+        if (need) A[cb][st] = bload_h8(rw, base + st * 1024);
+    }
+  };
+
+  // ---- software pipeline over the groups of the tile ----
+  // Group g is multiplied in step g. Step g requests, in this order, the
+  // weights of group g + LA (only if its tap changes: out-of-range loads
+  // would still cost address-unit cycles), the feature rows of group g + LA
+  // and the entry of
+  // group g + U. Every buffer is a ring indexed by g mod U and the loop is
+  // unrolled by U, so no register with a load in flight is ever copied, the
+  // wait counts are static, and each load has LA steps to arrive.
+  constexpr int U = PIPE;
+  constexpr int LA = U / 2;
+  half8 AL[U][NB][S];  // weights requested for a group (zeros if unchanged)
+  bool needA[U];
+  half8 Acur[NB][S];   // weights of the tap being multiplied
+  half8 B[U][S];       // feature rows
+  int2 E[U];           // entries {source row, row in tile}
+  Group G[U];          // schedule
+
+#pragma unroll
+  for (int i = 0; i < U; ++i) {
+    G[i] = sched(i);
+    E[i] = load_entry(G[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    needA[i] = i == 0 || tap_of(G[i]) != tap_of(G[i - 1]);
+    load_a(tap_of(G[i]), needA[i], AL[i]);
+    load_b(E[i], s < G[i].cnt, B[i]);
+  }
+
+  auto step = [&](int g, auto qc) {
+    constexpr int q = decltype(qc)::value;  // g mod U
+    constexpr int qn = (q + LA) % U;        // (g + LA) mod U
+    const Group cur = G[q];
+    const bool live = s < cur.cnt;
+    const int r = E[q].y;
+    // group g + LA: weights (if its tap changes) and feature rows
+    const Group gn = sched(g + LA);
+    const Group gp = sched(g + LA - 1);
+    needA[qn] = tap_of(gn) != tap_of(gp);
+    load_a(tap_of(gn), needA[qn], AL[qn]);
+    load_b(E[qn], s < G[qn].cnt, B[qn]);
+    // accumulator rows this lane will update (read before the multiply)
+    float4v old[NB];
+    if (live && cur.p != 0) {
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        const int qq = qw + cb * 4 + kg;
+        old[cb] = acc[r * C::NQ + (qq ^ (r & (C::NQ - 1)))];
       }
     }
-  }
-  if (w == 0 && lane < kTaps3) {
-    for (int j = 0; j < ng_p; ++j) {
-      const int left = cnt_p - 16 * j;
-      gtab[goff_p + j] = static_cast<uint32_t>(off_p + 16 * j) |
-                         (static_cast<uint32_t>(left < 16 ? left : 16) << 16) |
-                         (static_cast<uint32_t>(lane) << 24);
+    // weights of group g
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+      for (int st = 0; st < S; ++st) Acur[cb][st] = needA[q] ? AL[q][cb][st] : Acur[cb][st];
+    // group g: multiply and accumulate
+    float4v d[NB];
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+      d[cb] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < S; ++st)
+        d[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Acur[cb][st], B[q][st], d[cb], 0, 0, 0);
     }
+    if (live) {
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        const int qq = qw + cb * 4 + kg;
+        acc[r * C::NQ + (qq ^ (r & (C::NQ - 1)))] = cur.p == 0 ? d[cb] + bias4[cb] : old[cb] + d[cb];
+      }
+    }
+    // group g + U: entry, into the slot group g has just released
+    G[q] = sched(g + U);
+    E[q] = load_entry(G[q]);
+  };
+
+  for (int g = 0; g < n_groups; g += U) {
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (step(g + I, std::integral_constant<int, I>{}), ...);
+    }(std::make_integer_sequence<int, U>{});
   }
   __syncthreads();
 
-  // ---- 2. main loop: groups of 16 compacted rows ----
-  const int s = lane & 15;
-  const int kg = lane >> 4;
-  const int cwb = c0 + w * C::CW;  // first output column of this wave
-  const int qw = (w * C::CW) >> 2; // first float4 chunk of this wave in the tile
-  half8 A[C::NB][C::S];
-  int kcur = -1;
-  const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int g = 0; g < n_groups; ++g) {
-    const uint32_t e = gtab[g];
-    const int start = static_cast<int>(e & 0xffffu);
-    const int cnt = static_cast<int>((e >> 16) & 0xffu);
-    const int p = static_cast<int>(e >> 24);
-    const bool valid = s < cnt;
-    const int kw = ksize == 3 ? tap_at(p) : 0;
-    int r = 0;
-    int64_t src = 0;
-    if (valid) {
-      if (p == 0) {
-        r = start + s;
-        src = (ksize == 3 && order) ? order[t0 + r] : t0 + r;
-      } else {
-        r = lrow[start + s];
-        src = nbr[static_cast<int64_t>(kw) * n + t0 + r];
-      }
-    }
-    half8 B[C::S];
-    const _Float16* fp = feats + src * CIN + kg * (CIN / 4);
-#pragma unroll
-    for (int st = 0; st < C::S; ++st)
-      B[st] = valid ? *reinterpret_cast<const half8*>(fp + 8 * st) : zero8;
-    if (kw != kcur) {
-      kcur = kw;
-#pragma unroll
-      for (int cb = 0; cb < C::NB; ++cb) {
-        const _Float16* wq =
-            wp + ((static_cast<int64_t>(kw) * (cout / 16) + (cwb >> 4) + cb) * C::S) * 512 + lane * 8;
-#pragma unroll
-        for (int st = 0; st < C::S; ++st) A[cb][st] = *reinterpret_cast<const half8*>(wq + st * 512);
-      }
-    }
-#pragma unroll
-    for (int cb = 0; cb < C::NB; ++cb) {
-      float4v d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int st = 0; st < C::S; ++st) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[cb][st], B[st], d, 0, 0, 0);
-      if (valid) {
-        const int q = qw + cb * 4 + kg;
-        float4v* dst = &acc[r * C::NQ + (q ^ (r & (C::NQ - 1)))];
-        if (p == 0) {
-          if (bias) {
-            const float* bp = bias + cwb + cb * 16 + 4 * kg;
-            d[0] += bp[0];
-            d[1] += bp[1];
-            d[2] += bp[2];
-            d[3] += bp[3];
-          }
-          *dst = d;
-        } else {
-          *dst += d;
-        }
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- 3. epilogue: fp32 -> fp16 (RNE), rows to their caller index ----
+  // ---- epilogue: fp32 -> fp16 (RNE), rows to their caller index ----
   constexpr int C8 = COUT_T / 8;
   for (int idx = tid; idx < rows_here * C8; idx += 64 * NW) {
     const int r = idx / C8;
@@ -239,7 +297,7 @@ __global__ __launch_bounds__(64 * NW) void k_fwd_mfma(
     h[5] = static_cast<_Float16>(b[1]);
     h[6] = static_cast<_Float16>(b[2]);
     h[7] = static_cast<_Float16>(b[3]);
-    const int64_t orow = (ksize == 3 && order) ? order[t0 + r] : t0 + r;
+    const int64_t orow = (K3 && order) ? order[t0 + r] : t0 + r;
     *reinterpret_cast<half8*>(out + orow * cout + c0 + 8 * c8) = h;
   }
 }
@@ -321,6 +379,12 @@ bool use_mfma(int cin, int cout) {
   return cin_ok && cout % 16 == 0;
 }
 
+// The MFMA kernel addresses features, weights and lists through 32-bit
+// buffer offsets below 2 GiB.
+bool fits_buffers(const Map& m, int cin) {
+  return m.n * cin * 2 < (int64_t{1} << 31) - 64 && m.active_pairs * 8 < (int64_t{1} << 31) - 64;
+}
+
 int check_shape(int32_t ksize, int32_t cin, int32_t cout) {
   if (ksize != 1 && ksize != 3)
     return set_error(SUBMCONV_ERR_INVALID_ARG, "ksize = %d is not 1 or 3", ksize);
@@ -331,19 +395,25 @@ int check_shape(int32_t ksize, int32_t cin, int32_t cout) {
   return SUBMCONV_OK;
 }
 
-template <int CIN, int COUT_T, int M, int NW>
+template <int CIN, int COUT_T, int NW>
 int launch_mfma(const Map& m, int ksize, const _Float16* feats, const _Float16* wp,
                 const float* bias, _Float16* out, int cout, hipStream_t stream) {
-  const int64_t n_tiles64 = (m.n + M - 1) / M;
+  const int64_t n_tiles64 = (m.n + kTileRows - 1) / kTileRows;
   if (n_tiles64 > (int64_t{1} << 28))
     return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "too many rows");
   const int n_tiles = static_cast<int>(n_tiles64);
   const int n_ct = cout / COUT_T;
   const int tiles_per_xcd = (n_tiles + 7) / 8;
   const int64_t blocks = int64_t{8} * tiles_per_xcd * n_ct;
-  k_fwd_mfma<CIN, COUT_T, M, NW><<<static_cast<unsigned>(blocks), 64 * NW, 0, stream>>>(
-      ksize == 3 ? m.nbr : nullptr, ksize == 3 ? m.order : nullptr, m.n, ksize, feats, wp, bias,
-      out, cout, n_tiles, n_ct, tiles_per_xcd);
+  constexpr int PIPE = CIN <= 128 ? 4 : 2;  // ring depth (registers scale with CIN)
+  if (ksize == 3)
+    k_fwd_mfma<CIN, COUT_T, NW, true, PIPE><<<static_cast<unsigned>(blocks), 64 * NW, 0, stream>>>(
+        m.ent, m.tile_off, m.tile_cnt, m.order, m.n, feats, wp, bias, out, cout, n_tiles, n_ct,
+        tiles_per_xcd);
+  else
+    k_fwd_mfma<CIN, COUT_T, NW, false, PIPE><<<static_cast<unsigned>(blocks), 64 * NW, 0, stream>>>(
+        nullptr, nullptr, nullptr, nullptr, m.n, feats, wp, bias, out, cout, n_tiles, n_ct,
+        tiles_per_xcd);
   SUBMCONV_HIP_CHECK(hipGetLastError());
   return SUBMCONV_OK;
 }
@@ -351,13 +421,10 @@ int launch_mfma(const Map& m, int ksize, const _Float16* feats, const _Float16* 
 template <int CIN>
 int dispatch_cout(const Map& m, int ksize, const _Float16* feats, const _Float16* wp,
                   const float* bias, _Float16* out, int cout, hipStream_t stream) {
-  if (cout % 128 == 0)
-    return launch_mfma<CIN, 128, 256, 4>(m, ksize, feats, wp, bias, out, cout, stream);
-  if (cout % 64 == 0)
-    return launch_mfma<CIN, 64, 256, 4>(m, ksize, feats, wp, bias, out, cout, stream);
-  if (cout % 32 == 0)
-    return launch_mfma<CIN, 32, 256, 2>(m, ksize, feats, wp, bias, out, cout, stream);
-  return launch_mfma<CIN, 16, 256, 1>(m, ksize, feats, wp, bias, out, cout, stream);
+  if (cout % 128 == 0) return launch_mfma<CIN, 128, 4>(m, ksize, feats, wp, bias, out, cout, stream);
+  if (cout % 64 == 0) return launch_mfma<CIN, 64, 4>(m, ksize, feats, wp, bias, out, cout, stream);
+  if (cout % 32 == 0) return launch_mfma<CIN, 32, 2>(m, ksize, feats, wp, bias, out, cout, stream);
+  return launch_mfma<CIN, 16, 1>(m, ksize, feats, wp, bias, out, cout, stream);
 }
 
 }  // namespace
@@ -408,7 +475,7 @@ extern "C" int submconv_forward(submconv_map_t map, const uint16_t* feats_u16, c
   const _Float16* feats = reinterpret_cast<const _Float16*>(feats_u16);
   const _Float16* wp = reinterpret_cast<const _Float16*>(Wp);
   _Float16* out = reinterpret_cast<_Float16*>(out_u16);
-  if (use_mfma(cin, cout)) {
+  if (use_mfma(cin, cout) && fits_buffers(m, cin)) {
     switch (cin) {
       case 32: return dispatch_cout<32>(m, ksize, feats, wp, bias, out, cout, stream);
       case 64: return dispatch_cout<64>(m, ksize, feats, wp, bias, out, cout, stream);

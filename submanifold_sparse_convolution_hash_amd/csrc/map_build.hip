@@ -14,8 +14,12 @@
 //            that is already present raises the duplicate flag
 //   order    optional Morton codes + radix sort -> processing order
 //   query    27 probes per site -> nbr[27][n] (tap-major), pair count
-//   readback flags + pair count (the single host wait)
+//   tiles    per tile of kTileRows processing rows, the neighbours of each
+//            tap compacted into a list of {neighbour row, row in tile}
+//            (count, exclusive scan over tiles, fill)
+//   readback flags + pair count (the host wait that reports bad sites)
 #include <rocprim/device/device_radix_sort.hpp>
+#include <rocprim/device/device_scan.hpp>
 
 #include <cstdarg>
 #include <cstring>
@@ -155,6 +159,73 @@ __global__ void k_query(const int32_t* __restrict__ coords, const int32_t* __res
   if ((threadIdx.x & 63) == 0 && hits) atomicAdd(pairs, static_cast<unsigned long long>(hits));
 }
 
+// Per tile of kTileRows processing rows: entries per processing position
+// (wave ballots over 64-row chunks) and the tile's total.
+__global__ __launch_bounds__(kTileRows) void k_tile_count(const int32_t* __restrict__ nbr, int64_t n,
+                                                          uint16_t* __restrict__ tile_cnt,
+                                                          int32_t* __restrict__ tile_tot) {
+  __shared__ int cnt[kTileRows / 64][kTaps3];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTileRows + threadIdx.x;
+  const bool valid = t < n;
+  for (int k = 0; k < kTaps3; ++k) {
+    const uint64_t m = __ballot(valid && nbr[static_cast<int64_t>(k) * n + t] >= 0);
+    if (lane == 0) cnt[w][k] = __popcll(m);
+  }
+  __syncthreads();
+  if (threadIdx.x < kTaps3) {
+    const int k = tap_at(threadIdx.x);
+    int c = 0;
+    for (int ww = 0; ww < kTileRows / 64; ++ww) c += cnt[ww][k];
+    tile_cnt[static_cast<int64_t>(blockIdx.x) * kTaps3 + threadIdx.x] = static_cast<uint16_t>(c);
+  }
+  if (threadIdx.x == 0) {
+    int tot = 0;
+    for (int k = 0; k < kTaps3; ++k)
+      for (int ww = 0; ww < kTileRows / 64; ++ww) tot += cnt[ww][k];
+    tile_tot[blockIdx.x] = tot;
+  }
+}
+
+// Writes the tile's entries {neighbour's caller row, row in tile}, ordered by
+// processing position, then row.
+__global__ __launch_bounds__(kTileRows) void k_tile_fill(const int32_t* __restrict__ nbr, int64_t n,
+                                                         const int32_t* __restrict__ tile_off,
+                                                         int2* __restrict__ ent) {
+  __shared__ uint64_t masks[kTaps3][kTileRows / 64];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTileRows + threadIdx.x;
+  const bool valid = t < n;
+  int32_t v[kTaps3];
+  for (int k = 0; k < kTaps3; ++k) {
+    v[k] = valid ? nbr[static_cast<int64_t>(k) * n + t] : -1;
+    const uint64_t m = __ballot(v[k] >= 0);
+    if (lane == 0) masks[k][w] = m;
+  }
+  __syncthreads();
+  const uint64_t below = (1ull << lane) - 1ull;
+  int64_t base = tile_off[blockIdx.x];
+  for (int p = 0; p < kTaps3; ++p) {
+    const int k = tap_at(p);
+    int before = 0, total = 0;
+    for (int ww = 0; ww < kTileRows / 64; ++ww) {
+      const int c = __popcll(masks[k][ww]);
+      before += ww < w ? c : 0;
+      total += c;
+    }
+    const uint64_t m = masks[k][w];
+    if ((m >> lane) & 1ull) {
+      int2 e;
+      e.x = v[k];
+      e.y = static_cast<int>(threadIdx.x);
+      ent[base + before + __popcll(m & below)] = e;
+    }
+    base += total;
+  }
+}
+
 __global__ void k_export(const int32_t* __restrict__ nbr, const int32_t* __restrict__ order,
                          int64_t n, int32_t* __restrict__ kmap) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -256,12 +327,19 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   while (cap < 2 * n) cap <<= 1;
   const uint64_t mask = static_cast<uint64_t>(cap - 1);
 
-  DevBuf keys, tkeys, tvals, small, mcode_in, mcode_out, midx, sort_tmp;
+  DevBuf keys, tkeys, tvals, small, mcode_in, mcode_out, midx, sort_tmp, tile_tot, scan_tmp;
   int32_t* nbr = nullptr;
   int32_t* order = nullptr;
+  uint16_t* tile_cnt = nullptr;
+  int32_t* tile_off = nullptr;
+  int2* ent = nullptr;
   auto fail = [&](int status) {
+    (void)hipStreamSynchronize(stream);
     if (nbr) (void)hipFree(nbr);
     if (order) (void)hipFree(order);
+    if (tile_cnt) (void)hipFree(tile_cnt);
+    if (tile_off) (void)hipFree(tile_off);
+    if (ent) (void)hipFree(ent);
     return status;
   };
 #define BUILD_CHECK(expr)                                                                 \
@@ -322,6 +400,26 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
                                             pairs);
   BUILD_CHECK(hipGetLastError());
 
+  // per-tile compacted lists: counts, then tile offsets (exclusive scan)
+  const int64_t n_tiles = (n + kTileRows - 1) / kTileRows;
+  BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&tile_cnt), sizeof(uint16_t) * kTaps3 * n_tiles));
+  BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&tile_off), sizeof(int32_t) * (n_tiles + 1)));
+  BUILD_CHECK(hipMalloc(&tile_tot.p, sizeof(int32_t) * (n_tiles + 1)));
+  BUILD_CHECK(hipMemsetAsync(tile_tot.p, 0, sizeof(int32_t) * (n_tiles + 1), stream));
+  k_tile_count<<<static_cast<unsigned>(n_tiles), kTileRows, 0, stream>>>(
+      nbr, n, tile_cnt, static_cast<int32_t*>(tile_tot.p));
+  BUILD_CHECK(hipGetLastError());
+  {
+    size_t tmp_bytes = 0;
+    BUILD_CHECK(rocprim::exclusive_scan(nullptr, tmp_bytes, static_cast<const int32_t*>(tile_tot.p),
+                                        tile_off, 0, static_cast<size_t>(n_tiles + 1),
+                                        rocprim::plus<int32_t>(), stream));
+    BUILD_CHECK(hipMalloc(&scan_tmp.p, tmp_bytes > 0 ? tmp_bytes : 1));
+    BUILD_CHECK(rocprim::exclusive_scan(scan_tmp.p, tmp_bytes, static_cast<const int32_t*>(tile_tot.p),
+                                        tile_off, 0, static_cast<size_t>(n_tiles + 1),
+                                        rocprim::plus<int32_t>(), stream));
+  }
+
   uint64_t host_small[2] = {0, 0};
   BUILD_CHECK(hipMemcpyAsync(host_small, small.p, 16, hipMemcpyDeviceToHost, stream));
   BUILD_CHECK(hipStreamSynchronize(stream));
@@ -333,8 +431,19 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   if (eflags & kErrDuplicate)
     return fail(set_error(SUBMCONV_ERR_DUPLICATE_COORD, "a site occurs more than once"));
   m.active_pairs = static_cast<int64_t>(host_small[1]);
+  if (m.active_pairs >= INT32_MAX)
+    return fail(set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "too many active pairs for int32 offsets"));
+  BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&ent), sizeof(int2) * m.active_pairs));
+  k_tile_fill<<<static_cast<unsigned>(n_tiles), kTileRows, 0, stream>>>(nbr, n, tile_off, ent);
+  BUILD_CHECK(hipGetLastError());
+  // the forward may run on another stream: the map is complete on return
+  BUILD_CHECK(hipStreamSynchronize(stream));
   m.nbr = nbr;
   m.order = order;
+  m.n_tiles = n_tiles;
+  m.tile_cnt = tile_cnt;
+  m.tile_off = tile_off;
+  m.ent = ent;
   *out_map = new submconv_map_s{m};
   return SUBMCONV_OK;
 #undef BUILD_CHECK
@@ -384,6 +493,12 @@ extern "C" int submconv_map_free(submconv_map_t map) {
     status = set_error(SUBMCONV_ERR_HIP, "hipFree of the map failed");
   if (map->m.order && hipFree(map->m.order) != hipSuccess)
     status = set_error(SUBMCONV_ERR_HIP, "hipFree of the order failed");
+  if (map->m.tile_cnt && hipFree(map->m.tile_cnt) != hipSuccess)
+    status = set_error(SUBMCONV_ERR_HIP, "hipFree of the tile counts failed");
+  if (map->m.tile_off && hipFree(map->m.tile_off) != hipSuccess)
+    status = set_error(SUBMCONV_ERR_HIP, "hipFree of the tile offsets failed");
+  if (map->m.ent && hipFree(map->m.ent) != hipSuccess)
+    status = set_error(SUBMCONV_ERR_HIP, "hipFree of the tile lists failed");
   delete map;
   return status;
 }

@@ -16,10 +16,26 @@ namespace submconv {
 constexpr int kTaps3 = 27;
 constexpr int kCenterTap = 13;
 
+// Rows per output tile of the forward kernels; the map's per-tile lists are
+// built for this tile size.
+constexpr int kTileRows = 256;
+
+// Processing position p -> tap: the centre first (it initialises an output
+// accumulator), then the other 26 taps in ascending order.
+__host__ __device__ inline int tap_at(int p) {
+  return p == 0 ? kCenterTap : (p <= kCenterTap ? p - 1 : p);
+}
+
 // Kernel map: library-owned, immutable after the build.
-//  nbr   [27][n] int32, tap-major, rows in processing order t; each entry is
-//        the caller row of the neighbour at offset d_k, or -1.
-//  order [n] int32, processing order t -> caller row; nullptr = identity.
+//  nbr      [27][n] int32, tap-major, rows in processing order t; each entry
+//           is the caller row of the neighbour at offset d_k, or -1.
+//  order    [n] int32, processing order t -> caller row; nullptr = identity.
+//  The same map as per-tile compacted lists (tiles of kTileRows consecutive
+//  processing rows), the form the forward kernels stream:
+//  tile_cnt [n_tiles][27] uint16, entries per processing position p.
+//  tile_off [n_tiles + 1] int32, first entry of each tile.
+//  ent      [active_pairs] int2 {caller row of the neighbour, row in tile},
+//           ordered by (tile, position p, row in tile).
 struct Map {
   int device = 0;
   int64_t n = 0;
@@ -29,6 +45,10 @@ struct Map {
   int64_t active_pairs = 0;
   int32_t* nbr = nullptr;
   int32_t* order = nullptr;
+  int64_t n_tiles = 0;
+  uint16_t* tile_cnt = nullptr;
+  int32_t* tile_off = nullptr;
+  int2* ent = nullptr;
 };
 
 // Records a thread-local message and returns `status`.
