@@ -74,51 +74,43 @@ __device__ __forceinline__ int2 bload_i2(__amdgpu_buffer_rsrc_t r, uint32_t off)
 // MFMA kernel
 // ---------------------------------------------------------------------------
 
-template <int CIN, int COUT_T, int NW>
+template <int CIN, int COUT_T, bool K3, int NG>
 struct Cfg {
-  static constexpr int M = kTileRows;      // output rows per tile
-  static constexpr int S = CIN / 32;       // 32-channel MFMA K steps
-  static constexpr int CW = COUT_T / NW;   // output columns per wave
-  static constexpr int NB = CW / 16;       // 16-column MFMA blocks per wave
-  static constexpr int NQ = COUT_T / 4;    // float4 chunks per accumulator row
+  static constexpr int M = kTileRows;        // output rows per tile
+  static constexpr int NW = COUT_T / 32;     // waves; each owns 32 output columns
+  static constexpr int NT = 64 * NW;         // threads
+  static constexpr int S = CIN / 32;         // 32-channel MFMA K steps
+  static constexpr int NB = 2;               // 16-column MFMA blocks per wave
+  static constexpr int NQ = COUT_T / 4;      // float4 chunks per accumulator row
+  static constexpr int RC = CIN / 8;         // 16-byte chunks per feature row
+  static constexpr int GCH = 16 * RC;        // chunks per 16-row group
+  static constexpr int CPT = GCH >= NT ? GCH / NT : 1;  // chunks per loading thread
+  static constexpr int NLOAD = GCH >= NT ? NT : GCH;    // loading threads
+  static constexpr int NCG = M / 16;         // groups of the centre tap
+  static constexpr int R = NG > 8 ? NG : 8;  // ring size = unroll factor
+  static constexpr int LB = 4;               // chunks requested LB steps ahead
+  static constexpr int LE = 2;               // entries LE steps before that
   static_assert(CIN % 32 == 0 && CIN <= 256, "CIN");
-  static_assert(CW % 16 == 0 && NB >= 1, "COUT_T/NW");
-  static_assert((NQ & (NQ - 1)) == 0, "NQ must be a power of two");
+  static_assert(COUT_T % 32 == 0 && COUT_T <= 128, "COUT_T");
+  static_assert(GCH % NT == 0 || NT % GCH == 0, "chunk split");
+  static_assert(R % NG == 0 && NCG % R == 0, "schedule");
+  static_assert(LB + LE < R, "ring");
 };
 
-// One 16-row group of the tile's schedule (uniform across the wave).
-struct Group {
-  int p;      // processing position (0 = centre tap)
-  int start;  // first entry of the group within the tile's list
-  int cnt;    // live rows in the group (<= 16; <= 0 past the end)
-};
-
-// Group g of the schedule whose per-position entry counts, entry offsets and
-// group offsets sit in lanes p = 0..26 (cnt_p, off_p, goff_p).
-__device__ __forceinline__ Group group_at(int g, int cnt_p, int off_p, int goff_p, int lane) {
-  const uint64_t m = __ballot(lane < kTaps3 && cnt_p > 0 && goff_p <= g);
-  const int p = m ? 63 - __clzll(m) : 0;
-  const int j = g - __builtin_amdgcn_readlane(goff_p, p);
-  Group gr;
-  gr.p = p;
-  gr.start = __builtin_amdgcn_readlane(off_p, p) + 16 * j;
-  const int left = __builtin_amdgcn_readlane(cnt_p, p) - 16 * j;
-  gr.cnt = m ? (left < 16 ? left : 16) : 0;
-  return gr;
-}
-
-template <int CIN, int COUT_T, int NW, bool K3, int PIPE>
-__global__ __launch_bounds__(64 * NW) void k_fwd_mfma(
+template <int CIN, int COUT_T, bool K3, int NG>
+__global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
     const int2* __restrict__ ent, const int32_t* __restrict__ tile_off,
     const uint16_t* __restrict__ tile_cnt, const int32_t* __restrict__ order, int64_t n,
     const _Float16* __restrict__ feats, const _Float16* __restrict__ wp,
     const float* __restrict__ bias, _Float16* __restrict__ out, int cout, int n_tiles, int n_ct,
     int tiles_per_xcd) {
-  using C = Cfg<CIN, COUT_T, NW>;
-  constexpr int M = C::M;
-  constexpr int NB = C::NB;
-  constexpr int S = C::S;
+  using C = Cfg<CIN, COUT_T, K3, NG>;
+  static_assert(C::NT == 2 * COUT_T, "launch bounds");
+  constexpr int M = C::M, S = C::S, NB = C::NB, RC = C::RC, R = C::R, LB = C::LB, LE = C::LE;
+  constexpr int CPT = C::CPT;
   __shared__ float4v acc[M * C::NQ];
+  __shared__ half8 bt[2][C::GCH];  // feature rows of a group, 16-byte chunks, swizzled
+  __shared__ int brow[2][16];      // row in tile of each slot of that group (-1: none)
 
   // Workgroups are dealt to the 8 XCDs round robin; give each XCD a
   // contiguous run of row tiles (and all column tiles of a row tile) so that
@@ -138,7 +130,7 @@ __global__ __launch_bounds__(64 * NW) void k_fwd_mfma(
   const int rows_here = static_cast<int>(n - t0 < M ? n - t0 : M);
   const int c0 = ct * COUT_T;
 
-  // ---- schedule: entries per processing position, in lanes p < 27 ----
+  // ---- schedule: entries per processing position p, in lanes p < 27 ----
   int cnt_p = 0;
   int64_t ent0 = 0, ent1 = 0;
   if (K3) {
@@ -148,141 +140,203 @@ __global__ __launch_bounds__(64 * NW) void k_fwd_mfma(
   } else {
     cnt_p = lane == 0 ? rows_here : 0;
   }
-  const int ng_p = (cnt_p + 15) >> 4;
   const int off_p = excl_scan_wave(cnt_p, lane);
-  const int goff_p = excl_scan_wave(ng_p, lane);
-  const int n_groups = __builtin_amdgcn_readlane(goff_p + ng_p, kTaps3 - 1);
-
-  const int s = lane & 15;   // slot (row of the group) this lane gathers
-  const int kg = lane >> 4;  // channel quarter this lane covers
-  const int cwb = c0 + w * C::CW;
-  const int qw = (w * C::CW) >> 2;
-
-  // bias of this lane's output columns, added once by the centre tap
-  float4v bias4[NB];
-#pragma unroll
-  for (int cb = 0; cb < NB; ++cb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) bias4[cb][i] = bias ? bias[cwb + cb * 16 + 4 * kg + i] : 0.f;
+  // Static schedule: step f < 16 is group f of the centre tap (position 0);
+  // step f >= 16 is group (f-16) % NG of position 1 + (f-16) / NG. Groups
+  // beyond NG of a position are handled after the main loop.
+  auto pos_of = [&](int f) { return f < C::NCG ? 0 : 1 + (f - C::NCG) / NG; };
+  auto grp_of = [&](int f) { return f < C::NCG ? f : (f - C::NCG) % NG; };
+  auto start_of = [&](int p, int j) { return __builtin_amdgcn_readlane(off_p, p < kTaps3 ? p : 0) + 16 * j; };
+  auto count_of = [&](int p, int j) {
+    if (p >= (K3 ? kTaps3 : 1)) return 0;
+    const int c = __builtin_amdgcn_readlane(cnt_p, p) - 16 * j;
+    return c < 16 ? c : 16;
+  };
 
   const __amdgpu_buffer_rsrc_t rf = make_rsrc(feats, static_cast<uint32_t>(n * CIN * 2));
   const __amdgpu_buffer_rsrc_t rw =
       make_rsrc(wp, static_cast<uint32_t>((K3 ? kTaps3 : 1) * CIN * cout * 2));
   const __amdgpu_buffer_rsrc_t re = make_rsrc(ent + ent0, static_cast<uint32_t>((ent1 - ent0) * 8));
 
-  auto sched = [&](int g) { return group_at(g, cnt_p, off_p, goff_p, lane); };
-  auto tap_of = [&](const Group& gr) { return K3 ? tap_at(gr.p) : 0; };
-  // entry {source row, row in tile} of this lane's slot in group gr
-  auto load_entry = [&](const Group& gr) -> int2 {
-    const bool live = s < gr.cnt;
-    if (K3) return bload_i2(re, live ? static_cast<uint32_t>(gr.start + s) * 8u : kOob);
-    int2 e;
-    e.x = static_cast<int>(t0) + gr.start + s;
-    e.y = gr.start + s;
-    return e;
-  };
-  auto load_b = [&](int2 e, bool live, half8 (&B)[S]) {
-    const uint32_t base = static_cast<uint32_t>(e.x) * (CIN * 2) + kg * (CIN / 2);
+  // ---- loader role: this thread moves CPT 16-byte chunks of every group ----
+  const bool loader = tid < C::NLOAD;
+  int lrow[CPT], lpos[CPT];
+  uint32_t lcol[CPT];
 #pragma unroll
-    for (int st = 0; st < S; ++st) B[st] = bload_h8(rf, live ? base + st * 16 : kOob);
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + C::NT * i;
+    lrow[i] = c / RC;
+    const int lc = c % RC;
+    lcol[i] = static_cast<uint32_t>(lc * 16);
+    lpos[i] = lrow[i] * RC + (lc ^ (lrow[i] & (RC - 1)));
+  }
+  auto load_entries = [&](int f, int2 (&E)[CPT]) {
+    const int p = pos_of(f), j = grp_of(f);
+    const int st = start_of(p, j), cnt = count_of(p, j);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const bool live = loader && lrow[i] < cnt;
+      if (K3) {
+        E[i] = bload_i2(re, live ? static_cast<uint32_t>(st + lrow[i]) * 8u : kOob);
+        if (!live) E[i].y = -1;
+      } else {
+        E[i].x = static_cast<int>(t0) + st + lrow[i];
+        E[i].y = live ? st + lrow[i] : -1;
+      }
+    }
   };
-  auto load_a = [&](int tap, bool need, half8 (&A)[NB][S]) {
+  auto load_chunks = [&](const int2 (&E)[CPT], half8 (&D)[CPT]) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      D[i] = bload_h8(rf, E[i].y >= 0 ? static_cast<uint32_t>(E[i].x) * (CIN * 2) + lcol[i] : kOob);
+  };
+  auto store_chunks = [&](int slot, const int2 (&E)[CPT], const half8 (&D)[CPT]) {
+    if (loader) {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        bt[slot][lpos[i]] = D[i];
+        if (lcol[i] == 0) brow[slot][lrow[i]] = E[i].y;
+      }
+    }
+  };
+
+  // ---- MFMA role: this wave owns 32 output columns ----
+  const int s = lane & 15;   // slot of the group this lane multiplies
+  const int kg = lane >> 4;  // channel quarter of this lane
+  const int cwb = c0 + w * 32;
+  const int qw = w * 8;
+  float4v bias4[NB];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bias4[cb][i] = bias ? bias[cwb + cb * 16 + 4 * kg + i] : 0.f;
+  auto load_a = [&](int tap, half8 (&A)[NB][S]) {
+    const bool ok = tap >= 0;
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
       const uint32_t base =
           static_cast<uint32_t>(((tap * (cout / 16) + (cwb >> 4) + cb) * S) * 1024 + lane * 16);
 #pragma unroll
-      for (int st = 0; st < S; ++st)
-        if (need) A[cb][st] = bload_h8(rw, base + st * 1024);
+      for (int st = 0; st < S; ++st) A[cb][st] = bload_h8(rw, ok ? base + st * 1024 : kOob);
     }
   };
-
-  // ---- software pipeline over the groups of the tile ----
-  // Group g is multiplied in step g. Step g requests, in this order, the
-  // weights of group g + LA (only if its tap changes: out-of-range loads
-  // would still cost address-unit cycles), the feature rows of group g + LA
-  // and the entry of
-  // group g + U. Every buffer is a ring indexed by g mod U and the loop is
-  // unrolled by U, so no register with a load in flight is ever copied, the
-  // wait counts are static, and each load has LA steps to arrive.
-  constexpr int U = PIPE;
-  constexpr int LA = U / 2;
-  half8 AL[U][NB][S];  // weights requested for a group (zeros if unchanged)
-  bool needA[U];
-  half8 Acur[NB][S];   // weights of the tap being multiplied
-  half8 B[U][S];       // feature rows
-  int2 E[U];           // entries {source row, row in tile}
-  Group G[U];          // schedule
-
-#pragma unroll
-  for (int i = 0; i < U; ++i) {
-    G[i] = sched(i);
-    E[i] = load_entry(G[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < LA; ++i) {
-    needA[i] = i == 0 || tap_of(G[i]) != tap_of(G[i - 1]);
-    load_a(tap_of(G[i]), needA[i], AL[i]);
-    load_b(E[i], s < G[i].cnt, B[i]);
-  }
-
-  auto step = [&](int g, auto qc) {
-    constexpr int q = decltype(qc)::value;  // g mod U
-    constexpr int qn = (q + LA) % U;        // (g + LA) mod U
-    const Group cur = G[q];
-    const bool live = s < cur.cnt;
-    const int r = E[q].y;
-    // group g + LA: weights (if its tap changes) and feature rows
-    const Group gn = sched(g + LA);
-    const Group gp = sched(g + LA - 1);
-    needA[qn] = tap_of(gn) != tap_of(gp);
-    load_a(tap_of(gn), needA[qn], AL[qn]);
-    load_b(E[qn], s < G[qn].cnt, B[qn]);
-    // accumulator rows this lane will update (read before the multiply)
+  auto multiply = [&](int slot, bool centre, const half8 (&A)[NB][S]) {
+    const int r = brow[slot][s];
+    const bool live = r >= 0;
     float4v old[NB];
-    if (live && cur.p != 0) {
+    if (live && !centre) {
 #pragma unroll
       for (int cb = 0; cb < NB; ++cb) {
-        const int qq = qw + cb * 4 + kg;
-        old[cb] = acc[r * C::NQ + (qq ^ (r & (C::NQ - 1)))];
+        const int q = qw + cb * 4 + kg;
+        old[cb] = acc[r * C::NQ + (q ^ (r & (C::NQ - 1)))];
       }
     }
-    // weights of group g
+    half8 Bf[S];
 #pragma unroll
-    for (int cb = 0; cb < NB; ++cb)
-#pragma unroll
-      for (int st = 0; st < S; ++st) Acur[cb][st] = needA[q] ? AL[q][cb][st] : Acur[cb][st];
-    // group g: multiply and accumulate
+    for (int st = 0; st < S; ++st) {
+      const int lc = kg * (CIN / 32) + st;
+      Bf[st] = bt[slot][s * RC + (lc ^ (s & (RC - 1)))];
+    }
     float4v d[NB];
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
       d[cb] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < S; ++st)
-        d[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Acur[cb][st], B[q][st], d[cb], 0, 0, 0);
+        d[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[cb][st], Bf[st], d[cb], 0, 0, 0);
     }
     if (live) {
 #pragma unroll
       for (int cb = 0; cb < NB; ++cb) {
-        const int qq = qw + cb * 4 + kg;
-        acc[r * C::NQ + (qq ^ (r & (C::NQ - 1)))] = cur.p == 0 ? d[cb] + bias4[cb] : old[cb] + d[cb];
+        const int q = qw + cb * 4 + kg;
+        acc[r * C::NQ + (q ^ (r & (C::NQ - 1)))] = centre ? d[cb] + bias4[cb] : old[cb] + d[cb];
       }
     }
-    // group g + U: entry, into the slot group g has just released
-    G[q] = sched(g + U);
-    E[q] = load_entry(G[q]);
+  };
+  // LDS writes of this wave are complete, then all waves meet (no global
+  // memory fence: outstanding prefetches stay in flight across the barrier)
+  auto lds_barrier = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   };
 
-  for (int g = 0; g < n_groups; g += U) {
+  // ---- software pipeline over the static schedule ----
+  // Step f: write the chunks of group f+1 (requested LB-1 steps earlier) to
+  // LDS, request the chunks of group f+LB and the entries of group f+LB+LE,
+  // switch weights at a tap boundary, multiply group f from LDS, barrier.
+  // Rings are indexed by f mod R and the loops are unrolled by R, so every
+  // load has a static wait count.
+  int2 E[R][CPT];
+  half8 D[R][CPT];
+  half8 Acur[NB][S], Anext[NB][S];
+#pragma unroll
+  for (int f = 0; f < LB + LE; ++f) load_entries(f, E[f]);
+#pragma unroll
+  for (int f = 0; f < LB; ++f) load_chunks(E[f], D[f]);
+  load_a(K3 ? kCenterTap : 0, Acur);
+  if (K3) load_a(tap_at(1), Anext);
+  store_chunks(0, E[0], D[0]);
+  lds_barrier();
+
+  auto step = [&](int f, auto ic, bool centre) {
+    constexpr int i = decltype(ic)::value;  // f mod R
+    store_chunks((i + 1) & 1, E[(i + 1) % R], D[(i + 1) % R]);
+    load_chunks(E[(i + LB) % R], D[(i + LB) % R]);
+    load_entries(f + LB + LE, E[(i + LB + LE) % R]);
+    if (!centre && (i % NG) == 0) {
+      // first group of a tap: its weights arrived during the previous tap
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+        for (int st = 0; st < S; ++st) Acur[cb][st] = Anext[cb][st];
+      const int pn = pos_of(f) + 1;
+      load_a(pn < kTaps3 ? tap_at(pn) : -1, Anext);
+    }
+    multiply(i & 1, centre, Acur);
+    lds_barrier();
+  };
+  for (int f = 0; f < C::NCG; f += R) {
     [&]<int... I>(std::integer_sequence<int, I...>) {
-      (step(g + I, std::integral_constant<int, I>{}), ...);
-    }(std::make_integer_sequence<int, U>{});
+      (step(f + I, std::integral_constant<int, I>{}, true), ...);
+    }(std::make_integer_sequence<int, R>{});
+  }
+  if (K3) {
+    // the first off-centre tap starts at step NCG: make its weights current
+    for (int f = C::NCG; f < C::NCG + 26 * NG; f += R) {
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        (step(f + I, std::integral_constant<int, I>{}, false), ...);
+      }(std::make_integer_sequence<int, R>{});
+    }
+    // groups beyond NG of a tap: one at a time, without pipelining
+    for (int p = 1; p < kTaps3; ++p) {
+      const int ngp = (__builtin_amdgcn_readlane(cnt_p, p) + 15) >> 4;
+      if (ngp <= NG) continue;
+      half8 A[NB][S];
+      load_a(tap_at(p), A);
+      for (int j = NG; j < ngp; ++j) {
+        int2 e1[CPT];
+        half8 d1[CPT];
+        const int st = start_of(p, j), cnt = count_of(p, j);
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+          const bool live = loader && lrow[i] < cnt;
+          e1[i] = bload_i2(re, live ? static_cast<uint32_t>(st + lrow[i]) * 8u : kOob);
+          if (!live) e1[i].y = -1;
+        }
+        load_chunks(e1, d1);
+        store_chunks(0, e1, d1);
+        lds_barrier();
+        multiply(0, false, A);
+        lds_barrier();
+      }
+    }
   }
   __syncthreads();
 
   // ---- epilogue: fp32 -> fp16 (RNE), rows to their caller index ----
   constexpr int C8 = COUT_T / 8;
-  for (int idx = tid; idx < rows_here * C8; idx += 64 * NW) {
+  for (int idx = tid; idx < rows_here * C8; idx += C::NT) {
     const int r = idx / C8;
     const int c8 = idx - r * C8;
     const int q0 = 2 * c8, q1 = 2 * c8 + 1;
@@ -376,7 +430,7 @@ __global__ void k_copy_halves(const _Float16* __restrict__ W, int64_t total, _Fl
 
 bool use_mfma(int cin, int cout) {
   const bool cin_ok = cin == 32 || cin == 64 || cin == 128 || cin == 256;
-  return cin_ok && cout % 16 == 0;
+  return cin_ok && cout % 32 == 0;
 }
 
 // The MFMA kernel addresses features, weights and lists through 32-bit
@@ -395,9 +449,29 @@ int check_shape(int32_t ksize, int32_t cin, int32_t cout) {
   return SUBMCONV_OK;
 }
 
-template <int CIN, int COUT_T, int NW>
-int launch_mfma(const Map& m, int ksize, const _Float16* feats, const _Float16* wp,
-                const float* bias, _Float16* out, int cout, hipStream_t stream) {
+// Groups per off-centre tap in the static schedule: the NG that minimises
+// padded steps plus (about three times costlier) overflow groups, from the
+// map's histogram of groups per (tile, off-centre tap).
+int choose_ng(const Map& m) {
+  const int cands[3] = {2, 4, 16};
+  int best = 16;
+  double best_cost = 1e300;
+  for (int ng : cands) {
+    double over = 0;
+    for (int b = ng + 1; b < kNgHistBins; ++b) over += static_cast<double>(b - ng) * m.ng_hist[b];
+    const double cost = static_cast<double>(m.n_tiles) * (16 + 26 * ng) + 3.0 * over;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = ng;
+    }
+  }
+  return best;
+}
+
+template <int CIN, int COUT_T, bool K3, int NG>
+int launch_one(const Map& m, const _Float16* feats, const _Float16* wp, const float* bias,
+               _Float16* out, int cout, hipStream_t stream) {
+  using Cf = Cfg<CIN, COUT_T, K3, NG>;
   const int64_t n_tiles64 = (m.n + kTileRows - 1) / kTileRows;
   if (n_tiles64 > (int64_t{1} << 28))
     return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "too many rows");
@@ -405,26 +479,30 @@ int launch_mfma(const Map& m, int ksize, const _Float16* feats, const _Float16* 
   const int n_ct = cout / COUT_T;
   const int tiles_per_xcd = (n_tiles + 7) / 8;
   const int64_t blocks = int64_t{8} * tiles_per_xcd * n_ct;
-  constexpr int PIPE = CIN <= 128 ? 4 : 2;  // ring depth (registers scale with CIN)
-  if (ksize == 3)
-    k_fwd_mfma<CIN, COUT_T, NW, true, PIPE><<<static_cast<unsigned>(blocks), 64 * NW, 0, stream>>>(
-        m.ent, m.tile_off, m.tile_cnt, m.order, m.n, feats, wp, bias, out, cout, n_tiles, n_ct,
-        tiles_per_xcd);
-  else
-    k_fwd_mfma<CIN, COUT_T, NW, false, PIPE><<<static_cast<unsigned>(blocks), 64 * NW, 0, stream>>>(
-        nullptr, nullptr, nullptr, nullptr, m.n, feats, wp, bias, out, cout, n_tiles, n_ct,
-        tiles_per_xcd);
+  k_fwd_mfma<CIN, COUT_T, K3, NG><<<static_cast<unsigned>(blocks), Cf::NT, 0, stream>>>(
+      K3 ? m.ent : nullptr, K3 ? m.tile_off : nullptr, K3 ? m.tile_cnt : nullptr,
+      K3 ? m.order : nullptr, m.n, feats, wp, bias, out, cout, n_tiles, n_ct, tiles_per_xcd);
   SUBMCONV_HIP_CHECK(hipGetLastError());
   return SUBMCONV_OK;
+}
+
+template <int CIN, int COUT_T>
+int launch_mfma(const Map& m, int ksize, const _Float16* feats, const _Float16* wp,
+                const float* bias, _Float16* out, int cout, hipStream_t stream) {
+  if (ksize == 1) return launch_one<CIN, COUT_T, false, 2>(m, feats, wp, bias, out, cout, stream);
+  switch (choose_ng(m)) {
+    case 2: return launch_one<CIN, COUT_T, true, 2>(m, feats, wp, bias, out, cout, stream);
+    case 4: return launch_one<CIN, COUT_T, true, 4>(m, feats, wp, bias, out, cout, stream);
+    default: return launch_one<CIN, COUT_T, true, 16>(m, feats, wp, bias, out, cout, stream);
+  }
 }
 
 template <int CIN>
 int dispatch_cout(const Map& m, int ksize, const _Float16* feats, const _Float16* wp,
                   const float* bias, _Float16* out, int cout, hipStream_t stream) {
-  if (cout % 128 == 0) return launch_mfma<CIN, 128, 4>(m, ksize, feats, wp, bias, out, cout, stream);
-  if (cout % 64 == 0) return launch_mfma<CIN, 64, 4>(m, ksize, feats, wp, bias, out, cout, stream);
-  if (cout % 32 == 0) return launch_mfma<CIN, 32, 2>(m, ksize, feats, wp, bias, out, cout, stream);
-  return launch_mfma<CIN, 16, 1>(m, ksize, feats, wp, bias, out, cout, stream);
+  if (cout % 128 == 0) return launch_mfma<CIN, 128>(m, ksize, feats, wp, bias, out, cout, stream);
+  if (cout % 64 == 0) return launch_mfma<CIN, 64>(m, ksize, feats, wp, bias, out, cout, stream);
+  return launch_mfma<CIN, 32>(m, ksize, feats, wp, bias, out, cout, stream);
 }
 
 }  // namespace

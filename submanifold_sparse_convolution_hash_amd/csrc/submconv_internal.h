@@ -19,6 +19,8 @@ constexpr int kCenterTap = 13;
 // Rows per output tile of the forward kernels; the map's per-tile lists are
 // built for this tile size.
 constexpr int kTileRows = 256;
+// Bins of the per-(tile, off-centre tap) 16-row group count: 0..kTileRows/16.
+constexpr int kNgHistBins = kTileRows / 16 + 1;
 
 // Processing position p -> tap: the centre first (it initialises an output
 // accumulator), then the other 26 taps in ascending order.
@@ -49,6 +51,7 @@ struct Map {
   uint16_t* tile_cnt = nullptr;
   int32_t* tile_off = nullptr;
   int2* ent = nullptr;
+  int64_t ng_hist[kNgHistBins] = {};  // (tile, off-centre tap) pairs per group count
 };
 
 // Records a thread-local message and returns `status`.

@@ -223,7 +223,7 @@ def test_golden_hand_case_on_gpu(dev):
 
 
 @gpu
-def test_bitwise_determinism_and_morton_invariance(dev):
+def test_bitwise_determinism_and_morton_order(dev):
     sc = _sc()
     wl = workloads.make("c2_64_64")
     L = wl.layers[0]
@@ -233,9 +233,16 @@ def test_bitwise_determinism_and_morton_invariance(dev):
     a = sc.forward(km0, feats, W)
     b = sc.forward(km0, feats, W)
     c = sc.forward(km1, feats, W)
+    c2 = sc.forward(km1, feats, W)
+    # run to run: bit for bit (fixed accumulation order, no atomics)
     assert torch.equal(a, b)
+    assert torch.equal(c, c2)
+    # the processing order changes only which rows share a tile, hence the
+    # fp32 summation order of some rows: same map, outputs within tolerance
     assert torch.equal(km0.export(), km1.export())
-    assert torch.equal(a, c)
+    ref = oc.submconv_rows(km0.export().cpu().numpy(), wl.feats, L.W, None)
+    _assert_close(a.float().cpu().numpy(), ref, "raster order")
+    _assert_close(c.float().cpu().numpy(), ref, "morton order")
     assert not torch.equal(km1.order().cpu(), torch.arange(wl.n, dtype=torch.int32))
 
 
