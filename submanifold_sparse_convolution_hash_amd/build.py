@@ -17,6 +17,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++20", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # keep MFMA accumulators in VGPRs: the kernels read and write them
+         # through LDS every step, which AGPRs would cost extra moves for
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", os.path.join(os.path.dirname(HERE), "include")]
 
 

@@ -74,26 +74,28 @@ __device__ __forceinline__ int2 bload_i2(__amdgpu_buffer_rsrc_t r, uint32_t off)
 // MFMA kernel
 // ---------------------------------------------------------------------------
 
+typedef float float16v __attribute__((ext_vector_type(16)));
+
 template <int CIN, int COUT_T, bool K3, int NG>
 struct Cfg {
   static constexpr int M = kTileRows;        // output rows per tile
+  static constexpr int GR = 32;              // rows per group (MFMA 32x32x16)
   static constexpr int NW = COUT_T / 32;     // waves; each owns 32 output columns
   static constexpr int NT = 64 * NW;         // threads
-  static constexpr int S = CIN / 32;         // 32-channel MFMA K steps
-  static constexpr int NB = 2;               // 16-column MFMA blocks per wave
+  static constexpr int KS = CIN / 16;        // 16-channel MFMA K steps
   static constexpr int NQ = COUT_T / 4;      // float4 chunks per accumulator row
   static constexpr int RC = CIN / 8;         // 16-byte chunks per feature row
-  static constexpr int GCH = 16 * RC;        // chunks per 16-row group
+  static constexpr int GCH = GR * RC;        // chunks per group
   static constexpr int CPT = GCH >= NT ? GCH / NT : 1;  // chunks per loading thread
   static constexpr int NLOAD = GCH >= NT ? NT : GCH;    // loading threads
-  static constexpr int NCG = M / 16;         // groups of the centre tap
-  static constexpr int R = NG > 8 ? NG : 8;  // ring size = unroll factor
-  static constexpr int LB = 4;               // chunks requested LB steps ahead
+  static constexpr int NCG = M / GR;         // groups of the centre tap
+  static constexpr int R = 2 * NG > 8 ? 2 * NG : 8;     // ring size = unroll factor
+  static constexpr int LB = 3;               // chunks requested LB steps ahead
   static constexpr int LE = 2;               // entries LE steps before that
   static_assert(CIN % 32 == 0 && CIN <= 256, "CIN");
   static_assert(COUT_T % 32 == 0 && COUT_T <= 128, "COUT_T");
   static_assert(GCH % NT == 0 || NT % GCH == 0, "chunk split");
-  static_assert(R % NG == 0 && NCG % R == 0, "schedule");
+  static_assert((R / NG) % 2 == 0 && R % 2 == 0, "schedule");
   static_assert(LB + LE < R, "ring");
 };
 
@@ -106,11 +108,11 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
     int tiles_per_xcd) {
   using C = Cfg<CIN, COUT_T, K3, NG>;
   static_assert(C::NT == 2 * COUT_T, "launch bounds");
-  constexpr int M = C::M, S = C::S, NB = C::NB, RC = C::RC, R = C::R, LB = C::LB, LE = C::LE;
-  constexpr int CPT = C::CPT;
+  constexpr int M = C::M, GR = C::GR, KS = C::KS, RC = C::RC, R = C::R, LB = C::LB, LE = C::LE;
+  constexpr int CPT = C::CPT, NCG = C::NCG;
   __shared__ float4v acc[M * C::NQ];
   __shared__ half8 bt[2][C::GCH];  // feature rows of a group, 16-byte chunks, swizzled
-  __shared__ int brow[2][16];      // row in tile of each slot of that group (-1: none)
+  __shared__ int brow[2][GR];      // row in tile of each slot of that group (-1: none)
 
   // Workgroups are dealt to the 8 XCDs round robin; give each XCD a
   // contiguous run of row tiles (and all column tiles of a row tile) so that
@@ -141,16 +143,18 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
     cnt_p = lane == 0 ? rows_here : 0;
   }
   const int off_p = excl_scan_wave(cnt_p, lane);
-  // Static schedule: step f < 16 is group f of the centre tap (position 0);
-  // step f >= 16 is group (f-16) % NG of position 1 + (f-16) / NG. Groups
+  // Static schedule: step f < NCG is group f of the centre tap (position 0);
+  // step f >= NCG is group (f-NCG) % NG of position 1 + (f-NCG) / NG. Groups
   // beyond NG of a position are handled after the main loop.
-  auto pos_of = [&](int f) { return f < C::NCG ? 0 : 1 + (f - C::NCG) / NG; };
-  auto grp_of = [&](int f) { return f < C::NCG ? f : (f - C::NCG) % NG; };
-  auto start_of = [&](int p, int j) { return __builtin_amdgcn_readlane(off_p, p < kTaps3 ? p : 0) + 16 * j; };
+  auto pos_of = [&](int f) { return f < NCG ? 0 : 1 + (f - NCG) / NG; };
+  auto grp_of = [&](int f) { return f < NCG ? f : (f - NCG) % NG; };
+  auto start_of = [&](int p, int j) {
+    return __builtin_amdgcn_readlane(off_p, p < kTaps3 ? p : 0) + GR * j;
+  };
   auto count_of = [&](int p, int j) {
     if (p >= (K3 ? kTaps3 : 1)) return 0;
-    const int c = __builtin_amdgcn_readlane(cnt_p, p) - 16 * j;
-    return c < 16 ? c : 16;
+    const int c = __builtin_amdgcn_readlane(cnt_p, p) - GR * j;
+    return c < GR ? c : GR;
   };
 
   const __amdgpu_buffer_rsrc_t rf = make_rsrc(feats, static_cast<uint32_t>(n * CIN * 2));
@@ -170,9 +174,7 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
     lcol[i] = static_cast<uint32_t>(lc * 16);
     lpos[i] = lrow[i] * RC + (lc ^ (lrow[i] & (RC - 1)));
   }
-  auto load_entries = [&](int f, int2 (&E)[CPT]) {
-    const int p = pos_of(f), j = grp_of(f);
-    const int st = start_of(p, j), cnt = count_of(p, j);
+  auto entries_at = [&](int st, int cnt, int2 (&E)[CPT]) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const bool live = loader && lrow[i] < cnt;
@@ -184,6 +186,10 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
         E[i].y = live ? st + lrow[i] : -1;
       }
     }
+  };
+  auto load_entries = [&](int f, int2 (&E)[CPT]) {
+    const int p = pos_of(f), j = grp_of(f);
+    entries_at(start_of(p, j), count_of(p, j), E);
   };
   auto load_chunks = [&](const int2 (&E)[CPT], half8 (&D)[CPT]) {
 #pragma unroll
@@ -201,60 +207,66 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
   };
 
   // ---- MFMA role: this wave owns 32 output columns ----
-  const int s = lane & 15;   // slot of the group this lane multiplies
-  const int kg = lane >> 4;  // channel quarter of this lane
+  // v_mfma_f32_32x32x16_f16 computes out^T for the group: A = weights
+  // (lane: column lane%32, channels (lane/32)*Cin/2 + 8*st + 0..7), B =
+  // gathered rows (lane: slot lane%32, same channels), D: lane holds slot
+  // lane%32 and columns 8*a + 4*(lane/32) + b in register 4*a + b.
+  const int s32 = lane & 31;
+  const int h = lane >> 5;
   const int cwb = c0 + w * 32;
   const int qw = w * 8;
-  float4v bias4[NB];
+  float4v bias4[4];
 #pragma unroll
-  for (int cb = 0; cb < NB; ++cb)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bias4[cb][i] = bias ? bias[cwb + cb * 16 + 4 * kg + i] : 0.f;
-  auto load_a = [&](int tap, half8 (&A)[NB][S]) {
-    const bool ok = tap >= 0;
+    for (int b = 0; b < 4; ++b) bias4[a][b] = bias ? bias[cwb + 8 * a + 4 * h + b] : 0.f;
+  // weights of `tap` for this wave's 32 columns (one 16-byte load per K step)
+  auto load_a = [&](int tap, half8 (&A)[KS]) {
+    const uint32_t base =
+        static_cast<uint32_t>(((tap * (cout / 32) + (cwb >> 5)) * KS) * 1024 + lane * 16);
 #pragma unroll
-    for (int cb = 0; cb < NB; ++cb) {
-      const uint32_t base =
-          static_cast<uint32_t>(((tap * (cout / 16) + (cwb >> 4) + cb) * S) * 1024 + lane * 16);
-#pragma unroll
-      for (int st = 0; st < S; ++st) A[cb][st] = bload_h8(rw, ok ? base + st * 1024 : kOob);
-    }
+    for (int st = 0; st < KS; ++st) A[st] = bload_h8(rw, base + st * 1024);
   };
-  auto multiply = [&](int slot, bool centre, const half8 (&A)[NB][S]) {
-    const int r = brow[slot][s];
-    const bool live = r >= 0;
-    float4v old[NB];
-    if (live && !centre) {
+  // LDS offsets (in chunks) of this lane's B fragments within a group tile
+  int boff[KS];
 #pragma unroll
-      for (int cb = 0; cb < NB; ++cb) {
-        const int q = qw + cb * 4 + kg;
-        old[cb] = acc[r * C::NQ + (q ^ (r & (C::NQ - 1)))];
+  for (int st = 0; st < KS; ++st) {
+    const int lc = h * (CIN / 16) + st;
+    boff[st] = s32 * RC + (lc ^ (s32 & (RC - 1)));
+  }
+  // The accumulator rows of the group are the MFMA's C operand: the old
+  // values (or the bias for the centre tap) go in, the new values come out.
+  auto multiply = [&](int slot, bool centre, const half8 (&A)[KS]) {
+    const int r = brow[slot][s32];
+    const bool live = r >= 0;
+    const int rb = (r < 0 ? 0 : r) * C::NQ;
+    const int rx = r & (C::NQ - 1);
+    float16v d;
+    if (centre) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) d[4 * a + b] = bias4[a][b];
+    } else {
+      // (lanes without a row read row 0 and discard the result)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const float4v o = acc[rb + ((qw + 2 * a + h) ^ rx)];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) d[4 * a + b] = o[b];
       }
     }
-    half8 Bf[S];
 #pragma unroll
-    for (int st = 0; st < S; ++st) {
-      const int lc = kg * (CIN / 32) + st;
-      Bf[st] = bt[slot][s * RC + (lc ^ (s & (RC - 1)))];
-    }
-    float4v d[NB];
-#pragma unroll
-    for (int cb = 0; cb < NB; ++cb) {
-      d[cb] = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int st = 0; st < S; ++st)
-        d[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[cb][st], Bf[st], d[cb], 0, 0, 0);
-    }
+    for (int st = 0; st < KS; ++st)
+      d = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[st], bt[slot][boff[st]], d, 0, 0, 0);
     if (live) {
 #pragma unroll
-      for (int cb = 0; cb < NB; ++cb) {
-        const int q = qw + cb * 4 + kg;
-        acc[r * C::NQ + (q ^ (r & (C::NQ - 1)))] = centre ? d[cb] + bias4[cb] : old[cb] + d[cb];
-      }
+      for (int a = 0; a < 4; ++a)
+        acc[rb + ((qw + 2 * a + h) ^ rx)] = float4v{d[4 * a], d[4 * a + 1], d[4 * a + 2], d[4 * a + 3]};
     }
   };
-  // LDS writes of this wave are complete, then all waves meet (no global
-  // memory fence: outstanding prefetches stay in flight across the barrier)
+  // LDS writes of this wave are complete, then all waves meet (an LDS-only
+  // fence: outstanding global prefetches stay in flight across the barrier)
   auto lds_barrier = [&]() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
@@ -264,66 +276,60 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
   // ---- software pipeline over the static schedule ----
   // Step f: write the chunks of group f+1 (requested LB-1 steps earlier) to
   // LDS, request the chunks of group f+LB and the entries of group f+LB+LE,
-  // switch weights at a tap boundary, multiply group f from LDS, barrier.
-  // Rings are indexed by f mod R and the loops are unrolled by R, so every
-  // load has a static wait count.
+  // at the first group of a tap request the weights of the next tap, multiply
+  // group f from LDS, barrier. Rings are indexed by f mod R and the loops are
+  // unrolled by R, so every load has a static wait count; weights alternate
+  // between two register sets by tap parity, also static.
   int2 E[R][CPT];
   half8 D[R][CPT];
-  half8 Acur[NB][S], Anext[NB][S];
+  half8 AW[2][KS];
 #pragma unroll
   for (int f = 0; f < LB + LE; ++f) load_entries(f, E[f]);
 #pragma unroll
   for (int f = 0; f < LB; ++f) load_chunks(E[f], D[f]);
-  load_a(K3 ? kCenterTap : 0, Acur);
-  if (K3) load_a(tap_at(1), Anext);
+  load_a(K3 ? kCenterTap : 0, AW[0]);
+  if (K3) load_a(tap_at(1), AW[1]);
   store_chunks(0, E[0], D[0]);
   lds_barrier();
 
-  auto step = [&](int f, auto ic, bool centre) {
-    constexpr int i = decltype(ic)::value;  // f mod R
-    store_chunks((i + 1) & 1, E[(i + 1) % R], D[(i + 1) % R]);
-    load_chunks(E[(i + LB) % R], D[(i + LB) % R]);
-    load_entries(f + LB + LE, E[(i + LB + LE) % R]);
-    if (!centre && (i % NG) == 0) {
-      // first group of a tap: its weights arrived during the previous tap
-#pragma unroll
-      for (int cb = 0; cb < NB; ++cb)
-#pragma unroll
-        for (int st = 0; st < S; ++st) Acur[cb][st] = Anext[cb][st];
-      const int pn = pos_of(f) + 1;
-      load_a(pn < kTaps3 ? tap_at(pn) : -1, Anext);
+  // ri: f mod R; ap: register set of the tap of step f; ts: first group of a tap
+  auto step = [&](int f, auto ric, auto apc, auto tsc, bool centre) {
+    constexpr int ri = decltype(ric)::value;
+    constexpr int ap = decltype(apc)::value;
+    constexpr bool ts = decltype(tsc)::value;
+    store_chunks((ri + 1) & 1, E[(ri + 1) % R], D[(ri + 1) % R]);
+    load_chunks(E[(ri + LB) % R], D[(ri + LB) % R]);
+    load_entries(f + LB + LE, E[(ri + LB + LE) % R]);
+    if (ts) {
+      const int pn = pos_of(f) + 1;  // past the last tap: reload it (harmless)
+      load_a(tap_at(pn < kTaps3 ? pn : kTaps3 - 1), AW[1 - ap]);
     }
-    multiply(i & 1, centre, Acur);
+    multiply(ri & 1, centre, AW[ap]);
     lds_barrier();
   };
-  for (int f = 0; f < C::NCG; f += R) {
-    [&]<int... I>(std::integer_sequence<int, I...>) {
-      (step(f + I, std::integral_constant<int, I>{}, true), ...);
-    }(std::make_integer_sequence<int, R>{});
-  }
+  static_assert(NCG == 8, "centre steps");
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    (step(I, std::integral_constant<int, I>{}, std::integral_constant<int, 0>{},
+          std::false_type{}, true), ...);
+  }(std::make_integer_sequence<int, NCG>{});
   if (K3) {
-    // the first off-centre tap starts at step NCG: make its weights current
-    for (int f = C::NCG; f < C::NCG + 26 * NG; f += R) {
+    for (int f = NCG; f < NCG + 26 * NG; f += R) {
       [&]<int... I>(std::integer_sequence<int, I...>) {
-        (step(f + I, std::integral_constant<int, I>{}, false), ...);
+        (step(f + I, std::integral_constant<int, (NCG + I) % R>{},
+              std::integral_constant<int, (1 + I / NG) % 2>{},
+              std::integral_constant<bool, I % NG == 0>{}, false), ...);
       }(std::make_integer_sequence<int, R>{});
     }
     // groups beyond NG of a tap: one at a time, without pipelining
     for (int p = 1; p < kTaps3; ++p) {
-      const int ngp = (__builtin_amdgcn_readlane(cnt_p, p) + 15) >> 4;
+      const int ngp = (__builtin_amdgcn_readlane(cnt_p, p) + GR - 1) / GR;
       if (ngp <= NG) continue;
-      half8 A[NB][S];
+      half8 A[KS];
       load_a(tap_at(p), A);
       for (int j = NG; j < ngp; ++j) {
         int2 e1[CPT];
         half8 d1[CPT];
-        const int st = start_of(p, j), cnt = count_of(p, j);
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-          const bool live = loader && lrow[i] < cnt;
-          e1[i] = bload_i2(re, live ? static_cast<uint32_t>(st + lrow[i]) * 8u : kOob);
-          if (!live) e1[i].y = -1;
-        }
+        entries_at(start_of(p, j), count_of(p, j), e1);
         load_chunks(e1, d1);
         store_chunks(0, e1, d1);
         lds_barrier();
@@ -342,17 +348,17 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
     const int q0 = 2 * c8, q1 = 2 * c8 + 1;
     const float4v a = acc[r * C::NQ + (q0 ^ (r & (C::NQ - 1)))];
     const float4v b = acc[r * C::NQ + (q1 ^ (r & (C::NQ - 1)))];
-    half8 h;
-    h[0] = static_cast<_Float16>(a[0]);
-    h[1] = static_cast<_Float16>(a[1]);
-    h[2] = static_cast<_Float16>(a[2]);
-    h[3] = static_cast<_Float16>(a[3]);
-    h[4] = static_cast<_Float16>(b[0]);
-    h[5] = static_cast<_Float16>(b[1]);
-    h[6] = static_cast<_Float16>(b[2]);
-    h[7] = static_cast<_Float16>(b[3]);
+    half8 hv;
+    hv[0] = static_cast<_Float16>(a[0]);
+    hv[1] = static_cast<_Float16>(a[1]);
+    hv[2] = static_cast<_Float16>(a[2]);
+    hv[3] = static_cast<_Float16>(a[3]);
+    hv[4] = static_cast<_Float16>(b[0]);
+    hv[5] = static_cast<_Float16>(b[1]);
+    hv[6] = static_cast<_Float16>(b[2]);
+    hv[7] = static_cast<_Float16>(b[3]);
     const int64_t orow = (K3 && order) ? order[t0 + r] : t0 + r;
-    *reinterpret_cast<half8*>(out + orow * cout + c0 + 8 * c8) = h;
+    *reinterpret_cast<half8*>(out + orow * cout + c0 + 8 * c8) = hv;
   }
 }
 
@@ -401,25 +407,26 @@ __global__ __launch_bounds__(256) void k_fwd_valu(
 // weight preparation
 // ---------------------------------------------------------------------------
 
-// MFMA fragment order: for tap k, 16-column block cb, K step st and lane l,
-// 8 consecutive fp16 values W[k][ci][co] with co = 16*cb + (l % 16) and
-// ci = (l / 16) * (Cin / 4) + 8*st + j, j = 0..7: one contiguous 1 KiB run per
+// MFMA fragment order (v_mfma_f32_32x32x16_f16, weights as the A operand):
+// for tap k, 32-column block cb, 16-channel K step st and lane l, 8
+// consecutive fp16 values W[k][ci][co] with co = 32*cb + (l % 32) and
+// ci = (l / 32) * (Cin / 2) + 8*st + j, j = 0..7: one contiguous 1 KiB run per
 // (k, cb, st), loaded by a wave with one 16-byte load per lane.
 __global__ void k_prepare_mfma(const _Float16* __restrict__ W, int K, int cin, int cout,
                                _Float16* __restrict__ wp) {
   const int64_t total = static_cast<int64_t>(K) * cin * cout;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= total) return;
-  const int S = cin / 32;
+  const int KS = cin / 16;
   const int j = static_cast<int>(idx & 7);
   const int l = static_cast<int>((idx >> 3) & 63);
   int64_t rest = idx >> 9;
-  const int st = static_cast<int>(rest % S);
-  rest /= S;
-  const int cb = static_cast<int>(rest % (cout / 16));
-  const int k = static_cast<int>(rest / (cout / 16));
-  const int co = 16 * cb + (l & 15);
-  const int ci = (l >> 4) * (cin / 4) + 8 * st + j;
+  const int st = static_cast<int>(rest % KS);
+  rest /= KS;
+  const int cb = static_cast<int>(rest % (cout / 32));
+  const int k = static_cast<int>(rest / (cout / 32));
+  const int co = 32 * cb + (l & 31);
+  const int ci = (l >> 5) * (cin / 2) + 8 * st + j;
   wp[idx] = W[(static_cast<int64_t>(k) * cin + ci) * cout + co];
 }
 
@@ -449,17 +456,20 @@ int check_shape(int32_t ksize, int32_t cin, int32_t cout) {
   return SUBMCONV_OK;
 }
 
-// Groups per off-centre tap in the static schedule: the NG that minimises
-// padded steps plus (about three times costlier) overflow groups, from the
-// map's histogram of groups per (tile, off-centre tap).
+// 32-row groups per off-centre tap in the static schedule: the NG that
+// minimises padded steps plus (about three times costlier) overflow groups,
+// from the map's histogram of 16-row groups per (tile, off-centre tap).
 int choose_ng(const Map& m) {
-  const int cands[3] = {2, 4, 16};
-  int best = 16;
+  const int cands[4] = {1, 2, 4, 8};
+  int best = 8;
   double best_cost = 1e300;
   for (int ng : cands) {
     double over = 0;
-    for (int b = ng + 1; b < kNgHistBins; ++b) over += static_cast<double>(b - ng) * m.ng_hist[b];
-    const double cost = static_cast<double>(m.n_tiles) * (16 + 26 * ng) + 3.0 * over;
+    for (int b = 0; b < kNgHistBins; ++b) {
+      const int ng32 = (b + 1) / 2;
+      if (ng32 > ng) over += static_cast<double>(ng32 - ng) * m.ng_hist[b];
+    }
+    const double cost = static_cast<double>(m.n_tiles) * (8 + 26 * ng) + 3.0 * over;
     if (cost < best_cost) {
       best_cost = cost;
       best = ng;
@@ -489,18 +499,23 @@ int launch_one(const Map& m, const _Float16* feats, const _Float16* wp, const fl
 template <int CIN, int COUT_T>
 int launch_mfma(const Map& m, int ksize, const _Float16* feats, const _Float16* wp,
                 const float* bias, _Float16* out, int cout, hipStream_t stream) {
-  if (ksize == 1) return launch_one<CIN, COUT_T, false, 2>(m, feats, wp, bias, out, cout, stream);
+  if (ksize == 1) return launch_one<CIN, COUT_T, false, 1>(m, feats, wp, bias, out, cout, stream);
   switch (choose_ng(m)) {
+    case 1: return launch_one<CIN, COUT_T, true, 1>(m, feats, wp, bias, out, cout, stream);
     case 2: return launch_one<CIN, COUT_T, true, 2>(m, feats, wp, bias, out, cout, stream);
     case 4: return launch_one<CIN, COUT_T, true, 4>(m, feats, wp, bias, out, cout, stream);
-    default: return launch_one<CIN, COUT_T, true, 16>(m, feats, wp, bias, out, cout, stream);
+    default: return launch_one<CIN, COUT_T, true, 8>(m, feats, wp, bias, out, cout, stream);
   }
 }
 
 template <int CIN>
 int dispatch_cout(const Map& m, int ksize, const _Float16* feats, const _Float16* wp,
                   const float* bias, _Float16* out, int cout, hipStream_t stream) {
-  if (cout % 128 == 0) return launch_mfma<CIN, 128>(m, ksize, feats, wp, bias, out, cout, stream);
+  // the LDS holds a 256 x COUT_T fp32 accumulator plus two 32-row groups of
+  // Cin channels: 128 columns up to Cin = 128, 64 columns for Cin = 256
+  constexpr int kMaxCT = CIN <= 128 ? 128 : 64;
+  if constexpr (kMaxCT >= 128)
+    if (cout % 128 == 0) return launch_mfma<CIN, 128>(m, ksize, feats, wp, bias, out, cout, stream);
   if (cout % 64 == 0) return launch_mfma<CIN, 64>(m, ksize, feats, wp, bias, out, cout, stream);
   return launch_mfma<CIN, 32>(m, ksize, feats, wp, bias, out, cout, stream);
 }
