@@ -76,7 +76,7 @@ __device__ __forceinline__ int2 bload_i2(__amdgpu_buffer_rsrc_t r, uint32_t off)
 
 typedef float float16v __attribute__((ext_vector_type(16)));
 
-template <int CIN, int COUT_T, bool K3, int NG>
+template <int CIN, int COUT_T, bool K3, int NG, int NS>
 struct Cfg {
   static constexpr int M = kTileRows;        // output rows per tile
   static constexpr int GR = 32;              // rows per group (MFMA 32x32x16)
@@ -89,30 +89,37 @@ struct Cfg {
   static constexpr int CPT = GCH >= NT ? GCH / NT : 1;  // chunks per loading thread
   static constexpr int NLOAD = GCH >= NT ? NT : GCH;    // loading threads
   static constexpr int NCG = M / GR;         // groups of the centre tap
-  static constexpr int R = 2 * NG > 8 ? 2 * NG : 8;     // ring size = unroll factor
-  static constexpr int LB = 3;               // chunks requested LB steps ahead
+  static constexpr int R = 2 * NG > 8 ? 2 * NG : 8;     // unroll factor
+  // NS group tiles in LDS. With 4, a group's rows are stored two steps
+  // before it is multiplied and read into registers one step before; with
+  // 2, stored one step before and read in its own step.
+  static constexpr int SD = NS == 4 ? 2 : 1;
+  static constexpr int LB = SD + 2;          // chunks requested LB steps ahead
   static constexpr int LE = 2;               // entries LE steps before that
+  static constexpr int LR = 3;               // rows of a group requested LR steps ahead
+  static constexpr int RQ = 4;               // ring size of entries, chunks and rows
   static_assert(CIN % 32 == 0 && CIN <= 256, "CIN");
   static_assert(COUT_T % 32 == 0 && COUT_T <= 128, "COUT_T");
+  static_assert(NS == 2 || NS == 4, "NS");
   static_assert(GCH % NT == 0 || NT % GCH == 0, "chunk split");
-  static_assert((R / NG) % 2 == 0 && R % 2 == 0, "schedule");
-  static_assert(LB + LE < R, "ring");
+  static_assert((R / NG) % 2 == 0 && R % RQ == 0, "schedule");
+  static_assert(LB - SD + 1 <= RQ && LE + 1 <= RQ && LR + 1 <= RQ, "ring");
 };
 
-template <int CIN, int COUT_T, bool K3, int NG>
+template <int CIN, int COUT_T, bool K3, int NG, int NS>
 __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
     const int2* __restrict__ ent, const int32_t* __restrict__ tile_off,
     const uint16_t* __restrict__ tile_cnt, const int32_t* __restrict__ order, int64_t n,
     const _Float16* __restrict__ feats, const _Float16* __restrict__ wp,
     const float* __restrict__ bias, _Float16* __restrict__ out, int cout, int n_tiles, int n_ct,
     int tiles_per_xcd) {
-  using C = Cfg<CIN, COUT_T, K3, NG>;
+  using C = Cfg<CIN, COUT_T, K3, NG, NS>;
   static_assert(C::NT == 2 * COUT_T, "launch bounds");
-  constexpr int M = C::M, GR = C::GR, KS = C::KS, RC = C::RC, R = C::R, LB = C::LB, LE = C::LE;
+  constexpr int M = C::M, GR = C::GR, KS = C::KS, RC = C::RC, R = C::R;
+  constexpr int SD = C::SD, LB = C::LB, LE = C::LE, LR = C::LR, RQ = C::RQ;
   constexpr int CPT = C::CPT, NCG = C::NCG;
   __shared__ float4v acc[M * C::NQ];
-  __shared__ half8 bt[2][C::GCH];  // feature rows of a group, 16-byte chunks, swizzled
-  __shared__ int brow[2][GR];      // row in tile of each slot of that group (-1: none)
+  __shared__ half8 bt[NS][C::GCH];  // feature rows of a group, 16-byte chunks, swizzled
 
   // Workgroups are dealt to the 8 XCDs round robin; give each XCD a
   // contiguous run of row tiles (and all column tiles of a row tile) so that
@@ -196,30 +203,35 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
     for (int i = 0; i < CPT; ++i)
       D[i] = bload_h8(rf, E[i].y >= 0 ? static_cast<uint32_t>(E[i].x) * (CIN * 2) + lcol[i] : kOob);
   };
-  auto store_chunks = [&](int slot, const int2 (&E)[CPT], const half8 (&D)[CPT]) {
+  auto store_chunks = [&](int slot, const half8 (&D)[CPT]) {
     if (loader) {
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        bt[slot][lpos[i]] = D[i];
-        if (lcol[i] == 0) brow[slot][lrow[i]] = E[i].y;
-      }
+      for (int i = 0; i < CPT; ++i) bt[slot][lpos[i]] = D[i];
     }
+  };
+  // row in tile of this lane's slot of the group of step f (-1: none)
+  auto row_at = [&](int st, int cnt) -> int {
+    const int sl = lane & 31;
+    if (K3) {
+      const int2 e = bload_i2(re, sl < cnt ? static_cast<uint32_t>(st + sl) * 8u : kOob);
+      return sl < cnt ? e.y : -1;
+    }
+    return sl < cnt ? st + sl : -1;
+  };
+  auto load_row = [&](int f) -> int {
+    const int p = pos_of(f), j = grp_of(f);
+    return row_at(start_of(p, j), count_of(p, j));
   };
 
   // ---- MFMA role: this wave owns 32 output columns ----
-  // v_mfma_f32_32x32x16_f16 computes out^T for the group: A = weights
-  // (lane: column lane%32, channels (lane/32)*Cin/2 + 8*st + 0..7), B =
-  // gathered rows (lane: slot lane%32, same channels), D: lane holds slot
-  // lane%32 and columns 8*a + 4*(lane/32) + b in register 4*a + b.
+  // v_mfma_f32_32x32x16_f16 computes out^T for the group: A = weights (lane:
+  // column lane%32, channels (lane/32)*Cin/2 + 8*st + 0..7), B = gathered
+  // rows (lane: slot lane%32, same channels), D: lane holds slot lane%32 and
+  // columns 8*a + 4*(lane/32) + b in register 4*a + b.
   const int s32 = lane & 31;
   const int h = lane >> 5;
   const int cwb = c0 + w * 32;
   const int qw = w * 8;
-  float4v bias4[4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) bias4[a][b] = bias ? bias[cwb + 8 * a + 4 * h + b] : 0.f;
   // weights of `tap` for this wave's 32 columns (one 16-byte load per K step)
   auto load_a = [&](int tap, half8 (&A)[KS]) {
     const uint32_t base =
@@ -234,35 +246,33 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
     const int lc = h * (CIN / 16) + st;
     boff[st] = s32 * RC + (lc ^ (s32 & (RC - 1)));
   }
-  // The accumulator rows of the group are the MFMA's C operand: the old
-  // values (or the bias for the centre tap) go in, the new values come out.
-  auto multiply = [&](int slot, bool centre, const half8 (&A)[KS]) {
-    const int r = brow[slot][s32];
+  auto read_b = [&](int slot, half8 (&B)[KS]) {
+#pragma unroll
+    for (int st = 0; st < KS; ++st) B[st] = bt[slot][boff[st]];
+  };
+  // Multiply one group and add it to the accumulator rows of its slots. The
+  // old values are read before the multiply and added after it, so the LDS
+  // latency overlaps the MFMA chain. Lanes without a row read row 0 and
+  // discard the result.
+  auto multiply = [&](int r, bool centre, const half8 (&A)[KS], const half8 (&B)[KS]) {
     const bool live = r >= 0;
     const int rb = (r < 0 ? 0 : r) * C::NQ;
     const int rx = r & (C::NQ - 1);
-    float16v d;
-    if (centre) {
+    float4v old[4];
+    if (!centre) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) d[4 * a + b] = bias4[a][b];
-    } else {
-      // (lanes without a row read row 0 and discard the result)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const float4v o = acc[rb + ((qw + 2 * a + h) ^ rx)];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) d[4 * a + b] = o[b];
-      }
+      for (int a = 0; a < 4; ++a) old[a] = acc[rb + ((qw + 2 * a + h) ^ rx)];
     }
+    float16v d = {};
 #pragma unroll
     for (int st = 0; st < KS; ++st)
-      d = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[st], bt[slot][boff[st]], d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[st], B[st], d, 0, 0, 0);
     if (live) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-        acc[rb + ((qw + 2 * a + h) ^ rx)] = float4v{d[4 * a], d[4 * a + 1], d[4 * a + 2], d[4 * a + 3]};
+      for (int a = 0; a < 4; ++a) {
+        const float4v v = {d[4 * a], d[4 * a + 1], d[4 * a + 2], d[4 * a + 3]};
+        acc[rb + ((qw + 2 * a + h) ^ rx)] = centre ? v : old[a] + v;
+      }
     }
   };
   // LDS writes of this wave are complete, then all waves meet (an LDS-only
@@ -274,40 +284,56 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
   };
 
   // ---- software pipeline over the static schedule ----
-  // Step f: write the chunks of group f+1 (requested LB-1 steps earlier) to
-  // LDS, request the chunks of group f+LB and the entries of group f+LB+LE,
-  // at the first group of a tap request the weights of the next tap, multiply
-  // group f from LDS, barrier. Rings are indexed by f mod R and the loops are
-  // unrolled by R, so every load has a static wait count; weights alternate
-  // between two register sets by tap parity, also static.
-  int2 E[R][CPT];
-  half8 D[R][CPT];
+  // Step f: (NS = 4) read the B fragments of group f+1 from LDS into
+  // registers; store the chunks of group f+SD (requested LB-SD steps
+  // earlier); request the chunks of group f+LB, the rows of group f+LR and
+  // the entries of group f+LB+LE; at the first group of a tap request the
+  // weights of the next tap; multiply group f; barrier. Register rings are
+  // indexed by f mod RQ and the loops are unrolled by R, so every load has a
+  // static wait count; weights alternate between two register sets by tap
+  // parity, B fragments by step parity.
+  int2 E[RQ][CPT];
+  half8 D[RQ][CPT];
+  int RW[RQ];
   half8 AW[2][KS];
+  half8 BF[2][KS];
 #pragma unroll
-  for (int f = 0; f < LB + LE; ++f) load_entries(f, E[f]);
+  for (int f = 0; f < LB; ++f) load_entries(f, E[f % RQ]);
 #pragma unroll
-  for (int f = 0; f < LB; ++f) load_chunks(E[f], D[f]);
+  for (int f = 0; f < LB; ++f) load_chunks(E[f % RQ], D[f % RQ]);
+#pragma unroll
+  for (int f = 0; f < LR; ++f) RW[f % RQ] = load_row(f);
+#pragma unroll
+  for (int f = LB; f < LB + LE; ++f) load_entries(f, E[f % RQ]);
   load_a(K3 ? kCenterTap : 0, AW[0]);
   if (K3) load_a(tap_at(1), AW[1]);
-  store_chunks(0, E[0], D[0]);
+#pragma unroll
+  for (int f = 0; f < SD; ++f) store_chunks(f, D[f % RQ]);
   lds_barrier();
+  if (NS == 4) read_b(0, BF[0]);
 
   // ri: f mod R; ap: register set of the tap of step f; ts: first group of a tap
   auto step = [&](int f, auto ric, auto apc, auto tsc, bool centre) {
     constexpr int ri = decltype(ric)::value;
     constexpr int ap = decltype(apc)::value;
     constexpr bool ts = decltype(tsc)::value;
-    store_chunks((ri + 1) & 1, E[(ri + 1) % R], D[(ri + 1) % R]);
-    load_chunks(E[(ri + LB) % R], D[(ri + LB) % R]);
-    load_entries(f + LB + LE, E[(ri + LB + LE) % R]);
     if (ts) {
       const int pn = pos_of(f) + 1;  // past the last tap: reload it (harmless)
       load_a(tap_at(pn < kTaps3 ? pn : kTaps3 - 1), AW[1 - ap]);
     }
-    multiply(ri & 1, centre, AW[ap]);
+    if (NS == 4)
+      read_b((ri + 1) % NS, BF[(ri + 1) & 1]);
+    else
+      read_b(ri & 1, BF[ri & 1]);
+    store_chunks((ri + SD) % NS, D[(ri + SD) % RQ]);
+    load_chunks(E[(ri + LB) % RQ], D[(ri + LB) % RQ]);
+    const int r = RW[ri % RQ];
+    RW[(ri + LR) % RQ] = load_row(f + LR);
+    load_entries(f + LB + LE, E[(ri + LB + LE) % RQ]);
+    multiply(r, centre, AW[ap], BF[ri & 1]);
     lds_barrier();
   };
-  static_assert(NCG == 8, "centre steps");
+  static_assert(NCG == 8 && NCG % RQ == 0, "centre steps");
   [&]<int... I>(std::integer_sequence<int, I...>) {
     (step(I, std::integral_constant<int, I>{}, std::integral_constant<int, 0>{},
           std::false_type{}, true), ...);
@@ -328,12 +354,15 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
       load_a(tap_at(p), A);
       for (int j = NG; j < ngp; ++j) {
         int2 e1[CPT];
-        half8 d1[CPT];
-        entries_at(start_of(p, j), count_of(p, j), e1);
+        half8 d1[CPT], b1[KS];
+        const int st = start_of(p, j), cnt = count_of(p, j);
+        entries_at(st, cnt, e1);
         load_chunks(e1, d1);
-        store_chunks(0, e1, d1);
+        const int r1 = row_at(st, cnt);
+        store_chunks(0, d1);
         lds_barrier();
-        multiply(0, false, A);
+        read_b(0, b1);
+        multiply(r1, false, A, b1);
         lds_barrier();
       }
     }
@@ -348,15 +377,21 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
     const int q0 = 2 * c8, q1 = 2 * c8 + 1;
     const float4v a = acc[r * C::NQ + (q0 ^ (r & (C::NQ - 1)))];
     const float4v b = acc[r * C::NQ + (q1 ^ (r & (C::NQ - 1)))];
+    // the bias is added here, once, in fp32 before the single rounding
+    float4v b0 = {0.f, 0.f, 0.f, 0.f}, b1 = {0.f, 0.f, 0.f, 0.f};
+    if (bias) {
+      b0 = *reinterpret_cast<const float4v*>(bias + c0 + 8 * c8);
+      b1 = *reinterpret_cast<const float4v*>(bias + c0 + 8 * c8 + 4);
+    }
     half8 hv;
-    hv[0] = static_cast<_Float16>(a[0]);
-    hv[1] = static_cast<_Float16>(a[1]);
-    hv[2] = static_cast<_Float16>(a[2]);
-    hv[3] = static_cast<_Float16>(a[3]);
-    hv[4] = static_cast<_Float16>(b[0]);
-    hv[5] = static_cast<_Float16>(b[1]);
-    hv[6] = static_cast<_Float16>(b[2]);
-    hv[7] = static_cast<_Float16>(b[3]);
+    hv[0] = static_cast<_Float16>(a[0] + b0[0]);
+    hv[1] = static_cast<_Float16>(a[1] + b0[1]);
+    hv[2] = static_cast<_Float16>(a[2] + b0[2]);
+    hv[3] = static_cast<_Float16>(a[3] + b0[3]);
+    hv[4] = static_cast<_Float16>(b[0] + b1[0]);
+    hv[5] = static_cast<_Float16>(b[1] + b1[1]);
+    hv[6] = static_cast<_Float16>(b[2] + b1[2]);
+    hv[7] = static_cast<_Float16>(b[3] + b1[3]);
     const int64_t orow = (K3 && order) ? order[t0 + r] : t0 + r;
     *reinterpret_cast<half8*>(out + orow * cout + c0 + 8 * c8) = hv;
   }
@@ -436,8 +471,8 @@ __global__ void k_copy_halves(const _Float16* __restrict__ W, int64_t total, _Fl
 }
 
 bool use_mfma(int cin, int cout) {
-  const bool cin_ok = cin == 32 || cin == 64 || cin == 128 || cin == 256;
-  return cin_ok && cout % 32 == 0;
+  if (cin == 256) return cout % 128 == 0;
+  return (cin == 32 || cin == 64 || cin == 128) && cout % 32 == 0;
 }
 
 // The MFMA kernel addresses features, weights and lists through 32-bit
@@ -481,7 +516,9 @@ int choose_ng(const Map& m) {
 template <int CIN, int COUT_T, bool K3, int NG>
 int launch_one(const Map& m, const _Float16* feats, const _Float16* wp, const float* bias,
                _Float16* out, int cout, hipStream_t stream) {
-  using Cf = Cfg<CIN, COUT_T, K3, NG>;
+  // four group tiles when the LDS has room next to the accumulator
+  constexpr int NS = 2;
+  using Cf = Cfg<CIN, COUT_T, K3, NG, NS>;
   const int64_t n_tiles64 = (m.n + kTileRows - 1) / kTileRows;
   if (n_tiles64 > (int64_t{1} << 28))
     return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "too many rows");
@@ -489,7 +526,7 @@ int launch_one(const Map& m, const _Float16* feats, const _Float16* wp, const fl
   const int n_ct = cout / COUT_T;
   const int tiles_per_xcd = (n_tiles + 7) / 8;
   const int64_t blocks = int64_t{8} * tiles_per_xcd * n_ct;
-  k_fwd_mfma<CIN, COUT_T, K3, NG><<<static_cast<unsigned>(blocks), Cf::NT, 0, stream>>>(
+  k_fwd_mfma<CIN, COUT_T, K3, NG, NS><<<static_cast<unsigned>(blocks), Cf::NT, 0, stream>>>(
       K3 ? m.ent : nullptr, K3 ? m.tile_off : nullptr, K3 ? m.tile_cnt : nullptr,
       K3 ? m.order : nullptr, m.n, feats, wp, bias, out, cout, n_tiles, n_ct, tiles_per_xcd);
   SUBMCONV_HIP_CHECK(hipGetLastError());
@@ -511,13 +548,14 @@ int launch_mfma(const Map& m, int ksize, const _Float16* feats, const _Float16* 
 template <int CIN>
 int dispatch_cout(const Map& m, int ksize, const _Float16* feats, const _Float16* wp,
                   const float* bias, _Float16* out, int cout, hipStream_t stream) {
-  // the LDS holds a 256 x COUT_T fp32 accumulator plus two 32-row groups of
-  // Cin channels: 128 columns up to Cin = 128, 64 columns for Cin = 256
-  constexpr int kMaxCT = CIN <= 128 ? 128 : 64;
-  if constexpr (kMaxCT >= 128)
-    if (cout % 128 == 0) return launch_mfma<CIN, 128>(m, ksize, feats, wp, bias, out, cout, stream);
-  if (cout % 64 == 0) return launch_mfma<CIN, 64>(m, ksize, feats, wp, bias, out, cout, stream);
-  return launch_mfma<CIN, 32>(m, ksize, feats, wp, bias, out, cout, stream);
+  // The LDS holds a 256 x COUT_T fp32 accumulator plus two 32-row groups of
+  // Cin channels (at Cin = 256 and 128 columns that is exactly 160 KiB).
+  if (cout % 128 == 0) return launch_mfma<CIN, 128>(m, ksize, feats, wp, bias, out, cout, stream);
+  if constexpr (CIN <= 128) {
+    if (cout % 64 == 0) return launch_mfma<CIN, 64>(m, ksize, feats, wp, bias, out, cout, stream);
+    return launch_mfma<CIN, 32>(m, ksize, feats, wp, bias, out, cout, stream);
+  }
+  return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "internal: no MFMA tile for Cin = %d", CIN);
 }
 
 }  // namespace
