@@ -70,13 +70,48 @@ __device__ __forceinline__ int2 bload_i2(__amdgpu_buffer_rsrc_t r, uint32_t off)
   return __builtin_bit_cast(int2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 
+// Epilogue of both MFMA kernels: the tile's fp32 accumulator rows (float4
+// chunk q of row r at r*NQ + (q ^ (r % NQ))) plus the bias, rounded once to
+// fp16 (round to nearest even) and stored at the caller's row.
+template <int COUT_T, int NT, bool K3>
+__device__ __forceinline__ void store_tile(const float4v* acc, int rows_here, int tid,
+                                           const float* __restrict__ bias, int c0,
+                                           const int32_t* __restrict__ order, int64_t t0,
+                                           _Float16* __restrict__ out, int cout) {
+  constexpr int NQ = COUT_T / 4;
+  constexpr int C8 = COUT_T / 8;
+  for (int idx = tid; idx < rows_here * C8; idx += NT) {
+    const int r = idx / C8;
+    const int c8 = idx - r * C8;
+    const int q0 = 2 * c8, q1 = 2 * c8 + 1;
+    const float4v a = acc[r * NQ + (q0 ^ (r & (NQ - 1)))];
+    const float4v b = acc[r * NQ + (q1 ^ (r & (NQ - 1)))];
+    float4v b0 = {0.f, 0.f, 0.f, 0.f}, b1 = {0.f, 0.f, 0.f, 0.f};
+    if (bias) {
+      b0 = *reinterpret_cast<const float4v*>(bias + c0 + 8 * c8);
+      b1 = *reinterpret_cast<const float4v*>(bias + c0 + 8 * c8 + 4);
+    }
+    half8 hv;
+    hv[0] = static_cast<_Float16>(a[0] + b0[0]);
+    hv[1] = static_cast<_Float16>(a[1] + b0[1]);
+    hv[2] = static_cast<_Float16>(a[2] + b0[2]);
+    hv[3] = static_cast<_Float16>(a[3] + b0[3]);
+    hv[4] = static_cast<_Float16>(b[0] + b1[0]);
+    hv[5] = static_cast<_Float16>(b[1] + b1[1]);
+    hv[6] = static_cast<_Float16>(b[2] + b1[2]);
+    hv[7] = static_cast<_Float16>(b[3] + b1[3]);
+    const int64_t orow = (K3 && order) ? order[t0 + r] : t0 + r;
+    *reinterpret_cast<half8*>(out + orow * cout + c0 + 8 * c8) = hv;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // MFMA kernel
 // ---------------------------------------------------------------------------
 
 typedef float float16v __attribute__((ext_vector_type(16)));
 
-template <int CIN, int COUT_T, bool K3, int NG, int NS>
+template <int CIN, int COUT_T, bool K3>
 struct Cfg {
   static constexpr int M = kTileRows;        // output rows per tile
   static constexpr int GR = 32;              // rows per group (MFMA 32x32x16)
@@ -89,37 +124,29 @@ struct Cfg {
   static constexpr int CPT = GCH >= NT ? GCH / NT : 1;  // chunks per loading thread
   static constexpr int NLOAD = GCH >= NT ? NT : GCH;    // loading threads
   static constexpr int NCG = M / GR;         // groups of the centre tap
-  static constexpr int R = 2 * NG > 8 ? 2 * NG : 8;     // unroll factor
-  // NS group tiles in LDS. With 4, a group's rows are stored two steps
-  // before it is multiplied and read into registers one step before; with
-  // 2, stored one step before and read in its own step.
-  static constexpr int SD = NS == 4 ? 2 : 1;
-  static constexpr int LB = SD + 2;          // chunks requested LB steps ahead
-  static constexpr int LE = 2;               // entries LE steps before that
-  static constexpr int LR = 3;               // rows of a group requested LR steps ahead
-  static constexpr int RQ = 4;               // ring size of entries, chunks and rows
+  static constexpr int RQ = 4;               // register rings; unroll of the main loop
+  static constexpr int LB = 3;               // chunks requested LB steps before the multiply
+  static constexpr int LE = 2;               // entries requested LE steps before their chunks
+  static constexpr int LR = 2;               // rows requested LR steps before the multiply
   static_assert(CIN % 32 == 0 && CIN <= 256, "CIN");
   static_assert(COUT_T % 32 == 0 && COUT_T <= 128, "COUT_T");
-  static_assert(NS == 2 || NS == 4, "NS");
   static_assert(GCH % NT == 0 || NT % GCH == 0, "chunk split");
-  static_assert((R / NG) % 2 == 0 && R % RQ == 0, "schedule");
-  static_assert(LB - SD + 1 <= RQ && LE + 1 <= RQ && LR + 1 <= RQ, "ring");
+  static_assert(NCG == 8, "centre steps");
 };
 
-template <int CIN, int COUT_T, bool K3, int NG, int NS>
+template <int CIN, int COUT_T, bool K3>
 __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
     const int2* __restrict__ ent, const int32_t* __restrict__ tile_off,
     const uint16_t* __restrict__ tile_cnt, const int32_t* __restrict__ order, int64_t n,
     const _Float16* __restrict__ feats, const _Float16* __restrict__ wp,
     const float* __restrict__ bias, _Float16* __restrict__ out, int cout, int n_tiles, int n_ct,
-    int tiles_per_xcd) {
-  using C = Cfg<CIN, COUT_T, K3, NG, NS>;
+    int tiles_per_xcd, int n_pairs) {
+  using C = Cfg<CIN, COUT_T, K3>;
   static_assert(C::NT == 2 * COUT_T, "launch bounds");
-  constexpr int M = C::M, GR = C::GR, KS = C::KS, RC = C::RC, R = C::R;
-  constexpr int SD = C::SD, LB = C::LB, LE = C::LE, LR = C::LR, RQ = C::RQ;
-  constexpr int CPT = C::CPT, NCG = C::NCG;
+  constexpr int M = C::M, GR = C::GR, KS = C::KS, RC = C::RC, RQ = C::RQ;
+  constexpr int LB = C::LB, LE = C::LE, LR = C::LR, CPT = C::CPT, NCG = C::NCG;
   __shared__ float4v acc[M * C::NQ];
-  __shared__ half8 bt[NS][C::GCH];  // feature rows of a group, 16-byte chunks, swizzled
+  __shared__ half8 bt[2][C::GCH];  // feature rows of two groups, 16-byte chunks, swizzled
 
   // Workgroups are dealt to the 8 XCDs round robin; give each XCD a
   // contiguous run of row tiles (and all column tiles of a row tile) so that
@@ -139,35 +166,53 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
   const int rows_here = static_cast<int>(n - t0 < M ? n - t0 : M);
   const int c0 = ct * COUT_T;
 
-  // ---- schedule: entries per processing position p, in lanes p < 27 ----
+  // ---- schedule ----
+  // Lane p < 27 holds the number of entries of processing position p (the
+  // centre first) and their offset in the tile's list. The step sequence is
+  // the NCG groups of the centre (all rows of the tile), then every group of
+  // 32 entries of positions 1..26 in order; gs_p is the first step of
+  // position p and F the number of steps.
   int cnt_p = 0;
-  int64_t ent0 = 0, ent1 = 0;
+  int ent0 = 0;
   if (K3) {
     if (lane < kTaps3) cnt_p = tile_cnt[static_cast<int64_t>(tile) * kTaps3 + lane];
     ent0 = tile_off[tile];
-    ent1 = tile_off[tile + 1];
   } else {
     cnt_p = lane == 0 ? rows_here : 0;
   }
   const int off_p = excl_scan_wave(cnt_p, lane);
-  // Static schedule: step f < NCG is group f of the centre tap (position 0);
-  // step f >= NCG is group (f-NCG) % NG of position 1 + (f-NCG) / NG. Groups
-  // beyond NG of a position are handled after the main loop.
-  auto pos_of = [&](int f) { return f < NCG ? 0 : 1 + (f - NCG) / NG; };
-  auto grp_of = [&](int f) { return f < NCG ? f : (f - NCG) % NG; };
-  auto start_of = [&](int p, int j) {
-    return __builtin_amdgcn_readlane(off_p, p < kTaps3 ? p : 0) + GR * j;
+  const int ng_p = (lane >= 1 && lane < kTaps3) ? (cnt_p + GR - 1) / GR : 0;
+  const int gs_p = NCG + excl_scan_wave(ng_p, lane);
+  const int F = __builtin_amdgcn_readlane(gs_p, kTaps3);
+  struct Grp {
+    int start, cnt, tap;
   };
-  auto count_of = [&](int p, int j) {
-    if (p >= (K3 ? kTaps3 : 1)) return 0;
+  // Group of step f. Positions 1..26 whose first step is at or before f form
+  // a prefix of the lanes, and the last of them is the position of step f.
+  auto group_of = [&](int f) -> Grp {
+    int p, j;
+    if (f < NCG) {
+      p = 0;
+      j = f;
+    } else {
+      const uint64_t m = __ballot(lane >= 1 && lane < kTaps3 && gs_p <= f);
+      p = __popcll(m);
+      j = f - __builtin_amdgcn_readlane(gs_p, p);
+    }
+    Grp g;
+    g.start = __builtin_amdgcn_readlane(off_p, p) + GR * j;
     const int c = __builtin_amdgcn_readlane(cnt_p, p) - GR * j;
-    return c < GR ? c : GR;
+    g.cnt = f >= F ? 0 : (c < GR ? c : GR);
+    g.tap = K3 ? tap_at(p) : 0;
+    return g;
   };
 
   const __amdgpu_buffer_rsrc_t rf = make_rsrc(feats, static_cast<uint32_t>(n * CIN * 2));
   const __amdgpu_buffer_rsrc_t rw =
       make_rsrc(wp, static_cast<uint32_t>((K3 ? kTaps3 : 1) * CIN * cout * 2));
-  const __amdgpu_buffer_rsrc_t re = make_rsrc(ent + ent0, static_cast<uint32_t>((ent1 - ent0) * 8));
+  // the whole list plus its closing {-1, -1} entry, which masked lanes load
+  const __amdgpu_buffer_rsrc_t re = make_rsrc(ent, static_cast<uint32_t>(n_pairs + 1) * 8u);
+  const uint32_t e_none = static_cast<uint32_t>(n_pairs) * 8u;
 
   // ---- loader role: this thread moves CPT 16-byte chunks of every group ----
   const bool loader = tid < C::NLOAD;
@@ -181,22 +226,18 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
     lcol[i] = static_cast<uint32_t>(lc * 16);
     lpos[i] = lrow[i] * RC + (lc ^ (lrow[i] & (RC - 1)));
   }
-  auto entries_at = [&](int st, int cnt, int2 (&E)[CPT]) {
+  auto load_entries = [&](int f, int2 (&E)[CPT]) {
+    const Grp g = group_of(f);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const bool live = loader && lrow[i] < cnt;
+      const bool live = loader && lrow[i] < g.cnt;
       if (K3) {
-        E[i] = bload_i2(re, live ? static_cast<uint32_t>(st + lrow[i]) * 8u : kOob);
-        if (!live) E[i].y = -1;
+        E[i] = bload_i2(re, live ? static_cast<uint32_t>(ent0 + g.start + lrow[i]) * 8u : e_none);
       } else {
-        E[i].x = static_cast<int>(t0) + st + lrow[i];
-        E[i].y = live ? st + lrow[i] : -1;
+        E[i].x = static_cast<int>(t0) + g.start + lrow[i];
+        E[i].y = live ? g.start + lrow[i] : -1;
       }
     }
-  };
-  auto load_entries = [&](int f, int2 (&E)[CPT]) {
-    const int p = pos_of(f), j = grp_of(f);
-    entries_at(start_of(p, j), count_of(p, j), E);
   };
   auto load_chunks = [&](const int2 (&E)[CPT], half8 (&D)[CPT]) {
 #pragma unroll
@@ -210,17 +251,11 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
     }
   };
   // row in tile of this lane's slot of the group of step f (-1: none)
-  auto row_at = [&](int st, int cnt) -> int {
-    const int sl = lane & 31;
-    if (K3) {
-      const int2 e = bload_i2(re, sl < cnt ? static_cast<uint32_t>(st + sl) * 8u : kOob);
-      return sl < cnt ? e.y : -1;
-    }
-    return sl < cnt ? st + sl : -1;
-  };
   auto load_row = [&](int f) -> int {
-    const int p = pos_of(f), j = grp_of(f);
-    return row_at(start_of(p, j), count_of(p, j));
+    const Grp g = group_of(f);
+    const int sl = lane & 31;
+    if (K3) return bload_i2(re, sl < g.cnt ? static_cast<uint32_t>(ent0 + g.start + sl) * 8u : e_none).y;
+    return sl < g.cnt ? g.start + sl : -1;
   };
 
   // ---- MFMA role: this wave owns 32 output columns ----
@@ -232,12 +267,14 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
   const int h = lane >> 5;
   const int cwb = c0 + w * 32;
   const int qw = w * 8;
-  // weights of `tap` for this wave's 32 columns (one 16-byte load per K step)
-  auto load_a = [&](int tap, half8 (&A)[KS]) {
+  // weights of the tap of step f for this wave's 32 columns (one 16-byte load
+  // per K step; a step without rows loads nothing)
+  auto load_a = [&](int f, half8 (&A)[KS]) {
+    const Grp g = group_of(f);
     const uint32_t base =
-        static_cast<uint32_t>(((tap * (cout / 32) + (cwb >> 5)) * KS) * 1024 + lane * 16);
+        static_cast<uint32_t>(((g.tap * (cout / 32) + (cwb >> 5)) * KS) * 1024 + lane * 16);
 #pragma unroll
-    for (int st = 0; st < KS; ++st) A[st] = bload_h8(rw, base + st * 1024);
+    for (int st = 0; st < KS; ++st) A[st] = bload_h8(rw, g.cnt > 0 ? base + st * 1024 : kOob);
   };
   // LDS offsets (in chunks) of this lane's B fragments within a group tile
   int boff[KS];
@@ -250,28 +287,30 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
 #pragma unroll
     for (int st = 0; st < KS; ++st) B[st] = bt[slot][boff[st]];
   };
-  // Multiply one group and add it to the accumulator rows of its slots. The
-  // old values are read before the multiply and added after it, so the LDS
-  // latency overlaps the MFMA chain. Lanes without a row read row 0 and
-  // discard the result.
-  auto multiply = [&](int r, bool centre, const half8 (&A)[KS], const half8 (&B)[KS]) {
-    const bool live = r >= 0;
-    const int rb = (r < 0 ? 0 : r) * C::NQ;
-    const int rx = r & (C::NQ - 1);
-    float4v old[4];
-    if (!centre) {
-#pragma unroll
-      for (int a = 0; a < 4; ++a) old[a] = acc[rb + ((qw + 2 * a + h) ^ rx)];
-    }
+  auto multiply = [&](const half8 (&A)[KS], const half8 (&B)[KS]) {
     float16v d = {};
 #pragma unroll
     for (int st = 0; st < KS; ++st)
       d = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[st], B[st], d, 0, 0, 0);
-    if (live) {
+    return d;
+  };
+  // Accumulator rows of this lane's slot: the centre writes them, later taps
+  // add to them. Rows are unique within a group and columns are private to
+  // the wave, and a wave's LDS operations complete in order, so one group's
+  // update sees the previous group's without a barrier.
+  auto acc_at = [&](int r, int a) { return r * C::NQ + ((qw + 2 * a + h) ^ (r & (C::NQ - 1))); };
+  auto read_old = [&](int r, float4v (&old)[4]) {
+    if (r >= 0) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) old[a] = acc[acc_at(r, a)];
+    }
+  };
+  auto write_acc = [&](int r, bool centre, const float4v (&old)[4], const float16v& d) {
+    if (r >= 0) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const float4v v = {d[4 * a], d[4 * a + 1], d[4 * a + 2], d[4 * a + 3]};
-        acc[rb + ((qw + 2 * a + h) ^ rx)] = centre ? v : old[a] + v;
+        acc[acc_at(r, a)] = centre ? v : old[a] + v;
       }
     }
   };
@@ -283,118 +322,361 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   };
 
-  // ---- software pipeline over the static schedule ----
-  // Step f: (NS = 4) read the B fragments of group f+1 from LDS into
-  // registers; store the chunks of group f+SD (requested LB-SD steps
-  // earlier); request the chunks of group f+LB, the rows of group f+LR and
-  // the entries of group f+LB+LE; at the first group of a tap request the
-  // weights of the next tap; multiply group f; barrier. Register rings are
-  // indexed by f mod RQ and the loops are unrolled by R, so every load has a
-  // static wait count; weights alternate between two register sets by tap
-  // parity, B fragments by step parity.
+  // ---- software pipeline ----
+  // Group g: entries requested in step g-LB-LE, feature chunks in step g-LB,
+  // chunks stored to LDS slot g%2 in step g-2, B fragments read in step g-1,
+  // row indices requested in step g-LR, weights in step g-1; multiplied in
+  // step g into fresh registers, and added to the accumulator in step g+1,
+  // where the LDS traffic of the update overlaps the next group's MFMAs.
+  // Rings are indexed by g mod RQ (weights, B fragments and products by g
+  // mod 2) and the loops are unrolled to make every index static. The
+  // centre's weights stay in set 1 for steps 0..NCG-1.
+  static_assert(RQ > LE && LB <= RQ && LB >= 2 && LR < RQ - 1, "ring lifetimes and prologue");
   int2 E[RQ][CPT];
   half8 D[RQ][CPT];
   int RW[RQ];
   half8 AW[2][KS];
   half8 BF[2][KS];
+  float16v DD[2];
 #pragma unroll
-  for (int f = 0; f < LB; ++f) load_entries(f, E[f % RQ]);
+  for (int g = 0; g < LB; ++g) load_entries(g, E[g % RQ]);
 #pragma unroll
-  for (int f = 0; f < LB; ++f) load_chunks(E[f % RQ], D[f % RQ]);
+  for (int g = 0; g < LB; ++g) load_chunks(E[g % RQ], D[g % RQ]);
 #pragma unroll
-  for (int f = 0; f < LR; ++f) RW[f % RQ] = load_row(f);
+  for (int g = LB; g < LB + LE; ++g) load_entries(g, E[g % RQ]);
 #pragma unroll
-  for (int f = LB; f < LB + LE; ++f) load_entries(f, E[f % RQ]);
-  load_a(K3 ? kCenterTap : 0, AW[0]);
-  if (K3) load_a(tap_at(1), AW[1]);
-#pragma unroll
-  for (int f = 0; f < SD; ++f) store_chunks(f, D[f % RQ]);
+  for (int g = 0; g < LR; ++g) RW[g % RQ] = load_row(g);
+  load_a(0, AW[1]);
+  store_chunks(0, D[0]);
+  store_chunks(1, D[1]);
   lds_barrier();
-  if (NS == 4) read_b(0, BF[0]);
+  read_b(0, BF[0]);
+  lds_barrier();
 
-  // ri: f mod R; ap: register set of the tap of step f; ts: first group of a tap
-  auto step = [&](int f, auto ric, auto apc, auto tsc, bool centre) {
-    constexpr int ri = decltype(ric)::value;
-    constexpr int ap = decltype(apc)::value;
-    constexpr bool ts = decltype(tsc)::value;
-    if (ts) {
-      const int pn = pos_of(f) + 1;  // past the last tap: reload it (harmless)
-      load_a(tap_at(pn < kTaps3 ? pn : kTaps3 - 1), AW[1 - ap]);
-    }
-    if (NS == 4)
-      read_b((ri + 1) % NS, BF[(ri + 1) & 1]);
-    else
-      read_b(ri & 1, BF[ri & 1]);
-    store_chunks((ri + SD) % NS, D[(ri + SD) % RQ]);
-    load_chunks(E[(ri + LB) % RQ], D[(ri + LB) % RQ]);
-    const int r = RW[ri % RQ];
-    RW[(ri + LR) % RQ] = load_row(f + LR);
-    load_entries(f + LB + LE, E[(ri + LB + LE) % RQ]);
-    multiply(r, centre, AW[ap], BF[ri & 1]);
+  // kind: 1 = centre step, 2 = last centre step (requests the next weights),
+  // 3 = first step after the centre, 0 = any later step
+  auto step = [&](int f, auto ic, auto kc) {
+    constexpr int i = decltype(ic)::value;  // f mod RQ
+    constexpr int kind = decltype(kc)::value;
+    constexpr int aset = (kind == 1 || kind == 2) ? 1 : (i & 1);
+    if (kind != 1) load_a(f + 1, AW[(i + 1) & 1]);
+    const int rp = RW[(i + RQ - 1) % RQ];  // rows of step f-1
+    float4v old[4];
+    if (kind == 0) read_old(rp, old);
+    read_b((i + 1) & 1, BF[(i + 1) & 1]);
+    store_chunks(i & 1, D[(i + 2) % RQ]);
+    load_chunks(E[(i + LB) % RQ], D[(i + LB) % RQ]);
+    RW[(i + LR) % RQ] = load_row(f + LR);
+    load_entries(f + LB + LE, E[(i + LB + LE) % RQ]);
+    if (kind != 0 || f < F) DD[i & 1] = multiply(AW[aset], BF[i & 1]);
+    if (f > 0) write_acc(rp, kind != 0, old, DD[(i + 1) & 1]);
     lds_barrier();
   };
-  static_assert(NCG == 8 && NCG % RQ == 0, "centre steps");
   [&]<int... I>(std::integer_sequence<int, I...>) {
-    (step(I, std::integral_constant<int, I>{}, std::integral_constant<int, 0>{},
-          std::false_type{}, true), ...);
+    (step(I, std::integral_constant<int, I % RQ>{},
+          std::integral_constant<int, I == NCG - 1 ? 2 : 1>{}), ...);
   }(std::make_integer_sequence<int, NCG>{});
+  step(NCG, std::integral_constant<int, NCG % RQ>{}, std::integral_constant<int, 3>{});
+  int fe = NCG + 1;
   if (K3) {
-    for (int f = NCG; f < NCG + 26 * NG; f += R) {
+    for (; fe < F; fe += RQ) {
       [&]<int... I>(std::integer_sequence<int, I...>) {
-        (step(f + I, std::integral_constant<int, (NCG + I) % R>{},
-              std::integral_constant<int, (1 + I / NG) % 2>{},
-              std::integral_constant<bool, I % NG == 0>{}, false), ...);
-      }(std::make_integer_sequence<int, R>{});
+        (step(fe + I, std::integral_constant<int, (NCG + 1 + I) % RQ>{},
+              std::integral_constant<int, 0>{}), ...);
+      }(std::make_integer_sequence<int, RQ>{});
     }
-    // groups beyond NG of a tap: one at a time, without pipelining
-    for (int p = 1; p < kTaps3; ++p) {
-      const int ngp = (__builtin_amdgcn_readlane(cnt_p, p) + GR - 1) / GR;
-      if (ngp <= NG) continue;
-      half8 A[KS];
-      load_a(tap_at(p), A);
-      for (int j = NG; j < ngp; ++j) {
-        int2 e1[CPT];
-        half8 d1[CPT], b1[KS];
-        const int st = start_of(p, j), cnt = count_of(p, j);
-        entries_at(st, cnt, e1);
-        load_chunks(e1, d1);
-        const int r1 = row_at(st, cnt);
-        store_chunks(0, d1);
-        lds_barrier();
-        read_b(0, b1);
-        multiply(r1, false, A, b1);
-        lds_barrier();
-      }
-    }
+  }
+  // the update of the last step (fe - 1 = NCG mod RQ)
+  {
+    constexpr int il = NCG % RQ;
+    float4v old[4];
+    const int rp = RW[il];
+    read_old(rp, old);
+    write_acc(rp, false, old, DD[il & 1]);
   }
   __syncthreads();
 
-  // ---- epilogue: fp32 -> fp16 (RNE), rows to their caller index ----
-  constexpr int C8 = COUT_T / 8;
-  for (int idx = tid; idx < rows_here * C8; idx += C::NT) {
-    const int r = idx / C8;
-    const int c8 = idx - r * C8;
-    const int q0 = 2 * c8, q1 = 2 * c8 + 1;
-    const float4v a = acc[r * C::NQ + (q0 ^ (r & (C::NQ - 1)))];
-    const float4v b = acc[r * C::NQ + (q1 ^ (r & (C::NQ - 1)))];
-    // the bias is added here, once, in fp32 before the single rounding
-    float4v b0 = {0.f, 0.f, 0.f, 0.f}, b1 = {0.f, 0.f, 0.f, 0.f};
-    if (bias) {
-      b0 = *reinterpret_cast<const float4v*>(bias + c0 + 8 * c8);
-      b1 = *reinterpret_cast<const float4v*>(bias + c0 + 8 * c8 + 4);
-    }
-    half8 hv;
-    hv[0] = static_cast<_Float16>(a[0] + b0[0]);
-    hv[1] = static_cast<_Float16>(a[1] + b0[1]);
-    hv[2] = static_cast<_Float16>(a[2] + b0[2]);
-    hv[3] = static_cast<_Float16>(a[3] + b0[3]);
-    hv[4] = static_cast<_Float16>(b[0] + b1[0]);
-    hv[5] = static_cast<_Float16>(b[1] + b1[1]);
-    hv[6] = static_cast<_Float16>(b[2] + b1[2]);
-    hv[7] = static_cast<_Float16>(b[3] + b1[3]);
-    const int64_t orow = (K3 && order) ? order[t0 + r] : t0 + r;
-    *reinterpret_cast<half8*>(out + orow * cout + c0 + 8 * c8) = hv;
+  store_tile<COUT_T, C::NT, K3>(acc, rows_here, tid, bias, c0, order, t0, out, cout);
+}
+
+// ---------------------------------------------------------------------------
+// Two-wave (ping-pong) MFMA kernel for Cin <= 128
+// ---------------------------------------------------------------------------
+//
+// Same tile, schedule, lists and accumulator as k_fwd_mfma, but each 32-column
+// block has two waves that take the groups of the tile in turn. In step f the
+// wave of parity f % 2 multiplies group f (eight MFMAs into fresh registers)
+// while its partner adds the product of group f-1 to the LDS accumulator,
+// reads the B fragments of group f+1 and requests the weights of group f+3.
+// With two waves per SIMD, one wave's MFMAs overlap the other's LDS and
+// address work, and the instruction stream of a step is split between two
+// issuers. Consecutive groups may update the same rows; their updates are in
+// consecutive steps, ordered by the step barrier. All waves share the
+// gathering of feature rows into LDS, as in k_fwd_mfma.
+
+template <int CIN, int COUT_T, bool K3>
+struct CfgPP {
+  static constexpr int M = kTileRows;
+  static constexpr int GR = 32;
+  static constexpr int NC = COUT_T / 32;     // column blocks
+  static constexpr int NW = 2 * NC;          // waves: two per column block
+  static constexpr int NT = 64 * NW;
+  static constexpr int KS = CIN / 16;
+  static constexpr int NQ = COUT_T / 4;
+  static constexpr int RC = CIN / 8;
+  static constexpr int GCH = GR * RC;
+  static constexpr int CPT = GCH >= NT ? GCH / NT : 1;
+  static constexpr int NLOAD = GCH >= NT ? NT : GCH;
+  static constexpr int NCG = M / GR;
+  static constexpr int LB = 4;               // chunks requested LB steps before the multiply
+  static constexpr int LE = 2;               // entries LE steps before their chunks
+  static_assert(CIN % 32 == 0 && CIN <= 128, "CIN");
+  static_assert(COUT_T % 32 == 0 && COUT_T <= 128, "COUT_T");
+  static_assert(GCH % NT == 0 || NT % GCH == 0, "chunk split");
+  static_assert(NCG == 8 && LB <= 4 && LE < 4, "schedule");
+};
+
+template <int CIN, int COUT_T, bool K3>
+__global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
+    const int2* __restrict__ ent, const int32_t* __restrict__ tile_off,
+    const uint16_t* __restrict__ tile_cnt, const int32_t* __restrict__ order, int64_t n,
+    const _Float16* __restrict__ feats, const _Float16* __restrict__ wp,
+    const float* __restrict__ bias, _Float16* __restrict__ out, int cout, int n_tiles, int n_ct,
+    int tiles_per_xcd, int n_pairs) {
+  using C = CfgPP<CIN, COUT_T, K3>;
+  static_assert(C::NT == 4 * COUT_T, "launch bounds");
+  constexpr int M = C::M, GR = C::GR, KS = C::KS, RC = C::RC;
+  constexpr int LB = C::LB, LE = C::LE, CPT = C::CPT, NCG = C::NCG;
+  __shared__ float4v acc[M * C::NQ];
+  __shared__ half8 bt[2][C::GCH];
+
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7;
+  const int li = bid >> 3;
+  const int tl = li / n_ct;
+  const int ct = li - tl * n_ct;
+  const int tile = xcd * tiles_per_xcd + tl;
+  if (tl >= tiles_per_xcd || tile >= n_tiles) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int par = w / C::NC;   // the parity of the groups this wave multiplies
+  const int wc = w - par * C::NC;
+  const int64_t t0 = static_cast<int64_t>(tile) * M;
+  const int rows_here = static_cast<int>(n - t0 < M ? n - t0 : M);
+  const int c0 = ct * COUT_T;
+
+  // ---- schedule (as in k_fwd_mfma) ----
+  int cnt_p = 0;
+  int ent0 = 0;
+  if (K3) {
+    if (lane < kTaps3) cnt_p = tile_cnt[static_cast<int64_t>(tile) * kTaps3 + lane];
+    ent0 = tile_off[tile];
+  } else {
+    cnt_p = lane == 0 ? rows_here : 0;
   }
+  const int off_p = excl_scan_wave(cnt_p, lane);
+  const int ng_p = (lane >= 1 && lane < kTaps3) ? (cnt_p + GR - 1) / GR : 0;
+  const int gs_p = NCG + excl_scan_wave(ng_p, lane);
+  const int F = __builtin_amdgcn_readlane(gs_p, kTaps3);
+  struct Grp {
+    int start, cnt, tap;
+  };
+  auto group_of = [&](int f) -> Grp {
+    int p, j;
+    if (f < NCG) {
+      p = 0;
+      j = f;
+    } else {
+      const uint64_t m = __ballot(lane >= 1 && lane < kTaps3 && gs_p <= f);
+      p = __popcll(m);
+      j = f - __builtin_amdgcn_readlane(gs_p, p);
+    }
+    Grp g;
+    g.start = __builtin_amdgcn_readlane(off_p, p) + GR * j;
+    const int c = __builtin_amdgcn_readlane(cnt_p, p) - GR * j;
+    g.cnt = f >= F ? 0 : (c < GR ? c : GR);
+    g.tap = K3 ? tap_at(p) : 0;
+    return g;
+  };
+
+  const __amdgpu_buffer_rsrc_t rf = make_rsrc(feats, static_cast<uint32_t>(n * CIN * 2));
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(wp, static_cast<uint32_t>((K3 ? kTaps3 : 1) * CIN * cout * 2));
+  const __amdgpu_buffer_rsrc_t re = make_rsrc(ent, static_cast<uint32_t>(n_pairs + 1) * 8u);
+  const uint32_t e_none = static_cast<uint32_t>(n_pairs) * 8u;
+
+  // ---- loader role (all waves) ----
+  const bool loader = tid < C::NLOAD;
+  int lrow[CPT], lpos[CPT];
+  uint32_t lcol[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + C::NT * i;
+    lrow[i] = c / RC;
+    const int lc = c % RC;
+    lcol[i] = static_cast<uint32_t>(lc * 16);
+    lpos[i] = lrow[i] * RC + (lc ^ (lrow[i] & (RC - 1)));
+  }
+  auto load_entries = [&](int f, int2 (&E)[CPT]) {
+    const Grp g = group_of(f);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const bool live = loader && lrow[i] < g.cnt;
+      if (K3) {
+        E[i] = bload_i2(re, live ? static_cast<uint32_t>(ent0 + g.start + lrow[i]) * 8u : e_none);
+      } else {
+        E[i].x = static_cast<int>(t0) + g.start + lrow[i];
+        E[i].y = live ? g.start + lrow[i] : -1;
+      }
+    }
+  };
+  auto load_chunks = [&](const int2 (&E)[CPT], half8 (&D)[CPT]) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      D[i] = bload_h8(rf, E[i].y >= 0 ? static_cast<uint32_t>(E[i].x) * (CIN * 2) + lcol[i] : kOob);
+  };
+  auto store_chunks = [&](int slot, const half8 (&D)[CPT]) {
+    if (loader) {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) bt[slot][lpos[i]] = D[i];
+    }
+  };
+  auto load_row = [&](int f) -> int {
+    const Grp g = group_of(f);
+    const int sl = lane & 31;
+    if (K3) return bload_i2(re, sl < g.cnt ? static_cast<uint32_t>(ent0 + g.start + sl) * 8u : e_none).y;
+    return sl < g.cnt ? g.start + sl : -1;
+  };
+
+  // ---- MFMA role (fragment layouts as in k_fwd_mfma) ----
+  const int s32 = lane & 31;
+  const int h = lane >> 5;
+  const int cwb = c0 + wc * 32;
+  const int qw = wc * 8;
+  auto load_a = [&](int f, half8 (&A)[KS]) {
+    const Grp g = group_of(f);
+    const uint32_t base =
+        static_cast<uint32_t>(((g.tap * (cout / 32) + (cwb >> 5)) * KS) * 1024 + lane * 16);
+#pragma unroll
+    for (int st = 0; st < KS; ++st) A[st] = bload_h8(rw, g.cnt > 0 ? base + st * 1024 : kOob);
+  };
+  int boff[KS];
+#pragma unroll
+  for (int st = 0; st < KS; ++st) {
+    const int lc = h * (CIN / 16) + st;
+    boff[st] = s32 * RC + (lc ^ (s32 & (RC - 1)));
+  }
+  auto read_b = [&](int slot, half8 (&B)[KS]) {
+#pragma unroll
+    for (int st = 0; st < KS; ++st) B[st] = bt[slot][boff[st]];
+  };
+  auto multiply = [&](const half8 (&A)[KS], const half8 (&B)[KS]) {
+    float16v d = {};
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+      d = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[st], B[st], d, 0, 0, 0);
+    return d;
+  };
+  auto acc_at = [&](int r, int a) { return r * C::NQ + ((qw + 2 * a + h) ^ (r & (C::NQ - 1))); };
+  auto read_old = [&](int r, float4v (&old)[4]) {
+    if (r >= 0) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) old[a] = acc[acc_at(r, a)];
+    }
+  };
+  auto write_acc = [&](int r, bool centre, const float4v (&old)[4], const float16v& d) {
+    if (r >= 0) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const float4v v = {d[4 * a], d[4 * a + 1], d[4 * a + 2], d[4 * a + 3]};
+        acc[acc_at(r, a)] = centre ? v : old[a] + v;
+      }
+    }
+  };
+  auto lds_barrier = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+
+  // ---- pipeline ----
+  // Loader: group g's entries in step g-LB-LE, chunks in step g-LB, stored
+  // to slot g%2 in step g-2. A wave multiplies the groups g of its parity:
+  // weights requested in step g-3 (set (g/2)%2), B fragments and row indices
+  // in step g-1, multiply in step g, update in step g+1.
+  // The whole pipeline is instantiated once per parity, so that every wave's
+  // roles, and with them its memory-counter waits, are static.
+  auto run = [&](auto parc) {
+    constexpr int PAR = decltype(parc)::value;
+    int2 E[4][CPT];
+    half8 D[4][CPT];
+    int RW[2];
+    half8 AW[2][KS];
+    half8 BF[KS];
+#pragma unroll
+    for (int g = 0; g < LB; ++g) load_entries(g, E[g % 4]);
+#pragma unroll
+    for (int g = 0; g < LB; ++g) load_chunks(E[g % 4], D[g % 4]);
+#pragma unroll
+    for (int g = LB; g < LB + LE; ++g) load_entries(g, E[g % 4]);
+    if (PAR == 0) {
+      load_a(0, AW[0]);
+      load_a(2, AW[1]);
+      RW[0] = load_row(0);
+    } else {
+      load_a(1, AW[0]);
+    }
+    store_chunks(0, D[0]);
+    store_chunks(1, D[1]);
+    lds_barrier();
+    if (PAR == 0) read_b(0, BF);
+    lds_barrier();
+
+    // step f; i = f mod 4
+    auto step = [&](int f, auto ic, auto cc) {
+      constexpr int i = decltype(ic)::value;
+      constexpr bool centre_step = decltype(cc)::value;
+      store_chunks(i & 1, D[(i + 2) % 4]);
+      if constexpr (PAR == (i & 1)) {
+        // multiply group f and add it to the accumulator; the old rows are
+        // requested before the MFMAs so that their latency overlaps them
+        const int r = RW[(i >> 1) & 1];
+        float4v old[4];
+        if (!centre_step) read_old(r, old);
+        if (centre_step || f < F) {
+          const float16v d = multiply(AW[(i >> 1) & 1], BF);
+          write_acc(r, centre_step, old, d);
+        }
+        load_chunks(E[(i + LB) % 4], D[(i + LB) % 4]);
+        load_entries(f + LB + LE, E[(i + LB + LE) % 4]);
+      } else {
+        // prepare this wave's next group, f+1
+        read_b((i + 1) & 1, BF);
+        load_chunks(E[(i + LB) % 4], D[(i + LB) % 4]);
+        load_entries(f + LB + LE, E[(i + LB + LE) % 4]);
+        RW[((i + 1) >> 1) & 1] = load_row(f + 1);
+        load_a(f + 3, AW[((i + 3) >> 1) & 1]);
+      }
+      lds_barrier();
+    };
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (step(I, std::integral_constant<int, I % 4>{}, std::true_type{}), ...);
+    }(std::make_integer_sequence<int, NCG>{});
+    // steps NCG..F-1
+    for (int f0 = NCG; f0 < F; f0 += 4) {
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        (step(f0 + I, std::integral_constant<int, (NCG + I) % 4>{}, std::false_type{}), ...);
+      }(std::make_integer_sequence<int, 4>{});
+    }
+  };
+  if (par == 0)
+    run(std::integral_constant<int, 0>{});
+  else
+    run(std::integral_constant<int, 1>{});
+  __syncthreads();
+  store_tile<COUT_T, C::NT, K3>(acc, rows_here, tid, bias, c0, order, t0, out, cout);
 }
 
 // ---------------------------------------------------------------------------
@@ -491,34 +773,9 @@ int check_shape(int32_t ksize, int32_t cin, int32_t cout) {
   return SUBMCONV_OK;
 }
 
-// 32-row groups per off-centre tap in the static schedule: the NG that
-// minimises padded steps plus (about three times costlier) overflow groups,
-// from the map's histogram of 16-row groups per (tile, off-centre tap).
-int choose_ng(const Map& m) {
-  const int cands[4] = {1, 2, 4, 8};
-  int best = 8;
-  double best_cost = 1e300;
-  for (int ng : cands) {
-    double over = 0;
-    for (int b = 0; b < kNgHistBins; ++b) {
-      const int ng32 = (b + 1) / 2;
-      if (ng32 > ng) over += static_cast<double>(ng32 - ng) * m.ng_hist[b];
-    }
-    const double cost = static_cast<double>(m.n_tiles) * (8 + 26 * ng) + 3.0 * over;
-    if (cost < best_cost) {
-      best_cost = cost;
-      best = ng;
-    }
-  }
-  return best;
-}
-
-template <int CIN, int COUT_T, bool K3, int NG>
+template <int CIN, int COUT_T, bool K3>
 int launch_one(const Map& m, const _Float16* feats, const _Float16* wp, const float* bias,
                _Float16* out, int cout, hipStream_t stream) {
-  // four group tiles when the LDS has room next to the accumulator
-  constexpr int NS = 2;
-  using Cf = Cfg<CIN, COUT_T, K3, NG, NS>;
   const int64_t n_tiles64 = (m.n + kTileRows - 1) / kTileRows;
   if (n_tiles64 > (int64_t{1} << 28))
     return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "too many rows");
@@ -526,9 +783,20 @@ int launch_one(const Map& m, const _Float16* feats, const _Float16* wp, const fl
   const int n_ct = cout / COUT_T;
   const int tiles_per_xcd = (n_tiles + 7) / 8;
   const int64_t blocks = int64_t{8} * tiles_per_xcd * n_ct;
-  k_fwd_mfma<CIN, COUT_T, K3, NG, NS><<<static_cast<unsigned>(blocks), Cf::NT, 0, stream>>>(
-      K3 ? m.ent : nullptr, K3 ? m.tile_off : nullptr, K3 ? m.tile_cnt : nullptr,
-      K3 ? m.order : nullptr, m.n, feats, wp, bias, out, cout, n_tiles, n_ct, tiles_per_xcd);
+  const int n_pairs = static_cast<int>(K3 ? m.active_pairs : 0);
+  if constexpr (CIN <= 128) {
+    k_fwd_pp<CIN, COUT_T, K3><<<static_cast<unsigned>(blocks), CfgPP<CIN, COUT_T, K3>::NT, 0,
+                                stream>>>(
+        K3 ? m.ent : nullptr, K3 ? m.tile_off : nullptr, K3 ? m.tile_cnt : nullptr,
+        K3 ? m.order : nullptr, m.n, feats, wp, bias, out, cout, n_tiles, n_ct, tiles_per_xcd,
+        n_pairs);
+  } else {
+    k_fwd_mfma<CIN, COUT_T, K3><<<static_cast<unsigned>(blocks), Cfg<CIN, COUT_T, K3>::NT, 0,
+                                  stream>>>(
+        K3 ? m.ent : nullptr, K3 ? m.tile_off : nullptr, K3 ? m.tile_cnt : nullptr,
+        K3 ? m.order : nullptr, m.n, feats, wp, bias, out, cout, n_tiles, n_ct, tiles_per_xcd,
+        n_pairs);
+  }
   SUBMCONV_HIP_CHECK(hipGetLastError());
   return SUBMCONV_OK;
 }
@@ -536,13 +804,8 @@ int launch_one(const Map& m, const _Float16* feats, const _Float16* wp, const fl
 template <int CIN, int COUT_T>
 int launch_mfma(const Map& m, int ksize, const _Float16* feats, const _Float16* wp,
                 const float* bias, _Float16* out, int cout, hipStream_t stream) {
-  if (ksize == 1) return launch_one<CIN, COUT_T, false, 1>(m, feats, wp, bias, out, cout, stream);
-  switch (choose_ng(m)) {
-    case 1: return launch_one<CIN, COUT_T, true, 1>(m, feats, wp, bias, out, cout, stream);
-    case 2: return launch_one<CIN, COUT_T, true, 2>(m, feats, wp, bias, out, cout, stream);
-    case 4: return launch_one<CIN, COUT_T, true, 4>(m, feats, wp, bias, out, cout, stream);
-    default: return launch_one<CIN, COUT_T, true, 8>(m, feats, wp, bias, out, cout, stream);
-  }
+  if (ksize == 1) return launch_one<CIN, COUT_T, false>(m, feats, wp, bias, out, cout, stream);
+  return launch_one<CIN, COUT_T, true>(m, feats, wp, bias, out, cout, stream);
 }
 
 template <int CIN>

@@ -163,8 +163,7 @@ __global__ void k_query(const int32_t* __restrict__ coords, const int32_t* __res
 // (wave ballots over 64-row chunks) and the tile's total.
 __global__ __launch_bounds__(kTileRows) void k_tile_count(const int32_t* __restrict__ nbr, int64_t n,
                                                           uint16_t* __restrict__ tile_cnt,
-                                                          int32_t* __restrict__ tile_tot,
-                                                          unsigned long long* __restrict__ ng_hist) {
+                                                          int32_t* __restrict__ tile_tot) {
   __shared__ int cnt[kTileRows / 64][kTaps3];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -180,8 +179,6 @@ __global__ __launch_bounds__(kTileRows) void k_tile_count(const int32_t* __restr
     int c = 0;
     for (int ww = 0; ww < kTileRows / 64; ++ww) c += cnt[ww][k];
     tile_cnt[static_cast<int64_t>(blockIdx.x) * kTaps3 + threadIdx.x] = static_cast<uint16_t>(c);
-    // histogram of 16-row groups per off-centre tap (the forward's schedule)
-    if (threadIdx.x > 0) atomicAdd(&ng_hist[(c + 15) / 16], 1ull);
   }
   if (threadIdx.x == 0) {
     int tot = 0;
@@ -367,7 +364,6 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   }
   uint32_t* err = static_cast<uint32_t*>(small.p);
   unsigned long long* pairs = reinterpret_cast<unsigned long long*>(static_cast<char*>(small.p) + 8);
-  unsigned long long* hist = reinterpret_cast<unsigned long long*>(static_cast<char*>(small.p) + 16);
 
   BUILD_CHECK(hipMemsetAsync(small.p, 0, 256, stream));
   BUILD_CHECK(hipMemsetAsync(tkeys.p, 0xff, sizeof(uint64_t) * cap, stream));
@@ -411,7 +407,7 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   BUILD_CHECK(hipMalloc(&tile_tot.p, sizeof(int32_t) * (n_tiles + 1)));
   BUILD_CHECK(hipMemsetAsync(tile_tot.p, 0, sizeof(int32_t) * (n_tiles + 1), stream));
   k_tile_count<<<static_cast<unsigned>(n_tiles), kTileRows, 0, stream>>>(
-      nbr, n, tile_cnt, static_cast<int32_t*>(tile_tot.p), hist);
+      nbr, n, tile_cnt, static_cast<int32_t*>(tile_tot.p));
   BUILD_CHECK(hipGetLastError());
   {
     size_t tmp_bytes = 0;
@@ -424,7 +420,7 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
                                         rocprim::plus<int32_t>(), stream));
   }
 
-  uint64_t host_small[2 + kNgHistBins] = {};
+  uint64_t host_small[2] = {};
   BUILD_CHECK(hipMemcpyAsync(host_small, small.p, sizeof(host_small), hipMemcpyDeviceToHost, stream));
   BUILD_CHECK(hipStreamSynchronize(stream));
   const uint32_t eflags = static_cast<uint32_t>(host_small[0]);
@@ -435,10 +431,11 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   if (eflags & kErrDuplicate)
     return fail(set_error(SUBMCONV_ERR_DUPLICATE_COORD, "a site occurs more than once"));
   m.active_pairs = static_cast<int64_t>(host_small[1]);
-  for (int b = 0; b < kNgHistBins; ++b) m.ng_hist[b] = static_cast<int64_t>(host_small[2 + b]);
   if (m.active_pairs >= INT32_MAX)
     return fail(set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "too many active pairs for int32 offsets"));
-  BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&ent), sizeof(int2) * m.active_pairs));
+  // one more entry {-1, -1} after the lists: the target of masked loads
+  BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&ent), sizeof(int2) * (m.active_pairs + 1)));
+  BUILD_CHECK(hipMemsetAsync(ent + m.active_pairs, 0xff, sizeof(int2), stream));
   k_tile_fill<<<static_cast<unsigned>(n_tiles), kTileRows, 0, stream>>>(nbr, n, tile_off, ent);
   BUILD_CHECK(hipGetLastError());
   // the forward may run on another stream: the map is complete on return

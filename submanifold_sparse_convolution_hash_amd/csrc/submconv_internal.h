@@ -19,8 +19,6 @@ constexpr int kCenterTap = 13;
 // Rows per output tile of the forward kernels; the map's per-tile lists are
 // built for this tile size.
 constexpr int kTileRows = 256;
-// Bins of the per-(tile, off-centre tap) 16-row group count: 0..kTileRows/16.
-constexpr int kNgHistBins = kTileRows / 16 + 1;
 
 // Processing position p -> tap: the centre first (it initialises an output
 // accumulator), then the other 26 taps in ascending order.
@@ -36,8 +34,9 @@ __host__ __device__ inline int tap_at(int p) {
 //  processing rows), the form the forward kernels stream:
 //  tile_cnt [n_tiles][27] uint16, entries per processing position p.
 //  tile_off [n_tiles + 1] int32, first entry of each tile.
-//  ent      [active_pairs] int2 {caller row of the neighbour, row in tile},
-//           ordered by (tile, position p, row in tile).
+//  ent      [active_pairs + 1] int2 {caller row of the neighbour, row in
+//           tile}, ordered by (tile, position p, row in tile), then one
+//           entry {-1, -1} that masked lanes load instead of selecting -1.
 struct Map {
   int device = 0;
   int64_t n = 0;
@@ -51,7 +50,6 @@ struct Map {
   uint16_t* tile_cnt = nullptr;
   int32_t* tile_off = nullptr;
   int2* ent = nullptr;
-  int64_t ng_hist[kNgHistBins] = {};  // (tile, off-centre tap) pairs per group count
 };
 
 // Records a thread-local message and returns `status`.
