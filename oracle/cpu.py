@@ -36,6 +36,13 @@ def load(build_if_missing: bool = True):
     lib.oracle_submconv_rows.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P, P, P,
                                          ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int64, P]
     lib.oracle_submconv_rows.restype = ctypes.c_int
+    lib.oracle_backward_input_rows.argtypes = [P, ctypes.c_int64, P, ctypes.c_int32, ctypes.c_int32,
+                                               P, P, ctypes.c_int32, ctypes.c_int32, P,
+                                               ctypes.c_int64, P]
+    lib.oracle_backward_input_rows.restype = ctypes.c_int
+    lib.oracle_backward_weight.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P, P, ctypes.c_int32,
+                                           ctypes.c_int32, P]
+    lib.oracle_backward_weight.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -74,6 +81,42 @@ def submconv_rows(kmap: np.ndarray, feats: np.ndarray, W: np.ndarray, bias: Opti
     out = np.empty((nrows, cout), dtype=np.float64)
     rc = lib.oracle_submconv_rows(_ptr(km), n, K, _ptr(F), _ptr(Wd), _ptr(b), cin, cout,
                                   _ptr(r), nrows, _ptr(out))
+    if rc != 0:
+        raise OracleCError(f"error {rc}")
+    return out
+
+
+def backward_input_rows(coords: np.ndarray, grid: Sequence[int], batch: int, ksize: int,
+                        grad_out: np.ndarray, W: np.ndarray,
+                        rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """fp64 input gradient for ``rows`` (all rows if None), found through the
+    sites at ``coords[j] - d_k``."""
+    lib = load()
+    c = np.ascontiguousarray(coords, dtype=np.int32)
+    g = np.ascontiguousarray(grid, dtype=np.int32)
+    G = np.ascontiguousarray(grad_out, dtype=np.float64)
+    Wd = np.ascontiguousarray(W, dtype=np.float64)
+    n = c.shape[0]
+    cin, cout = Wd.shape[1], Wd.shape[2]
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nrows = n if r is None else r.shape[0]
+    out = np.empty((nrows, cin), dtype=np.float64)
+    rc = lib.oracle_backward_input_rows(_ptr(c), n, _ptr(g), int(batch), int(ksize), _ptr(G),
+                                        _ptr(Wd), cin, cout, _ptr(r), nrows, _ptr(out))
+    if rc != 0:
+        raise OracleCError(f"error {rc}")
+    return out
+
+
+def backward_weight(kmap: np.ndarray, feats: np.ndarray, grad_out: np.ndarray) -> np.ndarray:
+    """fp64 ``[K, Cin, Cout]`` weight gradient."""
+    lib = load()
+    km = np.ascontiguousarray(kmap, dtype=np.int32)
+    F = np.ascontiguousarray(feats, dtype=np.float64)
+    G = np.ascontiguousarray(grad_out, dtype=np.float64)
+    n, K = km.shape
+    out = np.empty((K, F.shape[1], G.shape[1]), dtype=np.float64)
+    rc = lib.oracle_backward_weight(_ptr(km), n, K, _ptr(F), _ptr(G), F.shape[1], G.shape[1], _ptr(out))
     if rc != 0:
         raise OracleCError(f"error {rc}")
     return out

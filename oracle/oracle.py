@@ -144,3 +144,52 @@ def submconv_rows(kmap: np.ndarray, feats: np.ndarray, W: np.ndarray, bias: Opti
             if j != SENTINEL:
                 out[r] += F[j].astype(np.float64) @ Wd[k]
     return out
+
+
+# ---------------------------------------------------------------------------
+# Backward of the same operation (gradients of a scalar loss L with
+# dL/dout = grad_out): the adjoint of the forward sum, written as scatters.
+# The issue #1 thread ("Fixed" list) names forward, input-gradient and
+# weight-gradient kernels; the sums below are what the chain rule makes of
+# the forward definition above.
+# ---------------------------------------------------------------------------
+
+
+def submconv_backward_input(coords: np.ndarray, grad_out: np.ndarray, W: np.ndarray,
+                            grid: Sequence[int], ksize: int = 3, batch: Optional[int] = None,
+                            kmap: Optional[np.ndarray] = None) -> np.ndarray:
+    """fp64 ``[N, Cin]``: every forward term ``feats[j] @ W[k]`` added to
+    ``out[i]`` (with ``j = kmap[i,k]``) sends ``grad_out[i] @ W[k]^T`` back
+    to row ``j``."""
+    G = np.asarray(grad_out).astype(np.float64)
+    Wd = np.asarray(W).astype(np.float64)
+    if kmap is None:
+        kmap = kernel_map(coords, grid, ksize, batch)
+    n = G.shape[0]
+    dx = np.zeros((n, Wd.shape[1]), dtype=np.float64)
+    for i in range(n):
+        for k in range(Wd.shape[0]):
+            j = int(kmap[i, k])
+            if j != SENTINEL:
+                dx[j] += Wd[k] @ G[i]
+    return dx
+
+
+def submconv_backward_weight(coords: np.ndarray, feats: np.ndarray, grad_out: np.ndarray,
+                             grid: Sequence[int], ksize: int = 3, batch: Optional[int] = None,
+                             kmap: Optional[np.ndarray] = None) -> np.ndarray:
+    """fp64 ``[K, Cin, Cout]``: every forward term ``feats[j] @ W[k]`` in
+    ``out[i]`` contributes the outer product ``feats[j]^T grad_out[i]`` to
+    the gradient of ``W[k]``."""
+    F = np.asarray(feats).astype(np.float64)
+    G = np.asarray(grad_out).astype(np.float64)
+    if kmap is None:
+        kmap = kernel_map(coords, grid, ksize, batch)
+    K = kmap.shape[1]
+    dw = np.zeros((K, F.shape[1], G.shape[1]), dtype=np.float64)
+    for i in range(G.shape[0]):
+        for k in range(K):
+            j = int(kmap[i, k])
+            if j != SENTINEL:
+                dw[k] += np.outer(F[j], G[i])
+    return dw

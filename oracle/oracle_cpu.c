@@ -132,6 +132,87 @@ int oracle_submconv_rows(const int32_t* kmap, int64_t n, int32_t K, const double
     return ORACLE_OK;
 }
 
+/* Input gradient for the selected rows j, in fp64: the forward term
+ * feats[j] @ W[k] of out[i] exists exactly when coords[i] + d_k = coords[j],
+ * i.e. when a site i sits at coords[j] - d_k; it returns grad_out[i] @ W[k]^T
+ * to row j. The site at coords[j] - d_k is found by the same sort + binary
+ * search as oracle_kernel_map (not through kmap). grad_out [n][cout] and
+ * W [K][cin][cout] up-cast to fp64; out [nrows][cin]. */
+int oracle_backward_input_rows(const int32_t* coords, int64_t n, const int32_t* grid,
+                               int32_t batch, int32_t ksize, const double* grad_out,
+                               const double* W, int32_t cin, int32_t cout, const int64_t* rows,
+                               int64_t nrows, double* out) {
+    if (n < 0 || nrows < 0 || cin <= 0 || cout <= 0 || (ksize != 1 && ksize != 3))
+        return ORACLE_ERR_ARG;
+    const int K = ksize == 3 ? 27 : 1;
+    site_t* sites = (site_t*)malloc((size_t)(n > 0 ? n : 1) * sizeof(site_t));
+    if (!sites) return ORACLE_ERR_NOMEM;
+    for (int64_t i = 0; i < n; ++i) {
+        const int32_t* c = coords + 4 * i;
+        if (c[0] < 0 || c[0] >= batch || c[1] < 0 || c[1] >= grid[0] || c[2] < 0 ||
+            c[2] >= grid[1] || c[3] < 0 || c[3] >= grid[2]) {
+            free(sites);
+            return ORACLE_ERR_RANGE;
+        }
+        sites[i].b = c[0];
+        sites[i].x = c[1];
+        sites[i].y = c[2];
+        sites[i].z = c[3];
+        sites[i].row = i;
+    }
+    qsort(sites, (size_t)n, sizeof(site_t), cmp_site);
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t j = rows ? rows[r] : r;
+        double* o = out + r * (int64_t)cin;
+        for (int32_t c = 0; c < cin; ++c) o[c] = 0.0;
+        if (j < 0 || j >= n) continue;
+        const int32_t* cj = coords + 4 * j;
+        for (int32_t k = 0; k < K; ++k) {
+            const int dx = K == 27 ? k / 9 - 1 : 0, dy = K == 27 ? (k / 3) % 3 - 1 : 0,
+                      dz = K == 27 ? k % 3 - 1 : 0;
+            site_t key = {cj[0], cj[1] - dx, cj[2] - dy, cj[3] - dz, 0};
+            if (key.x < 0 || key.x >= grid[0] || key.y < 0 || key.y >= grid[1] || key.z < 0 ||
+                key.z >= grid[2])
+                continue;
+            const site_t* hit = (const site_t*)bsearch(&key, sites, (size_t)n, sizeof(site_t), cmp_site);
+            if (!hit) continue;
+            const double* g = grad_out + hit->row * (int64_t)cout;
+            const double* w = W + (int64_t)k * cin * cout;
+            for (int32_t c = 0; c < cin; ++c) {
+                const double* wr = w + (int64_t)c * cout;
+                double s = 0.0;
+                for (int32_t q = 0; q < cout; ++q) s += wr[q] * g[q];
+                o[c] += s;
+            }
+        }
+    }
+    free(sites);
+    return ORACLE_OK;
+}
+
+/* Weight gradient in fp64: dW[k][c][q] = sum over rows i with
+ * kmap[i][k] = j != -1 of feats[j][c] * grad_out[i][q]. */
+int oracle_backward_weight(const int32_t* kmap, int64_t n, int32_t K, const double* feats,
+                           const double* grad_out, int32_t cin, int32_t cout, double* dw) {
+    if (n < 0 || cin <= 0 || cout <= 0 || (K != 1 && K != 27)) return ORACLE_ERR_ARG;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int32_t k = 0; k < K; ++k) {
+        for (int32_t c = 0; c < cin; ++c) {
+            double* o = dw + ((int64_t)k * cin + c) * cout;
+            for (int32_t q = 0; q < cout; ++q) o[q] = 0.0;
+            for (int64_t i = 0; i < n; ++i) {
+                const int32_t j = kmap[i * K + k];
+                if (j < 0) continue;
+                const double f = feats[(int64_t)j * cin + c];
+                const double* g = grad_out + i * (int64_t)cout;
+                for (int32_t q = 0; q < cout; ++q) o[q] += f * g[q];
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
 /* Threads an OpenMP parallel region uses here (for reporting). */
 int oracle_num_threads(void) {
     int t = 1;
