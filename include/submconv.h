@@ -60,6 +60,9 @@ extern "C" {
 /* Flags of submconv_build_map. */
 #define SUBMCONV_FLAG_MORTON 1u /* process output rows in Morton (Z-curve) order */
 
+/* Flags of submconv_prepare_weights_ex. */
+#define SUBMCONV_PREP_INPUT_GRAD 1u /* prepare the flipped, transposed kernel of the input gradient */
+
 /* Opaque kernel-map handle: library-owned device buffers, immutable after
  * submconv_build_map returns, released by submconv_map_free. One handle may
  * serve concurrent forwards on several streams of its device. */
@@ -130,6 +133,17 @@ int submconv_prepare_weights(const uint16_t* W, int32_t ksize, int32_t cin, int3
                              uint16_t* Wp, hipStream_t stream);
 
 /*
+ * submconv_prepare_weights_ex -- submconv_prepare_weights with flags.
+ * flags 0 is submconv_prepare_weights. With SUBMCONV_PREP_INPUT_GRAD, W
+ * [K,Cin,Cout] is prepared as the kernel W_t[k] = W[K-1-k]^T ([K,Cout,Cin]),
+ * the kernel of the input gradient (see submconv_backward_input); Wp then
+ * holds submconv_prepared_weights_elems(ksize, Cout, Cin) elements (the same
+ * count). Asynchronous on `stream`.
+ */
+int submconv_prepare_weights_ex(const uint16_t* W, int32_t ksize, int32_t cin, int32_t cout,
+                                uint32_t flags, uint16_t* Wp, hipStream_t stream);
+
+/*
  * submconv_forward -- one SubMConv3d layer on the sites of `map`.
  *
  * feats  [n,Cin] fp16, device, caller row order.
@@ -147,6 +161,53 @@ int submconv_prepare_weights(const uint16_t* W, int32_t ksize, int32_t cin, int3
 int submconv_forward(submconv_map_t map, const uint16_t* feats, const uint16_t* Wp,
                      const float* bias, uint16_t* out, int32_t cin, int32_t cout, int32_t ksize,
                      hipStream_t stream);
+
+/*
+ * submconv_backward_input -- gradient of a layer's loss with respect to its
+ * input features (the issue #1 thread's "bwd-input").
+ *
+ * grad_out [n,Cout] fp16, device: dL/dout, caller row order.
+ * Wp_grad  the layer's W [K,Cin,Cout] prepared with SUBMCONV_PREP_INPUT_GRAD.
+ * grad_in  [n,Cin] fp16, device: dL/dfeats[j] = sum over (i,k) with
+ *          coords[j] = coords[i] + d_k of grad_out[i] @ W[k]^T, accumulated in
+ *          fp32 and rounded once (round to nearest even).
+ *
+ * The terms of row j are the sites i at coords[j] - d_k = coords[j] +
+ * d_(K-1-k), so this is submconv_forward on the same map with the flipped,
+ * transposed kernel (Cout -> Cin channels, no bias): same requirements,
+ * asynchronous, no allocation, bitwise reproducible.
+ */
+int submconv_backward_input(submconv_map_t map, const uint16_t* grad_out, const uint16_t* Wp_grad,
+                            uint16_t* grad_in, int32_t cin, int32_t cout, int32_t ksize,
+                            hipStream_t stream);
+
+/*
+ * submconv_backward_weight_workspace_bytes -- device workspace that
+ * submconv_backward_weight needs for this map and shape (0 is possible).
+ * Negative on a bad argument.
+ */
+int64_t submconv_backward_weight_workspace_bytes(submconv_map_t map, int32_t cin, int32_t cout,
+                                                 int32_t ksize);
+
+/*
+ * submconv_backward_weight -- gradient of a layer's loss with respect to its
+ * weights (the issue #1 thread's "bwd-weight").
+ *
+ * feats     [n,Cin] fp16, device: the layer's input, caller row order.
+ * grad_out  [n,Cout] fp16, device: dL/dout, caller row order.
+ * grad_w    [K,Cin,Cout] fp32, device, overwritten: dL/dW[k] = sum over the
+ *           rows i with a neighbour j at coords[i] + d_k of
+ *           feats[j]^T grad_out[i] (outer products), fp32 accumulation.
+ * workspace device buffer of submconv_backward_weight_workspace_bytes bytes
+ *           (may be NULL when that is 0); its content is scratch.
+ *
+ * Enqueues on `stream`, allocates nothing and does not wait. Partial sums
+ * are combined in a fixed order, so results are bitwise reproducible.
+ * Cin and Cout must be multiples of 8 and at most 1024; 16-byte aligned rows.
+ */
+int submconv_backward_weight(submconv_map_t map, const uint16_t* feats, const uint16_t* grad_out,
+                             float* grad_w, void* workspace, int32_t cin, int32_t cout,
+                             int32_t ksize, hipStream_t stream);
 
 /* Message for a status code (static string). */
 const char* submconv_status_string(int status);

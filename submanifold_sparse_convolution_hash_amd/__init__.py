@@ -23,13 +23,15 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = [
-    "SubmconvError", "KernelMap", "build_map", "prepare_weights", "forward", "SubMConv3d",
-    "library_path", "load_library", "abi_version", "FLAG_MORTON",
+    "SubmconvError", "KernelMap", "build_map", "prepare_weights", "forward", "backward_input",
+    "backward_weight", "SubMConv3dFunction", "SubMConv3d", "library_path", "load_library",
+    "abi_version", "FLAG_MORTON",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsubmconv.so")
 FLAG_MORTON = 1
+PREP_INPUT_GRAD = 1
 _lib = None
 
 
@@ -64,6 +66,10 @@ def load_library():
         "submconv_map_free": ([P], ctypes.c_int),
         "submconv_prepared_weights_elems": ([I32, I32, I32], I64),
         "submconv_prepare_weights": ([P, I32, I32, I32, P, P], ctypes.c_int),
+        "submconv_prepare_weights_ex": ([P, I32, I32, I32, U32, P, P], ctypes.c_int),
+        "submconv_backward_input": ([P, P, P, P, I32, I32, I32, P], ctypes.c_int),
+        "submconv_backward_weight_workspace_bytes": ([P, I32, I32, I32], I64),
+        "submconv_backward_weight": ([P, P, P, P, P, I32, I32, I32, P], ctypes.c_int),
         "submconv_forward": ([P, P, P, P, P, I32, I32, I32, P], ctypes.c_int),
         "submconv_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "submconv_last_error": ([], ctypes.c_char_p),
@@ -176,9 +182,11 @@ def build_map(coords: torch.Tensor, grid: Sequence[int], batch: Optional[int] = 
     return KernelMap(h, coords.device, grid, batch, flags)
 
 
-def prepare_weights(W: torch.Tensor) -> torch.Tensor:
+def prepare_weights(W: torch.Tensor, input_grad: bool = False) -> torch.Tensor:
     """Reorders weights [K,Cin,Cout] fp16 (K = 27 or 1) into the forward
-    kernel's layout (an opaque fp16 buffer of the same element count)."""
+    kernel's layout (an opaque fp16 buffer of the same element count). With
+    ``input_grad``, prepares the flipped, transposed kernel of the input
+    gradient instead (for :func:`backward_input`)."""
     _require(W, "W", torch.float16, 3)
     K, cin, cout = W.shape
     if K not in (27, 1):
@@ -190,7 +198,9 @@ def prepare_weights(W: torch.Tensor) -> torch.Tensor:
         _check(n)
     wp = torch.empty((n,), dtype=torch.float16, device=W.device)
     with torch.cuda.device(W.device):
-        _check(lib.submconv_prepare_weights(_ptr(W), ksize, cin, cout, _ptr(wp), _stream(W.device)))
+        _check(lib.submconv_prepare_weights_ex(_ptr(W), ksize, cin, cout,
+                                               PREP_INPUT_GRAD if input_grad else 0, _ptr(wp),
+                                               _stream(W.device)))
     return wp
 
 
@@ -232,6 +242,93 @@ def forward(kmap: KernelMap, feats: torch.Tensor, W: Optional[torch.Tensor] = No
                                                _ptr(out), cin, cout, int(ksize),
                                                _stream(feats.device)))
     return out
+
+
+def backward_input(kmap: KernelMap, grad_out: torch.Tensor, W: Optional[torch.Tensor] = None, *,
+                   prepared: Optional[torch.Tensor] = None, ksize: Optional[int] = None,
+                   cin: Optional[int] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Input gradient ``[N,Cin]`` fp16 of a layer with weights ``W`` for the
+    output gradient ``grad_out`` ([N,Cout] fp16). Pass ``W`` or ``prepared``
+    (``prepare_weights(W, input_grad=True)``) with ``ksize`` and ``cin``."""
+    _require(grad_out, "grad_out", torch.float16, 2)
+    if grad_out.shape[0] != kmap.num_rows:
+        raise ValueError(f"grad_out has {grad_out.shape[0]} rows, the map {kmap.num_rows}")
+    cout = grad_out.shape[1]
+    if prepared is None:
+        if W is None:
+            raise ValueError("pass W or prepared")
+        if W.shape[2] != cout:
+            raise ValueError(f"W is {tuple(W.shape)} but grad_out has Cout = {cout}")
+        ksize = 3 if W.shape[0] == 27 else 1
+        cin = W.shape[1]
+        prepared = prepare_weights(W, input_grad=True)
+    elif ksize is None or cin is None:
+        raise ValueError("with prepared weights, pass ksize and cin")
+    if out is None:
+        out = torch.empty((grad_out.shape[0], cin), dtype=torch.float16, device=grad_out.device)
+    else:
+        _require(out, "out", torch.float16, 2)
+        if tuple(out.shape) != (grad_out.shape[0], cin):
+            raise ValueError("out must be [N,Cin]")
+    with torch.cuda.device(grad_out.device):
+        _check(load_library().submconv_backward_input(kmap.handle, _ptr(grad_out), _ptr(prepared),
+                                                      _ptr(out), int(cin), cout, int(ksize),
+                                                      _stream(grad_out.device)))
+    return out
+
+
+def backward_weight(kmap: KernelMap, feats: torch.Tensor, grad_out: torch.Tensor,
+                    ksize: int = 3, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Weight gradient ``[K,Cin,Cout]`` fp32 from the layer input ``feats``
+    ([N,Cin] fp16) and the output gradient ``grad_out`` ([N,Cout] fp16)."""
+    _require(feats, "feats", torch.float16, 2)
+    _require(grad_out, "grad_out", torch.float16, 2)
+    n, cin = feats.shape
+    cout = grad_out.shape[1]
+    if n != kmap.num_rows or grad_out.shape[0] != n:
+        raise ValueError("feats and grad_out must have the map's rows")
+    K = 27 if ksize == 3 else 1
+    lib = load_library()
+    ws = int(lib.submconv_backward_weight_workspace_bytes(kmap.handle, cin, cout, int(ksize)))
+    if ws < 0:
+        _check(ws)
+    work = torch.empty((max(ws, 1),), dtype=torch.uint8, device=feats.device)
+    if out is None:
+        out = torch.empty((K, cin, cout), dtype=torch.float32, device=feats.device)
+    else:
+        _require(out, "out", torch.float32, 3)
+        if tuple(out.shape) != (K, cin, cout):
+            raise ValueError("out must be [K,Cin,Cout]")
+    with torch.cuda.device(feats.device):
+        _check(lib.submconv_backward_weight(kmap.handle, _ptr(feats), _ptr(grad_out), _ptr(out),
+                                            _ptr(work), cin, cout, int(ksize), _stream(feats.device)))
+    return out
+
+
+class SubMConv3dFunction(torch.autograd.Function):
+    """Autograd over the library's kernels: forward, input gradient (the
+    forward with the flipped, transposed kernel on the same map) and weight
+    gradient. The weight gradient is returned in fp32 cast to the weight's
+    dtype; the bias gradient is the column sum of grad_out (fp32)."""
+
+    @staticmethod
+    def forward(ctx, feats, weight, bias, kmap):
+        ctx.kmap = kmap
+        ctx.save_for_backward(feats, weight)
+        ctx.has_bias = bias is not None
+        return forward(kmap, feats, weight, bias)
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        feats, weight = ctx.saved_tensors
+        kmap = ctx.kmap
+        g = grad_out.contiguous().to(torch.float16)
+        ksize = 3 if weight.shape[0] == 27 else 1
+        gx = backward_input(kmap, g, weight) if ctx.needs_input_grad[0] else None
+        gw = (backward_weight(kmap, feats, g, ksize).to(weight.dtype)
+              if ctx.needs_input_grad[1] else None)
+        gb = g.float().sum(0) if ctx.has_bias and ctx.needs_input_grad[2] else None
+        return gx, gw, gb, None
 
 
 class SubMConv3d(torch.nn.Module):

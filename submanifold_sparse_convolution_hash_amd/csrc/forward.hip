@@ -724,12 +724,24 @@ __global__ __launch_bounds__(256) void k_fwd_valu(
 // weight preparation
 // ---------------------------------------------------------------------------
 
+// Weights of the forward being prepared, W_t[k][ci][co] for a forward with
+// cin x cout channels: W itself, or for the input gradient the flipped,
+// transposed kernel W_t[k][ci][co] = W[K-1-k][co][ci] of W [K][cout][cin]
+// (out[i] gathers feats[c_i + d_k]; its input gradient gathers grad_out at
+// c_j - d_k = c_j + d_(K-1-k) through W[k]^T, so the same forward on the same
+// map computes it).
+__device__ __forceinline__ _Float16 weight_at(const _Float16* __restrict__ W, int K, int cin,
+                                              int cout, bool grad, int k, int ci, int co) {
+  return grad ? W[(static_cast<int64_t>(K - 1 - k) * cout + co) * cin + ci]
+              : W[(static_cast<int64_t>(k) * cin + ci) * cout + co];
+}
+
 // MFMA fragment order (v_mfma_f32_32x32x16_f16, weights as the A operand):
 // for tap k, 32-column block cb, 16-channel K step st and lane l, 8
-// consecutive fp16 values W[k][ci][co] with co = 32*cb + (l % 32) and
+// consecutive fp16 values W_t[k][ci][co] with co = 32*cb + (l % 32) and
 // ci = (l / 32) * (Cin / 2) + 8*st + j, j = 0..7: one contiguous 1 KiB run per
 // (k, cb, st), loaded by a wave with one 16-byte load per lane.
-__global__ void k_prepare_mfma(const _Float16* __restrict__ W, int K, int cin, int cout,
+__global__ void k_prepare_mfma(const _Float16* __restrict__ W, int K, int cin, int cout, bool grad,
                                _Float16* __restrict__ wp) {
   const int64_t total = static_cast<int64_t>(K) * cin * cout;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -744,12 +756,19 @@ __global__ void k_prepare_mfma(const _Float16* __restrict__ W, int K, int cin, i
   const int k = static_cast<int>(rest / (cout / 32));
   const int co = 32 * cb + (l & 31);
   const int ci = (l >> 5) * (cin / 2) + 8 * st + j;
-  wp[idx] = W[(static_cast<int64_t>(k) * cin + ci) * cout + co];
+  wp[idx] = weight_at(W, K, cin, cout, grad, k, ci, co);
 }
 
-__global__ void k_copy_halves(const _Float16* __restrict__ W, int64_t total, _Float16* __restrict__ wp) {
+// Natural order W_t[k][ci][co] (the VALU kernel's layout).
+__global__ void k_prepare_plain(const _Float16* __restrict__ W, int K, int cin, int cout, bool grad,
+                                _Float16* __restrict__ wp) {
+  const int64_t total = static_cast<int64_t>(K) * cin * cout;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx < total) wp[idx] = W[idx];
+  if (idx >= total) return;
+  const int co = static_cast<int>(idx % cout);
+  const int ci = static_cast<int>((idx / cout) % cin);
+  const int k = static_cast<int>(idx / (static_cast<int64_t>(cout) * cin));
+  wp[idx] = weight_at(W, K, cin, cout, grad, k, ci, co);
 }
 
 bool use_mfma(int cin, int cout) {
@@ -832,24 +851,35 @@ extern "C" int64_t submconv_prepared_weights_elems(int32_t ksize, int32_t cin, i
   return static_cast<int64_t>(ksize == 3 ? kTaps3 : 1) * cin * cout;
 }
 
-extern "C" int submconv_prepare_weights(const uint16_t* W, int32_t ksize, int32_t cin,
-                                        int32_t cout, uint16_t* Wp, hipStream_t stream) {
+extern "C" int submconv_prepare_weights_ex(const uint16_t* W, int32_t ksize, int32_t cin,
+                                           int32_t cout, uint32_t flags, uint16_t* Wp,
+                                           hipStream_t stream) {
   clear_error();
   const int st = check_shape(ksize, cin, cout);
   if (st != SUBMCONV_OK) return st;
   if (!W || !Wp) return set_error(SUBMCONV_ERR_INVALID_ARG, "W or Wp is NULL");
+  if (flags & ~SUBMCONV_PREP_INPUT_GRAD)
+    return set_error(SUBMCONV_ERR_INVALID_ARG, "unknown preparation flags 0x%x", flags);
+  const bool grad = flags & SUBMCONV_PREP_INPUT_GRAD;
+  // channels of the forward these weights are for
+  const int cin_t = grad ? cout : cin, cout_t = grad ? cin : cout;
   const int K = ksize == 3 ? kTaps3 : 1;
   const int64_t total = static_cast<int64_t>(K) * cin * cout;
   const int B = 256;
   const unsigned grid = static_cast<unsigned>((total + B - 1) / B);
   const _Float16* w = reinterpret_cast<const _Float16*>(W);
   _Float16* p = reinterpret_cast<_Float16*>(Wp);
-  if (use_mfma(cin, cout))
-    k_prepare_mfma<<<grid, B, 0, stream>>>(w, K, cin, cout, p);
+  if (use_mfma(cin_t, cout_t))
+    k_prepare_mfma<<<grid, B, 0, stream>>>(w, K, cin_t, cout_t, grad, p);
   else
-    k_copy_halves<<<grid, B, 0, stream>>>(w, total, p);
+    k_prepare_plain<<<grid, B, 0, stream>>>(w, K, cin_t, cout_t, grad, p);
   SUBMCONV_HIP_CHECK(hipGetLastError());
   return SUBMCONV_OK;
+}
+
+extern "C" int submconv_prepare_weights(const uint16_t* W, int32_t ksize, int32_t cin,
+                                        int32_t cout, uint16_t* Wp, hipStream_t stream) {
+  return submconv_prepare_weights_ex(W, ksize, cin, cout, 0u, Wp, stream);
 }
 
 extern "C" int submconv_forward(submconv_map_t map, const uint16_t* feats_u16, const uint16_t* Wp,
@@ -885,4 +915,11 @@ extern "C" int submconv_forward(submconv_map_t map, const uint16_t* feats_u16, c
       out, cin, cout);
   SUBMCONV_HIP_CHECK(hipGetLastError());
   return SUBMCONV_OK;
+}
+
+extern "C" int submconv_backward_input(submconv_map_t map, const uint16_t* grad_out,
+                                       const uint16_t* Wp_grad, uint16_t* grad_in, int32_t cin,
+                                       int32_t cout, int32_t ksize, hipStream_t stream) {
+  // the forward with the flipped, transposed kernel, cout -> cin channels
+  return submconv_forward(map, grad_out, Wp_grad, nullptr, grad_in, cout, cin, ksize, stream);
 }
