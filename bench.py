@@ -7,12 +7,18 @@ no bias; the kernel map is built once and reused (warm cache), as in the
 
 A step is one layer: weight preparation + the fused gather-GEMM forward,
 inputs resident in HBM. Effective TFLOP/s = 2 * active_pairs * Cin * Cout /
-time. The JSON line also carries the roofline of the forward kernel (HIP
-events around back-to-back forward launches on the launch stream), the
+time. The JSON line also carries the roofline of the dominant kernel (an
+event pair around each of its launches on the launch stream, averaged), the
 kernel-map build time, and the CPU oracle (C twin, all host threads) timed on
 the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+With --op backward_input or backward_weight the same workload times the
+layer's input gradient (weight preparation + the forward with the flipped,
+transposed kernel on the same map) or weight gradient (the MFMA pair
+contraction + the fixed-order reduction of its partials), each with its own
+roofline and oracle baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--op OP]
 """
 import argparse
 import hashlib
@@ -27,44 +33,56 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, TFLOP/s
-FORWARD_SRC = os.path.join(ROOT, "submanifold_sparse_convolution_hash_amd", "csrc", "forward.hip")
+CSRC = os.path.join(ROOT, "submanifold_sparse_convolution_hash_amd", "csrc")
 
-# HBM traffic of one forward launch from rocprofv3 counter runs of this script
-# (FETCH_SIZE and WRITE_SIZE, KiB per dispatch, averaged over its launches),
-# keyed by workload and by the SHA-256 of the forward kernel source they were
-# taken on. Scale factors come from a plain 512 MiB device copy measured in
-# the same runs (--calib-copy-mib 512): its FETCH_SIZE read 262,161 KiB and
-# its WRITE_SIZE 524,288 KiB for 524,288 KiB moved each way. A changed kernel
-# source makes the entry stale and the reported traffic null.
+# HBM traffic of one launch of an op's dominant kernel from rocprofv3 counter
+# runs of this script (FETCH_SIZE and WRITE_SIZE, KiB per dispatch, averaged
+# over its launches), keyed by (workload, op) and by the SHA-256 of the kernel
+# source they were taken on. Scale factors come from a plain 512 MiB device
+# copy measured in the same runs (--calib-copy-mib 512): its FETCH_SIZE read
+# 262,161 KiB and its WRITE_SIZE 524,288 KiB for 524,288 KiB moved each way.
+# A changed kernel source makes the entry stale and the reported traffic null.
 MEASURED_TRAFFIC = {
-    "c3_128_128": {"forward_sha256": "e4b17e78cf5c6f67db8021f4e87ad6e25aba44f04f387ce714ee021d8dae89d4", "fetch_kib": 42061.33, "write_kib": 52428.75,
-                   "fetch_factor": 524288.0 / 262160.94, "write_factor": 1.0},
+    ("c3_128_128", "forward"): {
+        "src": "forward.hip",
+        "sha256": "e4b17e78cf5c6f67db8021f4e87ad6e25aba44f04f387ce714ee021d8dae89d4",
+        "fetch_kib": 42061.33, "write_kib": 52428.75,
+        "fetch_factor": 524288.0 / 262160.94, "write_factor": 1.0},
 }
 
+METRICS = {
+    "forward": "SubMConv3d ms/layer + effective TFLOP/s (128^3 grid, C=128, 10% occ)",
+    "backward_input": "SubMConv3d input-gradient ms/layer + effective TFLOP/s",
+    "backward_weight": "SubMConv3d weight-gradient ms/layer + effective TFLOP/s",
+}
+KERNELS = {"forward": "k_fwd_pp", "backward_input": "k_fwd_pp", "backward_weight": "k_bwd_weight"}
 
-def algorithmic_bytes(n, cin, cout, ksize, has_order, has_bias):
-    """Compulsory HBM bytes of one forward launch: features read once, output
-    written once, the tap-major map read once (ksize 3), the processing order,
-    the prepared weights and the bias."""
+
+def algorithmic_bytes(op, n, cin, cout, ksize, has_order, has_bias):
+    """Compulsory HBM bytes of one launch of the op: its row inputs read once,
+    its output written once, the tap-major map read once (ksize 3) with the
+    processing order, the weights (fp16 in, or the fp32 weight gradient out)
+    and the bias."""
     K = 27 if ksize == 3 else 1
-    b = n * cin * 2 + n * cout * 2 + K * cin * cout * 2
+    b = n * cin * 2 + n * cout * 2
+    b += K * cin * cout * (4 if op == "backward_weight" else 2)
     if ksize == 3:
         b += 27 * n * 4
         if has_order:
             b += n * 4
-    if has_bias:
+    if has_bias and op == "forward":
         b += cout * 4
     return b
 
 
-def measured_traffic(config, morton):
-    """HBM bytes per forward launch from the counter table, or None when no
-    entry matches this workload and the current kernel source."""
-    t = MEASURED_TRAFFIC.get(config)
+def measured_traffic(config, op, morton):
+    """HBM bytes per launch from the counter table, or None when no entry
+    matches this workload, op and the current kernel source."""
+    t = MEASURED_TRAFFIC.get((config, op))
     if t is None or morton:
         return None
-    with open(FORWARD_SRC, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != t["forward_sha256"]:
+    with open(os.path.join(CSRC, t["src"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != t["sha256"]:
             return None
     return round((t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"]) * 1024)
 
@@ -75,6 +93,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c3_128_128")
+    ap.add_argument("--op", default="forward", choices=list(METRICS))
     ap.add_argument("--morton", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -96,12 +115,15 @@ def main():
     torch.cuda.set_device(dev)
     wl = workloads.make(args.config)
     L = wl.layers[0]
+    op = args.op
     coords = torch.from_numpy(wl.coords).to(dev)
     feats = torch.from_numpy(wl.feats).to(dev)
     W = torch.from_numpy(L.W).to(dev)
     bias = None if L.bias is None else torch.from_numpy(L.bias).to(dev)
+    g_np = np.random.default_rng(12345).standard_normal((wl.n, L.cout)).astype(np.float16)
+    grad_out = torch.from_numpy(g_np).to(dev)
     torch.cuda.synchronize()
-    print(f"[bench] {args.config}: N={wl.n} {L.cin}->{L.cout} ksize={L.ksize}", file=sys.stderr, flush=True)
+    print(f"[bench] {args.config} {op}: N={wl.n} {L.cin}->{L.cout} ksize={L.ksize}", file=sys.stderr, flush=True)
 
     # kernel-map build (cold, including allocation and the one host wait)
     build_ms = []
@@ -117,11 +139,33 @@ def main():
     pairs = km.active_pairs(L.ksize)
     flops = 2.0 * pairs * L.cin * L.cout
 
-    out = torch.empty((wl.n, L.cout), dtype=torch.float16, device=dev)
-
-    def step():
+    if op == "forward":
+        out = torch.empty((wl.n, L.cout), dtype=torch.float16, device=dev)
         wp = sc.prepare_weights(W)
-        sc.forward(km, feats, bias=bias, prepared=wp, ksize=L.ksize, cout=L.cout, out=out)
+
+        def step():
+            sc.forward(km, feats, bias=bias, prepared=sc.prepare_weights(W), ksize=L.ksize,
+                       cout=L.cout, out=out)
+
+        def kernel():
+            sc.forward(km, feats, bias=bias, prepared=wp, ksize=L.ksize, cout=L.cout, out=out)
+    elif op == "backward_input":
+        out = torch.empty((wl.n, L.cin), dtype=torch.float16, device=dev)
+        wp = sc.prepare_weights(W, input_grad=True)
+
+        def step():
+            sc.backward_input(km, grad_out, prepared=sc.prepare_weights(W, input_grad=True),
+                              ksize=L.ksize, cin=L.cin, out=out)
+
+        def kernel():
+            sc.backward_input(km, grad_out, prepared=wp, ksize=L.ksize, cin=L.cin, out=out)
+    else:
+        out = torch.empty((27 if L.ksize == 3 else 1, L.cin, L.cout), dtype=torch.float32, device=dev)
+
+        def step():
+            sc.backward_weight(km, feats, grad_out, L.ksize, out=out)
+
+        kernel = step
 
     for _ in range(args.warmup):
         step()
@@ -137,23 +181,22 @@ def main():
     ms_step = e0.elapsed_time(e1) / args.steps
     print(f"[bench] step {ms_step * 1e3:.1f} us (wall {wall_ms * 1e3:.1f} us)", file=sys.stderr, flush=True)
 
-    # forward kernel alone: an event pair around every launch, on the stream
-    # the binding launches on (torch's current stream), averaged over launches
-    wp = sc.prepare_weights(W)
+    # the op's kernels alone: an event pair around every launch, on the
+    # stream the binding launches on (torch's current stream), averaged
     for _ in range(args.warmup):
-        sc.forward(km, feats, bias=bias, prepared=wp, ksize=L.ksize, cout=L.cout, out=out)
+        kernel()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     for a, b in evs:
         a.record()
-        sc.forward(km, feats, bias=bias, prepared=wp, ksize=L.ksize, cout=L.cout, out=out)
+        kernel()
         b.record()
     torch.cuda.synchronize()
-    fwd_us = sum(a.elapsed_time(b) for a, b in evs) / args.steps * 1e3
-    alg_bytes = algorithmic_bytes(wl.n, L.cin, L.cout, L.ksize, args.morton, bias is not None)
-    achieved_gbs = alg_bytes / (fwd_us * 1e-6) / 1e9
-    print(f"[bench] forward kernel {fwd_us:.1f} us, {achieved_gbs:.0f} GB/s algorithmic", file=sys.stderr, flush=True)
+    k_us = sum(a.elapsed_time(b) for a, b in evs) / args.steps * 1e3
+    alg_bytes = algorithmic_bytes(op, wl.n, L.cin, L.cout, L.ksize, args.morton, bias is not None)
+    achieved_gbs = alg_bytes / (k_us * 1e-6) / 1e9
+    print(f"[bench] {op} kernels {k_us:.1f} us, {achieved_gbs:.0f} GB/s algorithmic", file=sys.stderr, flush=True)
 
     if args.calib_copy_mib > 0:
         nb = args.calib_copy_mib * 1024 * 1024
@@ -173,18 +216,25 @@ def main():
         times = []
         for _ in range(2):
             t = time.perf_counter()
-            oc.submconv_rows(kmap, wl.feats, L.W, L.bias)
+            if op == "forward":
+                oc.submconv_rows(kmap, wl.feats, L.W, L.bias)
+            elif op == "backward_input":
+                oc.backward_input_rows(wl.coords, wl.grid, wl.batch, L.ksize, g_np, L.W)
+            else:
+                oc.backward_weight(kmap, wl.feats, g_np)
             times.append(time.perf_counter() - t)
         conv_s = min(times)
+        what = {"forward": "conv", "backward_input": "input gradient",
+                "backward_weight": "weight gradient"}[op]
         cpu = {"value": round(flops / conv_s / 1e12, 6), "unit": "TFLOP/s", "cores": oc.num_threads(),
                "kind": "oracle",
                "sample": f"full {args.config} layer, all {wl.n} rows: C oracle (fp64, sort+bsearch map, "
-                         f"naive loops, OpenMP); conv {conv_s * 1e3:.0f} ms (best of 2), "
+                         f"naive loops, OpenMP); {what} {conv_s * 1e3:.0f} ms (best of 2), "
                          f"map {map_s * 1e3:.0f} ms"}
-        print(f"[bench] cpu oracle conv {conv_s:.2f} s", file=sys.stderr, flush=True)
+        print(f"[bench] cpu oracle {what} {conv_s:.2f} s", file=sys.stderr, flush=True)
 
     rec = {
-        "metric": "SubMConv3d ms/layer + effective TFLOP/s (128^3 grid, C=128, 10% occ)",
+        "metric": METRICS[op],
         "value": round(flops / (ms_step * 1e-3) / 1e12, 4),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -198,13 +248,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.config}: SubMConv3d {L.ksize}x{L.ksize}x{L.ksize}, grid {wl.grid[0]}^3, "
                                f"batch {wl.batch}, N={wl.n}, Cin={L.cin}, Cout={L.cout}, warm kernel map",
-                   "active_pairs": pairs, "morton": bool(args.morton)},
+                   "op": op, "active_pairs": pairs, "morton": bool(args.morton)},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(args.config, args.morton),
-                     "kernel": "k_fwd_mfma", "kernel_us": round(fwd_us, 2),
+                     "traffic": measured_traffic(args.config, op, args.morton),
+                     "kernel": KERNELS[op], "kernel_us": round(k_us, 2),
                      "algorithmic_bytes": alg_bytes,
-                     "mfma_effective_frac": round(flops / (fwd_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
+                     "mfma_effective_frac": round(flops / (k_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
         "map_build_ms": round(float(np.median(build_ms)), 3),
         "cpu_baseline": cpu,
     }

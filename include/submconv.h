@@ -209,6 +209,16 @@ int submconv_backward_weight(submconv_map_t map, const uint16_t* feats, const ui
                              float* grad_w, void* workspace, int32_t cin, int32_t cout,
                              int32_t ksize, hipStream_t stream);
 
+/*
+ * submconv_backward_bias -- gradient with respect to the bias: grad_b[c] =
+ * sum over the n rows of grad_out[row][c] (fp16 in, fp32 accumulation and
+ * result), summed in a fixed order (bitwise reproducible). grad_out [n,Cout]
+ * fp16 and grad_b [Cout] fp32, device; Cout a multiple of 8 up to 1024.
+ * Asynchronous on `stream`, no allocation.
+ */
+int submconv_backward_bias(const uint16_t* grad_out, int64_t n, int32_t cout, float* grad_b,
+                           hipStream_t stream);
+
 /* Message for a status code (static string). */
 const char* submconv_status_string(int status);
 

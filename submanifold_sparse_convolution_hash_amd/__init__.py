@@ -24,7 +24,7 @@ import torch
 
 __all__ = [
     "SubmconvError", "KernelMap", "build_map", "prepare_weights", "forward", "backward_input",
-    "backward_weight", "SubMConv3dFunction", "SubMConv3d", "library_path", "load_library",
+    "backward_weight", "backward_bias", "SubMConv3dFunction", "SubMConv3d", "library_path", "load_library",
     "abi_version", "FLAG_MORTON",
 ]
 
@@ -70,6 +70,7 @@ def load_library():
         "submconv_backward_input": ([P, P, P, P, I32, I32, I32, P], ctypes.c_int),
         "submconv_backward_weight_workspace_bytes": ([P, I32, I32, I32], I64),
         "submconv_backward_weight": ([P, P, P, P, P, I32, I32, I32, P], ctypes.c_int),
+        "submconv_backward_bias": ([P, I64, I32, P, P], ctypes.c_int),
         "submconv_forward": ([P, P, P, P, P, I32, I32, I32, P], ctypes.c_int),
         "submconv_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "submconv_last_error": ([], ctypes.c_char_p),
@@ -305,11 +306,22 @@ def backward_weight(kmap: KernelMap, feats: torch.Tensor, grad_out: torch.Tensor
     return out
 
 
+def backward_bias(grad_out: torch.Tensor) -> torch.Tensor:
+    """Bias gradient ``[Cout]`` fp32: the column sums of ``grad_out`` ([N,Cout] fp16)."""
+    _require(grad_out, "grad_out", torch.float16, 2)
+    out = torch.empty((grad_out.shape[1],), dtype=torch.float32, device=grad_out.device)
+    with torch.cuda.device(grad_out.device):
+        _check(load_library().submconv_backward_bias(_ptr(grad_out), grad_out.shape[0],
+                                                     grad_out.shape[1], _ptr(out),
+                                                     _stream(grad_out.device)))
+    return out
+
+
 class SubMConv3dFunction(torch.autograd.Function):
     """Autograd over the library's kernels: forward, input gradient (the
     forward with the flipped, transposed kernel on the same map) and weight
-    gradient. The weight gradient is returned in fp32 cast to the weight's
-    dtype; the bias gradient is the column sum of grad_out (fp32)."""
+    gradient. The weight gradient is computed in fp32 and returned in the
+    weight's dtype; the bias gradient is the fp32 column sum of grad_out."""
 
     @staticmethod
     def forward(ctx, feats, weight, bias, kmap):
@@ -327,7 +339,7 @@ class SubMConv3dFunction(torch.autograd.Function):
         gx = backward_input(kmap, g, weight) if ctx.needs_input_grad[0] else None
         gw = (backward_weight(kmap, feats, g, ksize).to(weight.dtype)
               if ctx.needs_input_grad[1] else None)
-        gb = g.float().sum(0) if ctx.has_bias and ctx.needs_input_grad[2] else None
+        gb = backward_bias(g) if ctx.has_bias and ctx.needs_input_grad[2] else None
         return gx, gw, gb, None
 
 

@@ -209,6 +209,32 @@ __global__ void k_bwd_weight_valu(const int32_t* __restrict__ nbr, const int32_t
   for (int q = 0; q < 8; ++q) dw[(static_cast<int64_t>(k) * cin + ci) * cout + o8 * 8 + q] = s[q];
 }
 
+// grad_b[c] = sum over rows of grad_out[row][c]: one workgroup per 8
+// columns, each thread a fixed stride of rows, then a fixed-order tree in LDS.
+__global__ __launch_bounds__(256) void k_bwd_bias(const _Float16* __restrict__ grad_out, int64_t n,
+                                                  int cout, float* __restrict__ grad_b) {
+  __shared__ float part[8][257];
+  const int c8 = blockIdx.x;
+  const int tid = threadIdx.x;
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int64_t r = tid; r < n; r += 256) {
+    const half8 v = *reinterpret_cast<const half8*>(grad_out + r * cout + c8 * 8);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) s[q] += static_cast<float>(v[q]);
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) part[q][tid] = s[q];
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) part[q][tid] += part[q][tid + w];
+    }
+    __syncthreads();
+  }
+  if (tid < 8) grad_b[c8 * 8 + tid] = part[tid][0];
+}
+
 bool use_mfma_w(int cin, int cout) {
   return cin % 32 == 0 && cout % 32 == 0 && cin <= 256 && cout <= 256;
 }
@@ -311,6 +337,20 @@ extern "C" int submconv_backward_weight(submconv_map_t map, const uint16_t* feat
   const int64_t items = static_cast<int64_t>(K) * cin * (cout / 8);
   k_bwd_weight_valu<<<static_cast<unsigned>((items + 255) / 256), 256, 0, stream>>>(
       K == kTaps3 ? m.nbr : nullptr, m.order, m.n, K, f, g, cin, cout, grad_w);
+  SUBMCONV_HIP_CHECK(hipGetLastError());
+  return SUBMCONV_OK;
+}
+
+extern "C" int submconv_backward_bias(const uint16_t* grad_out, int64_t n, int32_t cout,
+                                      float* grad_b, hipStream_t stream) {
+  clear_error();
+  if (n < 0 || cout <= 0 || cout % 8 || cout > 1024)
+    return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "n = %lld, Cout = %d", (long long)n, cout);
+  if (!grad_b || (n > 0 && !grad_out)) return set_error(SUBMCONV_ERR_INVALID_ARG, "NULL pointer");
+  if (reinterpret_cast<uintptr_t>(grad_out) & 15)
+    return set_error(SUBMCONV_ERR_INVALID_ARG, "grad_out must be 16-byte aligned");
+  k_bwd_bias<<<static_cast<unsigned>(cout / 8), 256, 0, stream>>>(
+      reinterpret_cast<const _Float16*>(grad_out), n, cout, grad_b);
   SUBMCONV_HIP_CHECK(hipGetLastError());
   return SUBMCONV_OK;
 }

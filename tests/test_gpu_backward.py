@@ -212,3 +212,16 @@ def test_autograd_function(dev):
     _assert_close(W.grad.float().cpu().numpy(), ref_w, "autograd dW", atol=1e-2, rtol=2e-3)
     _assert_close(b.grad.cpu().numpy(), g.astype(np.float64).sum(0), "autograd db", atol=1e-2, rtol=1e-4)
     km.free()
+
+
+@gpu
+@pytest.mark.parametrize("n,cout", [(0, 8), (1, 16), (1000, 64), (209715, 128)])
+def test_backward_bias(dev, n, cout):
+    sc = _sc()
+    g = np.random.default_rng(n + cout).standard_normal((n, cout)).astype(np.float16)
+    got = sc.backward_bias(_to(dev, g)).cpu().numpy()
+    ref = g.astype(np.float64).sum(0)
+    # fp32 sums of n fp16 values: bound from sqrt(n) u sum |g|
+    scale = np.abs(g.astype(np.float64)).sum(0)
+    _assert_close(got, ref, "bias grad", atol=1e-5, rtol=1e-5, extra=1e-6 * scale)
+    np.testing.assert_array_equal(got, sc.backward_bias(_to(dev, g)).cpu().numpy())
