@@ -193,3 +193,75 @@ def submconv_backward_weight(coords: np.ndarray, feats: np.ndarray, grad_out: np
             if j != SENTINEL:
                 dw[k] += np.outer(F[j], G[i])
     return dw
+
+
+# ---------------------------------------------------------------------------
+# The coordinate operations beside SubMConv3d in the same sparse stack
+# (trellis_sparse_mlx README, "What's in it" table, subdivide / downsample
+# row: x2 coordinate expansion, and x2 max-pooling -- the upstream reduce is
+# "amax" whatever its docstring says).
+# ---------------------------------------------------------------------------
+
+# child offsets of subdivide, c = 4*dx + 2*dy + dz (dx slowest)
+SUBDIVIDE_OFFSETS = tuple((dx, dy, dz) for dx in (0, 1) for dy in (0, 1) for dz in (0, 1))
+
+
+def downsample(coords: np.ndarray, feats: Optional[np.ndarray], grid: Sequence[int],
+               batch: Optional[int] = None):
+    """x2 max-pool of a sparse tensor.
+
+    Every site (b, x, y, z) belongs to the parent (b, x//2, y//2, z//2). The
+    parents are the distinct such tuples in ascending lexicographic order of
+    (b, x, y, z) (the order a sorting unique gives); a parent's feature row is
+    the channel-wise maximum over its sites. Returns (parent coords [M,4]
+    int32, inverse [N] int32 = parent row of each site, parent features
+    [M,C] in the input dtype or None, parent grid).
+    """
+    coords = np.asarray(coords)
+    for i in range(coords.shape[0]):  # range only: repeated sites are allowed here
+        b, x, y, z = (int(v) for v in coords[i])
+        if b < 0 or (batch is not None and b >= batch):
+            raise OracleInputError(f"row {i}: batch index {b} out of range")
+        if not (0 <= x < grid[0] and 0 <= y < grid[1] and 0 <= z < grid[2]):
+            raise OracleInputError(f"row {i}: site {(x, y, z)} outside the grid {tuple(grid)}")
+    parents = {}
+    for i in range(coords.shape[0]):
+        b, x, y, z = (int(v) for v in coords[i])
+        parents.setdefault((b, x // 2, y // 2, z // 2), []).append(i)
+    keys = sorted(parents)
+    pc = np.array(keys, dtype=np.int32).reshape(-1, 4)
+    inv = np.empty(coords.shape[0], dtype=np.int32)
+    for p, key in enumerate(keys):
+        for i in parents[key]:
+            inv[i] = p
+    pf = None
+    if feats is not None:
+        feats = np.asarray(feats)
+        pf = np.empty((len(keys), feats.shape[1]), dtype=feats.dtype)
+        for p, key in enumerate(keys):
+            rows = parents[key]
+            m = feats[rows[0]].copy()
+            for i in rows[1:]:
+                m = np.maximum(m, feats[i])
+            pf[p] = m
+    pgrid = tuple((int(g) + 1) // 2 for g in grid)
+    return pc, inv, pf, pgrid
+
+
+def subdivide(coords: np.ndarray, feats: Optional[np.ndarray], grid: Sequence[int]):
+    """x2 coordinate expansion: site i becomes the 8 sites
+    (b, 2x+dx, 2y+dy, 2z+dz) at rows 8*i + c, c = 4*dx + 2*dy + dz, each with
+    site i's feature row. Returns (child coords [8N,4] int32, child features
+    [8N,C] or None, child grid)."""
+    coords = np.asarray(coords)
+    n = coords.shape[0]
+    cc = np.empty((8 * n, 4), dtype=np.int32)
+    for i in range(n):
+        b, x, y, z = (int(v) for v in coords[i])
+        for c, (dx, dy, dz) in enumerate(SUBDIVIDE_OFFSETS):
+            cc[8 * i + c] = (b, 2 * x + dx, 2 * y + dy, 2 * z + dz)
+    cf = None
+    if feats is not None:
+        feats = np.asarray(feats)
+        cf = np.repeat(feats, 8, axis=0)
+    return cc, cf, tuple(2 * int(g) for g in grid)
