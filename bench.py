@@ -16,7 +16,10 @@ With --op backward_input or backward_weight the same workload times the
 layer's input gradient (weight preparation + the forward with the flipped,
 transposed kernel on the same map) or weight gradient (the MFMA pair
 contraction + the fixed-order reduction of its partials), each with its own
-roofline and oracle baseline.
+roofline and oracle baseline. --op downsample / subdivide time the x2
+coordinate operations on the workload's sites and first-layer features
+(sites per second; the downsample step includes its plan and one host wait,
+its roofline covers the max-pool kernel on a built plan).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--op OP]
 """
@@ -54,8 +57,11 @@ METRICS = {
     "forward": "SubMConv3d ms/layer + effective TFLOP/s (128^3 grid, C=128, 10% occ)",
     "backward_input": "SubMConv3d input-gradient ms/layer + effective TFLOP/s",
     "backward_weight": "SubMConv3d weight-gradient ms/layer + effective TFLOP/s",
+    "downsample": "x2 sparse downsample (max) input sites/s",
+    "subdivide": "x2 sparse subdivide input sites/s",
 }
-KERNELS = {"forward": "k_fwd_pp", "backward_input": "k_fwd_pp", "backward_weight": "k_bwd_weight"}
+KERNELS = {"forward": "k_fwd_pp", "backward_input": "k_fwd_pp", "backward_weight": "k_bwd_weight",
+           "downsample": "k_down_max", "subdivide": "k_subdivide"}
 
 
 def algorithmic_bytes(op, n, cin, cout, ksize, has_order, has_bias):
@@ -85,6 +91,96 @@ def measured_traffic(config, op, morton):
         if hashlib.sha256(f.read()).hexdigest() != t["sha256"]:
             return None
     return round((t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"]) * 1024)
+
+
+def _time(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / steps * 1e3  # us
+
+
+def coord_op_bench(args, sc, wl, coords, feats, dev):
+    import ctypes
+    import numpy as np
+    import torch
+    op = args.op
+    n, C = wl.n, feats.shape[1]
+    lib = sc.load_library()
+    st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    if op == "downsample":
+        def step():
+            sc.downsample(coords, feats, wl.grid, wl.batch)
+        t = time.perf_counter()
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        steps = max(3, args.steps // 10)
+        t = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        step_us = (time.perf_counter() - t) / steps * 1e6
+        g = (ctypes.c_int32 * 3)(*wl.grid)
+        h = ctypes.c_void_p()
+        sc._check(lib.submconv_downsample_plan(sc._ptr(coords), n, wl.batch, g, st, ctypes.byref(h)))
+        m = int(lib.submconv_downsample_rows(h))
+        pf = torch.empty((m, C), dtype=torch.float16, device=dev)
+        k_us = _time(lambda: sc._check(lib.submconv_downsample_max(h, sc._ptr(feats), C, sc._ptr(pf), st)),
+                     args.steps, args.warmup, torch)
+        lib.submconv_downsample_free(h)
+        alg = n * C * 2 + m * C * 2 + n * 4 + (m + 1) * 4
+        detail = {"parents": m}
+    else:
+        cc = torch.empty((8 * n, 4), dtype=torch.int32, device=dev)
+        cf = torch.empty((8 * n, C), dtype=torch.float16, device=dev)
+
+        def step():
+            sc._check(lib.submconv_subdivide(sc._ptr(coords), n, sc._ptr(feats), C, sc._ptr(cc),
+                                             sc._ptr(cf), st))
+        k_us = _time(step, args.steps, args.warmup, torch)
+        step_us = k_us
+        alg = n * 16 + n * C * 2 + 8 * n * 16 + 8 * n * C * 2
+        detail = {"children": 8 * n}
+    gbs = alg / (k_us * 1e-6) / 1e9
+    print(f"[bench] {op}: step {step_us:.1f} us, kernel {k_us:.1f} us, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        if op == "downsample":
+            ns = n
+            t = time.perf_counter()
+            O.downsample_np(wl.coords, wl.feats, wl.grid)
+            what = "all sites, numpy sorting unique + maximum scatter"
+        else:
+            ns = min(n, 50000)
+            t = time.perf_counter()
+            O.subdivide(wl.coords[:ns], wl.feats[:ns], wl.grid)
+            what = f"first {ns} sites, per-site loop"
+        cpu_s = time.perf_counter() - t
+        cpu = {"value": round(ns / cpu_s / 1e6, 4), "unit": "Msites/s", "cores": 1, "kind": "oracle",
+               "sample": f"{args.config}: {what} ({cpu_s * 1e3:.0f} ms)"}
+    rec = {
+        "metric": METRICS[op], "value": round(n / (step_us * 1e-6) / 1e6, 3), "unit": "Msites/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_us / 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16 / int32",
+        "data": "synthetic",
+        "config": dict({"workload": f"{args.config}: {n} sites, grid {wl.grid[0]}^3, batch {wl.batch}, C={C}",
+                        "op": op}, **detail),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": KERNELS[op],
+                     "kernel_us": round(k_us, 2), "algorithmic_bytes": alg},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
 
 
 def main():
@@ -124,6 +220,9 @@ def main():
     grad_out = torch.from_numpy(g_np).to(dev)
     torch.cuda.synchronize()
     print(f"[bench] {args.config} {op}: N={wl.n} {L.cin}->{L.cout} ksize={L.ksize}", file=sys.stderr, flush=True)
+
+    if op in ("downsample", "subdivide"):
+        return coord_op_bench(args, sc, wl, coords, feats, dev)
 
     # kernel-map build (cold, including allocation and the one host wait)
     build_ms = []

@@ -219,6 +219,65 @@ int submconv_backward_weight(submconv_map_t map, const uint16_t* feats, const ui
 int submconv_backward_bias(const uint16_t* grad_out, int64_t n, int32_t cout, float* grad_b,
                            hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Coordinate operations of the same sparse stack (trellis_sparse_mlx README,
+ * "What's in it" table, subdivide / downsample row): x2 max-pooling and x2
+ * coordinate expansion.
+ * ---------------------------------------------------------------------- */
+
+/* Opaque downsample plan: library-owned device buffers describing which
+ * sites fall into which parent; immutable, released by submconv_downsample_free. */
+typedef struct submconv_down_s* submconv_down_t;
+
+/*
+ * submconv_downsample_plan -- group the sites by parent (b, x/2, y/2, z/2).
+ *
+ * coords [n,4] int32 (b,x,y,z), device, 0 <= b < batch, 0 <= x < grid[0],
+ * ... (a repeated site is simply one more child). The parents are the
+ * distinct parent sites in ascending lexicographic (b,x,y,z) order; the
+ * parent grid is ceil(grid/2). Builds on `stream`, then waits for it once (to
+ * learn the parent count and report SUBMCONV_ERR_COORD_OUT_OF_RANGE). Allocates
+ * device memory (about 24 bytes per site, plus temporaries freed on return).
+ */
+int submconv_downsample_plan(const int32_t* coords, int64_t n, int32_t batch, const int32_t grid[3],
+                             hipStream_t stream, submconv_down_t* out_plan);
+
+/* Number of parents M of a plan (negative on a bad argument). */
+int64_t submconv_downsample_rows(submconv_down_t plan);
+
+/* Parent grid extents (host array of 3). */
+int submconv_downsample_grid(submconv_down_t plan, int32_t pgrid[3]);
+
+/*
+ * submconv_downsample_coords -- pcoords [M,4] int32 (parent sites, sorted) and
+ * inverse [n] int32 (parent row of each site); either may be NULL. Device
+ * pointers, asynchronous on `stream`.
+ */
+int submconv_downsample_coords(submconv_down_t plan, int32_t* pcoords, int32_t* inverse,
+                               hipStream_t stream);
+
+/*
+ * submconv_downsample_max -- parent features: out[p][c] = max over the sites
+ * of parent p of feats[site][c] (fp16, exact). feats [n,C] and out [M,C] fp16,
+ * device, 16-byte aligned, C a multiple of 8 up to 4096. Asynchronous, no
+ * allocation; may be called for any number of feature tensors per plan.
+ */
+int submconv_downsample_max(submconv_down_t plan, const uint16_t* feats, int32_t cdim, uint16_t* out,
+                            hipStream_t stream);
+
+/* Release a plan (waits for the device). NULL is a no-op. */
+int submconv_downsample_free(submconv_down_t plan);
+
+/*
+ * submconv_subdivide -- x2 expansion: site i becomes the rows 8i + c,
+ * c = 4dx + 2dy + dz (dx slowest), at (b, 2x+dx, 2y+dy, 2z+dz), each with site
+ * i's feature row. coords [n,4] int32, out_coords [8n,4] int32; feats [n,C]
+ * and out_feats [8n,C] fp16 (both NULL for coordinates only; C a multiple of
+ * 8 up to 4096, 16-byte aligned). Device pointers, asynchronous, no allocation.
+ */
+int submconv_subdivide(const int32_t* coords, int64_t n, const uint16_t* feats, int32_t cdim,
+                       int32_t* out_coords, uint16_t* out_feats, hipStream_t stream);
+
 /* Message for a status code (static string). */
 const char* submconv_status_string(int status);
 

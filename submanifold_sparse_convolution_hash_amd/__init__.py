@@ -25,7 +25,7 @@ import torch
 __all__ = [
     "SubmconvError", "KernelMap", "build_map", "prepare_weights", "forward", "backward_input",
     "backward_weight", "backward_bias", "SubMConv3dFunction", "SubMConv3d", "library_path", "load_library",
-    "abi_version", "FLAG_MORTON",
+    "abi_version", "FLAG_MORTON", "downsample", "subdivide",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -71,6 +71,13 @@ def load_library():
         "submconv_backward_weight_workspace_bytes": ([P, I32, I32, I32], I64),
         "submconv_backward_weight": ([P, P, P, P, P, I32, I32, I32, P], ctypes.c_int),
         "submconv_backward_bias": ([P, I64, I32, P, P], ctypes.c_int),
+        "submconv_downsample_plan": ([P, I64, I32, P, P, P], ctypes.c_int),
+        "submconv_downsample_rows": ([P], I64),
+        "submconv_downsample_grid": ([P, P], ctypes.c_int),
+        "submconv_downsample_coords": ([P, P, P, P], ctypes.c_int),
+        "submconv_downsample_max": ([P, P, I32, P, P], ctypes.c_int),
+        "submconv_downsample_free": ([P], ctypes.c_int),
+        "submconv_subdivide": ([P, I64, P, I32, P, P, P], ctypes.c_int),
         "submconv_forward": ([P, P, P, P, P, I32, I32, I32, P], ctypes.c_int),
         "submconv_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "submconv_last_error": ([], ctypes.c_char_p),
@@ -315,6 +322,56 @@ def backward_bias(grad_out: torch.Tensor) -> torch.Tensor:
                                                      grad_out.shape[1], _ptr(out),
                                                      _stream(grad_out.device)))
     return out
+
+
+def downsample(coords: torch.Tensor, feats: Optional[torch.Tensor], grid: Sequence[int],
+               batch: Optional[int] = None):
+    """x2 max-pool: returns ``(pcoords [M,4] int32, inverse [N] int32, pfeats
+    [M,C] fp16 or None, pgrid)``; parents in ascending (b,x,y,z) order, each
+    parent's features the channel-wise max over its sites."""
+    _require(coords, "coords", torch.int32, 2)
+    if batch is None:
+        batch = int(coords[:, 0].max().item()) + 1 if coords.shape[0] else 1
+    lib = load_library()
+    g = (ctypes.c_int32 * 3)(*[int(v) for v in grid])
+    h = ctypes.c_void_p()
+    st = _stream(coords.device)
+    with torch.cuda.device(coords.device):
+        _check(lib.submconv_downsample_plan(_ptr(coords), coords.shape[0], int(batch), g, st,
+                                            ctypes.byref(h)))
+        try:
+            m = int(lib.submconv_downsample_rows(h))
+            pg = (ctypes.c_int32 * 3)()
+            _check(lib.submconv_downsample_grid(h, pg))
+            pcoords = torch.empty((m, 4), dtype=torch.int32, device=coords.device)
+            inverse = torch.empty((coords.shape[0],), dtype=torch.int32, device=coords.device)
+            _check(lib.submconv_downsample_coords(h, _ptr(pcoords), _ptr(inverse), st))
+            pfeats = None
+            if feats is not None:
+                _require(feats, "feats", torch.float16, 2)
+                pfeats = torch.empty((m, feats.shape[1]), dtype=torch.float16, device=coords.device)
+                _check(lib.submconv_downsample_max(h, _ptr(feats), feats.shape[1], _ptr(pfeats), st))
+        finally:
+            lib.submconv_downsample_free(h)
+    return pcoords, inverse, pfeats, tuple(int(v) for v in pg)
+
+
+def subdivide(coords: torch.Tensor, feats: Optional[torch.Tensor], grid: Sequence[int]):
+    """x2 expansion: returns ``(ccoords [8N,4] int32, cfeats [8N,C] fp16 or
+    None, cgrid)``, children of site i at rows 8i + 4dx + 2dy + dz."""
+    _require(coords, "coords", torch.int32, 2)
+    n = coords.shape[0]
+    cc = torch.empty((8 * n, 4), dtype=torch.int32, device=coords.device)
+    cf = None
+    cdim = 0
+    if feats is not None:
+        _require(feats, "feats", torch.float16, 2)
+        cdim = feats.shape[1]
+        cf = torch.empty((8 * n, cdim), dtype=torch.float16, device=coords.device)
+    with torch.cuda.device(coords.device):
+        _check(load_library().submconv_subdivide(_ptr(coords), n, _ptr(feats), cdim, _ptr(cc),
+                                                 _ptr(cf), _stream(coords.device)))
+    return cc, cf, tuple(2 * int(v) for v in grid)
 
 
 class SubMConv3dFunction(torch.autograd.Function):

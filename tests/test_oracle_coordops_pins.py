@@ -91,3 +91,13 @@ def test_range_errors_and_repeated_sites():
     np.testing.assert_array_equal(pc, [[0, 0, 0, 0]])
     np.testing.assert_array_equal(inv, [0, 0])
     assert pf[0, 0] == 2.0
+
+
+@pytest.mark.parametrize("seed", [6, 7])
+def test_vectorised_downsample_matches_loop(seed):
+    wl = workloads.random_small(seed, G=10, occ=0.3, cin=8, cout=1, batch=3)
+    a = O.downsample(wl.coords, wl.feats, wl.grid)
+    b = O.downsample_np(wl.coords, wl.feats, wl.grid)
+    for x, y in zip(a[:3], b[:3]):
+        np.testing.assert_array_equal(x, y)
+    assert a[3] == b[3]
