@@ -191,6 +191,8 @@ def main():
     ap.add_argument("--config", default="c3_128_128")
     ap.add_argument("--op", default="forward", choices=list(METRICS))
     ap.add_argument("--morton", action="store_true")
+    ap.add_argument("--sorted-keys", action="store_true",
+                    help="build the map with the sorted-key lookup instead of the hash table")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a device copy of this many MiB (counter calibration)")
@@ -232,7 +234,7 @@ def main():
             km.free()
         torch.cuda.synchronize()
         t = time.perf_counter()
-        km = sc.build_map(coords, wl.grid, wl.batch, morton=args.morton)
+        km = sc.build_map(coords, wl.grid, wl.batch, morton=args.morton, sorted_keys=args.sorted_keys)
         torch.cuda.synchronize()
         build_ms.append((time.perf_counter() - t) * 1e3)
     pairs = km.active_pairs(L.ksize)
@@ -347,7 +349,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.config}: SubMConv3d {L.ksize}x{L.ksize}x{L.ksize}, grid {wl.grid[0]}^3, "
                                f"batch {wl.batch}, N={wl.n}, Cin={L.cin}, Cout={L.cout}, warm kernel map",
-                   "op": op, "active_pairs": pairs, "morton": bool(args.morton)},
+                   "op": op, "active_pairs": pairs, "morton": bool(args.morton),
+                   "map_lookup": "sorted keys" if args.sorted_keys else "hash"},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(args.config, op, args.morton),

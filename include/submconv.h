@@ -59,6 +59,10 @@ extern "C" {
 
 /* Flags of submconv_build_map. */
 #define SUBMCONV_FLAG_MORTON 1u /* process output rows in Morton (Z-curve) order */
+/* find neighbours by binary search in the radix-sorted packed site keys
+ * instead of the hash table (the packing + sort + search lookup of "Running
+ * TRELLIS.2 on a Mac (3/3)", section E); the map is the same */
+#define SUBMCONV_FLAG_SORTED_KEYS 2u
 
 /* Flags of submconv_prepare_weights_ex. */
 #define SUBMCONV_PREP_INPUT_GRAD 1u /* prepare the flipped, transposed kernel of the input gradient */
@@ -77,7 +81,8 @@ typedef struct submconv_map_s* submconv_map_t;
  * batch    number of batch items (>= 1).
  * grid     host array of 3 positive extents.
  * flags    0 or SUBMCONV_FLAG_MORTON (iteration order only; results are the
- *          same bit for bit either way).
+ *          same bit for bit either way), optionally | SUBMCONV_FLAG_SORTED_KEYS
+ *          (another lookup structure, the same map).
  * out_map  receives the handle (host pointer).
  *
  * The map is built on `stream`; the function then waits for that stream once

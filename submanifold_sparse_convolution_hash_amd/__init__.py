@@ -31,6 +31,7 @@ __all__ = [
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsubmconv.so")
 FLAG_MORTON = 1
+FLAG_SORTED_KEYS = 2
 PREP_INPUT_GRAD = 1
 _lib = None
 
@@ -172,9 +173,11 @@ class KernelMap:
 
 
 def build_map(coords: torch.Tensor, grid: Sequence[int], batch: Optional[int] = None,
-              morton: bool = False) -> KernelMap:
+              morton: bool = False, sorted_keys: bool = False) -> KernelMap:
     """Hashes the sites ``coords`` ([N,4] int32 (b,x,y,z), device) and builds
-    their 3x3x3 neighbour map. Waits once for the stream (validation)."""
+    their 3x3x3 neighbour map. Waits once for the stream (validation).
+    ``sorted_keys`` finds neighbours by binary search in the sorted site keys
+    instead of the hash table (same map)."""
     _require(coords, "coords", torch.int32, 2)
     if coords.shape[1] != 4:
         raise ValueError("coords must be [N,4]")
@@ -183,7 +186,7 @@ def build_map(coords: torch.Tensor, grid: Sequence[int], batch: Optional[int] = 
     lib = load_library()
     g = (ctypes.c_int32 * 3)(*[int(v) for v in grid])
     h = ctypes.c_void_p()
-    flags = FLAG_MORTON if morton else 0
+    flags = (FLAG_MORTON if morton else 0) | (FLAG_SORTED_KEYS if sorted_keys else 0)
     with torch.cuda.device(coords.device):
         _check(lib.submconv_build_map(_ptr(coords), coords.shape[0], int(batch), g, flags,
                                       _stream(coords.device), ctypes.byref(h)))

@@ -92,6 +92,11 @@ __global__ void k_pack(const int32_t* __restrict__ coords, int64_t n, int32_t ba
   }
 }
 
+__global__ void k_iota(int32_t* __restrict__ v, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) v[i] = static_cast<int32_t>(i);
+}
+
 __global__ void k_insert(const uint64_t* __restrict__ keys, int64_t n, uint64_t* tkeys,
                          int32_t* __restrict__ tvals, uint64_t mask, uint32_t* __restrict__ err) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -157,6 +162,50 @@ __global__ void k_query(const int32_t* __restrict__ coords, const int32_t* __res
   // wave-level sum, one atomic per wave
   for (int off = 32; off > 0; off >>= 1) hits += __shfl_down(hits, off, 64);
   if ((threadIdx.x & 63) == 0 && hits) atomicAdd(pairs, static_cast<unsigned long long>(hits));
+}
+
+// Sorted-key builder (the packing + sort + search lookup of "Running
+// TRELLIS.2 on a Mac (3/3)", section E): an independent second way to the
+// same map. skeys/srows are the packed keys and their rows sorted by key.
+__global__ void k_sorted_dups(const uint64_t* __restrict__ skeys, int64_t n, uint64_t none,
+                              uint32_t* __restrict__ err) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t > 0 && t < n && skeys[t] != none && skeys[t] == skeys[t - 1]) atomicOr(err, kErrDuplicate);
+}
+
+// One thread per (tap k, processing row t), t fastest: nbr[k][t] by a binary
+// search (lower bound) of the neighbour's key among the sorted keys.
+__global__ void k_query_sorted(const int32_t* __restrict__ coords, const int32_t* __restrict__ order,
+                               int64_t n, int32_t g0, int32_t g1, int32_t g2,
+                               const uint64_t* __restrict__ skeys, const int32_t* __restrict__ srows,
+                               int32_t* __restrict__ nbr, unsigned long long* __restrict__ pairs) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  int hit = 0;
+  if (idx < n * kTaps3) {
+    const int k = static_cast<int>(idx / n);
+    const int64_t t = idx - static_cast<int64_t>(k) * n;
+    const int64_t i = order ? order[t] : t;
+    const int32_t b = coords[4 * i + 0];
+    const int32_t nx = coords[4 * i + 1] + (k / 9) - 1;
+    const int32_t ny = coords[4 * i + 2] + ((k / 3) % 3) - 1;
+    const int32_t nz = coords[4 * i + 3] + (k % 3) - 1;
+    int32_t j = -1;
+    if (k == kCenterTap) {
+      j = static_cast<int32_t>(i);
+    } else if (nx >= 0 && nx < g0 && ny >= 0 && ny < g1 && nz >= 0 && nz < g2) {
+      const uint64_t key = pack_key(b, nx, ny, nz, g0, g1, g2);
+      int64_t lo = 0, hi = n;
+      while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (skeys[mid] < key) lo = mid + 1; else hi = mid;
+      }
+      if (lo < n && skeys[lo] == key) j = srows[lo];
+    }
+    nbr[idx] = j;
+    hit = j >= 0;
+  }
+  const unsigned long long m = __ballot(hit);
+  if ((threadIdx.x & 63) == 0 && m) atomicAdd(pairs, static_cast<unsigned long long>(__popcll(m)));
 }
 
 // Per tile of kTileRows processing rows: entries per processing position
@@ -289,7 +338,7 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   if (n < 0) return set_error(SUBMCONV_ERR_INVALID_ARG, "n = %lld is negative", (long long)n);
   if (n > 0 && !coords) return set_error(SUBMCONV_ERR_INVALID_ARG, "coords is NULL");
   if (batch < 1) return set_error(SUBMCONV_ERR_INVALID_ARG, "batch = %d < 1", batch);
-  if (flags & ~SUBMCONV_FLAG_MORTON)
+  if (flags & ~(SUBMCONV_FLAG_MORTON | SUBMCONV_FLAG_SORTED_KEYS))
     return set_error(SUBMCONV_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   for (int a = 0; a < 3; ++a)
     if (grid[a] < 1) return set_error(SUBMCONV_ERR_INVALID_ARG, "grid[%d] = %d < 1", a, grid[a]);
@@ -304,6 +353,7 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
       return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "batch*grid volume exceeds 2^63");
   }
   const bool morton = (flags & SUBMCONV_FLAG_MORTON) != 0;
+  const bool sorted_keys = (flags & SUBMCONV_FLAG_SORTED_KEYS) != 0;
   int mbits = 0;
   if (morton) {
     mbits = bits_for(std::max(grid[0], std::max(grid[1], grid[2])));
@@ -328,6 +378,7 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   const uint64_t mask = static_cast<uint64_t>(cap - 1);
 
   DevBuf keys, tkeys, tvals, small, mcode_in, mcode_out, midx, sort_tmp, tile_tot, scan_tmp;
+  DevBuf skeys, srows, rows_in, ksort_tmp;
   int32_t* nbr = nullptr;
   int32_t* order = nullptr;
   uint16_t* tile_cnt = nullptr;
@@ -352,8 +403,14 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   } while (0)
 
   BUILD_CHECK(hipMalloc(&keys.p, sizeof(uint64_t) * n));
-  BUILD_CHECK(hipMalloc(&tkeys.p, sizeof(uint64_t) * cap));
-  BUILD_CHECK(hipMalloc(&tvals.p, sizeof(int32_t) * cap));
+  if (sorted_keys) {
+    BUILD_CHECK(hipMalloc(&skeys.p, sizeof(uint64_t) * n));
+    BUILD_CHECK(hipMalloc(&srows.p, sizeof(int32_t) * n));
+    BUILD_CHECK(hipMalloc(&rows_in.p, sizeof(int32_t) * n));
+  } else {
+    BUILD_CHECK(hipMalloc(&tkeys.p, sizeof(uint64_t) * cap));
+    BUILD_CHECK(hipMalloc(&tvals.p, sizeof(int32_t) * cap));
+  }
   BUILD_CHECK(hipMalloc(&small.p, 256));
   BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&nbr), sizeof(int32_t) * kTaps3 * n));
   if (morton) {
@@ -366,7 +423,7 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   unsigned long long* pairs = reinterpret_cast<unsigned long long*>(static_cast<char*>(small.p) + 8);
 
   BUILD_CHECK(hipMemsetAsync(small.p, 0, 256, stream));
-  BUILD_CHECK(hipMemsetAsync(tkeys.p, 0xff, sizeof(uint64_t) * cap, stream));
+  if (!sorted_keys) BUILD_CHECK(hipMemsetAsync(tkeys.p, 0xff, sizeof(uint64_t) * cap, stream));
 
   const int B = 256;
   k_pack<<<grid_for(n, B), B, 0, stream>>>(coords, n, batch, grid[0], grid[1], grid[2],
@@ -374,9 +431,30 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
                                            static_cast<uint64_t*>(mcode_in.p),
                                            static_cast<int32_t*>(midx.p));
   BUILD_CHECK(hipGetLastError());
-  k_insert<<<grid_for(n, B), B, 0, stream>>>(static_cast<const uint64_t*>(keys.p), n,
-                                             static_cast<uint64_t*>(tkeys.p),
-                                             static_cast<int32_t*>(tvals.p), mask, err);
+  if (sorted_keys) {
+    // rows 0..n-1 as the sort's values; out-of-range sites carry the empty
+    // key, which sorts last and matches no query
+    k_iota<<<grid_for(n, B), B, 0, stream>>>(static_cast<int32_t*>(rows_in.p), n);
+    BUILD_CHECK(hipGetLastError());
+    size_t tmp_bytes = 0;
+    BUILD_CHECK(rocprim::radix_sort_pairs(nullptr, tmp_bytes, static_cast<const uint64_t*>(keys.p),
+                                          static_cast<uint64_t*>(skeys.p),
+                                          static_cast<const int32_t*>(rows_in.p),
+                                          static_cast<int32_t*>(srows.p), static_cast<size_t>(n),
+                                          0u, 64u, stream));
+    BUILD_CHECK(hipMalloc(&ksort_tmp.p, tmp_bytes > 0 ? tmp_bytes : 1));
+    BUILD_CHECK(rocprim::radix_sort_pairs(ksort_tmp.p, tmp_bytes, static_cast<const uint64_t*>(keys.p),
+                                          static_cast<uint64_t*>(skeys.p),
+                                          static_cast<const int32_t*>(rows_in.p),
+                                          static_cast<int32_t*>(srows.p), static_cast<size_t>(n),
+                                          0u, 64u, stream));
+    k_sorted_dups<<<grid_for(n, B), B, 0, stream>>>(static_cast<const uint64_t*>(skeys.p), n, kEmpty,
+                                                    err);
+  } else {
+    k_insert<<<grid_for(n, B), B, 0, stream>>>(static_cast<const uint64_t*>(keys.p), n,
+                                               static_cast<uint64_t*>(tkeys.p),
+                                               static_cast<int32_t*>(tvals.p), mask, err);
+  }
   BUILD_CHECK(hipGetLastError());
   if (morton) {
     const int bbits = batch > 1 ? bits_for(batch) : 0;
@@ -394,10 +472,16 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
                                           static_cast<const int32_t*>(midx.p), order,
                                           static_cast<size_t>(n), 0u, end_bit, stream));
   }
-  k_query<<<grid_for(n, B), B, 0, stream>>>(coords, order, n, grid[0], grid[1], grid[2],
-                                            static_cast<const uint64_t*>(tkeys.p),
-                                            static_cast<const int32_t*>(tvals.p), mask, nbr,
-                                            pairs);
+  if (sorted_keys) {
+    k_query_sorted<<<grid_for(n * kTaps3, B), B, 0, stream>>>(
+        coords, order, n, grid[0], grid[1], grid[2], static_cast<const uint64_t*>(skeys.p),
+        static_cast<const int32_t*>(srows.p), nbr, pairs);
+  } else {
+    k_query<<<grid_for(n, B), B, 0, stream>>>(coords, order, n, grid[0], grid[1], grid[2],
+                                              static_cast<const uint64_t*>(tkeys.p),
+                                              static_cast<const int32_t*>(tvals.p), mask, nbr,
+                                              pairs);
+  }
   BUILD_CHECK(hipGetLastError());
 
   // per-tile compacted lists: counts, then tile offsets (exclusive scan)

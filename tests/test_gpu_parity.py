@@ -331,3 +331,46 @@ def test_errors(dev):
                    bias=None, prepared=torch.zeros(27 * 16 * 16, dtype=torch.float16, device=dev),
                    ksize=2, cout=16)
     assert e.value.status == -1
+
+
+# ----------------------------------------------------------------------------
+# the sorted-key map builder: the same map, lists and results as the hash
+# ----------------------------------------------------------------------------
+
+
+@gpu
+@pytest.mark.parametrize("morton", [False, True])
+@pytest.mark.parametrize("name", ["c1_16_8", "c2_64_64", "c3_128_128", "c4_256_shell", "c5_512_chain"])
+def test_sorted_key_builder_same_map(dev, name, morton):
+    sc = _sc()
+    wl = workloads.make(name)
+    _say(f"[sorted keys] {name} morton={morton} N={wl.n}")
+    coords = _to(dev, wl.coords)
+    km_h = sc.build_map(coords, wl.grid, wl.batch, morton=morton)
+    km_s = sc.build_map(coords, wl.grid, wl.batch, morton=morton, sorted_keys=True)
+    a, b = km_h.export(), km_s.export()
+    assert torch.equal(a, b)
+    if name in ("c1_16_8", "c2_64_64"):
+        np.testing.assert_array_equal(b.cpu().numpy(), oc.kernel_map(wl.coords, wl.grid, wl.batch, 3))
+    assert km_h.active_pairs(3) == km_s.active_pairs(3)
+    L = wl.layers[0]
+    feats = _to(dev, wl.feats)
+    Wd = _to(dev, L.W)
+    bias = _to(dev, L.bias)
+    # identical per-tile lists, so bitwise identical outputs
+    assert torch.equal(sc.forward(km_h, feats, Wd, bias), sc.forward(km_s, feats, Wd, bias))
+    km_h.free()
+    km_s.free()
+
+
+@gpu
+def test_sorted_key_builder_errors(dev):
+    sc = _sc()
+    dup = _to(dev, np.array([[0, 1, 1, 1], [0, 2, 2, 2], [0, 1, 1, 1]], dtype=np.int32))
+    with pytest.raises(sc.SubmconvError) as ex:
+        sc.build_map(dup, (4, 4, 4), 1, sorted_keys=True)
+    assert ex.value.status == -3
+    out = _to(dev, np.array([[0, 1, 1, 4]], dtype=np.int32))
+    with pytest.raises(sc.SubmconvError) as ex:
+        sc.build_map(out, (4, 4, 4), 1, sorted_keys=True)
+    assert ex.value.status == -2
