@@ -190,6 +190,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c3_128_128")
     ap.add_argument("--op", default="forward", choices=list(METRICS))
+    ap.add_argument("--dtype", default="fp16", choices=["fp16", "bf16"],
+                    help="element type of features and weights (forward and input gradient)")
     ap.add_argument("--morton", action="store_true")
     ap.add_argument("--sorted-keys", action="store_true",
                     help="build the map with the sorted-key lookup instead of the hash table")
@@ -217,9 +219,13 @@ def main():
     coords = torch.from_numpy(wl.coords).to(dev)
     feats = torch.from_numpy(wl.feats).to(dev)
     W = torch.from_numpy(L.W).to(dev)
+    if args.dtype == "bf16":
+        if op not in ("forward", "backward_input"):
+            raise SystemExit("--dtype bf16 applies to the forward and the input gradient")
+        feats, W = feats.to(torch.bfloat16), W.to(torch.bfloat16)
     bias = None if L.bias is None else torch.from_numpy(L.bias).to(dev)
     g_np = np.random.default_rng(12345).standard_normal((wl.n, L.cout)).astype(np.float16)
-    grad_out = torch.from_numpy(g_np).to(dev)
+    grad_out = torch.from_numpy(g_np).to(dev).to(feats.dtype)
     torch.cuda.synchronize()
     print(f"[bench] {args.config} {op}: N={wl.n} {L.cin}->{L.cout} ksize={L.ksize}", file=sys.stderr, flush=True)
 
@@ -241,7 +247,7 @@ def main():
     flops = 2.0 * pairs * L.cin * L.cout
 
     if op == "forward":
-        out = torch.empty((wl.n, L.cout), dtype=torch.float16, device=dev)
+        out = torch.empty((wl.n, L.cout), dtype=feats.dtype, device=dev)
         wp = sc.prepare_weights(W)
 
         def step():
@@ -251,7 +257,7 @@ def main():
         def kernel():
             sc.forward(km, feats, bias=bias, prepared=wp, ksize=L.ksize, cout=L.cout, out=out)
     elif op == "backward_input":
-        out = torch.empty((wl.n, L.cin), dtype=torch.float16, device=dev)
+        out = torch.empty((wl.n, L.cin), dtype=feats.dtype, device=dev)
         wp = sc.prepare_weights(W, input_grad=True)
 
         def step():
@@ -345,7 +351,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16 (fp32 accumulate)",
+        "dtype": f"{args.dtype} (fp32 accumulate)",
         "data": "synthetic",
         "config": {"workload": f"{args.config}: SubMConv3d {L.ksize}x{L.ksize}x{L.ksize}, grid {wl.grid[0]}^3, "
                                f"batch {wl.batch}, N={wl.n}, Cin={L.cin}, Cout={L.cout}, warm kernel map",

@@ -64,6 +64,10 @@ extern "C" {
  * TRELLIS.2 on a Mac (3/3)", section E); the map is the same */
 #define SUBMCONV_FLAG_SORTED_KEYS 2u
 
+/* 16-bit element types of features and weights (the *_dtype entry points). */
+#define SUBMCONV_DTYPE_F16 0  /* IEEE binary16 */
+#define SUBMCONV_DTYPE_BF16 1 /* bfloat16 (the top 16 bits of a binary32) */
+
 /* Flags of submconv_prepare_weights_ex. */
 #define SUBMCONV_PREP_INPUT_GRAD 1u /* prepare the flipped, transposed kernel of the input gradient */
 
@@ -128,6 +132,8 @@ int64_t submconv_prepared_weights_elems(int32_t ksize, int32_t cin, int32_t cout
 
 /*
  * submconv_prepare_weights -- reorder weights into the forward kernel's layout.
+ * It moves 16-bit elements without converting them, so it serves fp16 and
+ * bf16 weights alike.
  * W   [K,Cin,Cout] fp16, device, out = feats @ W[k] per tap (k as above).
  * Wp  device buffer of submconv_prepared_weights_elems(...) fp16 elements,
  *     caller-allocated; its content is an opaque, shape-specific layout.
@@ -168,6 +174,18 @@ int submconv_forward(submconv_map_t map, const uint16_t* feats, const uint16_t* 
                      hipStream_t stream);
 
 /*
+ * submconv_forward_dtype -- submconv_forward for fp16 (SUBMCONV_DTYPE_F16)
+ * or bf16 (SUBMCONV_DTYPE_BF16) features, weights and output (the issue #1
+ * thread's "Fixed" list names fp16 and bf16 forwards). Products are
+ * accumulated in fp32 (v_mfma_f32_32x32x16_bf16 for bf16), the fp32 bias
+ * added, and the result rounded once to the element type (round to nearest
+ * even). Otherwise as submconv_forward.
+ */
+int submconv_forward_dtype(submconv_map_t map, const uint16_t* feats, const uint16_t* Wp,
+                           const float* bias, uint16_t* out, int32_t cin, int32_t cout,
+                           int32_t ksize, int32_t dtype, hipStream_t stream);
+
+/*
  * submconv_backward_input -- gradient of a layer's loss with respect to its
  * input features (the issue #1 thread's "bwd-input").
  *
@@ -185,6 +203,11 @@ int submconv_forward(submconv_map_t map, const uint16_t* feats, const uint16_t* 
 int submconv_backward_input(submconv_map_t map, const uint16_t* grad_out, const uint16_t* Wp_grad,
                             uint16_t* grad_in, int32_t cin, int32_t cout, int32_t ksize,
                             hipStream_t stream);
+
+/* submconv_backward_input for fp16 or bf16 data (SUBMCONV_DTYPE_*). */
+int submconv_backward_input_dtype(submconv_map_t map, const uint16_t* grad_out,
+                                  const uint16_t* Wp_grad, uint16_t* grad_in, int32_t cin,
+                                  int32_t cout, int32_t ksize, int32_t dtype, hipStream_t stream);
 
 /*
  * submconv_backward_weight_workspace_bytes -- device workspace that

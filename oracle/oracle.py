@@ -283,3 +283,11 @@ def downsample_np(coords: np.ndarray, feats: Optional[np.ndarray], grid: Sequenc
         np.maximum.at(pf, inv, feats.astype(np.float64))
         pf = pf.astype(feats.dtype)
     return pc.astype(np.int32), inv.astype(np.int32), pf, tuple((int(g) + 1) // 2 for g in grid)
+
+
+def bf16_bits_to_float64(bits: np.ndarray) -> np.ndarray:
+    """Exact values of bfloat16 numbers given as their 16-bit patterns: a
+    bfloat16 is the top half of an IEEE binary32, so the pattern shifted left
+    by 16 bits is that binary32, which fp64 holds exactly."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)

@@ -80,6 +80,8 @@ def load_library():
         "submconv_downsample_free": ([P], ctypes.c_int),
         "submconv_subdivide": ([P, I64, P, I32, P, P, P], ctypes.c_int),
         "submconv_forward": ([P, P, P, P, P, I32, I32, I32, P], ctypes.c_int),
+        "submconv_forward_dtype": ([P, P, P, P, P, I32, I32, I32, I32, P], ctypes.c_int),
+        "submconv_backward_input_dtype": ([P, P, P, P, I32, I32, I32, I32, P], ctypes.c_int),
         "submconv_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "submconv_last_error": ([], ctypes.c_char_p),
         "submconv_abi_version": ([], ctypes.c_int),
@@ -111,13 +113,17 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[ctypes.c_void_p]:
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _require(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
+_DTYPES = {torch.float16: 0, torch.bfloat16: 1}
+
+
+def _require(t: torch.Tensor, name: str, dtype, ndim: int) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a device tensor, got {t.device}")
-    if t.dtype != dtype:
-        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    allowed = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in allowed:
+        raise TypeError(f"{name} must be {' or '.join(str(d) for d in allowed)}, got {t.dtype}")
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
     if not t.is_contiguous():
@@ -194,11 +200,11 @@ def build_map(coords: torch.Tensor, grid: Sequence[int], batch: Optional[int] = 
 
 
 def prepare_weights(W: torch.Tensor, input_grad: bool = False) -> torch.Tensor:
-    """Reorders weights [K,Cin,Cout] fp16 (K = 27 or 1) into the forward
-    kernel's layout (an opaque fp16 buffer of the same element count). With
-    ``input_grad``, prepares the flipped, transposed kernel of the input
-    gradient instead (for :func:`backward_input`)."""
-    _require(W, "W", torch.float16, 3)
+    """Reorders weights [K,Cin,Cout] fp16 or bf16 (K = 27 or 1) into the
+    forward kernel's layout (an opaque buffer of the same dtype and element
+    count). With ``input_grad``, prepares the flipped, transposed kernel of
+    the input gradient instead (for :func:`backward_input`)."""
+    _require(W, "W", tuple(_DTYPES), 3)
     K, cin, cout = W.shape
     if K not in (27, 1):
         raise ValueError("W must be [27,Cin,Cout] or [1,Cin,Cout]")
@@ -207,7 +213,7 @@ def prepare_weights(W: torch.Tensor, input_grad: bool = False) -> torch.Tensor:
     n = int(lib.submconv_prepared_weights_elems(ksize, cin, cout))
     if n < 0:
         _check(n)
-    wp = torch.empty((n,), dtype=torch.float16, device=W.device)
+    wp = torch.empty((n,), dtype=W.dtype, device=W.device)
     with torch.cuda.device(W.device):
         _check(lib.submconv_prepare_weights_ex(_ptr(W), ksize, cin, cout,
                                                PREP_INPUT_GRAD if input_grad else 0, _ptr(wp),
@@ -219,12 +225,14 @@ def forward(kmap: KernelMap, feats: torch.Tensor, W: Optional[torch.Tensor] = No
             bias: Optional[torch.Tensor] = None, *, prepared: Optional[torch.Tensor] = None,
             ksize: Optional[int] = None, cout: Optional[int] = None,
             out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """One SubMConv3d layer: ``out[N,Cout]`` fp16 in the caller's row order.
+    """One SubMConv3d layer: ``out[N,Cout]`` in the caller's row order, in
+    the features' dtype (fp16 or bf16; fp32 accumulation).
 
-    Pass either ``W`` ([K,Cin,Cout] fp16, prepared on the fly) or ``prepared``
-    (from :func:`prepare_weights`) together with ``ksize`` and ``cout``.
+    Pass either ``W`` ([K,Cin,Cout], the features' dtype, prepared on the fly)
+    or ``prepared`` (from :func:`prepare_weights`) together with ``ksize`` and
+    ``cout``.
     """
-    _require(feats, "feats", torch.float16, 2)
+    _require(feats, "feats", tuple(_DTYPES), 2)
     if feats.shape[0] != kmap.num_rows:
         raise ValueError(f"feats has {feats.shape[0]} rows, the map {kmap.num_rows}")
     cin = feats.shape[1]
@@ -238,20 +246,22 @@ def forward(kmap: KernelMap, feats: torch.Tensor, W: Optional[torch.Tensor] = No
         prepared = prepare_weights(W)
     elif ksize is None or cout is None:
         raise ValueError("with prepared weights, pass ksize and cout")
+    if prepared.dtype != feats.dtype:
+        raise TypeError(f"weights are {prepared.dtype} but feats are {feats.dtype}")
     if bias is not None:
         _require(bias, "bias", torch.float32, 1)
         if bias.shape[0] != cout:
             raise ValueError("bias must be [Cout]")
     if out is None:
-        out = torch.empty((feats.shape[0], cout), dtype=torch.float16, device=feats.device)
+        out = torch.empty((feats.shape[0], cout), dtype=feats.dtype, device=feats.device)
     else:
-        _require(out, "out", torch.float16, 2)
+        _require(out, "out", feats.dtype, 2)
         if tuple(out.shape) != (feats.shape[0], cout):
             raise ValueError("out must be [N,Cout]")
     with torch.cuda.device(feats.device):
-        _check(load_library().submconv_forward(kmap.handle, _ptr(feats), _ptr(prepared), _ptr(bias),
-                                               _ptr(out), cin, cout, int(ksize),
-                                               _stream(feats.device)))
+        _check(load_library().submconv_forward_dtype(kmap.handle, _ptr(feats), _ptr(prepared),
+                                                     _ptr(bias), _ptr(out), cin, cout, int(ksize),
+                                                     _DTYPES[feats.dtype], _stream(feats.device)))
     return out
 
 
@@ -261,7 +271,7 @@ def backward_input(kmap: KernelMap, grad_out: torch.Tensor, W: Optional[torch.Te
     """Input gradient ``[N,Cin]`` fp16 of a layer with weights ``W`` for the
     output gradient ``grad_out`` ([N,Cout] fp16). Pass ``W`` or ``prepared``
     (``prepare_weights(W, input_grad=True)``) with ``ksize`` and ``cin``."""
-    _require(grad_out, "grad_out", torch.float16, 2)
+    _require(grad_out, "grad_out", tuple(_DTYPES), 2)
     if grad_out.shape[0] != kmap.num_rows:
         raise ValueError(f"grad_out has {grad_out.shape[0]} rows, the map {kmap.num_rows}")
     cout = grad_out.shape[1]
@@ -275,16 +285,18 @@ def backward_input(kmap: KernelMap, grad_out: torch.Tensor, W: Optional[torch.Te
         prepared = prepare_weights(W, input_grad=True)
     elif ksize is None or cin is None:
         raise ValueError("with prepared weights, pass ksize and cin")
+    if prepared.dtype != grad_out.dtype:
+        raise TypeError(f"weights are {prepared.dtype} but grad_out is {grad_out.dtype}")
     if out is None:
-        out = torch.empty((grad_out.shape[0], cin), dtype=torch.float16, device=grad_out.device)
+        out = torch.empty((grad_out.shape[0], cin), dtype=grad_out.dtype, device=grad_out.device)
     else:
-        _require(out, "out", torch.float16, 2)
+        _require(out, "out", grad_out.dtype, 2)
         if tuple(out.shape) != (grad_out.shape[0], cin):
             raise ValueError("out must be [N,Cin]")
     with torch.cuda.device(grad_out.device):
-        _check(load_library().submconv_backward_input(kmap.handle, _ptr(grad_out), _ptr(prepared),
-                                                      _ptr(out), int(cin), cout, int(ksize),
-                                                      _stream(grad_out.device)))
+        _check(load_library().submconv_backward_input_dtype(
+            kmap.handle, _ptr(grad_out), _ptr(prepared), _ptr(out), int(cin), cout, int(ksize),
+            _DTYPES[grad_out.dtype], _stream(grad_out.device)))
     return out
 
 
@@ -368,9 +380,9 @@ def subdivide(coords: torch.Tensor, feats: Optional[torch.Tensor], grid: Sequenc
     cf = None
     cdim = 0
     if feats is not None:
-        _require(feats, "feats", torch.float16, 2)
+        _require(feats, "feats", tuple(_DTYPES), 2)  # a copy: any 16-bit type
         cdim = feats.shape[1]
-        cf = torch.empty((8 * n, cdim), dtype=torch.float16, device=coords.device)
+        cf = torch.empty((8 * n, cdim), dtype=feats.dtype, device=coords.device)
     with torch.cuda.device(coords.device):
         _check(load_library().submconv_subdivide(_ptr(coords), n, _ptr(feats), cdim, _ptr(cc),
                                                  _ptr(cf), _stream(coords.device)))
@@ -378,9 +390,9 @@ def subdivide(coords: torch.Tensor, feats: Optional[torch.Tensor], grid: Sequenc
 
 
 class SubMConv3dFunction(torch.autograd.Function):
-    """Autograd over the library's kernels: forward, input gradient (the
-    forward with the flipped, transposed kernel on the same map) and weight
-    gradient. The weight gradient is computed in fp32 and returned in the
+    """Autograd over the library's kernels (fp16): forward, input gradient
+    (the forward with the flipped, transposed kernel on the same map) and
+    weight gradient. The weight gradient is computed in fp32 and returned in the
     weight's dtype; the bias gradient is the fp32 column sum of grad_out."""
 
     @staticmethod

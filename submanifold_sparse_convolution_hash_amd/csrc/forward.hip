@@ -40,7 +40,25 @@ namespace submconv {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+
+// 16-bit element types: rows and fragments move as opaque 16-byte chunks
+// (half8); only the MFMA and the final rounding depend on the type.
+template <bool IS_BF16>
+__device__ __forceinline__ _Float16 round16(float v) {
+  if constexpr (IS_BF16)
+    return __builtin_bit_cast(_Float16, static_cast<__bf16>(v));  // round to nearest even
+  else
+    return static_cast<_Float16>(v);  // round to nearest even
+}
+template <bool IS_BF16>
+__device__ __forceinline__ float widen16(_Float16 v) {
+  if constexpr (IS_BF16)
+    return static_cast<float>(__builtin_bit_cast(__bf16, v));
+  else
+    return static_cast<float>(v);
+}
 
 constexpr int kMaxChannels = 1024;
 
@@ -73,7 +91,7 @@ __device__ __forceinline__ int2 bload_i2(__amdgpu_buffer_rsrc_t r, uint32_t off)
 // Epilogue of both MFMA kernels: the tile's fp32 accumulator rows (float4
 // chunk q of row r at r*NQ + (q ^ (r % NQ))) plus the bias, rounded once to
 // fp16 (round to nearest even) and stored at the caller's row.
-template <int COUT_T, int NT, bool K3>
+template <int COUT_T, int NT, bool K3, bool IS_BF16>
 __device__ __forceinline__ void store_tile(const float4v* acc, int rows_here, int tid,
                                            const float* __restrict__ bias, int c0,
                                            const int32_t* __restrict__ order, int64_t t0,
@@ -92,14 +110,14 @@ __device__ __forceinline__ void store_tile(const float4v* acc, int rows_here, in
       b1 = *reinterpret_cast<const float4v*>(bias + c0 + 8 * c8 + 4);
     }
     half8 hv;
-    hv[0] = static_cast<_Float16>(a[0] + b0[0]);
-    hv[1] = static_cast<_Float16>(a[1] + b0[1]);
-    hv[2] = static_cast<_Float16>(a[2] + b0[2]);
-    hv[3] = static_cast<_Float16>(a[3] + b0[3]);
-    hv[4] = static_cast<_Float16>(b[0] + b1[0]);
-    hv[5] = static_cast<_Float16>(b[1] + b1[1]);
-    hv[6] = static_cast<_Float16>(b[2] + b1[2]);
-    hv[7] = static_cast<_Float16>(b[3] + b1[3]);
+    hv[0] = round16<IS_BF16>(a[0] + b0[0]);
+    hv[1] = round16<IS_BF16>(a[1] + b0[1]);
+    hv[2] = round16<IS_BF16>(a[2] + b0[2]);
+    hv[3] = round16<IS_BF16>(a[3] + b0[3]);
+    hv[4] = round16<IS_BF16>(b[0] + b1[0]);
+    hv[5] = round16<IS_BF16>(b[1] + b1[1]);
+    hv[6] = round16<IS_BF16>(b[2] + b1[2]);
+    hv[7] = round16<IS_BF16>(b[3] + b1[3]);
     const int64_t orow = (K3 && order) ? order[t0 + r] : t0 + r;
     *reinterpret_cast<half8*>(out + orow * cout + c0 + 8 * c8) = hv;
   }
@@ -134,7 +152,7 @@ struct Cfg {
   static_assert(NCG == 8, "centre steps");
 };
 
-template <int CIN, int COUT_T, bool K3>
+template <int CIN, int COUT_T, bool K3, bool IS_BF16>
 __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
     const int2* __restrict__ ent, const int32_t* __restrict__ tile_off,
     const uint16_t* __restrict__ tile_cnt, const int32_t* __restrict__ order, int64_t n,
@@ -291,7 +309,11 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
     float16v d = {};
 #pragma unroll
     for (int st = 0; st < KS; ++st)
-      d = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[st], B[st], d, 0, 0, 0);
+      if constexpr (IS_BF16)
+        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, A[st]),
+                                                    __builtin_bit_cast(bf16x8, B[st]), d, 0, 0, 0);
+      else
+        d = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[st], B[st], d, 0, 0, 0);
     return d;
   };
   // Accumulator rows of this lane's slot: the centre writes them, later taps
@@ -396,7 +418,7 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
   }
   __syncthreads();
 
-  store_tile<COUT_T, C::NT, K3>(acc, rows_here, tid, bias, c0, order, t0, out, cout);
+  store_tile<COUT_T, C::NT, K3, IS_BF16>(acc, rows_here, tid, bias, c0, order, t0, out, cout);
 }
 
 // ---------------------------------------------------------------------------
@@ -436,7 +458,7 @@ struct CfgPP {
   static_assert(NCG == 8 && LB <= 4 && LE < 4, "schedule");
 };
 
-template <int CIN, int COUT_T, bool K3>
+template <int CIN, int COUT_T, bool K3, bool IS_BF16>
 __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
     const int2* __restrict__ ent, const int32_t* __restrict__ tile_off,
     const uint16_t* __restrict__ tile_cnt, const int32_t* __restrict__ order, int64_t n,
@@ -576,7 +598,11 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
     float16v d = {};
 #pragma unroll
     for (int st = 0; st < KS; ++st)
-      d = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[st], B[st], d, 0, 0, 0);
+      if constexpr (IS_BF16)
+        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, A[st]),
+                                                    __builtin_bit_cast(bf16x8, B[st]), d, 0, 0, 0);
+      else
+        d = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[st], B[st], d, 0, 0, 0);
     return d;
   };
   auto acc_at = [&](int r, int a) { return r * C::NQ + ((qw + 2 * a + h) ^ (r & (C::NQ - 1))); };
@@ -676,13 +702,14 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
   else
     run(std::integral_constant<int, 1>{});
   __syncthreads();
-  store_tile<COUT_T, C::NT, K3>(acc, rows_here, tid, bias, c0, order, t0, out, cout);
+  store_tile<COUT_T, C::NT, K3, IS_BF16>(acc, rows_here, tid, bias, c0, order, t0, out, cout);
 }
 
 // ---------------------------------------------------------------------------
 // VALU kernel for channel counts the MFMA tiles do not cover (multiples of 8)
 // ---------------------------------------------------------------------------
 
+template <bool IS_BF16>
 __global__ __launch_bounds__(256) void k_fwd_valu(
     const int32_t* __restrict__ nbr, const int32_t* __restrict__ order, int64_t n, int ksize,
     const _Float16* __restrict__ feats, const _Float16* __restrict__ w,
@@ -707,15 +734,15 @@ __global__ __launch_bounds__(256) void k_fwd_valu(
     const _Float16* f = feats + j * cin;
     const _Float16* wk = w + static_cast<int64_t>(k) * cin * cout + o8 * 8;
     for (int c = 0; c < cin; ++c) {
-      const float fc = static_cast<float>(f[c]);
+      const float fc = widen16<IS_BF16>(f[c]);
       const half8 wv = *reinterpret_cast<const half8*>(wk + static_cast<int64_t>(c) * cout);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) a[q] += fc * static_cast<float>(wv[q]);
+      for (int q = 0; q < 8; ++q) a[q] += fc * widen16<IS_BF16>(wv[q]);
     }
   }
   half8 h;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) h[q] = static_cast<_Float16>(a[q]);
+  for (int q = 0; q < 8; ++q) h[q] = round16<IS_BF16>(a[q]);
   const int64_t orow = (ksize == 3 && order) ? order[t] : t;
   *reinterpret_cast<half8*>(out + orow * cout + o8 * 8) = h;
 }
@@ -792,7 +819,7 @@ int check_shape(int32_t ksize, int32_t cin, int32_t cout) {
   return SUBMCONV_OK;
 }
 
-template <int CIN, int COUT_T, bool K3>
+template <int CIN, int COUT_T, bool K3, bool IS_BF16>
 int launch_one(const Map& m, const _Float16* feats, const _Float16* wp, const float* bias,
                _Float16* out, int cout, hipStream_t stream) {
   const int64_t n_tiles64 = (m.n + kTileRows - 1) / kTileRows;
@@ -804,14 +831,14 @@ int launch_one(const Map& m, const _Float16* feats, const _Float16* wp, const fl
   const int64_t blocks = int64_t{8} * tiles_per_xcd * n_ct;
   const int n_pairs = static_cast<int>(K3 ? m.active_pairs : 0);
   if constexpr (CIN <= 128) {
-    k_fwd_pp<CIN, COUT_T, K3><<<static_cast<unsigned>(blocks), CfgPP<CIN, COUT_T, K3>::NT, 0,
-                                stream>>>(
+    k_fwd_pp<CIN, COUT_T, K3, IS_BF16><<<static_cast<unsigned>(blocks), CfgPP<CIN, COUT_T, K3>::NT, 0,
+                                    stream>>>(
         K3 ? m.ent : nullptr, K3 ? m.tile_off : nullptr, K3 ? m.tile_cnt : nullptr,
         K3 ? m.order : nullptr, m.n, feats, wp, bias, out, cout, n_tiles, n_ct, tiles_per_xcd,
         n_pairs);
   } else {
-    k_fwd_mfma<CIN, COUT_T, K3><<<static_cast<unsigned>(blocks), Cfg<CIN, COUT_T, K3>::NT, 0,
-                                  stream>>>(
+    k_fwd_mfma<CIN, COUT_T, K3, IS_BF16><<<static_cast<unsigned>(blocks), Cfg<CIN, COUT_T, K3>::NT, 0,
+                                      stream>>>(
         K3 ? m.ent : nullptr, K3 ? m.tile_off : nullptr, K3 ? m.tile_cnt : nullptr,
         K3 ? m.order : nullptr, m.n, feats, wp, bias, out, cout, n_tiles, n_ct, tiles_per_xcd,
         n_pairs);
@@ -820,24 +847,45 @@ int launch_one(const Map& m, const _Float16* feats, const _Float16* wp, const fl
   return SUBMCONV_OK;
 }
 
-template <int CIN, int COUT_T>
+template <int CIN, int COUT_T, bool IS_BF16>
 int launch_mfma(const Map& m, int ksize, const _Float16* feats, const _Float16* wp,
                 const float* bias, _Float16* out, int cout, hipStream_t stream) {
-  if (ksize == 1) return launch_one<CIN, COUT_T, false>(m, feats, wp, bias, out, cout, stream);
-  return launch_one<CIN, COUT_T, true>(m, feats, wp, bias, out, cout, stream);
+  if (ksize == 1) return launch_one<CIN, COUT_T, false, IS_BF16>(m, feats, wp, bias, out, cout, stream);
+  return launch_one<CIN, COUT_T, true, IS_BF16>(m, feats, wp, bias, out, cout, stream);
 }
 
-template <int CIN>
+template <int CIN, bool IS_BF16>
 int dispatch_cout(const Map& m, int ksize, const _Float16* feats, const _Float16* wp,
                   const float* bias, _Float16* out, int cout, hipStream_t stream) {
   // The LDS holds a 256 x COUT_T fp32 accumulator plus two 32-row groups of
   // Cin channels (at Cin = 256 and 128 columns that is exactly 160 KiB).
-  if (cout % 128 == 0) return launch_mfma<CIN, 128>(m, ksize, feats, wp, bias, out, cout, stream);
+  if (cout % 128 == 0) return launch_mfma<CIN, 128, IS_BF16>(m, ksize, feats, wp, bias, out, cout, stream);
   if constexpr (CIN <= 128) {
-    if (cout % 64 == 0) return launch_mfma<CIN, 64>(m, ksize, feats, wp, bias, out, cout, stream);
-    return launch_mfma<CIN, 32>(m, ksize, feats, wp, bias, out, cout, stream);
+    if (cout % 64 == 0) return launch_mfma<CIN, 64, IS_BF16>(m, ksize, feats, wp, bias, out, cout, stream);
+    return launch_mfma<CIN, 32, IS_BF16>(m, ksize, feats, wp, bias, out, cout, stream);
   }
   return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "internal: no MFMA tile for Cin = %d", CIN);
+}
+
+template <bool IS_BF16>
+int forward_typed(const Map& m, int ksize, int cin, int cout, const _Float16* feats,
+                  const _Float16* wp, const float* bias, _Float16* out, hipStream_t stream) {
+  if (use_mfma(cin, cout) && fits_buffers(m, cin)) {
+    switch (cin) {
+      case 32: return dispatch_cout<32, IS_BF16>(m, ksize, feats, wp, bias, out, cout, stream);
+      case 64: return dispatch_cout<64, IS_BF16>(m, ksize, feats, wp, bias, out, cout, stream);
+      case 128: return dispatch_cout<128, IS_BF16>(m, ksize, feats, wp, bias, out, cout, stream);
+      case 256: return dispatch_cout<256, IS_BF16>(m, ksize, feats, wp, bias, out, cout, stream);
+      default: break;
+    }
+  }
+  const int64_t items = m.n * (cout / 8);
+  const int B = 256;
+  k_fwd_valu<IS_BF16><<<static_cast<unsigned>((items + B - 1) / B), B, 0, stream>>>(
+      ksize == 3 ? m.nbr : nullptr, ksize == 3 ? m.order : nullptr, m.n, ksize, feats, wp, bias,
+      out, cin, cout);
+  SUBMCONV_HIP_CHECK(hipGetLastError());
+  return SUBMCONV_OK;
 }
 
 }  // namespace
@@ -882,11 +930,14 @@ extern "C" int submconv_prepare_weights(const uint16_t* W, int32_t ksize, int32_
   return submconv_prepare_weights_ex(W, ksize, cin, cout, 0u, Wp, stream);
 }
 
-extern "C" int submconv_forward(submconv_map_t map, const uint16_t* feats_u16, const uint16_t* Wp,
-                                const float* bias, uint16_t* out_u16, int32_t cin, int32_t cout,
-                                int32_t ksize, hipStream_t stream) {
+extern "C" int submconv_forward_dtype(submconv_map_t map, const uint16_t* feats_u16,
+                                      const uint16_t* Wp, const float* bias, uint16_t* out_u16,
+                                      int32_t cin, int32_t cout, int32_t ksize, int32_t dtype,
+                                      hipStream_t stream) {
   clear_error();
   if (!map) return set_error(SUBMCONV_ERR_INVALID_ARG, "map is NULL");
+  if (dtype != SUBMCONV_DTYPE_F16 && dtype != SUBMCONV_DTYPE_BF16)
+    return set_error(SUBMCONV_ERR_INVALID_ARG, "dtype = %d is not fp16 (0) or bf16 (1)", dtype);
   const int st = check_shape(ksize, cin, cout);
   if (st != SUBMCONV_OK) return st;
   const Map& m = map->m;
@@ -899,27 +950,30 @@ extern "C" int submconv_forward(submconv_map_t map, const uint16_t* feats_u16, c
   const _Float16* feats = reinterpret_cast<const _Float16*>(feats_u16);
   const _Float16* wp = reinterpret_cast<const _Float16*>(Wp);
   _Float16* out = reinterpret_cast<_Float16*>(out_u16);
-  if (use_mfma(cin, cout) && fits_buffers(m, cin)) {
-    switch (cin) {
-      case 32: return dispatch_cout<32>(m, ksize, feats, wp, bias, out, cout, stream);
-      case 64: return dispatch_cout<64>(m, ksize, feats, wp, bias, out, cout, stream);
-      case 128: return dispatch_cout<128>(m, ksize, feats, wp, bias, out, cout, stream);
-      case 256: return dispatch_cout<256>(m, ksize, feats, wp, bias, out, cout, stream);
-      default: break;
-    }
-  }
-  const int64_t items = m.n * (cout / 8);
-  const int B = 256;
-  k_fwd_valu<<<static_cast<unsigned>((items + B - 1) / B), B, 0, stream>>>(
-      ksize == 3 ? m.nbr : nullptr, ksize == 3 ? m.order : nullptr, m.n, ksize, feats, wp, bias,
-      out, cin, cout);
-  SUBMCONV_HIP_CHECK(hipGetLastError());
-  return SUBMCONV_OK;
+  if (dtype == SUBMCONV_DTYPE_BF16)
+    return forward_typed<true>(m, ksize, cin, cout, feats, wp, bias, out, stream);
+  return forward_typed<false>(m, ksize, cin, cout, feats, wp, bias, out, stream);
+}
+
+extern "C" int submconv_forward(submconv_map_t map, const uint16_t* feats_u16, const uint16_t* Wp,
+                                const float* bias, uint16_t* out_u16, int32_t cin, int32_t cout,
+                                int32_t ksize, hipStream_t stream) {
+  return submconv_forward_dtype(map, feats_u16, Wp, bias, out_u16, cin, cout, ksize,
+                                SUBMCONV_DTYPE_F16, stream);
+}
+
+extern "C" int submconv_backward_input_dtype(submconv_map_t map, const uint16_t* grad_out,
+                                             const uint16_t* Wp_grad, uint16_t* grad_in,
+                                             int32_t cin, int32_t cout, int32_t ksize,
+                                             int32_t dtype, hipStream_t stream) {
+  // the forward with the flipped, transposed kernel, cout -> cin channels
+  return submconv_forward_dtype(map, grad_out, Wp_grad, nullptr, grad_in, cout, cin, ksize, dtype,
+                                stream);
 }
 
 extern "C" int submconv_backward_input(submconv_map_t map, const uint16_t* grad_out,
                                        const uint16_t* Wp_grad, uint16_t* grad_in, int32_t cin,
                                        int32_t cout, int32_t ksize, hipStream_t stream) {
-  // the forward with the flipped, transposed kernel, cout -> cin channels
-  return submconv_forward(map, grad_out, Wp_grad, nullptr, grad_in, cout, cin, ksize, stream);
+  return submconv_backward_input_dtype(map, grad_out, Wp_grad, grad_in, cin, cout, ksize,
+                                       SUBMCONV_DTYPE_F16, stream);
 }

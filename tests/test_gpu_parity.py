@@ -374,3 +374,65 @@ def test_sorted_key_builder_errors(dev):
     with pytest.raises(sc.SubmconvError) as ex:
         sc.build_map(out, (4, 4, 4), 1, sorted_keys=True)
     assert ex.value.status == -2
+
+
+# ----------------------------------------------------------------------------
+# bf16: features, weights and output in bfloat16, fp32 accumulation. The
+# output rounding is 2^-9 relative, inside the same tolerance.
+# ----------------------------------------------------------------------------
+
+
+def _bf16_case(wl_seed, n_rows_G, occ, cin, cout, ksize, batch=1):
+    wl = workloads.random_small(wl_seed, G=n_rows_G, occ=occ, cin=cin, cout=cout, batch=batch,
+                                ksize=ksize)
+    rng = np.random.default_rng(wl_seed + 77)
+    fb = workloads.normal_bf16_bits(rng, (wl.n, cin))
+    Wb = workloads.normal_bf16_bits(rng, wl.layers[0].W.shape, std=1.0 / np.sqrt(27 * cin))
+    return wl, fb, Wb
+
+
+def _bf16_tensor(dev, bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def _bf16_values(t):
+    return op.bf16_bits_to_float64(t.view(torch.int16).cpu().numpy().view(np.uint16))
+
+
+@gpu
+@pytest.mark.parametrize("ksize", [3, 1])
+@pytest.mark.parametrize("cin,cout", [(8, 8), (32, 32), (64, 32), (64, 64), (128, 128), (256, 256), (40, 48)])
+def test_bf16_forward_shapes(dev, cin, cout, ksize):
+    sc = _sc()
+    wl, fb, Wb = _bf16_case(900 + cin + cout, 14, 0.25, cin, cout, ksize, batch=2)
+    _say(f"[bf16] forward {cin}->{cout} ksize={ksize} N={wl.n}")
+    km = sc.build_map(_to(dev, wl.coords), wl.grid, wl.batch)
+    bias = _to(dev, wl.layers[0].bias)
+    out = sc.forward(km, _bf16_tensor(dev, fb), _bf16_tensor(dev, Wb), bias)
+    assert out.dtype == torch.bfloat16
+    kmap = oc.kernel_map(wl.coords, wl.grid, wl.batch, ksize)
+    ref = oc.submconv_rows(kmap, op.bf16_bits_to_float64(fb), op.bf16_bits_to_float64(Wb),
+                           wl.layers[0].bias)
+    _assert_close(_bf16_values(out), ref, f"bf16 {cin}->{cout}")
+    km.free()
+
+
+@gpu
+def test_bf16_c3_sampled_and_input_grad(dev):
+    sc = _sc()
+    wl = workloads.make("c3_128_128")
+    L = wl.layers[0]
+    rng = np.random.default_rng(31)
+    fb = workloads.normal_bf16_bits(rng, (wl.n, L.cin))
+    Wb = workloads.normal_bf16_bits(rng, L.W.shape, std=1.0 / np.sqrt(27 * L.cin))
+    _say(f"[bf16] c3 N={wl.n}")
+    km = sc.build_map(_to(dev, wl.coords), wl.grid, wl.batch)
+    out = sc.forward(km, _bf16_tensor(dev, fb), _bf16_tensor(dev, Wb))
+    rows = np.random.default_rng(4).choice(wl.n, 3000, replace=False)
+    kmap = oc.kernel_map(wl.coords, wl.grid, wl.batch, 3)
+    F, Wd = op.bf16_bits_to_float64(fb), op.bf16_bits_to_float64(Wb)
+    _assert_close(_bf16_values(out)[rows], oc.submconv_rows(kmap, F, Wd, None, rows), "bf16 c3")
+    dx = sc.backward_input(km, _bf16_tensor(dev, fb), _bf16_tensor(dev, Wb))
+    _assert_close(_bf16_values(dx)[rows],
+                  oc.backward_input_rows(wl.coords, wl.grid, wl.batch, 3, F, Wd, rows), "bf16 c3 input grad")
+    km.free()

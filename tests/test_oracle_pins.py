@@ -301,3 +301,14 @@ def test_mutation_dropped_tap_fails_dense_pin():
         km[:, 5] = -1
         return O.submconv(wl.coords, wl.feats, L.W, L.bias, wl.grid, kmap=km)
     assert not _dense_pin_passes(wrong)
+
+
+def test_bf16_decoding_pins():
+    # bfloat16 patterns with known values (the top half of the binary32 pattern)
+    bits = np.array([0x3F80, 0xC000, 0x3F81, 0x0000, 0x8000, 0x4049, 0x7F7F, 0x0001], dtype=np.uint16)
+    exp = [1.0, -2.0, 1.0078125, 0.0, -0.0, 3.140625, 3.3895313892515355e38, 9.183549615799121e-41]
+    np.testing.assert_array_equal(O.bf16_bits_to_float64(bits), np.array(exp))
+    # the generator's rounding: nearest, ties to even, against exact values
+    x = np.array([1.0, 1.00390625, 1.01171875, -3.0, 1.0 + 2 ** -8 + 2 ** -20], dtype=np.float32)
+    r = O.bf16_bits_to_float64(workloads.f32_to_bf16_bits(x))
+    np.testing.assert_array_equal(r, [1.0, 1.0, 1.015625, -3.0, 1.0078125])

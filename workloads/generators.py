@@ -164,6 +164,22 @@ def normal_f16(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
     return x.astype(np.float16)
 
 
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 values rounded to bfloat16 (nearest, ties to even), returned as
+    16-bit patterns (numpy has no bfloat16 type). Finite inputs only."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def normal_bf16_bits(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
+    """N(0, std^2) samples rounded to bfloat16, as 16-bit patterns."""
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return f32_to_bf16_bits(x)
+
+
 @dataclass
 class Layer:
     ksize: int                     # 3 (27 taps) or 1 (1 tap)
