@@ -57,10 +57,12 @@ METRICS = {
     "forward": "SubMConv3d ms/layer + effective TFLOP/s (128^3 grid, C=128, 10% occ)",
     "backward_input": "SubMConv3d input-gradient ms/layer + effective TFLOP/s",
     "backward_weight": "SubMConv3d weight-gradient ms/layer + effective TFLOP/s",
+    "forward_masked": "SubMConv3d masked implicit-GEMM ms/layer + effective TFLOP/s",
     "downsample": "x2 sparse downsample (max) input sites/s",
     "subdivide": "x2 sparse subdivide input sites/s",
 }
 KERNELS = {"forward": "k_fwd_pp", "backward_input": "k_fwd_pp", "backward_weight": "k_bwd_weight",
+           "forward_masked": "k_fwd_masked",
            "downsample": "k_down_max", "subdivide": "k_subdivide"}
 
 
@@ -76,7 +78,7 @@ def algorithmic_bytes(op, n, cin, cout, ksize, has_order, has_bias):
         b += 27 * n * 4
         if has_order:
             b += n * 4
-    if has_bias and op == "forward":
+    if has_bias and op in ("forward", "forward_masked"):
         b += cout * 4
     return b
 
@@ -266,6 +268,18 @@ def main():
 
         def kernel():
             sc.backward_input(km, grad_out, prepared=wp, ksize=L.ksize, cin=L.cin, out=out)
+    elif op == "forward_masked":
+        out = torch.empty((wl.n, L.cout), dtype=torch.float16, device=dev)
+        wp = sc.prepare_weights(W)
+        mplan = sc.masked_plan(km)
+        print(f"[bench] masked plan: {mplan.row_taps} row-taps executed for {pairs} pairs "
+              f"({mplan.row_taps / pairs:.2f}x)", file=sys.stderr, flush=True)
+
+        def step():
+            sc.forward_masked(mplan, feats, bias=bias, prepared=sc.prepare_weights(W), cout=L.cout, out=out)
+
+        def kernel():
+            sc.forward_masked(mplan, feats, bias=bias, prepared=wp, cout=L.cout, out=out)
     else:
         out = torch.empty((27 if L.ksize == 3 else 1, L.cin, L.cout), dtype=torch.float32, device=dev)
 
@@ -323,7 +337,7 @@ def main():
         times = []
         for _ in range(2):
             t = time.perf_counter()
-            if op == "forward":
+            if op in ("forward", "forward_masked"):
                 oc.submconv_rows(kmap, wl.feats, L.W, L.bias)
             elif op == "backward_input":
                 oc.backward_input_rows(wl.coords, wl.grid, wl.batch, L.ksize, g_np, L.W)
@@ -331,7 +345,7 @@ def main():
                 oc.backward_weight(kmap, wl.feats, g_np)
             times.append(time.perf_counter() - t)
         conv_s = min(times)
-        what = {"forward": "conv", "backward_input": "input gradient",
+        what = {"forward": "conv", "forward_masked": "conv", "backward_input": "input gradient",
                 "backward_weight": "weight gradient"}[op]
         cpu = {"value": round(flops / conv_s / 1e12, 6), "unit": "TFLOP/s", "cores": oc.num_threads(),
                "kind": "oracle",
@@ -340,6 +354,9 @@ def main():
                          f"map {map_s * 1e3:.0f} ms"}
         print(f"[bench] cpu oracle {what} {conv_s:.2f} s", file=sys.stderr, flush=True)
 
+    extra = {}
+    if op == "forward_masked":
+        extra = {"masked_row_taps": mplan.row_taps, "padding_factor": round(mplan.row_taps / pairs, 3)}
     rec = {
         "metric": METRICS[op],
         "value": round(flops / (ms_step * 1e-3) / 1e12, 4),
@@ -355,7 +372,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.config}: SubMConv3d {L.ksize}x{L.ksize}x{L.ksize}, grid {wl.grid[0]}^3, "
                                f"batch {wl.batch}, N={wl.n}, Cin={L.cin}, Cout={L.cout}, warm kernel map",
-                   "op": op, "active_pairs": pairs, "morton": bool(args.morton),
+                   "op": op, "active_pairs": pairs, "morton": bool(args.morton), **extra,
                    "map_lookup": "sorted keys" if args.sorted_keys else "hash"},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
@@ -367,6 +384,8 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+    if op == "forward_masked":
+        mplan.free()
     km.free()
     return 0
 

@@ -248,6 +248,44 @@ int submconv_backward_bias(const uint16_t* grad_out, int64_t n, int32_t cout, fl
                            hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Masked implicit-GEMM forward: the variant the trellis-mac issue #1 thread
+ * measures against its dense kernel ("Fixed" list and the dense-vs-masked
+ * table). Rows are sorted by their 27-bit neighbour mask (sorted_idx); each
+ * block of 64 sorted rows runs the taps in the union of its rows' masks
+ * (valid_kernel / valid_kernel_seg), every row taking part with zeros where
+ * its neighbour is absent. Same result as submconv_forward (fp32
+ * accumulation, one rounding), different cost: fp32 accumulators in
+ * registers, but each tap padded to the block.
+ * ---------------------------------------------------------------------- */
+
+typedef struct submconv_masked_s* submconv_masked_t;
+
+/*
+ * submconv_masked_plan -- sort the map's rows by neighbour mask and build the
+ * per-block tap lists and neighbour tables (about 4 bytes per (block row, run
+ * tap)). Builds on `stream` and waits for it twice; allocates device memory.
+ * The plan refers to `map`'s buffers: free it before the map.
+ */
+int submconv_masked_plan(submconv_map_t map, hipStream_t stream, submconv_masked_t* out_plan);
+
+/* (row, tap) products the masked forward executes, padding included
+ * (64 x the number of block taps); negative on a bad argument. */
+int64_t submconv_masked_row_taps(submconv_masked_t plan);
+
+/*
+ * submconv_forward_masked -- the masked forward of a 3x3x3 layer: arguments as
+ * submconv_forward (fp16, prepared weights for (3, Cin, Cout)); Cin in
+ * {32, 64, 128} with Cout a multiple of 32, or Cin 256 with Cout a multiple of
+ * 128. Asynchronous, no allocation, bitwise reproducible.
+ */
+int submconv_forward_masked(submconv_masked_t plan, const uint16_t* feats, const uint16_t* Wp,
+                            const float* bias, uint16_t* out, int32_t cin, int32_t cout,
+                            hipStream_t stream);
+
+/* Release a masked plan (waits for the device). NULL is a no-op. */
+int submconv_masked_free(submconv_masked_t plan);
+
+/* ------------------------------------------------------------------------
  * Coordinate operations of the same sparse stack (trellis_sparse_mlx README,
  * "What's in it" table, subdivide / downsample row): x2 max-pooling and x2
  * coordinate expansion.

@@ -25,7 +25,8 @@ import torch
 __all__ = [
     "SubmconvError", "KernelMap", "build_map", "prepare_weights", "forward", "backward_input",
     "backward_weight", "backward_bias", "SubMConv3dFunction", "SubMConv3d", "library_path", "load_library",
-    "abi_version", "FLAG_MORTON", "downsample", "subdivide",
+    "abi_version", "FLAG_MORTON", "downsample", "subdivide", "MaskedPlan", "masked_plan",
+    "forward_masked",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -79,6 +80,10 @@ def load_library():
         "submconv_downsample_max": ([P, P, I32, P, P], ctypes.c_int),
         "submconv_downsample_free": ([P], ctypes.c_int),
         "submconv_subdivide": ([P, I64, P, I32, P, P, P], ctypes.c_int),
+        "submconv_masked_plan": ([P, P, P], ctypes.c_int),
+        "submconv_masked_row_taps": ([P], I64),
+        "submconv_forward_masked": ([P, P, P, P, P, I32, I32, P], ctypes.c_int),
+        "submconv_masked_free": ([P], ctypes.c_int),
         "submconv_forward": ([P, P, P, P, P, I32, I32, I32, P], ctypes.c_int),
         "submconv_forward_dtype": ([P, P, P, P, P, I32, I32, I32, I32, P], ctypes.c_int),
         "submconv_backward_input_dtype": ([P, P, P, P, I32, I32, I32, I32, P], ctypes.c_int),
@@ -336,6 +341,64 @@ def backward_bias(grad_out: torch.Tensor) -> torch.Tensor:
         _check(load_library().submconv_backward_bias(_ptr(grad_out), grad_out.shape[0],
                                                      grad_out.shape[1], _ptr(out),
                                                      _stream(grad_out.device)))
+    return out
+
+
+class MaskedPlan:
+    """Handle of a masked implicit-GEMM plan built on a map (rows sorted by
+    neighbour mask, per-block tap lists); free it before the map."""
+
+    def __init__(self, handle, kmap: KernelMap):
+        self._h = handle
+        self.kmap = kmap
+        self.row_taps = int(load_library().submconv_masked_row_taps(handle))
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise SubmconvError(-1, "plan already freed")
+        return self._h
+
+    def free(self) -> None:
+        if self._h is not None and _lib is not None:
+            _check(_lib.submconv_masked_free(self._h))
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def masked_plan(kmap: KernelMap) -> MaskedPlan:
+    """Builds the masked implicit-GEMM plan of a map (waits for the stream)."""
+    h = ctypes.c_void_p()
+    with torch.cuda.device(kmap.device):
+        _check(load_library().submconv_masked_plan(kmap.handle, _stream(kmap.device), ctypes.byref(h)))
+    return MaskedPlan(h, kmap)
+
+
+def forward_masked(plan: MaskedPlan, feats: torch.Tensor, W: Optional[torch.Tensor] = None,
+                   bias: Optional[torch.Tensor] = None, *, prepared: Optional[torch.Tensor] = None,
+                   cout: Optional[int] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The 3x3x3 forward by the masked implicit GEMM (fp16); same result as
+    :func:`forward` up to the order of the fp32 additions."""
+    _require(feats, "feats", torch.float16, 2)
+    cin = feats.shape[1]
+    if prepared is None:
+        if W is None or W.shape[0] != 27:
+            raise ValueError("pass W [27,Cin,Cout] or prepared")
+        cout = W.shape[2]
+        prepared = prepare_weights(W)
+    elif cout is None:
+        raise ValueError("with prepared weights, pass cout")
+    if out is None:
+        out = torch.empty((feats.shape[0], cout), dtype=torch.float16, device=feats.device)
+    with torch.cuda.device(feats.device):
+        _check(load_library().submconv_forward_masked(plan.handle, _ptr(feats), _ptr(prepared),
+                                                      _ptr(bias), _ptr(out), cin, int(cout),
+                                                      _stream(feats.device)))
     return out
 
 

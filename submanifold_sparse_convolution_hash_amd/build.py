@@ -12,7 +12,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsubmconv.so")
-SOURCES = ["map_build.hip", "forward.hip", "backward.hip", "coord_ops.hip"]
+SOURCES = ["map_build.hip", "forward.hip", "backward.hip", "coord_ops.hip", "masked.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++20", "-fPIC", "-Wall",

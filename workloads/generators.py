@@ -261,6 +261,14 @@ def make(name: str) -> Workload:
                                 bias_kind="normal", name=name)
     if name == "c3_128_128":
         return uniform_workload(128, 209715, [(3, 128, 128)], seed=3, bias_kind=None, name=name)
+    # the 128^3 / C=128 layer at 1 % and 30 % occupancy (the masked-GEMM
+    # comparison's other occupancies)
+    if name == "c3_occ1":
+        return uniform_workload(128, round(0.01 * 128 ** 3), [(3, 128, 128)], seed=31, bias_kind=None,
+                                name=name)
+    if name == "c3_occ30":
+        return uniform_workload(128, round(0.30 * 128 ** 3), [(3, 128, 128)], seed=33, bias_kind=None,
+                                name=name)
     if name == "c4_256_shell":
         return shell_workload(256, 100.0, 15.0, [40, 41], [(3, 256, 256)], seed=4, name=name)
     if name == "c5_512_chain":
