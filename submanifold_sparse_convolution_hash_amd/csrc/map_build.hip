@@ -121,47 +121,55 @@ __global__ void k_insert(const uint64_t* __restrict__ keys, int64_t n, uint64_t*
   }
 }
 
+// One thread per (tap k, processing row t), t fastest (coalesced writes of
+// the tap-major map, 27 independent probes in flight per row).
 __global__ void k_query(const int32_t* __restrict__ coords, const int32_t* __restrict__ order,
                         int64_t n, int32_t g0, int32_t g1, int32_t g2,
                         const uint64_t* __restrict__ tkeys, const int32_t* __restrict__ tvals,
-                        uint64_t mask, int32_t* __restrict__ nbr,
-                        unsigned long long* __restrict__ pairs) {
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  int hits = 0;
-  if (t < n) {
+                        uint64_t mask, int32_t* __restrict__ nbr) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx < n * kTaps3) {
+    const int k = static_cast<int>(idx / n);
+    const int64_t t = idx - static_cast<int64_t>(k) * n;
     const int64_t i = order ? order[t] : t;
     const int32_t b = coords[4 * i + 0];
-    const int32_t x = coords[4 * i + 1];
-    const int32_t y = coords[4 * i + 2];
-    const int32_t z = coords[4 * i + 3];
-#pragma unroll 1
-    for (int k = 0; k < kTaps3; ++k) {
-      const int32_t nx = x + (k / 9) - 1;
-      const int32_t ny = y + ((k / 3) % 3) - 1;
-      const int32_t nz = z + (k % 3) - 1;
-      int32_t j = -1;
-      if (k == kCenterTap) {
-        j = static_cast<int32_t>(i);
-      } else if (nx >= 0 && nx < g0 && ny >= 0 && ny < g1 && nz >= 0 && nz < g2) {
-        const uint64_t key = pack_key(b, nx, ny, nz, g0, g1, g2);
-        uint64_t h = mix64(key) & mask;
-        while (true) {
-          const uint64_t s = tkeys[h];
-          if (s == key) {
-            j = tvals[h];
-            break;
-          }
-          if (s == kEmpty) break;
-          h = (h + 1) & mask;
+    const int32_t nx = coords[4 * i + 1] + (k / 9) - 1;
+    const int32_t ny = coords[4 * i + 2] + ((k / 3) % 3) - 1;
+    const int32_t nz = coords[4 * i + 3] + (k % 3) - 1;
+    int32_t j = -1;
+    if (k == kCenterTap) {
+      j = static_cast<int32_t>(i);
+    } else if (nx >= 0 && nx < g0 && ny >= 0 && ny < g1 && nz >= 0 && nz < g2) {
+      const uint64_t key = pack_key(b, nx, ny, nz, g0, g1, g2);
+      uint64_t h = mix64(key) & mask;
+      while (true) {
+        const uint64_t s = tkeys[h];
+        if (s == key) {
+          j = tvals[h];
+          break;
         }
+        if (s == kEmpty) break;
+        h = (h + 1) & mask;
       }
-      nbr[static_cast<int64_t>(k) * n + t] = j;
-      hits += (j >= 0);
     }
+    nbr[idx] = j;
   }
-  // wave-level sum, one atomic per wave
-  for (int off = 32; off > 0; off >>= 1) hits += __shfl_down(hits, off, 64);
-  if ((threadIdx.x & 63) == 0 && hits) atomicAdd(pairs, static_cast<unsigned long long>(hits));
+}
+
+// Sum of the per-tile entry counts in 64 bits (the active pairs): one
+// workgroup, fixed order, no atomics.
+__global__ __launch_bounds__(1024) void k_total(const int32_t* __restrict__ tile_tot, int64_t n_tiles,
+                                                unsigned long long* __restrict__ total) {
+  __shared__ unsigned long long part[1024];
+  unsigned long long s = 0;
+  for (int64_t i = threadIdx.x; i < n_tiles; i += 1024) s += static_cast<unsigned long long>(tile_tot[i]);
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if (static_cast<int>(threadIdx.x) < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *total = part[0];
 }
 
 // Sorted-key builder (the packing + sort + search lookup of "Running
@@ -178,9 +186,8 @@ __global__ void k_sorted_dups(const uint64_t* __restrict__ skeys, int64_t n, uin
 __global__ void k_query_sorted(const int32_t* __restrict__ coords, const int32_t* __restrict__ order,
                                int64_t n, int32_t g0, int32_t g1, int32_t g2,
                                const uint64_t* __restrict__ skeys, const int32_t* __restrict__ srows,
-                               int32_t* __restrict__ nbr, unsigned long long* __restrict__ pairs) {
+                               int32_t* __restrict__ nbr) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  int hit = 0;
   if (idx < n * kTaps3) {
     const int k = static_cast<int>(idx / n);
     const int64_t t = idx - static_cast<int64_t>(k) * n;
@@ -202,10 +209,7 @@ __global__ void k_query_sorted(const int32_t* __restrict__ coords, const int32_t
       if (lo < n && skeys[lo] == key) j = srows[lo];
     }
     nbr[idx] = j;
-    hit = j >= 0;
   }
-  const unsigned long long m = __ballot(hit);
-  if ((threadIdx.x & 63) == 0 && m) atomicAdd(pairs, static_cast<unsigned long long>(__popcll(m)));
 }
 
 // Per tile of kTileRows processing rows: entries per processing position
@@ -475,12 +479,11 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   if (sorted_keys) {
     k_query_sorted<<<grid_for(n * kTaps3, B), B, 0, stream>>>(
         coords, order, n, grid[0], grid[1], grid[2], static_cast<const uint64_t*>(skeys.p),
-        static_cast<const int32_t*>(srows.p), nbr, pairs);
+        static_cast<const int32_t*>(srows.p), nbr);
   } else {
-    k_query<<<grid_for(n, B), B, 0, stream>>>(coords, order, n, grid[0], grid[1], grid[2],
+    k_query<<<grid_for(n * kTaps3, B), B, 0, stream>>>(coords, order, n, grid[0], grid[1], grid[2],
                                               static_cast<const uint64_t*>(tkeys.p),
-                                              static_cast<const int32_t*>(tvals.p), mask, nbr,
-                                              pairs);
+                                              static_cast<const int32_t*>(tvals.p), mask, nbr);
   }
   BUILD_CHECK(hipGetLastError());
 
@@ -503,6 +506,9 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
                                         tile_off, 0, static_cast<size_t>(n_tiles + 1),
                                         rocprim::plus<int32_t>(), stream));
   }
+  // the active pairs in 64 bits (the int32 offsets are checked against it)
+  k_total<<<1, 1024, 0, stream>>>(static_cast<const int32_t*>(tile_tot.p), n_tiles, pairs);
+  BUILD_CHECK(hipGetLastError());
 
   uint64_t host_small[2] = {};
   BUILD_CHECK(hipMemcpyAsync(host_small, small.p, sizeof(host_small), hipMemcpyDeviceToHost, stream));
