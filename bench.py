@@ -41,14 +41,14 @@ CSRC = os.path.join(ROOT, "submanifold_sparse_convolution_hash_amd", "csrc")
 # HBM traffic of one launch of an op's dominant kernel from rocprofv3 counter
 # runs of this script (FETCH_SIZE and WRITE_SIZE, KiB per dispatch, averaged
 # over its launches), keyed by (workload, op) and by the SHA-256 of the kernel
-# source they were taken on. Scale factors come from a plain 512 MiB device
+# source's code (comments stripped) they were taken on. Scale factors come from a plain 512 MiB device
 # copy measured in the same runs (--calib-copy-mib 512): its FETCH_SIZE read
 # 262,161 KiB and its WRITE_SIZE 524,288 KiB for 524,288 KiB moved each way.
 # A changed kernel source makes the entry stale and the reported traffic null.
 MEASURED_TRAFFIC = {
     ("c3_128_128", "forward"): {
         "src": "forward.hip",
-        "sha256": "462cc4ae4b48755e9f315aaa2937c63f1e0f51dc658157b50fe0b2c8aa8709ae",
+        "sha256": "2a4c52ec23b1202365875ebc29d2dfa9db38914c4c2dd2cd5c14572227eadf70",
         "fetch_kib": 44887.31, "write_kib": 52428.75,
         "fetch_factor": 524288.0 / 262161.69, "write_factor": 1.0},
 }
@@ -83,15 +83,26 @@ def algorithmic_bytes(op, n, cin, cout, ksize, has_order, has_bias):
     return b
 
 
+def code_sha256(path):
+    """SHA-256 of a source file's code: // comments and blank lines removed,
+    so that editing a comment does not invalidate counters taken on the code."""
+    lines = []
+    with open(path) as f:
+        for line in f:
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
 def measured_traffic(config, op, morton):
     """HBM bytes per launch from the counter table, or None when no entry
-    matches this workload, op and the current kernel source."""
+    matches this workload, op and the current kernel code."""
     t = MEASURED_TRAFFIC.get((config, op))
     if t is None or morton:
         return None
-    with open(os.path.join(CSRC, t["src"]), "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != t["sha256"]:
-            return None
+    if code_sha256(os.path.join(CSRC, t["src"])) != t["sha256"]:
+        return None
     return round((t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"]) * 1024)
 
 

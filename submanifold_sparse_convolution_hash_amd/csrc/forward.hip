@@ -4,33 +4,27 @@
 // [N, K^3*Cin] x [K^3*Cin, Cout] of the trellis_sparse_mlx README
 // ("Performance": one matmul over all taps instead of 2*K^3 dispatches, and a
 // cached gather index). The accumulator stays fp32 and the tile operands are
-// fp16 (the mixed-precision shape of the "Fixed" list of the trellis-mac
-// issue #1 thread); the absent-neighbour skip generalises that thread's
-// skip-empty-V vote to single rows.
+// fp16 or bf16 (the mixed-precision shape of the "Fixed" list of the
+// trellis-mac issue #1 thread).
 //
-// Design of the MFMA kernel (one workgroup = one tile of 256 output rows x
-// COUT_T output columns; nothing is shared between workgroups, no atomics):
+// One workgroup = one tile of 256 output rows (in the map's processing
+// order) x COUT_T output columns; nothing is shared between workgroups and
+// there are no atomics:
 //   * The map holds, per tile, the neighbours of every tap compacted into a
-//     list of {neighbour row, row in tile} (built once with the map), so
-//     absent neighbours cost nothing here: only the padding of the last
-//     16-row group of a tap is multiplied by zeros.
-//   * Each wave owns COUT_T/NW output columns and walks all 16-row groups of
-//     the tile (centre tap first, then taps 0..26, in list order). For a group
-//     it gathers the 16 feature rows straight into MFMA B fragments
-//     (contiguous 16-byte loads per lane), multiplies them with the tap's
-//     weight fragments on v_mfma_f32_16x16x32_f16 (fp32 accumulate) and adds
-//     the 16x16 results into an fp32 accumulator tile in LDS. The centre tap
-//     initialises the accumulator with the bias, later taps read-modify-write
-//     it; rows are unique within a tap and columns are private to a wave, so
-//     there are no conflicts and the order of additions is fixed.
-//   * The group loop is software-pipelined: list entries are fetched PIPE
-//     groups ahead, feature rows and weight fragments (when the tap
-//     changes) PIPE/2 groups ahead.
-//     Feature rows and entries go through buffer loads whose masked lanes
-//     use an out-of-range offset (zeros, no memory traffic) instead of
-//     branches; weight fragments are loaded only when the tap changes.
-//   * Epilogue: one rounding to fp16 (round to nearest even) and coalesced
-//     row stores at the caller's row index.
+//     list of {neighbour row, row in tile}; the tile's steps are the 32-row
+//     groups of those lists (the centre tap first, covering every row), so an
+//     absent neighbour costs nothing.
+//   * A step gathers its 32 feature rows into LDS (16-byte loads, XOR
+//     swizzled), multiplies them on v_mfma_f32_32x32x16_f16 (or _bf16) with
+//     the tap's weights and adds the 32 x COUT_T result to an fp32 accumulator
+//     tile in LDS. Rows are unique within a group and a wave's columns are
+//     its own, so the read-modify-write needs no atomics.
+//   * k_fwd_pp (Cin <= 128) gives each 32-column block two waves that take
+//     the groups in turn; k_fwd_mfma (Cin = 256) has one wave per block.
+//     Both are software pipelined with rings of register buffers unrolled to
+//     static indices, and end every step with an LDS-only fence and barrier.
+//   * Epilogue: bias in fp32, one rounding (round to nearest even), 16-byte
+//     row stores at the caller's row.
 #include <type_traits>
 #include <utility>
 
@@ -427,14 +421,14 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
 //
 // Same tile, schedule, lists and accumulator as k_fwd_mfma, but each 32-column
 // block has two waves that take the groups of the tile in turn. In step f the
-// wave of parity f % 2 multiplies group f (eight MFMAs into fresh registers)
-// while its partner adds the product of group f-1 to the LDS accumulator,
-// reads the B fragments of group f+1 and requests the weights of group f+3.
-// With two waves per SIMD, one wave's MFMAs overlap the other's LDS and
-// address work, and the instruction stream of a step is split between two
-// issuers. Consecutive groups may update the same rows; their updates are in
-// consecutive steps, ordered by the step barrier. All waves share the
-// gathering of feature rows into LDS, as in k_fwd_mfma.
+// wave of parity f % 2 multiplies group f and adds it to its rows of the LDS
+// accumulator (the old rows are requested before the MFMAs, so their latency
+// overlaps them), while its partner reads the B fragments of group f+1 and
+// requests the row indices of group f+1 and the weights of group f+3. With
+// two waves per SIMD the instruction stream of a step has two issuers and one
+// wave's MFMAs overlap the other's LDS and address work. Consecutive groups
+// may update the same rows; their updates are in consecutive steps, ordered
+// by the step barrier. All waves share the gathering of feature rows.
 
 template <int CIN, int COUT_T, bool K3>
 struct CfgPP {
