@@ -661,14 +661,18 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
       store_chunks(i & 1, D[(i + 2) % 4]);
       if constexpr (PAR == (i & 1)) {
         // multiply group f and add it to the accumulator; the old rows are
-        // requested before the MFMAs so that their latency overlaps them
+        // requested before the MFMAs so that their latency overlaps them.
+        // This chain ends the step, so the wave issues ahead of its partner
+        // (whose B-fragment reads would otherwise queue in front in LDS).
         const int r = RW[(i >> 1) & 1];
         float4v old[4];
+        __builtin_amdgcn_s_setprio(3);
         if (!centre_step) read_old(r, old);
         if (centre_step || f < F) {
           const float16v d = multiply(AW[(i >> 1) & 1], BF);
           write_acc(r, centre_step, old, d);
         }
+        __builtin_amdgcn_s_setprio(0);
         load_chunks(E[(i + LB) % 4], D[(i + LB) % 4]);
         load_entries(f + LB + LE, E[(i + LB + LE) % 4]);
       } else {
