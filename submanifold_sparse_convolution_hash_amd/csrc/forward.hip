@@ -7,9 +7,9 @@
 // fp16 or bf16 (the mixed-precision shape of the "Fixed" list of the
 // trellis-mac issue #1 thread).
 //
-// One workgroup = one tile of 256 output rows (in the map's processing
-// order) x COUT_T output columns; nothing is shared between workgroups and
-// there are no atomics:
+// A unit of work is one tile of 256 output rows (in the map's processing
+// order) x COUT_T output columns; nothing is shared between units and there
+// are no atomics:
 //   * The map holds, per tile, the neighbours of every tap compacted into a
 //     list of {neighbour row, row in tile}; the tile's steps are the 32-row
 //     groups of those lists (the centre tap first, covering every row), so an
@@ -20,11 +20,17 @@
 //     tile in LDS. Rows are unique within a group and a wave's columns are
 //     its own, so the read-modify-write needs no atomics.
 //   * k_fwd_pp (Cin <= 128) gives each 32-column block two waves that take
-//     the groups in turn; k_fwd_mfma (Cin = 256) has one wave per block.
+//     the groups in turn, and is persistent: one workgroup per compute unit
+//     walks a run of units with its pipeline running on across them;
+//     k_fwd_mfma (Cin = 256) has one wave per block and one unit per
+//     workgroup.
 //     Both are software pipelined with rings of register buffers unrolled to
 //     static indices, and end every step with an LDS-only fence and barrier.
 //   * Epilogue: bias in fp32, one rounding (round to nearest even), 16-byte
 //     row stores at the caller's row.
+#include <algorithm>
+#include <atomic>
+#include <climits>
 #include <type_traits>
 #include <utility>
 
@@ -429,6 +435,14 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
 // wave's MFMAs overlap the other's LDS and address work. Consecutive groups
 // may update the same rows; their updates are in consecutive steps, ordered
 // by the step barrier. All waves share the gathering of feature rows.
+//
+// The accumulator tile takes most of the LDS, so a compute unit holds one
+// workgroup; the grid is one workgroup per compute unit and each walks every
+// wpx-th unit of its XCD's run. The steps of successive units form one
+// stream: the lookahead reads the next unit's schedule, so that unit's
+// entries, rows, weights and first gathered groups are in flight while the
+// current one finishes and writes its outputs, and only the first unit pays
+// for filling the pipeline.
 
 template <int CIN, int COUT_T, bool K3>
 struct CfgPP {
@@ -466,54 +480,99 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
   __shared__ float4v acc[M * C::NQ];
   __shared__ half8 bt[2][C::GCH];
 
+  // Persistent: the workgroups of an XCD (blockIdx % 8) walk that XCD's
+  // contiguous run of units (row tile, column tile), so neighbouring tiles,
+  // which gather the same feature rows, share an L2; each workgroup takes
+  // every wpx-th unit.
   const int bid = blockIdx.x;
   const int xcd = bid & 7;
-  const int li = bid >> 3;
-  const int tl = li / n_ct;
-  const int ct = li - tl * n_ct;
-  const int tile = xcd * tiles_per_xcd + tl;
-  if (tl >= tiles_per_xcd || tile >= n_tiles) return;
+  const int j0 = bid >> 3;
+  const int wpx = static_cast<int>(gridDim.x >> 3);
+  const int units = tiles_per_xcd * n_ct;
+  // units past the end come last in a workgroup's walk; one that starts
+  // there has nothing to do
+  if (j0 >= units || xcd * tiles_per_xcd + j0 / n_ct >= n_tiles) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int par = w / C::NC;   // the parity of the groups this wave multiplies
   const int wc = w - par * C::NC;
-  const int64_t t0 = static_cast<int64_t>(tile) * M;
-  const int rows_here = static_cast<int>(n - t0 < M ? n - t0 : M);
-  const int c0 = ct * COUT_T;
 
-  // ---- schedule (as in k_fwd_mfma) ----
-  int cnt_p = 0;
-  int ent0 = 0;
-  if (K3) {
-    if (lane < kTaps3) cnt_p = tile_cnt[static_cast<int64_t>(tile) * kTaps3 + lane];
-    ent0 = tile_off[tile];
-  } else {
-    cnt_p = lane == 0 ? rows_here : 0;
-  }
-  const int off_p = excl_scan_wave(cnt_p, lane);
-  const int ng_p = (lane >= 1 && lane < kTaps3) ? (cnt_p + GR - 1) / GR : 0;
-  const int gs_p = NCG + excl_scan_wave(ng_p, lane);
-  const int F = __builtin_amdgcn_readlane(gs_p, kTaps3);
-  struct Grp {
-    int start, cnt, tap;
+  // ---- per-unit schedules ----
+  struct Raw {
+    int cnt, ent0, tile, ct;
   };
-  auto group_of = [&](int f) -> Grp {
-    int p, j;
-    if (f < NCG) {
-      p = 0;
-      j = f;
-    } else {
-      const uint64_t m = __ballot(lane >= 1 && lane < kTaps3 && gs_p <= f);
-      p = __popcll(m);
-      j = f - __builtin_amdgcn_readlane(gs_p, p);
+  auto raw_of = [&](int u) -> Raw {  // issue the loads of unit u's counts
+    Raw r{0, 0, -1, 0};
+    const int tl = u / n_ct;
+    const int tile = xcd * tiles_per_xcd + tl;
+    if (u < units && tl < tiles_per_xcd && tile < n_tiles) {
+      r.tile = tile;
+      r.ct = u - tl * n_ct;
+      if (K3) {
+        if (lane < kTaps3) r.cnt = tile_cnt[static_cast<int64_t>(tile) * kTaps3 + lane];
+        r.ent0 = tile_off[tile];
+      }
     }
+    return r;
+  };
+  // One unit's schedule in lanes 0..31. For processing position p < 27 (the
+  // centre first): cnt entries, the first at off (in the whole list, or the
+  // row in the tile for a 1x1x1 kernel), processed from step gs on (the
+  // centre in NCG steps, then each position in steps of 32 entries). Lane 27
+  // is an empty position at step F, where the unit's steps end; the unit
+  // takes Fp steps (F rounded up to a multiple of 4 past the centre), so that
+  // step residues mod 4 carry over to the next unit. Lanes 28..31 start at
+  // no step.
+  struct Half {
+    int cnt, off, gs;  // per lane
+    int F, Fp, c0, rows_here;
+    int64_t t0;
+  };
+  auto half_of = [&](const Raw& r) -> Half {  // the counts have arrived
+    Half hf;
+    const bool live = r.tile >= 0;
+    hf.t0 = static_cast<int64_t>(live ? r.tile : 0) * M;
+    hf.rows_here = live ? static_cast<int>(n - hf.t0 < M ? n - hf.t0 : M) : 0;
+    hf.c0 = r.ct * COUT_T;
+    hf.cnt = K3 ? (live ? r.cnt : 0) : (lane == 0 ? hf.rows_here : 0);
+    hf.off = excl_scan_wave(hf.cnt, lane) + (K3 ? __builtin_amdgcn_readfirstlane(r.ent0) : 0);
+    const int ng = (lane >= 1 && lane < kTaps3) ? (hf.cnt + GR - 1) / GR : 0;
+    const int gs = NCG + excl_scan_wave(ng, lane);
+    hf.F = live ? __builtin_amdgcn_readlane(gs, kTaps3) : 0;
+    hf.Fp = live ? NCG + ((hf.F - NCG + 3) & ~3) : 0;
+    hf.gs = lane == 0 ? 0 : (lane <= kTaps3 ? gs : INT_MAX);
+    return hf;
+  };
+  struct Grp {
+    int start, cnt, tap, c0;
+    int64_t t0;
+  };
+  // The stream's schedule: the current unit a in lanes 0..31, the next unit b
+  // in lanes 32..63 with its steps counted on from a's last.
+  int s_cnt, s_off, s_gs;
+  auto join = [&](const Half& a, const Half& b) {
+    const int bc = __shfl_xor(b.cnt, 32);
+    const int bo = __shfl_xor(b.off, 32);
+    const int bg = __shfl_xor(b.gs, 32);
+    const bool lo = lane < 32;
+    s_cnt = lo ? a.cnt : bc;
+    s_off = lo ? a.off : bo;
+    s_gs = lo ? a.gs : (bg == INT_MAX ? INT_MAX : bg + a.Fp);
+  };
+  // group of step f: the last lane whose position starts at or before f
+  auto group_at = [&](const Half& a, const Half& b, int f) -> Grp {
+    const uint64_t m = __ballot(s_gs <= f);
+    const int p = 63 - __builtin_clzll(m);
+    const int j = f - __builtin_amdgcn_readlane(s_gs, p);
     Grp g;
-    g.start = __builtin_amdgcn_readlane(off_p, p) + GR * j;
-    const int c = __builtin_amdgcn_readlane(cnt_p, p) - GR * j;
-    g.cnt = f >= F ? 0 : (c < GR ? c : GR);
-    g.tap = K3 ? tap_at(p) : 0;
+    g.start = __builtin_amdgcn_readlane(s_off, p) + GR * j;
+    const int c = __builtin_amdgcn_readlane(s_cnt, p) - GR * j;
+    g.cnt = c < GR ? c : GR;  // <= 0 past the position's entries
+    g.tap = K3 ? tap_at(p & 31) : 0;
+    g.c0 = p < 32 ? a.c0 : b.c0;
+    g.t0 = p < 32 ? a.t0 : b.t0;
     return g;
   };
 
@@ -535,15 +594,14 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
     lcol[i] = static_cast<uint32_t>(lc * 16);
     lpos[i] = lrow[i] * RC + (lc ^ (lrow[i] & (RC - 1)));
   }
-  auto load_entries = [&](int f, int2 (&E)[CPT]) {
-    const Grp g = group_of(f);
+  auto load_entries = [&](const Grp& g, int2 (&E)[CPT]) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const bool live = loader && lrow[i] < g.cnt;
       if (K3) {
-        E[i] = bload_i2(re, live ? static_cast<uint32_t>(ent0 + g.start + lrow[i]) * 8u : e_none);
+        E[i] = bload_i2(re, live ? static_cast<uint32_t>(g.start + lrow[i]) * 8u : e_none);
       } else {
-        E[i].x = static_cast<int>(t0) + g.start + lrow[i];
+        E[i].x = static_cast<int>(g.t0) + g.start + lrow[i];
         E[i].y = live ? g.start + lrow[i] : -1;
       }
     }
@@ -559,20 +617,18 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
       for (int i = 0; i < CPT; ++i) bt[slot][lpos[i]] = D[i];
     }
   };
-  auto load_row = [&](int f) -> int {
-    const Grp g = group_of(f);
+  auto load_row = [&](const Grp& g) -> int {
     const int sl = lane & 31;
-    if (K3) return bload_i2(re, sl < g.cnt ? static_cast<uint32_t>(ent0 + g.start + sl) * 8u : e_none).y;
+    if (K3) return bload_i2(re, sl < g.cnt ? static_cast<uint32_t>(g.start + sl) * 8u : e_none).y;
     return sl < g.cnt ? g.start + sl : -1;
   };
 
   // ---- MFMA role (fragment layouts as in k_fwd_mfma) ----
   const int s32 = lane & 31;
   const int h = lane >> 5;
-  const int cwb = c0 + wc * 32;
   const int qw = wc * 8;
-  auto load_a = [&](int f, half8 (&A)[KS]) {
-    const Grp g = group_of(f);
+  auto load_a = [&](const Grp& g, half8 (&A)[KS]) {
+    const int cwb = g.c0 + wc * 32;
     const uint32_t base =
         static_cast<uint32_t>(((g.tap * (cout / 32) + (cwb >> 5)) * KS) * 1024 + lane * 16);
 #pragma unroll
@@ -622,31 +678,42 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
   };
 
   // ---- pipeline ----
+  // The steps of this workgroup's units form one stream: a step's lookahead
+  // past the end of the current unit reads the next unit's schedule, so the
+  // next unit's entries, rows, weights and first gathered groups are in
+  // flight while the current one finishes and writes its epilogue.
   // Loader: group g's entries in step g-LB-LE, chunks in step g-LB, stored
   // to slot g%2 in step g-2. A wave multiplies the groups g of its parity:
   // weights requested in step g-3 (set (g/2)%2), B fragments and row indices
-  // in step g-1, multiply in step g, update in step g+1.
-  // The whole pipeline is instantiated once per parity, so that every wave's
-  // roles, and with them its memory-counter waits, are static.
+  // in step g-1; in step g it multiplies g and adds it to its rows.
+  // The pipeline is instantiated once per parity, so that every wave's roles,
+  // and with them its memory-counter waits, are static.
   auto run = [&](auto parc) {
     constexpr int PAR = decltype(parc)::value;
+    int u = j0;
+    Half cur = half_of(raw_of(u));
+    Half nxt = half_of(raw_of(u + wpx));
+    Raw raw = raw_of(u + 2 * wpx);
+    join(cur, nxt);
+    auto grp = [&](int f) -> Grp { return group_at(cur, nxt, f); };
+
     int2 E[4][CPT];
     half8 D[4][CPT];
     int RW[2];
     half8 AW[2][KS];
     half8 BF[KS];
 #pragma unroll
-    for (int g = 0; g < LB; ++g) load_entries(g, E[g % 4]);
+    for (int g = 0; g < LB; ++g) load_entries(grp(g), E[g % 4]);
 #pragma unroll
     for (int g = 0; g < LB; ++g) load_chunks(E[g % 4], D[g % 4]);
 #pragma unroll
-    for (int g = LB; g < LB + LE; ++g) load_entries(g, E[g % 4]);
+    for (int g = LB; g < LB + LE; ++g) load_entries(grp(g), E[g % 4]);
     if (PAR == 0) {
-      load_a(0, AW[0]);
-      load_a(2, AW[1]);
-      RW[0] = load_row(0);
+      load_a(grp(0), AW[0]);
+      load_a(grp(2), AW[1]);
+      RW[0] = load_row(grp(0));
     } else {
-      load_a(1, AW[0]);
+      load_a(grp(1), AW[0]);
     }
     store_chunks(0, D[0]);
     store_chunks(1, D[1]);
@@ -654,7 +721,7 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
     if (PAR == 0) read_b(0, BF);
     lds_barrier();
 
-    // step f; i = f mod 4
+    // step f of the current unit; i = f mod 4
     auto step = [&](int f, auto ic, auto cc) {
       constexpr int i = decltype(ic)::value;
       constexpr bool centre_step = decltype(cc)::value;
@@ -668,39 +735,48 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
         float4v old[4];
         __builtin_amdgcn_s_setprio(3);
         if (!centre_step) read_old(r, old);
-        if (centre_step || f < F) {
+        if (centre_step || f < cur.F) {
           const float16v d = multiply(AW[(i >> 1) & 1], BF);
           write_acc(r, centre_step, old, d);
         }
         __builtin_amdgcn_s_setprio(0);
         load_chunks(E[(i + LB) % 4], D[(i + LB) % 4]);
-        load_entries(f + LB + LE, E[(i + LB + LE) % 4]);
+        load_entries(grp(f + LB + LE), E[(i + LB + LE) % 4]);
       } else {
         // prepare this wave's next group, f+1
         read_b((i + 1) & 1, BF);
         load_chunks(E[(i + LB) % 4], D[(i + LB) % 4]);
-        load_entries(f + LB + LE, E[(i + LB + LE) % 4]);
-        RW[((i + 1) >> 1) & 1] = load_row(f + 1);
-        load_a(f + 3, AW[((i + 3) >> 1) & 1]);
+        load_entries(grp(f + LB + LE), E[(i + LB + LE) % 4]);
+        RW[((i + 1) >> 1) & 1] = load_row(grp(f + 1));
+        load_a(grp(f + 3), AW[((i + 3) >> 1) & 1]);
       }
       lds_barrier();
     };
-    [&]<int... I>(std::integer_sequence<int, I...>) {
-      (step(I, std::integral_constant<int, I % 4>{}, std::true_type{}), ...);
-    }(std::make_integer_sequence<int, NCG>{});
-    // steps NCG..F-1
-    for (int f0 = NCG; f0 < F; f0 += 4) {
+    while (true) {
       [&]<int... I>(std::integer_sequence<int, I...>) {
-        (step(f0 + I, std::integral_constant<int, (NCG + I) % 4>{}, std::false_type{}), ...);
-      }(std::make_integer_sequence<int, 4>{});
+        (step(I, std::integral_constant<int, I % 4>{}, std::true_type{}), ...);
+      }(std::make_integer_sequence<int, NCG>{});
+      for (int f0 = NCG; f0 < cur.Fp; f0 += 4) {
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+          (step(f0 + I, std::integral_constant<int, (NCG + I) % 4>{}, std::false_type{}), ...);
+        }(std::make_integer_sequence<int, 4>{});
+      }
+      // the last step's barrier made every update visible
+      store_tile<COUT_T, C::NT, K3, IS_BF16>(acc, cur.rows_here, tid, bias, cur.c0, order, cur.t0,
+                                             out, cout);
+      if (nxt.F == 0) break;
+      lds_barrier();  // the epilogue's reads are done before the next centre writes
+      cur = nxt;
+      nxt = half_of(raw);
+      join(cur, nxt);
+      u += wpx;
+      raw = raw_of(u + 2 * wpx);
     }
   };
   if (par == 0)
     run(std::integral_constant<int, 0>{});
   else
     run(std::integral_constant<int, 1>{});
-  __syncthreads();
-  store_tile<COUT_T, C::NT, K3, IS_BF16>(acc, rows_here, tid, bias, c0, order, t0, out, cout);
 }
 
 // ---------------------------------------------------------------------------
@@ -817,6 +893,23 @@ int check_shape(int32_t ksize, int32_t cin, int32_t cout) {
   return SUBMCONV_OK;
 }
 
+// compute units per XCD of the current device (MI355X: 256 / 8), cached per
+// device
+int cus_per_xcd() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 32;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int cus = 256;
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    v = std::max(1, cus / 8);
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
 template <int CIN, int COUT_T, bool K3, bool IS_BF16>
 int launch_one(const Map& m, const _Float16* feats, const _Float16* wp, const float* bias,
                _Float16* out, int cout, hipStream_t stream) {
@@ -829,7 +922,11 @@ int launch_one(const Map& m, const _Float16* feats, const _Float16* wp, const fl
   const int64_t blocks = int64_t{8} * tiles_per_xcd * n_ct;
   const int n_pairs = static_cast<int>(K3 ? m.active_pairs : 0);
   if constexpr (CIN <= 128) {
-    k_fwd_pp<CIN, COUT_T, K3, IS_BF16><<<static_cast<unsigned>(blocks), CfgPP<CIN, COUT_T, K3>::NT, 0,
+    // persistent: one workgroup per CU (the accumulator tile fills its LDS),
+    // dealt evenly to the 8 XCDs
+    const int64_t units_per_xcd = int64_t{tiles_per_xcd} * n_ct;
+    const int64_t wpx = std::min<int64_t>(units_per_xcd, cus_per_xcd());
+    k_fwd_pp<CIN, COUT_T, K3, IS_BF16><<<static_cast<unsigned>(8 * wpx), CfgPP<CIN, COUT_T, K3>::NT, 0,
                                     stream>>>(
         K3 ? m.ent : nullptr, K3 ? m.tile_off : nullptr, K3 ? m.tile_cnt : nullptr,
         K3 ? m.order : nullptr, m.n, feats, wp, bias, out, cout, n_tiles, n_ct, tiles_per_xcd,
