@@ -524,9 +524,10 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
   // is an empty position at step F, where the unit's steps end; the unit
   // takes Fp steps (F rounded up to a multiple of 4 past the centre), so that
   // step residues mod 4 carry over to the next unit. Lanes 28..31 start at
-  // no step.
+  // no step. wb is the byte offset of the position's weights for the
+  // unit's column tile.
   struct Half {
-    int cnt, off, gs;  // per lane
+    int cnt, off, gs, wb;  // per lane
     int F, Fp, c0, rows_here;
     int64_t t0;
   };
@@ -543,35 +544,41 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
     hf.F = live ? __builtin_amdgcn_readlane(gs, kTaps3) : 0;
     hf.Fp = live ? NCG + ((hf.F - NCG + 3) & ~3) : 0;
     hf.gs = lane == 0 ? 0 : (lane <= kTaps3 ? gs : INT_MAX);
+    hf.wb = ((K3 ? tap_at(lane & 31) * (cout / 32) : 0) + r.ct * (COUT_T / 32)) * KS * 1024;
     return hf;
   };
   struct Grp {
-    int start, cnt, tap, c0;
+    int start, cnt, wb;
     int64_t t0;
   };
   // The stream's schedule: the current unit a in lanes 0..31, the next unit b
   // in lanes 32..63 with its steps counted on from a's last.
-  int s_cnt, s_off, s_gs;
+  // Per lane: gs, the first step of the position; offg = off - 32 gs, so
+  // that step f of the position starts at entry offg + 32 f; end = off + cnt;
+  // and wb.
+  int s_gs, s_offg, s_end, s_wb;
   auto join = [&](const Half& a, const Half& b) {
     const int bc = __shfl_xor(b.cnt, 32);
     const int bo = __shfl_xor(b.off, 32);
     const int bg = __shfl_xor(b.gs, 32);
+    const int bw = __shfl_xor(b.wb, 32);
     const bool lo = lane < 32;
-    s_cnt = lo ? a.cnt : bc;
-    s_off = lo ? a.off : bo;
+    const int cnt = lo ? a.cnt : bc;
+    const int off = lo ? a.off : bo;
     s_gs = lo ? a.gs : (bg == INT_MAX ? INT_MAX : bg + a.Fp);
+    s_offg = s_gs == INT_MAX ? 0 : off - GR * s_gs;
+    s_end = off + cnt;
+    s_wb = lo ? a.wb : bw;
   };
   // group of step f: the last lane whose position starts at or before f
   auto group_at = [&](const Half& a, const Half& b, int f) -> Grp {
     const uint64_t m = __ballot(s_gs <= f);
     const int p = 63 - __builtin_clzll(m);
-    const int j = f - __builtin_amdgcn_readlane(s_gs, p);
     Grp g;
-    g.start = __builtin_amdgcn_readlane(s_off, p) + GR * j;
-    const int c = __builtin_amdgcn_readlane(s_cnt, p) - GR * j;
+    g.start = __builtin_amdgcn_readlane(s_offg, p) + GR * f;
+    const int c = __builtin_amdgcn_readlane(s_end, p) - g.start;
     g.cnt = c < GR ? c : GR;  // <= 0 past the position's entries
-    g.tap = K3 ? tap_at(p & 31) : 0;
-    g.c0 = p < 32 ? a.c0 : b.c0;
+    g.wb = __builtin_amdgcn_readlane(s_wb, p);
     g.t0 = p < 32 ? a.t0 : b.t0;
     return g;
   };
@@ -628,11 +635,11 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
   const int h = lane >> 5;
   const int qw = wc * 8;
   auto load_a = [&](const Grp& g, half8 (&A)[KS]) {
-    const int cwb = g.c0 + wc * 32;
-    const uint32_t base =
-        static_cast<uint32_t>(((g.tap * (cout / 32) + (cwb >> 5)) * KS) * 1024 + lane * 16);
+    const uint32_t base = static_cast<uint32_t>(g.wb + wc * KS * 1024 + lane * 16);
+    // one select; the K-step offsets fold into the loads' immediate offsets
+    const uint32_t b = g.cnt > 0 ? base : kOob;
 #pragma unroll
-    for (int st = 0; st < KS; ++st) A[st] = bload_h8(rw, g.cnt > 0 ? base + st * 1024 : kOob);
+    for (int st = 0; st < KS; ++st) A[st] = bload_h8(rw, b + st * 1024);
   };
   int boff[KS];
 #pragma unroll
@@ -655,19 +662,25 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
         d = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[st], B[st], d, 0, 0, 0);
     return d;
   };
-  auto acc_at = [&](int r, int a) { return r * C::NQ + ((qw + 2 * a + h) ^ (r & (C::NQ - 1))); };
+  // chunk qw + 2a + h of row r sits at r*NQ + ((qw + 2a + h) ^ (r % NQ));
+  // qw is a multiple of 8 and 2a + h < 8, so that is a0 ^ 2a with a0 the
+  // slot of a = 0
+  auto acc_at = [&](int a0, int a) { return a0 ^ (2 * a); };
+  auto acc_row = [&](int r) { return r * C::NQ + ((qw + h) ^ (r & (C::NQ - 1))); };
   auto read_old = [&](int r, float4v (&old)[4]) {
     if (r >= 0) {
+      const int a0 = acc_row(r);
 #pragma unroll
-      for (int a = 0; a < 4; ++a) old[a] = acc[acc_at(r, a)];
+      for (int a = 0; a < 4; ++a) old[a] = acc[acc_at(a0, a)];
     }
   };
   auto write_acc = [&](int r, bool centre, const float4v (&old)[4], const float16v& d) {
     if (r >= 0) {
+      const int a0 = acc_row(r);
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const float4v v = {d[4 * a], d[4 * a + 1], d[4 * a + 2], d[4 * a + 3]};
-        acc[acc_at(r, a)] = centre ? v : old[a] + v;
+        acc[acc_at(a0, a)] = centre ? v : old[a] + v;
       }
     }
   };
