@@ -231,7 +231,9 @@ int64_t submconv_backward_weight_workspace_bytes(submconv_map_t map, int32_t cin
  *
  * Enqueues on `stream`, allocates nothing and does not wait. Partial sums
  * are combined in a fixed order, so results are bitwise reproducible.
- * Cin and Cout must be multiples of 8 and at most 1024; 16-byte aligned rows.
+ * Cin and Cout must be multiples of 8 and at most 1024. feats, grad_out,
+ * grad_w and workspace must be 16-byte aligned (SUBMCONV_ERR_INVALID_ARG
+ * otherwise).
  */
 int submconv_backward_weight(submconv_map_t map, const uint16_t* feats, const uint16_t* grad_out,
                              float* grad_w, void* workspace, int32_t cin, int32_t cout,

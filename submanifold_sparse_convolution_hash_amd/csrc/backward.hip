@@ -14,6 +14,10 @@
 // workgroup writes its fp32 partial dW[k] to a workspace; a second kernel
 // adds the partials of a tap in a fixed order, so the result does not depend
 // on scheduling.
+#include <algorithm>
+#include <cmath>
+#include <tuple>
+#include <climits>
 #include <type_traits>
 #include <utility>
 
@@ -28,6 +32,7 @@ typedef float float16v __attribute__((ext_vector_type(16)));
 constexpr int kPairs = 32;          // pairs per group
 constexpr int kRowPad = kPairs + 8; // LDS row (one channel): 32 pairs + 8 halves of padding
 constexpr int kTargetBlocks = 1024; // workgroups to aim for (taps x tile runs)
+constexpr int kGroupsPerBlock = 64; // groups of 32 pairs per workgroup, pipelined kernel
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
@@ -164,6 +169,325 @@ __global__ __launch_bounds__(2 * COUT) void k_bwd_weight(
   (void)n_pairs;
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined weight-gradient kernel for Cin, Cout in {32, 64, 128, 256}
+// ---------------------------------------------------------------------------
+//
+// Same decomposition and partials as k_bwd_weight, restructured as a software
+// pipeline over the groups of 32 pairs of the workgroup's tap. The gathered
+// feature and gradient rows go to LDS as they are (16-byte chunks, XOR
+// swizzled rows); the MFMA operands, 8 consecutive pairs of one channel, are
+// read from those rows with ds_read_b64_tr_b16, which transposes 16 lanes'
+// 4-element row pieces into 4-element column pieces. Group g: list entries
+// requested in step g-5, gradient rows resolved (through the processing
+// order) in step g-3, rows gathered in step g-2, stored to LDS slot g%2 in
+// step g-1, multiplied in step g. Wave (wr, wc) owns input-channel blocks
+// wr*RB.. and output-column blocks wc*CB.. of dW[k] in registers.
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int2 bload_i2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(int2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ int bload_i1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+__device__ __forceinline__ int excl_scan_wave(int v, int lane) {
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x - v;
+}
+
+template <int CIN, int COUT>
+struct PCfg {
+  static constexpr int MB = CIN / 32, NB = COUT / 32;
+  static constexpr int RB = (MB % 4 == 0 && MB * NB > 16) ? 4 : (MB % 2 == 0 ? 2 : 1);
+  static constexpr int CB = NB % 2 == 0 ? 2 : 1;
+  static constexpr int WR = MB / RB, WC = NB / CB;
+  static constexpr int NW = WR * WC;
+  static constexpr int NT = 64 * NW;
+  static constexpr int FC = CIN / 8, YC = COUT / 8;  // 16-byte chunks per row
+  static constexpr int FT = kPairs * FC, YT = kPairs * YC;
+  static constexpr int CF = FT >= NT ? FT / NT : 1;  // chunks per thread, one row each
+  static constexpr int CY = YT >= NT ? YT / NT : 1;
+  static constexpr int NF = FT >= NT ? NT : FT;      // threads that gather
+  static constexpr int NY = YT >= NT ? NT : YT;
+  static constexpr int TW = 64;                      // tiles per schedule window
+  static_assert((CIN == 32 || CIN == 64 || CIN == 128 || CIN == 256) &&
+                    (COUT == 32 || COUT == 64 || COUT == 128 || COUT == 256),
+                "channels");
+  static_assert(FT % NT == 0 || NT % FT == 0, "feature chunk split");
+  static_assert(YT % NT == 0 || NT % YT == 0, "gradient chunk split");
+  static_assert(FC % CF == 0 && YC % CY == 0, "a thread's chunks share a row");
+};
+
+// grid: blocks [0, runs0) take the centre (position 0) in runs of tpr0
+// tiles; block runs0 + r*(K-1) + (kp-1) takes position kp >= 1, tiles
+// [r*tpr, (r+1)*tpr). The centre covers every row, so it gets more runs.
+template <int CIN, int COUT, bool ORD>
+__global__ __launch_bounds__((PCfg<CIN, COUT>::NT)) void k_bwd_weight_pp(
+    const int2* __restrict__ ent, const int32_t* __restrict__ tile_off,
+    const uint16_t* __restrict__ tile_cnt, const int32_t* __restrict__ order, int64_t n,
+    int32_t n_tiles, int32_t K, int32_t runs0, int32_t tpr0, int32_t tpr,
+    const _Float16* __restrict__ feats, const _Float16* __restrict__ grad_out,
+    float* __restrict__ partial, int32_t n_pairs) {
+  using C = PCfg<CIN, COUT>;
+  constexpr int FC = C::FC, YC = C::YC, CF = C::CF, CY = C::CY, RB = C::RB, CB = C::CB;
+  __shared__ half8 fs[2][kPairs * FC];  // feature rows of a group, pair-major
+  __shared__ half8 ys[2][kPairs * YC];  // gradient rows of a group
+
+  const int bid = blockIdx.x;
+  int p, t_begin, t_end;
+  if (bid < runs0) {
+    p = 0;
+    t_begin = bid * tpr0;
+    t_end = min(t_begin + tpr0, n_tiles);
+  } else {
+    const int b = bid - runs0;
+    p = 1 + b % (K - 1);
+    t_begin = (b / (K - 1)) * tpr;
+    t_end = min(t_begin + tpr, n_tiles);
+  }
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = w / C::WC, wc = w - (w / C::WC) * C::WC;
+
+  const __amdgpu_buffer_rsrc_t rf = make_rsrc(feats, static_cast<uint32_t>(n * CIN * 2));
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(grad_out, static_cast<uint32_t>(n * COUT * 2));
+  const __amdgpu_buffer_rsrc_t re = make_rsrc(ent, static_cast<uint32_t>(n_pairs + 1) * 8u);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(order, ORD ? static_cast<uint32_t>(n * 4) : 0u);
+  const uint32_t e_none = static_cast<uint32_t>(n_pairs) * 8u;  // the closing {-1, -1} entry
+
+  // gather roles: CF consecutive chunks of one feature row, CY of one
+  // gradient row
+  const bool gf = tid < C::NF, gy = tid < C::NY;
+  const int pf = (tid * CF) / FC, cf0 = (tid * CF) % FC;
+  const int py = (tid * CY) / YC, cy0 = (tid * CY) % YC;
+
+  float16v acc[RB][CB];
+#pragma unroll
+  for (int a = 0; a < RB; ++a)
+#pragma unroll
+    for (int b = 0; b < CB; ++b) acc[a][b] = float16v{};
+
+  // transposed operand reads: lane (group gq = lane/16, s = lane%16) names
+  // row 8*(gq/2) + 4*r + s/4 and channels 16*(gq%2) + 4*(s%4).. of a 32-row,
+  // 32-channel block; it receives channel 16*(gq%2) + s of rows
+  // 8*(gq/2) + 4*r + 0..3
+  const int gq = lane >> 4, sl = lane & 15;
+  auto tr_addr = [&](int rc, int blk, int kk, int r) {  // in halves, rc chunks per row
+    const int row = 16 * kk + 8 * (gq >> 1) + 4 * r + (sl >> 2);
+    const int ch = 32 * blk + 16 * (gq & 1) + 4 * (sl & 3);
+    return row * rc * 8 + (((ch >> 3) ^ (row & (rc - 1))) << 3) + (((ch >> 2) & 1) << 2);
+  };
+  auto operand = [&](const half8* base, int rc, int blk, int kk) {
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    const _Float16* hb = reinterpret_cast<const _Float16*>(base);
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4s*)(hb + tr_addr(rc, blk, kk, 0)));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4s*)(hb + tr_addr(rc, blk, kk, 1)));
+    return __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto lds_barrier = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+
+  for (int wb = t_begin; wb < t_end; wb += C::TW) {
+    // ---- schedule of this window: lane i holds tile wb + i ----
+    const int nt = min(C::TW, t_end - wb);
+    int cnt = 0, off = 0;
+    if (lane < nt) {
+      const int64_t tb = static_cast<int64_t>(wb + lane) * kTaps3;
+      int before = 0;
+      for (int q = 0; q < p; ++q) before += tile_cnt[tb + q];
+      cnt = tile_cnt[tb + p];  // p = 0: every row of the tile
+      off = tile_off[wb + lane] + before;
+    }
+    const int ng = (cnt + kPairs - 1) / kPairs;
+    const int gsx = excl_scan_wave(ng, lane);
+    const int G = __builtin_amdgcn_readlane(gsx + ng, 63);
+    if (G == 0) continue;
+    const int s_gs = lane < nt ? gsx : INT_MAX;
+    const int s_offg = off - kPairs * gsx;
+    const int s_end = off + cnt;
+    struct Grp {
+      int start, cnt, tile;
+    };
+    auto grp = [&](int g) -> Grp {
+      Grp r{0, 0, wb};
+      if (g < 0) return r;  // before the window: nothing
+      const uint64_t m = __ballot(s_gs <= g);
+      const int i = 63 - __builtin_clzll(m);
+      r.start = __builtin_amdgcn_readlane(s_offg, i) + kPairs * g;
+      const int c = __builtin_amdgcn_readlane(s_end, i) - r.start;
+      r.cnt = c < kPairs ? c : kPairs;  // <= 0 past the window's pairs
+      r.tile = wb + i;
+      return r;
+    };
+
+    // ---- pipeline stages ----
+    // group g: list entries requested in step g-8, rows resolved in step
+    // g-6 (the gradient row through the processing order), rows gathered in
+    // step g-4, stored to LDS slot g%2 in step g-1, multiplied in step g
+    struct Ent {
+      int2 f, y;
+    };
+    struct Rows {
+      int f, y;   // feature row (-1: none), caller row of the gradient row
+      bool ylive;
+    };
+    struct Chunks {
+      half8 f[CF], y[CY];
+    };
+    auto load_entries = [&](const Grp& g) {
+      Ent e;
+      e.f = bload_i2(re, gf && pf < g.cnt ? static_cast<uint32_t>(g.start + pf) * 8u : e_none);
+      if constexpr (C::NF == C::NY && CF * YC == CY * FC) {
+        e.y = e.f;  // the same pair
+      } else {
+        e.y = bload_i2(re, gy && py < g.cnt ? static_cast<uint32_t>(g.start + py) * 8u : e_none);
+      }
+      return e;
+    };
+    auto rows_of = [&](const Ent& e, const Grp& g) {
+      Rows r;
+      r.f = e.f.x;
+      r.ylive = e.y.y >= 0;
+      const int t_row = g.tile * kTileRows + e.y.y;
+      if constexpr (ORD)
+        r.y = bload_i1(ro, r.ylive ? static_cast<uint32_t>(t_row) * 4u : kOob);
+      else
+        r.y = t_row;
+      return r;
+    };
+    auto load_chunks = [&](const Rows& r, Chunks& d) {
+#pragma unroll
+      for (int k = 0; k < CF; ++k)
+        d.f[k] = bload_h8(rf, r.f >= 0 ? static_cast<uint32_t>(r.f) * (CIN * 2) + (cf0 + k) * 16
+                                       : kOob);
+#pragma unroll
+      for (int k = 0; k < CY; ++k)
+        d.y[k] = bload_h8(rg, r.ylive ? static_cast<uint32_t>(r.y) * (COUT * 2) + (cy0 + k) * 16
+                                      : kOob);
+    };
+    auto store_chunks = [&](int slot, const Chunks& d) {
+      if (gf) {
+#pragma unroll
+        for (int k = 0; k < CF; ++k) fs[slot][pf * FC + ((cf0 + k) ^ (pf & (FC - 1)))] = d.f[k];
+      }
+      if (gy) {
+#pragma unroll
+        for (int k = 0; k < CY; ++k) ys[slot][py * YC + ((cy0 + k) ^ (py & (YC - 1)))] = d.y[k];
+      }
+    };
+    auto multiply = [&](int slot) {
+#pragma unroll
+      for (int kk = 0; kk < kPairs / 16; ++kk) {
+        half8 bo[CB];
+#pragma unroll
+        for (int b = 0; b < CB; ++b) bo[b] = operand(ys[slot], YC, wc * CB + b, kk);
+#pragma unroll
+        for (int a = 0; a < RB; ++a) {
+          const half8 ao = operand(fs[slot], FC, wr * RB + a, kk);
+#pragma unroll
+          for (int b = 0; b < CB; ++b)
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ao, bo[b], acc[a][b], 0, 0, 0);
+        }
+      }
+    };
+
+    // the rings start empty (masked entries, no rows); steps -8..-1 fill them
+    Ent E[4];
+    Rows RW[4];
+    Chunks D[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      E[k].f = E[k].y = int2{-1, -1};
+      RW[k] = Rows{-1, 0, false};
+#pragma unroll
+      for (int q = 0; q < CF; ++q) D[k].f[q] = half8{};
+#pragma unroll
+      for (int q = 0; q < CY; ++q) D[k].y[q] = half8{};
+    }
+    auto step = [&](int g, auto ic) {
+      constexpr int i = decltype(ic)::value;                 // g mod 4
+      store_chunks((i + 1) & 1, D[(i + 1) & 3]);             // group g+1
+      if (g >= 0 && g < G) multiply(i & 1);                  // group g, stored last step
+      load_chunks(RW[i], D[i]);                              // group g+4
+      RW[(i + 2) & 3] = rows_of(E[(i + 2) & 3], grp(g + 6)); // group g+6
+      E[i] = load_entries(grp(g + 8));                       // group g+8
+      lds_barrier();
+    };
+    for (int g0 = -8; g0 < G; g0 += 4) {
+      step(g0, std::integral_constant<int, 0>{});
+      step(g0 + 1, std::integral_constant<int, 1>{});
+      step(g0 + 2, std::integral_constant<int, 2>{});
+      step(g0 + 3, std::integral_constant<int, 3>{});
+    }
+  }
+
+  // D: lane holds column 32*cb + lane%32 and channels 32*rb + 8a + 4h + b in
+  // register 4a + b
+  const int h = lane >> 5, s32 = lane & 31;
+  float* dst = partial + static_cast<int64_t>(bid) * CIN * COUT;
+#pragma unroll
+  for (int a = 0; a < RB; ++a)
+#pragma unroll
+    for (int b = 0; b < CB; ++b)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+        for (int b4 = 0; b4 < 4; ++b4) {
+          const int ci = 32 * (wr * RB + a) + 8 * a4 + 4 * h + b4;
+          const int co = 32 * (wc * CB + b) + s32;
+          dst[static_cast<int64_t>(ci) * COUT + co] = acc[a][b][4 * a4 + b4];
+        }
+}
+
+// dW[tap_at(kp)] = the sum of the partials of position kp's blocks (the
+// layout of k_bwd_weight_pp's grid). A workgroup takes 64 float4s of one
+// position; thread (s, c) adds the blocks s, s+4, s+8, ... of float4 c in
+// order, then thread (0, c) adds the four sums in order: a fixed order, so
+// the result does not depend on scheduling.
+__global__ __launch_bounds__(256) void k_bwd_weight_reduce_pp(const float* __restrict__ partial,
+                                                              int runs0, int runs, int K, int cin,
+                                                              int cout, float* __restrict__ dw) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  __shared__ f4 part[4][64];
+  const int64_t per4 = static_cast<int64_t>(cin) * cout / 4;
+  const int64_t chunks = (per4 + 63) / 64;
+  const int kp = static_cast<int>(blockIdx.x / chunks);
+  const int64_t c4 = (blockIdx.x % chunks) * 64 + (threadIdx.x & 63);
+  const int s = threadIdx.x >> 6;
+  const f4* p4 = reinterpret_cast<const f4*>(partial);
+  f4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (c4 < per4) {
+    if (kp == 0) {
+      for (int r = s; r < runs0; r += 4) acc += p4[static_cast<int64_t>(r) * per4 + c4];
+    } else {
+      for (int r = s; r < runs; r += 4)
+        acc += p4[(static_cast<int64_t>(runs0) + static_cast<int64_t>(r) * (K - 1) + kp - 1) * per4 + c4];
+    }
+  }
+  part[s][threadIdx.x & 63] = acc;
+  __syncthreads();
+  if (s == 0 && c4 < per4) {
+    const f4 t = ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) +
+                 part[3][threadIdx.x];
+    const int k = K == kTaps3 ? tap_at(kp) : 0;
+    reinterpret_cast<f4*>(dw)[k * per4 + c4] = t;
+  }
+}
+
 // dW[tap_at(kp)][ci][co] = sum over runs of partial[run][kp][ci][co], runs in order.
 __global__ void k_bwd_weight_reduce(const float* __restrict__ partial, int runs, int K, int cin,
                                     int cout, float* __restrict__ dw) {
@@ -239,30 +563,77 @@ bool use_mfma_w(int cin, int cout) {
   return cin % 32 == 0 && cout % 32 == 0 && cin <= 256 && cout <= 256;
 }
 
+bool use_pp_w(int cin, int cout) {
+  auto ok = [](int c) { return c == 32 || c == 64 || c == 128 || c == 256; };
+  return ok(cin) && ok(cout);
+}
+
+// Work split of a weight gradient: the centre in runs0 runs of tpr0 tiles,
+// each other position in runs runs of tpr tiles (the old kernel: every
+// position in runs runs, runs0 = 0).
 struct Runs {
-  int runs, tpr;
+  int runs, tpr, runs0, tpr0;
+  int blocks(int K) const { return runs0 + (runs0 > 0 ? K - 1 : K) * runs; }
 };
-Runs runs_for(const Map& m, int K) {
+Runs runs_for(const Map& m, int K, int cin, int cout) {
   const int64_t nt = m.n_tiles;
+  auto split = [nt](double groups_per_tile, double target) {
+    int64_t r = static_cast<int64_t>(std::ceil(nt * groups_per_tile / target));
+    r = std::max<int64_t>(1, std::min<int64_t>(r, nt));
+    const int64_t t = (nt + r - 1) / r;
+    return std::pair<int, int>(static_cast<int>((nt + t - 1) / t), static_cast<int>(t));
+  };
+  if (use_pp_w(cin, cout)) {
+    // groups of 32 pairs per tile: 8 for the centre, and for the other
+    // positions their mean pair count over 32, rounded up on average
+    const double off = K == kTaps3 && nt > 0
+                           ? static_cast<double>(m.active_pairs - m.n) / (26.0 * nt) : 0.0;
+    const double g_off = std::max(1.0, off / kPairs + 0.5);
+    Runs r{};
+    std::tie(r.runs0, r.tpr0) = split(kTileRows / kPairs, kGroupsPerBlock);
+    if (K == kTaps3)
+      std::tie(r.runs, r.tpr) = split(g_off, kGroupsPerBlock);
+    else
+      r.runs = r.tpr = 0;
+    return r;
+  }
   int64_t runs = (kTargetBlocks + K - 1) / K;
   if (runs > nt) runs = nt;
   if (runs < 1) runs = 1;
   const int64_t tpr = (nt + runs - 1) / runs;
   runs = (nt + tpr - 1) / tpr;
-  return {static_cast<int>(runs), static_cast<int>(tpr)};
+  return {static_cast<int>(runs), static_cast<int>(tpr), 0, 0};
 }
 
 template <int CIN, int COUT>
 int launch_w(const Map& m, int K, const _Float16* feats, const _Float16* grad_out, float* partial,
              float* dw, hipStream_t stream) {
-  const Runs r = runs_for(m, K);
-  k_bwd_weight<CIN, COUT><<<static_cast<unsigned>(r.runs * K), WCfg<CIN, COUT>::NT, 0, stream>>>(
-      m.ent, m.tile_off, m.tile_cnt, m.order, m.n, static_cast<int32_t>(m.n_tiles), K, r.tpr,
-      feats, grad_out, partial, static_cast<int32_t>(m.active_pairs));
-  SUBMCONV_HIP_CHECK(hipGetLastError());
+  const Runs r = runs_for(m, K, CIN, COUT);
+  const unsigned blocks = static_cast<unsigned>(r.blocks(K));
+  const int32_t nt = static_cast<int32_t>(m.n_tiles), np = static_cast<int32_t>(m.active_pairs);
   const int64_t total = static_cast<int64_t>(K) * CIN * COUT;
-  k_bwd_weight_reduce<<<static_cast<unsigned>((total + 255) / 256), 256, 0, stream>>>(
-      partial, r.runs, K, CIN, COUT, dw);
+  const unsigned rblocks = static_cast<unsigned>((total + 255) / 256);
+  if constexpr ((CIN == 32 || CIN == 64 || CIN == 128 || CIN == 256) &&
+                (COUT == 32 || COUT == 64 || COUT == 128 || COUT == 256)) {
+    constexpr int NT = PCfg<CIN, COUT>::NT;
+    if (m.order)
+      k_bwd_weight_pp<CIN, COUT, true><<<blocks, NT, 0, stream>>>(
+          m.ent, m.tile_off, m.tile_cnt, m.order, m.n, nt, K, r.runs0, r.tpr0, r.tpr, feats,
+          grad_out, partial, np);
+    else
+      k_bwd_weight_pp<CIN, COUT, false><<<blocks, NT, 0, stream>>>(
+          m.ent, m.tile_off, m.tile_cnt, m.order, m.n, nt, K, r.runs0, r.tpr0, r.tpr, feats,
+          grad_out, partial, np);
+    SUBMCONV_HIP_CHECK(hipGetLastError());
+    const int64_t chunks = (int64_t{CIN} * COUT / 4 + 63) / 64;
+    k_bwd_weight_reduce_pp<<<static_cast<unsigned>(K * chunks), 256, 0, stream>>>(
+        partial, r.runs0, r.runs, K, CIN, COUT, dw);
+  } else {
+    k_bwd_weight<CIN, COUT><<<blocks, WCfg<CIN, COUT>::NT, 0, stream>>>(
+        m.ent, m.tile_off, m.tile_cnt, m.order, m.n, nt, K, r.tpr, feats, grad_out, partial, np);
+    SUBMCONV_HIP_CHECK(hipGetLastError());
+    k_bwd_weight_reduce<<<rblocks, 256, 0, stream>>>(partial, r.runs, K, CIN, COUT, dw);
+  }
   SUBMCONV_HIP_CHECK(hipGetLastError());
   return SUBMCONV_OK;
 }
@@ -296,8 +667,8 @@ extern "C" int64_t submconv_backward_weight_workspace_bytes(submconv_map_t map, 
     return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "Cin = %d, Cout = %d", cin, cout);
   if (!use_mfma_w(cin, cout) || map->m.n == 0) return 0;
   const int K = ksize == 3 ? kTaps3 : 1;
-  const Runs r = runs_for(map->m, K);
-  return static_cast<int64_t>(r.runs) * K * cin * cout * static_cast<int64_t>(sizeof(float));
+  const Runs r = runs_for(map->m, K, cin, cout);
+  return static_cast<int64_t>(r.blocks(K)) * cin * cout * static_cast<int64_t>(sizeof(float));
 }
 
 extern "C" int submconv_backward_weight(submconv_map_t map, const uint16_t* feats,
@@ -318,6 +689,8 @@ extern "C" int submconv_backward_weight(submconv_map_t map, const uint16_t* feat
   if ((reinterpret_cast<uintptr_t>(feats) | reinterpret_cast<uintptr_t>(grad_out)) & 15)
     return set_error(SUBMCONV_ERR_INVALID_ARG, "feats and grad_out must be 16-byte aligned");
   if (ws > 0 && !workspace) return set_error(SUBMCONV_ERR_INVALID_ARG, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(grad_w) | reinterpret_cast<uintptr_t>(workspace)) & 15)
+    return set_error(SUBMCONV_ERR_INVALID_ARG, "grad_w and workspace must be 16-byte aligned");
   const _Float16* f = reinterpret_cast<const _Float16*>(feats);
   const _Float16* g = reinterpret_cast<const _Float16*>(grad_out);
   float* part = static_cast<float*>(workspace);
