@@ -935,10 +935,19 @@ int launch_one(const Map& m, const _Float16* feats, const _Float16* wp, const fl
   const int64_t blocks = int64_t{8} * tiles_per_xcd * n_ct;
   const int n_pairs = static_cast<int>(K3 ? m.active_pairs : 0);
   if constexpr (CIN <= 128) {
-    // persistent: one workgroup per CU (the accumulator tile fills its LDS),
+    // persistent: as many workgroups as the CUs hold at once (one per CU
+    // when the accumulator fills the LDS, more for narrow column tiles),
     // dealt evenly to the 8 XCDs
+    static const int per_cu = [] {
+      int nb = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+              &nb, reinterpret_cast<const void*>(k_fwd_pp<CIN, COUT_T, K3, IS_BF16>),
+              CfgPP<CIN, COUT_T, K3>::NT, 0) != hipSuccess)
+        nb = 1;
+      return std::max(1, nb);
+    }();
     const int64_t units_per_xcd = int64_t{tiles_per_xcd} * n_ct;
-    const int64_t wpx = std::min<int64_t>(units_per_xcd, cus_per_xcd());
+    const int64_t wpx = std::min<int64_t>(units_per_xcd, int64_t{cus_per_xcd()} * per_cu);
     k_fwd_pp<CIN, COUT_T, K3, IS_BF16><<<static_cast<unsigned>(8 * wpx), CfgPP<CIN, COUT_T, K3>::NT, 0,
                                     stream>>>(
         K3 ? m.ent : nullptr, K3 ? m.tile_off : nullptr, K3 ? m.tile_cnt : nullptr,
