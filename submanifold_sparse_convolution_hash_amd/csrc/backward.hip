@@ -15,6 +15,7 @@
 // adds the partials of a tap in a fixed order, so the result does not depend
 // on scheduling.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <tuple>
 #include <climits>
@@ -32,7 +33,8 @@ typedef float float16v __attribute__((ext_vector_type(16)));
 constexpr int kPairs = 32;          // pairs per group
 constexpr int kRowPad = kPairs + 8; // LDS row (one channel): 32 pairs + 8 halves of padding
 constexpr int kTargetBlocks = 1024; // workgroups to aim for (taps x tile runs)
-constexpr int kGroupsPerBlock = 64; // groups of 32 pairs per workgroup, pipelined kernel
+constexpr int kBlocksPerCU = 2;     // workgroups per compute unit, pipelined kernel
+constexpr double kGroupsSmall = 64;  // groups per workgroup, pipelined kernel, < 4 waves
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
@@ -203,13 +205,23 @@ __device__ __forceinline__ int excl_scan_wave(int v, int lane) {
   return x - v;
 }
 
+// register tile of a wave: RB x CB blocks of 32 x 32 (input x output channels)
+constexpr int pp_rb(int cin, int cout) {
+  return ((cin / 32) % 4 == 0 && (cin / 32) * (cout / 32) > 16) ? 4 : ((cin / 32) % 2 == 0 ? 2 : 1);
+}
+constexpr int pp_cb(int cout) { return (cout / 32) % 2 == 0 ? 2 : 1; }
+constexpr int pp_waves(int cin, int cout) {
+  return (cin / 32 / pp_rb(cin, cout)) * (cout / 32 / pp_cb(cout));
+}
+
 template <int CIN, int COUT>
 struct PCfg {
   static constexpr int MB = CIN / 32, NB = COUT / 32;
-  static constexpr int RB = (MB % 4 == 0 && MB * NB > 16) ? 4 : (MB % 2 == 0 ? 2 : 1);
-  static constexpr int CB = NB % 2 == 0 ? 2 : 1;
+  static constexpr int RB = pp_rb(CIN, COUT);
+  static constexpr int CB = pp_cb(COUT);
   static constexpr int WR = MB / RB, WC = NB / CB;
   static constexpr int NW = WR * WC;
+  static_assert(NW == pp_waves(CIN, COUT), "wave count");
   static constexpr int NT = 64 * NW;
   static constexpr int FC = CIN / 8, YC = COUT / 8;  // 16-byte chunks per row
   static constexpr int FT = kPairs * FC, YT = kPairs * YC;
@@ -226,33 +238,42 @@ struct PCfg {
   static_assert(FC % CF == 0 && YC % CY == 0, "a thread's chunks share a row");
 };
 
-// grid: blocks [0, runs0) take the centre (position 0) in runs of tpr0
-// tiles; block runs0 + r*(K-1) + (kp-1) takes position kp >= 1, tiles
-// [r*tpr, (r+1)*tpr). The centre covers every row, so it gets more runs.
+// Work split of the pipelined weight gradient. Blocks [0, runs0) take the
+// centre (position 0, every row of a tile) in runs of tpr0 tiles; block
+// runs0 + r*26 + (p-1) takes position p >= 1, tiles [r*tpr, (r+1)*tpr). The
+// positions of one tile range are neighbours in the grid, so blocks that run
+// together gather the same rows and share the L2.
+struct WSplit {
+  int32_t np;  // positions: 27, or 1 for a 1x1x1 kernel
+  int32_t runs0, tpr0, runs, tpr;
+  __host__ __device__ int32_t blocks() const { return runs0 + (np - 1) * runs; }
+  __host__ __device__ int32_t first(int p) const { return p == 0 ? 0 : runs0 + p - 1; }
+  __host__ __device__ int32_t count(int p) const { return p == 0 ? runs0 : runs; }
+  __host__ __device__ int32_t stride(int p) const { return p == 0 ? 1 : np - 1; }
+};
+
 template <int CIN, int COUT, bool ORD>
 __global__ __launch_bounds__((PCfg<CIN, COUT>::NT)) void k_bwd_weight_pp(
     const int2* __restrict__ ent, const int32_t* __restrict__ tile_off,
     const uint16_t* __restrict__ tile_cnt, const int32_t* __restrict__ order, int64_t n,
-    int32_t n_tiles, int32_t K, int32_t runs0, int32_t tpr0, int32_t tpr,
-    const _Float16* __restrict__ feats, const _Float16* __restrict__ grad_out,
-    float* __restrict__ partial, int32_t n_pairs) {
+    int32_t n_tiles, const WSplit ws, const _Float16* __restrict__ feats,
+    const _Float16* __restrict__ grad_out, float* __restrict__ partial, int32_t n_pairs) {
   using C = PCfg<CIN, COUT>;
   constexpr int FC = C::FC, YC = C::YC, CF = C::CF, CY = C::CY, RB = C::RB, CB = C::CB;
   __shared__ half8 fs[2][kPairs * FC];  // feature rows of a group, pair-major
   __shared__ half8 ys[2][kPairs * YC];  // gradient rows of a group
 
   const int bid = blockIdx.x;
-  int p, t_begin, t_end;
-  if (bid < runs0) {
+  int p, t_begin;
+  if (bid < ws.runs0) {
     p = 0;
-    t_begin = bid * tpr0;
-    t_end = min(t_begin + tpr0, n_tiles);
+    t_begin = bid * ws.tpr0;
   } else {
-    const int b = bid - runs0;
-    p = 1 + b % (K - 1);
-    t_begin = (b / (K - 1)) * tpr;
-    t_end = min(t_begin + tpr, n_tiles);
+    const int b = bid - ws.runs0;
+    p = 1 + b % (ws.np - 1);
+    t_begin = (b / (ws.np - 1)) * ws.tpr;
   }
+  const int t_end = min(t_begin + (p == 0 ? ws.tpr0 : ws.tpr), n_tiles);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -453,14 +474,14 @@ __global__ __launch_bounds__((PCfg<CIN, COUT>::NT)) void k_bwd_weight_pp(
         }
 }
 
-// dW[tap_at(kp)] = the sum of the partials of position kp's blocks (the
-// layout of k_bwd_weight_pp's grid). A workgroup takes 64 float4s of one
-// position; thread (s, c) adds the blocks s, s+4, s+8, ... of float4 c in
-// order, then thread (0, c) adds the four sums in order: a fixed order, so
-// the result does not depend on scheduling.
+// dW[tap_at(kp)] = the sum of the partials of position kp's blocks. A
+// workgroup takes 64 float4s of one position; thread (s, c) adds the
+// position's runs s, s+4, s+8, ... for float4 c in order, then thread
+// (0, c) adds the four sums in order: a fixed order, so the result does not
+// depend on scheduling.
 __global__ __launch_bounds__(256) void k_bwd_weight_reduce_pp(const float* __restrict__ partial,
-                                                              int runs0, int runs, int K, int cin,
-                                                              int cout, float* __restrict__ dw) {
+                                                              const WSplit ws, int cin, int cout,
+                                                              float* __restrict__ dw) {
   typedef float f4 __attribute__((ext_vector_type(4)));
   __shared__ f4 part[4][64];
   const int64_t per4 = static_cast<int64_t>(cin) * cout / 4;
@@ -471,19 +492,16 @@ __global__ __launch_bounds__(256) void k_bwd_weight_reduce_pp(const float* __res
   const f4* p4 = reinterpret_cast<const f4*>(partial);
   f4 acc = {0.f, 0.f, 0.f, 0.f};
   if (c4 < per4) {
-    if (kp == 0) {
-      for (int r = s; r < runs0; r += 4) acc += p4[static_cast<int64_t>(r) * per4 + c4];
-    } else {
-      for (int r = s; r < runs; r += 4)
-        acc += p4[(static_cast<int64_t>(runs0) + static_cast<int64_t>(r) * (K - 1) + kp - 1) * per4 + c4];
-    }
+    const int n = ws.count(kp), first = ws.first(kp), stride = ws.stride(kp);
+    for (int r = s; r < n; r += 4)
+      acc += p4[static_cast<int64_t>(first + r * stride) * per4 + c4];
   }
   part[s][threadIdx.x & 63] = acc;
   __syncthreads();
   if (s == 0 && c4 < per4) {
     const f4 t = ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) +
                  part[3][threadIdx.x];
-    const int k = K == kTaps3 ? tap_at(kp) : 0;
+    const int k = ws.np == kTaps3 ? tap_at(kp) : 0;
     reinterpret_cast<f4*>(dw)[k * per4 + c4] = t;
   }
 }
@@ -568,71 +586,100 @@ bool use_pp_w(int cin, int cout) {
   return ok(cin) && ok(cout);
 }
 
-// Work split of a weight gradient: the centre in runs0 runs of tpr0 tiles,
-// each other position in runs runs of tpr tiles (the old kernel: every
-// position in runs runs, runs0 = 0).
 struct Runs {
-  int runs, tpr, runs0, tpr0;
-  int blocks(int K) const { return runs0 + (runs0 > 0 ? K - 1 : K) * runs; }
+  int runs, tpr;
 };
-Runs runs_for(const Map& m, int K, int cin, int cout) {
+// the old kernel: every position in the same runs of tpr tiles
+Runs runs_for(const Map& m, int K) {
   const int64_t nt = m.n_tiles;
-  auto split = [nt](double groups_per_tile, double target) {
-    int64_t r = static_cast<int64_t>(std::ceil(nt * groups_per_tile / target));
-    r = std::max<int64_t>(1, std::min<int64_t>(r, nt));
-    const int64_t t = (nt + r - 1) / r;
-    return std::pair<int, int>(static_cast<int>((nt + t - 1) / t), static_cast<int>(t));
-  };
-  if (use_pp_w(cin, cout)) {
-    // groups of 32 pairs per tile: 8 for the centre, and for the other
-    // positions their mean pair count over 32, rounded up on average
-    const double off = K == kTaps3 && nt > 0
-                           ? static_cast<double>(m.active_pairs - m.n) / (26.0 * nt) : 0.0;
-    const double g_off = std::max(1.0, off / kPairs + 0.5);
-    Runs r{};
-    std::tie(r.runs0, r.tpr0) = split(kTileRows / kPairs, kGroupsPerBlock);
-    if (K == kTaps3)
-      std::tie(r.runs, r.tpr) = split(g_off, kGroupsPerBlock);
-    else
-      r.runs = r.tpr = 0;
-    return r;
-  }
   int64_t runs = (kTargetBlocks + K - 1) / K;
   if (runs > nt) runs = nt;
   if (runs < 1) runs = 1;
   const int64_t tpr = (nt + runs - 1) / runs;
   runs = (nt + tpr - 1) / tpr;
-  return {static_cast<int>(runs), static_cast<int>(tpr), 0, 0};
+  return {static_cast<int>(runs), static_cast<int>(tpr)};
+}
+
+// compute units of a device, cached
+int device_cus(int dev) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  if (dev < 0 || dev >= kMaxDevices) return 256;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int cus = 256;
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    v = std::max(1, cus);
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// the pipelined kernel: runs from the map's exact group counts (the centre's,
+// and the mean of the other positions'). Workgroups of 4 or more waves: at
+// most kBlocksPerCU per compute unit, all resident at once (a few blocks
+// more than the CUs hold at that count would make some CUs take a third).
+// Smaller workgroups: about kGroupsSmall groups each, many per CU.
+WSplit split_for(const Map& m, int K, int cin, int cout) {
+  WSplit ws{};
+  ws.np = K == kTaps3 ? kTaps3 : 1;
+  const int64_t nt = m.n_tiles;
+  int64_t off = 0;
+  for (int p = 1; p < ws.np; ++p) off += m.pos_groups[p];
+  const double g0 = static_cast<double>(m.pos_groups[0]);
+  const double goff = ws.np > 1 ? static_cast<double>(off) / (ws.np - 1) : 0.0;
+  auto runs_of = [nt](double groups, double target, int32_t& runs, int32_t& tpr) {
+    int64_t r = static_cast<int64_t>(std::ceil(groups / target));
+    r = std::max<int64_t>(1, std::min<int64_t>(r, nt));
+    const int64_t t = (nt + r - 1) / r;
+    tpr = static_cast<int32_t>(t);
+    runs = static_cast<int32_t>((nt + t - 1) / t);
+  };
+  auto fill = [&](double target) {
+    runs_of(g0, target, ws.runs0, ws.tpr0);
+    if (ws.np > 1) runs_of(goff, target, ws.runs, ws.tpr);
+  };
+  if (pp_waves(cin, cout) >= 4) {
+    const int64_t cap = int64_t{device_cus(m.device)} * kBlocksPerCU;
+    double target = std::max(16.0, (g0 + off) / static_cast<double>(cap));
+    fill(target);
+    for (int it = 0; it < 200 && ws.blocks() > cap; ++it) {
+      target *= 1.02;
+      fill(target);
+    }
+  } else {
+    fill(kGroupsSmall);
+  }
+  return ws;
 }
 
 template <int CIN, int COUT>
 int launch_w(const Map& m, int K, const _Float16* feats, const _Float16* grad_out, float* partial,
              float* dw, hipStream_t stream) {
-  const Runs r = runs_for(m, K, CIN, COUT);
-  const unsigned blocks = static_cast<unsigned>(r.blocks(K));
   const int32_t nt = static_cast<int32_t>(m.n_tiles), np = static_cast<int32_t>(m.active_pairs);
-  const int64_t total = static_cast<int64_t>(K) * CIN * COUT;
-  const unsigned rblocks = static_cast<unsigned>((total + 255) / 256);
   if constexpr ((CIN == 32 || CIN == 64 || CIN == 128 || CIN == 256) &&
                 (COUT == 32 || COUT == 64 || COUT == 128 || COUT == 256)) {
     constexpr int NT = PCfg<CIN, COUT>::NT;
+    const WSplit ws = split_for(m, K, CIN, COUT);
+    const unsigned blocks = static_cast<unsigned>(ws.blocks());
     if (m.order)
       k_bwd_weight_pp<CIN, COUT, true><<<blocks, NT, 0, stream>>>(
-          m.ent, m.tile_off, m.tile_cnt, m.order, m.n, nt, K, r.runs0, r.tpr0, r.tpr, feats,
-          grad_out, partial, np);
+          m.ent, m.tile_off, m.tile_cnt, m.order, m.n, nt, ws, feats, grad_out, partial, np);
     else
       k_bwd_weight_pp<CIN, COUT, false><<<blocks, NT, 0, stream>>>(
-          m.ent, m.tile_off, m.tile_cnt, m.order, m.n, nt, K, r.runs0, r.tpr0, r.tpr, feats,
-          grad_out, partial, np);
+          m.ent, m.tile_off, m.tile_cnt, m.order, m.n, nt, ws, feats, grad_out, partial, np);
     SUBMCONV_HIP_CHECK(hipGetLastError());
     const int64_t chunks = (int64_t{CIN} * COUT / 4 + 63) / 64;
-    k_bwd_weight_reduce_pp<<<static_cast<unsigned>(K * chunks), 256, 0, stream>>>(
-        partial, r.runs0, r.runs, K, CIN, COUT, dw);
+    k_bwd_weight_reduce_pp<<<static_cast<unsigned>(ws.np * chunks), 256, 0, stream>>>(
+        partial, ws, CIN, COUT, dw);
   } else {
-    k_bwd_weight<CIN, COUT><<<blocks, WCfg<CIN, COUT>::NT, 0, stream>>>(
+    const Runs r = runs_for(m, K);
+    const int64_t total = static_cast<int64_t>(K) * CIN * COUT;
+    k_bwd_weight<CIN, COUT><<<static_cast<unsigned>(r.runs * K), WCfg<CIN, COUT>::NT, 0, stream>>>(
         m.ent, m.tile_off, m.tile_cnt, m.order, m.n, nt, K, r.tpr, feats, grad_out, partial, np);
     SUBMCONV_HIP_CHECK(hipGetLastError());
-    k_bwd_weight_reduce<<<rblocks, 256, 0, stream>>>(partial, r.runs, K, CIN, COUT, dw);
+    k_bwd_weight_reduce<<<static_cast<unsigned>((total + 255) / 256), 256, 0, stream>>>(
+        partial, r.runs, K, CIN, COUT, dw);
   }
   SUBMCONV_HIP_CHECK(hipGetLastError());
   return SUBMCONV_OK;
@@ -667,8 +714,9 @@ extern "C" int64_t submconv_backward_weight_workspace_bytes(submconv_map_t map, 
     return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "Cin = %d, Cout = %d", cin, cout);
   if (!use_mfma_w(cin, cout) || map->m.n == 0) return 0;
   const int K = ksize == 3 ? kTaps3 : 1;
-  const Runs r = runs_for(map->m, K, cin, cout);
-  return static_cast<int64_t>(r.blocks(K)) * cin * cout * static_cast<int64_t>(sizeof(float));
+  const int64_t blocks = use_pp_w(cin, cout) ? split_for(map->m, K, cin, cout).blocks()
+                                             : static_cast<int64_t>(runs_for(map->m, K).runs) * K;
+  return blocks * cin * cout * static_cast<int64_t>(sizeof(float));
 }
 
 extern "C" int submconv_backward_weight(submconv_map_t map, const uint16_t* feats,

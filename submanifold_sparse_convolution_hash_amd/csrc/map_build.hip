@@ -172,6 +172,26 @@ __global__ __launch_bounds__(1024) void k_total(const int32_t* __restrict__ tile
   if (threadIdx.x == 0) *total = part[0];
 }
 
+// Groups of 32 entries per processing position, summed over the tiles
+// (the work of the weight gradient's positions): one workgroup per
+// position, fixed order, no atomics.
+__global__ __launch_bounds__(256) void k_pos_groups(const uint16_t* __restrict__ tile_cnt,
+                                                   int64_t n_tiles,
+                                                   unsigned long long* __restrict__ groups) {
+  __shared__ unsigned long long part[256];
+  const int p = blockIdx.x;
+  unsigned long long s = 0;
+  for (int64_t t = threadIdx.x; t < n_tiles; t += 256)
+    s += (tile_cnt[t * kTaps3 + p] + kGroupRows - 1) / kGroupRows;
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (static_cast<int>(threadIdx.x) < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) groups[p] = part[0];
+}
+
 // Sorted-key builder (the packing + sort + search lookup of "Running
 // TRELLIS.2 on a Mac (3/3)", section E): an independent second way to the
 // same map. skeys/srows are the packed keys and their rows sorted by key.
@@ -509,8 +529,10 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   // the active pairs in 64 bits (the int32 offsets are checked against it)
   k_total<<<1, 1024, 0, stream>>>(static_cast<const int32_t*>(tile_tot.p), n_tiles, pairs);
   BUILD_CHECK(hipGetLastError());
+  k_pos_groups<<<kTaps3, 256, 0, stream>>>(tile_cnt, n_tiles, pairs + 1);
+  BUILD_CHECK(hipGetLastError());
 
-  uint64_t host_small[2] = {};
+  uint64_t host_small[2 + kTaps3] = {};
   BUILD_CHECK(hipMemcpyAsync(host_small, small.p, sizeof(host_small), hipMemcpyDeviceToHost, stream));
   BUILD_CHECK(hipStreamSynchronize(stream));
   const uint32_t eflags = static_cast<uint32_t>(host_small[0]);
@@ -521,6 +543,7 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   if (eflags & kErrDuplicate)
     return fail(set_error(SUBMCONV_ERR_DUPLICATE_COORD, "a site occurs more than once"));
   m.active_pairs = static_cast<int64_t>(host_small[1]);
+  for (int q = 0; q < kTaps3; ++q) m.pos_groups[q] = static_cast<int64_t>(host_small[2 + q]);
   if (m.active_pairs >= INT32_MAX)
     return fail(set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "too many active pairs for int32 offsets"));
   // one more entry {-1, -1} after the lists: the target of masked loads

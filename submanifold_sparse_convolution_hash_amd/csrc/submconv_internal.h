@@ -20,6 +20,10 @@ constexpr int kCenterTap = 13;
 // built for this tile size.
 constexpr int kTileRows = 256;
 
+// Entries per group: the kernels take a tile's entries of one position 32
+// at a time (one MFMA operand block).
+constexpr int kGroupRows = 32;
+
 // Processing position p -> tap: the centre first (it initialises an output
 // accumulator), then the other 26 taps in ascending order.
 __host__ __device__ inline int tap_at(int p) {
@@ -50,6 +54,8 @@ struct Map {
   uint16_t* tile_cnt = nullptr;
   int32_t* tile_off = nullptr;
   int2* ent = nullptr;
+  // groups of kGroupRows entries per processing position, over all tiles
+  int64_t pos_groups[kTaps3] = {};
 };
 
 // Records a thread-local message and returns `status`.
