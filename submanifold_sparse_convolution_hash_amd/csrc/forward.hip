@@ -20,8 +20,8 @@
 //     tile in LDS. Rows are unique within a group and a wave's columns are
 //     its own, so the read-modify-write needs no atomics.
 //   * k_fwd_pp (Cin <= 128) gives each 32-column block two waves that take
-//     the groups in turn, and is persistent: one workgroup per compute unit
-//     walks a run of units with its pipeline running on across them;
+//     the groups in turn, and is persistent: each workgroup walks a run of
+//     units with its pipeline running on across them;
 //     k_fwd_mfma (Cin = 256) has one wave per block and one unit per
 //     workgroup.
 //     Both are software pipelined with rings of register buffers unrolled to
@@ -436,8 +436,8 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
 // may update the same rows; their updates are in consecutive steps, ordered
 // by the step barrier. All waves share the gathering of feature rows.
 //
-// The accumulator tile takes most of the LDS, so a compute unit holds one
-// workgroup; the grid is one workgroup per compute unit and each walks every
+// The grid is as many workgroups as the compute units hold at once (one per
+// CU when the 128-column accumulator fills the LDS), and each walks every
 // wpx-th unit of its XCD's run. The steps of successive units form one
 // stream: the lookahead reads the next unit's schedule, so that unit's
 // entries, rows, weights and first gathered groups are in flight while the
