@@ -97,13 +97,14 @@ def test_backward_uniform_full(dev, name, morton):
 
 
 @gpu
-def test_backward_c3_sampled_and_weight_grad(dev):
+@pytest.mark.parametrize("morton", [False, True])
+def test_backward_c3_sampled_and_weight_grad(dev, morton):
     sc = _sc()
     wl = workloads.make("c3_128_128")
     L = wl.layers[0]
     rows = np.random.default_rng(7).choice(wl.n, 3000, replace=False)
-    _say(f"[backward] c3 N={wl.n}")
-    km, g, gd = _layer_case(sc, dev, wl, L, 60, rows=rows)
+    _say(f"[backward] c3 N={wl.n} morton={morton}")
+    km, g, gd = _layer_case(sc, dev, wl, L, 60, morton=morton, rows=rows)
     dw = sc.backward_weight(km, _to(dev, wl.feats), gd, 3).cpu().numpy()
     kmap = oc.kernel_map(wl.coords, wl.grid, wl.batch, 3)
     _check_weight_grad(dw, kmap, wl.feats, g, "c3 weight grad")

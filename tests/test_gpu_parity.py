@@ -153,6 +153,26 @@ def test_shapes_small(dev, cin, cout, ksize):
 
 
 @gpu
+@pytest.mark.parametrize("cin,cout,ksize,morton", [(64, 256, 3, False), (128, 64, 3, True),
+                                                   (32, 32, 3, False), (128, 128, 1, False)])
+def test_persistent_walk_many_units(dev, cin, cout, ksize, morton):
+    # ~60k rows: 235 row tiles, several units per workgroup of the persistent
+    # forward (two column tiles at Cout = 256, several workgroups per CU at
+    # 32 and 64 columns), every output row against the oracle
+    sc = _sc()
+    wl = workloads.uniform_workload(64, 60000, [(ksize, cin, cout)], seed=900 + cin + cout,
+                                    bias_kind="normal", name="walk")
+    L = wl.layers[0]
+    _say(f"[walk {cin}->{cout} k{ksize} morton={morton}] N={wl.n}")
+    km = _run_map(sc, dev, wl, morton)
+    out = sc.forward(km, _to(dev, wl.feats), _to(dev, L.W), _to(dev, L.bias)).float().cpu().numpy()
+    kref = oc.kernel_map(wl.coords, wl.grid, wl.batch, ksize)
+    ref = oc.submconv_rows(kref, wl.feats, L.W, L.bias)
+    _assert_close(out, ref, f"walk {cin}->{cout} k{ksize}")
+    km.free()
+
+
+@gpu
 @pytest.mark.parametrize("n", [1, 2, 15, 16, 17, 63, 64, 65, 255, 256, 257, 511, 513, 1000])
 def test_ragged_row_counts(dev, n):
     sc = _sc()
