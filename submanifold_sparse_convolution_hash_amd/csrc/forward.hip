@@ -61,6 +61,9 @@ __device__ __forceinline__ float widen16(_Float16 v) {
 }
 
 constexpr int kMaxChannels = 1024;
+// mean groups of 32 entries per off-centre position and tile from which a
+// map counts as dense (64-row groups at Cin <= 64)
+constexpr int kDenseGroups = 3;
 
 __device__ __forceinline__ int excl_scan_wave(int v, int lane) {
   int x = v;
@@ -444,10 +447,11 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
 // current one finishes and writes its outputs, and only the first unit pays
 // for filling the pipeline.
 
-template <int CIN, int COUT_T, bool K3>
+template <int CIN, int COUT_T, bool K3, int GR_ = 32>
 struct CfgPP {
   static constexpr int M = kTileRows;
-  static constexpr int GR = 32;
+  static constexpr int GR = GR_;             // rows per group: 32, or 64 for dense maps
+  static constexpr int NRB = GR / 32;        // 32-row MFMA blocks per group
   static constexpr int NC = COUT_T / 32;     // column blocks
   static constexpr int NW = 2 * NC;          // waves: two per column block
   static constexpr int NT = 64 * NW;
@@ -463,19 +467,20 @@ struct CfgPP {
   static_assert(CIN % 32 == 0 && CIN <= 128, "CIN");
   static_assert(COUT_T % 32 == 0 && COUT_T <= 128, "COUT_T");
   static_assert(GCH % NT == 0 || NT % GCH == 0, "chunk split");
-  static_assert(NCG == 8 && LB <= 4 && LE < 4, "schedule");
+  static_assert(NCG % 4 == 0 && LB <= 4 && LE < 4, "schedule");
+  static_assert(GR == 32 || (GR == 64 && CIN <= 64), "64-row groups for Cin <= 64");
 };
 
-template <int CIN, int COUT_T, bool K3, bool IS_BF16>
+template <int CIN, int COUT_T, bool K3, bool IS_BF16, int GR_>
 __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
     const int2* __restrict__ ent, const int32_t* __restrict__ tile_off,
     const uint16_t* __restrict__ tile_cnt, const int32_t* __restrict__ order, int64_t n,
     const _Float16* __restrict__ feats, const _Float16* __restrict__ wp,
     const float* __restrict__ bias, _Float16* __restrict__ out, int cout, int n_tiles, int n_ct,
     int tiles_per_xcd, int n_pairs) {
-  using C = CfgPP<CIN, COUT_T, K3>;
+  using C = CfgPP<CIN, COUT_T, K3, GR_>;
   static_assert(C::NT == 4 * COUT_T, "launch bounds");
-  constexpr int M = C::M, GR = C::GR, KS = C::KS, RC = C::RC;
+  constexpr int M = C::M, GR = C::GR, NRB = C::NRB, KS = C::KS, RC = C::RC;
   constexpr int LB = C::LB, LE = C::LE, CPT = C::CPT, NCG = C::NCG;
   __shared__ float4v acc[M * C::NQ];
   __shared__ half8 bt[2][C::GCH];
@@ -520,7 +525,7 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
   // One unit's schedule in lanes 0..31. For processing position p < 27 (the
   // centre first): cnt entries, the first at off (in the whole list, or the
   // row in the tile for a 1x1x1 kernel), processed from step gs on (the
-  // centre in NCG steps, then each position in steps of 32 entries). Lane 27
+  // centre in NCG steps, then each position in steps of GR entries). Lane 27
   // is an empty position at step F, where the unit's steps end; the unit
   // takes Fp steps (F rounded up to a multiple of 4 past the centre), so that
   // step residues mod 4 carry over to the next unit. Lanes 28..31 start at
@@ -553,8 +558,8 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
   };
   // The stream's schedule: the current unit a in lanes 0..31, the next unit b
   // in lanes 32..63 with its steps counted on from a's last.
-  // Per lane: gs, the first step of the position; offg = off - 32 gs, so
-  // that step f of the position starts at entry offg + 32 f; end = off + cnt;
+  // Per lane: gs, the first step of the position; offg = off - GR gs, so
+  // that step f of the position starts at entry offg + GR f; end = off + cnt;
   // and wb.
   int s_gs, s_offg, s_end, s_wb;
   auto join = [&](const Half& a, const Half& b) {
@@ -624,10 +629,16 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
       for (int i = 0; i < CPT; ++i) bt[slot][lpos[i]] = D[i];
     }
   };
-  auto load_row = [&](const Grp& g) -> int {
-    const int sl = lane & 31;
-    if (K3) return bload_i2(re, sl < g.cnt ? static_cast<uint32_t>(g.start + sl) * 8u : e_none).y;
-    return sl < g.cnt ? g.start + sl : -1;
+  // row in tile of this lane's slot in each 32-row block of group g (-1: none)
+  auto load_row = [&](const Grp& g, int (&R)[NRB]) {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int sl = (lane & 31) + 32 * rb;
+      if (K3)
+        R[rb] = bload_i2(re, sl < g.cnt ? static_cast<uint32_t>(g.start + sl) * 8u : e_none).y;
+      else
+        R[rb] = sl < g.cnt ? g.start + sl : -1;
+    }
   };
 
   // ---- MFMA role (fragment layouts as in k_fwd_mfma) ----
@@ -647,9 +658,13 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
     const int lc = h * (CIN / 16) + st;
     boff[st] = s32 * RC + (lc ^ (s32 & (RC - 1)));
   }
-  auto read_b = [&](int slot, half8 (&B)[KS]) {
+  // B fragments of each 32-row block (block rb: rows 32 rb.., the same
+  // swizzle since 32 rb is a multiple of RC)
+  auto read_b = [&](int slot, half8 (&B)[NRB][KS]) {
 #pragma unroll
-    for (int st = 0; st < KS; ++st) B[st] = bt[slot][boff[st]];
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int st = 0; st < KS; ++st) B[rb][st] = bt[slot][boff[st] + 32 * rb * RC];
   };
   auto multiply = [&](const half8 (&A)[KS], const half8 (&B)[KS]) {
     float16v d = {};
@@ -712,9 +727,9 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
 
     int2 E[4][CPT];
     half8 D[4][CPT];
-    int RW[2];
+    int RW[2][NRB];
     half8 AW[2][KS];
-    half8 BF[KS];
+    half8 BF[NRB][KS];
 #pragma unroll
     for (int g = 0; g < LB; ++g) load_entries(grp(g), E[g % 4]);
 #pragma unroll
@@ -724,7 +739,7 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
     if (PAR == 0) {
       load_a(grp(0), AW[0]);
       load_a(grp(2), AW[1]);
-      RW[0] = load_row(grp(0));
+      load_row(grp(0), RW[0]);
     } else {
       load_a(grp(1), AW[0]);
     }
@@ -744,13 +759,18 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
         // requested before the MFMAs so that their latency overlaps them.
         // This chain ends the step, so the wave issues ahead of its partner
         // (whose B-fragment reads would otherwise queue in front in LDS).
-        const int r = RW[(i >> 1) & 1];
-        float4v old[4];
+        float4v old[NRB][4];
         __builtin_amdgcn_s_setprio(3);
-        if (!centre_step) read_old(r, old);
+        if (!centre_step) {
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb) read_old(RW[(i >> 1) & 1][rb], old[rb]);
+        }
         if (centre_step || f < cur.F) {
-          const float16v d = multiply(AW[(i >> 1) & 1], BF);
-          write_acc(r, centre_step, old, d);
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb) {
+            const float16v d = multiply(AW[(i >> 1) & 1], BF[rb]);
+            write_acc(RW[(i >> 1) & 1][rb], centre_step, old[rb], d);
+          }
         }
         __builtin_amdgcn_s_setprio(0);
         load_chunks(E[(i + LB) % 4], D[(i + LB) % 4]);
@@ -760,7 +780,7 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
         read_b((i + 1) & 1, BF);
         load_chunks(E[(i + LB) % 4], D[(i + LB) % 4]);
         load_entries(grp(f + LB + LE), E[(i + LB + LE) % 4]);
-        RW[((i + 1) >> 1) & 1] = load_row(grp(f + 1));
+        load_row(grp(f + 1), RW[((i + 1) >> 1) & 1]);
         load_a(grp(f + 3), AW[((i + 3) >> 1) & 1]);
       }
       lds_barrier();
@@ -923,6 +943,32 @@ int cus_per_xcd() {
   return v;
 }
 
+template <int CIN, int COUT_T, bool K3, bool IS_BF16, int GR>
+int launch_pp(const Map& m, const _Float16* feats, const _Float16* wp, const float* bias,
+              _Float16* out, int cout, int n_tiles, int n_ct, int tiles_per_xcd, int n_pairs,
+              hipStream_t stream) {
+  using C = CfgPP<CIN, COUT_T, K3, GR>;
+  // persistent: as many workgroups as the CUs hold at once (one per CU when
+  // the accumulator fills the LDS, more for narrow column tiles), dealt
+  // evenly to the 8 XCDs
+  static const int per_cu = [] {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &nb, reinterpret_cast<const void*>(k_fwd_pp<CIN, COUT_T, K3, IS_BF16, GR>), C::NT, 0) !=
+        hipSuccess)
+      nb = 1;
+    return std::max(1, nb);
+  }();
+  const int64_t units_per_xcd = int64_t{tiles_per_xcd} * n_ct;
+  const int64_t wpx = std::min<int64_t>(units_per_xcd, int64_t{cus_per_xcd()} * per_cu);
+  k_fwd_pp<CIN, COUT_T, K3, IS_BF16, GR><<<static_cast<unsigned>(8 * wpx), C::NT, 0, stream>>>(
+      K3 ? m.ent : nullptr, K3 ? m.tile_off : nullptr, K3 ? m.tile_cnt : nullptr,
+      K3 ? m.order : nullptr, m.n, feats, wp, bias, out, cout, n_tiles, n_ct, tiles_per_xcd,
+      n_pairs);
+  SUBMCONV_HIP_CHECK(hipGetLastError());
+  return SUBMCONV_OK;
+}
+
 template <int CIN, int COUT_T, bool K3, bool IS_BF16>
 int launch_one(const Map& m, const _Float16* feats, const _Float16* wp, const float* bias,
                _Float16* out, int cout, hipStream_t stream) {
@@ -935,24 +981,17 @@ int launch_one(const Map& m, const _Float16* feats, const _Float16* wp, const fl
   const int64_t blocks = int64_t{8} * tiles_per_xcd * n_ct;
   const int n_pairs = static_cast<int>(K3 ? m.active_pairs : 0);
   if constexpr (CIN <= 128) {
-    // persistent: as many workgroups as the CUs hold at once (one per CU
-    // when the accumulator fills the LDS, more for narrow column tiles),
-    // dealt evenly to the 8 XCDs
-    static const int per_cu = [] {
-      int nb = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-              &nb, reinterpret_cast<const void*>(k_fwd_pp<CIN, COUT_T, K3, IS_BF16>),
-              CfgPP<CIN, COUT_T, K3>::NT, 0) != hipSuccess)
-        nb = 1;
-      return std::max(1, nb);
-    }();
-    const int64_t units_per_xcd = int64_t{tiles_per_xcd} * n_ct;
-    const int64_t wpx = std::min<int64_t>(units_per_xcd, int64_t{cus_per_xcd()} * per_cu);
-    k_fwd_pp<CIN, COUT_T, K3, IS_BF16><<<static_cast<unsigned>(8 * wpx), CfgPP<CIN, COUT_T, K3>::NT, 0,
-                                    stream>>>(
-        K3 ? m.ent : nullptr, K3 ? m.tile_off : nullptr, K3 ? m.tile_cnt : nullptr,
-        K3 ? m.order : nullptr, m.n, feats, wp, bias, out, cout, n_tiles, n_ct, tiles_per_xcd,
-        n_pairs);
+    // dense maps (many groups per position) take 64-row groups at Cin <= 64:
+    // half the steps, each weight load serving two MFMA row blocks
+    if constexpr (CIN <= 64 && K3) {
+      int64_t off_groups = 0;
+      for (int q = 1; q < kTaps3; ++q) off_groups += m.pos_groups[q];
+      if (off_groups >= int64_t{kDenseGroups} * (kTaps3 - 1) * n_tiles)
+        return launch_pp<CIN, COUT_T, K3, IS_BF16, 64>(m, feats, wp, bias, out, cout, n_tiles, n_ct,
+                                                      tiles_per_xcd, n_pairs, stream);
+    }
+    return launch_pp<CIN, COUT_T, K3, IS_BF16, 32>(m, feats, wp, bias, out, cout, n_tiles, n_ct,
+                                                  tiles_per_xcd, n_pairs, stream);
   } else {
     k_fwd_mfma<CIN, COUT_T, K3, IS_BF16><<<static_cast<unsigned>(blocks), Cfg<CIN, COUT_T, K3>::NT, 0,
                                       stream>>>(

@@ -456,3 +456,32 @@ def test_bf16_c3_sampled_and_input_grad(dev):
     _assert_close(_bf16_values(dx)[rows],
                   oc.backward_input_rows(wl.coords, wl.grid, wl.batch, 3, F, Wd, rows), "bf16 c3 input grad")
     km.free()
+
+
+@gpu
+@pytest.mark.parametrize("cin,cout,dtype", [(32, 32, "fp16"), (64, 32, "bf16"), (32, 128, "fp16"),
+                                            (64, 64, "bf16")])
+def test_dense_maps_64row_groups(dev, cin, cout, dtype):
+    # 95 % occupancy: ~240 entries per position and tile, so the Cin <= 64
+    # forward takes 64-row groups; every row against the oracle
+    sc = _sc()
+    seed = 700 + cin + cout
+    _say(f"[dense {cin}->{cout} {dtype}]")
+    if dtype == "fp16":
+        wl = workloads.random_small(seed, G=14, occ=0.95, cin=cin, cout=cout, batch=2, ksize=3,
+                                    bias=True)
+        L = wl.layers[0]
+        km = sc.build_map(_to(dev, wl.coords), wl.grid, wl.batch)
+        out = sc.forward(km, _to(dev, wl.feats), _to(dev, L.W), _to(dev, L.bias)).float().cpu().numpy()
+        kmap = oc.kernel_map(wl.coords, wl.grid, wl.batch, 3)
+        ref = oc.submconv_rows(kmap, wl.feats, L.W, L.bias)
+    else:
+        wl, fb, Wb = _bf16_case(seed, 14, 0.95, cin, cout, 3, batch=2)
+        km = sc.build_map(_to(dev, wl.coords), wl.grid, wl.batch)
+        out = _bf16_values(sc.forward(km, _bf16_tensor(dev, fb), _bf16_tensor(dev, Wb),
+                                      _to(dev, wl.layers[0].bias)))
+        kmap = oc.kernel_map(wl.coords, wl.grid, wl.batch, 3)
+        ref = oc.submconv_rows(kmap, op.bf16_bits_to_float64(fb), op.bf16_bits_to_float64(Wb),
+                               wl.layers[0].bias)
+    _assert_close(out, ref, f"dense {cin}->{cout} {dtype}")
+    km.free()
