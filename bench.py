@@ -48,9 +48,9 @@ CSRC = os.path.join(ROOT, "submanifold_sparse_convolution_hash_amd", "csrc")
 MEASURED_TRAFFIC = {
     ("c3_128_128", "forward"): {
         "src": "forward.hip",
-        "sha256": "b1d59f840d5b06608f4110e3db93d8f4e5236e39c2c4acd518bf373da3d59887",
-        "fetch_kib": 49875.56, "write_kib": 52428.75,
-        "fetch_factor": 524288.0 / 262169.375, "write_factor": 1.0},
+        "sha256": "1681c9c7222f12986434482db10a98ce17a8d4331a75cb272da7cde03d0f0af9",
+        "fetch_kib": 50005.51, "write_kib": 52428.75,
+        "fetch_factor": 524288.0 / 262169.75, "write_factor": 1.0},
 }
 
 METRICS = {
@@ -118,6 +118,33 @@ def _time(fn, steps, warmup, torch):
         b.record()
     torch.cuda.synchronize()
     return sum(a.elapsed_time(b) for a, b in evs) / steps * 1e3  # us
+
+
+def python_oracle_times():
+    """Wall-clock seconds of the pure-Python oracle (dictionary map, fp64
+    per-pair products), one thread, on the three uniform workloads."""
+    from threadpoolctl import threadpool_limits
+
+    import workloads
+    from oracle import oracle as O
+    res = []
+    with threadpool_limits(limits=1):
+        for name in ("c1_16_8", "c2_64_64", "c3_128_128"):
+            wl = workloads.make(name)
+            L = wl.layers[0]
+            t = time.perf_counter()
+            kmap = O.kernel_map(wl.coords, wl.grid, L.ksize, wl.batch)
+            map_s = time.perf_counter() - t
+            t = time.perf_counter()
+            O.submconv(wl.coords, wl.feats, L.W, L.bias, wl.grid, L.ksize, wl.batch, kmap=kmap)
+            conv_s = time.perf_counter() - t
+            pairs = O.active_pairs(kmap)
+            res.append({"workload": name, "rows": wl.n, "active_pairs": pairs, "map_s": round(map_s, 3),
+                        "conv_s": round(conv_s, 3),
+                        "conv_tflops": round(2.0 * pairs * L.cin * L.cout / conv_s / 1e12, 7)})
+            print(f"[bench] python oracle {name}: map {map_s:.2f} s, conv {conv_s:.2f} s",
+                  file=sys.stderr, flush=True)
+    return {"threads": 1, "runs": res}
 
 
 def coord_op_bench(args, sc, wl, coords, feats, dev):
@@ -211,6 +238,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a device copy of this many MiB (counter calibration)")
+    ap.add_argument("--scrub-mib", type=int, default=512,
+                    help="also time the op's kernels with a device copy of this many MiB before "
+                         "each launch, which evicts the L2s and the 256 MiB MALL (0: skip)")
+    ap.add_argument("--python-oracle", action="store_true",
+                    help="also time the pure-Python oracle, single-threaded, on c1_16_8, "
+                         "c2_64_64 and c3_128_128 (tens of seconds)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -330,6 +363,30 @@ def main():
     achieved_gbs = alg_bytes / (k_us * 1e-6) / 1e9
     print(f"[bench] {op} kernels {k_us:.1f} us, {achieved_gbs:.0f} GB/s algorithmic", file=sys.stderr, flush=True)
 
+    cold = None
+    if args.scrub_mib > 0:
+        # the same launches with every cache cold: a copy of scrub_mib MiB
+        # between launches, outside the event pair
+        nb = args.scrub_mib * 1024 * 1024 // 2
+        sa = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(3)
+        sb = torch.empty_like(sa)
+        n_cold = max(1, min(args.steps, 50))
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_cold)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            sb.copy_(sa)
+            a.record()
+            kernel()
+            b.record()
+        torch.cuda.synchronize()
+        cold_us = sorted(a.elapsed_time(b) for a, b in evs)[n_cold // 2] * 1e3
+        del sa, sb
+        cold = {"kernel_us_median": round(cold_us, 2), "launches": n_cold, "scrub_mib": args.scrub_mib,
+                "achieved_gbs": round(alg_bytes / (cold_us * 1e-6) / 1e9, 1)}
+        print(f"[bench] {op} kernels after a {args.scrub_mib} MiB scrub: {cold_us:.1f} us (median of "
+              f"{n_cold})", file=sys.stderr, flush=True)
+
     if args.calib_copy_mib > 0:
         nb = args.calib_copy_mib * 1024 * 1024
         a = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
@@ -365,6 +422,10 @@ def main():
                          f"map {map_s * 1e3:.0f} ms"}
         print(f"[bench] cpu oracle {what} {conv_s:.2f} s", file=sys.stderr, flush=True)
 
+    py_oracle = None
+    if args.python_oracle:
+        py_oracle = python_oracle_times()
+
     extra = {}
     if op == "forward_masked":
         extra = {"masked_row_taps": mplan.row_taps, "padding_factor": round(mplan.row_taps / pairs, 3)}
@@ -392,8 +453,11 @@ def main():
                      "algorithmic_bytes": alg_bytes,
                      "mfma_effective_frac": round(flops / (k_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
         "map_build_ms": round(float(np.median(build_ms)), 3),
+        "mall_cold": cold,
         "cpu_baseline": cpu,
     }
+    if py_oracle is not None:
+        rec["python_oracle"] = py_oracle
     print(json.dumps(rec), flush=True)
     if op == "forward_masked":
         mplan.free()

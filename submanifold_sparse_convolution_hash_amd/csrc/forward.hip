@@ -776,12 +776,15 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
         load_chunks(E[(i + LB) % 4], D[(i + LB) % 4]);
         load_entries(grp(f + LB + LE), E[(i + LB + LE) % 4]);
       } else {
-        // prepare this wave's next group, f+1
+        // prepare this wave's next group, f+1. Its rows are requested
+        // first: the memory counter completes in order, so the multiply's
+        // wait for them then leaves every later load of this step in flight.
+        load_row(grp(f + 1), RW[((i + 1) >> 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
         read_b((i + 1) & 1, BF);
+        load_a(grp(f + 3), AW[((i + 3) >> 1) & 1]);
         load_chunks(E[(i + LB) % 4], D[(i + LB) % 4]);
         load_entries(grp(f + LB + LE), E[(i + LB + LE) % 4]);
-        load_row(grp(f + 1), RW[((i + 1) >> 1) & 1]);
-        load_a(grp(f + 3), AW[((i + 3) >> 1) & 1]);
       }
       lds_barrier();
     };
