@@ -19,13 +19,12 @@
 //     the tap's weights and adds the 32 x COUT_T result to an fp32 accumulator
 //     tile in LDS. Rows are unique within a group and a wave's columns are
 //     its own, so the read-modify-write needs no atomics.
-//   * k_fwd_pp (Cin <= 128) gives each 32-column block two waves that take
-//     the groups in turn, and is persistent: each workgroup walks a run of
-//     units with its pipeline running on across them;
-//     k_fwd_mfma (Cin = 256) has one wave per block and one unit per
-//     workgroup.
-//     Both are software pipelined with rings of register buffers unrolled to
-//     static indices, and end every step with an LDS-only fence and barrier.
+//   * k_fwd_pp gives each 32-column block two waves that take the groups in
+//     turn, and is persistent: each workgroup walks a run of units with its
+//     pipeline running on across them. 256 input channels run as two passes
+//     of 128 over each unit. The pipeline is software pipelined with rings of
+//     register buffers unrolled to static indices, and ends every step with
+//     an LDS-only fence and barrier.
 //   * Epilogue: bias in fp32, one rounding (round to nearest even), 16-byte
 //     row stores at the caller's row.
 #include <algorithm>
@@ -91,7 +90,7 @@ __device__ __forceinline__ int2 bload_i2(__amdgpu_buffer_rsrc_t r, uint32_t off)
   return __builtin_bit_cast(int2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 
-// Epilogue of both MFMA kernels: the tile's fp32 accumulator rows (float4
+// Epilogue of the MFMA kernel: the tile's fp32 accumulator rows (float4
 // chunk q of row r at r*NQ + (q ^ (r % NQ))) plus the bias, rounded once to
 // fp16 (round to nearest even) and stored at the caller's row.
 template <int COUT_T, int NT, bool K3, bool IS_BF16>
@@ -126,310 +125,15 @@ __device__ __forceinline__ void store_tile(const float4v* acc, int rows_here, in
   }
 }
 
-// ---------------------------------------------------------------------------
-// MFMA kernel
-// ---------------------------------------------------------------------------
-
 typedef float float16v __attribute__((ext_vector_type(16)));
 
-template <int CIN, int COUT_T, bool K3>
-struct Cfg {
-  static constexpr int M = kTileRows;        // output rows per tile
-  static constexpr int GR = 32;              // rows per group (MFMA 32x32x16)
-  static constexpr int NW = COUT_T / 32;     // waves; each owns 32 output columns
-  static constexpr int NT = 64 * NW;         // threads
-  static constexpr int KS = CIN / 16;        // 16-channel MFMA K steps
-  static constexpr int NQ = COUT_T / 4;      // float4 chunks per accumulator row
-  static constexpr int RC = CIN / 8;         // 16-byte chunks per feature row
-  static constexpr int GCH = GR * RC;        // chunks per group
-  static constexpr int CPT = GCH >= NT ? GCH / NT : 1;  // chunks per loading thread
-  static constexpr int NLOAD = GCH >= NT ? NT : GCH;    // loading threads
-  static constexpr int NCG = M / GR;         // groups of the centre tap
-  static constexpr int RQ = 4;               // register rings; unroll of the main loop
-  static constexpr int LB = 3;               // chunks requested LB steps before the multiply
-  static constexpr int LE = 2;               // entries requested LE steps before their chunks
-  static constexpr int LR = 2;               // rows requested LR steps before the multiply
-  static_assert(CIN % 32 == 0 && CIN <= 256, "CIN");
-  static_assert(COUT_T % 32 == 0 && COUT_T <= 128, "COUT_T");
-  static_assert(GCH % NT == 0 || NT % GCH == 0, "chunk split");
-  static_assert(NCG == 8, "centre steps");
-};
-
-template <int CIN, int COUT_T, bool K3, bool IS_BF16>
-__global__ __launch_bounds__(2 * COUT_T) void k_fwd_mfma(
-    const int2* __restrict__ ent, const int32_t* __restrict__ tile_off,
-    const uint16_t* __restrict__ tile_cnt, const int32_t* __restrict__ order, int64_t n,
-    const _Float16* __restrict__ feats, const _Float16* __restrict__ wp,
-    const float* __restrict__ bias, _Float16* __restrict__ out, int cout, int n_tiles, int n_ct,
-    int tiles_per_xcd, int n_pairs) {
-  using C = Cfg<CIN, COUT_T, K3>;
-  static_assert(C::NT == 2 * COUT_T, "launch bounds");
-  constexpr int M = C::M, GR = C::GR, KS = C::KS, RC = C::RC, RQ = C::RQ;
-  constexpr int LB = C::LB, LE = C::LE, LR = C::LR, CPT = C::CPT, NCG = C::NCG;
-  __shared__ float4v acc[M * C::NQ];
-  __shared__ half8 bt[2][C::GCH];  // feature rows of two groups, 16-byte chunks, swizzled
-
-  // Workgroups are dealt to the 8 XCDs round robin; give each XCD a
-  // contiguous run of row tiles (and all column tiles of a row tile) so that
-  // neighbouring tiles, which gather the same feature rows, share an L2.
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7;
-  const int li = bid >> 3;
-  const int tl = li / n_ct;
-  const int ct = li - tl * n_ct;
-  const int tile = xcd * tiles_per_xcd + tl;
-  if (tl >= tiles_per_xcd || tile >= n_tiles) return;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int64_t t0 = static_cast<int64_t>(tile) * M;
-  const int rows_here = static_cast<int>(n - t0 < M ? n - t0 : M);
-  const int c0 = ct * COUT_T;
-
-  // ---- schedule ----
-  // Lane p < 27 holds the number of entries of processing position p (the
-  // centre first) and their offset in the tile's list. The step sequence is
-  // the NCG groups of the centre (all rows of the tile), then every group of
-  // 32 entries of positions 1..26 in order; gs_p is the first step of
-  // position p and F the number of steps.
-  int cnt_p = 0;
-  int ent0 = 0;
-  if (K3) {
-    if (lane < kTaps3) cnt_p = tile_cnt[static_cast<int64_t>(tile) * kTaps3 + lane];
-    ent0 = tile_off[tile];
-  } else {
-    cnt_p = lane == 0 ? rows_here : 0;
-  }
-  const int off_p = excl_scan_wave(cnt_p, lane);
-  const int ng_p = (lane >= 1 && lane < kTaps3) ? (cnt_p + GR - 1) / GR : 0;
-  const int gs_p = NCG + excl_scan_wave(ng_p, lane);
-  const int F = __builtin_amdgcn_readlane(gs_p, kTaps3);
-  struct Grp {
-    int start, cnt, tap;
-  };
-  // Group of step f. Positions 1..26 whose first step is at or before f form
-  // a prefix of the lanes, and the last of them is the position of step f.
-  auto group_of = [&](int f) -> Grp {
-    int p, j;
-    if (f < NCG) {
-      p = 0;
-      j = f;
-    } else {
-      const uint64_t m = __ballot(lane >= 1 && lane < kTaps3 && gs_p <= f);
-      p = __popcll(m);
-      j = f - __builtin_amdgcn_readlane(gs_p, p);
-    }
-    Grp g;
-    g.start = __builtin_amdgcn_readlane(off_p, p) + GR * j;
-    const int c = __builtin_amdgcn_readlane(cnt_p, p) - GR * j;
-    g.cnt = f >= F ? 0 : (c < GR ? c : GR);
-    g.tap = K3 ? tap_at(p) : 0;
-    return g;
-  };
-
-  const __amdgpu_buffer_rsrc_t rf = make_rsrc(feats, static_cast<uint32_t>(n * CIN * 2));
-  const __amdgpu_buffer_rsrc_t rw =
-      make_rsrc(wp, static_cast<uint32_t>((K3 ? kTaps3 : 1) * CIN * cout * 2));
-  // the whole list plus its closing {-1, -1} entry, which masked lanes load
-  const __amdgpu_buffer_rsrc_t re = make_rsrc(ent, static_cast<uint32_t>(n_pairs + 1) * 8u);
-  const uint32_t e_none = static_cast<uint32_t>(n_pairs) * 8u;
-
-  // ---- loader role: this thread moves CPT 16-byte chunks of every group ----
-  const bool loader = tid < C::NLOAD;
-  int lrow[CPT], lpos[CPT];
-  uint32_t lcol[CPT];
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int c = tid + C::NT * i;
-    lrow[i] = c / RC;
-    const int lc = c % RC;
-    lcol[i] = static_cast<uint32_t>(lc * 16);
-    lpos[i] = lrow[i] * RC + (lc ^ (lrow[i] & (RC - 1)));
-  }
-  auto load_entries = [&](int f, int2 (&E)[CPT]) {
-    const Grp g = group_of(f);
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const bool live = loader && lrow[i] < g.cnt;
-      if (K3) {
-        E[i] = bload_i2(re, live ? static_cast<uint32_t>(ent0 + g.start + lrow[i]) * 8u : e_none);
-      } else {
-        E[i].x = static_cast<int>(t0) + g.start + lrow[i];
-        E[i].y = live ? g.start + lrow[i] : -1;
-      }
-    }
-  };
-  auto load_chunks = [&](const int2 (&E)[CPT], half8 (&D)[CPT]) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i)
-      D[i] = bload_h8(rf, E[i].y >= 0 ? static_cast<uint32_t>(E[i].x) * (CIN * 2) + lcol[i] : kOob);
-  };
-  auto store_chunks = [&](int slot, const half8 (&D)[CPT]) {
-    if (loader) {
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) bt[slot][lpos[i]] = D[i];
-    }
-  };
-  // row in tile of this lane's slot of the group of step f (-1: none)
-  auto load_row = [&](int f) -> int {
-    const Grp g = group_of(f);
-    const int sl = lane & 31;
-    if (K3) return bload_i2(re, sl < g.cnt ? static_cast<uint32_t>(ent0 + g.start + sl) * 8u : e_none).y;
-    return sl < g.cnt ? g.start + sl : -1;
-  };
-
-  // ---- MFMA role: this wave owns 32 output columns ----
-  // v_mfma_f32_32x32x16_f16 computes out^T for the group: A = weights (lane:
-  // column lane%32, channels (lane/32)*Cin/2 + 8*st + 0..7), B = gathered
-  // rows (lane: slot lane%32, same channels), D: lane holds slot lane%32 and
-  // columns 8*a + 4*(lane/32) + b in register 4*a + b.
-  const int s32 = lane & 31;
-  const int h = lane >> 5;
-  const int cwb = c0 + w * 32;
-  const int qw = w * 8;
-  // weights of the tap of step f for this wave's 32 columns (one 16-byte load
-  // per K step; a step without rows loads nothing)
-  auto load_a = [&](int f, half8 (&A)[KS]) {
-    const Grp g = group_of(f);
-    const uint32_t base =
-        static_cast<uint32_t>(((g.tap * (cout / 32) + (cwb >> 5)) * KS) * 1024 + lane * 16);
-#pragma unroll
-    for (int st = 0; st < KS; ++st) A[st] = bload_h8(rw, g.cnt > 0 ? base + st * 1024 : kOob);
-  };
-  // LDS offsets (in chunks) of this lane's B fragments within a group tile
-  int boff[KS];
-#pragma unroll
-  for (int st = 0; st < KS; ++st) {
-    const int lc = h * (CIN / 16) + st;
-    boff[st] = s32 * RC + (lc ^ (s32 & (RC - 1)));
-  }
-  auto read_b = [&](int slot, half8 (&B)[KS]) {
-#pragma unroll
-    for (int st = 0; st < KS; ++st) B[st] = bt[slot][boff[st]];
-  };
-  auto multiply = [&](const half8 (&A)[KS], const half8 (&B)[KS]) {
-    float16v d = {};
-#pragma unroll
-    for (int st = 0; st < KS; ++st)
-      if constexpr (IS_BF16)
-        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, A[st]),
-                                                    __builtin_bit_cast(bf16x8, B[st]), d, 0, 0, 0);
-      else
-        d = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[st], B[st], d, 0, 0, 0);
-    return d;
-  };
-  // Accumulator rows of this lane's slot: the centre writes them, later taps
-  // add to them. Rows are unique within a group and columns are private to
-  // the wave, and a wave's LDS operations complete in order, so one group's
-  // update sees the previous group's without a barrier.
-  auto acc_at = [&](int r, int a) { return r * C::NQ + ((qw + 2 * a + h) ^ (r & (C::NQ - 1))); };
-  auto read_old = [&](int r, float4v (&old)[4]) {
-    if (r >= 0) {
-#pragma unroll
-      for (int a = 0; a < 4; ++a) old[a] = acc[acc_at(r, a)];
-    }
-  };
-  auto write_acc = [&](int r, bool centre, const float4v (&old)[4], const float16v& d) {
-    if (r >= 0) {
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const float4v v = {d[4 * a], d[4 * a + 1], d[4 * a + 2], d[4 * a + 3]};
-        acc[acc_at(r, a)] = centre ? v : old[a] + v;
-      }
-    }
-  };
-  // LDS writes of this wave are complete, then all waves meet (an LDS-only
-  // fence: outstanding global prefetches stay in flight across the barrier)
-  auto lds_barrier = [&]() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  };
-
-  // ---- software pipeline ----
-  // Group g: entries requested in step g-LB-LE, feature chunks in step g-LB,
-  // chunks stored to LDS slot g%2 in step g-2, B fragments read in step g-1,
-  // row indices requested in step g-LR, weights in step g-1; multiplied in
-  // step g into fresh registers, and added to the accumulator in step g+1,
-  // where the LDS traffic of the update overlaps the next group's MFMAs.
-  // Rings are indexed by g mod RQ (weights, B fragments and products by g
-  // mod 2) and the loops are unrolled to make every index static. The
-  // centre's weights stay in set 1 for steps 0..NCG-1.
-  static_assert(RQ > LE && LB <= RQ && LB >= 2 && LR < RQ - 1, "ring lifetimes and prologue");
-  int2 E[RQ][CPT];
-  half8 D[RQ][CPT];
-  int RW[RQ];
-  half8 AW[2][KS];
-  half8 BF[2][KS];
-  float16v DD[2];
-#pragma unroll
-  for (int g = 0; g < LB; ++g) load_entries(g, E[g % RQ]);
-#pragma unroll
-  for (int g = 0; g < LB; ++g) load_chunks(E[g % RQ], D[g % RQ]);
-#pragma unroll
-  for (int g = LB; g < LB + LE; ++g) load_entries(g, E[g % RQ]);
-#pragma unroll
-  for (int g = 0; g < LR; ++g) RW[g % RQ] = load_row(g);
-  load_a(0, AW[1]);
-  store_chunks(0, D[0]);
-  store_chunks(1, D[1]);
-  lds_barrier();
-  read_b(0, BF[0]);
-  lds_barrier();
-
-  // kind: 1 = centre step, 2 = last centre step (requests the next weights),
-  // 3 = first step after the centre, 0 = any later step
-  auto step = [&](int f, auto ic, auto kc) {
-    constexpr int i = decltype(ic)::value;  // f mod RQ
-    constexpr int kind = decltype(kc)::value;
-    constexpr int aset = (kind == 1 || kind == 2) ? 1 : (i & 1);
-    if (kind != 1) load_a(f + 1, AW[(i + 1) & 1]);
-    const int rp = RW[(i + RQ - 1) % RQ];  // rows of step f-1
-    float4v old[4];
-    if (kind == 0) read_old(rp, old);
-    read_b((i + 1) & 1, BF[(i + 1) & 1]);
-    store_chunks(i & 1, D[(i + 2) % RQ]);
-    load_chunks(E[(i + LB) % RQ], D[(i + LB) % RQ]);
-    RW[(i + LR) % RQ] = load_row(f + LR);
-    load_entries(f + LB + LE, E[(i + LB + LE) % RQ]);
-    if (kind != 0 || f < F) DD[i & 1] = multiply(AW[aset], BF[i & 1]);
-    if (f > 0) write_acc(rp, kind != 0, old, DD[(i + 1) & 1]);
-    lds_barrier();
-  };
-  [&]<int... I>(std::integer_sequence<int, I...>) {
-    (step(I, std::integral_constant<int, I % RQ>{},
-          std::integral_constant<int, I == NCG - 1 ? 2 : 1>{}), ...);
-  }(std::make_integer_sequence<int, NCG>{});
-  step(NCG, std::integral_constant<int, NCG % RQ>{}, std::integral_constant<int, 3>{});
-  int fe = NCG + 1;
-  if (K3) {
-    for (; fe < F; fe += RQ) {
-      [&]<int... I>(std::integer_sequence<int, I...>) {
-        (step(fe + I, std::integral_constant<int, (NCG + 1 + I) % RQ>{},
-              std::integral_constant<int, 0>{}), ...);
-      }(std::make_integer_sequence<int, RQ>{});
-    }
-  }
-  // the update of the last step (fe - 1 = NCG mod RQ)
-  {
-    constexpr int il = NCG % RQ;
-    float4v old[4];
-    const int rp = RW[il];
-    read_old(rp, old);
-    write_acc(rp, false, old, DD[il & 1]);
-  }
-  __syncthreads();
-
-  store_tile<COUT_T, C::NT, K3, IS_BF16>(acc, rows_here, tid, bias, c0, order, t0, out, cout);
-}
-
 // ---------------------------------------------------------------------------
-// Two-wave (ping-pong) MFMA kernel for Cin <= 128
+// Two-wave (ping-pong) MFMA kernel
 // ---------------------------------------------------------------------------
 //
-// Same tile, schedule, lists and accumulator as k_fwd_mfma, but each 32-column
-// block has two waves that take the groups of the tile in turn. In step f the
+// A workgroup owns a unit's 256 x COUT_T fp32 accumulator in LDS. Each
+// 32-column block has two waves that take the groups of the tile in turn
+// (group: 32 entries of one position's list, or 64 on dense maps). In step f the
 // wave of parity f % 2 multiplies group f and adds it to its rows of the LDS
 // accumulator (the old rows are requested before the MFMAs, so their latency
 // overlaps them), while its partner reads the B fragments of group f+1 and
@@ -468,10 +172,17 @@ struct CfgPP {
   static_assert(COUT_T % 32 == 0 && COUT_T <= 128, "COUT_T");
   static_assert(GCH % NT == 0 || NT % GCH == 0, "chunk split");
   static_assert(NCG % 4 == 0 && LB <= 4 && LE < 4, "schedule");
-  static_assert(GR == 32 || (GR == 64 && CIN <= 64), "64-row groups for Cin <= 64");
+  static_assert(GR == 32 || GR == 64, "GR");
+  static_assert(M * COUT_T * 4 + 2 * GCH * 16 <= 163840, "LDS");
 };
 
-template <int CIN, int COUT_T, bool K3, bool IS_BF16, int GR_>
+// NP > 1 splits the channels of each feature row into NP passes of CIN (the
+// 256-channel layer runs as two 128-channel passes over each unit): a unit
+// then takes NP runs of its schedule into the same accumulator, the first
+// pass's centre steps writing it and the last pass writing the outputs. Pass
+// p takes K steps p KS .. p KS + KS - 1 of the row's MFMA K order (channels
+// h CIN_T/2 + 8 st + j of lane half h), so the weights keep their layout.
+template <int CIN, int COUT_T, bool K3, bool IS_BF16, int GR_, int NP = 1>
 __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
     const int2* __restrict__ ent, const int32_t* __restrict__ tile_off,
     const uint16_t* __restrict__ tile_cnt, const int32_t* __restrict__ order, int64_t n,
@@ -482,6 +193,7 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
   static_assert(C::NT == 4 * COUT_T, "launch bounds");
   constexpr int M = C::M, GR = C::GR, NRB = C::NRB, KS = C::KS, RC = C::RC;
   constexpr int LB = C::LB, LE = C::LE, CPT = C::CPT, NCG = C::NCG;
+  constexpr int CIN_T = CIN * NP, KST = KS * NP;  // channels and K steps of a whole row
   __shared__ float4v acc[M * C::NQ];
   __shared__ half8 bt[2][C::GCH];
 
@@ -505,11 +217,13 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
   const int wc = w - par * C::NC;
 
   // ---- per-unit schedules ----
+  // The workgroup's s-th run of a schedule: unit j0 + (s / NP) wpx, pass s % NP.
   struct Raw {
-    int cnt, ent0, tile, ct;
+    int cnt, ent0, tile, ct, pass;
   };
-  auto raw_of = [&](int u) -> Raw {  // issue the loads of unit u's counts
-    Raw r{0, 0, -1, 0};
+  auto raw_of = [&](int s) -> Raw {  // issue the loads of run s's counts
+    Raw r{0, 0, -1, 0, s % NP};
+    const int u = j0 + (s / NP) * wpx;
     const int tl = u / n_ct;
     const int tile = xcd * tiles_per_xcd + tl;
     if (u < units && tl < tiles_per_xcd && tile < n_tiles) {
@@ -533,7 +247,7 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
   // unit's column tile.
   struct Half {
     int cnt, off, gs, wb;  // per lane
-    int F, Fp, c0, rows_here;
+    int F, Fp, c0, rows_here, pass;
     int64_t t0;
   };
   auto half_of = [&](const Raw& r) -> Half {  // the counts have arrived
@@ -549,11 +263,13 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
     hf.F = live ? __builtin_amdgcn_readlane(gs, kTaps3) : 0;
     hf.Fp = live ? NCG + ((hf.F - NCG + 3) & ~3) : 0;
     hf.gs = lane == 0 ? 0 : (lane <= kTaps3 ? gs : INT_MAX);
-    hf.wb = ((K3 ? tap_at(lane & 31) * (cout / 32) : 0) + r.ct * (COUT_T / 32)) * KS * 1024;
+    hf.wb = (((K3 ? tap_at(lane & 31) * (cout / 32) : 0) + r.ct * (COUT_T / 32)) * KST +
+             r.pass * KS) * 1024;
+    hf.pass = r.pass;
     return hf;
   };
   struct Grp {
-    int start, cnt, wb;
+    int start, cnt, wb, pass;
     int64_t t0;
   };
   // The stream's schedule: the current unit a in lanes 0..31, the next unit b
@@ -585,12 +301,13 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
     g.cnt = c < GR ? c : GR;  // <= 0 past the position's entries
     g.wb = __builtin_amdgcn_readlane(s_wb, p);
     g.t0 = p < 32 ? a.t0 : b.t0;
+    g.pass = NP == 1 ? 0 : (p < 32 ? a.pass : b.pass);
     return g;
   };
 
-  const __amdgpu_buffer_rsrc_t rf = make_rsrc(feats, static_cast<uint32_t>(n * CIN * 2));
+  const __amdgpu_buffer_rsrc_t rf = make_rsrc(feats, static_cast<uint32_t>(n * CIN_T * 2));
   const __amdgpu_buffer_rsrc_t rw =
-      make_rsrc(wp, static_cast<uint32_t>((K3 ? kTaps3 : 1) * CIN * cout * 2));
+      make_rsrc(wp, static_cast<uint32_t>((K3 ? kTaps3 : 1) * CIN_T * cout * 2));
   const __amdgpu_buffer_rsrc_t re = make_rsrc(ent, static_cast<uint32_t>(n_pairs + 1) * 8u);
   const uint32_t e_none = static_cast<uint32_t>(n_pairs) * 8u;
 
@@ -603,10 +320,14 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
     const int c = tid + C::NT * i;
     lrow[i] = c / RC;
     const int lc = c % RC;
-    lcol[i] = static_cast<uint32_t>(lc * 16);
+    // byte offset in the row of local chunk lc (K steps lc % KS of lane half
+    // lc / KS) in pass 0
+    lcol[i] = static_cast<uint32_t>(((lc / KS) * (CIN_T / 16) + lc % KS) * 16);
     lpos[i] = lrow[i] * RC + (lc ^ (lrow[i] & (RC - 1)));
   }
-  auto load_entries = [&](const Grp& g, int2 (&E)[CPT]) {
+  // entries of group g, and (ep) the pass its chunks are for
+  auto load_entries = [&](const Grp& g, int2 (&E)[CPT], int& ep) {
+    ep = g.pass;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const bool live = loader && lrow[i] < g.cnt;
@@ -618,10 +339,12 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
       }
     }
   };
-  auto load_chunks = [&](const int2 (&E)[CPT], half8 (&D)[CPT]) {
+  auto load_chunks = [&](const int2 (&E)[CPT], int ep, half8 (&D)[CPT]) {
+    const uint32_t pc = NP == 1 ? 0u : static_cast<uint32_t>(ep * KS * 16);
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
-      D[i] = bload_h8(rf, E[i].y >= 0 ? static_cast<uint32_t>(E[i].x) * (CIN * 2) + lcol[i] : kOob);
+      D[i] = bload_h8(rf, E[i].y >= 0 ? static_cast<uint32_t>(E[i].x) * (CIN_T * 2) + pc + lcol[i]
+                                      : kOob);
   };
   auto store_chunks = [&](int slot, const half8 (&D)[CPT]) {
     if (loader) {
@@ -641,12 +364,17 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
     }
   };
 
-  // ---- MFMA role (fragment layouts as in k_fwd_mfma) ----
+  // ---- MFMA role: the two waves of a block own its 32 output columns ----
+  // v_mfma_f32_32x32x16_f16 computes out^T for 32 rows of the group: A =
+  // weights (lane: column lane%32, K steps st of lane half lane/32, 8
+  // channels each), B = gathered rows (lane: slot lane%32, the same
+  // channels), D: lane holds slot lane%32 and columns 8*a + 4*(lane/32) + b
+  // in register 4*a + b.
   const int s32 = lane & 31;
   const int h = lane >> 5;
   const int qw = wc * 8;
   auto load_a = [&](const Grp& g, half8 (&A)[KS]) {
-    const uint32_t base = static_cast<uint32_t>(g.wb + wc * KS * 1024 + lane * 16);
+    const uint32_t base = static_cast<uint32_t>(g.wb + wc * KST * 1024 + lane * 16);
     // one select; the K-step offsets fold into the loads' immediate offsets
     const uint32_t b = g.cnt > 0 ? base : kOob;
 #pragma unroll
@@ -718,24 +446,25 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
   // and with them its memory-counter waits, are static.
   auto run = [&](auto parc) {
     constexpr int PAR = decltype(parc)::value;
-    int u = j0;
-    Half cur = half_of(raw_of(u));
-    Half nxt = half_of(raw_of(u + wpx));
-    Raw raw = raw_of(u + 2 * wpx);
+    int s = 0;
+    Half cur = half_of(raw_of(0));
+    Half nxt = half_of(raw_of(1));
+    Raw raw = raw_of(2);
     join(cur, nxt);
     auto grp = [&](int f) -> Grp { return group_at(cur, nxt, f); };
 
     int2 E[4][CPT];
+    int EP[4];
     half8 D[4][CPT];
     int RW[2][NRB];
     half8 AW[2][KS];
     half8 BF[NRB][KS];
 #pragma unroll
-    for (int g = 0; g < LB; ++g) load_entries(grp(g), E[g % 4]);
+    for (int g = 0; g < LB; ++g) load_entries(grp(g), E[g % 4], EP[g % 4]);
 #pragma unroll
-    for (int g = 0; g < LB; ++g) load_chunks(E[g % 4], D[g % 4]);
+    for (int g = 0; g < LB; ++g) load_chunks(E[g % 4], EP[g % 4], D[g % 4]);
 #pragma unroll
-    for (int g = LB; g < LB + LE; ++g) load_entries(grp(g), E[g % 4]);
+    for (int g = LB; g < LB + LE; ++g) load_entries(grp(g), E[g % 4], EP[g % 4]);
     if (PAR == 0) {
       load_a(grp(0), AW[0]);
       load_a(grp(2), AW[1]);
@@ -761,7 +490,9 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
         // (whose B-fragment reads would otherwise queue in front in LDS).
         float4v old[NRB][4];
         __builtin_amdgcn_s_setprio(3);
-        if (!centre_step) {
+        // the centre steps of the first pass write the accumulator
+        const bool first = centre_step && (NP == 1 || cur.pass == 0);
+        if (!first) {
 #pragma unroll
           for (int rb = 0; rb < NRB; ++rb) read_old(RW[(i >> 1) & 1][rb], old[rb]);
         }
@@ -769,12 +500,12 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
 #pragma unroll
           for (int rb = 0; rb < NRB; ++rb) {
             const float16v d = multiply(AW[(i >> 1) & 1], BF[rb]);
-            write_acc(RW[(i >> 1) & 1][rb], centre_step, old[rb], d);
+            write_acc(RW[(i >> 1) & 1][rb], first, old[rb], d);
           }
         }
         __builtin_amdgcn_s_setprio(0);
-        load_chunks(E[(i + LB) % 4], D[(i + LB) % 4]);
-        load_entries(grp(f + LB + LE), E[(i + LB + LE) % 4]);
+        load_chunks(E[(i + LB) % 4], EP[(i + LB) % 4], D[(i + LB) % 4]);
+        load_entries(grp(f + LB + LE), E[(i + LB + LE) % 4], EP[(i + LB + LE) % 4]);
       } else {
         // prepare this wave's next group, f+1. Its rows are requested
         // first: the memory counter completes in order, so the multiply's
@@ -783,8 +514,8 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
         __builtin_amdgcn_sched_barrier(0);
         read_b((i + 1) & 1, BF);
         load_a(grp(f + 3), AW[((i + 3) >> 1) & 1]);
-        load_chunks(E[(i + LB) % 4], D[(i + LB) % 4]);
-        load_entries(grp(f + LB + LE), E[(i + LB + LE) % 4]);
+        load_chunks(E[(i + LB) % 4], EP[(i + LB) % 4], D[(i + LB) % 4]);
+        load_entries(grp(f + LB + LE), E[(i + LB + LE) % 4], EP[(i + LB + LE) % 4]);
       }
       lds_barrier();
     };
@@ -798,15 +529,16 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
         }(std::make_integer_sequence<int, 4>{});
       }
       // the last step's barrier made every update visible
-      store_tile<COUT_T, C::NT, K3, IS_BF16>(acc, cur.rows_here, tid, bias, cur.c0, order, cur.t0,
-                                             out, cout);
+      if (NP == 1 || cur.pass == NP - 1)
+        store_tile<COUT_T, C::NT, K3, IS_BF16>(acc, cur.rows_here, tid, bias, cur.c0, order,
+                                               cur.t0, out, cout);
       if (nxt.F == 0) break;
       lds_barrier();  // the epilogue's reads are done before the next centre writes
       cur = nxt;
       nxt = half_of(raw);
       join(cur, nxt);
-      u += wpx;
-      raw = raw_of(u + 2 * wpx);
+      ++s;
+      raw = raw_of(s + 2);
     }
   };
   if (par == 0)
@@ -946,7 +678,7 @@ int cus_per_xcd() {
   return v;
 }
 
-template <int CIN, int COUT_T, bool K3, bool IS_BF16, int GR>
+template <int CIN, int COUT_T, bool K3, bool IS_BF16, int GR, int NP = 1>
 int launch_pp(const Map& m, const _Float16* feats, const _Float16* wp, const float* bias,
               _Float16* out, int cout, int n_tiles, int n_ct, int tiles_per_xcd, int n_pairs,
               hipStream_t stream) {
@@ -957,14 +689,15 @@ int launch_pp(const Map& m, const _Float16* feats, const _Float16* wp, const flo
   static const int per_cu = [] {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &nb, reinterpret_cast<const void*>(k_fwd_pp<CIN, COUT_T, K3, IS_BF16, GR>), C::NT, 0) !=
+            &nb, reinterpret_cast<const void*>(k_fwd_pp<CIN, COUT_T, K3, IS_BF16, GR, NP>), C::NT,
+            0) !=
         hipSuccess)
       nb = 1;
     return std::max(1, nb);
   }();
   const int64_t units_per_xcd = int64_t{tiles_per_xcd} * n_ct;
   const int64_t wpx = std::min<int64_t>(units_per_xcd, int64_t{cus_per_xcd()} * per_cu);
-  k_fwd_pp<CIN, COUT_T, K3, IS_BF16, GR><<<static_cast<unsigned>(8 * wpx), C::NT, 0, stream>>>(
+  k_fwd_pp<CIN, COUT_T, K3, IS_BF16, GR, NP><<<static_cast<unsigned>(8 * wpx), C::NT, 0, stream>>>(
       K3 ? m.ent : nullptr, K3 ? m.tile_off : nullptr, K3 ? m.tile_cnt : nullptr,
       K3 ? m.order : nullptr, m.n, feats, wp, bias, out, cout, n_tiles, n_ct, tiles_per_xcd,
       n_pairs);
@@ -981,26 +714,31 @@ int launch_one(const Map& m, const _Float16* feats, const _Float16* wp, const fl
   const int n_tiles = static_cast<int>(n_tiles64);
   const int n_ct = cout / COUT_T;
   const int tiles_per_xcd = (n_tiles + 7) / 8;
-  const int64_t blocks = int64_t{8} * tiles_per_xcd * n_ct;
   const int n_pairs = static_cast<int>(K3 ? m.active_pairs : 0);
+  // dense maps (many groups per position) take 64-row groups: half the
+  // steps, each weight load serving two MFMA row blocks. At 128 channels a
+  // pass that fits the LDS only with 128 columns (exactly 160 KiB); narrower
+  // column tiles keep 32-row groups, and two or more workgroups per CU.
+  bool dense = false;
+  if constexpr (K3 && (CIN <= 64 || COUT_T == 128)) {
+    int64_t off_groups = 0;
+    for (int q = 1; q < kTaps3; ++q) off_groups += m.pos_groups[q];
+    dense = off_groups >= int64_t{kDenseGroups} * (kTaps3 - 1) * n_tiles;
+  }
   if constexpr (CIN <= 128) {
-    // dense maps (many groups per position) take 64-row groups at Cin <= 64:
-    // half the steps, each weight load serving two MFMA row blocks
-    if constexpr (CIN <= 64 && K3) {
-      int64_t off_groups = 0;
-      for (int q = 1; q < kTaps3; ++q) off_groups += m.pos_groups[q];
-      if (off_groups >= int64_t{kDenseGroups} * (kTaps3 - 1) * n_tiles)
-        return launch_pp<CIN, COUT_T, K3, IS_BF16, 64>(m, feats, wp, bias, out, cout, n_tiles, n_ct,
-                                                      tiles_per_xcd, n_pairs, stream);
-    }
+    if (dense)
+      return launch_pp<CIN, COUT_T, K3, IS_BF16, 64>(m, feats, wp, bias, out, cout, n_tiles, n_ct,
+                                                    tiles_per_xcd, n_pairs, stream);
     return launch_pp<CIN, COUT_T, K3, IS_BF16, 32>(m, feats, wp, bias, out, cout, n_tiles, n_ct,
                                                   tiles_per_xcd, n_pairs, stream);
   } else {
-    k_fwd_mfma<CIN, COUT_T, K3, IS_BF16><<<static_cast<unsigned>(blocks), Cfg<CIN, COUT_T, K3>::NT, 0,
-                                      stream>>>(
-        K3 ? m.ent : nullptr, K3 ? m.tile_off : nullptr, K3 ? m.tile_cnt : nullptr,
-        K3 ? m.order : nullptr, m.n, feats, wp, bias, out, cout, n_tiles, n_ct, tiles_per_xcd,
-        n_pairs);
+    // 256 channels: two 128-channel passes over each unit
+    static_assert(CIN == 256, "CIN");
+    if (dense)
+      return launch_pp<128, COUT_T, K3, IS_BF16, 64, 2>(m, feats, wp, bias, out, cout, n_tiles,
+                                                       n_ct, tiles_per_xcd, n_pairs, stream);
+    return launch_pp<128, COUT_T, K3, IS_BF16, 32, 2>(m, feats, wp, bias, out, cout, n_tiles, n_ct,
+                                                     tiles_per_xcd, n_pairs, stream);
   }
   SUBMCONV_HIP_CHECK(hipGetLastError());
   return SUBMCONV_OK;

@@ -460,10 +460,12 @@ def test_bf16_c3_sampled_and_input_grad(dev):
 
 @gpu
 @pytest.mark.parametrize("cin,cout,dtype", [(32, 32, "fp16"), (64, 32, "bf16"), (32, 128, "fp16"),
-                                            (64, 64, "bf16")])
+                                            (64, 64, "bf16"), (128, 128, "fp16"), (128, 128, "bf16"),
+                                            (256, 128, "bf16"), (256, 256, "fp16")])
 def test_dense_maps_64row_groups(dev, cin, cout, dtype):
-    # 95 % occupancy: ~240 entries per position and tile, so the Cin <= 64
-    # forward takes 64-row groups; every row against the oracle
+    # 95 % occupancy: ~240 entries per position and tile, so the forward takes
+    # 64-row groups (Cin <= 64, or 128-channel passes with 128 columns);
+    # every row against the oracle
     sc = _sc()
     seed = 700 + cin + cout
     _say(f"[dense {cin}->{cout} {dtype}]")
