@@ -157,7 +157,11 @@ struct CfgPP {
   static constexpr int GR = GR_;             // rows per group: 32, or 64 for dense maps
   static constexpr int NRB = GR / 32;        // 32-row MFMA blocks per group
   static constexpr int NC = COUT_T / 32;     // column blocks
-  static constexpr int NW = 2 * NC;          // waves: two per column block
+  // waves sharing a group's row blocks: narrow tiles of 64-row groups split
+  // them, so that a step's work is spread over more waves
+  static constexpr int RS = (GR == 64 && COUT_T <= 64) ? 2 : 1;
+  static constexpr int NRBW = NRB / RS;      // row blocks per wave
+  static constexpr int NW = 2 * NC * RS;     // waves: two per column block and row split
   static constexpr int NT = 64 * NW;
   static constexpr int KS = CIN / 16;
   static constexpr int NQ = COUT_T / 4;
@@ -183,15 +187,14 @@ struct CfgPP {
 // p takes K steps p KS .. p KS + KS - 1 of the row's MFMA K order (channels
 // h CIN_T/2 + 8 st + j of lane half h), so the weights keep their layout.
 template <int CIN, int COUT_T, bool K3, bool IS_BF16, int GR_, int NP = 1>
-__global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
+__global__ __launch_bounds__((CfgPP<CIN, COUT_T, K3, GR_>::NT)) void k_fwd_pp(
     const int2* __restrict__ ent, const int32_t* __restrict__ tile_off,
     const uint16_t* __restrict__ tile_cnt, const int32_t* __restrict__ order, int64_t n,
     const _Float16* __restrict__ feats, const _Float16* __restrict__ wp,
     const float* __restrict__ bias, _Float16* __restrict__ out, int cout, int n_tiles, int n_ct,
     int tiles_per_xcd, int n_pairs) {
   using C = CfgPP<CIN, COUT_T, K3, GR_>;
-  static_assert(C::NT == 4 * COUT_T, "launch bounds");
-  constexpr int M = C::M, GR = C::GR, NRB = C::NRB, KS = C::KS, RC = C::RC;
+  constexpr int M = C::M, GR = C::GR, NRBW = C::NRBW, KS = C::KS, RC = C::RC;
   constexpr int LB = C::LB, LE = C::LE, CPT = C::CPT, NCG = C::NCG;
   constexpr int CIN_T = CIN * NP, KST = KS * NP;  // channels and K steps of a whole row
   __shared__ float4v acc[M * C::NQ];
@@ -213,8 +216,10 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int par = w / C::NC;   // the parity of the groups this wave multiplies
-  const int wc = w - par * C::NC;
+  const int par = w / (C::NC * C::RS);  // the parity of the groups this wave multiplies
+  const int wr = w - par * C::NC * C::RS;
+  const int wc = wr % C::NC;            // its column block
+  const int rb0 = (wr / C::NC) * NRBW;  // and its first row block
 
   // ---- per-unit schedules ----
   // The workgroup's s-th run of a schedule: unit j0 + (s / NP) wpx, pass s % NP.
@@ -353,10 +358,10 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
     }
   };
   // row in tile of this lane's slot in each 32-row block of group g (-1: none)
-  auto load_row = [&](const Grp& g, int (&R)[NRB]) {
+  auto load_row = [&](const Grp& g, int (&R)[NRBW]) {
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      const int sl = (lane & 31) + 32 * rb;
+    for (int rb = 0; rb < NRBW; ++rb) {
+      const int sl = (lane & 31) + 32 * (rb0 + rb);
       if (K3)
         R[rb] = bload_i2(re, sl < g.cnt ? static_cast<uint32_t>(g.start + sl) * 8u : e_none).y;
       else
@@ -386,13 +391,13 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
     const int lc = h * (CIN / 16) + st;
     boff[st] = s32 * RC + (lc ^ (s32 & (RC - 1)));
   }
-  // B fragments of each 32-row block (block rb: rows 32 rb.., the same
-  // swizzle since 32 rb is a multiple of RC)
-  auto read_b = [&](int slot, half8 (&B)[NRB][KS]) {
+  // B fragments of this wave's 32-row blocks (block rb: rows 32 rb.., the
+  // same swizzle since 32 rb is a multiple of RC)
+  auto read_b = [&](int slot, half8 (&B)[NRBW][KS]) {
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
+    for (int rb = 0; rb < NRBW; ++rb)
 #pragma unroll
-      for (int st = 0; st < KS; ++st) B[rb][st] = bt[slot][boff[st] + 32 * rb * RC];
+      for (int st = 0; st < KS; ++st) B[rb][st] = bt[slot][boff[st] + 32 * (rb0 + rb) * RC];
   };
   auto multiply = [&](const half8 (&A)[KS], const half8 (&B)[KS]) {
     float16v d = {};
@@ -456,9 +461,9 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
     int2 E[4][CPT];
     int EP[4];
     half8 D[4][CPT];
-    int RW[2][NRB];
+    int RW[2][NRBW];
     half8 AW[2][KS];
-    half8 BF[NRB][KS];
+    half8 BF[NRBW][KS];
 #pragma unroll
     for (int g = 0; g < LB; ++g) load_entries(grp(g), E[g % 4], EP[g % 4]);
 #pragma unroll
@@ -488,17 +493,17 @@ __global__ __launch_bounds__(4 * COUT_T) void k_fwd_pp(
         // requested before the MFMAs so that their latency overlaps them.
         // This chain ends the step, so the wave issues ahead of its partner
         // (whose B-fragment reads would otherwise queue in front in LDS).
-        float4v old[NRB][4];
+        float4v old[NRBW][4];
         __builtin_amdgcn_s_setprio(3);
         // the centre steps of the first pass write the accumulator
         const bool first = centre_step && (NP == 1 || cur.pass == 0);
         if (!first) {
 #pragma unroll
-          for (int rb = 0; rb < NRB; ++rb) read_old(RW[(i >> 1) & 1][rb], old[rb]);
+          for (int rb = 0; rb < NRBW; ++rb) read_old(RW[(i >> 1) & 1][rb], old[rb]);
         }
         if (centre_step || f < cur.F) {
 #pragma unroll
-          for (int rb = 0; rb < NRB; ++rb) {
+          for (int rb = 0; rb < NRBW; ++rb) {
             const float16v d = multiply(AW[(i >> 1) & 1], BF[rb]);
             write_acc(RW[(i >> 1) & 1][rb], first, old[rb], d);
           }
@@ -726,9 +731,10 @@ int launch_one(const Map& m, const _Float16* feats, const _Float16* wp, const fl
     dense = off_groups >= int64_t{kDenseGroups} * (kTaps3 - 1) * n_tiles;
   }
   if constexpr (CIN <= 128) {
-    if (dense)
-      return launch_pp<CIN, COUT_T, K3, IS_BF16, 64>(m, feats, wp, bias, out, cout, n_tiles, n_ct,
-                                                    tiles_per_xcd, n_pairs, stream);
+    if constexpr (CIN <= 64 || COUT_T == 128)
+      if (dense)
+        return launch_pp<CIN, COUT_T, K3, IS_BF16, 64>(m, feats, wp, bias, out, cout, n_tiles,
+                                                      n_ct, tiles_per_xcd, n_pairs, stream);
     return launch_pp<CIN, COUT_T, K3, IS_BF16, 32>(m, feats, wp, bias, out, cout, n_tiles, n_ct,
                                                   tiles_per_xcd, n_pairs, stream);
   } else {
