@@ -92,7 +92,12 @@ __device__ __forceinline__ int2 bload_i2(__amdgpu_buffer_rsrc_t r, uint32_t off)
 
 // Epilogue of the MFMA kernel: the tile's fp32 accumulator rows (float4
 // chunk q of row r at r*NQ + (q ^ (r % NQ))) plus the bias, rounded once to
-// fp16 (round to nearest even) and stored at the caller's row.
+// fp16 (round to nearest even) and stored at the caller's row. Thread tid
+// takes 8 columns c8 = tid % C8 of rows tid / C8 + RPI k. The loop is
+// instantiated per presence of bias and order, so that the common case
+// issues no vector loads (a wait for one would also wait for the next unit's
+// loads already in flight). The outputs are not read again here: streaming
+// (non-temporal) stores.
 template <int COUT_T, int NT, bool K3, bool IS_BF16>
 __device__ __forceinline__ void store_tile(const float4v* acc, int rows_here, int tid,
                                            const float* __restrict__ bias, int c0,
@@ -100,28 +105,51 @@ __device__ __forceinline__ void store_tile(const float4v* acc, int rows_here, in
                                            _Float16* __restrict__ out, int cout) {
   constexpr int NQ = COUT_T / 4;
   constexpr int C8 = COUT_T / 8;
-  for (int idx = tid; idx < rows_here * C8; idx += NT) {
-    const int r = idx / C8;
-    const int c8 = idx - r * C8;
-    const int q0 = 2 * c8, q1 = 2 * c8 + 1;
-    const float4v a = acc[r * NQ + (q0 ^ (r & (NQ - 1)))];
-    const float4v b = acc[r * NQ + (q1 ^ (r & (NQ - 1)))];
+  constexpr int RPI = NT / C8;  // rows per pass
+  static_assert(NT % C8 == 0 && kTileRows % RPI == 0, "epilogue split");
+  const int c8 = tid % C8;
+  const int r0 = tid / C8;
+  auto body = [&](auto hb, auto ho) {
+    constexpr bool HB = decltype(hb)::value, HO = decltype(ho)::value;
     float4v b0 = {0.f, 0.f, 0.f, 0.f}, b1 = {0.f, 0.f, 0.f, 0.f};
-    if (bias) {
+    if constexpr (HB) {
       b0 = *reinterpret_cast<const float4v*>(bias + c0 + 8 * c8);
       b1 = *reinterpret_cast<const float4v*>(bias + c0 + 8 * c8 + 4);
     }
-    half8 hv;
-    hv[0] = round16<IS_BF16>(a[0] + b0[0]);
-    hv[1] = round16<IS_BF16>(a[1] + b0[1]);
-    hv[2] = round16<IS_BF16>(a[2] + b0[2]);
-    hv[3] = round16<IS_BF16>(a[3] + b0[3]);
-    hv[4] = round16<IS_BF16>(b[0] + b1[0]);
-    hv[5] = round16<IS_BF16>(b[1] + b1[1]);
-    hv[6] = round16<IS_BF16>(b[2] + b1[2]);
-    hv[7] = round16<IS_BF16>(b[3] + b1[3]);
-    const int64_t orow = (K3 && order) ? order[t0 + r] : t0 + r;
-    *reinterpret_cast<half8*>(out + orow * cout + c0 + 8 * c8) = hv;
+#pragma unroll 2
+    for (int k = 0; k < kTileRows / RPI; ++k) {
+      const int r = r0 + RPI * k;
+      if (r < rows_here) {
+        const int q0 = 2 * c8, q1 = 2 * c8 + 1;
+        const float4v a = acc[r * NQ + (q0 ^ (r & (NQ - 1)))];
+        const float4v b = acc[r * NQ + (q1 ^ (r & (NQ - 1)))];
+        half8 hv;
+        hv[0] = round16<IS_BF16>(a[0] + b0[0]);
+        hv[1] = round16<IS_BF16>(a[1] + b0[1]);
+        hv[2] = round16<IS_BF16>(a[2] + b0[2]);
+        hv[3] = round16<IS_BF16>(a[3] + b0[3]);
+        hv[4] = round16<IS_BF16>(b[0] + b1[0]);
+        hv[5] = round16<IS_BF16>(b[1] + b1[1]);
+        hv[6] = round16<IS_BF16>(b[2] + b1[2]);
+        hv[7] = round16<IS_BF16>(b[3] + b1[3]);
+        const int64_t orow = HO ? order[t0 + r] : t0 + r;
+        __builtin_nontemporal_store(hv,
+                                    reinterpret_cast<half8*>(out + orow * cout + c0 + 8 * c8));
+      }
+    }
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  if (bias) {
+    if (K3 && order)
+      body(T{}, T{});
+    else
+      body(T{}, F{});
+  } else {
+    if (K3 && order)
+      body(F{}, T{});
+    else
+      body(F{}, F{});
   }
 }
 
