@@ -63,6 +63,13 @@ extern "C" {
  * instead of the hash table (the packing + sort + search lookup of "Running
  * TRELLIS.2 on a Mac (3/3)", section E); the map is the same */
 #define SUBMCONV_FLAG_SORTED_KEYS 2u
+/* tile size of the per-tile neighbour lists the forward streams: by default
+ * 288-row tiles when the map is sparse (under 32 entries per off-centre tap
+ * and 256-row tile on average) and they need fewer rounds of one tile per
+ * compute unit, else 256-row tiles; these flags force one size (the results
+ * are the same bit for bit) */
+#define SUBMCONV_FLAG_TILES_256 4u
+#define SUBMCONV_FLAG_TILES_288 8u
 
 /* 16-bit element types of features and weights (the *_dtype entry points). */
 #define SUBMCONV_DTYPE_F16 0  /* IEEE binary16 */
@@ -86,11 +93,13 @@ typedef struct submconv_map_s* submconv_map_t;
  * grid     host array of 3 positive extents.
  * flags    0 or SUBMCONV_FLAG_MORTON (iteration order only; results are the
  *          same bit for bit either way), optionally | SUBMCONV_FLAG_SORTED_KEYS
- *          (another lookup structure, the same map).
+ *          (another lookup structure, the same map) and at most one of
+ *          SUBMCONV_FLAG_TILES_256 / SUBMCONV_FLAG_TILES_288.
  * out_map  receives the handle (host pointer).
  *
  * The map is built on `stream`; the function then waits for that stream once
- * (to read back the validation flags and the active-pair count) and returns
+ * (to read back the validation flags and the active-pair count; a second
+ * time when it switches to 288-row tiles) and returns
  * SUBMCONV_ERR_COORD_OUT_OF_RANGE or SUBMCONV_ERR_DUPLICATE_COORD, with no
  * handle, when the sites are invalid. It allocates device memory
  * (27*n*4 bytes for the map, plus temporaries freed before return).
@@ -100,6 +109,10 @@ int submconv_build_map(const int32_t* coords, int64_t n, int32_t batch, const in
 
 /* Number of sites of the map. */
 int64_t submconv_map_num_rows(submconv_map_t map);
+
+/* Rows per tile of the map's per-tile neighbour lists: 256 or 288 (see
+ * SUBMCONV_FLAG_TILES_256). Negative on a bad argument. */
+int32_t submconv_map_tile_rows(submconv_map_t map);
 
 /* Number of (row, tap) pairs with a neighbour, the centre tap included
  * (ksize 3), or n (ksize 1). Effective work of a forward is

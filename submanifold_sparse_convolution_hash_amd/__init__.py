@@ -33,6 +33,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsubmconv.so")
 FLAG_MORTON = 1
 FLAG_SORTED_KEYS = 2
+FLAG_TILES_256 = 4
+FLAG_TILES_288 = 8
 PREP_INPUT_GRAD = 1
 _lib = None
 
@@ -62,6 +64,7 @@ def load_library():
     sig = {
         "submconv_build_map": ([P, I64, I32, P, U32, P, P], ctypes.c_int),
         "submconv_map_num_rows": ([P], I64),
+        "submconv_map_tile_rows": ([P], I32),
         "submconv_map_active_pairs": ([P, I32], I64),
         "submconv_map_export": ([P, P, P], ctypes.c_int),
         "submconv_map_order": ([P, P, P], ctypes.c_int),
@@ -146,6 +149,7 @@ class KernelMap:
         self.flags = int(flags)
         lib = load_library()
         self.num_rows = int(lib.submconv_map_num_rows(self._h))
+        self.tile_rows = int(lib.submconv_map_tile_rows(self._h))
 
     @property
     def handle(self) -> ctypes.c_void_p:
@@ -184,11 +188,16 @@ class KernelMap:
 
 
 def build_map(coords: torch.Tensor, grid: Sequence[int], batch: Optional[int] = None,
-              morton: bool = False, sorted_keys: bool = False) -> KernelMap:
+              morton: bool = False, sorted_keys: bool = False,
+              tile_rows: Optional[int] = None) -> KernelMap:
     """Hashes the sites ``coords`` ([N,4] int32 (b,x,y,z), device) and builds
-    their 3x3x3 neighbour map. Waits once for the stream (validation).
+    their 3x3x3 neighbour map. Waits for the stream (validation).
     ``sorted_keys`` finds neighbours by binary search in the sorted site keys
-    instead of the hash table (same map)."""
+    instead of the hash table (same map). ``tile_rows`` (256 or 288) forces
+    the tile size of the lists the forward streams (default: the library's
+    choice; the results are the same)."""
+    if tile_rows not in (None, 256, 288):
+        raise ValueError("tile_rows must be None, 256 or 288")
     _require(coords, "coords", torch.int32, 2)
     if coords.shape[1] != 4:
         raise ValueError("coords must be [N,4]")
@@ -198,6 +207,7 @@ def build_map(coords: torch.Tensor, grid: Sequence[int], batch: Optional[int] = 
     g = (ctypes.c_int32 * 3)(*[int(v) for v in grid])
     h = ctypes.c_void_p()
     flags = (FLAG_MORTON if morton else 0) | (FLAG_SORTED_KEYS if sorted_keys else 0)
+    flags |= {None: 0, 256: FLAG_TILES_256, 288: FLAG_TILES_288}[tile_rows]
     with torch.cuda.device(coords.device):
         _check(lib.submconv_build_map(_ptr(coords), coords.shape[0], int(batch), g, flags,
                                       _stream(coords.device), ctypes.byref(h)))

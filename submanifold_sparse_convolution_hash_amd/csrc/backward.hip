@@ -63,7 +63,7 @@ template <int CIN, int COUT>
 __global__ __launch_bounds__(2 * COUT) void k_bwd_weight(
     const int2* __restrict__ ent, const int32_t* __restrict__ tile_off,
     const uint16_t* __restrict__ tile_cnt, const int32_t* __restrict__ order, int64_t n,
-    int32_t n_tiles, int32_t K, int32_t tpr, const _Float16* __restrict__ feats,
+    int32_t n_tiles, int32_t tile_rows, int32_t K, int32_t tpr, const _Float16* __restrict__ feats,
     const _Float16* __restrict__ grad_out, float* __restrict__ partial, int32_t n_pairs) {
   using C = WCfg<CIN, COUT>;
   static_assert(C::NT == 2 * COUT, "launch bounds");
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(2 * COUT) void k_bwd_weight(
         uint32_t off = kOob;
         if (ych[i] < C::YC && g0 + ypair[i] < cnt) {
           const int2 e = ent[first + g0 + ypair[i]];
-          const int64_t t_row = int64_t{t} * kTileRows + e.y;
+          const int64_t t_row = int64_t{t} * tile_rows + e.y;
           const int64_t row = order ? order[t_row] : t_row;
           off = static_cast<uint32_t>(row) * (COUT * 2) + ych[i] * 16;
         }
@@ -256,7 +256,7 @@ template <int CIN, int COUT, bool ORD>
 __global__ __launch_bounds__((PCfg<CIN, COUT>::NT)) void k_bwd_weight_pp(
     const int2* __restrict__ ent, const int32_t* __restrict__ tile_off,
     const uint16_t* __restrict__ tile_cnt, const int32_t* __restrict__ order, int64_t n,
-    int32_t n_tiles, const WSplit ws, const _Float16* __restrict__ feats,
+    int32_t n_tiles, int32_t tile_rows, const WSplit ws, const _Float16* __restrict__ feats,
     const _Float16* __restrict__ grad_out, float* __restrict__ partial, int32_t n_pairs) {
   using C = PCfg<CIN, COUT>;
   constexpr int FC = C::FC, YC = C::YC, CF = C::CF, CY = C::CY, RB = C::RB, CB = C::CB;
@@ -383,7 +383,7 @@ __global__ __launch_bounds__((PCfg<CIN, COUT>::NT)) void k_bwd_weight_pp(
       Rows r;
       r.f = e.f.x;
       r.ylive = e.y.y >= 0;
-      const int t_row = g.tile * kTileRows + e.y.y;
+      const int t_row = g.tile * tile_rows + e.y.y;
       if constexpr (ORD)
         r.y = bload_i1(ro, r.ylive ? static_cast<uint32_t>(t_row) * 4u : kOob);
       else
@@ -664,10 +664,12 @@ int launch_w(const Map& m, int K, const _Float16* feats, const _Float16* grad_ou
     const unsigned blocks = static_cast<unsigned>(ws.blocks());
     if (m.order)
       k_bwd_weight_pp<CIN, COUT, true><<<blocks, NT, 0, stream>>>(
-          m.ent, m.tile_off, m.tile_cnt, m.order, m.n, nt, ws, feats, grad_out, partial, np);
+          m.ent, m.tile_off, m.tile_cnt, m.order, m.n, nt, m.tile_rows, ws, feats, grad_out, partial,
+          np);
     else
       k_bwd_weight_pp<CIN, COUT, false><<<blocks, NT, 0, stream>>>(
-          m.ent, m.tile_off, m.tile_cnt, m.order, m.n, nt, ws, feats, grad_out, partial, np);
+          m.ent, m.tile_off, m.tile_cnt, m.order, m.n, nt, m.tile_rows, ws, feats, grad_out, partial,
+          np);
     SUBMCONV_HIP_CHECK(hipGetLastError());
     const int64_t chunks = (int64_t{CIN} * COUT / 4 + 63) / 64;
     k_bwd_weight_reduce_pp<<<static_cast<unsigned>(ws.np * chunks), 256, 0, stream>>>(
@@ -676,7 +678,8 @@ int launch_w(const Map& m, int K, const _Float16* feats, const _Float16* grad_ou
     const Runs r = runs_for(m, K);
     const int64_t total = static_cast<int64_t>(K) * CIN * COUT;
     k_bwd_weight<CIN, COUT><<<static_cast<unsigned>(r.runs * K), WCfg<CIN, COUT>::NT, 0, stream>>>(
-        m.ent, m.tile_off, m.tile_cnt, m.order, m.n, nt, K, r.tpr, feats, grad_out, partial, np);
+        m.ent, m.tile_off, m.tile_cnt, m.order, m.n, nt, m.tile_rows, K, r.tpr, feats, grad_out,
+        partial, np);
     SUBMCONV_HIP_CHECK(hipGetLastError());
     k_bwd_weight_reduce<<<static_cast<unsigned>((total + 255) / 256), 256, 0, stream>>>(
         partial, r.runs, K, CIN, COUT, dw);

@@ -98,7 +98,7 @@ __device__ __forceinline__ int2 bload_i2(__amdgpu_buffer_rsrc_t r, uint32_t off)
 // issues no vector loads (a wait for one would also wait for the next unit's
 // loads already in flight). The outputs are not read again here: streaming
 // (non-temporal) stores.
-template <int COUT_T, int NT, bool K3, bool IS_BF16>
+template <int COUT_T, int NT, bool K3, bool IS_BF16, int M>
 __device__ __forceinline__ void store_tile(const float4v* acc, int rows_here, int tid,
                                            const float* __restrict__ bias, int c0,
                                            const int32_t* __restrict__ order, int64_t t0,
@@ -106,7 +106,7 @@ __device__ __forceinline__ void store_tile(const float4v* acc, int rows_here, in
   constexpr int NQ = COUT_T / 4;
   constexpr int C8 = COUT_T / 8;
   constexpr int RPI = NT / C8;  // rows per pass
-  static_assert(NT % C8 == 0 && kTileRows % RPI == 0, "epilogue split");
+  static_assert(NT % C8 == 0 && M % RPI == 0, "epilogue split");
   const int c8 = tid % C8;
   const int r0 = tid / C8;
   auto body = [&](auto hb, auto ho) {
@@ -117,7 +117,7 @@ __device__ __forceinline__ void store_tile(const float4v* acc, int rows_here, in
       b1 = *reinterpret_cast<const float4v*>(bias + c0 + 8 * c8 + 4);
     }
 #pragma unroll 2
-    for (int k = 0; k < kTileRows / RPI; ++k) {
+    for (int k = 0; k < M / RPI; ++k) {
       const int r = r0 + RPI * k;
       if (r < rows_here) {
         const int q0 = 2 * c8, q1 = 2 * c8 + 1;
@@ -179,9 +179,9 @@ typedef float float16v __attribute__((ext_vector_type(16)));
 // current one finishes and writes its outputs, and only the first unit pays
 // for filling the pipeline.
 
-template <int CIN, int COUT_T, bool K3, int GR_ = 32>
+template <int CIN, int COUT_T, bool K3, int GR_ = 32, int M_ = kTileRows>
 struct CfgPP {
-  static constexpr int M = kTileRows;
+  static constexpr int M = M_;               // rows per tile (the map's tile size)
   static constexpr int GR = GR_;             // rows per group: 32, or 64 for dense maps
   static constexpr int NRB = GR / 32;        // 32-row MFMA blocks per group
   static constexpr int NC = COUT_T / 32;     // column blocks
@@ -197,13 +197,14 @@ struct CfgPP {
   static constexpr int GCH = GR * RC;
   static constexpr int CPT = GCH >= NT ? GCH / NT : 1;
   static constexpr int NLOAD = GCH >= NT ? NT : GCH;
-  static constexpr int NCG = M / GR;
+  static constexpr int NCG = M / GR;         // steps of the centre
+  static constexpr int BR = (4 - NCG % 4) % 4;  // steps after them up to a multiple of 4
   static constexpr int LB = 4;               // chunks requested LB steps before the multiply
   static constexpr int LE = 2;               // entries LE steps before their chunks
   static_assert(CIN % 32 == 0 && CIN <= 128, "CIN");
   static_assert(COUT_T % 32 == 0 && COUT_T <= 128, "COUT_T");
   static_assert(GCH % NT == 0 || NT % GCH == 0, "chunk split");
-  static_assert(NCG % 4 == 0 && LB <= 4 && LE < 4, "schedule");
+  static_assert(M % GR == 0 && LB <= 4 && LE < 4, "schedule");
   static_assert(GR == 32 || GR == 64, "GR");
   static_assert(M * COUT_T * 4 + 2 * GCH * 16 <= 163840, "LDS");
 };
@@ -214,16 +215,16 @@ struct CfgPP {
 // pass's centre steps writing it and the last pass writing the outputs. Pass
 // p takes K steps p KS .. p KS + KS - 1 of the row's MFMA K order (channels
 // h CIN_T/2 + 8 st + j of lane half h), so the weights keep their layout.
-template <int CIN, int COUT_T, bool K3, bool IS_BF16, int GR_, int NP = 1>
-__global__ __launch_bounds__((CfgPP<CIN, COUT_T, K3, GR_>::NT)) void k_fwd_pp(
+template <int CIN, int COUT_T, bool K3, bool IS_BF16, int GR_, int NP = 1, int M_ = kTileRows>
+__global__ __launch_bounds__((CfgPP<CIN, COUT_T, K3, GR_, M_>::NT)) void k_fwd_pp(
     const int2* __restrict__ ent, const int32_t* __restrict__ tile_off,
     const uint16_t* __restrict__ tile_cnt, const int32_t* __restrict__ order, int64_t n,
     const _Float16* __restrict__ feats, const _Float16* __restrict__ wp,
     const float* __restrict__ bias, _Float16* __restrict__ out, int cout, int n_tiles, int n_ct,
     int tiles_per_xcd, int n_pairs) {
-  using C = CfgPP<CIN, COUT_T, K3, GR_>;
+  using C = CfgPP<CIN, COUT_T, K3, GR_, M_>;
   constexpr int M = C::M, GR = C::GR, NRBW = C::NRBW, KS = C::KS, RC = C::RC;
-  constexpr int LB = C::LB, LE = C::LE, CPT = C::CPT, NCG = C::NCG;
+  constexpr int LB = C::LB, LE = C::LE, CPT = C::CPT, NCG = C::NCG, BR = C::BR;
   constexpr int CIN_T = CIN * NP, KST = KS * NP;  // channels and K steps of a whole row
   __shared__ float4v acc[M * C::NQ];
   __shared__ half8 bt[2][C::GCH];
@@ -274,8 +275,9 @@ __global__ __launch_bounds__((CfgPP<CIN, COUT_T, K3, GR_>::NT)) void k_fwd_pp(
   // row in the tile for a 1x1x1 kernel), processed from step gs on (the
   // centre in NCG steps, then each position in steps of GR entries). Lane 27
   // is an empty position at step F, where the unit's steps end; the unit
-  // takes Fp steps (F rounded up to a multiple of 4 past the centre), so that
-  // step residues mod 4 carry over to the next unit. Lanes 28..31 start at
+  // takes Fp steps (F rounded up to a multiple of 4, and to at least the
+  // centre's steps rounded up), so that step residues mod 4 carry over to the
+  // next unit. Lanes 28..31 start at
   // no step. wb is the byte offset of the position's weights for the
   // unit's column tile.
   struct Half {
@@ -294,7 +296,7 @@ __global__ __launch_bounds__((CfgPP<CIN, COUT_T, K3, GR_>::NT)) void k_fwd_pp(
     const int ng = (lane >= 1 && lane < kTaps3) ? (hf.cnt + GR - 1) / GR : 0;
     const int gs = NCG + excl_scan_wave(ng, lane);
     hf.F = live ? __builtin_amdgcn_readlane(gs, kTaps3) : 0;
-    hf.Fp = live ? NCG + ((hf.F - NCG + 3) & ~3) : 0;
+    hf.Fp = live ? NCG + BR + ((max(hf.F - NCG - BR, 0) + 3) & ~3) : 0;
     hf.gs = lane == 0 ? 0 : (lane <= kTaps3 ? gs : INT_MAX);
     hf.wb = (((K3 ? tap_at(lane & 31) * (cout / 32) : 0) + r.ct * (COUT_T / 32)) * KST +
              r.pass * KS) * 1024;
@@ -556,15 +558,20 @@ __global__ __launch_bounds__((CfgPP<CIN, COUT_T, K3, GR_>::NT)) void k_fwd_pp(
       [&]<int... I>(std::integer_sequence<int, I...>) {
         (step(I, std::integral_constant<int, I % 4>{}, std::true_type{}), ...);
       }(std::make_integer_sequence<int, NCG>{});
-      for (int f0 = NCG; f0 < cur.Fp; f0 += 4) {
+      // steps up to a multiple of 4, so that the ring indices below are
+      // static and carry over to the next unit
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        (step(NCG + I, std::integral_constant<int, (NCG + I) % 4>{}, std::false_type{}), ...);
+      }(std::make_integer_sequence<int, BR>{});
+      for (int f0 = NCG + BR; f0 < cur.Fp; f0 += 4) {
         [&]<int... I>(std::integer_sequence<int, I...>) {
-          (step(f0 + I, std::integral_constant<int, (NCG + I) % 4>{}, std::false_type{}), ...);
+          (step(f0 + I, std::integral_constant<int, I>{}, std::false_type{}), ...);
         }(std::make_integer_sequence<int, 4>{});
       }
       // the last step's barrier made every update visible
       if (NP == 1 || cur.pass == NP - 1)
-        store_tile<COUT_T, C::NT, K3, IS_BF16>(acc, cur.rows_here, tid, bias, cur.c0, order,
-                                               cur.t0, out, cout);
+        store_tile<COUT_T, C::NT, K3, IS_BF16, M>(acc, cur.rows_here, tid, bias, cur.c0, order,
+                                                  cur.t0, out, cout);
       if (nxt.F == 0) break;
       lds_barrier();  // the epilogue's reads are done before the next centre writes
       cur = nxt;
@@ -711,26 +718,27 @@ int cus_per_xcd() {
   return v;
 }
 
-template <int CIN, int COUT_T, bool K3, bool IS_BF16, int GR, int NP = 1>
+template <int CIN, int COUT_T, bool K3, bool IS_BF16, int GR, int NP = 1, int M = kTileRows>
 int launch_pp(const Map& m, const _Float16* feats, const _Float16* wp, const float* bias,
               _Float16* out, int cout, int n_tiles, int n_ct, int tiles_per_xcd, int n_pairs,
               hipStream_t stream) {
-  using C = CfgPP<CIN, COUT_T, K3, GR>;
+  using C = CfgPP<CIN, COUT_T, K3, GR, M>;
   // persistent: as many workgroups as the CUs hold at once (one per CU when
   // the accumulator fills the LDS, more for narrow column tiles), dealt
   // evenly to the 8 XCDs
   static const int per_cu = [] {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &nb, reinterpret_cast<const void*>(k_fwd_pp<CIN, COUT_T, K3, IS_BF16, GR, NP>), C::NT,
-            0) !=
+            &nb, reinterpret_cast<const void*>(k_fwd_pp<CIN, COUT_T, K3, IS_BF16, GR, NP, M>),
+            C::NT, 0) !=
         hipSuccess)
       nb = 1;
     return std::max(1, nb);
   }();
   const int64_t units_per_xcd = int64_t{tiles_per_xcd} * n_ct;
   const int64_t wpx = std::min<int64_t>(units_per_xcd, int64_t{cus_per_xcd()} * per_cu);
-  k_fwd_pp<CIN, COUT_T, K3, IS_BF16, GR, NP><<<static_cast<unsigned>(8 * wpx), C::NT, 0, stream>>>(
+  k_fwd_pp<CIN, COUT_T, K3, IS_BF16, GR, NP, M><<<static_cast<unsigned>(8 * wpx), C::NT, 0,
+                                                 stream>>>(
       K3 ? m.ent : nullptr, K3 ? m.tile_off : nullptr, K3 ? m.tile_cnt : nullptr,
       K3 ? m.order : nullptr, m.n, feats, wp, bias, out, cout, n_tiles, n_ct, tiles_per_xcd,
       n_pairs);
@@ -741,7 +749,8 @@ int launch_pp(const Map& m, const _Float16* feats, const _Float16* wp, const flo
 template <int CIN, int COUT_T, bool K3, bool IS_BF16>
 int launch_one(const Map& m, const _Float16* feats, const _Float16* wp, const float* bias,
                _Float16* out, int cout, hipStream_t stream) {
-  const int64_t n_tiles64 = (m.n + kTileRows - 1) / kTileRows;
+  // a 3x3x3 forward streams the map's tiles; a 1x1x1 one tiles the rows itself
+  const int64_t n_tiles64 = K3 ? m.n_tiles : (m.n + kTileRows - 1) / kTileRows;
   if (n_tiles64 > (int64_t{1} << 28))
     return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "too many rows");
   const int n_tiles = static_cast<int>(n_tiles64);
@@ -757,6 +766,14 @@ int launch_one(const Map& m, const _Float16* feats, const _Float16* wp, const fl
     int64_t off_groups = 0;
     for (int q = 1; q < kTaps3; ++q) off_groups += m.pos_groups[q];
     dense = off_groups >= int64_t{kDenseGroups} * (kTaps3 - 1) * n_tiles;
+  }
+  if constexpr (K3) {
+    // maps of 288-row tiles (sparse, so never dense): 32-row groups
+    if (m.tile_rows == kTileRowsWide) {
+      constexpr int CP = CIN <= 128 ? CIN : 128, NP = CIN <= 128 ? 1 : 2;
+      return launch_pp<CP, COUT_T, K3, IS_BF16, 32, NP, kTileRowsWide>(
+          m, feats, wp, bias, out, cout, n_tiles, n_ct, tiles_per_xcd, n_pairs, stream);
+    }
   }
   if constexpr (CIN <= 128) {
     if constexpr (CIN <= 64 || COUT_T == 128)

@@ -232,16 +232,19 @@ __global__ void k_query_sorted(const int32_t* __restrict__ coords, const int32_t
   }
 }
 
-// Per tile of kTileRows processing rows: entries per processing position
-// (wave ballots over 64-row chunks) and the tile's total.
-__global__ __launch_bounds__(kTileRows) void k_tile_count(const int32_t* __restrict__ nbr, int64_t n,
-                                                          uint16_t* __restrict__ tile_cnt,
-                                                          int32_t* __restrict__ tile_tot) {
-  __shared__ int cnt[kTileRows / 64][kTaps3];
+// Per tile of TR processing rows: entries per processing position (wave
+// ballots over 64-row chunks; a block has TR rounded up to 64 threads) and
+// the tile's total.
+template <int TR>
+__global__ __launch_bounds__((TR + 63) / 64 * 64) void k_tile_count(
+    const int32_t* __restrict__ nbr, int64_t n, uint16_t* __restrict__ tile_cnt,
+    int32_t* __restrict__ tile_tot) {
+  constexpr int NWV = (TR + 63) / 64;
+  __shared__ int cnt[NWV][kTaps3];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTileRows + threadIdx.x;
-  const bool valid = t < n;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * TR + threadIdx.x;
+  const bool valid = static_cast<int>(threadIdx.x) < TR && t < n;
   for (int k = 0; k < kTaps3; ++k) {
     const uint64_t m = __ballot(valid && nbr[static_cast<int64_t>(k) * n + t] >= 0);
     if (lane == 0) cnt[w][k] = __popcll(m);
@@ -250,27 +253,29 @@ __global__ __launch_bounds__(kTileRows) void k_tile_count(const int32_t* __restr
   if (threadIdx.x < kTaps3) {
     const int k = tap_at(threadIdx.x);
     int c = 0;
-    for (int ww = 0; ww < kTileRows / 64; ++ww) c += cnt[ww][k];
+    for (int ww = 0; ww < NWV; ++ww) c += cnt[ww][k];
     tile_cnt[static_cast<int64_t>(blockIdx.x) * kTaps3 + threadIdx.x] = static_cast<uint16_t>(c);
   }
   if (threadIdx.x == 0) {
     int tot = 0;
     for (int k = 0; k < kTaps3; ++k)
-      for (int ww = 0; ww < kTileRows / 64; ++ww) tot += cnt[ww][k];
+      for (int ww = 0; ww < NWV; ++ww) tot += cnt[ww][k];
     tile_tot[blockIdx.x] = tot;
   }
 }
 
 // Writes the tile's entries {neighbour's caller row, row in tile}, ordered by
 // processing position, then row.
-__global__ __launch_bounds__(kTileRows) void k_tile_fill(const int32_t* __restrict__ nbr, int64_t n,
-                                                         const int32_t* __restrict__ tile_off,
-                                                         int2* __restrict__ ent) {
-  __shared__ uint64_t masks[kTaps3][kTileRows / 64];
+template <int TR>
+__global__ __launch_bounds__((TR + 63) / 64 * 64) void k_tile_fill(
+    const int32_t* __restrict__ nbr, int64_t n, const int32_t* __restrict__ tile_off,
+    int2* __restrict__ ent) {
+  constexpr int NWV = (TR + 63) / 64;
+  __shared__ uint64_t masks[kTaps3][NWV];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTileRows + threadIdx.x;
-  const bool valid = t < n;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * TR + threadIdx.x;
+  const bool valid = static_cast<int>(threadIdx.x) < TR && t < n;
   int32_t v[kTaps3];
   for (int k = 0; k < kTaps3; ++k) {
     v[k] = valid ? nbr[static_cast<int64_t>(k) * n + t] : -1;
@@ -283,7 +288,7 @@ __global__ __launch_bounds__(kTileRows) void k_tile_fill(const int32_t* __restri
   for (int p = 0; p < kTaps3; ++p) {
     const int k = tap_at(p);
     int before = 0, total = 0;
-    for (int ww = 0; ww < kTileRows / 64; ++ww) {
+    for (int ww = 0; ww < NWV; ++ww) {
       const int c = __popcll(masks[k][ww]);
       before += ww < w ? c : 0;
       total += c;
@@ -327,10 +332,24 @@ int bits_for(int64_t extent) {  // smallest b with 2^b >= extent (at least 1)
 // Device buffers freed on scope exit (temporaries of one build).
 struct DevBuf {
   void* p = nullptr;
-  ~DevBuf() {
+  void reset() {
     if (p) (void)hipFree(p);
+    p = nullptr;
   }
+  ~DevBuf() { reset(); }
 };
+
+// 288-row tiles when the map is sparse (fewer than one 32-entry group per
+// off-centre position of a 256-row tile on average, so that a tile's step
+// count barely grows with its rows) and they need fewer rounds of one tile
+// per compute unit: the forward's last round is then fuller.
+bool prefer_wide_tiles(int64_t n, int64_t pairs, int cus) {
+  if (n <= 0 || cus <= 0) return false;
+  if ((pairs - n) * kTileRows >= int64_t{kGroupRows} * (kTaps3 - 1) * n) return false;
+  const int64_t r256 = ((n + kTileRows - 1) / kTileRows + cus - 1) / cus;
+  const int64_t r288 = ((n + kTileRowsWide - 1) / kTileRowsWide + cus - 1) / cus;
+  return r288 < r256;
+}
 
 }  // namespace
 
@@ -362,8 +381,11 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   if (n < 0) return set_error(SUBMCONV_ERR_INVALID_ARG, "n = %lld is negative", (long long)n);
   if (n > 0 && !coords) return set_error(SUBMCONV_ERR_INVALID_ARG, "coords is NULL");
   if (batch < 1) return set_error(SUBMCONV_ERR_INVALID_ARG, "batch = %d < 1", batch);
-  if (flags & ~(SUBMCONV_FLAG_MORTON | SUBMCONV_FLAG_SORTED_KEYS))
+  if (flags & ~(SUBMCONV_FLAG_MORTON | SUBMCONV_FLAG_SORTED_KEYS | SUBMCONV_FLAG_TILES_256 |
+                SUBMCONV_FLAG_TILES_288))
     return set_error(SUBMCONV_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if ((flags & SUBMCONV_FLAG_TILES_256) && (flags & SUBMCONV_FLAG_TILES_288))
+    return set_error(SUBMCONV_ERR_INVALID_ARG, "flags ask for two tile sizes");
   for (int a = 0; a < 3; ++a)
     if (grid[a] < 1) return set_error(SUBMCONV_ERR_INVALID_ARG, "grid[%d] = %d < 1", a, grid[a]);
   if (n > INT32_MAX - 1)
@@ -507,16 +529,29 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   }
   BUILD_CHECK(hipGetLastError());
 
-  // per-tile compacted lists: counts, then tile offsets (exclusive scan)
-  const int64_t n_tiles = (n + kTileRows - 1) / kTileRows;
-  BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&tile_cnt), sizeof(uint16_t) * kTaps3 * n_tiles));
-  BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&tile_off), sizeof(int32_t) * (n_tiles + 1)));
-  BUILD_CHECK(hipMalloc(&tile_tot.p, sizeof(int32_t) * (n_tiles + 1)));
-  BUILD_CHECK(hipMemsetAsync(tile_tot.p, 0, sizeof(int32_t) * (n_tiles + 1), stream));
-  k_tile_count<<<static_cast<unsigned>(n_tiles), kTileRows, 0, stream>>>(
-      nbr, n, tile_cnt, static_cast<int32_t*>(tile_tot.p));
-  BUILD_CHECK(hipGetLastError());
-  {
+  // per-tile compacted lists of tr-row tiles: counts, tile offsets
+  // (exclusive scan), the active pairs and the groups per position, read back
+  int64_t n_tiles = 0;
+  uint64_t host_small[2 + kTaps3] = {};
+  auto count_tiles = [&](int tr) -> int {
+    if (tile_cnt) BUILD_CHECK(hipFree(tile_cnt));
+    if (tile_off) BUILD_CHECK(hipFree(tile_off));
+    tile_cnt = nullptr;
+    tile_off = nullptr;
+    tile_tot.reset();
+    scan_tmp.reset();
+    n_tiles = (n + tr - 1) / tr;
+    BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&tile_cnt), sizeof(uint16_t) * kTaps3 * n_tiles));
+    BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&tile_off), sizeof(int32_t) * (n_tiles + 1)));
+    BUILD_CHECK(hipMalloc(&tile_tot.p, sizeof(int32_t) * (n_tiles + 1)));
+    BUILD_CHECK(hipMemsetAsync(tile_tot.p, 0, sizeof(int32_t) * (n_tiles + 1), stream));
+    if (tr == kTileRowsWide)
+      k_tile_count<kTileRowsWide><<<static_cast<unsigned>(n_tiles), (kTileRowsWide + 63) / 64 * 64, 0,
+                                    stream>>>(nbr, n, tile_cnt, static_cast<int32_t*>(tile_tot.p));
+    else
+      k_tile_count<kTileRows><<<static_cast<unsigned>(n_tiles), kTileRows, 0, stream>>>(
+          nbr, n, tile_cnt, static_cast<int32_t*>(tile_tot.p));
+    BUILD_CHECK(hipGetLastError());
     size_t tmp_bytes = 0;
     BUILD_CHECK(rocprim::exclusive_scan(nullptr, tmp_bytes, static_cast<const int32_t*>(tile_tot.p),
                                         tile_off, 0, static_cast<size_t>(n_tiles + 1),
@@ -525,16 +560,18 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
     BUILD_CHECK(rocprim::exclusive_scan(scan_tmp.p, tmp_bytes, static_cast<const int32_t*>(tile_tot.p),
                                         tile_off, 0, static_cast<size_t>(n_tiles + 1),
                                         rocprim::plus<int32_t>(), stream));
-  }
-  // the active pairs in 64 bits (the int32 offsets are checked against it)
-  k_total<<<1, 1024, 0, stream>>>(static_cast<const int32_t*>(tile_tot.p), n_tiles, pairs);
-  BUILD_CHECK(hipGetLastError());
-  k_pos_groups<<<kTaps3, 256, 0, stream>>>(tile_cnt, n_tiles, pairs + 1);
-  BUILD_CHECK(hipGetLastError());
-
-  uint64_t host_small[2 + kTaps3] = {};
-  BUILD_CHECK(hipMemcpyAsync(host_small, small.p, sizeof(host_small), hipMemcpyDeviceToHost, stream));
-  BUILD_CHECK(hipStreamSynchronize(stream));
+    // the active pairs in 64 bits (the int32 offsets are checked against it)
+    k_total<<<1, 1024, 0, stream>>>(static_cast<const int32_t*>(tile_tot.p), n_tiles, pairs);
+    BUILD_CHECK(hipGetLastError());
+    k_pos_groups<<<kTaps3, 256, 0, stream>>>(tile_cnt, n_tiles, pairs + 1);
+    BUILD_CHECK(hipGetLastError());
+    BUILD_CHECK(hipMemcpyAsync(host_small, small.p, sizeof(host_small), hipMemcpyDeviceToHost,
+                               stream));
+    BUILD_CHECK(hipStreamSynchronize(stream));
+    return SUBMCONV_OK;
+  };
+  int tr = (flags & SUBMCONV_FLAG_TILES_288) ? kTileRowsWide : kTileRows;
+  if (const int st = count_tiles(tr); st != SUBMCONV_OK) return st;
   const uint32_t eflags = static_cast<uint32_t>(host_small[0]);
   if (eflags & kErrRange)
     return fail(set_error(SUBMCONV_ERR_COORD_OUT_OF_RANGE,
@@ -543,19 +580,33 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   if (eflags & kErrDuplicate)
     return fail(set_error(SUBMCONV_ERR_DUPLICATE_COORD, "a site occurs more than once"));
   m.active_pairs = static_cast<int64_t>(host_small[1]);
-  for (int q = 0; q < kTaps3; ++q) m.pos_groups[q] = static_cast<int64_t>(host_small[2 + q]);
   if (m.active_pairs >= INT32_MAX)
     return fail(set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "too many active pairs for int32 offsets"));
+  if (!(flags & (SUBMCONV_FLAG_TILES_256 | SUBMCONV_FLAG_TILES_288))) {
+    int cus = 256;
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, m.device);
+    if (prefer_wide_tiles(n, m.active_pairs, cus)) {
+      tr = kTileRowsWide;
+      if (const int st = count_tiles(tr); st != SUBMCONV_OK) return st;
+    }
+  }
+  for (int q = 0; q < kTaps3; ++q) m.pos_groups[q] = static_cast<int64_t>(host_small[2 + q]);
   // one more entry {-1, -1} after the lists: the target of masked loads
   BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&ent), sizeof(int2) * (m.active_pairs + 1)));
   BUILD_CHECK(hipMemsetAsync(ent + m.active_pairs, 0xff, sizeof(int2), stream));
-  k_tile_fill<<<static_cast<unsigned>(n_tiles), kTileRows, 0, stream>>>(nbr, n, tile_off, ent);
+  if (tr == kTileRowsWide)
+    k_tile_fill<kTileRowsWide><<<static_cast<unsigned>(n_tiles), (kTileRowsWide + 63) / 64 * 64, 0,
+                                 stream>>>(nbr, n, tile_off, ent);
+  else
+    k_tile_fill<kTileRows><<<static_cast<unsigned>(n_tiles), kTileRows, 0, stream>>>(nbr, n, tile_off,
+                                                                                    ent);
   BUILD_CHECK(hipGetLastError());
   // the forward may run on another stream: the map is complete on return
   BUILD_CHECK(hipStreamSynchronize(stream));
   m.nbr = nbr;
   m.order = order;
   m.n_tiles = n_tiles;
+  m.tile_rows = tr;
   m.tile_cnt = tile_cnt;
   m.tile_off = tile_off;
   m.ent = ent;
@@ -567,6 +618,11 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
 extern "C" int64_t submconv_map_num_rows(submconv_map_t map) {
   if (!map) return set_error(SUBMCONV_ERR_INVALID_ARG, "map is NULL");
   return map->m.n;
+}
+
+extern "C" int32_t submconv_map_tile_rows(submconv_map_t map) {
+  if (!map) return set_error(SUBMCONV_ERR_INVALID_ARG, "map is NULL");
+  return map->m.tile_rows;
 }
 
 extern "C" int64_t submconv_map_active_pairs(submconv_map_t map, int32_t ksize) {

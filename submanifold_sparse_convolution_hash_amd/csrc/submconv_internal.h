@@ -17,8 +17,10 @@ constexpr int kTaps3 = 27;
 constexpr int kCenterTap = 13;
 
 // Rows per output tile of the forward kernels; the map's per-tile lists are
-// built for this tile size.
+// built for this tile size, or for kTileRowsWide (Map.tile_rows) when that
+// spreads a sparse map more evenly over the compute units.
 constexpr int kTileRows = 256;
+constexpr int kTileRowsWide = 288;
 
 // Entries per group: the kernels take a tile's entries of one position 32
 // at a time (one MFMA operand block).
@@ -34,7 +36,7 @@ __host__ __device__ inline int tap_at(int p) {
 //  nbr      [27][n] int32, tap-major, rows in processing order t; each entry
 //           is the caller row of the neighbour at offset d_k, or -1.
 //  order    [n] int32, processing order t -> caller row; nullptr = identity.
-//  The same map as per-tile compacted lists (tiles of kTileRows consecutive
+//  The same map as per-tile compacted lists (tiles of tile_rows consecutive
 //  processing rows), the form the forward kernels stream:
 //  tile_cnt [n_tiles][27] uint16, entries per processing position p.
 //  tile_off [n_tiles + 1] int32, first entry of each tile.
@@ -51,6 +53,7 @@ struct Map {
   int32_t* nbr = nullptr;
   int32_t* order = nullptr;
   int64_t n_tiles = 0;
+  int32_t tile_rows = kTileRows;  // kTileRows or kTileRowsWide
   uint16_t* tile_cnt = nullptr;
   int32_t* tile_off = nullptr;
   int2* ent = nullptr;

@@ -66,6 +66,8 @@ def test_host_only_entry_points(lib):
     assert lib.submconv_build_map(None, -1, 1, g, 0, None, ctypes.byref(h)) == -1  # n < 0
     g0 = (ctypes.c_int32 * 3)(0, 4, 4)
     assert lib.submconv_build_map(None, 0, 1, g0, 0, None, ctypes.byref(h)) == -1  # grid[0] < 1
+    assert lib.submconv_build_map(None, 0, 1, g, 4 | 8, None, ctypes.byref(h)) == -1  # two tile sizes
+    assert lib.submconv_build_map(None, 0, 1, g, 16, None, ctypes.byref(h)) == -1  # unknown flag
     lib.submconv_forward.restype = ctypes.c_int
     assert lib.submconv_forward(None, None, None, None, None, 8, 8, 3, None) == -1  # map NULL
     lib.submconv_map_free.restype = ctypes.c_int

@@ -487,3 +487,76 @@ def test_dense_maps_64row_groups(dev, cin, cout, dtype):
                                wl.layers[0].bias)
     _assert_close(out, ref, f"dense {cin}->{cout} {dtype}")
     km.free()
+
+
+@gpu
+@pytest.mark.parametrize("cin,cout,dtype,morton,bias", [(128, 128, "fp16", False, False),
+                                                       (128, 128, "bf16", True, True),
+                                                       (256, 128, "fp16", False, True),
+                                                       (64, 32, "fp16", True, False),
+                                                       (32, 64, "bf16", False, False)])
+def test_tiles_288_same_results(dev, cin, cout, dtype, morton, bias):
+    # ~60k rows at 10 %: lists of 288-row tiles (209 tiles, a ragged last one)
+    # give bit-identical forward and input-gradient outputs to 256-row tiles
+    # (each row's products are summed in the same order); the weight gradient
+    # against the oracle; every forward row against the oracle
+    sc = _sc()
+    seed = 950 + cin + cout
+    wl = workloads.uniform_workload(85, 60000, [(3, cin, cout)], seed=seed,
+                                    bias_kind="normal" if bias else None, name="t288")
+    L = wl.layers[0]
+    _say(f"[tiles 288 {cin}->{cout} {dtype} morton={morton} bias={bias}] N={wl.n}")
+    coords = _to(dev, wl.coords)
+    km256 = sc.build_map(coords, wl.grid, wl.batch, morton=morton, tile_rows=256)
+    km288 = sc.build_map(coords, wl.grid, wl.batch, morton=morton, tile_rows=288)
+    assert (km256.tile_rows, km288.tile_rows) == (256, 288)
+    assert km256.active_pairs() == km288.active_pairs()
+    assert torch.equal(km256.export(), km288.export())
+    tdt = torch.float16 if dtype == "fp16" else torch.bfloat16
+    feats = _to(dev, wl.feats).to(tdt)
+    W = _to(dev, L.W).to(tdt)
+    b = _to(dev, L.bias) if bias else None
+    o256 = sc.forward(km256, feats, W, b)
+    o288 = sc.forward(km288, feats, W, b)
+    assert torch.equal(o256, o288), "forward differs between tile sizes"
+    g = torch.from_numpy(np.random.default_rng(seed).standard_normal((wl.n, cout)).astype(np.float16))
+    g = g.to(dev).to(tdt)
+    gi256 = sc.backward_input(km256, g, W)
+    gi288 = sc.backward_input(km288, g, W)
+    assert torch.equal(gi256, gi288), "input gradient differs between tile sizes"
+    if dtype == "fp16":
+        feats64 = wl.feats.astype(np.float64)
+        W64 = L.W.astype(np.float64)
+    else:
+        feats64 = feats.float().cpu().numpy().astype(np.float64)
+        W64 = W.float().cpu().numpy().astype(np.float64)
+    kref = oc.kernel_map(wl.coords, wl.grid, wl.batch, 3)
+    ref = oc.submconv_rows(kref, feats64, W64, L.bias if bias else None)
+    _assert_close(o288.float().cpu().numpy(), ref, f"t288 {cin}->{cout}")
+    if dtype == "fp16":
+        dw = sc.backward_weight(km288, feats, g, 3).cpu().numpy()
+        dref = oc.backward_weight(kref, wl.feats, g.cpu().numpy())
+        tol = 1e-3 + 1e-2 * np.abs(dref)
+        assert (np.abs(dw - dref) <= tol).all(), "weight gradient (288-row tiles)"
+    km256.free()
+    km288.free()
+
+
+@gpu
+def test_c3_map_takes_288_row_tiles(dev):
+    # 128^3 at 10 %: under one 32-entry group per off-centre position and
+    # 256-row tile, and 729 tiles of 288 rows fill three rounds of 256 CUs
+    # where 820 tiles of 256 rows need four
+    sc = _sc()
+    wl = workloads.make("c3_128_128")
+    km = sc.build_map(_to(dev, wl.coords), wl.grid, wl.batch)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    _say(f"[c3 tiles] CUs={cus} tile_rows={km.tile_rows}")
+    if cus == 256:
+        assert km.tile_rows == 288
+    # and a dense map keeps 256-row tiles
+    wd = workloads.random_small(17, G=14, occ=0.95, cin=8, cout=8, batch=2, ksize=3)
+    kd = sc.build_map(_to(dev, wd.coords), wd.grid, wd.batch)
+    assert kd.tile_rows == 256
+    km.free()
+    kd.free()
