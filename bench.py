@@ -47,10 +47,10 @@ CSRC = os.path.join(ROOT, "submanifold_sparse_convolution_hash_amd", "csrc")
 # A changed kernel source makes the entry stale and the reported traffic null.
 MEASURED_TRAFFIC = {
     ("c3_128_128", "forward"): {
-        "src": "forward.hip",
-        "sha256": "f1964e553b71fa1afab718d1630d02492266bb4af04420345908e2b0a82a3990",
-        "fetch_kib": 49913.47, "write_kib": 52428.75,
-        "fetch_factor": 524288.0 / 262169.375, "write_factor": 1.0},
+        "src": ["forward.hip", "map_build.hip"],  # the kernel, and the map's tile size
+        "sha256": "427a87d5af9889c75b0f994f2c01642e380b3556c70c381fbf5a9b11ab0f4b41",
+        "fetch_kib": 39158.51, "write_kib": 52429.96,
+        "fetch_factor": 524288.0 / 262177.3125, "write_factor": 524288.0 / 524290.5},
 }
 
 METRICS = {
@@ -83,15 +83,16 @@ def algorithmic_bytes(op, n, cin, cout, ksize, has_order, has_bias):
     return b
 
 
-def code_sha256(path):
-    """SHA-256 of a source file's code: // comments and blank lines removed,
+def code_sha256(*paths):
+    """SHA-256 of source files' code: // comments and blank lines removed,
     so that editing a comment does not invalidate counters taken on the code."""
     lines = []
-    with open(path) as f:
-        for line in f:
-            code = line.split("//", 1)[0].rstrip()
-            if code:
-                lines.append(code)
+    for path in paths:
+        with open(path) as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    lines.append(code)
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
@@ -101,7 +102,7 @@ def measured_traffic(config, op, morton):
     t = MEASURED_TRAFFIC.get((config, op))
     if t is None or morton:
         return None
-    if code_sha256(os.path.join(CSRC, t["src"])) != t["sha256"]:
+    if code_sha256(*(os.path.join(CSRC, f) for f in t["src"])) != t["sha256"]:
         return None
     return round((t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"]) * 1024)
 
