@@ -591,42 +591,48 @@ __global__ __launch_bounds__((CfgPP<CIN, COUT_T, K3, GR_, M_>::NT)) void k_fwd_p
 // VALU kernel for channel counts the MFMA tiles do not cover (multiples of 8)
 // ---------------------------------------------------------------------------
 
-template <bool IS_BF16>
+// One thread per (row, output column): consecutive threads take consecutive
+// columns of a row, so the row's neighbour indices and feature chunks are
+// shared loads and the weight loads and output stores are coalesced. The
+// neighbour indices are loaded first, all at once, and the taps are unrolled
+// with a select instead of a branch, so that the loads of successive taps
+// are in flight together (a tiny layer is otherwise a chain of load
+// latencies).
+template <bool K3, bool IS_BF16>
 __global__ __launch_bounds__(256) void k_fwd_valu(
-    const int32_t* __restrict__ nbr, const int32_t* __restrict__ order, int64_t n, int ksize,
+    const int32_t* __restrict__ nbr, const int32_t* __restrict__ order, int64_t n,
     const _Float16* __restrict__ feats, const _Float16* __restrict__ w,
     const float* __restrict__ bias, _Float16* __restrict__ out, int cin, int cout) {
-  const int c8n = cout / 8;
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= n * c8n) return;
-  const int64_t t = idx / c8n;
-  const int o8 = static_cast<int>(idx - t * c8n);
-  float a[8];
+  constexpr int K = K3 ? kTaps3 : 1;
+  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < n * cout;
+       idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t t = idx / cout;
+    const int o = static_cast<int>(idx - t * cout);
+    float a = bias ? bias[o] : 0.f;
+    int js[K];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) a[q] = bias ? bias[o8 * 8 + q] : 0.f;
-  const int K = ksize == 3 ? kTaps3 : 1;
-  for (int k = 0; k < K; ++k) {
-    int64_t j;
-    if (ksize == 3) {
-      j = nbr[static_cast<int64_t>(k) * n + t];
-      if (j < 0) continue;
-    } else {
-      j = t;
-    }
-    const _Float16* f = feats + j * cin;
-    const _Float16* wk = w + static_cast<int64_t>(k) * cin * cout + o8 * 8;
-    for (int c = 0; c < cin; ++c) {
-      const float fc = widen16<IS_BF16>(f[c]);
-      const half8 wv = *reinterpret_cast<const half8*>(wk + static_cast<int64_t>(c) * cout);
+    for (int k = 0; k < K; ++k)
+      js[k] = K3 ? nbr[static_cast<int64_t>(k) * n + t] : static_cast<int>(t);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) a[q] += fc * widen16<IS_BF16>(wv[q]);
+    for (int k = 0; k < K; ++k) {
+      // an absent neighbour reads row 0 and leaves the sum unchanged
+      const bool live = js[k] >= 0;
+      const half8* f8 =
+          reinterpret_cast<const half8*>(feats + static_cast<int64_t>(live ? js[k] : 0) * cin);
+      const _Float16* wk = w + static_cast<int64_t>(k) * cin * cout + o;
+      for (int c8 = 0; c8 < cin / 8; ++c8) {
+        const half8 fv = f8[c8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = fmaf(widen16<IS_BF16>(fv[e]),
+                               widen16<IS_BF16>(wk[static_cast<int64_t>(8 * c8 + e) * cout]), a);
+          a = live ? v : a;
+        }
+      }
     }
+    const int64_t orow = (K3 && order) ? order[t] : t;
+    out[orow * cout + o] = round16<IS_BF16>(a);
   }
-  half8 h;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) h[q] = round16<IS_BF16>(a[q]);
-  const int64_t orow = (ksize == 3 && order) ? order[t] : t;
-  *reinterpret_cast<half8*>(out + orow * cout + o8 * 8) = h;
 }
 
 // ---------------------------------------------------------------------------
@@ -827,11 +833,16 @@ int forward_typed(const Map& m, int ksize, int cin, int cout, const _Float16* fe
       default: break;
     }
   }
-  const int64_t items = m.n * (cout / 8);
+  const int64_t items = m.n * cout;
+  // a grid-stride loop over (row, column) items
+  const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((items + 255) / 256, 1 << 20));
   const int B = 256;
-  k_fwd_valu<IS_BF16><<<static_cast<unsigned>((items + B - 1) / B), B, 0, stream>>>(
-      ksize == 3 ? m.nbr : nullptr, ksize == 3 ? m.order : nullptr, m.n, ksize, feats, wp, bias,
-      out, cin, cout);
+  if (ksize == 3)
+    k_fwd_valu<true, IS_BF16><<<blocks, B, 0, stream>>>(
+        m.nbr, m.order, m.n, feats, wp, bias, out, cin, cout);
+  else
+    k_fwd_valu<false, IS_BF16><<<blocks, B, 0, stream>>>(
+        nullptr, nullptr, m.n, feats, wp, bias, out, cin, cout);
   SUBMCONV_HIP_CHECK(hipGetLastError());
   return SUBMCONV_OK;
 }
