@@ -149,7 +149,8 @@ int64_t submconv_prepared_weights_elems(int32_t ksize, int32_t cin, int32_t cout
  * bf16 weights alike.
  * W   [K,Cin,Cout] fp16, device, out = feats @ W[k] per tap (k as above).
  * Wp  device buffer of submconv_prepared_weights_elems(...) fp16 elements,
- *     caller-allocated; its content is an opaque, shape-specific layout.
+ *     caller-allocated, 16-byte aligned (SUBMCONV_ERR_INVALID_ARG
+ *     otherwise); its content is an opaque, shape-specific layout.
  * Prepared weights stay valid for every forward with the same ksize, Cin and
  * Cout. Asynchronous on `stream`; W and Wp must not overlap.
  */

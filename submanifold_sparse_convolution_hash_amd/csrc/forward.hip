@@ -655,23 +655,26 @@ __device__ __forceinline__ _Float16 weight_at(const _Float16* __restrict__ W, in
 // for tap k, 32-column block cb, 16-channel K step st and lane l, 8
 // consecutive fp16 values W_t[k][ci][co] with co = 32*cb + (l % 32) and
 // ci = (l / 32) * (Cin / 2) + 8*st + j, j = 0..7: one contiguous 1 KiB run per
-// (k, cb, st), loaded by a wave with one 16-byte load per lane.
+// (k, cb, st), loaded by a wave with one 16-byte load per lane. One thread
+// writes one lane's 8 values (a 16-byte store).
 __global__ void k_prepare_mfma(const _Float16* __restrict__ W, int K, int cin, int cout, bool grad,
                                _Float16* __restrict__ wp) {
-  const int64_t total = static_cast<int64_t>(K) * cin * cout;
+  const int64_t total8 = static_cast<int64_t>(K) * cin * cout / 8;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
+  if (idx >= total8) return;
   const int KS = cin / 16;
-  const int j = static_cast<int>(idx & 7);
-  const int l = static_cast<int>((idx >> 3) & 63);
-  int64_t rest = idx >> 9;
+  const int l = static_cast<int>(idx & 63);
+  int64_t rest = idx >> 6;
   const int st = static_cast<int>(rest % KS);
   rest /= KS;
   const int cb = static_cast<int>(rest % (cout / 32));
   const int k = static_cast<int>(rest / (cout / 32));
   const int co = 32 * cb + (l & 31);
-  const int ci = (l >> 5) * (cin / 2) + 8 * st + j;
-  wp[idx] = weight_at(W, K, cin, cout, grad, k, ci, co);
+  const int ci0 = (l >> 5) * (cin / 2) + 8 * st;
+  half8 v;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = weight_at(W, K, cin, cout, grad, k, ci0 + j, co);
+  *reinterpret_cast<half8*>(wp + 8 * idx) = v;
 }
 
 // Natural order W_t[k][ci][co] (the VALU kernel's layout).
@@ -865,6 +868,8 @@ extern "C" int submconv_prepare_weights_ex(const uint16_t* W, int32_t ksize, int
   const int st = check_shape(ksize, cin, cout);
   if (st != SUBMCONV_OK) return st;
   if (!W || !Wp) return set_error(SUBMCONV_ERR_INVALID_ARG, "W or Wp is NULL");
+  if (reinterpret_cast<uintptr_t>(Wp) & 15)
+    return set_error(SUBMCONV_ERR_INVALID_ARG, "Wp must be 16-byte aligned");
   if (flags & ~SUBMCONV_PREP_INPUT_GRAD)
     return set_error(SUBMCONV_ERR_INVALID_ARG, "unknown preparation flags 0x%x", flags);
   const bool grad = flags & SUBMCONV_PREP_INPUT_GRAD;
@@ -877,7 +882,8 @@ extern "C" int submconv_prepare_weights_ex(const uint16_t* W, int32_t ksize, int
   const _Float16* w = reinterpret_cast<const _Float16*>(W);
   _Float16* p = reinterpret_cast<_Float16*>(Wp);
   if (use_mfma(cin_t, cout_t))
-    k_prepare_mfma<<<grid, B, 0, stream>>>(w, K, cin_t, cout_t, grad, p);
+    k_prepare_mfma<<<static_cast<unsigned>((total / 8 + B - 1) / B), B, 0, stream>>>(w, K, cin_t,
+                                                                                    cout_t, grad, p);
   else
     k_prepare_plain<<<grid, B, 0, stream>>>(w, K, cin_t, cout_t, grad, p);
   SUBMCONV_HIP_CHECK(hipGetLastError());
