@@ -560,3 +560,69 @@ def test_c3_map_takes_288_row_tiles(dev):
     assert kd.tile_rows == 256
     km.free()
     kd.free()
+
+
+@gpu
+def test_two_streams_share_a_map(dev):
+    # one immutable map serves forwards on two side streams at once; each
+    # stream's outputs equal the same forward run alone
+    sc = _sc()
+    wl = workloads.uniform_workload(48, 11000, [(3, 64, 64)], seed=1201, bias_kind="normal", name="st")
+    L = wl.layers[0]
+    km = sc.build_map(_to(dev, wl.coords), wl.grid, wl.batch)
+    rng = np.random.default_rng(1202)
+    fa = _to(dev, rng.standard_normal((wl.n, 64)).astype(np.float16))
+    fb = _to(dev, rng.standard_normal((wl.n, 64)).astype(np.float16))
+    W, b = _to(dev, L.W), _to(dev, L.bias)
+    wp = sc.prepare_weights(W)
+    ra = sc.forward(km, fa, prepared=wp, bias=b, ksize=3, cout=64)
+    rb = sc.forward(km, fb, prepared=wp, bias=b, ksize=3, cout=64)
+    oa = torch.empty_like(ra)
+    ob = torch.empty_like(rb)
+    s1, s2 = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
+    s1.wait_stream(torch.cuda.current_stream(dev))
+    s2.wait_stream(torch.cuda.current_stream(dev))
+    for _ in range(4):
+        with torch.cuda.stream(s1):
+            sc.forward(km, fa, prepared=wp, bias=b, ksize=3, cout=64, out=oa)
+        with torch.cuda.stream(s2):
+            sc.forward(km, fb, prepared=wp, bias=b, ksize=3, cout=64, out=ob)
+    torch.cuda.current_stream(dev).wait_stream(s1)
+    torch.cuda.current_stream(dev).wait_stream(s2)
+    torch.cuda.synchronize(dev)
+    assert torch.equal(oa, ra) and torch.equal(ob, rb)
+    km.free()
+
+
+@gpu
+def test_forward_in_a_captured_graph(dev):
+    # the forward (prepared weights, caller's output) launches kernels only:
+    # it can be captured in a HIP graph; every replay, with new features
+    # copied in eagerly between replays, equals the eager forward
+    sc = _sc()
+    wl = workloads.uniform_workload(48, 11000, [(3, 128, 128)], seed=1203, bias_kind=None, name="gr")
+    L = wl.layers[0]
+    km = sc.build_map(_to(dev, wl.coords), wl.grid, wl.batch)
+    feats = _to(dev, wl.feats).clone()
+    wp = sc.prepare_weights(_to(dev, L.W))
+    out = torch.empty((wl.n, 128), dtype=torch.float16, device=dev)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            sc.forward(km, feats, prepared=wp, ksize=3, cout=128, out=out)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sc.forward(km, feats, prepared=wp, ksize=3, cout=128, out=out)
+    rng = np.random.default_rng(1204)
+    for rep in range(3):
+        feats.copy_(_to(dev, rng.standard_normal((wl.n, 128)).astype(np.float16)))
+        torch.cuda.synchronize(dev)
+        g.replay()
+        torch.cuda.synchronize(dev)
+        ref = sc.forward(km, feats, prepared=wp, ksize=3, cout=128)
+        torch.cuda.synchronize(dev)
+        assert torch.equal(out, ref), f"replay {rep}"
+    km.free()
