@@ -64,10 +64,11 @@ extern "C" {
  * TRELLIS.2 on a Mac (3/3)", section E); the map is the same */
 #define SUBMCONV_FLAG_SORTED_KEYS 2u
 /* tile size of the per-tile neighbour lists the forward streams: by default
- * 288-row tiles when the map is sparse (under 32 entries per off-centre tap
- * and 256-row tile on average) and they need fewer rounds of one tile per
- * compute unit, else 256-row tiles; these flags force one size (the results
- * are the same bit for bit) */
+ * 256 rows, or, when the map is sparse (under 32 entries per off-centre tap
+ * and 256-row tile on average) and tiles of up to 288 rows need fewer rounds
+ * of one tile per compute unit, the fewest rows (257..288) that fit the tiles
+ * into those rounds; these flags force 256 or 288 (the results are the same
+ * bit for bit) */
 #define SUBMCONV_FLAG_TILES_256 4u
 #define SUBMCONV_FLAG_TILES_288 8u
 
@@ -99,7 +100,7 @@ typedef struct submconv_map_s* submconv_map_t;
  *
  * The map is built on `stream`; the function then waits for that stream once
  * (to read back the validation flags and the active-pair count; a second
- * time when it switches to 288-row tiles) and returns
+ * time when it switches to wider tiles) and returns
  * SUBMCONV_ERR_COORD_OUT_OF_RANGE or SUBMCONV_ERR_DUPLICATE_COORD, with no
  * handle, when the sites are invalid. It allocates device memory
  * (27*n*4 bytes for the map, plus temporaries freed before return).
@@ -110,7 +111,7 @@ int submconv_build_map(const int32_t* coords, int64_t n, int32_t batch, const in
 /* Number of sites of the map. */
 int64_t submconv_map_num_rows(submconv_map_t map);
 
-/* Rows per tile of the map's per-tile neighbour lists: 256 or 288 (see
+/* Rows per tile of the map's per-tile neighbour lists: 256 .. 288 (see
  * SUBMCONV_FLAG_TILES_256). Negative on a bad argument. */
 int32_t submconv_map_tile_rows(submconv_map_t map);
 

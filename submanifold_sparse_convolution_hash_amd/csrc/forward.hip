@@ -181,7 +181,7 @@ typedef float float16v __attribute__((ext_vector_type(16)));
 
 template <int CIN, int COUT_T, bool K3, int GR_ = 32, int M_ = kTileRows>
 struct CfgPP {
-  static constexpr int M = M_;               // rows per tile (the map's tile size)
+  static constexpr int M = M_;               // accumulator rows: the map's tiles have at most M
   static constexpr int GR = GR_;             // rows per group: 32, or 64 for dense maps
   static constexpr int NRB = GR / 32;        // 32-row MFMA blocks per group
   static constexpr int NC = COUT_T / 32;     // column blocks
@@ -221,7 +221,8 @@ __global__ __launch_bounds__((CfgPP<CIN, COUT_T, K3, GR_, M_>::NT)) void k_fwd_p
     const uint16_t* __restrict__ tile_cnt, const int32_t* __restrict__ order, int64_t n,
     const _Float16* __restrict__ feats, const _Float16* __restrict__ wp,
     const float* __restrict__ bias, _Float16* __restrict__ out, int cout, int n_tiles, int n_ct,
-    int tiles_per_xcd, int n_pairs) {
+    int tiles_per_xcd, int n_pairs, int tile_rows) {
+  // tile_rows: the map's rows per tile, at most M (the LDS accumulator's rows)
   using C = CfgPP<CIN, COUT_T, K3, GR_, M_>;
   constexpr int M = C::M, GR = C::GR, NRBW = C::NRBW, KS = C::KS, RC = C::RC;
   constexpr int LB = C::LB, LE = C::LE, CPT = C::CPT, NCG = C::NCG, BR = C::BR;
@@ -288,8 +289,8 @@ __global__ __launch_bounds__((CfgPP<CIN, COUT_T, K3, GR_, M_>::NT)) void k_fwd_p
   auto half_of = [&](const Raw& r) -> Half {  // the counts have arrived
     Half hf;
     const bool live = r.tile >= 0;
-    hf.t0 = static_cast<int64_t>(live ? r.tile : 0) * M;
-    hf.rows_here = live ? static_cast<int>(n - hf.t0 < M ? n - hf.t0 : M) : 0;
+    hf.t0 = static_cast<int64_t>(live ? r.tile : 0) * tile_rows;
+    hf.rows_here = live ? static_cast<int>(n - hf.t0 < tile_rows ? n - hf.t0 : tile_rows) : 0;
     hf.c0 = r.ct * COUT_T;
     hf.cnt = K3 ? (live ? r.cnt : 0) : (lane == 0 ? hf.rows_here : 0);
     hf.off = excl_scan_wave(hf.cnt, lane) + (K3 ? __builtin_amdgcn_readfirstlane(r.ent0) : 0);
@@ -731,6 +732,9 @@ template <int CIN, int COUT_T, bool K3, bool IS_BF16, int GR, int NP = 1, int M 
 int launch_pp(const Map& m, const _Float16* feats, const _Float16* wp, const float* bias,
               _Float16* out, int cout, int n_tiles, int n_ct, int tiles_per_xcd, int n_pairs,
               hipStream_t stream) {
+  const int tile_rows = K3 ? m.tile_rows : kTileRows;
+  if (tile_rows > M)
+    return set_error(SUBMCONV_ERR_INVALID_ARG, "internal: %d tile rows above %d", tile_rows, M);
   using C = CfgPP<CIN, COUT_T, K3, GR, M>;
   // persistent: as many workgroups as the CUs hold at once (one per CU when
   // the accumulator fills the LDS, more for narrow column tiles), dealt
@@ -750,7 +754,7 @@ int launch_pp(const Map& m, const _Float16* feats, const _Float16* wp, const flo
                                                  stream>>>(
       K3 ? m.ent : nullptr, K3 ? m.tile_off : nullptr, K3 ? m.tile_cnt : nullptr,
       K3 ? m.order : nullptr, m.n, feats, wp, bias, out, cout, n_tiles, n_ct, tiles_per_xcd,
-      n_pairs);
+      n_pairs, tile_rows);
   SUBMCONV_HIP_CHECK(hipGetLastError());
   return SUBMCONV_OK;
 }
@@ -777,8 +781,8 @@ int launch_one(const Map& m, const _Float16* feats, const _Float16* wp, const fl
     dense = off_groups >= int64_t{kDenseGroups} * (kTaps3 - 1) * n_tiles;
   }
   if constexpr (K3) {
-    // maps of 288-row tiles (sparse, so never dense): 32-row groups
-    if (m.tile_rows == kTileRowsWide) {
+    // maps of 257..288-row tiles (sparse, so never dense): 32-row groups
+    if (m.tile_rows > kTileRows) {
       constexpr int CP = CIN <= 128 ? CIN : 128, NP = CIN <= 128 ? 1 : 2;
       return launch_pp<CP, COUT_T, K3, IS_BF16, 32, NP, kTileRowsWide>(
           m, feats, wp, bias, out, cout, n_tiles, n_ct, tiles_per_xcd, n_pairs, stream);

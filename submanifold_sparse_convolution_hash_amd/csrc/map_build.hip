@@ -21,6 +21,7 @@
 #include <rocprim/device/device_radix_sort.hpp>
 #include <rocprim/device/device_scan.hpp>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstring>
 #include <vector>
@@ -232,19 +233,19 @@ __global__ void k_query_sorted(const int32_t* __restrict__ coords, const int32_t
   }
 }
 
-// Per tile of TR processing rows: entries per processing position (wave
-// ballots over 64-row chunks; a block has TR rounded up to 64 threads) and
-// the tile's total.
+// Per tile of tr <= TR processing rows: entries per processing position
+// (wave ballots over 64-row chunks; a block has TR rounded up to 64 threads)
+// and the tile's total.
 template <int TR>
 __global__ __launch_bounds__((TR + 63) / 64 * 64) void k_tile_count(
-    const int32_t* __restrict__ nbr, int64_t n, uint16_t* __restrict__ tile_cnt,
+    const int32_t* __restrict__ nbr, int64_t n, int tr, uint16_t* __restrict__ tile_cnt,
     int32_t* __restrict__ tile_tot) {
   constexpr int NWV = (TR + 63) / 64;
   __shared__ int cnt[NWV][kTaps3];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * TR + threadIdx.x;
-  const bool valid = static_cast<int>(threadIdx.x) < TR && t < n;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * tr + threadIdx.x;
+  const bool valid = static_cast<int>(threadIdx.x) < tr && t < n;
   for (int k = 0; k < kTaps3; ++k) {
     const uint64_t m = __ballot(valid && nbr[static_cast<int64_t>(k) * n + t] >= 0);
     if (lane == 0) cnt[w][k] = __popcll(m);
@@ -268,14 +269,14 @@ __global__ __launch_bounds__((TR + 63) / 64 * 64) void k_tile_count(
 // processing position, then row.
 template <int TR>
 __global__ __launch_bounds__((TR + 63) / 64 * 64) void k_tile_fill(
-    const int32_t* __restrict__ nbr, int64_t n, const int32_t* __restrict__ tile_off,
+    const int32_t* __restrict__ nbr, int64_t n, int tr, const int32_t* __restrict__ tile_off,
     int2* __restrict__ ent) {
   constexpr int NWV = (TR + 63) / 64;
   __shared__ uint64_t masks[kTaps3][NWV];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * TR + threadIdx.x;
-  const bool valid = static_cast<int>(threadIdx.x) < TR && t < n;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * tr + threadIdx.x;
+  const bool valid = static_cast<int>(threadIdx.x) < tr && t < n;
   int32_t v[kTaps3];
   for (int k = 0; k < kTaps3; ++k) {
     v[k] = valid ? nbr[static_cast<int64_t>(k) * n + t] : -1;
@@ -339,16 +340,19 @@ struct DevBuf {
   ~DevBuf() { reset(); }
 };
 
-// 288-row tiles when the map is sparse (fewer than one 32-entry group per
-// off-centre position of a 256-row tile on average, so that a tile's step
-// count barely grows with its rows) and they need fewer rounds of one tile
-// per compute unit: the forward's last round is then fuller.
-bool prefer_wide_tiles(int64_t n, int64_t pairs, int cus) {
-  if (n <= 0 || cus <= 0) return false;
-  if ((pairs - n) * kTileRows >= int64_t{kGroupRows} * (kTaps3 - 1) * n) return false;
+// Rows per tile: 256, or, when the map is sparse (fewer than one 32-entry
+// group per off-centre position of a 256-row tile on average, so that a
+// tile's step count barely grows with its rows) and tiles of up to 288 rows
+// need fewer rounds of one tile per compute unit, the fewest rows that fit
+// the tiles into those rounds.
+int choose_tile_rows(int64_t n, int64_t pairs, int cus) {
+  if (n <= 0 || cus <= 0) return kTileRows;
+  if ((pairs - n) * kTileRows >= int64_t{kGroupRows} * (kTaps3 - 1) * n) return kTileRows;
   const int64_t r256 = ((n + kTileRows - 1) / kTileRows + cus - 1) / cus;
   const int64_t r288 = ((n + kTileRowsWide - 1) / kTileRowsWide + cus - 1) / cus;
-  return r288 < r256;
+  if (r288 >= r256) return kTileRows;
+  const int64_t slots = r288 * cus;
+  return static_cast<int>(std::min<int64_t>((n + slots - 1) / slots, kTileRowsWide));
 }
 
 }  // namespace
@@ -545,12 +549,12 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
     BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&tile_off), sizeof(int32_t) * (n_tiles + 1)));
     BUILD_CHECK(hipMalloc(&tile_tot.p, sizeof(int32_t) * (n_tiles + 1)));
     BUILD_CHECK(hipMemsetAsync(tile_tot.p, 0, sizeof(int32_t) * (n_tiles + 1), stream));
-    if (tr == kTileRowsWide)
+    if (tr > kTileRows)
       k_tile_count<kTileRowsWide><<<static_cast<unsigned>(n_tiles), (kTileRowsWide + 63) / 64 * 64, 0,
-                                    stream>>>(nbr, n, tile_cnt, static_cast<int32_t*>(tile_tot.p));
+                                    stream>>>(nbr, n, tr, tile_cnt, static_cast<int32_t*>(tile_tot.p));
     else
       k_tile_count<kTileRows><<<static_cast<unsigned>(n_tiles), kTileRows, 0, stream>>>(
-          nbr, n, tile_cnt, static_cast<int32_t*>(tile_tot.p));
+          nbr, n, tr, tile_cnt, static_cast<int32_t*>(tile_tot.p));
     BUILD_CHECK(hipGetLastError());
     size_t tmp_bytes = 0;
     BUILD_CHECK(rocprim::exclusive_scan(nullptr, tmp_bytes, static_cast<const int32_t*>(tile_tot.p),
@@ -585,8 +589,9 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   if (!(flags & (SUBMCONV_FLAG_TILES_256 | SUBMCONV_FLAG_TILES_288))) {
     int cus = 256;
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, m.device);
-    if (prefer_wide_tiles(n, m.active_pairs, cus)) {
-      tr = kTileRowsWide;
+    const int want = choose_tile_rows(n, m.active_pairs, cus);
+    if (want != tr) {
+      tr = want;
       if (const int st = count_tiles(tr); st != SUBMCONV_OK) return st;
     }
   }
@@ -594,12 +599,12 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   // one more entry {-1, -1} after the lists: the target of masked loads
   BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&ent), sizeof(int2) * (m.active_pairs + 1)));
   BUILD_CHECK(hipMemsetAsync(ent + m.active_pairs, 0xff, sizeof(int2), stream));
-  if (tr == kTileRowsWide)
+  if (tr > kTileRows)
     k_tile_fill<kTileRowsWide><<<static_cast<unsigned>(n_tiles), (kTileRowsWide + 63) / 64 * 64, 0,
-                                 stream>>>(nbr, n, tile_off, ent);
+                                 stream>>>(nbr, n, tr, tile_off, ent);
   else
-    k_tile_fill<kTileRows><<<static_cast<unsigned>(n_tiles), kTileRows, 0, stream>>>(nbr, n, tile_off,
-                                                                                    ent);
+    k_tile_fill<kTileRows><<<static_cast<unsigned>(n_tiles), kTileRows, 0, stream>>>(nbr, n, tr,
+                                                                                    tile_off, ent);
   BUILD_CHECK(hipGetLastError());
   // the forward may run on another stream: the map is complete on return
   BUILD_CHECK(hipStreamSynchronize(stream));

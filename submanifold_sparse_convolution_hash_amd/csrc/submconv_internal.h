@@ -17,8 +17,8 @@ constexpr int kTaps3 = 27;
 constexpr int kCenterTap = 13;
 
 // Rows per output tile of the forward kernels; the map's per-tile lists are
-// built for this tile size, or for kTileRowsWide (Map.tile_rows) when that
-// spreads a sparse map more evenly over the compute units.
+// built for this tile size, or for up to kTileRowsWide rows (Map.tile_rows)
+// when that spreads a sparse map more evenly over the compute units.
 constexpr int kTileRows = 256;
 constexpr int kTileRowsWide = 288;
 
@@ -53,7 +53,7 @@ struct Map {
   int32_t* nbr = nullptr;
   int32_t* order = nullptr;
   int64_t n_tiles = 0;
-  int32_t tile_rows = kTileRows;  // kTileRows or kTileRowsWide
+  int32_t tile_rows = kTileRows;  // kTileRows, or kTileRows+1 .. kTileRowsWide
   uint16_t* tile_cnt = nullptr;
   int32_t* tile_off = nullptr;
   int2* ent = nullptr;

@@ -543,17 +543,25 @@ def test_tiles_288_same_results(dev, cin, cout, dtype, morton, bias):
 
 
 @gpu
-def test_c3_map_takes_288_row_tiles(dev):
+def test_c3_map_takes_wider_tiles(dev):
     # 128^3 at 10 %: under one 32-entry group per off-centre position and
-    # 256-row tile, and 729 tiles of 288 rows fill three rounds of 256 CUs
-    # where 820 tiles of 256 rows need four
+    # 256-row tile, and tiles of up to 288 rows fill three rounds of 256 CUs
+    # where 820 tiles of 256 rows need four: the builder takes the fewest
+    # rows that do, ceil(209715 / 768) = 274; the outputs equal those of
+    # 256-row tiles bit for bit
     sc = _sc()
     wl = workloads.make("c3_128_128")
-    km = sc.build_map(_to(dev, wl.coords), wl.grid, wl.batch)
+    L = wl.layers[0]
+    coords = _to(dev, wl.coords)
+    km = sc.build_map(coords, wl.grid, wl.batch)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     _say(f"[c3 tiles] CUs={cus} tile_rows={km.tile_rows}")
     if cus == 256:
-        assert km.tile_rows == 288
+        assert km.tile_rows == 274
+    k256 = sc.build_map(coords, wl.grid, wl.batch, tile_rows=256)
+    feats, W = _to(dev, wl.feats), _to(dev, L.W)
+    assert torch.equal(sc.forward(km, feats, W), sc.forward(k256, feats, W))
+    k256.free()
     # and a dense map keeps 256-row tiles
     wd = workloads.random_small(17, G=14, occ=0.95, cin=8, cout=8, batch=2, ksize=3)
     kd = sc.build_map(_to(dev, wd.coords), wd.grid, wd.batch)
