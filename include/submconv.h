@@ -63,12 +63,15 @@ extern "C" {
  * instead of the hash table (the packing + sort + search lookup of "Running
  * TRELLIS.2 on a Mac (3/3)", section E); the map is the same */
 #define SUBMCONV_FLAG_SORTED_KEYS 2u
-/* tile size of the per-tile neighbour lists the forward streams: by default
- * 256 rows, or, when the map is sparse (under 32 entries per off-centre tap
- * and 256-row tile on average) and tiles of up to 288 rows need fewer rounds
- * of one tile per compute unit, the fewest rows (257..288) that fit the tiles
- * into those rounds; these flags force 256 or 288 (the results are the same
- * bit for bit) */
+/* tile size of the per-tile neighbour lists the forward streams: the map
+ * always holds lists of 256-row tiles; when it is sparse (under 32 entries
+ * per off-centre tap and 256-row tile on average) and tiles of up to 288 rows
+ * need fewer rounds of one tile per compute unit, it also holds lists of the
+ * fewest rows (257..288) that fit the tiles into those rounds, and each
+ * forward takes whichever fits its own workgroups into fewer rounds.
+ * SUBMCONV_FLAG_TILES_256 builds no wider lists; SUBMCONV_FLAG_TILES_288
+ * builds 288-row lists and makes every forward that can use them (the
+ * results are the same bit for bit) */
 #define SUBMCONV_FLAG_TILES_256 4u
 #define SUBMCONV_FLAG_TILES_288 8u
 
@@ -100,7 +103,7 @@ typedef struct submconv_map_s* submconv_map_t;
  *
  * The map is built on `stream`; the function then waits for that stream once
  * (to read back the validation flags and the active-pair count; a second
- * time when it switches to wider tiles) and returns
+ * time when it also builds wider tiles) and returns
  * SUBMCONV_ERR_COORD_OUT_OF_RANGE or SUBMCONV_ERR_DUPLICATE_COORD, with no
  * handle, when the sites are invalid. It allocates device memory
  * (27*n*4 bytes for the map, plus temporaries freed before return).
@@ -111,8 +114,8 @@ int submconv_build_map(const int32_t* coords, int64_t n, int32_t batch, const in
 /* Number of sites of the map. */
 int64_t submconv_map_num_rows(submconv_map_t map);
 
-/* Rows per tile of the map's per-tile neighbour lists: 256 .. 288 (see
- * SUBMCONV_FLAG_TILES_256). Negative on a bad argument. */
+/* Rows per tile of the map's widest per-tile neighbour lists: 256 .. 288
+ * (see SUBMCONV_FLAG_TILES_256). Negative on a bad argument. */
 int32_t submconv_map_tile_rows(submconv_map_t map);
 
 /* Number of (row, tap) pairs with a neighbour, the centre tap included

@@ -591,7 +591,7 @@ struct Runs {
 };
 // the old kernel: every position in the same runs of tpr tiles
 Runs runs_for(const Map& m, int K) {
-  const int64_t nt = m.n_tiles;
+  const int64_t nt = m.tiles.n;
   int64_t runs = (kTargetBlocks + K - 1) / K;
   if (runs > nt) runs = nt;
   if (runs < 1) runs = 1;
@@ -623,10 +623,10 @@ int device_cus(int dev) {
 WSplit split_for(const Map& m, int K, int cin, int cout) {
   WSplit ws{};
   ws.np = K == kTaps3 ? kTaps3 : 1;
-  const int64_t nt = m.n_tiles;
+  const int64_t nt = m.tiles.n;
   int64_t off = 0;
-  for (int p = 1; p < ws.np; ++p) off += m.pos_groups[p];
-  const double g0 = static_cast<double>(m.pos_groups[0]);
+  for (int p = 1; p < ws.np; ++p) off += m.tiles.pos_groups[p];
+  const double g0 = static_cast<double>(m.tiles.pos_groups[0]);
   const double goff = ws.np > 1 ? static_cast<double>(off) / (ws.np - 1) : 0.0;
   auto runs_of = [nt](double groups, double target, int32_t& runs, int32_t& tpr) {
     int64_t r = static_cast<int64_t>(std::ceil(groups / target));
@@ -656,7 +656,8 @@ WSplit split_for(const Map& m, int K, int cin, int cout) {
 template <int CIN, int COUT>
 int launch_w(const Map& m, int K, const _Float16* feats, const _Float16* grad_out, float* partial,
              float* dw, hipStream_t stream) {
-  const int32_t nt = static_cast<int32_t>(m.n_tiles), np = static_cast<int32_t>(m.active_pairs);
+  const Tiles& T = m.tiles;
+  const int32_t nt = static_cast<int32_t>(T.n), np = static_cast<int32_t>(m.active_pairs);
   if constexpr ((CIN == 32 || CIN == 64 || CIN == 128 || CIN == 256) &&
                 (COUT == 32 || COUT == 64 || COUT == 128 || COUT == 256)) {
     constexpr int NT = PCfg<CIN, COUT>::NT;
@@ -664,12 +665,10 @@ int launch_w(const Map& m, int K, const _Float16* feats, const _Float16* grad_ou
     const unsigned blocks = static_cast<unsigned>(ws.blocks());
     if (m.order)
       k_bwd_weight_pp<CIN, COUT, true><<<blocks, NT, 0, stream>>>(
-          m.ent, m.tile_off, m.tile_cnt, m.order, m.n, nt, m.tile_rows, ws, feats, grad_out, partial,
-          np);
+          T.ent, T.off, T.cnt, m.order, m.n, nt, T.rows, ws, feats, grad_out, partial, np);
     else
       k_bwd_weight_pp<CIN, COUT, false><<<blocks, NT, 0, stream>>>(
-          m.ent, m.tile_off, m.tile_cnt, m.order, m.n, nt, m.tile_rows, ws, feats, grad_out, partial,
-          np);
+          T.ent, T.off, T.cnt, m.order, m.n, nt, T.rows, ws, feats, grad_out, partial, np);
     SUBMCONV_HIP_CHECK(hipGetLastError());
     const int64_t chunks = (int64_t{CIN} * COUT / 4 + 63) / 64;
     k_bwd_weight_reduce_pp<<<static_cast<unsigned>(ws.np * chunks), 256, 0, stream>>>(
@@ -678,8 +677,7 @@ int launch_w(const Map& m, int K, const _Float16* feats, const _Float16* grad_ou
     const Runs r = runs_for(m, K);
     const int64_t total = static_cast<int64_t>(K) * CIN * COUT;
     k_bwd_weight<CIN, COUT><<<static_cast<unsigned>(r.runs * K), WCfg<CIN, COUT>::NT, 0, stream>>>(
-        m.ent, m.tile_off, m.tile_cnt, m.order, m.n, nt, m.tile_rows, K, r.tpr, feats, grad_out,
-        partial, np);
+        T.ent, T.off, T.cnt, m.order, m.n, nt, T.rows, K, r.tpr, feats, grad_out, partial, np);
     SUBMCONV_HIP_CHECK(hipGetLastError());
     k_bwd_weight_reduce<<<static_cast<unsigned>((total + 255) / 256), 256, 0, stream>>>(
         partial, r.runs, K, CIN, COUT, dw);

@@ -728,33 +728,49 @@ int cus_per_xcd() {
   return v;
 }
 
-template <int CIN, int COUT_T, bool K3, bool IS_BF16, int GR, int NP = 1, int M = kTileRows>
-int launch_pp(const Map& m, const _Float16* feats, const _Float16* wp, const float* bias,
-              _Float16* out, int cout, int n_tiles, int n_ct, int tiles_per_xcd, int n_pairs,
-              hipStream_t stream) {
-  const int tile_rows = K3 ? m.tile_rows : kTileRows;
-  if (tile_rows > M)
-    return set_error(SUBMCONV_ERR_INVALID_ARG, "internal: %d tile rows above %d", tile_rows, M);
-  using C = CfgPP<CIN, COUT_T, K3, GR, M>;
-  // persistent: as many workgroups as the CUs hold at once (one per CU when
-  // the accumulator fills the LDS, more for narrow column tiles), dealt
-  // evenly to the 8 XCDs
+// workgroups of one instance that a CU holds at once (cached)
+template <int CIN, int COUT_T, bool K3, bool IS_BF16, int GR, int NP, int M>
+int pp_per_cu() {
   static const int per_cu = [] {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &nb, reinterpret_cast<const void*>(k_fwd_pp<CIN, COUT_T, K3, IS_BF16, GR, NP, M>),
-            C::NT, 0) !=
-        hipSuccess)
+            CfgPP<CIN, COUT_T, K3, GR, M>::NT, 0) != hipSuccess)
       nb = 1;
     return std::max(1, nb);
   }();
+  return per_cu;
+}
+
+// rounds of the persistent grid: units of an XCD over its workgroups
+template <int CIN, int COUT_T, bool K3, bool IS_BF16, int GR, int NP, int M>
+int64_t pp_rounds(int64_t n_tiles, int n_ct) {
+  const int64_t units_per_xcd = (n_tiles + 7) / 8 * n_ct;
+  const int64_t slots = int64_t{cus_per_xcd()} * pp_per_cu<CIN, COUT_T, K3, IS_BF16, GR, NP, M>();
+  return (units_per_xcd + slots - 1) / slots;
+}
+
+template <int CIN, int COUT_T, bool K3, bool IS_BF16, int GR, int NP = 1, int M = kTileRows>
+int launch_pp(const Map& m, const Tiles& T, const _Float16* feats, const _Float16* wp,
+              const float* bias, _Float16* out, int cout, hipStream_t stream) {
+  if (T.n > (int64_t{1} << 28)) return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "too many rows");
+  if (T.rows > M)
+    return set_error(SUBMCONV_ERR_INVALID_ARG, "internal: %d tile rows above %d", T.rows, M);
+  using C = CfgPP<CIN, COUT_T, K3, GR, M>;
+  const int n_tiles = static_cast<int>(T.n);
+  const int n_ct = cout / COUT_T;
+  const int tiles_per_xcd = (n_tiles + 7) / 8;
+  const int n_pairs = static_cast<int>(K3 ? m.active_pairs : 0);
+  // persistent: as many workgroups as the CUs hold at once (one per CU when
+  // the accumulator fills the LDS, more for narrow column tiles), dealt
+  // evenly to the 8 XCDs
+  const int per_cu = pp_per_cu<CIN, COUT_T, K3, IS_BF16, GR, NP, M>();
   const int64_t units_per_xcd = int64_t{tiles_per_xcd} * n_ct;
   const int64_t wpx = std::min<int64_t>(units_per_xcd, int64_t{cus_per_xcd()} * per_cu);
   k_fwd_pp<CIN, COUT_T, K3, IS_BF16, GR, NP, M><<<static_cast<unsigned>(8 * wpx), C::NT, 0,
                                                  stream>>>(
-      K3 ? m.ent : nullptr, K3 ? m.tile_off : nullptr, K3 ? m.tile_cnt : nullptr,
-      K3 ? m.order : nullptr, m.n, feats, wp, bias, out, cout, n_tiles, n_ct, tiles_per_xcd,
-      n_pairs, tile_rows);
+      K3 ? T.ent : nullptr, K3 ? T.off : nullptr, K3 ? T.cnt : nullptr, K3 ? m.order : nullptr,
+      m.n, feats, wp, bias, out, cout, n_tiles, n_ct, tiles_per_xcd, n_pairs, T.rows);
   SUBMCONV_HIP_CHECK(hipGetLastError());
   return SUBMCONV_OK;
 }
@@ -762,50 +778,37 @@ int launch_pp(const Map& m, const _Float16* feats, const _Float16* wp, const flo
 template <int CIN, int COUT_T, bool K3, bool IS_BF16>
 int launch_one(const Map& m, const _Float16* feats, const _Float16* wp, const float* bias,
                _Float16* out, int cout, hipStream_t stream) {
-  // a 3x3x3 forward streams the map's tiles; a 1x1x1 one tiles the rows itself
-  const int64_t n_tiles64 = K3 ? m.n_tiles : (m.n + kTileRows - 1) / kTileRows;
-  if (n_tiles64 > (int64_t{1} << 28))
-    return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "too many rows");
-  const int n_tiles = static_cast<int>(n_tiles64);
-  const int n_ct = cout / COUT_T;
-  const int tiles_per_xcd = (n_tiles + 7) / 8;
-  const int n_pairs = static_cast<int>(K3 ? m.active_pairs : 0);
-  // dense maps (many groups per position) take 64-row groups: half the
-  // steps, each weight load serving two MFMA row blocks. At 128 channels a
-  // pass that fits the LDS only with 128 columns (exactly 160 KiB); narrower
-  // column tiles keep 32-row groups, and two or more workgroups per CU.
-  bool dense = false;
-  if constexpr (K3 && (CIN <= 64 || COUT_T == 128)) {
-    int64_t off_groups = 0;
-    for (int q = 1; q < kTaps3; ++q) off_groups += m.pos_groups[q];
-    dense = off_groups >= int64_t{kDenseGroups} * (kTaps3 - 1) * n_tiles;
-  }
-  if constexpr (K3) {
-    // maps of 257..288-row tiles (sparse, so never dense): 32-row groups
-    if (m.tile_rows > kTileRows) {
-      constexpr int CP = CIN <= 128 ? CIN : 128, NP = CIN <= 128 ? 1 : 2;
-      return launch_pp<CP, COUT_T, K3, IS_BF16, 32, NP, kTileRowsWide>(
-          m, feats, wp, bias, out, cout, n_tiles, n_ct, tiles_per_xcd, n_pairs, stream);
-    }
-  }
-  if constexpr (CIN <= 128) {
-    if constexpr (CIN <= 64 || COUT_T == 128)
-      if (dense)
-        return launch_pp<CIN, COUT_T, K3, IS_BF16, 64>(m, feats, wp, bias, out, cout, n_tiles,
-                                                      n_ct, tiles_per_xcd, n_pairs, stream);
-    return launch_pp<CIN, COUT_T, K3, IS_BF16, 32>(m, feats, wp, bias, out, cout, n_tiles, n_ct,
-                                                  tiles_per_xcd, n_pairs, stream);
+  constexpr int CP = CIN <= 128 ? CIN : 128, NP = CIN <= 128 ? 1 : 2;  // 256 channels: two passes
+  static_assert(CIN <= 128 || CIN == 256, "CIN");
+  if constexpr (!K3) {
+    // a 1x1x1 forward tiles the rows itself
+    Tiles rows;
+    rows.n = (m.n + kTileRows - 1) / kTileRows;
+    return launch_pp<CP, COUT_T, K3, IS_BF16, 32, NP>(m, rows, feats, wp, bias, out, cout, stream);
   } else {
-    // 256 channels: two 128-channel passes over each unit
-    static_assert(CIN == 256, "CIN");
-    if (dense)
-      return launch_pp<128, COUT_T, K3, IS_BF16, 64, 2>(m, feats, wp, bias, out, cout, n_tiles,
-                                                       n_ct, tiles_per_xcd, n_pairs, stream);
-    return launch_pp<128, COUT_T, K3, IS_BF16, 32, 2>(m, feats, wp, bias, out, cout, n_tiles, n_ct,
-                                                     tiles_per_xcd, n_pairs, stream);
+    const int n_ct = cout / COUT_T;
+    // dense maps (many groups per position) take 64-row groups: half the
+    // steps, each weight load serving two MFMA row blocks. At 128 channels a
+    // pass fits the LDS only with 128 columns (exactly 160 KiB); narrower
+    // column tiles keep 32-row groups, and two or more workgroups per CU.
+    if constexpr (CIN <= 64 || COUT_T == 128) {
+      int64_t off_groups = 0;
+      for (int q = 1; q < kTaps3; ++q) off_groups += m.tiles.pos_groups[q];
+      if (off_groups >= int64_t{kDenseGroups} * (kTaps3 - 1) * m.tiles.n)
+        return launch_pp<CP, COUT_T, K3, IS_BF16, 64, NP>(m, m.tiles, feats, wp, bias, out, cout,
+                                                         stream);
+    }
+    // a sparse map's wide tiles (32-row groups) when they fit this layer's
+    // workgroups into fewer rounds than 256-row tiles
+    if (m.wide.n > 0 &&
+        (m.wide_always ||
+         pp_rounds<CP, COUT_T, K3, IS_BF16, 32, NP, kTileRowsWide>(m.wide.n, n_ct) <
+             pp_rounds<CP, COUT_T, K3, IS_BF16, 32, NP, kTileRows>(m.tiles.n, n_ct)))
+      return launch_pp<CP, COUT_T, K3, IS_BF16, 32, NP, kTileRowsWide>(m, m.wide, feats, wp, bias,
+                                                                      out, cout, stream);
+    return launch_pp<CP, COUT_T, K3, IS_BF16, 32, NP>(m, m.tiles, feats, wp, bias, out, cout,
+                                                     stream);
   }
-  SUBMCONV_HIP_CHECK(hipGetLastError());
-  return SUBMCONV_OK;
 }
 
 template <int CIN, int COUT_T, bool IS_BF16>

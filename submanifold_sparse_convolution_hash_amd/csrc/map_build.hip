@@ -431,16 +431,16 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   DevBuf skeys, srows, rows_in, ksort_tmp;
   int32_t* nbr = nullptr;
   int32_t* order = nullptr;
-  uint16_t* tile_cnt = nullptr;
-  int32_t* tile_off = nullptr;
-  int2* ent = nullptr;
+  Tiles base, wide;  // 256-row tiles, and wider ones for sparse maps
   auto fail = [&](int status) {
     (void)hipStreamSynchronize(stream);
     if (nbr) (void)hipFree(nbr);
     if (order) (void)hipFree(order);
-    if (tile_cnt) (void)hipFree(tile_cnt);
-    if (tile_off) (void)hipFree(tile_off);
-    if (ent) (void)hipFree(ent);
+    for (Tiles* T : {&base, &wide}) {
+      if (T->cnt) (void)hipFree(T->cnt);
+      if (T->off) (void)hipFree(T->off);
+      if (T->ent) (void)hipFree(T->ent);
+    }
     return status;
   };
 #define BUILD_CHECK(expr)                                                                 \
@@ -535,18 +535,17 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
 
   // per-tile compacted lists of tr-row tiles: counts, tile offsets
   // (exclusive scan), the active pairs and the groups per position, read back
-  int64_t n_tiles = 0;
   uint64_t host_small[2 + kTaps3] = {};
-  auto count_tiles = [&](int tr) -> int {
-    if (tile_cnt) BUILD_CHECK(hipFree(tile_cnt));
-    if (tile_off) BUILD_CHECK(hipFree(tile_off));
-    tile_cnt = nullptr;
-    tile_off = nullptr;
+  auto count_tiles = [&](int tr, Tiles& T) -> int {
     tile_tot.reset();
     scan_tmp.reset();
-    n_tiles = (n + tr - 1) / tr;
-    BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&tile_cnt), sizeof(uint16_t) * kTaps3 * n_tiles));
-    BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&tile_off), sizeof(int32_t) * (n_tiles + 1)));
+    const int64_t n_tiles = (n + tr - 1) / tr;
+    T.rows = tr;
+    T.n = n_tiles;
+    BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&T.cnt), sizeof(uint16_t) * kTaps3 * n_tiles));
+    BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&T.off), sizeof(int32_t) * (n_tiles + 1)));
+    uint16_t* tile_cnt = T.cnt;
+    int32_t* tile_off = T.off;
     BUILD_CHECK(hipMalloc(&tile_tot.p, sizeof(int32_t) * (n_tiles + 1)));
     BUILD_CHECK(hipMemsetAsync(tile_tot.p, 0, sizeof(int32_t) * (n_tiles + 1), stream));
     if (tr > kTileRows)
@@ -572,10 +571,24 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
     BUILD_CHECK(hipMemcpyAsync(host_small, small.p, sizeof(host_small), hipMemcpyDeviceToHost,
                                stream));
     BUILD_CHECK(hipStreamSynchronize(stream));
+    for (int q = 0; q < kTaps3; ++q) T.pos_groups[q] = static_cast<int64_t>(host_small[2 + q]);
     return SUBMCONV_OK;
   };
-  int tr = (flags & SUBMCONV_FLAG_TILES_288) ? kTileRowsWide : kTileRows;
-  if (const int st = count_tiles(tr); st != SUBMCONV_OK) return st;
+  // the lists themselves; one more entry {-1, -1} after them: the target of
+  // masked loads
+  auto fill_tiles = [&](Tiles& T) -> int {
+    BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&T.ent), sizeof(int2) * (m.active_pairs + 1)));
+    BUILD_CHECK(hipMemsetAsync(T.ent + m.active_pairs, 0xff, sizeof(int2), stream));
+    if (T.rows > kTileRows)
+      k_tile_fill<kTileRowsWide><<<static_cast<unsigned>(T.n), (kTileRowsWide + 63) / 64 * 64, 0,
+                                   stream>>>(nbr, n, T.rows, T.off, T.ent);
+    else
+      k_tile_fill<kTileRows><<<static_cast<unsigned>(T.n), kTileRows, 0, stream>>>(nbr, n, T.rows,
+                                                                                  T.off, T.ent);
+    BUILD_CHECK(hipGetLastError());
+    return SUBMCONV_OK;
+  };
+  if (const int st = count_tiles(kTileRows, base); st != SUBMCONV_OK) return st;
   const uint32_t eflags = static_cast<uint32_t>(host_small[0]);
   if (eflags & kErrRange)
     return fail(set_error(SUBMCONV_ERR_COORD_OUT_OF_RANGE,
@@ -586,35 +599,27 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   m.active_pairs = static_cast<int64_t>(host_small[1]);
   if (m.active_pairs >= INT32_MAX)
     return fail(set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "too many active pairs for int32 offsets"));
-  if (!(flags & (SUBMCONV_FLAG_TILES_256 | SUBMCONV_FLAG_TILES_288))) {
+  int wide_rows = 0;
+  if (flags & SUBMCONV_FLAG_TILES_288) {
+    wide_rows = kTileRowsWide;
+  } else if (!(flags & SUBMCONV_FLAG_TILES_256)) {
     int cus = 256;
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, m.device);
     const int want = choose_tile_rows(n, m.active_pairs, cus);
-    if (want != tr) {
-      tr = want;
-      if (const int st = count_tiles(tr); st != SUBMCONV_OK) return st;
-    }
+    if (want > kTileRows) wide_rows = want;
   }
-  for (int q = 0; q < kTaps3; ++q) m.pos_groups[q] = static_cast<int64_t>(host_small[2 + q]);
-  // one more entry {-1, -1} after the lists: the target of masked loads
-  BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&ent), sizeof(int2) * (m.active_pairs + 1)));
-  BUILD_CHECK(hipMemsetAsync(ent + m.active_pairs, 0xff, sizeof(int2), stream));
-  if (tr > kTileRows)
-    k_tile_fill<kTileRowsWide><<<static_cast<unsigned>(n_tiles), (kTileRowsWide + 63) / 64 * 64, 0,
-                                 stream>>>(nbr, n, tr, tile_off, ent);
-  else
-    k_tile_fill<kTileRows><<<static_cast<unsigned>(n_tiles), kTileRows, 0, stream>>>(nbr, n, tr,
-                                                                                    tile_off, ent);
-  BUILD_CHECK(hipGetLastError());
+  if (wide_rows > 0)
+    if (const int st = count_tiles(wide_rows, wide); st != SUBMCONV_OK) return st;
+  if (const int st = fill_tiles(base); st != SUBMCONV_OK) return st;
+  if (wide_rows > 0)
+    if (const int st = fill_tiles(wide); st != SUBMCONV_OK) return st;
   // the forward may run on another stream: the map is complete on return
   BUILD_CHECK(hipStreamSynchronize(stream));
   m.nbr = nbr;
   m.order = order;
-  m.n_tiles = n_tiles;
-  m.tile_rows = tr;
-  m.tile_cnt = tile_cnt;
-  m.tile_off = tile_off;
-  m.ent = ent;
+  m.tiles = base;
+  m.wide = wide;
+  m.wide_always = (flags & SUBMCONV_FLAG_TILES_288) != 0;
   *out_map = new submconv_map_s{m};
   return SUBMCONV_OK;
 #undef BUILD_CHECK
@@ -627,7 +632,7 @@ extern "C" int64_t submconv_map_num_rows(submconv_map_t map) {
 
 extern "C" int32_t submconv_map_tile_rows(submconv_map_t map) {
   if (!map) return set_error(SUBMCONV_ERR_INVALID_ARG, "map is NULL");
-  return map->m.tile_rows;
+  return map->m.wide.n > 0 ? map->m.wide.rows : map->m.tiles.rows;
 }
 
 extern "C" int64_t submconv_map_active_pairs(submconv_map_t map, int32_t ksize) {
@@ -669,12 +674,14 @@ extern "C" int submconv_map_free(submconv_map_t map) {
     status = set_error(SUBMCONV_ERR_HIP, "hipFree of the map failed");
   if (map->m.order && hipFree(map->m.order) != hipSuccess)
     status = set_error(SUBMCONV_ERR_HIP, "hipFree of the order failed");
-  if (map->m.tile_cnt && hipFree(map->m.tile_cnt) != hipSuccess)
-    status = set_error(SUBMCONV_ERR_HIP, "hipFree of the tile counts failed");
-  if (map->m.tile_off && hipFree(map->m.tile_off) != hipSuccess)
-    status = set_error(SUBMCONV_ERR_HIP, "hipFree of the tile offsets failed");
-  if (map->m.ent && hipFree(map->m.ent) != hipSuccess)
-    status = set_error(SUBMCONV_ERR_HIP, "hipFree of the tile lists failed");
+  for (Tiles* T : {&map->m.tiles, &map->m.wide}) {
+    if (T->cnt && hipFree(T->cnt) != hipSuccess)
+      status = set_error(SUBMCONV_ERR_HIP, "hipFree of the tile counts failed");
+    if (T->off && hipFree(T->off) != hipSuccess)
+      status = set_error(SUBMCONV_ERR_HIP, "hipFree of the tile offsets failed");
+    if (T->ent && hipFree(T->ent) != hipSuccess)
+      status = set_error(SUBMCONV_ERR_HIP, "hipFree of the tile lists failed");
+  }
   delete map;
   return status;
 }

@@ -36,13 +36,26 @@ __host__ __device__ inline int tap_at(int p) {
 //  nbr      [27][n] int32, tap-major, rows in processing order t; each entry
 //           is the caller row of the neighbour at offset d_k, or -1.
 //  order    [n] int32, processing order t -> caller row; nullptr = identity.
-//  The same map as per-tile compacted lists (tiles of tile_rows consecutive
-//  processing rows), the form the forward kernels stream:
-//  tile_cnt [n_tiles][27] uint16, entries per processing position p.
-//  tile_off [n_tiles + 1] int32, first entry of each tile.
-//  ent      [active_pairs + 1] int2 {caller row of the neighbour, row in
-//           tile}, ordered by (tile, position p, row in tile), then one
-//           entry {-1, -1} that masked lanes load instead of selecting -1.
+//  tiles    the same map as per-tile compacted lists of kTileRows-row
+//           tiles, the form the forward kernels stream;
+//  wide     for sparse maps, the lists of tiles of up to kTileRowsWide rows
+//           as well (wide.n == 0: none); a forward takes them when they fit
+//           its workgroups into fewer rounds.
+// One tiling (tiles of `rows` consecutive processing rows):
+//  cnt  [n][27] uint16, entries per processing position p.
+//  off  [n + 1] int32, first entry of each tile.
+//  ent  [active_pairs + 1] int2 {caller row of the neighbour, row in tile},
+//       ordered by (tile, position p, row in tile), then one entry {-1, -1}
+//       that masked lanes load instead of selecting -1.
+struct Tiles {
+  int32_t rows = kTileRows;
+  int64_t n = 0;
+  uint16_t* cnt = nullptr;
+  int32_t* off = nullptr;
+  int2* ent = nullptr;
+  // groups of kGroupRows entries per processing position, over all tiles
+  int64_t pos_groups[kTaps3] = {};
+};
 struct Map {
   int device = 0;
   int64_t n = 0;
@@ -52,13 +65,9 @@ struct Map {
   int64_t active_pairs = 0;
   int32_t* nbr = nullptr;
   int32_t* order = nullptr;
-  int64_t n_tiles = 0;
-  int32_t tile_rows = kTileRows;  // kTileRows, or kTileRows+1 .. kTileRowsWide
-  uint16_t* tile_cnt = nullptr;
-  int32_t* tile_off = nullptr;
-  int2* ent = nullptr;
-  // groups of kGroupRows entries per processing position, over all tiles
-  int64_t pos_groups[kTaps3] = {};
+  Tiles tiles;
+  Tiles wide;
+  bool wide_always = false;  // forwards take the wide tiles whenever their kernel can
 };
 
 // Records a thread-local message and returns `status`.
