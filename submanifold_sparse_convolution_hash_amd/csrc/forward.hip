@@ -660,22 +660,23 @@ __device__ __forceinline__ _Float16 weight_at(const _Float16* __restrict__ W, in
 // writes one lane's 8 values (a 16-byte store).
 __global__ void k_prepare_mfma(const _Float16* __restrict__ W, int K, int cin, int cout, bool grad,
                                _Float16* __restrict__ wp) {
-  const int64_t total8 = static_cast<int64_t>(K) * cin * cout / 8;
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  // (32-bit index arithmetic: at most 27 x 1024 x 1024 / 8 chunks)
+  const uint32_t total8 = static_cast<uint32_t>(K) * cin * cout / 8;
+  const uint32_t idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total8) return;
-  const int KS = cin / 16;
+  const uint32_t KS = cin / 16, NCB = cout / 32;
   const int l = static_cast<int>(idx & 63);
-  int64_t rest = idx >> 6;
+  uint32_t rest = idx >> 6;
   const int st = static_cast<int>(rest % KS);
   rest /= KS;
-  const int cb = static_cast<int>(rest % (cout / 32));
-  const int k = static_cast<int>(rest / (cout / 32));
+  const int cb = static_cast<int>(rest % NCB);
+  const int k = static_cast<int>(rest / NCB);
   const int co = 32 * cb + (l & 31);
   const int ci0 = (l >> 5) * (cin / 2) + 8 * st;
   half8 v;
 #pragma unroll
   for (int j = 0; j < 8; ++j) v[j] = weight_at(W, K, cin, cout, grad, k, ci0 + j, co);
-  *reinterpret_cast<half8*>(wp + 8 * idx) = v;
+  *reinterpret_cast<half8*>(wp + 8 * static_cast<int64_t>(idx)) = v;
 }
 
 // Natural order W_t[k][ci][co] (the VALU kernel's layout).
