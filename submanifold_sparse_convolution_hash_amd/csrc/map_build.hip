@@ -340,20 +340,38 @@ struct DevBuf {
   ~DevBuf() { reset(); }
 };
 
-// Rows per tile: 256, or, when the map is sparse (fewer than one 32-entry
-// group per off-centre position of a 256-row tile on average, so that a
-// tile's step count barely grows with its rows) and tiles of up to 288 rows
-// need fewer rounds of one tile per compute unit, the fewest rows that fit
-// the tiles into those rounds.
-int choose_tile_rows(int64_t n, int64_t pairs, int cus) {
-  if (n <= 0 || cus <= 0) return kTileRows;
-  if ((pairs - n) * kTileRows >= int64_t{kGroupRows} * (kTaps3 - 1) * n) return kTileRows;
+// Sparse map: fewer than one kGroupRows-entry group per off-centre position
+// of a 256-row tile on average, so that a tile's step count barely grows
+// with its rows.
+bool sparse_map(int64_t n, int64_t pairs) {
+  return (pairs - n) * kTileRows < int64_t{kGroupRows} * (kTaps3 - 1) * n;
+}
+
+// Rows of the wider tiles a sparse map would take: when tiles of up to 288
+// rows need fewer rounds of one tile per compute unit than 256-row ones, the
+// fewest rows that fit the tiles into those rounds; otherwise 0 (none).
+int wide_tile_rows(int64_t n, int cus) {
+  if (n <= 0 || cus <= 0) return 0;
   const int64_t r256 = ((n + kTileRows - 1) / kTileRows + cus - 1) / cus;
   const int64_t r288 = ((n + kTileRowsWide - 1) / kTileRowsWide + cus - 1) / cus;
-  if (r288 >= r256) return kTileRows;
+  if (r288 >= r256) return 0;
   const int64_t slots = r288 * cus;
-  return static_cast<int>(std::min<int64_t>((n + slots - 1) / slots, kTileRowsWide));
+  const int tr = static_cast<int>(std::min<int64_t>((n + slots - 1) / slots, kTileRowsWide));
+  return tr > kTileRows ? tr : 0;
 }
+
+// Hands out 256-byte aligned pieces of one allocation: a first pass with no
+// base sizes it, a second pass over the same requests gives the pointers.
+struct Carve {
+  char* base = nullptr;
+  size_t used = 0;
+  template <class T>
+  T* take(size_t count) {
+    const size_t at = (used + 255) & ~size_t{255};
+    used = at + sizeof(T) * (count > 0 ? count : 1);
+    return base ? reinterpret_cast<T*>(base + at) : nullptr;
+  }
+};
 
 }  // namespace
 
@@ -427,20 +445,100 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   while (cap < 2 * n) cap <<= 1;
   const uint64_t mask = static_cast<uint64_t>(cap - 1);
 
-  DevBuf keys, tkeys, tvals, small, mcode_in, mcode_out, midx, sort_tmp, tile_tot, scan_tmp;
-  DevBuf skeys, srows, rows_in, ksort_tmp;
+  // tile sets: 256-row tiles always; wider ones when asked for, or (unless
+  // 256 rows are asked for) when the map turns out sparse and they save a
+  // round of tiles
+  int cus = 256;
+  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, m.device);
+  const int wide_cand = (flags & SUBMCONV_FLAG_TILES_288)   ? kTileRowsWide
+                        : (flags & SUBMCONV_FLAG_TILES_256) ? 0
+                                                            : wide_tile_rows(n, cus);
+  const int64_t nt_base = (n + kTileRows - 1) / kTileRows;
+  const int64_t nt_wide = wide_cand > 0 ? (n + wide_cand - 1) / wide_cand : 0;
+
+  // library scratch sizes, asked for before anything is allocated
+  size_t ksort_bytes = 0, msort_bytes = 0, scan_bytes = 0;
+  const int bbits = batch > 1 ? bits_for(batch) : 0;
+  const unsigned end_bit = static_cast<unsigned>(3 * mbits + bbits);
+  auto check_size = [&](hipError_t e) -> int {
+    if (e != hipSuccess)
+      return set_error(SUBMCONV_ERR_HIP, "scratch size query failed: %s", hipGetErrorString(e));
+    return SUBMCONV_OK;
+  };
+  if (sorted_keys)
+    if (const int st = check_size(rocprim::radix_sort_pairs(
+            nullptr, ksort_bytes, static_cast<const uint64_t*>(nullptr), static_cast<uint64_t*>(nullptr),
+            static_cast<const int32_t*>(nullptr), static_cast<int32_t*>(nullptr),
+            static_cast<size_t>(n), 0u, 64u, stream));
+        st != SUBMCONV_OK)
+      return st;
+  if (morton)
+    if (const int st = check_size(rocprim::radix_sort_pairs(
+            nullptr, msort_bytes, static_cast<const uint64_t*>(nullptr), static_cast<uint64_t*>(nullptr),
+            static_cast<const int32_t*>(nullptr), static_cast<int32_t*>(nullptr),
+            static_cast<size_t>(n), 0u, end_bit, stream));
+        st != SUBMCONV_OK)
+      return st;
+  for (const int64_t nt : {nt_base, nt_wide}) {
+    if (nt == 0) continue;
+    size_t b = 0;
+    if (const int st = check_size(rocprim::exclusive_scan(
+            nullptr, b, static_cast<const int32_t*>(nullptr), static_cast<int32_t*>(nullptr), 0,
+            static_cast<size_t>(nt + 1), rocprim::plus<int32_t>(), stream));
+        st != SUBMCONV_OK)
+      return st;
+    scan_bytes = std::max(scan_bytes, b);
+  }
+
+  // the build's temporaries, in one allocation freed on return
+  struct Temps {
+    uint64_t *keys, *tkeys, *skeys, *mcode_in, *mcode_out;
+    int32_t *tvals, *srows, *rows_in, *midx, *tile_tot;
+    void *small, *ksort, *msort, *scan;
+  } t{};
+  auto temps = [&](Carve& c) {
+    t.keys = c.take<uint64_t>(n);
+    if (sorted_keys) {
+      t.skeys = c.take<uint64_t>(n);
+      t.srows = c.take<int32_t>(n);
+      t.rows_in = c.take<int32_t>(n);
+      t.ksort = c.take<char>(ksort_bytes);
+    } else {
+      t.tkeys = c.take<uint64_t>(cap);
+      t.tvals = c.take<int32_t>(cap);
+    }
+    t.small = c.take<char>(256);
+    if (morton) {
+      t.mcode_in = c.take<uint64_t>(n);
+      t.mcode_out = c.take<uint64_t>(n);
+      t.midx = c.take<int32_t>(n);
+      t.msort = c.take<char>(msort_bytes);
+    }
+    t.tile_tot = c.take<int32_t>(nt_base + 1);  // the wide set has fewer tiles
+    t.scan = c.take<char>(scan_bytes);
+  };
+  // what the map keeps, but the lists (sized once the pairs are counted)
+  Tiles base, wide;
   int32_t* nbr = nullptr;
   int32_t* order = nullptr;
-  Tiles base, wide;  // 256-row tiles, and wider ones for sparse maps
+  auto kept = [&](Carve& c) {
+    nbr = c.take<int32_t>(kTaps3 * n);
+    if (morton) order = c.take<int32_t>(n);
+    base.cnt = c.take<uint16_t>(kTaps3 * nt_base);
+    base.off = c.take<int32_t>(nt_base + 1);
+    if (nt_wide > 0) {
+      wide.cnt = c.take<uint16_t>(kTaps3 * nt_wide);
+      wide.off = c.take<int32_t>(nt_wide + 1);
+    }
+  };
+
+  DevBuf tmp;
+  void* mem = nullptr;
+  void* ent_mem = nullptr;
   auto fail = [&](int status) {
     (void)hipStreamSynchronize(stream);
-    if (nbr) (void)hipFree(nbr);
-    if (order) (void)hipFree(order);
-    for (Tiles* T : {&base, &wide}) {
-      if (T->cnt) (void)hipFree(T->cnt);
-      if (T->off) (void)hipFree(T->off);
-      if (T->ent) (void)hipFree(T->ent);
-    }
+    if (mem) (void)hipFree(mem);
+    if (ent_mem) (void)hipFree(ent_mem);
     return status;
   };
 #define BUILD_CHECK(expr)                                                                 \
@@ -452,84 +550,54 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
                             "%s failed: %s", #expr, hipGetErrorString(e_)));             \
   } while (0)
 
-  BUILD_CHECK(hipMalloc(&keys.p, sizeof(uint64_t) * n));
-  if (sorted_keys) {
-    BUILD_CHECK(hipMalloc(&skeys.p, sizeof(uint64_t) * n));
-    BUILD_CHECK(hipMalloc(&srows.p, sizeof(int32_t) * n));
-    BUILD_CHECK(hipMalloc(&rows_in.p, sizeof(int32_t) * n));
-  } else {
-    BUILD_CHECK(hipMalloc(&tkeys.p, sizeof(uint64_t) * cap));
-    BUILD_CHECK(hipMalloc(&tvals.p, sizeof(int32_t) * cap));
+  {
+    Carve c;
+    temps(c);
+    BUILD_CHECK(hipMalloc(&tmp.p, c.used));
+    c = Carve{static_cast<char*>(tmp.p), 0};
+    temps(c);
   }
-  BUILD_CHECK(hipMalloc(&small.p, 256));
-  BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&nbr), sizeof(int32_t) * kTaps3 * n));
-  if (morton) {
-    BUILD_CHECK(hipMalloc(&mcode_in.p, sizeof(uint64_t) * n));
-    BUILD_CHECK(hipMalloc(&mcode_out.p, sizeof(uint64_t) * n));
-    BUILD_CHECK(hipMalloc(&midx.p, sizeof(int32_t) * n));
-    BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&order), sizeof(int32_t) * n));
+  {
+    Carve c;
+    kept(c);
+    BUILD_CHECK(hipMalloc(&mem, c.used));
+    c = Carve{static_cast<char*>(mem), 0};
+    kept(c);
   }
-  uint32_t* err = static_cast<uint32_t*>(small.p);
-  unsigned long long* pairs = reinterpret_cast<unsigned long long*>(static_cast<char*>(small.p) + 8);
+  uint32_t* err = static_cast<uint32_t*>(t.small);
+  unsigned long long* pairs = reinterpret_cast<unsigned long long*>(static_cast<char*>(t.small) + 8);
 
-  BUILD_CHECK(hipMemsetAsync(small.p, 0, 256, stream));
-  if (!sorted_keys) BUILD_CHECK(hipMemsetAsync(tkeys.p, 0xff, sizeof(uint64_t) * cap, stream));
+  BUILD_CHECK(hipMemsetAsync(t.small, 0, 256, stream));
+  if (!sorted_keys) BUILD_CHECK(hipMemsetAsync(t.tkeys, 0xff, sizeof(uint64_t) * cap, stream));
 
   const int B = 256;
-  k_pack<<<grid_for(n, B), B, 0, stream>>>(coords, n, batch, grid[0], grid[1], grid[2],
-                                           static_cast<uint64_t*>(keys.p), err, mbits,
-                                           static_cast<uint64_t*>(mcode_in.p),
-                                           static_cast<int32_t*>(midx.p));
+  k_pack<<<grid_for(n, B), B, 0, stream>>>(coords, n, batch, grid[0], grid[1], grid[2], t.keys, err,
+                                           mbits, t.mcode_in, t.midx);
   BUILD_CHECK(hipGetLastError());
   if (sorted_keys) {
     // rows 0..n-1 as the sort's values; out-of-range sites carry the empty
     // key, which sorts last and matches no query
-    k_iota<<<grid_for(n, B), B, 0, stream>>>(static_cast<int32_t*>(rows_in.p), n);
+    k_iota<<<grid_for(n, B), B, 0, stream>>>(t.rows_in, n);
     BUILD_CHECK(hipGetLastError());
-    size_t tmp_bytes = 0;
-    BUILD_CHECK(rocprim::radix_sort_pairs(nullptr, tmp_bytes, static_cast<const uint64_t*>(keys.p),
-                                          static_cast<uint64_t*>(skeys.p),
-                                          static_cast<const int32_t*>(rows_in.p),
-                                          static_cast<int32_t*>(srows.p), static_cast<size_t>(n),
-                                          0u, 64u, stream));
-    BUILD_CHECK(hipMalloc(&ksort_tmp.p, tmp_bytes > 0 ? tmp_bytes : 1));
-    BUILD_CHECK(rocprim::radix_sort_pairs(ksort_tmp.p, tmp_bytes, static_cast<const uint64_t*>(keys.p),
-                                          static_cast<uint64_t*>(skeys.p),
-                                          static_cast<const int32_t*>(rows_in.p),
-                                          static_cast<int32_t*>(srows.p), static_cast<size_t>(n),
-                                          0u, 64u, stream));
-    k_sorted_dups<<<grid_for(n, B), B, 0, stream>>>(static_cast<const uint64_t*>(skeys.p), n, kEmpty,
-                                                    err);
+    BUILD_CHECK(rocprim::radix_sort_pairs(t.ksort, ksort_bytes, static_cast<const uint64_t*>(t.keys),
+                                          t.skeys, static_cast<const int32_t*>(t.rows_in), t.srows,
+                                          static_cast<size_t>(n), 0u, 64u, stream));
+    k_sorted_dups<<<grid_for(n, B), B, 0, stream>>>(t.skeys, n, kEmpty, err);
   } else {
-    k_insert<<<grid_for(n, B), B, 0, stream>>>(static_cast<const uint64_t*>(keys.p), n,
-                                               static_cast<uint64_t*>(tkeys.p),
-                                               static_cast<int32_t*>(tvals.p), mask, err);
+    k_insert<<<grid_for(n, B), B, 0, stream>>>(t.keys, n, t.tkeys, t.tvals, mask, err);
   }
   BUILD_CHECK(hipGetLastError());
-  if (morton) {
-    const int bbits = batch > 1 ? bits_for(batch) : 0;
-    const unsigned end_bit = static_cast<unsigned>(3 * mbits + bbits);
-    size_t tmp_bytes = 0;
-    BUILD_CHECK(rocprim::radix_sort_pairs(nullptr, tmp_bytes,
-                                          static_cast<const uint64_t*>(mcode_in.p),
-                                          static_cast<uint64_t*>(mcode_out.p),
-                                          static_cast<const int32_t*>(midx.p), order,
+  if (morton)
+    BUILD_CHECK(rocprim::radix_sort_pairs(t.msort, msort_bytes,
+                                          static_cast<const uint64_t*>(t.mcode_in), t.mcode_out,
+                                          static_cast<const int32_t*>(t.midx), order,
                                           static_cast<size_t>(n), 0u, end_bit, stream));
-    BUILD_CHECK(hipMalloc(&sort_tmp.p, tmp_bytes > 0 ? tmp_bytes : 1));
-    BUILD_CHECK(rocprim::radix_sort_pairs(sort_tmp.p, tmp_bytes,
-                                          static_cast<const uint64_t*>(mcode_in.p),
-                                          static_cast<uint64_t*>(mcode_out.p),
-                                          static_cast<const int32_t*>(midx.p), order,
-                                          static_cast<size_t>(n), 0u, end_bit, stream));
-  }
   if (sorted_keys) {
-    k_query_sorted<<<grid_for(n * kTaps3, B), B, 0, stream>>>(
-        coords, order, n, grid[0], grid[1], grid[2], static_cast<const uint64_t*>(skeys.p),
-        static_cast<const int32_t*>(srows.p), nbr);
+    k_query_sorted<<<grid_for(n * kTaps3, B), B, 0, stream>>>(coords, order, n, grid[0], grid[1],
+                                                              grid[2], t.skeys, t.srows, nbr);
   } else {
     k_query<<<grid_for(n * kTaps3, B), B, 0, stream>>>(coords, order, n, grid[0], grid[1], grid[2],
-                                              static_cast<const uint64_t*>(tkeys.p),
-                                              static_cast<const int32_t*>(tvals.p), mask, nbr);
+                                                       t.tkeys, t.tvals, mask, nbr);
   }
   BUILD_CHECK(hipGetLastError());
 
@@ -537,38 +605,27 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   // (exclusive scan), the active pairs and the groups per position, read back
   uint64_t host_small[2 + kTaps3] = {};
   auto count_tiles = [&](int tr, Tiles& T) -> int {
-    tile_tot.reset();
-    scan_tmp.reset();
     const int64_t n_tiles = (n + tr - 1) / tr;
     T.rows = tr;
     T.n = n_tiles;
-    BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&T.cnt), sizeof(uint16_t) * kTaps3 * n_tiles));
-    BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&T.off), sizeof(int32_t) * (n_tiles + 1)));
-    uint16_t* tile_cnt = T.cnt;
-    int32_t* tile_off = T.off;
-    BUILD_CHECK(hipMalloc(&tile_tot.p, sizeof(int32_t) * (n_tiles + 1)));
-    BUILD_CHECK(hipMemsetAsync(tile_tot.p, 0, sizeof(int32_t) * (n_tiles + 1), stream));
+    BUILD_CHECK(hipMemsetAsync(t.tile_tot, 0, sizeof(int32_t) * (n_tiles + 1), stream));
     if (tr > kTileRows)
       k_tile_count<kTileRowsWide><<<static_cast<unsigned>(n_tiles), (kTileRowsWide + 63) / 64 * 64, 0,
-                                    stream>>>(nbr, n, tr, tile_cnt, static_cast<int32_t*>(tile_tot.p));
+                                    stream>>>(nbr, n, tr, T.cnt, t.tile_tot);
     else
       k_tile_count<kTileRows><<<static_cast<unsigned>(n_tiles), kTileRows, 0, stream>>>(
-          nbr, n, tr, tile_cnt, static_cast<int32_t*>(tile_tot.p));
+          nbr, n, tr, T.cnt, t.tile_tot);
     BUILD_CHECK(hipGetLastError());
-    size_t tmp_bytes = 0;
-    BUILD_CHECK(rocprim::exclusive_scan(nullptr, tmp_bytes, static_cast<const int32_t*>(tile_tot.p),
-                                        tile_off, 0, static_cast<size_t>(n_tiles + 1),
-                                        rocprim::plus<int32_t>(), stream));
-    BUILD_CHECK(hipMalloc(&scan_tmp.p, tmp_bytes > 0 ? tmp_bytes : 1));
-    BUILD_CHECK(rocprim::exclusive_scan(scan_tmp.p, tmp_bytes, static_cast<const int32_t*>(tile_tot.p),
-                                        tile_off, 0, static_cast<size_t>(n_tiles + 1),
-                                        rocprim::plus<int32_t>(), stream));
+    size_t sb = scan_bytes;
+    BUILD_CHECK(rocprim::exclusive_scan(t.scan, sb, static_cast<const int32_t*>(t.tile_tot), T.off, 0,
+                                        static_cast<size_t>(n_tiles + 1), rocprim::plus<int32_t>(),
+                                        stream));
     // the active pairs in 64 bits (the int32 offsets are checked against it)
-    k_total<<<1, 1024, 0, stream>>>(static_cast<const int32_t*>(tile_tot.p), n_tiles, pairs);
+    k_total<<<1, 1024, 0, stream>>>(t.tile_tot, n_tiles, pairs);
     BUILD_CHECK(hipGetLastError());
-    k_pos_groups<<<kTaps3, 256, 0, stream>>>(tile_cnt, n_tiles, pairs + 1);
+    k_pos_groups<<<kTaps3, 256, 0, stream>>>(T.cnt, n_tiles, pairs + 1);
     BUILD_CHECK(hipGetLastError());
-    BUILD_CHECK(hipMemcpyAsync(host_small, small.p, sizeof(host_small), hipMemcpyDeviceToHost,
+    BUILD_CHECK(hipMemcpyAsync(host_small, t.small, sizeof(host_small), hipMemcpyDeviceToHost,
                                stream));
     BUILD_CHECK(hipStreamSynchronize(stream));
     for (int q = 0; q < kTaps3; ++q) T.pos_groups[q] = static_cast<int64_t>(host_small[2 + q]);
@@ -577,7 +634,6 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   // the lists themselves; one more entry {-1, -1} after them: the target of
   // masked loads
   auto fill_tiles = [&](Tiles& T) -> int {
-    BUILD_CHECK(hipMalloc(reinterpret_cast<void**>(&T.ent), sizeof(int2) * (m.active_pairs + 1)));
     BUILD_CHECK(hipMemsetAsync(T.ent + m.active_pairs, 0xff, sizeof(int2), stream));
     if (T.rows > kTileRows)
       k_tile_fill<kTileRowsWide><<<static_cast<unsigned>(T.n), (kTileRowsWide + 63) / 64 * 64, 0,
@@ -599,22 +655,26 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   m.active_pairs = static_cast<int64_t>(host_small[1]);
   if (m.active_pairs >= INT32_MAX)
     return fail(set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "too many active pairs for int32 offsets"));
-  int wide_rows = 0;
-  if (flags & SUBMCONV_FLAG_TILES_288) {
-    wide_rows = kTileRowsWide;
-  } else if (!(flags & SUBMCONV_FLAG_TILES_256)) {
-    int cus = 256;
-    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, m.device);
-    const int want = choose_tile_rows(n, m.active_pairs, cus);
-    if (want > kTileRows) wide_rows = want;
+  const bool use_wide =
+      wide_cand > 0 && ((flags & SUBMCONV_FLAG_TILES_288) || sparse_map(n, m.active_pairs));
+  if (use_wide) {
+    if (const int st = count_tiles(wide_cand, wide); st != SUBMCONV_OK) return st;
+  } else {
+    wide = Tiles{};  // its counts and offsets go unused
   }
-  if (wide_rows > 0)
-    if (const int st = count_tiles(wide_rows, wide); st != SUBMCONV_OK) return st;
+  {
+    const size_t lists = (use_wide ? 2 : 1) * static_cast<size_t>(m.active_pairs + 1);
+    BUILD_CHECK(hipMalloc(&ent_mem, sizeof(int2) * lists));
+    base.ent = static_cast<int2*>(ent_mem);
+    if (use_wide) wide.ent = base.ent + (m.active_pairs + 1);
+  }
   if (const int st = fill_tiles(base); st != SUBMCONV_OK) return st;
-  if (wide_rows > 0)
+  if (use_wide)
     if (const int st = fill_tiles(wide); st != SUBMCONV_OK) return st;
   // the forward may run on another stream: the map is complete on return
   BUILD_CHECK(hipStreamSynchronize(stream));
+  m.mem = mem;
+  m.ent_mem = ent_mem;
   m.nbr = nbr;
   m.order = order;
   m.tiles = base;
@@ -670,18 +730,10 @@ extern "C" int submconv_map_free(submconv_map_t map) {
   clear_error();
   if (!map) return SUBMCONV_OK;
   int status = SUBMCONV_OK;
-  if (map->m.nbr && hipFree(map->m.nbr) != hipSuccess)
+  if (map->m.mem && hipFree(map->m.mem) != hipSuccess)
     status = set_error(SUBMCONV_ERR_HIP, "hipFree of the map failed");
-  if (map->m.order && hipFree(map->m.order) != hipSuccess)
-    status = set_error(SUBMCONV_ERR_HIP, "hipFree of the order failed");
-  for (Tiles* T : {&map->m.tiles, &map->m.wide}) {
-    if (T->cnt && hipFree(T->cnt) != hipSuccess)
-      status = set_error(SUBMCONV_ERR_HIP, "hipFree of the tile counts failed");
-    if (T->off && hipFree(T->off) != hipSuccess)
-      status = set_error(SUBMCONV_ERR_HIP, "hipFree of the tile offsets failed");
-    if (T->ent && hipFree(T->ent) != hipSuccess)
-      status = set_error(SUBMCONV_ERR_HIP, "hipFree of the tile lists failed");
-  }
+  if (map->m.ent_mem && hipFree(map->m.ent_mem) != hipSuccess)
+    status = set_error(SUBMCONV_ERR_HIP, "hipFree of the tile lists failed");
   delete map;
   return status;
 }

@@ -63,6 +63,10 @@ struct Map {
   int32_t grid[3] = {0, 0, 0};
   uint32_t flags = 0;
   int64_t active_pairs = 0;
+  // two device allocations hold everything below: `mem` the neighbour table,
+  // the order and both tile sets' counts and offsets, `ent_mem` the lists
+  void* mem = nullptr;
+  void* ent_mem = nullptr;
   int32_t* nbr = nullptr;
   int32_t* order = nullptr;
   Tiles tiles;
