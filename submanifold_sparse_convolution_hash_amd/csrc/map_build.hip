@@ -11,13 +11,17 @@
 // Steps (one stream, one host wait at the end):
 //   pack     coords -> keys, range validation (error flag)
 //   insert   keys -> table, 64-bit compare-and-swap, linear probing; a key
-//            that is already present raises the duplicate flag
+//            that is already present raises the duplicate flag. When every
+//            key fits in 32 bits a slot is one 64-bit word, key and row, so
+//            that a probe reads both with one load
 //   order    optional Morton codes + radix sort -> processing order
-//   query    27 probes per site -> nbr[27][n] (tap-major), pair count
-//   tiles    per tile of kTileRows processing rows, the neighbours of each
-//            tap compacted into a list of {neighbour row, row in tile}
+//   query    27 probes per site -> nbr[27][n] (tap-major), and the entries
+//            per tap of each kTileRows-row tile
+//   tiles    per tile of processing rows, the neighbours of each tap
+//            compacted into a list of {neighbour row, row in tile}
 //            (count, exclusive scan over tiles, fill)
-//   readback flags + pair count (the host wait that reports bad sites)
+//   readback flags + pair count (the host waits that report bad sites and
+//            size the lists)
 #include <rocprim/device/device_radix_sort.hpp>
 #include <rocprim/device/device_scan.hpp>
 
@@ -98,23 +102,37 @@ __global__ void k_iota(int32_t* __restrict__ v, int64_t n) {
   if (i < n) v[i] = static_cast<int32_t>(i);
 }
 
-__global__ void k_insert(const uint64_t* __restrict__ keys, int64_t n, uint64_t* tkeys,
+// First slot of a key: 8 consecutive keys (consecutive z of one line when
+// the z extent is a multiple of 8) share an aligned run of 8 slots, and the
+// runs scatter. A site's neighbours at z-1, z, z+1 then mostly share a cache
+// line of the table.
+__device__ __forceinline__ uint64_t start_slot(uint64_t key, uint64_t mask) {
+  return ((mix64(key >> 3) << 3) | (key & 7ull)) & mask;
+}
+
+// COMPACT: a slot is the key (below 2^32) in the low half and the row in the
+// high half, written by the one compare-and-swap; rows are below 2^31 - 1,
+// so a full slot never equals the empty one. Otherwise keys and rows sit in
+// two arrays.
+template <bool COMPACT>
+__global__ void k_insert(const uint64_t* __restrict__ keys, int64_t n, uint64_t* table,
                          int32_t* __restrict__ tvals, uint64_t mask, uint32_t* __restrict__ err) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= n) return;
   const uint64_t key = keys[i];
   if (key == kEmpty) return;  // out-of-range site, already flagged
-  uint64_t h = mix64(key) & mask;
+  const uint64_t want = COMPACT ? (static_cast<uint64_t>(i) << 32) | key : key;
+  uint64_t h = start_slot(key, mask);
   // The table holds at most n keys in >= 2n slots, so an empty slot exists.
   while (true) {
-    const unsigned long long prev = atomicCAS(reinterpret_cast<unsigned long long*>(tkeys + h),
+    const unsigned long long prev = atomicCAS(reinterpret_cast<unsigned long long*>(table + h),
                                               static_cast<unsigned long long>(kEmpty),
-                                              static_cast<unsigned long long>(key));
+                                              static_cast<unsigned long long>(want));
     if (prev == kEmpty) {
-      tvals[h] = static_cast<int32_t>(i);
+      if constexpr (!COMPACT) tvals[h] = static_cast<int32_t>(i);
       return;
     }
-    if (prev == key) {
+    if ((COMPACT ? (prev & 0xffffffffull) : prev) == key) {
       atomicOr(err, kErrDuplicate);
       return;
     }
@@ -122,38 +140,63 @@ __global__ void k_insert(const uint64_t* __restrict__ keys, int64_t n, uint64_t*
   }
 }
 
-// One thread per (tap k, processing row t), t fastest (coalesced writes of
-// the tap-major map, 27 independent probes in flight per row).
-__global__ void k_query(const int32_t* __restrict__ coords, const int32_t* __restrict__ order,
-                        int64_t n, int32_t g0, int32_t g1, int32_t g2,
-                        const uint64_t* __restrict__ tkeys, const int32_t* __restrict__ tvals,
-                        uint64_t mask, int32_t* __restrict__ nbr) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx < n * kTaps3) {
-    const int k = static_cast<int>(idx / n);
-    const int64_t t = idx - static_cast<int64_t>(k) * n;
+// Processing position of tap k (the inverse of tap_at).
+__device__ __forceinline__ int pos_of(int k) {
+  return k == kCenterTap ? 0 : (k < kCenterTap ? k + 1 : k);
+}
+
+// One workgroup per (kTileRows-row tile of processing rows, tap): thread r
+// probes the tap's neighbour of the tile's row r and writes nbr[k][t]
+// (coalesced, tap-major). The workgroups of an XCD (blockIdx % 8) take one
+// contiguous run of units, tap fastest, so that a tile's coordinates and the
+// table lines its neighbours share stay in that XCD's L2 over its 27 taps.
+// Each workgroup also writes the tile's entry count at its tap and adds it
+// to the tile's total (tile_tot zeroed before).
+template <bool COMPACT>
+__global__ __launch_bounds__(kTileRows) void k_query(
+    const int32_t* __restrict__ coords, const int32_t* __restrict__ order, int64_t n, int32_t g0,
+    int32_t g1, int32_t g2, const uint64_t* __restrict__ table, const int32_t* __restrict__ tvals,
+    uint64_t mask, int32_t* __restrict__ nbr, uint16_t* __restrict__ tile_cnt,
+    int32_t* __restrict__ tile_tot, uint32_t units) {
+  __shared__ int wcnt[kTileRows / 64];
+  const uint32_t bid = blockIdx.x, xcd = bid & 7u, q = units >> 3, rem = units & 7u;
+  const uint32_t u = xcd * q + (xcd < rem ? xcd : rem) + (bid >> 3);
+  const uint32_t tile = u / kTaps3;
+  const int k = static_cast<int>(u - tile * kTaps3);
+  const int64_t t = static_cast<int64_t>(tile) * kTileRows + threadIdx.x;
+  int32_t j = -1;
+  if (t < n) {
     const int64_t i = order ? order[t] : t;
     const int32_t b = coords[4 * i + 0];
     const int32_t nx = coords[4 * i + 1] + (k / 9) - 1;
     const int32_t ny = coords[4 * i + 2] + ((k / 3) % 3) - 1;
     const int32_t nz = coords[4 * i + 3] + (k % 3) - 1;
-    int32_t j = -1;
     if (k == kCenterTap) {
       j = static_cast<int32_t>(i);
     } else if (nx >= 0 && nx < g0 && ny >= 0 && ny < g1 && nz >= 0 && nz < g2) {
       const uint64_t key = pack_key(b, nx, ny, nz, g0, g1, g2);
-      uint64_t h = mix64(key) & mask;
+      uint64_t h = start_slot(key, mask);
       while (true) {
-        const uint64_t s = tkeys[h];
-        if (s == key) {
-          j = tvals[h];
+        const uint64_t s = table[h];
+        if (s == kEmpty) break;
+        if ((COMPACT ? (s & 0xffffffffull) : s) == key) {
+          j = COMPACT ? static_cast<int32_t>(s >> 32) : tvals[h];
           break;
         }
-        if (s == kEmpty) break;
         h = (h + 1) & mask;
       }
     }
-    nbr[idx] = j;
+    nbr[static_cast<int64_t>(k) * n + t] = j;
+  }
+  const uint64_t m = __ballot(j >= 0);
+  if ((threadIdx.x & 63) == 0) wcnt[threadIdx.x >> 6] = __popcll(m);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kTileRows / 64; ++w) c += wcnt[w];
+    tile_cnt[static_cast<int64_t>(tile) * kTaps3 + pos_of(k)] = static_cast<uint16_t>(c);
+    atomicAdd(tile_tot + tile, c);
   }
 }
 
@@ -444,6 +487,15 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   int64_t cap = 64;
   while (cap < 2 * n) cap <<= 1;
   const uint64_t mask = static_cast<uint64_t>(cap - 1);
+  // one-word slots when every packed key is below 2^32
+  bool compact = true;
+  {
+    uint64_t v = static_cast<uint64_t>(batch);
+    for (int a = 0; a < 3 && compact; ++a) {
+      v *= static_cast<uint64_t>(grid[a]);  // < 2^63 (checked above)
+      compact = v <= (uint64_t{1} << 32);
+    }
+  }
 
   // tile sets: 256-row tiles always; wider ones when asked for, or (unless
   // 256 rows are asked for) when the map turns out sparse and they save a
@@ -505,7 +557,7 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
       t.ksort = c.take<char>(ksort_bytes);
     } else {
       t.tkeys = c.take<uint64_t>(cap);
-      t.tvals = c.take<int32_t>(cap);
+      if (!compact) t.tvals = c.take<int32_t>(cap);
     }
     t.small = c.take<char>(256);
     if (morton) {
@@ -583,8 +635,10 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
                                           t.skeys, static_cast<const int32_t*>(t.rows_in), t.srows,
                                           static_cast<size_t>(n), 0u, 64u, stream));
     k_sorted_dups<<<grid_for(n, B), B, 0, stream>>>(t.skeys, n, kEmpty, err);
+  } else if (compact) {
+    k_insert<true><<<grid_for(n, B), B, 0, stream>>>(t.keys, n, t.tkeys, nullptr, mask, err);
   } else {
-    k_insert<<<grid_for(n, B), B, 0, stream>>>(t.keys, n, t.tkeys, t.tvals, mask, err);
+    k_insert<false><<<grid_for(n, B), B, 0, stream>>>(t.keys, n, t.tkeys, t.tvals, mask, err);
   }
   BUILD_CHECK(hipGetLastError());
   if (morton)
@@ -596,26 +650,37 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
     k_query_sorted<<<grid_for(n * kTaps3, B), B, 0, stream>>>(coords, order, n, grid[0], grid[1],
                                                               grid[2], t.skeys, t.srows, nbr);
   } else {
-    k_query<<<grid_for(n * kTaps3, B), B, 0, stream>>>(coords, order, n, grid[0], grid[1], grid[2],
-                                                       t.tkeys, t.tvals, mask, nbr);
+    // the query also counts the 256-row tiles' entries
+    BUILD_CHECK(hipMemsetAsync(t.tile_tot, 0, sizeof(int32_t) * (nt_base + 1), stream));
+    const uint32_t units = static_cast<uint32_t>(nt_base * kTaps3);
+    if (compact)
+      k_query<true><<<units, kTileRows, 0, stream>>>(coords, order, n, grid[0], grid[1], grid[2],
+                                                     t.tkeys, nullptr, mask, nbr, base.cnt,
+                                                     t.tile_tot, units);
+    else
+      k_query<false><<<units, kTileRows, 0, stream>>>(coords, order, n, grid[0], grid[1], grid[2],
+                                                      t.tkeys, t.tvals, mask, nbr, base.cnt,
+                                                      t.tile_tot, units);
   }
   BUILD_CHECK(hipGetLastError());
 
   // per-tile compacted lists of tr-row tiles: counts, tile offsets
   // (exclusive scan), the active pairs and the groups per position, read back
   uint64_t host_small[2 + kTaps3] = {};
-  auto count_tiles = [&](int tr, Tiles& T) -> int {
+  auto count_tiles = [&](int tr, Tiles& T, bool counted) -> int {
     const int64_t n_tiles = (n + tr - 1) / tr;
     T.rows = tr;
     T.n = n_tiles;
-    BUILD_CHECK(hipMemsetAsync(t.tile_tot, 0, sizeof(int32_t) * (n_tiles + 1), stream));
-    if (tr > kTileRows)
-      k_tile_count<kTileRowsWide><<<static_cast<unsigned>(n_tiles), (kTileRowsWide + 63) / 64 * 64, 0,
-                                    stream>>>(nbr, n, tr, T.cnt, t.tile_tot);
-    else
-      k_tile_count<kTileRows><<<static_cast<unsigned>(n_tiles), kTileRows, 0, stream>>>(
-          nbr, n, tr, T.cnt, t.tile_tot);
-    BUILD_CHECK(hipGetLastError());
+    if (!counted) {  // (the hash query counts the 256-row tiles itself)
+      BUILD_CHECK(hipMemsetAsync(t.tile_tot, 0, sizeof(int32_t) * (n_tiles + 1), stream));
+      if (tr > kTileRows)
+        k_tile_count<kTileRowsWide><<<static_cast<unsigned>(n_tiles), (kTileRowsWide + 63) / 64 * 64,
+                                      0, stream>>>(nbr, n, tr, T.cnt, t.tile_tot);
+      else
+        k_tile_count<kTileRows><<<static_cast<unsigned>(n_tiles), kTileRows, 0, stream>>>(
+            nbr, n, tr, T.cnt, t.tile_tot);
+      BUILD_CHECK(hipGetLastError());
+    }
     size_t sb = scan_bytes;
     BUILD_CHECK(rocprim::exclusive_scan(t.scan, sb, static_cast<const int32_t*>(t.tile_tot), T.off, 0,
                                         static_cast<size_t>(n_tiles + 1), rocprim::plus<int32_t>(),
@@ -644,7 +709,7 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
     BUILD_CHECK(hipGetLastError());
     return SUBMCONV_OK;
   };
-  if (const int st = count_tiles(kTileRows, base); st != SUBMCONV_OK) return st;
+  if (const int st = count_tiles(kTileRows, base, !sorted_keys); st != SUBMCONV_OK) return st;
   const uint32_t eflags = static_cast<uint32_t>(host_small[0]);
   if (eflags & kErrRange)
     return fail(set_error(SUBMCONV_ERR_COORD_OUT_OF_RANGE,
@@ -658,7 +723,7 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   const bool use_wide =
       wide_cand > 0 && ((flags & SUBMCONV_FLAG_TILES_288) || sparse_map(n, m.active_pairs));
   if (use_wide) {
-    if (const int st = count_tiles(wide_cand, wide); st != SUBMCONV_OK) return st;
+    if (const int st = count_tiles(wide_cand, wide, false); st != SUBMCONV_OK) return st;
   } else {
     wide = Tiles{};  // its counts and offsets go unused
   }

@@ -353,6 +353,59 @@ def test_errors(dev):
     assert e.value.status == -1
 
 
+def _blob_sites(rng, grid, batch, corners, side=10, occ=0.35):
+    """Sites of occupancy ``occ`` in blocks of up to side^3 cells at the given
+    corners (one per batch item and corner), with their batch column."""
+    dims = [min(side, g) for g in grid]
+    out = []
+    for b in range(batch):
+        for c in corners:
+            lo = np.array([min(max(c[a], 0), grid[a] - dims[a]) for a in range(3)])
+            cells = np.argwhere(rng.random(dims) < occ) + lo
+            out.append(np.concatenate([np.full((len(cells), 1), b), cells], axis=1))
+    return np.ascontiguousarray(np.concatenate(out).astype(np.int32))
+
+
+@gpu
+@pytest.mark.parametrize("grid,batch", [
+    ((2048, 2048, 1024), 1),  # batch x volume = 2^32: one-word slots, top key 2^32 - 1
+    ((2048, 2048, 1024), 2),  # 2^33: keys and rows in two arrays
+    ((4096, 4096, 4096), 1),  # 2^36
+    ((100, 3000, 7), 3),      # z extent not a multiple of 8
+])
+def test_map_key_widths(dev, grid, batch):
+    """The hash table's two slot layouts (packed keys below 2^32, or wider)
+    give the oracle's map bit for bit, including the largest key; duplicates
+    are found in both."""
+    sc = _sc()
+    rng = np.random.default_rng(sum(grid) + batch)
+    far = tuple(g - 1 for g in grid)
+    coords = _blob_sites(rng, grid, batch, [(0, 0, 0), far, (grid[0] // 2, grid[1] // 3, grid[2] // 5)])
+    top = np.array([[batch - 1, *far]], dtype=np.int32)
+    if not (coords == top).all(axis=1).any():
+        coords = np.concatenate([coords, top])
+    coords = coords[rng.permutation(len(coords))]
+    _say(f"[map_key_widths] grid {grid} batch {batch}: {len(coords)} sites")
+    ref = oc.kernel_map(coords, grid, batch, 3)
+    for morton in (False, True):
+        km = sc.build_map(_to(dev, coords), grid, batch, morton=morton)
+        np.testing.assert_array_equal(km.export().cpu().numpy(), ref)
+        assert km.active_pairs(3) == int((ref >= 0).sum())
+        km.free()
+    # a small forward on the same map
+    cin = cout = 32
+    feats = rng.standard_normal((len(coords), cin)).astype(np.float16)
+    W = (rng.standard_normal((27, cin, cout)) / np.sqrt(27 * cin)).astype(np.float16)
+    km = sc.build_map(_to(dev, coords), grid, batch)
+    out = sc.forward(km, _to(dev, feats), _to(dev, W), None)
+    _assert_close(out.float().cpu().numpy(), oc.submconv_rows(ref, feats, W, None), "forward")
+    km.free()
+    dup = np.concatenate([coords, coords[len(coords) // 2:len(coords) // 2 + 1]])
+    with pytest.raises(sc.SubmconvError) as e:
+        sc.build_map(_to(dev, dup), grid, batch)
+    assert e.value.status == -3
+
+
 # ----------------------------------------------------------------------------
 # the sorted-key map builder: the same map, lists and results as the hash
 # ----------------------------------------------------------------------------
