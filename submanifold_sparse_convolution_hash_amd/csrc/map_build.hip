@@ -20,10 +20,10 @@
 //   tiles    per tile of processing rows, the neighbours of each tap
 //            compacted into a list of {neighbour row, row in tile}
 //            (count, exclusive scan over tiles, fill)
-//   readback flags + pair count (the host waits that report bad sites and
-//            size the lists)
+//   readback flags + pair count: the one host wait before the lists, which
+//            reports bad sites and sizes the lists (the wider tiles' counts
+//            and lists follow it, read back at the final wait)
 #include <rocprim/device/device_radix_sort.hpp>
-#include <rocprim/device/device_scan.hpp>
 
 #include <algorithm>
 #include <cstdarg>
@@ -200,40 +200,67 @@ __global__ __launch_bounds__(kTileRows) void k_query(
   }
 }
 
-// Sum of the per-tile entry counts in 64 bits (the active pairs): one
-// workgroup, fixed order, no atomics.
-__global__ __launch_bounds__(1024) void k_total(const int32_t* __restrict__ tile_tot, int64_t n_tiles,
-                                                unsigned long long* __restrict__ total) {
-  __shared__ unsigned long long part[1024];
-  unsigned long long s = 0;
-  for (int64_t i = threadIdx.x; i < n_tiles; i += 1024) s += static_cast<unsigned long long>(tile_tot[i]);
-  part[threadIdx.x] = s;
-  __syncthreads();
-  for (int w = 512; w > 0; w >>= 1) {
-    if (static_cast<int>(threadIdx.x) < w) part[threadIdx.x] += part[threadIdx.x + w];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) *total = part[0];
+// Clears a build's scratch in one launch: the hash table's slots (all ones)
+// and a run of words to zero (flags, pair count, groups, tile totals).
+__global__ void k_init(uint64_t* __restrict__ table, int64_t cap, uint32_t* __restrict__ zero,
+                       int64_t n_zero) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (int64_t i = i0; i < cap; i += stride) table[i] = kEmpty;
+  for (int64_t i = i0; i < n_zero; i += stride) zero[i] = 0u;
 }
 
-// Groups of 32 entries per processing position, summed over the tiles
-// (the work of the weight gradient's positions): one workgroup per
-// position, fixed order, no atomics.
-__global__ __launch_bounds__(256) void k_pos_groups(const uint16_t* __restrict__ tile_cnt,
-                                                   int64_t n_tiles,
-                                                   unsigned long long* __restrict__ groups) {
-  __shared__ unsigned long long part[256];
-  const int p = blockIdx.x;
+// The sums of one tile set after its counts, in one launch with a fixed
+// summation order and no atomics. Blocks 0..26: the groups of kGroupRows
+// entries at processing position p, over the tiles (the work of the weight
+// gradient's positions). Block 27: the tiles' list offsets, an exclusive scan
+// of the tile totals whose entry n_tiles holds all entries, and the active
+// pairs in 64 bits when asked for (the int32 offsets are checked against it).
+__global__ __launch_bounds__(1024) void k_tile_sums(const int32_t* __restrict__ tile_tot,
+                                                    const uint16_t* __restrict__ tile_cnt,
+                                                    int64_t n_tiles, int32_t* __restrict__ tile_off,
+                                                    unsigned long long* __restrict__ pairs,
+                                                    unsigned long long* __restrict__ groups) {
+  __shared__ unsigned long long part[1024];
+  const int tid = threadIdx.x;
+  if (blockIdx.x < kTaps3) {
+    const int p = blockIdx.x;
+    unsigned long long s = 0;
+    for (int64_t t = tid; t < n_tiles; t += 1024)
+      s += (tile_cnt[t * kTaps3 + p] + kGroupRows - 1) / kGroupRows;
+    part[tid] = s;
+    __syncthreads();
+    for (int w = 512; w > 0; w >>= 1) {
+      if (tid < w) part[tid] += part[tid + w];
+      __syncthreads();
+    }
+    if (tid == 0) groups[p] = part[0];
+    return;
+  }
+  // thread tid owns the tiles [lo, hi): their sum, a scan of the 1024 sums,
+  // then the running offsets
+  const int64_t per = (n_tiles + 1023) / 1024;
+  const int64_t lo = std::min<int64_t>(tid * per, n_tiles);
+  const int64_t hi = std::min<int64_t>(lo + per, n_tiles);
   unsigned long long s = 0;
-  for (int64_t t = threadIdx.x; t < n_tiles; t += 256)
-    s += (tile_cnt[t * kTaps3 + p] + kGroupRows - 1) / kGroupRows;
-  part[threadIdx.x] = s;
+  for (int64_t t = lo; t < hi; ++t) s += static_cast<unsigned long long>(tile_tot[t]);
+  part[tid] = s;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (static_cast<int>(threadIdx.x) < w) part[threadIdx.x] += part[threadIdx.x + w];
+  for (int w = 1; w < 1024; w <<= 1) {  // inclusive scan
+    const unsigned long long v = tid >= w ? part[tid - w] : 0ull;
+    __syncthreads();
+    part[tid] += v;
     __syncthreads();
   }
-  if (threadIdx.x == 0) groups[p] = part[0];
+  unsigned long long run = part[tid] - s;
+  for (int64_t t = lo; t < hi; ++t) {
+    tile_off[t] = static_cast<int32_t>(run);
+    run += static_cast<unsigned long long>(tile_tot[t]);
+  }
+  if (tid == 1023) {
+    tile_off[n_tiles] = static_cast<int32_t>(part[1023]);
+    if (pairs) *pairs = part[1023];
+  }
 }
 
 // Sorted-key builder (the packing + sort + search lookup of "Running
@@ -327,6 +354,8 @@ __global__ __launch_bounds__((TR + 63) / 64 * 64) void k_tile_fill(
     if (lane == 0) masks[k][w] = m;
   }
   __syncthreads();
+  // one more entry {-1, -1} after all lists: the target of masked loads
+  if (blockIdx.x == 0 && threadIdx.x == 0) ent[tile_off[gridDim.x]] = make_int2(-1, -1);
   const uint64_t below = (1ull << lane) - 1ull;
   int64_t base = tile_off[blockIdx.x];
   for (int p = 0; p < kTaps3; ++p) {
@@ -509,7 +538,7 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   const int64_t nt_wide = wide_cand > 0 ? (n + wide_cand - 1) / wide_cand : 0;
 
   // library scratch sizes, asked for before anything is allocated
-  size_t ksort_bytes = 0, msort_bytes = 0, scan_bytes = 0;
+  size_t ksort_bytes = 0, msort_bytes = 0;
   const int bbits = batch > 1 ? bits_for(batch) : 0;
   const unsigned end_bit = static_cast<unsigned>(3 * mbits + bbits);
   auto check_size = [&](hipError_t e) -> int {
@@ -531,22 +560,12 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
             static_cast<size_t>(n), 0u, end_bit, stream));
         st != SUBMCONV_OK)
       return st;
-  for (const int64_t nt : {nt_base, nt_wide}) {
-    if (nt == 0) continue;
-    size_t b = 0;
-    if (const int st = check_size(rocprim::exclusive_scan(
-            nullptr, b, static_cast<const int32_t*>(nullptr), static_cast<int32_t*>(nullptr), 0,
-            static_cast<size_t>(nt + 1), rocprim::plus<int32_t>(), stream));
-        st != SUBMCONV_OK)
-      return st;
-    scan_bytes = std::max(scan_bytes, b);
-  }
 
   // the build's temporaries, in one allocation freed on return
   struct Temps {
     uint64_t *keys, *tkeys, *skeys, *mcode_in, *mcode_out;
-    int32_t *tvals, *srows, *rows_in, *midx, *tile_tot;
-    void *small, *ksort, *msort, *scan;
+    int32_t *tvals, *srows, *rows_in, *midx, *tile_tot, *tile_tot_wide;
+    void *small, *ksort, *msort;
   } t{};
   auto temps = [&](Carve& c) {
     t.keys = c.take<uint64_t>(n);
@@ -559,15 +578,16 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
       t.tkeys = c.take<uint64_t>(cap);
       if (!compact) t.tvals = c.take<int32_t>(cap);
     }
-    t.small = c.take<char>(256);
     if (morton) {
       t.mcode_in = c.take<uint64_t>(n);
       t.mcode_out = c.take<uint64_t>(n);
       t.midx = c.take<int32_t>(n);
       t.msort = c.take<char>(msort_bytes);
     }
-    t.tile_tot = c.take<int32_t>(nt_base + 1);  // the wide set has fewer tiles
-    t.scan = c.take<char>(scan_bytes);
+    // zeroed together, at the end: flags and sums, and the tile totals
+    t.small = c.take<char>(512);
+    t.tile_tot = c.take<int32_t>(nt_base + 1);
+    t.tile_tot_wide = c.take<int32_t>(nt_wide + 1);
   };
   // what the map keeps, but the lists (sized once the pairs are counted)
   Tiles base, wide;
@@ -619,10 +639,16 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   uint32_t* err = static_cast<uint32_t*>(t.small);
   unsigned long long* pairs = reinterpret_cast<unsigned long long*>(static_cast<char*>(t.small) + 8);
 
-  BUILD_CHECK(hipMemsetAsync(t.small, 0, 256, stream));
-  if (!sorted_keys) BUILD_CHECK(hipMemsetAsync(t.tkeys, 0xff, sizeof(uint64_t) * cap, stream));
-
   const int B = 256;
+  {
+    const int64_t n_table = sorted_keys ? 0 : cap;
+    const int64_t n_zero =
+        (reinterpret_cast<char*>(t.tile_tot_wide + nt_wide + 1) - static_cast<char*>(t.small)) / 4;
+    const int64_t most = std::max(n_table, n_zero);
+    k_init<<<static_cast<unsigned>(std::min<int64_t>((most + B - 1) / B, 2048)), B, 0, stream>>>(
+        t.tkeys, n_table, static_cast<uint32_t*>(t.small), n_zero);
+    BUILD_CHECK(hipGetLastError());
+  }
   k_pack<<<grid_for(n, B), B, 0, stream>>>(coords, n, batch, grid[0], grid[1], grid[2], t.keys, err,
                                            mbits, t.mcode_in, t.midx);
   BUILD_CHECK(hipGetLastError());
@@ -651,7 +677,6 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
                                                               grid[2], t.skeys, t.srows, nbr);
   } else {
     // the query also counts the 256-row tiles' entries
-    BUILD_CHECK(hipMemsetAsync(t.tile_tot, 0, sizeof(int32_t) * (nt_base + 1), stream));
     const uint32_t units = static_cast<uint32_t>(nt_base * kTaps3);
     if (compact)
       k_query<true><<<units, kTileRows, 0, stream>>>(coords, order, n, grid[0], grid[1], grid[2],
@@ -664,42 +689,32 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   }
   BUILD_CHECK(hipGetLastError());
 
-  // per-tile compacted lists of tr-row tiles: counts, tile offsets
-  // (exclusive scan), the active pairs and the groups per position, read back
-  uint64_t host_small[2 + kTaps3] = {};
-  auto count_tiles = [&](int tr, Tiles& T, bool counted) -> int {
+  // per-tile compacted lists of tr-row tiles: counts (into zeroed totals),
+  // list offsets and groups per position; for the 256-row tiles also the
+  // active pairs (the same for every tile size)
+  unsigned long long* groups_wide =
+      reinterpret_cast<unsigned long long*>(static_cast<char*>(t.small) + 256);
+  auto count_tiles = [&](int tr, Tiles& T, int32_t* tot, bool counted, bool total,
+                         unsigned long long* groups) -> int {
     const int64_t n_tiles = (n + tr - 1) / tr;
     T.rows = tr;
     T.n = n_tiles;
     if (!counted) {  // (the hash query counts the 256-row tiles itself)
-      BUILD_CHECK(hipMemsetAsync(t.tile_tot, 0, sizeof(int32_t) * (n_tiles + 1), stream));
       if (tr > kTileRows)
         k_tile_count<kTileRowsWide><<<static_cast<unsigned>(n_tiles), (kTileRowsWide + 63) / 64 * 64,
-                                      0, stream>>>(nbr, n, tr, T.cnt, t.tile_tot);
+                                      0, stream>>>(nbr, n, tr, T.cnt, tot);
       else
         k_tile_count<kTileRows><<<static_cast<unsigned>(n_tiles), kTileRows, 0, stream>>>(
-            nbr, n, tr, T.cnt, t.tile_tot);
+            nbr, n, tr, T.cnt, tot);
       BUILD_CHECK(hipGetLastError());
     }
-    size_t sb = scan_bytes;
-    BUILD_CHECK(rocprim::exclusive_scan(t.scan, sb, static_cast<const int32_t*>(t.tile_tot), T.off, 0,
-                                        static_cast<size_t>(n_tiles + 1), rocprim::plus<int32_t>(),
-                                        stream));
-    // the active pairs in 64 bits (the int32 offsets are checked against it)
-    k_total<<<1, 1024, 0, stream>>>(t.tile_tot, n_tiles, pairs);
+    k_tile_sums<<<kTaps3 + 1, 1024, 0, stream>>>(tot, T.cnt, n_tiles, T.off, total ? pairs : nullptr,
+                                                 groups);
     BUILD_CHECK(hipGetLastError());
-    k_pos_groups<<<kTaps3, 256, 0, stream>>>(T.cnt, n_tiles, pairs + 1);
-    BUILD_CHECK(hipGetLastError());
-    BUILD_CHECK(hipMemcpyAsync(host_small, t.small, sizeof(host_small), hipMemcpyDeviceToHost,
-                               stream));
-    BUILD_CHECK(hipStreamSynchronize(stream));
-    for (int q = 0; q < kTaps3; ++q) T.pos_groups[q] = static_cast<int64_t>(host_small[2 + q]);
     return SUBMCONV_OK;
   };
-  // the lists themselves; one more entry {-1, -1} after them: the target of
-  // masked loads
+  // the lists themselves, and the entry {-1, -1} after them
   auto fill_tiles = [&](Tiles& T) -> int {
-    BUILD_CHECK(hipMemsetAsync(T.ent + m.active_pairs, 0xff, sizeof(int2), stream));
     if (T.rows > kTileRows)
       k_tile_fill<kTileRowsWide><<<static_cast<unsigned>(T.n), (kTileRowsWide + 63) / 64 * 64, 0,
                                    stream>>>(nbr, n, T.rows, T.off, T.ent);
@@ -709,7 +724,13 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
     BUILD_CHECK(hipGetLastError());
     return SUBMCONV_OK;
   };
-  if (const int st = count_tiles(kTileRows, base, !sorted_keys); st != SUBMCONV_OK) return st;
+  // the one host wait before the lists: flags, active pairs, groups
+  uint64_t host_small[2 + kTaps3] = {};
+  if (const int st = count_tiles(kTileRows, base, t.tile_tot, !sorted_keys, true, pairs + 1); st != SUBMCONV_OK)
+    return st;
+  BUILD_CHECK(hipMemcpyAsync(host_small, t.small, sizeof(host_small), hipMemcpyDeviceToHost, stream));
+  BUILD_CHECK(hipStreamSynchronize(stream));
+  for (int q = 0; q < kTaps3; ++q) base.pos_groups[q] = static_cast<int64_t>(host_small[2 + q]);
   const uint32_t eflags = static_cast<uint32_t>(host_small[0]);
   if (eflags & kErrRange)
     return fail(set_error(SUBMCONV_ERR_COORD_OUT_OF_RANGE,
@@ -722,11 +743,7 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
     return fail(set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "too many active pairs for int32 offsets"));
   const bool use_wide =
       wide_cand > 0 && ((flags & SUBMCONV_FLAG_TILES_288) || sparse_map(n, m.active_pairs));
-  if (use_wide) {
-    if (const int st = count_tiles(wide_cand, wide, false); st != SUBMCONV_OK) return st;
-  } else {
-    wide = Tiles{};  // its counts and offsets go unused
-  }
+  if (!use_wide) wide = Tiles{};  // its counts and offsets go unused
   {
     const size_t lists = (use_wide ? 2 : 1) * static_cast<size_t>(m.active_pairs + 1);
     BUILD_CHECK(hipMalloc(&ent_mem, sizeof(int2) * lists));
@@ -734,10 +751,17 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
     if (use_wide) wide.ent = base.ent + (m.active_pairs + 1);
   }
   if (const int st = fill_tiles(base); st != SUBMCONV_OK) return st;
-  if (use_wide)
+  uint64_t host_groups[kTaps3] = {};
+  if (use_wide) {
+    if (const int st = count_tiles(wide_cand, wide, t.tile_tot_wide, false, false, groups_wide); st != SUBMCONV_OK) return st;
     if (const int st = fill_tiles(wide); st != SUBMCONV_OK) return st;
+    BUILD_CHECK(hipMemcpyAsync(host_groups, groups_wide, sizeof(host_groups), hipMemcpyDeviceToHost,
+                               stream));
+  }
   // the forward may run on another stream: the map is complete on return
   BUILD_CHECK(hipStreamSynchronize(stream));
+  if (use_wide)
+    for (int q = 0; q < kTaps3; ++q) wide.pos_groups[q] = static_cast<int64_t>(host_groups[q]);
   m.mem = mem;
   m.ent_mem = ent_mem;
   m.nbr = nbr;
