@@ -101,12 +101,17 @@ typedef struct submconv_map_s* submconv_map_t;
  *          SUBMCONV_FLAG_TILES_256 / SUBMCONV_FLAG_TILES_288.
  * out_map  receives the handle (host pointer).
  *
- * The map is built on `stream`; the function then waits for that stream once
- * (to read back the validation flags and the active-pair count; a second
- * time when it also builds wider tiles) and returns
- * SUBMCONV_ERR_COORD_OUT_OF_RANGE or SUBMCONV_ERR_DUPLICATE_COORD, with no
- * handle, when the sites are invalid. It allocates device memory
- * (27*n*4 bytes for the map, plus temporaries freed before return).
+ * The map is built on `stream`. The function waits for that stream twice:
+ * once to read back the validation flags and the active-pair count, when it
+ * returns SUBMCONV_ERR_COORD_OUT_OF_RANGE or SUBMCONV_ERR_DUPLICATE_COORD,
+ * with no handle, for invalid sites; and once at the end, so that the map
+ * is complete on return. The map's device memory is 27*n*4 bytes for the
+ * neighbour table plus the per-tile lists (8 bytes per active pair and tile
+ * set). The build's scratch (the hash table: at least 2n slots of 8 bytes,
+ * or 12 when packed keys exceed 32 bits; 8 bytes of key per site; sort space
+ * with SUBMCONV_FLAG_MORTON or SUBMCONV_FLAG_SORTED_KEYS) stays with the
+ * device after the call, up to 256 MiB, for the next build, until the
+ * process ends. Builds on one device run one at a time.
  */
 int submconv_build_map(const int32_t* coords, int64_t n, int32_t batch, const int32_t grid[3],
                        uint32_t flags, hipStream_t stream, submconv_map_t* out_map);

@@ -8,7 +8,8 @@
 // open-addressing hash table in HBM, and every site then probes its 27
 // neighbours c + d (cross-correlation, README "Correctness").
 //
-// Steps (one stream, one host wait at the end):
+// Steps (one stream; the host waits for it twice, after the counts and at
+// the end):
 //   pack     coords -> keys, range validation (error flag)
 //   insert   keys -> table, 64-bit compare-and-swap, linear probing; a key
 //            that is already present raises the duplicate flag. When every
@@ -28,6 +29,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "submconv_internal.h"
@@ -402,14 +404,67 @@ int bits_for(int64_t extent) {  // smallest b with 2^b >= extent (at least 1)
   return b;
 }
 
-// Device buffers freed on scope exit (temporaries of one build).
-struct DevBuf {
+// A build's scratch (keys, hash table, sort space, counts) stays with its
+// device after the build, up to kKeepScratch bytes, for the next build: its
+// allocation and release otherwise take about as much host time as a small
+// build's kernels. A build holds its device's lease from taking the scratch
+// to its last wait for the stream, so builds on one device take turns.
+constexpr size_t kKeepScratch = size_t{256} << 20;
+constexpr int kScratchDevices = 64;
+struct KeptScratch {
+  std::mutex mu;
   void* p = nullptr;
-  void reset() {
-    if (p) (void)hipFree(p);
-    p = nullptr;
+  size_t bytes = 0;
+};
+KeptScratch g_kept[kScratchDevices];
+
+class ScratchLease {
+ public:
+  explicit ScratchLease(int device)
+      : kept_(device >= 0 && device < kScratchDevices ? &g_kept[device] : nullptr) {
+    if (kept_) lock_ = std::unique_lock<std::mutex>(kept_->mu);
   }
-  ~DevBuf() { reset(); }
+  ScratchLease(const ScratchLease&) = delete;
+  ScratchLease& operator=(const ScratchLease&) = delete;
+  // at least `bytes` of device memory, the kept scratch when it is as large
+  hipError_t take(size_t bytes, void** out) {
+    if (kept_ && kept_->p && kept_->bytes >= bytes) {
+      p_ = kept_->p;
+      bytes_ = kept_->bytes;
+      kept_->p = nullptr;
+      kept_->bytes = 0;
+    } else {
+      if (kept_ && kept_->p) {
+        (void)hipFree(kept_->p);
+        kept_->p = nullptr;
+        kept_->bytes = 0;
+      }
+      const hipError_t e = hipMalloc(&p_, bytes);
+      if (e != hipSuccess) {
+        p_ = nullptr;
+        return e;
+      }
+      bytes_ = bytes;
+    }
+    *out = p_;
+    return hipSuccess;
+  }
+  // the stream no longer uses the scratch when this runs
+  ~ScratchLease() {
+    if (!p_) return;
+    if (kept_ && bytes_ <= kKeepScratch) {
+      kept_->p = p_;
+      kept_->bytes = bytes_;
+    } else {
+      (void)hipFree(p_);
+    }
+  }
+
+ private:
+  KeptScratch* kept_;
+  std::unique_lock<std::mutex> lock_;
+  void* p_ = nullptr;
+  size_t bytes_ = 0;
 };
 
 // Sparse map: fewer than one kGroupRows-entry group per off-centre position
@@ -604,7 +659,8 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
     }
   };
 
-  DevBuf tmp;
+  ScratchLease lease(m.device);  // released after the waits below
+  void* tmp = nullptr;
   void* mem = nullptr;
   void* ent_mem = nullptr;
   auto fail = [&](int status) {
@@ -625,8 +681,8 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   {
     Carve c;
     temps(c);
-    BUILD_CHECK(hipMalloc(&tmp.p, c.used));
-    c = Carve{static_cast<char*>(tmp.p), 0};
+    BUILD_CHECK(lease.take(c.used, &tmp));
+    c = Carve{static_cast<char*>(tmp), 0};
     temps(c);
   }
   {
@@ -744,6 +800,11 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   const bool use_wide =
       wide_cand > 0 && ((flags & SUBMCONV_FLAG_TILES_288) || sparse_map(n, m.active_pairs));
   if (!use_wide) wide = Tiles{};  // its counts and offsets go unused
+  // the wider tiles' counts run while the lists are allocated
+  if (use_wide)
+    if (const int st = count_tiles(wide_cand, wide, t.tile_tot_wide, false, false, groups_wide);
+        st != SUBMCONV_OK)
+      return st;
   {
     const size_t lists = (use_wide ? 2 : 1) * static_cast<size_t>(m.active_pairs + 1);
     BUILD_CHECK(hipMalloc(&ent_mem, sizeof(int2) * lists));
@@ -753,7 +814,6 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   if (const int st = fill_tiles(base); st != SUBMCONV_OK) return st;
   uint64_t host_groups[kTaps3] = {};
   if (use_wide) {
-    if (const int st = count_tiles(wide_cand, wide, t.tile_tot_wide, false, false, groups_wide); st != SUBMCONV_OK) return st;
     if (const int st = fill_tiles(wide); st != SUBMCONV_OK) return st;
     BUILD_CHECK(hipMemcpyAsync(host_groups, groups_wide, sizeof(host_groups), hipMemcpyDeviceToHost,
                                stream));

@@ -406,6 +406,42 @@ def test_map_key_widths(dev, grid, batch):
     assert e.value.status == -3
 
 
+@gpu
+def test_builds_from_two_threads(dev):
+    """Builds from two host threads on their own streams (they share the
+    device's kept scratch, one at a time), of different sizes, in both
+    orders: every map is the oracle's."""
+    import threading
+    sc = _sc()
+    wls = [workloads.random_small(300 + i, G=g, occ=0.2, cin=32, cout=32) for i, g in enumerate((40, 14))]
+    refs = [oc.kernel_map(w.coords, w.grid, w.batch, 3) for w in wls]
+    coords = [_to(dev, w.coords) for w in wls]
+    torch.cuda.synchronize()
+    got = {}
+    errs = []
+
+    def work(i, reps):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for r in range(reps):
+                    km = sc.build_map(coords[i], wls[i].grid, wls[i].batch, morton=bool(r & 1))
+                    got[(i, r)] = km.export().cpu().numpy()
+                    km.free()
+        except Exception as e:  # reported below
+            errs.append(repr(e))
+
+    ts = [threading.Thread(target=work, args=(i, 6)) for i in (0, 1)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not errs, errs
+    for (i, r), k in got.items():
+        np.testing.assert_array_equal(k, refs[i], err_msg=f"item {i} build {r}")
+    assert len(got) == 12
+
+
 # ----------------------------------------------------------------------------
 # the sorted-key map builder: the same map, lists and results as the hash
 # ----------------------------------------------------------------------------
