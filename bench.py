@@ -43,14 +43,14 @@ CSRC = os.path.join(ROOT, "submanifold_sparse_convolution_hash_amd", "csrc")
 # over its launches), keyed by (workload, op) and by the SHA-256 of the kernel
 # source's code (comments stripped) they were taken on. Scale factors come from a plain 512 MiB device
 # copy measured in the same runs (--calib-copy-mib 512): its FETCH_SIZE read
-# 262,161 KiB and its WRITE_SIZE 524,288 KiB for 524,288 KiB moved each way.
+# 262,176 KiB and its WRITE_SIZE 524,290 KiB for 524,288 KiB moved each way.
 # A changed kernel source makes the entry stale and the reported traffic null.
 MEASURED_TRAFFIC = {
     ("c3_128_128", "forward"): {
         "src": ["forward.hip", "map_build.hip"],  # the kernel, and the map's tile size
-        "sha256": "df2d25fdd84769cce282f1f747aad925f1b4b93478c8f1f54fde51e92fabe20f",
-        "fetch_kib": 38939.84, "write_kib": 52429.99,
-        "fetch_factor": 524288.0 / 262177.375, "write_factor": 524288.0 / 524290.5},
+        "sha256": "f0aaebe418269bc869e9fc1601560720726c3056bbe75a7527cebf8801a51888",
+        "fetch_kib": 38964.69, "write_kib": 52433.44,
+        "fetch_factor": 524288.0 / 262176.1, "write_factor": 524288.0 / 524290.3},
 }
 
 METRICS = {

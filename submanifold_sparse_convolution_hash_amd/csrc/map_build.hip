@@ -5,8 +5,9 @@
 // built once and reused; "What's in it": the indice-map cache of the sparse
 // tensor). Sites are packed injectively into one 64-bit key (the coordinate
 // packing of "Running TRELLIS.2 on a Mac (3/3)", section E), inserted into an
-// open-addressing hash table in HBM, and every site then probes its 27
-// neighbours c + d (cross-correlation, README "Correctness").
+// open-addressing hash table in HBM, and every site then finds its 27
+// neighbours c + d (cross-correlation, README "Correctness"): 13 by probing
+// the table, 13 by the symmetry of the map, and itself.
 //
 // Steps (one stream; the host waits for it twice, after the counts and at
 // the end):
@@ -16,8 +17,9 @@
 //            key fits in 32 bits a slot is one 64-bit word, key and row, so
 //            that a probe reads both with one load
 //   order    optional Morton codes + radix sort -> processing order
-//   query    27 probes per site -> nbr[27][n] (tap-major), and the entries
-//            per tap of each kTileRows-row tile
+//   query    13 probes per site -> nbr[27][n] (tap-major): taps 0..12
+//            directly, 14..26 by symmetry, 13 the site itself; and the
+//            entries per tap 0..13 of each kTileRows-row tile
 //   tiles    per tile of processing rows, the neighbours of each tap
 //            compacted into a list of {neighbour row, row in tile}
 //            (count, exclusive scan over tiles, fill)
@@ -147,46 +149,58 @@ __device__ __forceinline__ int pos_of(int k) {
   return k == kCenterTap ? 0 : (k < kCenterTap ? k + 1 : k);
 }
 
-// One workgroup per (kTileRows-row tile of processing rows, tap): thread r
-// probes the tap's neighbour of the tile's row r and writes nbr[k][t]
-// (coalesced, tap-major). The workgroups of an XCD (blockIdx % 8) take one
-// contiguous run of units, tap fastest, so that a tile's coordinates and the
-// table lines its neighbours share stay in that XCD's L2 over its 27 taps.
-// Each workgroup also writes the tile's entry count at its tap and adds it
-// to the tile's total (tile_tot zeroed before).
+// The map is symmetric: j is row i's neighbour at offset d exactly when i
+// is j's neighbour at -d, and tap 26 - k has the offset of tap k negated. So
+// the query probes only taps 0..12 (and fills the centre, 13): each found
+// pair also gives the entry of tap 26 - k at j's processing position (inv,
+// or j itself without an order), into a map whose taps 14..26 hold -1.
+//
+// One workgroup per (kTileRows-row tile of processing rows, tap 0..13):
+// thread r probes the tap's neighbour of the tile's row r and writes
+// nbr[k][t] (coalesced, tap-major). The workgroups of an XCD (blockIdx % 8)
+// take one contiguous run of units, tap fastest, so that a tile's
+// coordinates and the table lines its neighbours share stay in that XCD's
+// L2 over its taps. Each workgroup also writes the tile's entry count at
+// its tap and adds it to the tile's total (tile_tot zeroed before).
+constexpr int kQueryTaps = kCenterTap + 1;
 template <bool COMPACT>
 __global__ __launch_bounds__(kTileRows) void k_query(
-    const int32_t* __restrict__ coords, const int32_t* __restrict__ order, int64_t n, int32_t g0,
-    int32_t g1, int32_t g2, const uint64_t* __restrict__ table, const int32_t* __restrict__ tvals,
-    uint64_t mask, int32_t* __restrict__ nbr, uint16_t* __restrict__ tile_cnt,
-    int32_t* __restrict__ tile_tot, uint32_t units) {
+    const int32_t* __restrict__ coords, const int32_t* __restrict__ order,
+    const int32_t* __restrict__ inv, int64_t n, int32_t g0, int32_t g1, int32_t g2,
+    const uint64_t* __restrict__ table, const int32_t* __restrict__ tvals, uint64_t mask,
+    int32_t* __restrict__ nbr, uint16_t* __restrict__ tile_cnt, int32_t* __restrict__ tile_tot,
+    uint32_t units) {
   __shared__ int wcnt[kTileRows / 64];
   const uint32_t bid = blockIdx.x, xcd = bid & 7u, q = units >> 3, rem = units & 7u;
   const uint32_t u = xcd * q + (xcd < rem ? xcd : rem) + (bid >> 3);
-  const uint32_t tile = u / kTaps3;
-  const int k = static_cast<int>(u - tile * kTaps3);
+  const uint32_t tile = u / kQueryTaps;
+  const int k = static_cast<int>(u - tile * kQueryTaps);
   const int64_t t = static_cast<int64_t>(tile) * kTileRows + threadIdx.x;
   int32_t j = -1;
   if (t < n) {
     const int64_t i = order ? order[t] : t;
-    const int32_t b = coords[4 * i + 0];
-    const int32_t nx = coords[4 * i + 1] + (k / 9) - 1;
-    const int32_t ny = coords[4 * i + 2] + ((k / 3) % 3) - 1;
-    const int32_t nz = coords[4 * i + 3] + (k % 3) - 1;
     if (k == kCenterTap) {
       j = static_cast<int32_t>(i);
-    } else if (nx >= 0 && nx < g0 && ny >= 0 && ny < g1 && nz >= 0 && nz < g2) {
-      const uint64_t key = pack_key(b, nx, ny, nz, g0, g1, g2);
-      uint64_t h = start_slot(key, mask);
-      while (true) {
-        const uint64_t s = table[h];
-        if (s == kEmpty) break;
-        if ((COMPACT ? (s & 0xffffffffull) : s) == key) {
-          j = COMPACT ? static_cast<int32_t>(s >> 32) : tvals[h];
-          break;
+    } else {
+      const int32_t b = coords[4 * i + 0];
+      const int32_t nx = coords[4 * i + 1] + (k / 9) - 1;
+      const int32_t ny = coords[4 * i + 2] + ((k / 3) % 3) - 1;
+      const int32_t nz = coords[4 * i + 3] + (k % 3) - 1;
+      if (nx >= 0 && nx < g0 && ny >= 0 && ny < g1 && nz >= 0 && nz < g2) {
+        const uint64_t key = pack_key(b, nx, ny, nz, g0, g1, g2);
+        uint64_t h = start_slot(key, mask);
+        while (true) {
+          const uint64_t s = table[h];
+          if (s == kEmpty) break;
+          if ((COMPACT ? (s & 0xffffffffull) : s) == key) {
+            j = COMPACT ? static_cast<int32_t>(s >> 32) : tvals[h];
+            break;
+          }
+          h = (h + 1) & mask;
         }
-        h = (h + 1) & mask;
       }
+      if (j >= 0)
+        nbr[static_cast<int64_t>(kTaps3 - 1 - k) * n + (inv ? inv[j] : j)] = static_cast<int32_t>(i);
     }
     nbr[static_cast<int64_t>(k) * n + t] = j;
   }
@@ -202,14 +216,22 @@ __global__ __launch_bounds__(kTileRows) void k_query(
   }
 }
 
-// Clears a build's scratch in one launch: the hash table's slots (all ones)
-// and a run of words to zero (flags, pair count, groups, tile totals).
+// Clears a build's scratch in one launch: the hash table's slots (all ones),
+// a run of words to zero (flags, pair count, groups, tile totals) and a run
+// of map entries to -1 (the taps the query fills by symmetry).
 __global__ void k_init(uint64_t* __restrict__ table, int64_t cap, uint32_t* __restrict__ zero,
-                       int64_t n_zero) {
+                       int64_t n_zero, int32_t* __restrict__ none, int64_t n_none) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   const int64_t i0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   for (int64_t i = i0; i < cap; i += stride) table[i] = kEmpty;
   for (int64_t i = i0; i < n_zero; i += stride) zero[i] = 0u;
+  for (int64_t i = i0; i < n_none; i += stride) none[i] = -1;
+}
+
+// inv[order[t]] = t: the processing position of each row.
+__global__ void k_invert(const int32_t* __restrict__ order, int64_t n, int32_t* __restrict__ inv) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t < n) inv[order[t]] = static_cast<int32_t>(t);
 }
 
 // The sums of one tile set after its counts, in one launch with a fixed
@@ -305,12 +327,12 @@ __global__ void k_query_sorted(const int32_t* __restrict__ coords, const int32_t
   }
 }
 
-// Per tile of tr <= TR processing rows: entries per processing position
-// (wave ballots over 64-row chunks; a block has TR rounded up to 64 threads)
-// and the tile's total.
+// Per tile of tr <= TR processing rows: entries of taps k_lo..26 per
+// processing position (wave ballots over 64-row chunks; a block has TR
+// rounded up to 64 threads), added to the tile's total.
 template <int TR>
 __global__ __launch_bounds__((TR + 63) / 64 * 64) void k_tile_count(
-    const int32_t* __restrict__ nbr, int64_t n, int tr, uint16_t* __restrict__ tile_cnt,
+    const int32_t* __restrict__ nbr, int64_t n, int tr, int k_lo, uint16_t* __restrict__ tile_cnt,
     int32_t* __restrict__ tile_tot) {
   constexpr int NWV = (TR + 63) / 64;
   __shared__ int cnt[NWV][kTaps3];
@@ -318,12 +340,12 @@ __global__ __launch_bounds__((TR + 63) / 64 * 64) void k_tile_count(
   const int w = threadIdx.x >> 6;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * tr + threadIdx.x;
   const bool valid = static_cast<int>(threadIdx.x) < tr && t < n;
-  for (int k = 0; k < kTaps3; ++k) {
+  for (int k = k_lo; k < kTaps3; ++k) {
     const uint64_t m = __ballot(valid && nbr[static_cast<int64_t>(k) * n + t] >= 0);
     if (lane == 0) cnt[w][k] = __popcll(m);
   }
   __syncthreads();
-  if (threadIdx.x < kTaps3) {
+  if (threadIdx.x < kTaps3 && tap_at(threadIdx.x) >= k_lo) {
     const int k = tap_at(threadIdx.x);
     int c = 0;
     for (int ww = 0; ww < NWV; ++ww) c += cnt[ww][k];
@@ -331,9 +353,9 @@ __global__ __launch_bounds__((TR + 63) / 64 * 64) void k_tile_count(
   }
   if (threadIdx.x == 0) {
     int tot = 0;
-    for (int k = 0; k < kTaps3; ++k)
+    for (int k = k_lo; k < kTaps3; ++k)
       for (int ww = 0; ww < NWV; ++ww) tot += cnt[ww][k];
-    tile_tot[blockIdx.x] = tot;
+    atomicAdd(tile_tot + blockIdx.x, tot);
   }
 }
 
@@ -619,7 +641,7 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   // the build's temporaries, in one allocation freed on return
   struct Temps {
     uint64_t *keys, *tkeys, *skeys, *mcode_in, *mcode_out;
-    int32_t *tvals, *srows, *rows_in, *midx, *tile_tot, *tile_tot_wide;
+    int32_t *tvals, *srows, *rows_in, *midx, *inv, *tile_tot, *tile_tot_wide;
     void *small, *ksort, *msort;
   } t{};
   auto temps = [&](Carve& c) {
@@ -637,6 +659,7 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
       t.mcode_in = c.take<uint64_t>(n);
       t.mcode_out = c.take<uint64_t>(n);
       t.midx = c.take<int32_t>(n);
+      if (!sorted_keys) t.inv = c.take<int32_t>(n);
       t.msort = c.take<char>(msort_bytes);
     }
     // zeroed together, at the end: flags and sums, and the tile totals
@@ -700,9 +723,11 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
     const int64_t n_table = sorted_keys ? 0 : cap;
     const int64_t n_zero =
         (reinterpret_cast<char*>(t.tile_tot_wide + nt_wide + 1) - static_cast<char*>(t.small)) / 4;
-    const int64_t most = std::max(n_table, n_zero);
+    // the hash query fills taps 14..26 by symmetry
+    const int64_t n_none = sorted_keys ? 0 : (kTaps3 - kQueryTaps) * n;
+    const int64_t most = std::max(n_table, std::max(n_zero, n_none));
     k_init<<<static_cast<unsigned>(std::min<int64_t>((most + B - 1) / B, 2048)), B, 0, stream>>>(
-        t.tkeys, n_table, static_cast<uint32_t*>(t.small), n_zero);
+        t.tkeys, n_table, static_cast<uint32_t*>(t.small), n_zero, nbr + kQueryTaps * n, n_none);
     BUILD_CHECK(hipGetLastError());
   }
   k_pack<<<grid_for(n, B), B, 0, stream>>>(coords, n, batch, grid[0], grid[1], grid[2], t.keys, err,
@@ -723,24 +748,29 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
     k_insert<false><<<grid_for(n, B), B, 0, stream>>>(t.keys, n, t.tkeys, t.tvals, mask, err);
   }
   BUILD_CHECK(hipGetLastError());
-  if (morton)
+  if (morton) {
     BUILD_CHECK(rocprim::radix_sort_pairs(t.msort, msort_bytes,
                                           static_cast<const uint64_t*>(t.mcode_in), t.mcode_out,
                                           static_cast<const int32_t*>(t.midx), order,
                                           static_cast<size_t>(n), 0u, end_bit, stream));
+    if (!sorted_keys) {
+      k_invert<<<grid_for(n, B), B, 0, stream>>>(order, n, t.inv);
+      BUILD_CHECK(hipGetLastError());
+    }
+  }
   if (sorted_keys) {
     k_query_sorted<<<grid_for(n * kTaps3, B), B, 0, stream>>>(coords, order, n, grid[0], grid[1],
                                                               grid[2], t.skeys, t.srows, nbr);
   } else {
-    // the query also counts the 256-row tiles' entries
-    const uint32_t units = static_cast<uint32_t>(nt_base * kTaps3);
+    // the query also counts the 256-row tiles' entries of taps 0..13
+    const uint32_t units = static_cast<uint32_t>(nt_base * kQueryTaps);
     if (compact)
-      k_query<true><<<units, kTileRows, 0, stream>>>(coords, order, n, grid[0], grid[1], grid[2],
-                                                     t.tkeys, nullptr, mask, nbr, base.cnt,
+      k_query<true><<<units, kTileRows, 0, stream>>>(coords, order, t.inv, n, grid[0], grid[1],
+                                                     grid[2], t.tkeys, nullptr, mask, nbr, base.cnt,
                                                      t.tile_tot, units);
     else
-      k_query<false><<<units, kTileRows, 0, stream>>>(coords, order, n, grid[0], grid[1], grid[2],
-                                                      t.tkeys, t.tvals, mask, nbr, base.cnt,
+      k_query<false><<<units, kTileRows, 0, stream>>>(coords, order, t.inv, n, grid[0], grid[1],
+                                                      grid[2], t.tkeys, t.tvals, mask, nbr, base.cnt,
                                                       t.tile_tot, units);
   }
   BUILD_CHECK(hipGetLastError());
@@ -750,20 +780,19 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   // active pairs (the same for every tile size)
   unsigned long long* groups_wide =
       reinterpret_cast<unsigned long long*>(static_cast<char*>(t.small) + 256);
-  auto count_tiles = [&](int tr, Tiles& T, int32_t* tot, bool counted, bool total,
+  // (the hash query counts taps 0..13 of the 256-row tiles itself: k_lo)
+  auto count_tiles = [&](int tr, Tiles& T, int32_t* tot, int k_lo, bool total,
                          unsigned long long* groups) -> int {
     const int64_t n_tiles = (n + tr - 1) / tr;
     T.rows = tr;
     T.n = n_tiles;
-    if (!counted) {  // (the hash query counts the 256-row tiles itself)
-      if (tr > kTileRows)
-        k_tile_count<kTileRowsWide><<<static_cast<unsigned>(n_tiles), (kTileRowsWide + 63) / 64 * 64,
-                                      0, stream>>>(nbr, n, tr, T.cnt, tot);
-      else
-        k_tile_count<kTileRows><<<static_cast<unsigned>(n_tiles), kTileRows, 0, stream>>>(
-            nbr, n, tr, T.cnt, tot);
-      BUILD_CHECK(hipGetLastError());
-    }
+    if (tr > kTileRows)
+      k_tile_count<kTileRowsWide><<<static_cast<unsigned>(n_tiles), (kTileRowsWide + 63) / 64 * 64,
+                                    0, stream>>>(nbr, n, tr, k_lo, T.cnt, tot);
+    else
+      k_tile_count<kTileRows><<<static_cast<unsigned>(n_tiles), kTileRows, 0, stream>>>(
+          nbr, n, tr, k_lo, T.cnt, tot);
+    BUILD_CHECK(hipGetLastError());
     k_tile_sums<<<kTaps3 + 1, 1024, 0, stream>>>(tot, T.cnt, n_tiles, T.off, total ? pairs : nullptr,
                                                  groups);
     BUILD_CHECK(hipGetLastError());
@@ -782,7 +811,7 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   };
   // the one host wait before the lists: flags, active pairs, groups
   uint64_t host_small[2 + kTaps3] = {};
-  if (const int st = count_tiles(kTileRows, base, t.tile_tot, !sorted_keys, true, pairs + 1); st != SUBMCONV_OK)
+  if (const int st = count_tiles(kTileRows, base, t.tile_tot, sorted_keys ? 0 : kQueryTaps, true, pairs + 1); st != SUBMCONV_OK)
     return st;
   BUILD_CHECK(hipMemcpyAsync(host_small, t.small, sizeof(host_small), hipMemcpyDeviceToHost, stream));
   BUILD_CHECK(hipStreamSynchronize(stream));
@@ -802,7 +831,7 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   if (!use_wide) wide = Tiles{};  // its counts and offsets go unused
   // the wider tiles' counts run while the lists are allocated
   if (use_wide)
-    if (const int st = count_tiles(wide_cand, wide, t.tile_tot_wide, false, false, groups_wide);
+    if (const int st = count_tiles(wide_cand, wide, t.tile_tot_wide, 0, false, groups_wide);
         st != SUBMCONV_OK)
       return st;
   {
