@@ -106,12 +106,11 @@ __global__ void k_iota(int32_t* __restrict__ v, int64_t n) {
   if (i < n) v[i] = static_cast<int32_t>(i);
 }
 
-// First slot of a key: 8 consecutive keys (consecutive z of one line when
-// the z extent is a multiple of 8) share an aligned run of 8 slots, and the
-// runs scatter. A site's neighbours at z-1, z, z+1 then mostly share a cache
-// line of the table.
+// First slot of a key: the mixed key, so that the sites of dense surfaces,
+// runs of consecutive keys, do not pile up into long probe runs (keeping 8
+// consecutive keys in one run of slots measured 1.4x slower on such maps).
 __device__ __forceinline__ uint64_t start_slot(uint64_t key, uint64_t mask) {
-  return ((mix64(key >> 3) << 3) | (key & 7ull)) & mask;
+  return mix64(key) & mask;
 }
 
 // COMPACT: a slot is the key (below 2^32) in the low half and the row in the

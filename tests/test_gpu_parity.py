@@ -371,7 +371,7 @@ def _blob_sites(rng, grid, batch, corners, side=10, occ=0.35):
     ((2048, 2048, 1024), 1),  # batch x volume = 2^32: one-word slots, top key 2^32 - 1
     ((2048, 2048, 1024), 2),  # 2^33: keys and rows in two arrays
     ((4096, 4096, 4096), 1),  # 2^36
-    ((100, 3000, 7), 3),      # z extent not a multiple of 8
+    ((100, 3000, 7), 3),      # odd extents, a z extent below the blocks
 ])
 def test_map_key_widths(dev, grid, batch):
     """The hash table's two slot layouts (packed keys below 2^32, or wider)
