@@ -276,11 +276,14 @@ __global__ __launch_bounds__((CfgPP<CIN, COUT_T, K3, GR_, M_>::NT)) void k_fwd_p
   // row in the tile for a 1x1x1 kernel), processed from step gs on (the
   // centre in NCG steps, then each position in steps of GR entries). Lane 27
   // is an empty position at step F, where the unit's steps end; the unit
-  // takes Fp steps (F rounded up to a multiple of 4, and to at least the
-  // centre's steps rounded up), so that step residues mod 4 carry over to the
-  // next unit. Lanes 28..31 start at
-  // no step. wb is the byte offset of the position's weights for the
-  // unit's column tile.
+  // takes Fp steps: F rounded up to a multiple of 4, so that step residues
+  // mod 4 carry over to the next unit, and to at least the centre's steps
+  // rounded up and kMinSteps. The pipeline looks LB + LE steps ahead, and the
+  // schedule holds two units: a unit's last steps must not look past the
+  // next one, even when that one is all centre (64-row groups take the centre
+  // in 4 steps). Lanes 28..31 start at no step. wb is the byte offset of the
+  // position's weights for the unit's column tile.
+  constexpr int kMinSteps = (LB + LE + 3) & ~3;
   struct Half {
     int cnt, off, gs, wb;  // per lane
     int F, Fp, c0, rows_here, pass;
@@ -297,7 +300,7 @@ __global__ __launch_bounds__((CfgPP<CIN, COUT_T, K3, GR_, M_>::NT)) void k_fwd_p
     const int ng = (lane >= 1 && lane < kTaps3) ? (hf.cnt + GR - 1) / GR : 0;
     const int gs = NCG + excl_scan_wave(ng, lane);
     hf.F = live ? __builtin_amdgcn_readlane(gs, kTaps3) : 0;
-    hf.Fp = live ? NCG + BR + ((max(hf.F - NCG - BR, 0) + 3) & ~3) : 0;
+    hf.Fp = live ? max(NCG + BR + ((max(hf.F - NCG - BR, 0) + 3) & ~3), kMinSteps) : 0;
     hf.gs = lane == 0 ? 0 : (lane <= kTaps3 ? gs : INT_MAX);
     hf.wb = (((K3 ? tap_at(lane & 31) * (cout / 32) : 0) + r.ct * (COUT_T / 32)) * KST +
              r.pass * KS) * 1024;
