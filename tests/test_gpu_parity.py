@@ -407,20 +407,24 @@ def test_map_key_widths(dev, grid, batch):
 
 
 @gpu
-@pytest.mark.parametrize("cin,cout", [(64, 64), (128, 128)])
-def test_dense_map_with_isolated_tiles(dev, cin, cout):
-    """A dense map (64-row groups) whose row order puts 64 tiles of isolated
-    sites (no neighbour: only the centre's steps) between dense ones, in a map
-    large enough that the workgroups walk several units: every unit's lookahead
-    must reach past such a short unit into the next one. The first 128 rows
-    of each tile of the first XCD's run are checked against the oracle."""
+@pytest.mark.parametrize("cin,cout,side,iso0,n_iso,checked", [
+    (64, 64, 75, 64, 64, 128),
+    (128, 128, 75, 64, 64, 128),
+    (256, 256, 46, 16, 16, 64),  # two 128-channel passes per unit
+])
+def test_dense_map_with_isolated_tiles(dev, cin, cout, side, iso0, n_iso, checked):
+    """A dense map (64-row groups) whose row order puts n_iso tiles of
+    isolated sites (no neighbour: only the centre's steps) after iso0 dense
+    tiles, in a map large enough that the workgroups walk several units: every
+    unit's lookahead must reach past such a short unit into the next one. The
+    first `checked` rows of each tile of the first XCD's run are compared with
+    the oracle."""
     sc = _sc()
     rng = np.random.default_rng(cin + cout)
     G = 160
-    side = 75
     dense = np.argwhere(np.ones((side, side, side), dtype=bool)).astype(np.int32)  # raster order
-    iso = (np.argwhere(np.ones((26, 26, 26), dtype=bool)) * 2 + 100).astype(np.int32)[:64 * 256]
-    xyz = np.concatenate([dense[:64 * 256], iso, dense[64 * 256:]])
+    iso = (np.argwhere(np.ones((26, 26, 26), dtype=bool)) * 2 + 100).astype(np.int32)[:n_iso * 256]
+    xyz = np.concatenate([dense[:iso0 * 256], iso, dense[iso0 * 256:]])
     coords = np.ascontiguousarray(np.concatenate([np.zeros((len(xyz), 1), np.int32), xyz], axis=1))
     n = len(coords)
     n_tiles = (n + 255) // 256
@@ -432,13 +436,13 @@ def test_dense_map_with_isolated_tiles(dev, cin, cout):
     assert km.tile_rows == 256  # dense: no wider tiles
     out = sc.forward(km, _to(dev, feats), _to(dev, W), None).float().cpu().numpy()
     kmap = km.export().cpu().numpy()
-    assert (kmap[64 * 256:128 * 256] >= 0).sum() == 64 * 256  # the isolated rows see only themselves
-    rows = (np.arange(per_xcd)[:, None] * 256 + np.arange(128)[None, :]).reshape(-1)
+    # the isolated rows see only themselves
+    assert (kmap[iso0 * 256:(iso0 + n_iso) * 256] >= 0).sum() == n_iso * 256
+    rows = (np.arange(per_xcd)[:, None] * 256 + np.arange(checked)[None, :]).reshape(-1)
     rows = rows[rows < n]
     ref = oc.submconv_rows(kmap, feats, W, None, rows)
     _assert_close(out[rows], ref, "rows after short units")
     km.free()
-
 
 @gpu
 def test_builds_from_two_threads(dev):
