@@ -226,3 +226,32 @@ def test_backward_bias(dev, n, cout):
     scale = np.abs(g.astype(np.float64)).sum(0)
     _assert_close(got, ref, "bias grad", atol=1e-5, rtol=1e-5, extra=1e-6 * scale)
     np.testing.assert_array_equal(got, sc.backward_bias(_to(dev, g)).cpu().numpy())
+
+
+@gpu
+@pytest.mark.parametrize("cin,cout", [(64, 64), (128, 128)])
+def test_backward_dense_map_with_isolated_tiles(dev, cin, cout):
+    """Input and weight gradients on a dense map (64-row groups) with 16 tiles
+    of isolated sites between dense ones: units and positions with no
+    off-centre entries inside the walks and windows."""
+    sc = _sc()
+    rng = np.random.default_rng(cin * 3 + cout)
+    G, side, iso0, n_iso = 128, 32, 24, 16
+    dense = np.argwhere(np.ones((side, side, side), dtype=bool)).astype(np.int32)
+    iso = (np.argwhere(np.ones((20, 20, 20), dtype=bool)) * 2 + 70).astype(np.int32)[:n_iso * 256]
+    xyz = np.concatenate([dense[:iso0 * 256], iso, dense[iso0 * 256:]])
+    coords = np.ascontiguousarray(np.concatenate([np.zeros((len(xyz), 1), np.int32), xyz], axis=1))
+    n = len(coords)
+    _say(f"[backward isolated tiles] {cin}->{cout} N={n}")
+    feats = rng.standard_normal((n, cin)).astype(np.float16)
+    g = rng.standard_normal((n, cout)).astype(np.float16)
+    W = (rng.standard_normal((27, cin, cout)) / np.sqrt(27 * cin)).astype(np.float16)
+    km = sc.build_map(_to(dev, coords), (G, G, G), 1)
+    gd = _to(dev, g)
+    dx = sc.backward_input(km, gd, _to(dev, W)).cpu().numpy()
+    rows = np.arange(0, n, 3)
+    ref = oc.backward_input_rows(coords, (G, G, G), 1, 3, g, W, rows)
+    _assert_close(dx[rows], ref, "input grad")
+    dw = sc.backward_weight(km, _to(dev, feats), gd, 3).cpu().numpy()
+    _check_weight_grad(dw, km.export().cpu().numpy(), feats, g, "weight grad")
+    km.free()
