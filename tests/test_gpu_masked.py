@@ -87,3 +87,29 @@ def test_masked_shapes_and_errors(dev):
     assert ex.value.status == -4
     plan.free()
     km.free()
+
+
+@gpu
+@pytest.mark.parametrize("cin,cout", [(64, 64), (128, 128)])
+def test_masked_dense_map_with_isolated_tiles(dev, cin, cout):
+    """The masked variant on a dense block with tiles of isolated sites (mask:
+    the centre only) between its rows: sampled rows of both kinds."""
+    sc = _sc()
+    rng = np.random.default_rng(cin + 5 * cout)
+    G, side, iso0, n_iso = 128, 32, 24, 16
+    dense = np.argwhere(np.ones((side, side, side), dtype=bool)).astype(np.int32)
+    iso = (np.argwhere(np.ones((20, 20, 20), dtype=bool)) * 2 + 70).astype(np.int32)[:n_iso * 256]
+    xyz = np.concatenate([dense[:iso0 * 256], iso, dense[iso0 * 256:]])
+    coords = np.ascontiguousarray(np.concatenate([np.zeros((len(xyz), 1), np.int32), xyz], axis=1))
+    n = len(coords)
+    feats = rng.standard_normal((n, cin)).astype(np.float16)
+    W = (rng.standard_normal((27, cin, cout)) / np.sqrt(27 * cin)).astype(np.float16)
+    bias = (rng.standard_normal(cout) * 0.1).astype(np.float32)
+    km = sc.build_map(_to(dev, coords), (G, G, G), 1)
+    plan = sc.masked_plan(km)
+    out = sc.forward_masked(plan, _to(dev, feats), _to(dev, W), _to(dev, bias)).float().cpu().numpy()
+    rows = np.concatenate([np.arange(iso0 * 256 - 300, (iso0 + n_iso) * 256 + 300, 7),
+                           rng.choice(n, 1500, replace=False)])
+    ref = oc.submconv_rows(km.export().cpu().numpy(), feats, W, bias, rows)
+    _assert_close(out[rows], ref, "masked, isolated tiles")
+    km.free()
