@@ -445,6 +445,24 @@ def test_dense_map_with_isolated_tiles(dev, cin, cout, side, iso0, n_iso, checke
     km.free()
 
 @gpu
+def test_builds_reuse_the_kept_scratch(dev):
+    """Builds of alternating sizes and builders in one process: each reuses
+    (or regrows) the device's kept scratch, left holding the previous build's
+    table, keys and counts, and still gives the oracle's map."""
+    sc = _sc()
+    wls = [workloads.random_small(400 + i, G=g, occ=o, cin=8, cout=8)
+           for i, (g, o) in enumerate([(48, 0.3), (10, 0.5), (64, 0.1), (6, 0.9), (48, 0.3)])]
+    for i, w in enumerate(wls):
+        ref = oc.kernel_map(w.coords, w.grid, w.batch, 3)
+        for morton, sk in [(False, False), (True, False), (False, True), (True, True)]:
+            km = sc.build_map(_to(dev, w.coords), w.grid, w.batch, morton=morton, sorted_keys=sk)
+            np.testing.assert_array_equal(km.export().cpu().numpy(), ref,
+                                          err_msg=f"build {i} morton={morton} sorted={sk}")
+            assert km.active_pairs(3) == int((ref >= 0).sum())
+            km.free()
+
+
+@gpu
 def test_builds_from_two_threads(dev):
     """Builds from two host threads on their own streams (they share the
     device's kept scratch, one at a time), of different sizes, in both
