@@ -476,14 +476,15 @@ __global__ __launch_bounds__((PCfg<CIN, COUT>::NT)) void k_bwd_weight_pp(
 
 // dW[tap_at(kp)] = the sum of the partials of position kp's blocks. A
 // workgroup takes 64 float4s of one position; thread (s, c) adds the
-// position's runs s, s+4, s+8, ... for float4 c in order, then thread
-// (0, c) adds the four sums in order: a fixed order, so the result does not
-// depend on scheduling.
-__global__ __launch_bounds__(256) void k_bwd_weight_reduce_pp(const float* __restrict__ partial,
-                                                              const WSplit ws, int cin, int cout,
-                                                              float* __restrict__ dw) {
+// position's runs s, s+kRedStrands, ... for float4 c in order, then thread
+// (0, c) adds the strands' sums in order: a fixed order, so the result does
+// not depend on scheduling. (The centre has a run per few tiles, over a
+// hundred at 128^3: its strands are the reduction's long pole.)
+constexpr int kRedStrands = 16;
+__global__ __launch_bounds__(64 * kRedStrands) void k_bwd_weight_reduce_pp(
+    const float* __restrict__ partial, const WSplit ws, int cin, int cout, float* __restrict__ dw) {
   typedef float f4 __attribute__((ext_vector_type(4)));
-  __shared__ f4 part[4][64];
+  __shared__ f4 part[kRedStrands][64];
   const int64_t per4 = static_cast<int64_t>(cin) * cout / 4;
   const int64_t chunks = (per4 + 63) / 64;
   const int kp = static_cast<int>(blockIdx.x / chunks);
@@ -493,14 +494,15 @@ __global__ __launch_bounds__(256) void k_bwd_weight_reduce_pp(const float* __res
   f4 acc = {0.f, 0.f, 0.f, 0.f};
   if (c4 < per4) {
     const int n = ws.count(kp), first = ws.first(kp), stride = ws.stride(kp);
-    for (int r = s; r < n; r += 4)
+    for (int r = s; r < n; r += kRedStrands)
       acc += p4[static_cast<int64_t>(first + r * stride) * per4 + c4];
   }
   part[s][threadIdx.x & 63] = acc;
   __syncthreads();
   if (s == 0 && c4 < per4) {
-    const f4 t = ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) +
-                 part[3][threadIdx.x];
+    f4 t = part[0][threadIdx.x];
+#pragma unroll
+    for (int q = 1; q < kRedStrands; ++q) t += part[q][threadIdx.x];
     const int k = ws.np == kTaps3 ? tap_at(kp) : 0;
     reinterpret_cast<f4*>(dw)[k * per4 + c4] = t;
   }
@@ -671,7 +673,7 @@ int launch_w(const Map& m, int K, const _Float16* feats, const _Float16* grad_ou
           T.ent, T.off, T.cnt, m.order, m.n, nt, T.rows, ws, feats, grad_out, partial, np);
     SUBMCONV_HIP_CHECK(hipGetLastError());
     const int64_t chunks = (int64_t{CIN} * COUT / 4 + 63) / 64;
-    k_bwd_weight_reduce_pp<<<static_cast<unsigned>(ws.np * chunks), 256, 0, stream>>>(
+    k_bwd_weight_reduce_pp<<<static_cast<unsigned>(ws.np * chunks), 64 * kRedStrands, 0, stream>>>(
         partial, ws, CIN, COUT, dw);
   } else {
     const Runs r = runs_for(m, K);
