@@ -5,16 +5,25 @@ occupancy), Cin = Cout = 128, fp16 features and weights, fp32 accumulation,
 no bias; the kernel map is built once and reused (warm cache), as in the
 "Performance" table of the trellis_sparse_mlx README.
 
-A step is one layer: weight preparation + the fused gather-GEMM forward,
-inputs resident in HBM. Effective TFLOP/s = 2 * active_pairs * Cin * Cout /
-time. The JSON line also carries the roofline of the dominant kernel (an
-event pair around each of its launches on the launch stream, averaged), the
-kernel-map build time, and the CPU oracle (C twin, all host threads) timed on
-the same workload.
+A step is one layer through the C ABI's submconv_forward on the layer's own
+weights W [27,128,128] (the call rearranges W into the MFMA fragment order,
+then runs the fused gather-GEMM), inputs resident in HBM. Effective TFLOP/s =
+2 * active_pairs * Cin * Cout / time. The JSON line also carries:
+  * the roofline of the dominant kernel: the forward on prepared weights
+    (submconv_forward_prepared), launched back to back inside one event pair
+    on the launch stream, as the steps are timed; its algorithmic bytes are
+    the structures it reads and writes (features, output, the per-tile lists
+    and counts, weights);
+  * measured ceilings from the same process: a 512 MiB device copy's GB/s and
+    a dense fp16 GEMM's TFLOP/s (torch.matmul), with the kernel's fractions
+    of both;
+  * the kernel-map build time, the CPU oracle (C twin, all host threads, the
+    host CPU's model) timed on the same workload, and for context the pages'
+    own figures for this workload (other hardware: not a target).
 
 With --op backward_input or backward_weight the same workload times the
-layer's input gradient (weight preparation + the forward with the flipped,
-transposed kernel on the same map) or weight gradient (the MFMA pair
+layer's input gradient (submconv_backward_input on W: the forward with the
+flipped, transposed kernel on the same map) or weight gradient (the MFMA pair
 contraction + the fixed-order reduction of its partials), each with its own
 roofline and oracle baseline. --op downsample / subdivide time the x2
 coordinate operations on the workload's sites and first-layer features
@@ -45,13 +54,7 @@ CSRC = os.path.join(ROOT, "submanifold_sparse_convolution_hash_amd", "csrc")
 # copy measured in the same runs (--calib-copy-mib 512): its FETCH_SIZE read
 # 262,176 KiB and its WRITE_SIZE 524,290 KiB for 524,288 KiB moved each way.
 # A changed kernel source makes the entry stale and the reported traffic null.
-MEASURED_TRAFFIC = {
-    ("c3_128_128", "forward"): {
-        "src": ["forward.hip", "map_build.hip"],  # the kernel, and the map's tile size
-        "sha256": "1602707a7836c8e33b9bed0fc07164d7c4780c9a999e1c9c157019fa10893db7",
-        "fetch_kib": 38968.30, "write_kib": 52431.88,
-        "fetch_factor": 524288.0 / 262176.1, "write_factor": 524288.0 / 524290.3},
-}
+MEASURED_TRAFFIC = {}
 
 METRICS = {
     "forward": "SubMConv3d ms/layer + effective TFLOP/s (128^3 grid, C=128, 10% occ)",
@@ -66,16 +69,20 @@ KERNELS = {"forward": "k_fwd_pp", "backward_input": "k_fwd_pp", "backward_weight
            "downsample": "k_down_max", "subdivide": "k_subdivide"}
 
 
-def algorithmic_bytes(op, n, cin, cout, ksize, has_order, has_bias):
-    """Compulsory HBM bytes of one launch of the op: its row inputs read once,
-    its output written once, the tap-major map read once (ksize 3) with the
-    processing order, the weights (fp16 in, or the fp32 weight gradient out)
-    and the bias."""
+def algorithmic_bytes(op, n, cin, cout, ksize, has_order, has_bias, pairs, tile_rows):
+    """Compulsory HBM bytes of one launch of the op's dominant kernel: its row
+    inputs read once and its output written once; for a 3x3x3 forward (or
+    input gradient) the per-tile lists it streams (8 bytes per active pair,
+    plus the terminating entry) with the tiles' counts (27 x 2 bytes) and
+    offsets (4 bytes), for the weight gradient the same lists; the processing
+    order when there is one; the weights (fp16 in, or the fp32 weight
+    gradient out) and the bias."""
     K = 27 if ksize == 3 else 1
     b = n * cin * 2 + n * cout * 2
     b += K * cin * cout * (4 if op == "backward_weight" else 2)
     if ksize == 3:
-        b += 27 * n * 4
+        n_tiles = -(-n // tile_rows)
+        b += (pairs + 1) * 8 + n_tiles * (27 * 2 + 4) + 4
         if has_order:
             b += n * 4
     if has_bias and op in ("forward", "forward_masked"):
@@ -119,6 +126,53 @@ def _time(fn, steps, warmup, torch):
         b.record()
     torch.cuda.synchronize()
     return sum(a.elapsed_time(b) for a, b in evs) / steps * 1e3  # us
+
+
+def measured_ceilings(torch, dev):
+    """Achievable ceilings measured in this process: a 512 MiB device copy
+    (GB/s counting the bytes read and written) and a dense fp16 GEMM,
+    torch.matmul 8192^3 on the vendor library (TFLOP/s), each the best of
+    three back-to-back batches."""
+    nb = 512 * 1024 * 1024
+    a = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+
+    def best(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / reps * 1e-3)
+        return min(ts)
+
+    copy_s = best(lambda: b.copy_(a), 10)
+    del a, b
+    m = 8192
+    x = torch.randn((m, m), device=dev).to(torch.float16)
+    y = torch.randn((m, m), device=dev).to(torch.float16)
+    gemm_s = best(lambda: torch.matmul(x, y), 10)
+    del x, y
+    return {"copy_gbs": round(2 * nb / copy_s / 1e9, 1),
+            "gemm_f16_tflops": round(2.0 * m ** 3 / gemm_s / 1e12, 1),
+            "how": "512 MiB device copy (read + write bytes); torch.matmul fp16 8192^3; best of 3x10"}
+
+
+def cpu_model():
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def python_oracle_times():
@@ -293,74 +347,90 @@ def main():
     pairs = km.active_pairs(L.ksize)
     flops = 2.0 * pairs * L.cin * L.cout
 
+    # Steps and kernels call the C ABI directly (ctypes, arguments built
+    # once): the Python binding's checks would add host time to every launch.
+    import ctypes
+    lib = sc.load_library()
+    st = sc._stream(dev)
+    P = ctypes.c_void_p
+    dt = sc._DTYPES[feats.dtype]
     if op == "forward":
         out = torch.empty((wl.n, L.cout), dtype=feats.dtype, device=dev)
         wp = sc.prepare_weights(W)
+        a_step = (km.handle, P(feats.data_ptr()), P(W.data_ptr()), sc._ptr(bias),
+                  P(out.data_ptr()), L.cin, L.cout, L.ksize, dt, st)
+        a_kern = (km.handle, P(feats.data_ptr()), wp.handle, sc._ptr(bias), P(out.data_ptr()), st)
 
         def step():
-            sc.forward(km, feats, bias=bias, prepared=sc.prepare_weights(W), ksize=L.ksize,
-                       cout=L.cout, out=out)
+            sc._check(lib.submconv_forward_dtype(*a_step))
 
         def kernel():
-            sc.forward(km, feats, bias=bias, prepared=wp, ksize=L.ksize, cout=L.cout, out=out)
+            sc._check(lib.submconv_forward_prepared(*a_kern))
     elif op == "backward_input":
         out = torch.empty((wl.n, L.cin), dtype=feats.dtype, device=dev)
         wp = sc.prepare_weights(W, input_grad=True)
+        a_step = (km.handle, P(grad_out.data_ptr()), P(W.data_ptr()), P(out.data_ptr()), L.cin,
+                  L.cout, L.ksize, dt, st)
+        a_kern = (km.handle, P(grad_out.data_ptr()), wp.handle, P(out.data_ptr()), st)
 
         def step():
-            sc.backward_input(km, grad_out, prepared=sc.prepare_weights(W, input_grad=True),
-                              ksize=L.ksize, cin=L.cin, out=out)
+            sc._check(lib.submconv_backward_input_dtype(*a_step))
 
         def kernel():
-            sc.backward_input(km, grad_out, prepared=wp, ksize=L.ksize, cin=L.cin, out=out)
+            sc._check(lib.submconv_backward_input_prepared(*a_kern))
     elif op == "forward_masked":
         out = torch.empty((wl.n, L.cout), dtype=torch.float16, device=dev)
         wp = sc.prepare_weights(W)
         mplan = sc.masked_plan(km)
         print(f"[bench] masked plan: {mplan.row_taps} row-taps executed for {pairs} pairs "
               f"({mplan.row_taps / pairs:.2f}x)", file=sys.stderr, flush=True)
+        a_kern = (mplan.handle, P(feats.data_ptr()), wp.handle, sc._ptr(bias), P(out.data_ptr()), st)
 
         def step():
-            sc.forward_masked(mplan, feats, bias=bias, prepared=sc.prepare_weights(W), cout=L.cout, out=out)
+            wp.set(W)
+            sc._check(lib.submconv_forward_masked(*a_kern))
 
         def kernel():
-            sc.forward_masked(mplan, feats, bias=bias, prepared=wp, cout=L.cout, out=out)
+            sc._check(lib.submconv_forward_masked(*a_kern))
     else:
         out = torch.empty((27 if L.ksize == 3 else 1, L.cin, L.cout), dtype=torch.float32, device=dev)
+        ws = int(lib.submconv_backward_weight_workspace_bytes(km.handle, L.cin, L.cout, L.ksize))
+        work = torch.empty((max(ws, 1),), dtype=torch.uint8, device=dev)
+        a_kern = (km.handle, P(feats.data_ptr()), P(grad_out.data_ptr()), P(out.data_ptr()),
+                  P(work.data_ptr()), L.cin, L.cout, L.ksize, st)
 
         def step():
-            sc.backward_weight(km, feats, grad_out, L.ksize, out=out)
+            sc._check(lib.submconv_backward_weight(*a_kern))
 
         kernel = step
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t) * 1e3 / args.steps
-    ms_step = e0.elapsed_time(e1) / args.steps
-    print(f"[bench] step {ms_step * 1e3:.1f} us (wall {wall_ms * 1e3:.1f} us)", file=sys.stderr, flush=True)
+    def timed(fn, steps):
+        """Average µs of `steps` back-to-back calls inside one event pair on
+        the launch stream (torch's current stream), after a synchronisation."""
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps * 1e3
 
-    # the op's kernels alone: an event pair around every launch, on the
-    # stream the binding launches on (torch's current stream), averaged
+    for _ in range(args.warmup):
+        step()
+    t = time.perf_counter()
+    step_us = timed(step, args.steps)
+    wall_ms = (time.perf_counter() - t) * 1e3 / args.steps
+    ms_step = step_us / 1e3
+    print(f"[bench] step {step_us:.1f} us (wall {wall_ms * 1e3:.1f} us)", file=sys.stderr, flush=True)
+
+    # the op's dominant kernel alone, timed as the steps are: back to back in
+    # one event pair
     for _ in range(args.warmup):
         kernel()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for a, b in evs:
-        a.record()
-        kernel()
-        b.record()
-    torch.cuda.synchronize()
-    k_us = sum(a.elapsed_time(b) for a, b in evs) / args.steps * 1e3
-    alg_bytes = algorithmic_bytes(op, wl.n, L.cin, L.cout, L.ksize, args.morton, bias is not None)
+    k_us = timed(kernel, args.steps)
+    alg_bytes = algorithmic_bytes(op, wl.n, L.cin, L.cout, L.ksize, args.morton, bias is not None,
+                                  pairs, km.tile_rows)
     achieved_gbs = alg_bytes / (k_us * 1e-6) / 1e9
     print(f"[bench] {op} kernels {k_us:.1f} us, {achieved_gbs:.0f} GB/s algorithmic", file=sys.stderr, flush=True)
 
@@ -389,6 +459,7 @@ def main():
               f"{n_cold})", file=sys.stderr, flush=True)
 
     if args.calib_copy_mib > 0:
+        # one plain device copy of known size, for scaling the HBM counters
         nb = args.calib_copy_mib * 1024 * 1024
         a = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
         b = torch.empty_like(a)
@@ -396,6 +467,10 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
+
+    ceil = measured_ceilings(torch, dev)
+    print(f"[bench] ceilings: copy {ceil['copy_gbs']:.0f} GB/s, fp16 GEMM {ceil['gemm_f16_tflops']:.0f} "
+          f"TFLOP/s", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -417,7 +492,7 @@ def main():
         what = {"forward": "conv", "forward_masked": "conv", "backward_input": "input gradient",
                 "backward_weight": "weight gradient"}[op]
         cpu = {"value": round(flops / conv_s / 1e12, 6), "unit": "TFLOP/s", "cores": oc.num_threads(),
-               "kind": "oracle",
+               "kind": "oracle", "cpu_model": cpu_model(),
                "sample": f"full {args.config} layer, all {wl.n} rows: C oracle (fp64, sort+bsearch map, "
                          f"naive loops, OpenMP); {what} {conv_s * 1e3:.0f} ms (best of 2), "
                          f"map {map_s * 1e3:.0f} ms"}
@@ -452,11 +527,21 @@ def main():
                      "traffic": measured_traffic(args.config, op, args.morton),
                      "kernel": KERNELS[op], "kernel_us": round(k_us, 2),
                      "algorithmic_bytes": alg_bytes,
-                     "mfma_effective_frac": round(flops / (k_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
+                     "mfma_effective_frac": round(flops / (k_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                     "measured_ceilings": dict(ceil, **{
+                         "frac_of_copy": round(achieved_gbs / ceil["copy_gbs"], 4),
+                         "mfma_effective_frac_of_gemm": round(
+                             flops / (k_us * 1e-6) / 1e12 / ceil["gemm_f16_tflops"], 4)})},
         "map_build_ms": round(float(np.median(build_ms)), 3),
         "mall_cold": cold,
         "cpu_baseline": cpu,
     }
+    if op == "forward" and args.config == "c3_128_128":
+        rec["context"] = {
+            "source": "trellis_sparse_mlx README, Performance table (MLX on Apple GPUs; other "
+                      "hardware, context only, not a target)",
+            "conv_ms": {"M3 Ultra (80 GPU cores)": 13.8, "M4 Pro (~20 GPU cores)": 55.1},
+            "this_step_ms": round(ms_step, 5)}
     if py_oracle is not None:
         rec["python_oracle"] = py_oracle
     print(json.dumps(rec), flush=True)

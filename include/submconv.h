@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SUBMCONV_ABI_VERSION 1
+#define SUBMCONV_ABI_VERSION 2
 
 /* Status codes. */
 #define SUBMCONV_OK 0
@@ -79,7 +79,7 @@ extern "C" {
 #define SUBMCONV_DTYPE_F16 0  /* IEEE binary16 */
 #define SUBMCONV_DTYPE_BF16 1 /* bfloat16 (the top 16 bits of a binary32) */
 
-/* Flags of submconv_prepare_weights_ex. */
+/* Flags of submconv_weights_create. */
 #define SUBMCONV_PREP_INPUT_GRAD 1u /* prepare the flipped, transposed kernel of the input gradient */
 
 /* Opaque kernel-map handle: library-owned device buffers, immutable after
@@ -88,7 +88,14 @@ extern "C" {
 typedef struct submconv_map_s* submconv_map_t;
 
 /*
- * submconv_build_map -- hash the sites and build the neighbour map.
+ * submconv_build_map -- hash the sites and build the neighbour map: the
+ * cached gather index of the README's "Performance" section (a one-time cost
+ * per site set that every layer on those sites reuses), for the sparse
+ * tensor of its "What's in it" SparseTensor row (coords [N,4], batch index
+ * first). It is a GPU coordinate hash where "Running TRELLIS.2 on a Mac
+ * (3/3)", section E, replaces a Python dict of coordinates with injectively
+ * packed int64 keys and a sorted search (which SUBMCONV_FLAG_SORTED_KEYS
+ * builds as well).
  *
  * coords   [n,4] int32 (b,x,y,z), device. Sites must be distinct and satisfy
  *          0 <= b < batch, 0 <= x < grid[0], 0 <= y < grid[1], 0 <= z < grid[2].
@@ -111,7 +118,9 @@ typedef struct submconv_map_s* submconv_map_t;
  * or 12 when packed keys exceed 32 bits; 8 bytes of key per site; sort space
  * with SUBMCONV_FLAG_MORTON or SUBMCONV_FLAG_SORTED_KEYS) stays with the
  * device after the call, up to 256 MiB, for the next build, until the
- * process ends. Builds on one device run one at a time.
+ * process ends; so does a 14 MiB buffer that forwards on W stage the weights
+ * in (see submconv_forward), allocated by the first build on the device.
+ * Builds on one device run one at a time.
  */
 int submconv_build_map(const int32_t* coords, int64_t n, int32_t batch, const int32_t grid[3],
                        uint32_t flags, hipStream_t stream, submconv_map_t* out_map);
@@ -129,7 +138,9 @@ int32_t submconv_map_tile_rows(submconv_map_t map);
 int64_t submconv_map_active_pairs(submconv_map_t map, int32_t ksize);
 
 /*
- * submconv_map_export -- write the neighbour map in the caller's row order.
+ * submconv_map_export -- write the neighbour map in the caller's row order
+ * (the indice map the README's "What's in it" SparseTensor row caches; the
+ * naive check of its "Correctness" section compares against the same table).
  * kmap [n,27] int32, device: kmap[i][k] = row j of the site coords[i] + d_k in
  * the same batch item, or -1. Asynchronous on `stream`.
  */
@@ -145,54 +156,86 @@ int submconv_map_order(submconv_map_t map, int32_t* order, hipStream_t stream);
 /* Release the map's device memory (waits for the device). NULL is a no-op. */
 int submconv_map_free(submconv_map_t map);
 
-/*
- * submconv_prepared_weights_elems -- number of fp16 elements of the prepared
- * weight buffer for a K x Cin x Cout kernel (K = 27 for ksize 3, 1 for 1).
- * Negative for an unsupported shape.
- */
-int64_t submconv_prepared_weights_elems(int32_t ksize, int32_t cin, int32_t cout);
+/* ------------------------------------------------------------------------
+ * Layer weights. W is [K,Cin,Cout] row-major (K = 27 for a 3x3x3 kernel, 1
+ * for 1x1x1), 16-bit elements, out = feats @ W[k] per tap k as above. The
+ * MFMA kernels read the weights in a fragment order of their own; the calls
+ * below that take W rearrange it on the fly (a small kernel on `stream`,
+ * into a fixed per-device buffer of the library), and a prepared-weights
+ * handle holds the rearranged copy for layers that run many times (the
+ * README's "Performance" section caches what it prepares; the forward of
+ * the issue #1 thread's "Fixed" list works on the framework's own device
+ * tensors).
+ * ---------------------------------------------------------------------- */
+
+/* Opaque prepared weights of one layer: library-owned device memory on the
+ * device that was current at submconv_weights_create, with the layer's
+ * shape, element type and use recorded, so that a forward can check them. */
+typedef struct submconv_weights_s* submconv_weights_t;
 
 /*
- * submconv_prepare_weights -- reorder weights into the forward kernel's layout.
- * It moves 16-bit elements without converting them, so it serves fp16 and
- * bf16 weights alike.
- * W   [K,Cin,Cout] fp16, device, out = feats @ W[k] per tap (k as above).
- * Wp  device buffer of submconv_prepared_weights_elems(...) fp16 elements,
- *     caller-allocated, 16-byte aligned (SUBMCONV_ERR_INVALID_ARG
- *     otherwise); its content is an opaque, shape-specific layout.
- * Prepared weights stay valid for every forward with the same ksize, Cin and
- * Cout. Asynchronous on `stream`; W and Wp must not overlap.
+ * submconv_weights_create -- allocate prepared weights for a layer.
+ * ksize 3 or 1; Cin, Cout positive multiples of 8 up to 1024 (the layer's
+ * W is [K,Cin,Cout]); dtype SUBMCONV_DTYPE_F16 or SUBMCONV_DTYPE_BF16;
+ * flags 0 (for submconv_forward_prepared and submconv_forward_masked) or
+ * SUBMCONV_PREP_INPUT_GRAD (for submconv_backward_input_prepared).
+ * Allocates K*Cin*Cout*2 bytes on the current device; the content is
+ * undefined until submconv_weights_set. *out receives the handle.
  */
-int submconv_prepare_weights(const uint16_t* W, int32_t ksize, int32_t cin, int32_t cout,
-                             uint16_t* Wp, hipStream_t stream);
+int submconv_weights_create(int32_t ksize, int32_t cin, int32_t cout, int32_t dtype,
+                            uint32_t flags, submconv_weights_t* out);
 
 /*
- * submconv_prepare_weights_ex -- submconv_prepare_weights with flags.
- * flags 0 is submconv_prepare_weights. With SUBMCONV_PREP_INPUT_GRAD, W
- * [K,Cin,Cout] is prepared as the kernel W_t[k] = W[K-1-k]^T ([K,Cout,Cin]),
- * the kernel of the input gradient (see submconv_backward_input); Wp then
- * holds submconv_prepared_weights_elems(ksize, Cout, Cin) elements (the same
- * count). Asynchronous on `stream`.
+ * submconv_weights_set -- prepare the values of W [K,Cin,Cout] (device, the
+ * handle's shape and element type, 16-byte aligned) into the handle: W
+ * itself, or with SUBMCONV_PREP_INPUT_GRAD the flipped, transposed kernel
+ * W_t[k] = W[K-1-k]^T of the input gradient. 16-bit elements are moved
+ * without conversion. Asynchronous on `stream`, no allocation; call it again
+ * whenever W changes.
  */
-int submconv_prepare_weights_ex(const uint16_t* W, int32_t ksize, int32_t cin, int32_t cout,
-                                uint32_t flags, uint16_t* Wp, hipStream_t stream);
+int submconv_weights_set(submconv_weights_t w, const uint16_t* W, hipStream_t stream);
+
+/* Release prepared weights (waits for the device). NULL is a no-op. */
+int submconv_weights_free(submconv_weights_t w);
 
 /*
- * submconv_forward -- one SubMConv3d layer on the sites of `map`.
+ * submconv_forward -- one SubMConv3d layer on the sites of `map` (the
+ * operation at the top of this file: the README's "What's in it" SubMConv3d
+ * row, computed as the fused product of its "Performance" section).
  *
  * feats  [n,Cin] fp16, device, caller row order.
- * Wp     prepared weights (submconv_prepare_weights) for (ksize, Cin, Cout).
- * bias   [Cout] fp32, device, or NULL for no bias.
+ * W      [K,Cin,Cout] fp16, device: the layer's weights as they are.
+ * bias   [Cout] fp32, device, 16-byte aligned, or NULL for no bias.
  * out    [n,Cout] fp16, device, caller row order; must not overlap feats.
  * ksize  3 (27 taps, uses the neighbour map) or 1 (centre tap only).
  *
  * Accumulates in fp32, adds the bias in fp32 and rounds once to fp16 (round to
- * nearest even). Cin and Cout must be multiples of 8 and at most 1024.
- * Enqueues on `stream`, allocates nothing and does not wait. Every output row
- * is written by exactly one workgroup without atomics, so results are
- * bitwise reproducible run to run.
+ * nearest even). Cin and Cout must be multiples of 8 and at most 1024;
+ * feats, W and out 16-byte aligned; map, W's buffer and the current device
+ * the same device (SUBMCONV_ERR_INVALID_ARG otherwise).
+ * Enqueues on `stream` and does not wait. Every output row is written by
+ * exactly one workgroup without atomics, so results are bitwise
+ * reproducible run to run, and the same for any row order and tile size.
+ *
+ * Kernels: Cin in {32, 64, 128} with Cout a multiple of 32, and Cin = 256
+ * with Cout a multiple of 128, run the MFMA gather-GEMM; its buffer offsets
+ * are 32-bit, so feats ([n,Cin] * 2 bytes) and the map's per-tile lists
+ * (8 bytes per active pair) must each stay below 2 GiB, or the call returns
+ * SUBMCONV_ERR_UNSUPPORTED_SHAPE before enqueueing anything
+ * (submconv_forward_kernel tells which case applies). Other channel counts
+ * run a VALU kernel with 64-bit addressing.
+ *
+ * Allocation: none. For the MFMA kernels W is rearranged first into a
+ * per-device buffer of the library (14 MiB, the largest MFMA layer; the
+ * first map build on a device allocates it, and it stays until the process
+ * ends, like the build's scratch); forwards that take W on different streams of one
+ * device are ordered after one another through an event on that buffer
+ * (none is recorded while `stream` is being captured into a graph: a
+ * captured forward must not run at the same time as another forward that
+ * takes W on its device). Forwards with prepared weights
+ * (submconv_forward_prepared) run concurrently on any streams.
  */
-int submconv_forward(submconv_map_t map, const uint16_t* feats, const uint16_t* Wp,
+int submconv_forward(submconv_map_t map, const uint16_t* feats, const uint16_t* W,
                      const float* bias, uint16_t* out, int32_t cin, int32_t cout, int32_t ksize,
                      hipStream_t stream);
 
@@ -204,33 +247,63 @@ int submconv_forward(submconv_map_t map, const uint16_t* feats, const uint16_t* 
  * added, and the result rounded once to the element type (round to nearest
  * even). Otherwise as submconv_forward.
  */
-int submconv_forward_dtype(submconv_map_t map, const uint16_t* feats, const uint16_t* Wp,
+int submconv_forward_dtype(submconv_map_t map, const uint16_t* feats, const uint16_t* W,
                            const float* bias, uint16_t* out, int32_t cin, int32_t cout,
                            int32_t ksize, int32_t dtype, hipStream_t stream);
 
 /*
+ * submconv_forward_prepared -- submconv_forward_dtype with weights prepared
+ * by submconv_weights_set (created without SUBMCONV_PREP_INPUT_GRAD): ksize,
+ * Cin, Cout and the element type are the handle's. Saves the rearrangement
+ * (one small kernel) per call and takes no shared buffer: forwards on one
+ * map run concurrently on several streams. Asynchronous, no allocation.
+ */
+int submconv_forward_prepared(submconv_map_t map, const uint16_t* feats, submconv_weights_t w,
+                              const float* bias, uint16_t* out, hipStream_t stream);
+
+/*
+ * submconv_forward_kernel -- which kernel a forward of this shape takes, on
+ * the host, without a device: 1 the MFMA gather-GEMM, 0 the VALU kernel, or
+ * a negative status: SUBMCONV_ERR_UNSUPPORTED_SHAPE for an MFMA shape whose
+ * features or lists reach 2 GiB (submconv_forward's limit), or a shape
+ * error. n rows, active_pairs as submconv_map_active_pairs reports them.
+ */
+int submconv_forward_kernel(int64_t n, int64_t active_pairs, int32_t cin, int32_t cout,
+                            int32_t ksize);
+
+/*
  * submconv_backward_input -- gradient of a layer's loss with respect to its
- * input features (the issue #1 thread's "bwd-input").
+ * input features (the issue #1 thread's "Fixed" list: "bwd-input").
  *
  * grad_out [n,Cout] fp16, device: dL/dout, caller row order.
- * Wp_grad  the layer's W [K,Cin,Cout] prepared with SUBMCONV_PREP_INPUT_GRAD.
+ * W        [K,Cin,Cout] fp16, device: the layer's weights as they are.
  * grad_in  [n,Cin] fp16, device: dL/dfeats[j] = sum over (i,k) with
  *          coords[j] = coords[i] + d_k of grad_out[i] @ W[k]^T, accumulated in
  *          fp32 and rounded once (round to nearest even).
  *
  * The terms of row j are the sites i at coords[j] - d_k = coords[j] +
- * d_(K-1-k), so this is submconv_forward on the same map with the flipped,
+ * d_(K-1-k), so this is the forward on the same map with the flipped,
  * transposed kernel (Cout -> Cin channels, no bias): same requirements,
- * asynchronous, no allocation, bitwise reproducible.
+ * kernels, limits and staging as submconv_forward (with Cin and Cout
+ * swapped), asynchronous, no allocation, bitwise reproducible.
  */
-int submconv_backward_input(submconv_map_t map, const uint16_t* grad_out, const uint16_t* Wp_grad,
+int submconv_backward_input(submconv_map_t map, const uint16_t* grad_out, const uint16_t* W,
                             uint16_t* grad_in, int32_t cin, int32_t cout, int32_t ksize,
                             hipStream_t stream);
 
 /* submconv_backward_input for fp16 or bf16 data (SUBMCONV_DTYPE_*). */
-int submconv_backward_input_dtype(submconv_map_t map, const uint16_t* grad_out,
-                                  const uint16_t* Wp_grad, uint16_t* grad_in, int32_t cin,
-                                  int32_t cout, int32_t ksize, int32_t dtype, hipStream_t stream);
+int submconv_backward_input_dtype(submconv_map_t map, const uint16_t* grad_out, const uint16_t* W,
+                                  uint16_t* grad_in, int32_t cin, int32_t cout, int32_t ksize,
+                                  int32_t dtype, hipStream_t stream);
+
+/*
+ * submconv_backward_input_prepared -- submconv_backward_input with the
+ * layer's weights prepared under SUBMCONV_PREP_INPUT_GRAD (the handle's
+ * Cin, Cout, ksize and element type are the layer's). Concurrent on any
+ * streams; asynchronous, no allocation.
+ */
+int submconv_backward_input_prepared(submconv_map_t map, const uint16_t* grad_out,
+                                     submconv_weights_t w, uint16_t* grad_in, hipStream_t stream);
 
 /*
  * submconv_backward_weight_workspace_bytes -- device workspace that
@@ -299,13 +372,13 @@ int64_t submconv_masked_row_taps(submconv_masked_t plan);
 
 /*
  * submconv_forward_masked -- the masked forward of a 3x3x3 layer: arguments as
- * submconv_forward (fp16, prepared weights for (3, Cin, Cout)); Cin in
- * {32, 64, 128} with Cout a multiple of 32, or Cin 256 with Cout a multiple of
- * 128. Asynchronous, no allocation, bitwise reproducible.
+ * submconv_forward_prepared, with fp16 weights prepared for (3, Cin, Cout)
+ * (no SUBMCONV_PREP_INPUT_GRAD); Cin in {32, 64, 128} with Cout a multiple of
+ * 32, or Cin 256 with Cout a multiple of 128; features below 2 GiB.
+ * Asynchronous, no allocation, bitwise reproducible.
  */
-int submconv_forward_masked(submconv_masked_t plan, const uint16_t* feats, const uint16_t* Wp,
-                            const float* bias, uint16_t* out, int32_t cin, int32_t cout,
-                            hipStream_t stream);
+int submconv_forward_masked(submconv_masked_t plan, const uint16_t* feats, submconv_weights_t w,
+                            const float* bias, uint16_t* out, hipStream_t stream);
 
 /* Release a masked plan (waits for the device). NULL is a no-op. */
 int submconv_masked_free(submconv_masked_t plan);

@@ -14,8 +14,9 @@ What it computes, written from the definition:
   (same table, SparseTensor row).
 * Each output row accumulates, over the kernel offsets, the gathered input
   feature row times that offset's weight matrix (same README, "Performance":
-  the naive loop accumulating ``gather(i) @ W[i]`` over the 27 offsets; the
-  fused ``[N, K^3*Cin] x [K^3*Cin, Cout]`` matmul is the same sum).
+  it describes the unfused form as one gather and one product per offset,
+  and its fused ``[N, K^3*Cin] x [K^3*Cin, Cout]`` matmul computes the same
+  sum).
 * The gather reads ``feats[c + d]``, cross-correlation (same README,
   "Correctness", the unverified c+d assumption; this oracle takes c+d).
 * It is a deliberately naive dict lookup with a per-voxel loop, sharing no

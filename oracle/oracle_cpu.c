@@ -8,7 +8,8 @@
  *
  * Definition followed (trellis_sparse_mlx README: "What's in it" table for
  * the 3x3x3 / 1x1x1 kernel and the [N,4] coordinates; "Performance" for the
- * per-offset gather(i) @ W[i] accumulation; "Correctness" for the c+d
+ * sum over offsets of each gathered row times that offset's weights;
+ * "Correctness" for the c+d
  * cross-correlation and the naive per-voxel reference):
  *
  *   kmap[i][k] = row j with coords[j] == coords[i] + d_k (same batch item),

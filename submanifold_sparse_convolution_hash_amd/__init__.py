@@ -23,7 +23,8 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = [
-    "SubmconvError", "KernelMap", "build_map", "prepare_weights", "forward", "backward_input",
+    "SubmconvError", "KernelMap", "build_map", "Weights", "prepare_weights", "forward",
+    "forward_kernel", "backward_input",
     "backward_weight", "backward_bias", "SubMConv3dFunction", "SubMConv3d", "library_path", "load_library",
     "abi_version", "FLAG_MORTON", "downsample", "subdivide", "MaskedPlan", "masked_plan",
     "forward_masked",
@@ -69,10 +70,13 @@ def load_library():
         "submconv_map_export": ([P, P, P], ctypes.c_int),
         "submconv_map_order": ([P, P, P], ctypes.c_int),
         "submconv_map_free": ([P], ctypes.c_int),
-        "submconv_prepared_weights_elems": ([I32, I32, I32], I64),
-        "submconv_prepare_weights": ([P, I32, I32, I32, P, P], ctypes.c_int),
-        "submconv_prepare_weights_ex": ([P, I32, I32, I32, U32, P, P], ctypes.c_int),
+        "submconv_weights_create": ([I32, I32, I32, I32, U32, P], ctypes.c_int),
+        "submconv_weights_set": ([P, P, P], ctypes.c_int),
+        "submconv_weights_free": ([P], ctypes.c_int),
+        "submconv_forward_prepared": ([P, P, P, P, P, P], ctypes.c_int),
+        "submconv_forward_kernel": ([I64, I64, I32, I32, I32], ctypes.c_int),
         "submconv_backward_input": ([P, P, P, P, I32, I32, I32, P], ctypes.c_int),
+        "submconv_backward_input_prepared": ([P, P, P, P, P], ctypes.c_int),
         "submconv_backward_weight_workspace_bytes": ([P, I32, I32, I32], I64),
         "submconv_backward_weight": ([P, P, P, P, P, I32, I32, I32, P], ctypes.c_int),
         "submconv_backward_bias": ([P, I64, I32, P, P], ctypes.c_int),
@@ -85,7 +89,7 @@ def load_library():
         "submconv_subdivide": ([P, I64, P, I32, P, P, P], ctypes.c_int),
         "submconv_masked_plan": ([P, P, P], ctypes.c_int),
         "submconv_masked_row_taps": ([P], I64),
-        "submconv_forward_masked": ([P, P, P, P, P, I32, I32, P], ctypes.c_int),
+        "submconv_forward_masked": ([P, P, P, P, P, P], ctypes.c_int),
         "submconv_masked_free": ([P], ctypes.c_int),
         "submconv_forward": ([P, P, P, P, P, I32, I32, I32, P], ctypes.c_int),
         "submconv_forward_dtype": ([P, P, P, P, P, I32, I32, I32, I32, P], ctypes.c_int),
@@ -214,103 +218,174 @@ def build_map(coords: torch.Tensor, grid: Sequence[int], batch: Optional[int] = 
     return KernelMap(h, coords.device, grid, batch, flags)
 
 
-def prepare_weights(W: torch.Tensor, input_grad: bool = False) -> torch.Tensor:
-    """Reorders weights [K,Cin,Cout] fp16 or bf16 (K = 27 or 1) into the
-    forward kernel's layout (an opaque buffer of the same dtype and element
-    count). With ``input_grad``, prepares the flipped, transposed kernel of
-    the input gradient instead (for :func:`backward_input`)."""
-    _require(W, "W", tuple(_DTYPES), 3)
-    K, cin, cout = W.shape
-    if K not in (27, 1):
-        raise ValueError("W must be [27,Cin,Cout] or [1,Cin,Cout]")
-    ksize = 3 if K == 27 else 1
-    lib = load_library()
-    n = int(lib.submconv_prepared_weights_elems(ksize, cin, cout))
-    if n < 0:
-        _check(n)
-    wp = torch.empty((n,), dtype=W.dtype, device=W.device)
-    with torch.cuda.device(W.device):
-        _check(lib.submconv_prepare_weights_ex(_ptr(W), ksize, cin, cout,
-                                               PREP_INPUT_GRAD if input_grad else 0, _ptr(wp),
-                                               _stream(W.device)))
-    return wp
+class Weights:
+    """Prepared weights of one layer (``submconv_weights_t``): the library's
+    device copy of ``W`` ([K,Cin,Cout], K = 27 or 1, fp16 or bf16) in the MFMA
+    kernels' order, for the forward, or with ``input_grad`` for the input
+    gradient. The handle records the shape, dtype and use, and the library
+    checks them at every call. ``set`` re-prepares new values of ``W``."""
+
+    def __init__(self, W: torch.Tensor, input_grad: bool = False):
+        _require(W, "W", tuple(_DTYPES), 3)
+        K, cin, cout = (int(v) for v in W.shape)
+        if K not in (27, 1):
+            raise ValueError("W must be [27,Cin,Cout] or [1,Cin,Cout]")
+        self.ksize = 3 if K == 27 else 1
+        self.cin, self.cout = cin, cout
+        self.dtype = W.dtype
+        self.device = W.device
+        self.input_grad = bool(input_grad)
+        self._h = None
+        h = ctypes.c_void_p()
+        with torch.cuda.device(W.device):
+            _check(load_library().submconv_weights_create(
+                self.ksize, cin, cout, _DTYPES[W.dtype], PREP_INPUT_GRAD if input_grad else 0,
+                ctypes.byref(h)))
+        self._h = h
+        self.set(W)
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if self._h is None:
+            raise SubmconvError(-1, "weights already freed")
+        return self._h
+
+    def set(self, W: torch.Tensor) -> None:
+        _require(W, "W", self.dtype, 3)
+        if tuple(W.shape) != (27 if self.ksize == 3 else 1, self.cin, self.cout):
+            raise ValueError(f"W is {tuple(W.shape)}, the handle's layer "
+                             f"[{27 if self.ksize == 3 else 1},{self.cin},{self.cout}]")
+        if W.device != self.device:
+            raise ValueError(f"W is on {W.device}, the handle on {self.device}")
+        with torch.cuda.device(W.device):
+            _check(load_library().submconv_weights_set(self.handle, _ptr(W), _stream(W.device)))
+
+    def free(self) -> None:
+        if self._h is not None and _lib is not None:
+            _check(_lib.submconv_weights_free(self._h))
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def prepare_weights(W: torch.Tensor, input_grad: bool = False) -> Weights:
+    """Prepares ``W`` ([K,Cin,Cout], fp16 or bf16) for :func:`forward` (or,
+    with ``input_grad``, for :func:`backward_input`)."""
+    return Weights(W, input_grad)
+
+
+def forward_kernel(n: int, active_pairs: int, cin: int, cout: int, ksize: int = 3) -> int:
+    """The kernel a forward of this shape takes (host only): 1 MFMA, 0 VALU;
+    raises :class:`SubmconvError` for a shape the library rejects (e.g. MFMA
+    features of 2 GiB or more)."""
+    v = int(load_library().submconv_forward_kernel(int(n), int(active_pairs), int(cin), int(cout),
+                                                    int(ksize)))
+    if v < 0:
+        _check(v)
+    return v
+
+
+def _check_bias(bias, cout):
+    if bias is not None:
+        _require(bias, "bias", torch.float32, 1)
+        if bias.shape[0] != cout:
+            raise ValueError(f"bias must be [Cout] = [{cout}], got {tuple(bias.shape)}")
+
+
+def _out_tensor(out, rows, cols, dtype, device):
+    if out is None:
+        return torch.empty((rows, cols), dtype=dtype, device=device)
+    _require(out, "out", dtype, 2)
+    if tuple(out.shape) != (rows, cols):
+        raise ValueError(f"out must be [{rows},{cols}], got {tuple(out.shape)}")
+    return out
 
 
 def forward(kmap: KernelMap, feats: torch.Tensor, W: Optional[torch.Tensor] = None,
-            bias: Optional[torch.Tensor] = None, *, prepared: Optional[torch.Tensor] = None,
-            ksize: Optional[int] = None, cout: Optional[int] = None,
+            bias: Optional[torch.Tensor] = None, *, prepared: Optional[Weights] = None,
             out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One SubMConv3d layer: ``out[N,Cout]`` in the caller's row order, in
     the features' dtype (fp16 or bf16; fp32 accumulation).
 
-    Pass either ``W`` ([K,Cin,Cout], the features' dtype, prepared on the fly)
-    or ``prepared`` (from :func:`prepare_weights`) together with ``ksize`` and
-    ``cout``.
-    """
+    Pass either ``W`` ([K,Cin,Cout], the features' dtype: ``submconv_forward``,
+    which rearranges it on the fly) or ``prepared`` (a :class:`Weights`:
+    ``submconv_forward_prepared``)."""
     _require(feats, "feats", tuple(_DTYPES), 2)
     if feats.shape[0] != kmap.num_rows:
         raise ValueError(f"feats has {feats.shape[0]} rows, the map {kmap.num_rows}")
     cin = feats.shape[1]
-    if prepared is None:
-        if W is None:
-            raise ValueError("pass W or prepared")
-        if W.shape[1] != cin:
-            raise ValueError(f"W is {tuple(W.shape)} but feats has Cin = {cin}")
-        ksize = 3 if W.shape[0] == 27 else 1
-        cout = W.shape[2]
-        prepared = prepare_weights(W)
-    elif ksize is None or cout is None:
-        raise ValueError("with prepared weights, pass ksize and cout")
-    if prepared.dtype != feats.dtype:
-        raise TypeError(f"weights are {prepared.dtype} but feats are {feats.dtype}")
-    if bias is not None:
-        _require(bias, "bias", torch.float32, 1)
-        if bias.shape[0] != cout:
-            raise ValueError("bias must be [Cout]")
-    if out is None:
-        out = torch.empty((feats.shape[0], cout), dtype=feats.dtype, device=feats.device)
-    else:
-        _require(out, "out", feats.dtype, 2)
-        if tuple(out.shape) != (feats.shape[0], cout):
-            raise ValueError("out must be [N,Cout]")
+    lib = load_library()
+    if prepared is not None:
+        if W is not None:
+            raise ValueError("pass W or prepared, not both")
+        if prepared.input_grad:
+            raise ValueError("these weights are prepared for the input gradient")
+        if prepared.dtype != feats.dtype or prepared.cin != cin:
+            raise ValueError(f"weights are {prepared.dtype} with Cin = {prepared.cin}, feats "
+                             f"{feats.dtype} with Cin = {cin}")
+        cout = prepared.cout
+        _check_bias(bias, cout)
+        out = _out_tensor(out, feats.shape[0], cout, feats.dtype, feats.device)
+        with torch.cuda.device(feats.device):
+            _check(lib.submconv_forward_prepared(kmap.handle, _ptr(feats), prepared.handle,
+                                                 _ptr(bias), _ptr(out), _stream(feats.device)))
+        return out
+    if W is None:
+        raise ValueError("pass W or prepared")
+    _require(W, "W", feats.dtype, 3)
+    if W.shape[0] not in (27, 1) or W.shape[1] != cin:
+        raise ValueError(f"W is {tuple(W.shape)} but feats has Cin = {cin}")
+    ksize = 3 if W.shape[0] == 27 else 1
+    cout = W.shape[2]
+    _check_bias(bias, cout)
+    out = _out_tensor(out, feats.shape[0], cout, feats.dtype, feats.device)
     with torch.cuda.device(feats.device):
-        _check(load_library().submconv_forward_dtype(kmap.handle, _ptr(feats), _ptr(prepared),
-                                                     _ptr(bias), _ptr(out), cin, cout, int(ksize),
-                                                     _DTYPES[feats.dtype], _stream(feats.device)))
+        _check(lib.submconv_forward_dtype(kmap.handle, _ptr(feats), _ptr(W), _ptr(bias), _ptr(out),
+                                          cin, cout, ksize, _DTYPES[feats.dtype],
+                                          _stream(feats.device)))
     return out
 
 
 def backward_input(kmap: KernelMap, grad_out: torch.Tensor, W: Optional[torch.Tensor] = None, *,
-                   prepared: Optional[torch.Tensor] = None, ksize: Optional[int] = None,
-                   cin: Optional[int] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Input gradient ``[N,Cin]`` fp16 of a layer with weights ``W`` for the
-    output gradient ``grad_out`` ([N,Cout] fp16). Pass ``W`` or ``prepared``
-    (``prepare_weights(W, input_grad=True)``) with ``ksize`` and ``cin``."""
+                   prepared: Optional[Weights] = None,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Input gradient ``[N,Cin]`` (fp16 or bf16) of a layer with weights ``W``
+    ([K,Cin,Cout]) for the output gradient ``grad_out`` ([N,Cout]). Pass ``W``
+    or ``prepared`` (``Weights(W, input_grad=True)``)."""
     _require(grad_out, "grad_out", tuple(_DTYPES), 2)
     if grad_out.shape[0] != kmap.num_rows:
         raise ValueError(f"grad_out has {grad_out.shape[0]} rows, the map {kmap.num_rows}")
     cout = grad_out.shape[1]
-    if prepared is None:
-        if W is None:
-            raise ValueError("pass W or prepared")
-        if W.shape[2] != cout:
-            raise ValueError(f"W is {tuple(W.shape)} but grad_out has Cout = {cout}")
-        ksize = 3 if W.shape[0] == 27 else 1
-        cin = W.shape[1]
-        prepared = prepare_weights(W, input_grad=True)
-    elif ksize is None or cin is None:
-        raise ValueError("with prepared weights, pass ksize and cin")
-    if prepared.dtype != grad_out.dtype:
-        raise TypeError(f"weights are {prepared.dtype} but grad_out is {grad_out.dtype}")
-    if out is None:
-        out = torch.empty((grad_out.shape[0], cin), dtype=grad_out.dtype, device=grad_out.device)
-    else:
-        _require(out, "out", grad_out.dtype, 2)
-        if tuple(out.shape) != (grad_out.shape[0], cin):
-            raise ValueError("out must be [N,Cin]")
+    lib = load_library()
+    if prepared is not None:
+        if W is not None:
+            raise ValueError("pass W or prepared, not both")
+        if not prepared.input_grad:
+            raise ValueError("these weights are prepared for the forward, not the input gradient")
+        if prepared.dtype != grad_out.dtype or prepared.cout != cout:
+            raise ValueError(f"weights are {prepared.dtype} with Cout = {prepared.cout}, grad_out "
+                             f"{grad_out.dtype} with Cout = {cout}")
+        out = _out_tensor(out, grad_out.shape[0], prepared.cin, grad_out.dtype, grad_out.device)
+        with torch.cuda.device(grad_out.device):
+            _check(lib.submconv_backward_input_prepared(kmap.handle, _ptr(grad_out),
+                                                        prepared.handle, _ptr(out),
+                                                        _stream(grad_out.device)))
+        return out
+    if W is None:
+        raise ValueError("pass W or prepared")
+    _require(W, "W", grad_out.dtype, 3)
+    if W.shape[0] not in (27, 1) or W.shape[2] != cout:
+        raise ValueError(f"W is {tuple(W.shape)} but grad_out has Cout = {cout}")
+    ksize = 3 if W.shape[0] == 27 else 1
+    cin = W.shape[1]
+    out = _out_tensor(out, grad_out.shape[0], cin, grad_out.dtype, grad_out.device)
     with torch.cuda.device(grad_out.device):
-        _check(load_library().submconv_backward_input_dtype(
-            kmap.handle, _ptr(grad_out), _ptr(prepared), _ptr(out), int(cin), cout, int(ksize),
+        _check(lib.submconv_backward_input_dtype(
+            kmap.handle, _ptr(grad_out), _ptr(W), _ptr(out), cin, cout, ksize,
             _DTYPES[grad_out.dtype], _stream(grad_out.device)))
     return out
 
@@ -390,24 +465,27 @@ def masked_plan(kmap: KernelMap) -> MaskedPlan:
 
 
 def forward_masked(plan: MaskedPlan, feats: torch.Tensor, W: Optional[torch.Tensor] = None,
-                   bias: Optional[torch.Tensor] = None, *, prepared: Optional[torch.Tensor] = None,
-                   cout: Optional[int] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                   bias: Optional[torch.Tensor] = None, *, prepared: Optional[Weights] = None,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The 3x3x3 forward by the masked implicit GEMM (fp16); same result as
-    :func:`forward` up to the order of the fp32 additions."""
+    :func:`forward` up to the order of the fp32 additions. Pass ``W``
+    ([27,Cin,Cout] fp16, prepared here) or ``prepared``."""
     _require(feats, "feats", torch.float16, 2)
-    cin = feats.shape[1]
+    if feats.shape[0] != plan.kmap.num_rows:
+        raise ValueError(f"feats has {feats.shape[0]} rows, the map {plan.kmap.num_rows}")
     if prepared is None:
-        if W is None or W.shape[0] != 27:
-            raise ValueError("pass W [27,Cin,Cout] or prepared")
-        cout = W.shape[2]
-        prepared = prepare_weights(W)
-    elif cout is None:
-        raise ValueError("with prepared weights, pass cout")
-    if out is None:
-        out = torch.empty((feats.shape[0], cout), dtype=torch.float16, device=feats.device)
+        if W is None:
+            raise ValueError("pass W or prepared")
+        prepared = Weights(W)
+    if prepared.input_grad or prepared.ksize != 3 or prepared.dtype != torch.float16:
+        raise ValueError("masked forward: fp16 3x3x3 weights prepared for the forward")
+    if prepared.cin != feats.shape[1]:
+        raise ValueError(f"weights have Cin = {prepared.cin}, feats {feats.shape[1]}")
+    _check_bias(bias, prepared.cout)
+    out = _out_tensor(out, feats.shape[0], prepared.cout, torch.float16, feats.device)
     with torch.cuda.device(feats.device):
-        _check(load_library().submconv_forward_masked(plan.handle, _ptr(feats), _ptr(prepared),
-                                                      _ptr(bias), _ptr(out), cin, int(cout),
+        _check(load_library().submconv_forward_masked(plan.handle, _ptr(feats), prepared.handle,
+                                                      _ptr(bias), _ptr(out),
                                                       _stream(feats.device)))
     return out
 
@@ -504,13 +582,15 @@ class SubMConv3d(torch.nn.Module):
         self._cache = None
         self._cache_key = None
 
-    def prepared(self) -> torch.Tensor:
+    def prepared(self) -> Weights:
         key = (self.weight.data_ptr(), self.weight._version)
         if self._cache is None or self._cache_key != key:
-            self._cache = prepare_weights(self.weight)
+            if self._cache is None or self._cache.device != self.weight.device:
+                self._cache = Weights(self.weight.data)
+            else:
+                self._cache.set(self.weight.data)
             self._cache_key = key
         return self._cache
 
     def forward(self, kmap: KernelMap, feats: torch.Tensor) -> torch.Tensor:
-        return forward(kmap, feats, bias=self.bias, prepared=self.prepared(), ksize=self.ksize,
-                       cout=self.weight.shape[2])
+        return forward(kmap, feats, bias=self.bias, prepared=self.prepared())

@@ -742,10 +742,23 @@ extern "C" int submconv_backward_weight(submconv_map_t map, const uint16_t* feat
   if (ws > 0 && !workspace) return set_error(SUBMCONV_ERR_INVALID_ARG, "workspace is NULL");
   if ((reinterpret_cast<uintptr_t>(grad_w) | reinterpret_cast<uintptr_t>(workspace)) & 15)
     return set_error(SUBMCONV_ERR_INVALID_ARG, "grad_w and workspace must be 16-byte aligned");
+  int dev = -1;
+  SUBMCONV_HIP_CHECK(hipGetDevice(&dev));
+  if (dev != m.device)
+    return set_error(SUBMCONV_ERR_INVALID_ARG, "the map is on device %d, the current device is %d",
+                     m.device, dev);
   const _Float16* f = reinterpret_cast<const _Float16*>(feats);
   const _Float16* g = reinterpret_cast<const _Float16*>(grad_out);
   float* part = static_cast<float*>(workspace);
-  if (ws > 0 && m.n * cin * 2 < (int64_t{1} << 31) - 64 && m.n * cout * 2 < (int64_t{1} << 31) - 64) {
+  if (ws > 0) {
+    // the MFMA kernels address rows and lists through 32-bit buffer offsets
+    constexpr int64_t kMax = (int64_t{1} << 31) - 64;
+    if (m.n * cin * 2 > kMax || m.n * cout * 2 > kMax || (m.active_pairs + 1) * 8 > kMax)
+      return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE,
+                       "%lld rows x (%d, %d) channels, %lld pairs: features, gradients or lists "
+                       "reach 2 GiB, the weight-gradient kernel's 32-bit buffer offsets",
+                       static_cast<long long>(m.n), cin, cout,
+                       static_cast<long long>(m.active_pairs));
     switch (cin) {
       case 32: return dispatch_w<32>(m, K, cout, f, g, part, grad_w, stream);
       case 64: return dispatch_w<64>(m, K, cout, f, g, part, grad_w, stream);

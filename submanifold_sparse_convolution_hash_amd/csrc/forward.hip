@@ -30,6 +30,7 @@
 #include <algorithm>
 #include <atomic>
 #include <climits>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -601,8 +602,10 @@ __global__ __launch_bounds__((CfgPP<CIN, COUT_T, K3, GR_, M_>::NT)) void k_fwd_p
 // neighbour indices are loaded first, all at once, and the taps are unrolled
 // with a select instead of a branch, so that the loads of successive taps
 // are in flight together (a tiny layer is otherwise a chain of load
-// latencies).
-template <bool K3, bool IS_BF16>
+// latencies). The weights are read as the caller holds them: W_t[k][ci][co]
+// = W[k][ci][co], or for the input gradient (GRAD) the flipped, transposed
+// W[K-1-k][co][ci] of the layer's W [K][cout][cin].
+template <bool K3, bool IS_BF16, bool GRAD>
 __global__ __launch_bounds__(256) void k_fwd_valu(
     const int32_t* __restrict__ nbr, const int32_t* __restrict__ order, int64_t n,
     const _Float16* __restrict__ feats, const _Float16* __restrict__ w,
@@ -623,13 +626,16 @@ __global__ __launch_bounds__(256) void k_fwd_valu(
       const bool live = js[k] >= 0;
       const half8* f8 =
           reinterpret_cast<const half8*>(feats + static_cast<int64_t>(live ? js[k] : 0) * cin);
-      const _Float16* wk = w + static_cast<int64_t>(k) * cin * cout + o;
+      // W_t[k][ci][o] = wk[ci * ws]
+      const _Float16* wk = GRAD ? w + (static_cast<int64_t>(K - 1 - k) * cout + o) * cin
+                                : w + static_cast<int64_t>(k) * cin * cout + o;
+      const int64_t ws = GRAD ? 1 : cout;
       for (int c8 = 0; c8 < cin / 8; ++c8) {
         const half8 fv = f8[c8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float v = fmaf(widen16<IS_BF16>(fv[e]),
-                               widen16<IS_BF16>(wk[static_cast<int64_t>(8 * c8 + e) * cout]), a);
+                               widen16<IS_BF16>(wk[static_cast<int64_t>(8 * c8 + e) * ws]), a);
           a = live ? v : a;
         }
       }
@@ -699,10 +705,22 @@ bool use_mfma(int cin, int cout) {
   return (cin == 32 || cin == 64 || cin == 128) && cout % 32 == 0;
 }
 
-// The MFMA kernel addresses features, weights and lists through 32-bit
-// buffer offsets below 2 GiB.
-bool fits_buffers(const Map& m, int cin) {
-  return m.n * cin * 2 < (int64_t{1} << 31) - 64 && m.active_pairs * 8 < (int64_t{1} << 31) - 64;
+// The MFMA kernel addresses features and lists through 32-bit buffer
+// offsets, with kOob (2 GiB) as the offset of a lane that loads nothing.
+constexpr int64_t kMaxBufferBytes = (int64_t{1} << 31) - 64;
+
+// Kernel of a forward: 1 MFMA, 0 VALU, or a negative status.
+int kernel_path(int64_t n, int64_t pairs, int cin, int cout, int ksize) {
+  if (!use_mfma(cin, cout)) return 0;
+  if (n * cin * 2 > kMaxBufferBytes)
+    return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE,
+                     "features of %lld rows x %d channels reach 2 GiB, the MFMA kernel's "
+                     "32-bit buffer offsets", static_cast<long long>(n), cin);
+  if (ksize == 3 && (pairs + 1) * 8 > kMaxBufferBytes)
+    return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE,
+                     "%lld active pairs: the per-tile lists reach 2 GiB, the MFMA kernel's "
+                     "32-bit buffer offsets", static_cast<long long>(pairs));
+  return 1;
 }
 
 int check_shape(int32_t ksize, int32_t cin, int32_t cout) {
@@ -835,10 +853,16 @@ int dispatch_cout(const Map& m, int ksize, const _Float16* feats, const _Float16
   return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "internal: no MFMA tile for Cin = %d", CIN);
 }
 
+// The forward on weights in the kernel's layout: prepared MFMA fragments
+// when the shape takes the MFMA kernel, else W_t[k][ci][co] (or, with GRAD,
+// the layer's own W [K][cout][cin], read flipped and transposed).
 template <bool IS_BF16>
 int forward_typed(const Map& m, int ksize, int cin, int cout, const _Float16* feats,
-                  const _Float16* wp, const float* bias, _Float16* out, hipStream_t stream) {
-  if (use_mfma(cin, cout) && fits_buffers(m, cin)) {
+                  const _Float16* wp, bool grad, const float* bias, _Float16* out,
+                  hipStream_t stream) {
+  const int path = kernel_path(m.n, m.active_pairs, cin, cout, ksize);
+  if (path < 0) return path;
+  if (path == 1) {
     switch (cin) {
       case 32: return dispatch_cout<32, IS_BF16>(m, ksize, feats, wp, bias, out, cout, stream);
       case 64: return dispatch_cout<64, IS_BF16>(m, ksize, feats, wp, bias, out, cout, stream);
@@ -851,66 +875,204 @@ int forward_typed(const Map& m, int ksize, int cin, int cout, const _Float16* fe
   // a grid-stride loop over (row, column) items
   const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((items + 255) / 256, 1 << 20));
   const int B = 256;
+  auto go = [&](auto k3, auto gr) {
+    constexpr bool K3 = decltype(k3)::value, GR = decltype(gr)::value;
+    k_fwd_valu<K3, IS_BF16, GR><<<blocks, B, 0, stream>>>(K3 ? m.nbr : nullptr,
+                                                          K3 ? m.order : nullptr, m.n, feats, wp,
+                                                          bias, out, cin, cout);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
   if (ksize == 3)
-    k_fwd_valu<true, IS_BF16><<<blocks, B, 0, stream>>>(
-        m.nbr, m.order, m.n, feats, wp, bias, out, cin, cout);
+    grad ? go(T{}, T{}) : go(T{}, F{});
   else
-    k_fwd_valu<false, IS_BF16><<<blocks, B, 0, stream>>>(
-        nullptr, nullptr, m.n, feats, wp, bias, out, cin, cout);
+    grad ? go(F{}, T{}) : go(F{}, F{});
   SUBMCONV_HIP_CHECK(hipGetLastError());
+  return SUBMCONV_OK;
+}
+
+// Rearranges W [K][cin][cout] for a forward with cin_t x cout_t channels
+// (W itself, or with grad the input gradient's W[K-1-k]^T: cin_t = cout,
+// cout_t = cin) into wp.
+int prepare_into(const _Float16* W, int K, int cin, int cout, bool grad, _Float16* wp,
+                 hipStream_t stream) {
+  const int cin_t = grad ? cout : cin, cout_t = grad ? cin : cout;
+  const int64_t total = static_cast<int64_t>(K) * cin * cout;
+  const int B = 256;
+  if (use_mfma(cin_t, cout_t))
+    k_prepare_mfma<<<static_cast<unsigned>((total / 8 + B - 1) / B), B, 0, stream>>>(
+        W, K, cin_t, cout_t, grad, wp);
+  else
+    k_prepare_plain<<<static_cast<unsigned>((total + B - 1) / B), B, 0, stream>>>(
+        W, K, cin_t, cout_t, grad, wp);
+  SUBMCONV_HIP_CHECK(hipGetLastError());
+  return SUBMCONV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// per-device staging of weights passed as they are
+// ---------------------------------------------------------------------------
+
+// The largest prepared MFMA layer: 27 taps x 256 x 1024 (or 1024 x 256 for an
+// input gradient) 16-bit elements.
+constexpr size_t kStageBytes = size_t{kTaps3} * 256 * 1024 * 2;
+
+struct Stage {
+  std::mutex mu;
+  _Float16* ptr = nullptr;       // this device's staging buffer
+  hipEvent_t done = nullptr;     // recorded after the last forward that read it
+  hipStream_t last = nullptr;    // the stream of that forward
+  bool recorded = false;
+};
+constexpr int kMaxDevices = 64;
+Stage g_stages[kMaxDevices];
+
+// A forward with weights as the caller holds them: for the MFMA kernels they
+// are rearranged into this device's staging buffer first. Forwards on other
+// streams are ordered around the buffer by an event (the stream waits for
+// the previous user's event, and records its own after its launches); while
+// the stream is being captured into a graph no event is used.
+template <bool IS_BF16>
+int forward_raw(const Map& m, int ksize, int cin, int cout, const _Float16* feats,
+                const _Float16* W, bool grad, const float* bias, _Float16* out,
+                hipStream_t stream) {
+  // cin, cout: the channels of this forward (an input gradient's are the
+  // layer's swapped); W: the layer's weights
+  const int path = kernel_path(m.n, m.active_pairs, cin, cout, ksize);
+  if (path < 0) return path;
+  if (path == 0)
+    return forward_typed<IS_BF16>(m, ksize, cin, cout, feats, W, grad, bias, out, stream);
+  const int K = ksize == 3 ? kTaps3 : 1;
+  if (static_cast<size_t>(K) * cin * cout * 2 > kStageBytes)
+    return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "internal: %d x %d weights exceed the stage",
+                     cin, cout);
+  Stage& sg = g_stages[m.device];
+  std::lock_guard<std::mutex> lock(sg.mu);
+  if (!sg.ptr || !sg.done)  // a map build on the device sets both up
+    return set_error(SUBMCONV_ERR_INVALID_ARG, "internal: no weight stage on device %d", m.device);
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  const bool capturing =
+      hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone;
+  (void)hipGetLastError();  // a failed query is not this call's error
+  if (!capturing && sg.recorded && sg.last != stream)
+    SUBMCONV_HIP_CHECK(hipStreamWaitEvent(stream, sg.done, 0));
+  // the layer's W is [K][cin][cout], or [K][cout][cin] for an input gradient
+  const int st = prepare_into(W, K, grad ? cout : cin, grad ? cin : cout, grad, sg.ptr, stream);
+  if (st != SUBMCONV_OK) return st;
+  const int fs = forward_typed<IS_BF16>(m, ksize, cin, cout, feats, sg.ptr, false, bias, out,
+                                        stream);
+  if (!capturing) {
+    SUBMCONV_HIP_CHECK(hipEventRecord(sg.done, stream));
+    sg.recorded = true;
+    sg.last = stream;
+  }
+  return fs;
+}
+
+// Checks shared by every forward entry point; n == 0 is handled by the caller.
+int check_call(const Map& m, const void* feats, const void* w, const void* out, const float* bias) {
+  if (!feats || !w || !out) return set_error(SUBMCONV_ERR_INVALID_ARG, "feats, W or out is NULL");
+  if ((reinterpret_cast<uintptr_t>(feats) | reinterpret_cast<uintptr_t>(w) |
+       reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(bias)) & 15)
+    return set_error(SUBMCONV_ERR_INVALID_ARG,
+                     "feats, W, out and bias must be 16-byte aligned");
+  int dev = -1;
+  SUBMCONV_HIP_CHECK(hipGetDevice(&dev));
+  if (dev != m.device)
+    return set_error(SUBMCONV_ERR_INVALID_ARG, "the map is on device %d, the current device is %d",
+                     m.device, dev);
+  if (m.device < 0 || m.device >= kMaxDevices)
+    return set_error(SUBMCONV_ERR_INVALID_ARG, "device %d out of range", m.device);
   return SUBMCONV_OK;
 }
 
 }  // namespace
+
+// Sets up the device's weight stage (one allocation and one event per device,
+// kept until the process ends); every map build calls it, so that a forward,
+// which always has a map, finds it and allocates nothing.
+int ensure_weight_stage(int device) {
+  if (device < 0 || device >= kMaxDevices)
+    return set_error(SUBMCONV_ERR_INVALID_ARG, "device %d out of range", device);
+  Stage& sg = g_stages[device];
+  std::lock_guard<std::mutex> lock(sg.mu);
+  if (!sg.ptr) {
+    void* p = nullptr;
+    SUBMCONV_HIP_CHECK(hipMalloc(&p, kStageBytes));
+    sg.ptr = static_cast<_Float16*>(p);
+  }
+  if (!sg.done) SUBMCONV_HIP_CHECK(hipEventCreateWithFlags(&sg.done, hipEventDisableTiming));
+  return SUBMCONV_OK;
+}
+
 }  // namespace submconv
 
 using namespace submconv;
 
-extern "C" int64_t submconv_prepared_weights_elems(int32_t ksize, int32_t cin, int32_t cout) {
-  const int st = check_shape(ksize, cin, cout);
-  if (st != SUBMCONV_OK) return st;
-  return static_cast<int64_t>(ksize == 3 ? kTaps3 : 1) * cin * cout;
-}
-
-extern "C" int submconv_prepare_weights_ex(const uint16_t* W, int32_t ksize, int32_t cin,
-                                           int32_t cout, uint32_t flags, uint16_t* Wp,
-                                           hipStream_t stream) {
+extern "C" int submconv_forward_kernel(int64_t n, int64_t active_pairs, int32_t cin, int32_t cout,
+                                       int32_t ksize) {
   clear_error();
   const int st = check_shape(ksize, cin, cout);
   if (st != SUBMCONV_OK) return st;
-  if (!W || !Wp) return set_error(SUBMCONV_ERR_INVALID_ARG, "W or Wp is NULL");
-  if (reinterpret_cast<uintptr_t>(Wp) & 15)
-    return set_error(SUBMCONV_ERR_INVALID_ARG, "Wp must be 16-byte aligned");
+  if (n < 0 || active_pairs < 0)
+    return set_error(SUBMCONV_ERR_INVALID_ARG, "negative row or pair count");
+  return kernel_path(n, active_pairs, cin, cout, ksize);
+}
+
+extern "C" int submconv_weights_create(int32_t ksize, int32_t cin, int32_t cout, int32_t dtype,
+                                       uint32_t flags, submconv_weights_t* out) {
+  clear_error();
+  if (!out) return set_error(SUBMCONV_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  const int st = check_shape(ksize, cin, cout);
+  if (st != SUBMCONV_OK) return st;
+  if (dtype != SUBMCONV_DTYPE_F16 && dtype != SUBMCONV_DTYPE_BF16)
+    return set_error(SUBMCONV_ERR_INVALID_ARG, "dtype = %d is not fp16 (0) or bf16 (1)", dtype);
   if (flags & ~SUBMCONV_PREP_INPUT_GRAD)
     return set_error(SUBMCONV_ERR_INVALID_ARG, "unknown preparation flags 0x%x", flags);
-  const bool grad = flags & SUBMCONV_PREP_INPUT_GRAD;
-  // channels of the forward these weights are for
-  const int cin_t = grad ? cout : cin, cout_t = grad ? cin : cout;
-  const int K = ksize == 3 ? kTaps3 : 1;
-  const int64_t total = static_cast<int64_t>(K) * cin * cout;
-  const int B = 256;
-  const unsigned grid = static_cast<unsigned>((total + B - 1) / B);
-  const _Float16* w = reinterpret_cast<const _Float16*>(W);
-  _Float16* p = reinterpret_cast<_Float16*>(Wp);
-  if (use_mfma(cin_t, cout_t))
-    k_prepare_mfma<<<static_cast<unsigned>((total / 8 + B - 1) / B), B, 0, stream>>>(w, K, cin_t,
-                                                                                    cout_t, grad, p);
-  else
-    k_prepare_plain<<<grid, B, 0, stream>>>(w, K, cin_t, cout_t, grad, p);
-  SUBMCONV_HIP_CHECK(hipGetLastError());
+  Weights w;
+  SUBMCONV_HIP_CHECK(hipGetDevice(&w.device));
+  w.ksize = ksize;
+  w.cin = cin;
+  w.cout = cout;
+  w.dtype = dtype;
+  w.flags = flags;
+  const size_t bytes = static_cast<size_t>(ksize == 3 ? kTaps3 : 1) * cin * cout * 2;
+  SUBMCONV_HIP_CHECK(hipMalloc(&w.buf, bytes));
+  *out = new submconv_weights_s{w};
   return SUBMCONV_OK;
 }
 
-extern "C" int submconv_prepare_weights(const uint16_t* W, int32_t ksize, int32_t cin,
-                                        int32_t cout, uint16_t* Wp, hipStream_t stream) {
-  return submconv_prepare_weights_ex(W, ksize, cin, cout, 0u, Wp, stream);
+extern "C" int submconv_weights_set(submconv_weights_t h, const uint16_t* W, hipStream_t stream) {
+  clear_error();
+  if (!h || !W) return set_error(SUBMCONV_ERR_INVALID_ARG, "weights or W is NULL");
+  if (reinterpret_cast<uintptr_t>(W) & 15)
+    return set_error(SUBMCONV_ERR_INVALID_ARG, "W must be 16-byte aligned");
+  const Weights& w = h->w;
+  int dev = -1;
+  SUBMCONV_HIP_CHECK(hipGetDevice(&dev));
+  if (dev != w.device)
+    return set_error(SUBMCONV_ERR_INVALID_ARG,
+                     "the weights are on device %d, the current device is %d", w.device, dev);
+  return prepare_into(reinterpret_cast<const _Float16*>(W), w.ksize == 3 ? kTaps3 : 1, w.cin,
+                      w.cout, w.flags & SUBMCONV_PREP_INPUT_GRAD, w.buf, stream);
 }
 
-extern "C" int submconv_forward_dtype(submconv_map_t map, const uint16_t* feats_u16,
-                                      const uint16_t* Wp, const float* bias, uint16_t* out_u16,
-                                      int32_t cin, int32_t cout, int32_t ksize, int32_t dtype,
-                                      hipStream_t stream) {
+extern "C" int submconv_weights_free(submconv_weights_t h) {
   clear_error();
+  if (!h) return SUBMCONV_OK;
+  const hipError_t e = hipFree(h->w.buf);
+  delete h;
+  SUBMCONV_HIP_CHECK(e);
+  return SUBMCONV_OK;
+}
+
+// One forward of cin -> cout channels on weights W (the layer's, grad for an
+// input gradient) or on a prepared handle's buffer.
+static int forward_entry(submconv_map_t map, const uint16_t* feats_u16, const uint16_t* W,
+                         const float* bias, uint16_t* out_u16, int32_t cin, int32_t cout,
+                         int32_t ksize, int32_t dtype, bool grad, bool prepared,
+                         hipStream_t stream) {
   if (!map) return set_error(SUBMCONV_ERR_INVALID_ARG, "map is NULL");
   if (dtype != SUBMCONV_DTYPE_F16 && dtype != SUBMCONV_DTYPE_BF16)
     return set_error(SUBMCONV_ERR_INVALID_ARG, "dtype = %d is not fp16 (0) or bf16 (1)", dtype);
@@ -918,38 +1080,82 @@ extern "C" int submconv_forward_dtype(submconv_map_t map, const uint16_t* feats_
   if (st != SUBMCONV_OK) return st;
   const Map& m = map->m;
   if (m.n == 0) return SUBMCONV_OK;
-  if (!feats_u16 || !Wp || !out_u16)
-    return set_error(SUBMCONV_ERR_INVALID_ARG, "feats, Wp or out is NULL");
-  if ((reinterpret_cast<uintptr_t>(feats_u16) | reinterpret_cast<uintptr_t>(Wp) |
-       reinterpret_cast<uintptr_t>(out_u16)) & 15)
-    return set_error(SUBMCONV_ERR_INVALID_ARG, "feats, Wp and out must be 16-byte aligned");
+  const int cs = check_call(m, feats_u16, W, out_u16, bias);
+  if (cs != SUBMCONV_OK) return cs;
   const _Float16* feats = reinterpret_cast<const _Float16*>(feats_u16);
-  const _Float16* wp = reinterpret_cast<const _Float16*>(Wp);
+  const _Float16* w = reinterpret_cast<const _Float16*>(W);
   _Float16* out = reinterpret_cast<_Float16*>(out_u16);
+  if (prepared) {
+    if (dtype == SUBMCONV_DTYPE_BF16)
+      return forward_typed<true>(m, ksize, cin, cout, feats, w, false, bias, out, stream);
+    return forward_typed<false>(m, ksize, cin, cout, feats, w, false, bias, out, stream);
+  }
   if (dtype == SUBMCONV_DTYPE_BF16)
-    return forward_typed<true>(m, ksize, cin, cout, feats, wp, bias, out, stream);
-  return forward_typed<false>(m, ksize, cin, cout, feats, wp, bias, out, stream);
+    return forward_raw<true>(m, ksize, cin, cout, feats, w, grad, bias, out, stream);
+  return forward_raw<false>(m, ksize, cin, cout, feats, w, grad, bias, out, stream);
 }
 
-extern "C" int submconv_forward(submconv_map_t map, const uint16_t* feats_u16, const uint16_t* Wp,
-                                const float* bias, uint16_t* out_u16, int32_t cin, int32_t cout,
+extern "C" int submconv_forward_dtype(submconv_map_t map, const uint16_t* feats,
+                                      const uint16_t* W, const float* bias, uint16_t* out,
+                                      int32_t cin, int32_t cout, int32_t ksize, int32_t dtype,
+                                      hipStream_t stream) {
+  clear_error();
+  return forward_entry(map, feats, W, bias, out, cin, cout, ksize, dtype, false, false, stream);
+}
+
+extern "C" int submconv_forward(submconv_map_t map, const uint16_t* feats, const uint16_t* W,
+                                const float* bias, uint16_t* out, int32_t cin, int32_t cout,
                                 int32_t ksize, hipStream_t stream) {
-  return submconv_forward_dtype(map, feats_u16, Wp, bias, out_u16, cin, cout, ksize,
-                                SUBMCONV_DTYPE_F16, stream);
+  clear_error();
+  return forward_entry(map, feats, W, bias, out, cin, cout, ksize, SUBMCONV_DTYPE_F16, false,
+                       false, stream);
+}
+
+extern "C" int submconv_forward_prepared(submconv_map_t map, const uint16_t* feats,
+                                         submconv_weights_t h, const float* bias, uint16_t* out,
+                                         hipStream_t stream) {
+  clear_error();
+  if (!h) return set_error(SUBMCONV_ERR_INVALID_ARG, "weights is NULL");
+  const Weights& w = h->w;
+  if (w.flags & SUBMCONV_PREP_INPUT_GRAD)
+    return set_error(SUBMCONV_ERR_INVALID_ARG,
+                     "these weights are prepared for the input gradient, not the forward");
+  if (map && map->m.device != w.device)
+    return set_error(SUBMCONV_ERR_INVALID_ARG, "the map is on device %d, the weights on %d",
+                     map->m.device, w.device);
+  return forward_entry(map, feats, reinterpret_cast<const uint16_t*>(w.buf), bias, out, w.cin,
+                       w.cout, w.ksize, w.dtype, false, true, stream);
 }
 
 extern "C" int submconv_backward_input_dtype(submconv_map_t map, const uint16_t* grad_out,
-                                             const uint16_t* Wp_grad, uint16_t* grad_in,
-                                             int32_t cin, int32_t cout, int32_t ksize,
-                                             int32_t dtype, hipStream_t stream) {
+                                             const uint16_t* W, uint16_t* grad_in, int32_t cin,
+                                             int32_t cout, int32_t ksize, int32_t dtype,
+                                             hipStream_t stream) {
+  clear_error();
   // the forward with the flipped, transposed kernel, cout -> cin channels
-  return submconv_forward_dtype(map, grad_out, Wp_grad, nullptr, grad_in, cout, cin, ksize, dtype,
-                                stream);
+  return forward_entry(map, grad_out, W, nullptr, grad_in, cout, cin, ksize, dtype, true, false,
+                       stream);
 }
 
 extern "C" int submconv_backward_input(submconv_map_t map, const uint16_t* grad_out,
-                                       const uint16_t* Wp_grad, uint16_t* grad_in, int32_t cin,
+                                       const uint16_t* W, uint16_t* grad_in, int32_t cin,
                                        int32_t cout, int32_t ksize, hipStream_t stream) {
-  return submconv_backward_input_dtype(map, grad_out, Wp_grad, grad_in, cin, cout, ksize,
+  return submconv_backward_input_dtype(map, grad_out, W, grad_in, cin, cout, ksize,
                                        SUBMCONV_DTYPE_F16, stream);
+}
+
+extern "C" int submconv_backward_input_prepared(submconv_map_t map, const uint16_t* grad_out,
+                                                submconv_weights_t h, uint16_t* grad_in,
+                                                hipStream_t stream) {
+  clear_error();
+  if (!h) return set_error(SUBMCONV_ERR_INVALID_ARG, "weights is NULL");
+  const Weights& w = h->w;
+  if (!(w.flags & SUBMCONV_PREP_INPUT_GRAD))
+    return set_error(SUBMCONV_ERR_INVALID_ARG,
+                     "these weights are prepared for the forward, not the input gradient");
+  if (map && map->m.device != w.device)
+    return set_error(SUBMCONV_ERR_INVALID_ARG, "the map is on device %d, the weights on %d",
+                     map->m.device, w.device);
+  return forward_entry(map, grad_out, reinterpret_cast<const uint16_t*>(w.buf), nullptr, grad_in,
+                       w.cout, w.cin, w.ksize, w.dtype, false, true, stream);
 }

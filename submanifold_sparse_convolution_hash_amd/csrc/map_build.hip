@@ -588,6 +588,11 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
     *out_map = new submconv_map_s{m};
     return SUBMCONV_OK;
   }
+  {
+    // the forwards on this map that take W as it is stage it here
+    const int st = ensure_weight_stage(m.device);
+    if (st != SUBMCONV_OK) return st;
+  }
 
   int64_t cap = 64;
   while (cap < 2 * n) cap <<= 1;

@@ -357,11 +357,16 @@ extern "C" int64_t submconv_masked_row_taps(submconv_masked_t plan) {
 }
 
 extern "C" int submconv_forward_masked(submconv_masked_t plan, const uint16_t* feats,
-                                       const uint16_t* Wp, const float* bias, uint16_t* out,
-                                       int32_t cin, int32_t cout, hipStream_t stream) {
+                                       submconv_weights_t wh, const float* bias, uint16_t* out,
+                                       hipStream_t stream) {
   clear_error();
-  if (!plan) return set_error(SUBMCONV_ERR_INVALID_ARG, "plan is NULL");
+  if (!plan || !wh) return set_error(SUBMCONV_ERR_INVALID_ARG, "plan or weights is NULL");
   const MaskedPlan& p = plan->p;
+  const Weights& W = wh->w;
+  const int cin = W.cin, cout = W.cout;
+  if (W.ksize != 3 || W.dtype != SUBMCONV_DTYPE_F16 || (W.flags & SUBMCONV_PREP_INPUT_GRAD))
+    return set_error(SUBMCONV_ERR_INVALID_ARG,
+                     "masked forward: the weights must be fp16, 3x3x3, prepared for the forward");
   // the shapes whose prepared weights are in MFMA fragment order
   if (!(((cin == 32 || cin == 64 || cin == 128) && cout % 32 == 0) || (cin == 256 && cout % 128 == 0)) ||
       cout > 1024)
@@ -369,14 +374,20 @@ extern "C" int submconv_forward_masked(submconv_masked_t plan, const uint16_t* f
                      "masked forward: Cin in {32, 64, 128} with Cout a multiple of 32, or Cin 256 "
                      "with Cout a multiple of 128 (got %d, %d)", cin, cout);
   if (p.n == 0) return SUBMCONV_OK;
-  if (!feats || !Wp || !out) return set_error(SUBMCONV_ERR_INVALID_ARG, "feats, Wp or out is NULL");
-  if ((reinterpret_cast<uintptr_t>(feats) | reinterpret_cast<uintptr_t>(Wp) |
-       reinterpret_cast<uintptr_t>(out)) & 15)
-    return set_error(SUBMCONV_ERR_INVALID_ARG, "feats, Wp and out must be 16-byte aligned");
+  if (!feats || !out) return set_error(SUBMCONV_ERR_INVALID_ARG, "feats or out is NULL");
+  if ((reinterpret_cast<uintptr_t>(feats) | reinterpret_cast<uintptr_t>(out) |
+       reinterpret_cast<uintptr_t>(bias)) & 15)
+    return set_error(SUBMCONV_ERR_INVALID_ARG, "feats, out and bias must be 16-byte aligned");
+  int dev = -1;
+  SUBMCONV_HIP_CHECK(hipGetDevice(&dev));
+  if (dev != W.device || dev != p.device)
+    return set_error(SUBMCONV_ERR_INVALID_ARG,
+                     "plan (device %d), weights (device %d) and the current device (%d) differ",
+                     p.device, W.device, dev);
   if (p.n * cin * 2 >= (int64_t{1} << 31) - 64)
     return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "features beyond 2 GiB");
   const _Float16* f = reinterpret_cast<const _Float16*>(feats);
-  const _Float16* w = reinterpret_cast<const _Float16*>(Wp);
+  const _Float16* w = W.buf;
   _Float16* o = reinterpret_cast<_Float16*>(out);
   switch (cin) {
     case 32: return dispatch_masked<32>(p, f, w, bias, o, cout, stream);

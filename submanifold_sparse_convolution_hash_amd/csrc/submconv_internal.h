@@ -42,8 +42,8 @@ __host__ __device__ inline int tap_at(int p) {
 //           as well (wide.n == 0: none); a forward takes them when they fit
 //           its workgroups into fewer rounds.
 // One tiling (tiles of `rows` consecutive processing rows):
-//  cnt  [n][27] uint16, entries per processing position p.
-//  off  [n + 1] int32, first entry of each tile.
+//  cnt  [n_tiles][27] uint16, entries per processing position p.
+//  off  [n_tiles + 1] int32, first entry of each tile.
 //  ent  [active_pairs + 1] int2 {caller row of the neighbour, row in tile},
 //       ordered by (tile, position p, row in tile), then one entry {-1, -1}
 //       that masked lanes load instead of selecting -1.
@@ -74,6 +74,20 @@ struct Map {
   bool wide_always = false;  // forwards take the wide tiles whenever their kernel can
 };
 
+// Prepared weights of one layer (W [K][cin][cout]): the MFMA fragment order
+// for shapes the MFMA kernels take, else W_t[k][ci][co] of the forward they
+// serve (flipped and transposed under SUBMCONV_PREP_INPUT_GRAD).
+struct Weights {
+  int device = 0;
+  int ksize = 3, cin = 0, cout = 0, dtype = SUBMCONV_DTYPE_F16;
+  uint32_t flags = 0;
+  _Float16* buf = nullptr;  // K * cin * cout elements, library-owned
+};
+
+// Allocates the device's staging buffer for weights passed as the caller
+// holds them (once per device; every map build calls it).
+int ensure_weight_stage(int device);
+
 // Records a thread-local message and returns `status`.
 int set_error(int status, const char* fmt, ...);
 void clear_error();
@@ -83,6 +97,10 @@ const char* last_error_cstr();
 
 struct submconv_map_s {
   submconv::Map m;
+};
+
+struct submconv_weights_s {
+  submconv::Weights w;
 };
 
 #define SUBMCONV_HIP_CHECK(expr)                                                              \

@@ -29,7 +29,8 @@ def lib():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ["submconv_build_map", "submconv_forward", "submconv_map_export", "submconv_map_free",
-              "submconv_prepare_weights", "submconv_map_active_pairs"]:
+              "submconv_weights_create", "submconv_weights_set", "submconv_forward_prepared",
+              "submconv_forward_kernel", "submconv_map_active_pairs"]:
         assert n in names
 
 
@@ -44,18 +45,23 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_host_only_entry_points(lib):
     lib.submconv_abi_version.restype = ctypes.c_int
-    assert lib.submconv_abi_version() == 1
+    assert lib.submconv_abi_version() == 2
     lib.submconv_status_string.restype = ctypes.c_char_p
     lib.submconv_status_string.argtypes = [ctypes.c_int]
     assert lib.submconv_status_string(0) == b"ok"
     assert lib.submconv_status_string(-3) == b"duplicate coordinate"
-    f = lib.submconv_prepared_weights_elems
-    f.restype = ctypes.c_int64
-    f.argtypes = [ctypes.c_int32] * 3
-    assert f(3, 128, 128) == 27 * 128 * 128
-    assert f(1, 32, 32) == 32 * 32
-    assert f(3, 12, 16) == -4   # Cin not a multiple of 8
-    assert f(2, 16, 16) == -1   # bad ksize
+    # weights handles: shape, dtype and flag errors before any device call
+    wc = lib.submconv_weights_create
+    wc.restype = ctypes.c_int
+    wc.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_uint32, ctypes.c_void_p]
+    h = ctypes.c_void_p()
+    assert wc(3, 12, 16, 0, 0, ctypes.byref(h)) == -4   # Cin not a multiple of 8
+    assert wc(2, 16, 16, 0, 0, ctypes.byref(h)) == -1   # bad ksize
+    assert wc(3, 16, 16, 2, 0, ctypes.byref(h)) == -1   # bad dtype
+    assert wc(3, 16, 16, 0, 2, ctypes.byref(h)) == -1   # unknown flag
+    assert wc(3, 16, 16, 0, 0, None) == -1              # no handle pointer
+    lib.submconv_weights_free.restype = ctypes.c_int
+    assert lib.submconv_weights_free(None) == 0
     # argument errors are reported before any device work
     lib.submconv_build_map.restype = ctypes.c_int
     lib.submconv_build_map.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
@@ -72,6 +78,33 @@ def test_host_only_entry_points(lib):
     assert lib.submconv_forward(None, None, None, None, None, 8, 8, 3, None) == -1  # map NULL
     lib.submconv_map_free.restype = ctypes.c_int
     assert lib.submconv_map_free(None) == 0
+
+
+def test_forward_kernel_choice_and_buffer_limit(lib):
+    """Which kernel a forward takes, decided on the host: the MFMA gather-GEMM
+    for its channel counts while features and lists stay below 2 GiB (its
+    32-bit buffer offsets), an explicit SUBMCONV_ERR_UNSUPPORTED_SHAPE above,
+    the VALU kernel for other channel counts (64-bit addressing, no limit)."""
+    f = lib.submconv_forward_kernel
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    assert f(209715, 744981, 128, 128, 3) == 1
+    assert f(1495574, 31_200_000, 64, 32, 3) == 1
+    assert f(1000, 4000, 256, 256, 1) == 1
+    assert f(1000, 4000, 96, 96, 3) == 0        # no MFMA tile for 96 channels
+    assert f(1000, 4000, 256, 64, 3) == 0       # Cin 256 needs Cout a multiple of 128
+    limit = 2 ** 31 - 64
+    n_ok = limit // (256 * 2)                   # the last row count below the limit
+    assert f(n_ok, 10, 256, 256, 3) == 1
+    assert f(n_ok + 1, 10, 256, 256, 3) == -4
+    assert f(n_ok + 1, 10, 96, 96, 3) == 0      # the VALU kernel has no such limit
+    p_ok = limit // 8 - 1                       # (pairs + 1) * 8 at the limit
+    assert f(1000, p_ok, 128, 128, 3) == 1
+    assert f(1000, p_ok + 1, 128, 128, 3) == -4
+    assert f(1000, p_ok + 1, 128, 128, 1) == 1  # a 1x1x1 layer reads no lists
+    assert f(1000, 10, 12, 16, 3) == -4         # shape errors as the forward
+    assert f(1000, 10, 16, 16, 2) == -1
+    assert f(-1, 10, 16, 16, 3) == -1
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

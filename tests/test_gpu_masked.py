@@ -110,6 +110,8 @@ def test_masked_dense_map_with_isolated_tiles(dev, cin, cout):
     out = sc.forward_masked(plan, _to(dev, feats), _to(dev, W), _to(dev, bias)).float().cpu().numpy()
     rows = np.concatenate([np.arange(iso0 * 256 - 300, (iso0 + n_iso) * 256 + 300, 7),
                            rng.choice(n, 1500, replace=False)])
-    ref = oc.submconv_rows(km.export().cpu().numpy(), feats, W, bias, rows)
+    kmap = oc.kernel_map(coords, (G, G, G), 1, 3)
+    np.testing.assert_array_equal(km.export().cpu().numpy(), kmap)
+    ref = oc.submconv_rows(kmap, feats, W, bias, rows)
     _assert_close(out[rows], ref, "masked, isolated tiles")
     km.free()

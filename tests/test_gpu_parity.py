@@ -5,6 +5,8 @@ Features: |gpu - oracle| <= 1e-3 + 1e-2 |oracle| per element, the tolerance
 fixed for this operation (fp16 inputs, fp32 accumulation, one fp16 rounding:
 the rounding alone is 2^-11 relative, well inside it).
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -257,12 +259,13 @@ def test_bitwise_determinism_and_morton_order(dev):
     # run to run: bit for bit (fixed accumulation order, no atomics)
     assert torch.equal(a, b)
     assert torch.equal(c, c2)
-    # the processing order changes only which rows share a tile, hence the
-    # fp32 summation order of some rows: same map, outputs within tolerance
+    # the processing order changes which rows share a tile, not the order in
+    # which a row's terms are added (the centre first, then the other taps in
+    # a fixed order): the same map and the same outputs bit for bit
     assert torch.equal(km0.export(), km1.export())
-    ref = oc.submconv_rows(km0.export().cpu().numpy(), wl.feats, L.W, None)
+    assert torch.equal(a, c)
+    ref = oc.submconv_rows(oc.kernel_map(wl.coords, wl.grid, wl.batch, 3), wl.feats, L.W, None)
     _assert_close(a.float().cpu().numpy(), ref, "raster order")
-    _assert_close(c.float().cpu().numpy(), ref, "morton order")
     assert not torch.equal(km1.order().cpu(), torch.arange(wl.n, dtype=torch.int32))
 
 
@@ -291,11 +294,12 @@ def test_batch_items_are_independent(dev):
     # no neighbour crosses the batch items
     assert (kmap[:wl.n][kmap[:wl.n] >= 0] < wl.n).all() and (kmap[wl.n:][kmap[wl.n:] >= 0] >= wl.n).all()
     out = sc.forward(km, _to(dev, np.concatenate([wl.feats, wl.feats])), _to(dev, L.W), _to(dev, L.bias))
-    # both items equal the single-item result (the items sit in different
-    # tiles, so their fp32 summation order may differ: compare to tolerance)
+    # the two items sit in different tiles; each row's terms are still added
+    # in the same order, so the items' outputs are equal bit for bit, and
+    # both equal the single-item result to tolerance
+    assert torch.equal(out[:wl.n], out[wl.n:])
     ref = oc.submconv_rows(op.kernel_map(wl.coords, wl.grid), wl.feats, L.W, L.bias)
     _assert_close(out[:wl.n].float().cpu().numpy(), ref, "item 0")
-    _assert_close(out[wl.n:].float().cpu().numpy(), ref, "item 1")
 
 
 @gpu
@@ -307,8 +311,14 @@ def test_prepared_weights_and_module(dev):
     feats = _to(dev, wl.feats)
     ref = sc.forward(km, feats, _to(dev, L.W), _to(dev, L.bias))
     wp = sc.prepare_weights(_to(dev, L.W))
-    again = sc.forward(km, feats, bias=_to(dev, L.bias), prepared=wp, ksize=3, cout=128)
+    again = sc.forward(km, feats, bias=_to(dev, L.bias), prepared=wp)
     assert torch.equal(ref, again)
+    # new values into the same handle
+    W2 = _to(dev, (L.W * 0.5).astype(np.float16))
+    wp.set(W2)
+    assert torch.equal(sc.forward(km, feats, bias=_to(dev, L.bias), prepared=wp),
+                       sc.forward(km, feats, W2, _to(dev, L.bias)))
+    wp.free()
     mod = sc.SubMConv3d(64, 128, 3, bias=True, device=dev)
     with torch.no_grad():
         mod.weight.copy_(_to(dev, L.W))
@@ -346,11 +356,36 @@ def test_errors(dev):
         sc.forward(km, torch.zeros((2, 12), dtype=torch.float16, device=dev),
                    torch.zeros((27, 12, 16), dtype=torch.float16, device=dev))
     assert e.value.status == -4
-    with pytest.raises(sc.SubmconvError) as e:
-        sc.forward(km, torch.zeros((2, 16), dtype=torch.float16, device=dev),
-                   bias=None, prepared=torch.zeros(27 * 16 * 16, dtype=torch.float16, device=dev),
-                   ksize=2, cout=16)
-    assert e.value.status == -1
+    # prepared weights carry their use: input-gradient weights are refused by
+    # the forward, forward weights by the input gradient (checked in the
+    # library, through the C ABI)
+    lib = sc.load_library()
+    W16 = torch.zeros((27, 16, 16), dtype=torch.float16, device=dev)
+    wg = sc.Weights(W16, input_grad=True)
+    wf = sc.Weights(W16)
+    f16 = torch.zeros((2, 16), dtype=torch.float16, device=dev)
+    o16 = torch.zeros((2, 16), dtype=torch.float16, device=dev)
+    st = sc._stream(dev)
+    assert lib.submconv_forward_prepared(km.handle, sc._ptr(f16), wg.handle, None, sc._ptr(o16),
+                                         st) == -1
+    assert lib.submconv_backward_input_prepared(km.handle, sc._ptr(f16), wf.handle, sc._ptr(o16),
+                                                st) == -1
+    assert lib.submconv_forward_prepared(km.handle, sc._ptr(f16), wf.handle, None, sc._ptr(o16),
+                                         st) == 0
+    # a misaligned bias is refused before launch
+    b = torch.zeros(20, dtype=torch.float32, device=dev)
+    assert lib.submconv_forward(km.handle, sc._ptr(f16), sc._ptr(W16), ctypes.c_void_p(b.data_ptr() + 4),
+                                sc._ptr(o16), 16, 16, 3, st) == -1
+    # the binding checks shapes and dtypes of out and bias
+    with pytest.raises(ValueError):
+        sc.forward(km, f16, W16, torch.zeros(15, dtype=torch.float32, device=dev))
+    with pytest.raises(TypeError):
+        sc.forward(km, f16, W16, torch.zeros(16, dtype=torch.float16, device=dev))
+    with pytest.raises(ValueError):
+        sc.forward(km, f16, W16, out=torch.zeros((2, 8), dtype=torch.float16, device=dev))
+    torch.cuda.synchronize(dev)
+    wg.free()
+    wf.free()
 
 
 def _blob_sites(rng, grid, batch, corners, side=10, occ=0.35):
@@ -435,7 +470,9 @@ def test_dense_map_with_isolated_tiles(dev, cin, cout, side, iso0, n_iso, checke
     km = sc.build_map(_to(dev, coords), (G, G, G), 1)
     assert km.tile_rows == 256  # dense: no wider tiles
     out = sc.forward(km, _to(dev, feats), _to(dev, W), None).float().cpu().numpy()
-    kmap = km.export().cpu().numpy()
+    # the reference uses the oracle's own map, which the GPU's must equal
+    kmap = oc.kernel_map(coords, (G, G, G), 1, 3)
+    np.testing.assert_array_equal(km.export().cpu().numpy(), kmap)
     # the isolated rows see only themselves
     assert (kmap[iso0 * 256:(iso0 + n_iso) * 256] >= 0).sum() == n_iso * 256
     rows = (np.arange(per_xcd)[:, None] * 256 + np.arange(checked)[None, :]).reshape(-1)
@@ -728,8 +765,8 @@ def test_two_streams_share_a_map(dev):
     fb = _to(dev, rng.standard_normal((wl.n, 64)).astype(np.float16))
     W, b = _to(dev, L.W), _to(dev, L.bias)
     wp = sc.prepare_weights(W)
-    ra = sc.forward(km, fa, prepared=wp, bias=b, ksize=3, cout=64)
-    rb = sc.forward(km, fb, prepared=wp, bias=b, ksize=3, cout=64)
+    ra = sc.forward(km, fa, prepared=wp, bias=b)
+    rb = sc.forward(km, fb, prepared=wp, bias=b)
     oa = torch.empty_like(ra)
     ob = torch.empty_like(rb)
     s1, s2 = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
@@ -737,9 +774,9 @@ def test_two_streams_share_a_map(dev):
     s2.wait_stream(torch.cuda.current_stream(dev))
     for _ in range(4):
         with torch.cuda.stream(s1):
-            sc.forward(km, fa, prepared=wp, bias=b, ksize=3, cout=64, out=oa)
+            sc.forward(km, fa, prepared=wp, bias=b, out=oa)
         with torch.cuda.stream(s2):
-            sc.forward(km, fb, prepared=wp, bias=b, ksize=3, cout=64, out=ob)
+            sc.forward(km, fb, prepared=wp, bias=b, out=ob)
     torch.cuda.current_stream(dev).wait_stream(s1)
     torch.cuda.current_stream(dev).wait_stream(s2)
     torch.cuda.synchronize(dev)
@@ -763,19 +800,82 @@ def test_forward_in_a_captured_graph(dev):
     side.wait_stream(torch.cuda.current_stream(dev))
     with torch.cuda.stream(side):
         for _ in range(2):
-            sc.forward(km, feats, prepared=wp, ksize=3, cout=128, out=out)
+            sc.forward(km, feats, prepared=wp, out=out)
     torch.cuda.current_stream(dev).wait_stream(side)
     torch.cuda.synchronize(dev)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        sc.forward(km, feats, prepared=wp, ksize=3, cout=128, out=out)
+        sc.forward(km, feats, prepared=wp, out=out)
     rng = np.random.default_rng(1204)
     for rep in range(3):
         feats.copy_(_to(dev, rng.standard_normal((wl.n, 128)).astype(np.float16)))
         torch.cuda.synchronize(dev)
         g.replay()
         torch.cuda.synchronize(dev)
-        ref = sc.forward(km, feats, prepared=wp, ksize=3, cout=128)
+        ref = sc.forward(km, feats, prepared=wp)
         torch.cuda.synchronize(dev)
         assert torch.equal(out, ref), f"replay {rep}"
+    km.free()
+
+
+# ----------------------------------------------------------------------------
+# the MFMA kernel's 32-bit buffer offsets: largest features below 2 GiB, and
+# an explicit error above (no silent change of kernel)
+# ----------------------------------------------------------------------------
+
+
+@gpu
+@pytest.mark.slow
+def test_features_at_the_2gib_limit(dev):
+    """256 input channels on 4,194,303 rows: features of 2 GiB - 512 bytes,
+    the largest the MFMA gather-GEMM addresses (row offsets up to bit 30),
+    checked on sampled rows against the oracle on the oracle's own map. One
+    row more reaches 2 GiB: the forward, the input gradient and the weight
+    gradient return SUBMCONV_ERR_UNSUPPORTED_SHAPE before launching anything
+    (tiny placeholder buffers, since nothing is read)."""
+    sc = _sc()
+    lib = sc.load_library()
+    G, cin, cout = 256, 256, 128
+    n_ok = (2 ** 31 - 64) // (cin * 2)
+    assert n_ok * cin * 2 <= 2 ** 31 - 64 < (n_ok + 1) * cin * 2
+    rng = np.random.default_rng(2024)
+    lin = np.sort(rng.choice(G ** 3, n_ok + 1, replace=False))
+    xyz = np.stack([lin // (G * G), (lin // G) % G, lin % G], axis=1).astype(np.int32)
+    coords = np.ascontiguousarray(np.concatenate([np.zeros((n_ok + 1, 1), np.int32), xyz], axis=1))
+    _say(f"[2 GiB] N={n_ok} Cin={cin}: {n_ok * cin * 2} feature bytes")
+    # above: one more row
+    km_big = sc.build_map(_to(dev, coords), (G, G, G), 1)
+    with pytest.raises(sc.SubmconvError) as e:
+        sc.forward_kernel(km_big.num_rows, km_big.active_pairs(3), cin, cout, 3)
+    assert e.value.status == -4
+    tiny = torch.zeros(64, dtype=torch.float16, device=dev)
+    tw = torch.zeros(27 * cin * cout, dtype=torch.float16, device=dev)
+    st = sc._stream(dev)
+    assert lib.submconv_forward(km_big.handle, sc._ptr(tiny), sc._ptr(tw), None, sc._ptr(tiny),
+                                cin, cout, 3, st) == -4
+    assert lib.submconv_backward_input(km_big.handle, sc._ptr(tiny), sc._ptr(tw), sc._ptr(tiny),
+                                       cout, cin, 3, st) == -4
+    assert lib.submconv_backward_weight(km_big.handle, sc._ptr(tiny), sc._ptr(tiny), sc._ptr(tw),
+                                        sc._ptr(tiny), cin, cout, 3, st) == -4
+    torch.cuda.synchronize(dev)
+    km_big.free()
+    # just below: the largest features the kernel takes
+    coords = np.ascontiguousarray(coords[:n_ok])
+    km = sc.build_map(_to(dev, coords), (G, G, G), 1)
+    g = torch.Generator(device=dev)
+    g.manual_seed(2025)
+    feats = torch.randn((n_ok, cin), generator=g, device=dev, dtype=torch.float32).to(torch.float16)
+    W = (rng.standard_normal((27, cin, cout)) / np.sqrt(27 * cin)).astype(np.float16)
+    out = sc.forward(km, feats, _to(dev, W))
+    kmap = oc.kernel_map(coords, (G, G, G), 1, 3)
+    rows = np.concatenate([rng.choice(n_ok, 1500, replace=False), [0, n_ok - 1]])
+    # the oracle on the sampled rows and their neighbours only: a compact map
+    sub = kmap[rows]
+    need = np.unique(sub[sub >= 0])
+    f_sub = feats[torch.from_numpy(need.astype(np.int64)).to(dev)].cpu().numpy()
+    sub_c = np.where(sub >= 0, np.searchsorted(need, np.maximum(sub, 0)), -1).astype(np.int32)
+    ref = oc.submconv_rows(sub_c, f_sub, W, None)
+    got = out[torch.from_numpy(rows).to(dev)].float().cpu().numpy()
+    _assert_close(got, ref, "2 GiB features, sampled rows")
+    np.testing.assert_array_equal(km.export()[torch.from_numpy(rows).to(dev)].cpu().numpy(), sub)
     km.free()
