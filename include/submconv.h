@@ -336,6 +336,26 @@ int submconv_backward_weight(submconv_map_t map, const uint16_t* feats, const ui
                              int32_t ksize, hipStream_t stream);
 
 /*
+ * submconv_backward_weight_noalloc -- submconv_backward_weight for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same kernels, with the
+ * partial sums in a fixed 32 MiB workspace that is part of the library's
+ * device code (one per device, held until the process ends) instead of a
+ * caller's workspace. When the partials of the allocating entry point's work
+ * split would not fit, workgroups take longer runs of tiles (down to one run
+ * per tap), so every shape fits; the sum order then differs from
+ * submconv_backward_weight's (the same tolerance, not the same bits).
+ * Arguments, requirements and results as submconv_backward_weight. The call
+ * never allocates, frees or calls an allocating library routine. All calls on
+ * one device share its workspace, which keeps the last call's contents: calls
+ * that overlap in time on one device (several streams or threads) race and
+ * must be ordered by the caller. Asynchronous on `stream`.
+ */
+int submconv_backward_weight_noalloc(submconv_map_t map, const uint16_t* feats,
+                                     const uint16_t* grad_out, float* grad_w, int32_t cin,
+                                     int32_t cout, int32_t ksize, hipStream_t stream);
+
+/*
  * submconv_backward_bias -- gradient with respect to the bias: grad_b[c] =
  * sum over the n rows of grad_out[row][c] (fp16 in, fp32 accumulation and
  * result), summed in a fixed order (bitwise reproducible). grad_out [n,Cout]

@@ -79,6 +79,7 @@ def load_library():
         "submconv_backward_input_prepared": ([P, P, P, P, P], ctypes.c_int),
         "submconv_backward_weight_workspace_bytes": ([P, I32, I32, I32], I64),
         "submconv_backward_weight": ([P, P, P, P, P, I32, I32, I32, P], ctypes.c_int),
+        "submconv_backward_weight_noalloc": ([P, P, P, P, I32, I32, I32, P], ctypes.c_int),
         "submconv_backward_bias": ([P, I64, I32, P, P], ctypes.c_int),
         "submconv_downsample_plan": ([P, I64, I32, P, P, P], ctypes.c_int),
         "submconv_downsample_rows": ([P], I64),
@@ -391,9 +392,12 @@ def backward_input(kmap: KernelMap, grad_out: torch.Tensor, W: Optional[torch.Te
 
 
 def backward_weight(kmap: KernelMap, feats: torch.Tensor, grad_out: torch.Tensor,
-                    ksize: int = 3, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                    ksize: int = 3, out: Optional[torch.Tensor] = None,
+                    no_alloc: bool = False) -> torch.Tensor:
     """Weight gradient ``[K,Cin,Cout]`` fp32 from the layer input ``feats``
-    ([N,Cin] fp16) and the output gradient ``grad_out`` ([N,Cout] fp16)."""
+    ([N,Cin] fp16) and the output gradient ``grad_out`` ([N,Cout] fp16).
+    ``no_alloc`` takes ``submconv_backward_weight_noalloc`` (the library's
+    fixed per-device workspace instead of a workspace tensor)."""
     _require(feats, "feats", torch.float16, 2)
     _require(grad_out, "grad_out", torch.float16, 2)
     n, cin = feats.shape
@@ -402,6 +406,18 @@ def backward_weight(kmap: KernelMap, feats: torch.Tensor, grad_out: torch.Tensor
         raise ValueError("feats and grad_out must have the map's rows")
     K = 27 if ksize == 3 else 1
     lib = load_library()
+    if no_alloc:
+        if out is None:
+            out = torch.empty((K, cin, cout), dtype=torch.float32, device=feats.device)
+        else:
+            _require(out, "out", torch.float32, 3)
+            if tuple(out.shape) != (K, cin, cout):
+                raise ValueError("out must be [K,Cin,Cout]")
+        with torch.cuda.device(feats.device):
+            _check(lib.submconv_backward_weight_noalloc(kmap.handle, _ptr(feats), _ptr(grad_out),
+                                                        _ptr(out), cin, cout, int(ksize),
+                                                        _stream(feats.device)))
+        return out
     ws = int(lib.submconv_backward_weight_workspace_bytes(kmap.handle, cin, cout, int(ksize)))
     if ws < 0:
         _check(ws)

@@ -19,10 +19,19 @@
 #include <cmath>
 #include <tuple>
 #include <climits>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
 #include "submconv_internal.h"
+
+// Workspace of submconv_backward_weight_noalloc, for callers that cannot
+// allocate: device memory of the library's code object, one copy per device
+// from the time the library's kernels load on it until the process ends. In
+// host code the array's name is a stand-in, not a device address: host code
+// uses only the address hipGetSymbolAddress returns for the current device.
+constexpr size_t kNoAllocScratchBytes = size_t{32} << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 
 namespace submconv {
 namespace {
@@ -591,10 +600,12 @@ bool use_pp_w(int cin, int cout) {
 struct Runs {
   int runs, tpr;
 };
-// the old kernel: every position in the same runs of tpr tiles
-Runs runs_for(const Map& m, int K) {
+// the old kernel: every position in the same runs of tpr tiles (at most
+// max_blocks workgroups in all)
+Runs runs_for(const Map& m, int K, int64_t max_blocks = INT64_MAX) {
   const int64_t nt = m.tiles.n;
   int64_t runs = (kTargetBlocks + K - 1) / K;
+  if (runs > max_blocks / K) runs = max_blocks / K;
   if (runs > nt) runs = nt;
   if (runs < 1) runs = 1;
   const int64_t tpr = (nt + runs - 1) / runs;
@@ -622,7 +633,7 @@ int device_cus(int dev) {
 // most kBlocksPerCU per compute unit, all resident at once (a few blocks
 // more than the CUs hold at that count would make some CUs take a third).
 // Smaller workgroups: about kGroupsSmall groups each, many per CU.
-WSplit split_for(const Map& m, int K, int cin, int cout) {
+WSplit split_for(const Map& m, int K, int cin, int cout, int64_t max_blocks = INT64_MAX) {
   WSplit ws{};
   ws.np = K == kTaps3 ? kTaps3 : 1;
   const int64_t nt = m.tiles.n;
@@ -641,29 +652,36 @@ WSplit split_for(const Map& m, int K, int cin, int cout) {
     runs_of(g0, target, ws.runs0, ws.tpr0);
     if (ws.np > 1) runs_of(goff, target, ws.runs, ws.tpr);
   };
+  double target = kGroupsSmall;
   if (pp_waves(cin, cout) >= 4) {
     const int64_t cap = int64_t{device_cus(m.device)} * kBlocksPerCU;
-    double target = std::max(16.0, (g0 + off) / static_cast<double>(cap));
+    target = std::max(16.0, (g0 + off) / static_cast<double>(cap));
     fill(target);
     for (int it = 0; it < 200 && ws.blocks() > cap; ++it) {
       target *= 1.02;
       fill(target);
     }
   } else {
-    fill(kGroupsSmall);
+    fill(target);
+  }
+  // longer runs when the partials must fit a fixed workspace (down to one
+  // run per position)
+  for (int it = 0; it < 400 && ws.blocks() > max_blocks; ++it) {
+    target *= 1.05;
+    fill(target);
   }
   return ws;
 }
 
 template <int CIN, int COUT>
 int launch_w(const Map& m, int K, const _Float16* feats, const _Float16* grad_out, float* partial,
-             float* dw, hipStream_t stream) {
+             float* dw, int64_t max_blocks, hipStream_t stream) {
   const Tiles& T = m.tiles;
   const int32_t nt = static_cast<int32_t>(T.n), np = static_cast<int32_t>(m.active_pairs);
   if constexpr ((CIN == 32 || CIN == 64 || CIN == 128 || CIN == 256) &&
                 (COUT == 32 || COUT == 64 || COUT == 128 || COUT == 256)) {
     constexpr int NT = PCfg<CIN, COUT>::NT;
-    const WSplit ws = split_for(m, K, CIN, COUT);
+    const WSplit ws = split_for(m, K, CIN, COUT, max_blocks);
     const unsigned blocks = static_cast<unsigned>(ws.blocks());
     if (m.order)
       k_bwd_weight_pp<CIN, COUT, true><<<blocks, NT, 0, stream>>>(
@@ -676,7 +694,7 @@ int launch_w(const Map& m, int K, const _Float16* feats, const _Float16* grad_ou
     k_bwd_weight_reduce_pp<<<static_cast<unsigned>(ws.np * chunks), 64 * kRedStrands, 0, stream>>>(
         partial, ws, CIN, COUT, dw);
   } else {
-    const Runs r = runs_for(m, K);
+    const Runs r = runs_for(m, K, max_blocks);
     const int64_t total = static_cast<int64_t>(K) * CIN * COUT;
     k_bwd_weight<CIN, COUT><<<static_cast<unsigned>(r.runs * K), WCfg<CIN, COUT>::NT, 0, stream>>>(
         T.ent, T.off, T.cnt, m.order, m.n, nt, T.rows, K, r.tpr, feats, grad_out, partial, np);
@@ -690,46 +708,44 @@ int launch_w(const Map& m, int K, const _Float16* feats, const _Float16* grad_ou
 
 template <int CIN>
 int dispatch_w(const Map& m, int K, int cout, const _Float16* feats, const _Float16* grad_out,
-               float* partial, float* dw, hipStream_t stream) {
+               float* partial, float* dw, int64_t mb, hipStream_t stream) {
   switch (cout) {
-    case 32: return launch_w<CIN, 32>(m, K, feats, grad_out, partial, dw, stream);
-    case 64: return launch_w<CIN, 64>(m, K, feats, grad_out, partial, dw, stream);
-    case 96: return launch_w<CIN, 96>(m, K, feats, grad_out, partial, dw, stream);
-    case 128: return launch_w<CIN, 128>(m, K, feats, grad_out, partial, dw, stream);
-    case 160: return launch_w<CIN, 160>(m, K, feats, grad_out, partial, dw, stream);
-    case 192: return launch_w<CIN, 192>(m, K, feats, grad_out, partial, dw, stream);
-    case 224: return launch_w<CIN, 224>(m, K, feats, grad_out, partial, dw, stream);
-    case 256: return launch_w<CIN, 256>(m, K, feats, grad_out, partial, dw, stream);
+    case 32: return launch_w<CIN, 32>(m, K, feats, grad_out, partial, dw, mb, stream);
+    case 64: return launch_w<CIN, 64>(m, K, feats, grad_out, partial, dw, mb, stream);
+    case 96: return launch_w<CIN, 96>(m, K, feats, grad_out, partial, dw, mb, stream);
+    case 128: return launch_w<CIN, 128>(m, K, feats, grad_out, partial, dw, mb, stream);
+    case 160: return launch_w<CIN, 160>(m, K, feats, grad_out, partial, dw, mb, stream);
+    case 192: return launch_w<CIN, 192>(m, K, feats, grad_out, partial, dw, mb, stream);
+    case 224: return launch_w<CIN, 224>(m, K, feats, grad_out, partial, dw, mb, stream);
+    case 256: return launch_w<CIN, 256>(m, K, feats, grad_out, partial, dw, mb, stream);
     default: return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "internal: Cout = %d", cout);
   }
 }
 
-}  // namespace
-}  // namespace submconv
+// Workspace bytes of the weight gradient's partials with at most max_blocks
+// workgroups (0 for the VALU kernel, which needs none).
+int64_t workspace_bytes(const Map& m, int cin, int cout, int ksize, int64_t max_blocks) {
+  if (!use_mfma_w(cin, cout) || m.n == 0) return 0;
+  const int K = ksize == 3 ? kTaps3 : 1;
+  const int64_t blocks = use_pp_w(cin, cout)
+                             ? split_for(m, K, cin, cout, max_blocks).blocks()
+                             : static_cast<int64_t>(runs_for(m, K, max_blocks).runs) * K;
+  return blocks * cin * cout * static_cast<int64_t>(sizeof(float));
+}
 
-using namespace submconv;
-
-extern "C" int64_t submconv_backward_weight_workspace_bytes(submconv_map_t map, int32_t cin,
-                                                            int32_t cout, int32_t ksize) {
+int check_weight_args(submconv_map_t map, int32_t cin, int32_t cout, int32_t ksize) {
   if (!map) return set_error(SUBMCONV_ERR_INVALID_ARG, "map is NULL");
   if (ksize != 1 && ksize != 3) return set_error(SUBMCONV_ERR_INVALID_ARG, "ksize = %d", ksize);
   if (cin <= 0 || cout <= 0 || cin % 8 || cout % 8 || cin > 1024 || cout > 1024)
     return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "Cin = %d, Cout = %d", cin, cout);
-  if (!use_mfma_w(cin, cout) || map->m.n == 0) return 0;
-  const int K = ksize == 3 ? kTaps3 : 1;
-  const int64_t blocks = use_pp_w(cin, cout) ? split_for(map->m, K, cin, cout).blocks()
-                                             : static_cast<int64_t>(runs_for(map->m, K).runs) * K;
-  return blocks * cin * cout * static_cast<int64_t>(sizeof(float));
+  return SUBMCONV_OK;
 }
 
-extern "C" int submconv_backward_weight(submconv_map_t map, const uint16_t* feats,
-                                        const uint16_t* grad_out, float* grad_w, void* workspace,
-                                        int32_t cin, int32_t cout, int32_t ksize,
-                                        hipStream_t stream) {
-  clear_error();
-  const int64_t ws = submconv_backward_weight_workspace_bytes(map, cin, cout, ksize);
-  if (ws < 0) return static_cast<int>(ws);
-  const Map& m = map->m;
+// The weight gradient with partials in `workspace` (ws bytes, computed for at
+// most max_blocks workgroups).
+int backward_weight_impl(const Map& m, const uint16_t* feats, const uint16_t* grad_out,
+                                float* grad_w, void* workspace, int64_t ws, int64_t max_blocks,
+                                int32_t cin, int32_t cout, int32_t ksize, hipStream_t stream) {
   const int K = ksize == 3 ? kTaps3 : 1;
   if (!grad_w) return set_error(SUBMCONV_ERR_INVALID_ARG, "grad_w is NULL");
   if (m.n == 0) {
@@ -759,15 +775,16 @@ extern "C" int submconv_backward_weight(submconv_map_t map, const uint16_t* feat
                        "reach 2 GiB, the weight-gradient kernel's 32-bit buffer offsets",
                        static_cast<long long>(m.n), cin, cout,
                        static_cast<long long>(m.active_pairs));
+    const int64_t mb = max_blocks;
     switch (cin) {
-      case 32: return dispatch_w<32>(m, K, cout, f, g, part, grad_w, stream);
-      case 64: return dispatch_w<64>(m, K, cout, f, g, part, grad_w, stream);
-      case 96: return dispatch_w<96>(m, K, cout, f, g, part, grad_w, stream);
-      case 128: return dispatch_w<128>(m, K, cout, f, g, part, grad_w, stream);
-      case 160: return dispatch_w<160>(m, K, cout, f, g, part, grad_w, stream);
-      case 192: return dispatch_w<192>(m, K, cout, f, g, part, grad_w, stream);
-      case 224: return dispatch_w<224>(m, K, cout, f, g, part, grad_w, stream);
-      case 256: return dispatch_w<256>(m, K, cout, f, g, part, grad_w, stream);
+      case 32: return dispatch_w<32>(m, K, cout, f, g, part, grad_w, mb, stream);
+      case 64: return dispatch_w<64>(m, K, cout, f, g, part, grad_w, mb, stream);
+      case 96: return dispatch_w<96>(m, K, cout, f, g, part, grad_w, mb, stream);
+      case 128: return dispatch_w<128>(m, K, cout, f, g, part, grad_w, mb, stream);
+      case 160: return dispatch_w<160>(m, K, cout, f, g, part, grad_w, mb, stream);
+      case 192: return dispatch_w<192>(m, K, cout, f, g, part, grad_w, mb, stream);
+      case 224: return dispatch_w<224>(m, K, cout, f, g, part, grad_w, mb, stream);
+      case 256: return dispatch_w<256>(m, K, cout, f, g, part, grad_w, mb, stream);
       default: break;
     }
   }
@@ -776,6 +793,77 @@ extern "C" int submconv_backward_weight(submconv_map_t map, const uint16_t* feat
       K == kTaps3 ? m.nbr : nullptr, m.order, m.n, K, f, g, cin, cout, grad_w);
   SUBMCONV_HIP_CHECK(hipGetLastError());
   return SUBMCONV_OK;
+}
+
+}  // namespace
+}  // namespace submconv
+
+using namespace submconv;
+
+extern "C" int64_t submconv_backward_weight_workspace_bytes(submconv_map_t map, int32_t cin,
+                                                            int32_t cout, int32_t ksize) {
+  const int st = check_weight_args(map, cin, cout, ksize);
+  if (st != SUBMCONV_OK) return st;
+  return workspace_bytes(map->m, cin, cout, ksize, INT64_MAX);
+}
+
+extern "C" int submconv_backward_weight(submconv_map_t map, const uint16_t* feats,
+                                        const uint16_t* grad_out, float* grad_w, void* workspace,
+                                        int32_t cin, int32_t cout, int32_t ksize,
+                                        hipStream_t stream) {
+  clear_error();
+  const int st = check_weight_args(map, cin, cout, ksize);
+  if (st != SUBMCONV_OK) return st;
+  const int64_t ws = workspace_bytes(map->m, cin, cout, ksize, INT64_MAX);
+  return backward_weight_impl(map->m, feats, grad_out, grad_w, workspace, ws, INT64_MAX, cin, cout,
+                              ksize, stream);
+}
+
+// This device's address of `scratch`, looked up once per device (on the
+// entry point's first call there, with that device current) and kept.
+static int scratch_address(int dev, void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (dev < 0 || dev >= kMaxDevices)
+    return set_error(SUBMCONV_ERR_INVALID_ARG, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    SUBMCONV_HIP_CHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return SUBMCONV_OK;
+}
+
+extern "C" int submconv_backward_weight_noalloc(submconv_map_t map, const uint16_t* feats,
+                                                const uint16_t* grad_out, float* grad_w,
+                                                int32_t cin, int32_t cout, int32_t ksize,
+                                                hipStream_t stream) {
+  clear_error();
+  const int st = check_weight_args(map, cin, cout, ksize);
+  if (st != SUBMCONV_OK) return st;
+  const Map& m = map->m;
+  int dev = -1;
+  SUBMCONV_HIP_CHECK(hipGetDevice(&dev));
+  if (dev != m.device)
+    return set_error(SUBMCONV_ERR_INVALID_ARG, "the map is on device %d, the current device is %d",
+                     m.device, dev);
+  void* ws_ptr = nullptr;
+  const int sa = scratch_address(dev, &ws_ptr);
+  if (sa != SUBMCONV_OK) return sa;
+  // as many workgroups' partials as the static workspace holds (longer runs
+  // per workgroup than the allocating entry point when they do not all fit)
+  const int64_t max_blocks =
+      static_cast<int64_t>(kNoAllocScratchBytes / (static_cast<size_t>(cin) * cout * sizeof(float)));
+  const int64_t ws = workspace_bytes(m, cin, cout, ksize, max_blocks);
+  if (ws > static_cast<int64_t>(kNoAllocScratchBytes))
+    return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE,
+                     "the weight gradient needs %lld bytes of partials, the static workspace "
+                     "holds %zu", static_cast<long long>(ws), kNoAllocScratchBytes);
+  return backward_weight_impl(m, feats, grad_out, grad_w, ws_ptr, ws, max_blocks, cin, cout, ksize,
+                              stream);
 }
 
 extern "C" int submconv_backward_bias(const uint16_t* grad_out, int64_t n, int32_t cout,
