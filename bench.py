@@ -281,8 +281,8 @@ def coord_op_bench(args, sc, wl, coords, feats, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c3_128_128")
     ap.add_argument("--op", default="forward", choices=list(METRICS))
     ap.add_argument("--dtype", default="fp16", choices=["fp16", "bf16"],

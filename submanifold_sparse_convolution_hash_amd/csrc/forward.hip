@@ -87,8 +87,8 @@ constexpr uint32_t kOob = 0x80000000u;  // an offset past every buffer (< 2 GiB)
 __device__ __forceinline__ half8 bload_h8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
-__device__ __forceinline__ int2 bload_i2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(int2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+__device__ __forceinline__ int bload_i1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
 // Epilogue of the MFMA kernel: the tile's fp32 accumulator rows (float4
@@ -365,26 +365,26 @@ __global__ __launch_bounds__((CfgPP<CIN, COUT_T, K3, GR_, M_>::NT)) void k_fwd_p
     lcol[i] = static_cast<uint32_t>(((lc / KS) * (CIN_T / 16) + lc % KS) * 16);
     lpos[i] = lrow[i] * RC + (lc ^ (lrow[i] & (RC - 1)));
   }
-  // entries of group g, and (ep) the pass its chunks are for
-  auto load_entries = [&](const Grp& g, int2 (&E)[CPT], int& ep) {
+  // the feature row of each of this thread's chunks of group g (-1: none;
+  // only the entries' first word, the neighbour's row, is read), and (ep)
+  // the pass the chunks are for
+  auto load_entries = [&](const Grp& g, int (&E)[CPT], int& ep) {
     ep = g.pass;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const bool live = loader && lrow[i] < g.cnt;
-      if (K3) {
-        E[i] = bload_i2(re, live ? static_cast<uint32_t>(g.start + lrow[i]) * 8u : e_none);
-      } else {
-        E[i].x = static_cast<int>(g.t0) + g.start + lrow[i];
-        E[i].y = live ? g.start + lrow[i] : -1;
-      }
+      if (K3)
+        E[i] = bload_i1(re, live ? static_cast<uint32_t>(g.start + lrow[i]) * 8u : e_none);
+      else
+        E[i] = live ? static_cast<int>(g.t0) + g.start + lrow[i] : -1;
     }
   };
-  auto load_chunks = [&](const int2 (&E)[CPT], int ep, half8 (&D)[CPT]) {
+  auto load_chunks = [&](const int (&E)[CPT], int ep, half8 (&D)[CPT]) {
     const uint32_t pc = NP == 1 ? 0u : static_cast<uint32_t>(ep * KS * 16);
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
-      D[i] = bload_h8(rf, E[i].y >= 0 ? static_cast<uint32_t>(E[i].x) * (CIN_T * 2) + pc + lcol[i]
-                                      : kOob);
+      D[i] = bload_h8(rf, E[i] >= 0 ? static_cast<uint32_t>(E[i]) * (CIN_T * 2) + pc + lcol[i]
+                                    : kOob);
   };
   auto store_chunks = [&](int slot, const half8 (&D)[CPT]) {
     if (loader) {
@@ -398,7 +398,7 @@ __global__ __launch_bounds__((CfgPP<CIN, COUT_T, K3, GR_, M_>::NT)) void k_fwd_p
     for (int rb = 0; rb < NRBW; ++rb) {
       const int sl = (lane & 31) + 32 * (rb0 + rb);
       if (K3)
-        R[rb] = bload_i2(re, sl < g.cnt ? static_cast<uint32_t>(g.start + sl) * 8u : e_none).y;
+        R[rb] = bload_i1(re, (sl < g.cnt ? static_cast<uint32_t>(g.start + sl) * 8u : e_none) + 4u);
       else
         R[rb] = sl < g.cnt ? g.start + sl : -1;
     }
@@ -493,7 +493,7 @@ __global__ __launch_bounds__((CfgPP<CIN, COUT_T, K3, GR_, M_>::NT)) void k_fwd_p
     join(cur, nxt);
     auto grp = [&](int f) -> Grp { return group_at(cur, nxt, f); };
 
-    int2 E[4][CPT];
+    int E[4][CPT];
     int EP[4];
     half8 D[4][CPT];
     int RW[2][NRBW];
