@@ -51,10 +51,17 @@ CSRC = os.path.join(ROOT, "submanifold_sparse_convolution_hash_amd", "csrc")
 # runs of this script (FETCH_SIZE and WRITE_SIZE, KiB per dispatch, averaged
 # over its launches), keyed by (workload, op) and by the SHA-256 of the kernel
 # source's code (comments stripped) they were taken on. Scale factors come from a plain 512 MiB device
-# copy measured in the same runs (--calib-copy-mib 512): its FETCH_SIZE read
-# 262,176 KiB and its WRITE_SIZE 524,290 KiB for 524,288 KiB moved each way.
+# copy measured in the same runs (--calib-copy-mib 512, and the measured-ceiling
+# copies): its FETCH_SIZE read 262,156 KiB and its WRITE_SIZE 524,288 KiB for
+# 524,288 KiB moved each way.
 # A changed kernel source makes the entry stale and the reported traffic null.
-MEASURED_TRAFFIC = {}
+MEASURED_TRAFFIC = {
+    ("c3_128_128", "forward"): {
+        "src": ["forward.hip", "map_build.hip"],  # the kernel, and the map's tile size
+        "sha256": "3301a64e8b95e0107de52b5aa5dc6625d7a998281683df76fc5bb4b3800cc0de",
+        "fetch_kib": 38858.97, "write_kib": 52429.77,
+        "fetch_factor": 524288.0 / 262156.0, "write_factor": 524288.0 / 524288.0},
+}
 
 METRICS = {
     "forward": "SubMConv3d ms/layer + effective TFLOP/s (128^3 grid, C=128, 10% occ)",
