@@ -125,6 +125,15 @@ typedef struct submconv_map_s* submconv_map_t;
 int submconv_build_map(const int32_t* coords, int64_t n, int32_t batch, const int32_t grid[3],
                        uint32_t flags, hipStream_t stream, submconv_map_t* out_map);
 
+/*
+ * submconv_release_scratch -- free the build scratch that the current device
+ * keeps for its next map build (see submconv_build_map); waits for a build in
+ * progress on the device and for the device itself. Maps, prepared weights
+ * and the 14 MiB weight stage are not affected; the next build allocates its
+ * scratch again. Host call, safe at any time.
+ */
+int submconv_release_scratch(void);
+
 /* Number of sites of the map. */
 int64_t submconv_map_num_rows(submconv_map_t map);
 

@@ -26,7 +26,7 @@ __all__ = [
     "SubmconvError", "KernelMap", "build_map", "Weights", "prepare_weights", "forward",
     "forward_kernel", "backward_input",
     "backward_weight", "backward_bias", "SubMConv3dFunction", "SubMConv3d", "library_path", "load_library",
-    "abi_version", "FLAG_MORTON", "downsample", "subdivide", "MaskedPlan", "masked_plan",
+    "abi_version", "release_scratch", "FLAG_MORTON", "downsample", "subdivide", "MaskedPlan", "masked_plan",
     "forward_masked",
 ]
 
@@ -64,6 +64,7 @@ def load_library():
     P, I32, I64, U32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
     sig = {
         "submconv_build_map": ([P, I64, I32, P, U32, P, P], ctypes.c_int),
+        "submconv_release_scratch": ([], ctypes.c_int),
         "submconv_map_num_rows": ([P], I64),
         "submconv_map_tile_rows": ([P], I32),
         "submconv_map_active_pairs": ([P, I32], I64),
@@ -109,6 +110,13 @@ def load_library():
 
 def abi_version() -> int:
     return int(load_library().submconv_abi_version())
+
+
+def release_scratch(device: Optional[torch.device] = None) -> None:
+    """Frees the map-build scratch the library keeps on ``device`` (default:
+    the current device) for its next build."""
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        _check(load_library().submconv_release_scratch())
 
 
 def _check(status: int) -> None:

@@ -867,6 +867,22 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
 #undef BUILD_CHECK
 }
 
+extern "C" int submconv_release_scratch(void) {
+  clear_error();
+  int dev = -1;
+  SUBMCONV_HIP_CHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kScratchDevices) return SUBMCONV_OK;
+  KeptScratch& k = g_kept[dev];
+  std::lock_guard<std::mutex> lock(k.mu);  // waits for a build in progress on the device
+  if (k.p) {
+    const hipError_t e = hipFree(k.p);
+    k.p = nullptr;
+    k.bytes = 0;
+    SUBMCONV_HIP_CHECK(e);
+  }
+  return SUBMCONV_OK;
+}
+
 extern "C" int64_t submconv_map_num_rows(submconv_map_t map) {
   if (!map) return set_error(SUBMCONV_ERR_INVALID_ARG, "map is NULL");
   return map->m.n;

@@ -879,3 +879,95 @@ def test_features_at_the_2gib_limit(dev):
     _assert_close(got, ref, "2 GiB features, sampled rows")
     np.testing.assert_array_equal(km.export()[torch.from_numpy(rows).to(dev)].cpu().numpy(), sub)
     km.free()
+
+
+@gpu
+def test_two_streams_raw_weights(dev):
+    """Forwards on weights as the caller holds them share the device's
+    staging buffer: on two side streams at once, each with its own W, every
+    output equals the same forward run alone (the streams are ordered around
+    the buffer by an event)."""
+    sc = _sc()
+    wl = workloads.uniform_workload(48, 11000, [(3, 64, 64)], seed=1211, bias_kind="normal", name="rw")
+    L = wl.layers[0]
+    km = sc.build_map(_to(dev, wl.coords), wl.grid, wl.batch)
+    rng = np.random.default_rng(1212)
+    fa = _to(dev, rng.standard_normal((wl.n, 64)).astype(np.float16))
+    fb = _to(dev, rng.standard_normal((wl.n, 64)).astype(np.float16))
+    Wa = _to(dev, L.W)
+    Wb = _to(dev, (rng.standard_normal(L.W.shape) / 40).astype(np.float16))
+    b = _to(dev, L.bias)
+    ra = sc.forward(km, fa, Wa, b)
+    rb = sc.forward(km, fb, Wb, b)
+    torch.cuda.synchronize(dev)
+    oa = torch.empty_like(ra)
+    ob = torch.empty_like(rb)
+    s1, s2 = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
+    s1.wait_stream(torch.cuda.current_stream(dev))
+    s2.wait_stream(torch.cuda.current_stream(dev))
+    for _ in range(6):
+        with torch.cuda.stream(s1):
+            sc.forward(km, fa, Wa, b, out=oa)
+        with torch.cuda.stream(s2):
+            sc.forward(km, fb, Wb, b, out=ob)
+    torch.cuda.current_stream(dev).wait_stream(s1)
+    torch.cuda.current_stream(dev).wait_stream(s2)
+    torch.cuda.synchronize(dev)
+    assert torch.equal(oa, ra) and torch.equal(ob, rb)
+    ref = oc.submconv_rows(oc.kernel_map(wl.coords, wl.grid, wl.batch, 3), fb.cpu().numpy(),
+                           Wb.cpu().numpy(), L.bias)
+    _assert_close(ob.float().cpu().numpy(), ref, "stream b")
+    km.free()
+
+
+@gpu
+def test_raw_weights_forward_in_a_captured_graph(dev):
+    """submconv_forward on W inside a captured graph (the weight
+    rearrangement and the gather-GEMM are both captured): every replay, with
+    new features and new weights copied in eagerly between replays, equals
+    the eager forward."""
+    sc = _sc()
+    wl = workloads.uniform_workload(48, 11000, [(3, 128, 128)], seed=1213, bias_kind=None, name="gw")
+    L = wl.layers[0]
+    km = sc.build_map(_to(dev, wl.coords), wl.grid, wl.batch)
+    feats = _to(dev, wl.feats).clone()
+    W = _to(dev, L.W).clone()
+    out = torch.empty((wl.n, 128), dtype=torch.float16, device=dev)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            sc.forward(km, feats, W, out=out)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sc.forward(km, feats, W, out=out)
+    rng = np.random.default_rng(1214)
+    for rep in range(3):
+        feats.copy_(_to(dev, rng.standard_normal((wl.n, 128)).astype(np.float16)))
+        W.copy_(_to(dev, (rng.standard_normal(L.W.shape) / 60).astype(np.float16)))
+        torch.cuda.synchronize(dev)
+        g.replay()
+        torch.cuda.synchronize(dev)
+        ref = sc.forward(km, feats, W)
+        torch.cuda.synchronize(dev)
+        assert torch.equal(out, ref), f"replay {rep}"
+    km.free()
+
+
+@gpu
+def test_release_scratch_then_build(dev):
+    """The kept build scratch can be released between builds; the next build
+    allocates it again and gives the oracle's map."""
+    sc = _sc()
+    wl = workloads.random_small(91, G=20, occ=0.2, cin=32, cout=32, batch=2)
+    km = sc.build_map(_to(dev, wl.coords), wl.grid, wl.batch)
+    sc.release_scratch(dev)
+    sc.release_scratch(dev)  # nothing kept: a no-op
+    km2 = sc.build_map(_to(dev, wl.coords), wl.grid, wl.batch)
+    ref = oc.kernel_map(wl.coords, wl.grid, wl.batch, 3)
+    np.testing.assert_array_equal(km.export().cpu().numpy(), ref)
+    np.testing.assert_array_equal(km2.export().cpu().numpy(), ref)
+    km.free()
+    km2.free()
