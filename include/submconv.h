@@ -74,6 +74,15 @@ extern "C" {
  * results are the same bit for bit) */
 #define SUBMCONV_FLAG_TILES_256 4u
 #define SUBMCONV_FLAG_TILES_288 8u
+/* the staged plan: on a dense map (at least 12 neighbours per row on
+ * average, centre included, as on a surface) the build also cuts the rows
+ * into units of up to 128 whose distinct neighbour rows (at most 512) a
+ * forward of 32 or 64 channels in and out stages once in LDS, instead of
+ * gathering each (row, tap) pair; it costs 54 bytes per row plus 4 per staged
+ * row. SUBMCONV_FLAG_STAGED builds it on any map, SUBMCONV_FLAG_NO_STAGED on
+ * none (such forwards then take the compacted lists) */
+#define SUBMCONV_FLAG_STAGED 16u
+#define SUBMCONV_FLAG_NO_STAGED 32u
 
 /* 16-bit element types of features and weights (the *_dtype entry points). */
 #define SUBMCONV_DTYPE_F16 0  /* IEEE binary16 */
@@ -271,11 +280,14 @@ int submconv_forward_prepared(submconv_map_t map, const uint16_t* feats, submcon
                               const float* bias, uint16_t* out, hipStream_t stream);
 
 /*
- * submconv_forward_kernel -- which kernel a forward of this shape takes, on
- * the host, without a device: 1 the MFMA gather-GEMM, 0 the VALU kernel, or
- * a negative status: SUBMCONV_ERR_UNSUPPORTED_SHAPE for an MFMA shape whose
- * features or lists reach 2 GiB (submconv_forward's limit), or a shape
- * error. n rows, active_pairs as submconv_map_active_pairs reports them.
+ * submconv_forward_kernel -- which kernel a forward of this shape takes on a
+ * map built with default flags, on the host, without a device: 2 the staged
+ * gather-GEMM (a 3x3x3 forward of 32 -> 32, 64 -> 32 or 32 -> 64 channels on
+ * a dense map, see SUBMCONV_FLAG_STAGED), 1 the MFMA gather-GEMM on the
+ * per-tile lists, 0 the VALU kernel, or a negative status:
+ * SUBMCONV_ERR_UNSUPPORTED_SHAPE for an MFMA shape whose features or lists
+ * reach 2 GiB (submconv_forward's limit), or a shape error. n rows,
+ * active_pairs as submconv_map_active_pairs reports them.
  */
 int submconv_forward_kernel(int64_t n, int64_t active_pairs, int32_t cin, int32_t cout,
                             int32_t ksize);

@@ -36,6 +36,8 @@ FLAG_MORTON = 1
 FLAG_SORTED_KEYS = 2
 FLAG_TILES_256 = 4
 FLAG_TILES_288 = 8
+FLAG_STAGED = 16
+FLAG_NO_STAGED = 32
 PREP_INPUT_GRAD = 1
 _lib = None
 
@@ -202,13 +204,14 @@ class KernelMap:
 
 def build_map(coords: torch.Tensor, grid: Sequence[int], batch: Optional[int] = None,
               morton: bool = False, sorted_keys: bool = False,
-              tile_rows: Optional[int] = None) -> KernelMap:
+              tile_rows: Optional[int] = None, staged: Optional[bool] = None) -> KernelMap:
     """Hashes the sites ``coords`` ([N,4] int32 (b,x,y,z), device) and builds
     their 3x3x3 neighbour map. Waits for the stream (validation).
     ``sorted_keys`` finds neighbours by binary search in the sorted site keys
     instead of the hash table (same map). ``tile_rows`` (256 or 288) forces
     the tile size of the lists the forward streams (default: the library's
-    choice; the results are the same)."""
+    choice; the results are the same). ``staged`` True builds the staged plan
+    of dense maps on any map, False on none (default: on dense maps)."""
     if tile_rows not in (None, 256, 288):
         raise ValueError("tile_rows must be None, 256 or 288")
     _require(coords, "coords", torch.int32, 2)
@@ -221,6 +224,7 @@ def build_map(coords: torch.Tensor, grid: Sequence[int], batch: Optional[int] = 
     h = ctypes.c_void_p()
     flags = (FLAG_MORTON if morton else 0) | (FLAG_SORTED_KEYS if sorted_keys else 0)
     flags |= {None: 0, 256: FLAG_TILES_256, 288: FLAG_TILES_288}[tile_rows]
+    flags |= {None: 0, True: FLAG_STAGED, False: FLAG_NO_STAGED}[staged]
     with torch.cuda.device(coords.device):
         _check(lib.submconv_build_map(_ptr(coords), coords.shape[0], int(batch), g, flags,
                                       _stream(coords.device), ctypes.byref(h)))
@@ -288,9 +292,11 @@ def prepare_weights(W: torch.Tensor, input_grad: bool = False) -> Weights:
 
 
 def forward_kernel(n: int, active_pairs: int, cin: int, cout: int, ksize: int = 3) -> int:
-    """The kernel a forward of this shape takes (host only): 1 MFMA, 0 VALU;
-    raises :class:`SubmconvError` for a shape the library rejects (e.g. MFMA
-    features of 2 GiB or more)."""
+    """The kernel a forward of this shape takes on a map built with default
+    flags (host only): 2 the staged MFMA kernel (dense maps, 32 -> 32,
+    64 -> 32 or 32 -> 64 channels), 1 the MFMA kernel on the per-tile lists,
+    0 VALU; raises :class:`SubmconvError` for a shape the library rejects
+    (e.g. MFMA features of 2 GiB or more)."""
     v = int(load_library().submconv_forward_kernel(int(n), int(active_pairs), int(cin), int(cout),
                                                     int(ksize)))
     if v < 0:

@@ -862,6 +862,8 @@ int forward_typed(const Map& m, int ksize, int cin, int cout, const _Float16* fe
                   hipStream_t stream) {
   const int path = kernel_path(m.n, m.active_pairs, cin, cout, ksize);
   if (path < 0) return path;
+  if (path == 1 && staged_takes(m, ksize, cin, cout))
+    return forward_staged(m, cin, cout, IS_BF16, feats, wp, bias, out, stream);
   if (path == 1) {
     switch (cin) {
       case 32: return dispatch_cout<32, IS_BF16>(m, ksize, feats, wp, bias, out, cout, stream);
@@ -1016,7 +1018,12 @@ extern "C" int submconv_forward_kernel(int64_t n, int64_t active_pairs, int32_t 
   if (st != SUBMCONV_OK) return st;
   if (n < 0 || active_pairs < 0)
     return set_error(SUBMCONV_ERR_INVALID_ARG, "negative row or pair count");
-  return kernel_path(n, active_pairs, cin, cout, ksize);
+  const int path = kernel_path(n, active_pairs, cin, cout, ksize);
+  // a map built with default flags has a staged plan when it is dense
+  if (path == 1 && ksize == 3 && staged_shape(cin, cout) && n > 0 &&
+      active_pairs >= int64_t{kStageMinPairsPerRow} * n)
+    return 2;
+  return path;
 }
 
 extern "C" int submconv_weights_create(int32_t ksize, int32_t cin, int32_t cout, int32_t dtype,

@@ -552,10 +552,12 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   if (n > 0 && !coords) return set_error(SUBMCONV_ERR_INVALID_ARG, "coords is NULL");
   if (batch < 1) return set_error(SUBMCONV_ERR_INVALID_ARG, "batch = %d < 1", batch);
   if (flags & ~(SUBMCONV_FLAG_MORTON | SUBMCONV_FLAG_SORTED_KEYS | SUBMCONV_FLAG_TILES_256 |
-                SUBMCONV_FLAG_TILES_288))
+                SUBMCONV_FLAG_TILES_288 | SUBMCONV_FLAG_STAGED | SUBMCONV_FLAG_NO_STAGED))
     return set_error(SUBMCONV_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   if ((flags & SUBMCONV_FLAG_TILES_256) && (flags & SUBMCONV_FLAG_TILES_288))
     return set_error(SUBMCONV_ERR_INVALID_ARG, "flags ask for two tile sizes");
+  if ((flags & SUBMCONV_FLAG_STAGED) && (flags & SUBMCONV_FLAG_NO_STAGED))
+    return set_error(SUBMCONV_ERR_INVALID_ARG, "flags ask for and against the staged plan");
   for (int a = 0; a < 3; ++a)
     if (grid[a] < 1) return set_error(SUBMCONV_ERR_INVALID_ARG, "grid[%d] = %d < 1", a, grid[a]);
   if (n > INT32_MAX - 1)
@@ -617,6 +619,9 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
                                                             : wide_tile_rows(n, cus);
   const int64_t nt_base = (n + kTileRows - 1) / kTileRows;
   const int64_t nt_wide = wide_cand > 0 ? (n + wide_cand - 1) / wide_cand : 0;
+  // tiles of the staged plan, unless it is ruled out
+  const int64_t nt_stage =
+      (flags & SUBMCONV_FLAG_NO_STAGED) ? 0 : (n + kStageUnitRows - 1) / kStageUnitRows;
 
   // library scratch sizes, asked for before anything is allocated
   size_t ksort_bytes = 0, msort_bytes = 0;
@@ -648,6 +653,8 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
     int32_t *tvals, *srows, *rows_in, *midx, *inv, *tile_tot, *tile_tot_wide;
     void *small, *ksort, *msort;
   } t{};
+  StagedTemps stp;
+  stp.n_tiles = nt_stage;
   auto temps = [&](Carve& c) {
     t.keys = c.take<uint64_t>(n);
     if (sorted_keys) {
@@ -670,6 +677,14 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
     t.small = c.take<char>(512);
     t.tile_tot = c.take<int32_t>(nt_base + 1);
     t.tile_tot_wide = c.take<int32_t>(nt_wide + 1);
+    if (nt_stage > 0) {
+      stp.tile_units = c.take<int4>(kStageMaxUnitsPerTile * nt_stage);
+      stp.tile_nu = c.take<int32_t>(nt_stage);
+      stp.tile_ns = c.take<int32_t>(nt_stage);
+      stp.unit_off = c.take<int64_t>(nt_stage);
+      stp.staged_off = c.take<int64_t>(nt_stage);
+      stp.totals = c.take<int64_t>(2);
+    }
   };
   // what the map keeps, but the lists (sized once the pairs are counted)
   Tiles base, wide;
@@ -690,10 +705,12 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   void* tmp = nullptr;
   void* mem = nullptr;
   void* ent_mem = nullptr;
+  void* staged_mem = nullptr;
   auto fail = [&](int status) {
     (void)hipStreamSynchronize(stream);
     if (mem) (void)hipFree(mem);
     if (ent_mem) (void)hipFree(ent_mem);
+    if (staged_mem) (void)hipFree(staged_mem);
     return status;
   };
 #define BUILD_CHECK(expr)                                                                 \
@@ -851,10 +868,39 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
     BUILD_CHECK(hipMemcpyAsync(host_groups, groups_wide, sizeof(host_groups), hipMemcpyDeviceToHost,
                                stream));
   }
+  // the staged plan of a dense map (or of any map, when asked for): its
+  // units are counted before the wait, and written after it
+  const bool want_staged =
+      nt_stage > 0 && ((flags & SUBMCONV_FLAG_STAGED) ||
+                       m.active_pairs >= int64_t{kStageMinPairsPerRow} * n);
+  int64_t host_staged[2] = {0, 0};
+  if (want_staged) {
+    if (const int st = staged_count(nbr, n, stp, stream); st != SUBMCONV_OK) return fail(st);
+    BUILD_CHECK(hipMemcpyAsync(host_staged, stp.totals, sizeof(host_staged), hipMemcpyDeviceToHost,
+                               stream));
+  }
   // the forward may run on another stream: the map is complete on return
   BUILD_CHECK(hipStreamSynchronize(stream));
   if (use_wide)
     for (int q = 0; q < kTaps3; ++q) wide.pos_groups[q] = static_cast<int64_t>(host_groups[q]);
+  Staged staged;
+  // (the kernel's staged-row offsets are 32-bit)
+  if (want_staged && host_staged[0] > 0 && host_staged[1] < INT32_MAX) {
+    staged.n_units = host_staged[0];
+    staged.n_rows = host_staged[1];
+    auto parts = [&](Carve& c) {
+      staged.units = c.take<int4>(staged.n_units);
+      staged.rows = c.take<int32_t>(staged.n_rows);
+      staged.idx = c.take<uint16_t>(kTaps3 * staged_idx_stride(n));
+    };
+    Carve c;
+    parts(c);
+    BUILD_CHECK(hipMalloc(&staged_mem, c.used));
+    c = Carve{static_cast<char*>(staged_mem), 0};
+    parts(c);
+    if (const int st = staged_fill(nbr, n, stp, staged, stream); st != SUBMCONV_OK) return fail(st);
+    BUILD_CHECK(hipStreamSynchronize(stream));
+  }
   m.mem = mem;
   m.ent_mem = ent_mem;
   m.nbr = nbr;
@@ -862,6 +908,8 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   m.tiles = base;
   m.wide = wide;
   m.wide_always = (flags & SUBMCONV_FLAG_TILES_288) != 0;
+  m.staged_mem = staged_mem;
+  m.staged = staged;
   *out_map = new submconv_map_s{m};
   return SUBMCONV_OK;
 #undef BUILD_CHECK
@@ -932,6 +980,8 @@ extern "C" int submconv_map_free(submconv_map_t map) {
     status = set_error(SUBMCONV_ERR_HIP, "hipFree of the map failed");
   if (map->m.ent_mem && hipFree(map->m.ent_mem) != hipSuccess)
     status = set_error(SUBMCONV_ERR_HIP, "hipFree of the tile lists failed");
+  if (map->m.staged_mem && hipFree(map->m.staged_mem) != hipSuccess)
+    status = set_error(SUBMCONV_ERR_HIP, "hipFree of the staged plan failed");
   delete map;
   return status;
 }

@@ -56,6 +56,37 @@ struct Tiles {
   // groups of kGroupRows entries per processing position, over all tiles
   int64_t pos_groups[kTaps3] = {};
 };
+// Staged plan of a dense map (many neighbours per row): the rows cut into
+// units of up to kStageUnitRows consecutive processing rows whose distinct
+// neighbour rows over all 27 taps number at most kStageCap, so that a
+// workgroup holds them in LDS and every tap reads them from there.
+//  units  [n_units] int4 {first processing row, rows, first staged row,
+//         staged rows}, in processing order;
+//  rows   [n_rows] caller rows each unit stages, ascending within a unit;
+//  idx    [27][stride] uint16, stride = n rounded up to even: the neighbour
+//         of processing row t at tap k as a row of its unit's staged rows, or
+//         kStageNone. Units start on even rows, so that a unit's entries of a
+//         tap are whole 4-byte words.
+// A tile of kStageUnitRows rows whose neighbours exceed kStageCap is halved
+// until they fit; 27 * kStageMinRows <= kStageCap, so halves of at most
+// kStageMinRows rows always do.
+constexpr int kStageUnitRows = 128;
+constexpr int kStageCap = 512;
+constexpr int kStageMinRows = 16;
+constexpr uint16_t kStageNone = 0xFFFF;
+// mean neighbours per row (centre included) from which a build makes the
+// staged plan
+constexpr int kStageMinPairsPerRow = 12;
+inline int64_t staged_idx_stride(int64_t n) { return n + (n & 1); }
+constexpr int kStageMaxUnitsPerTile = 16;
+struct Staged {
+  int64_t n_units = 0;
+  int64_t n_rows = 0;
+  int4* units = nullptr;
+  int32_t* rows = nullptr;
+  uint16_t* idx = nullptr;
+};
+
 struct Map {
   int device = 0;
   int64_t n = 0;
@@ -72,6 +103,9 @@ struct Map {
   Tiles tiles;
   Tiles wide;
   bool wide_always = false;  // forwards take the wide tiles whenever their kernel can
+  // the staged plan (staged.n_units == 0: none), in its own allocation
+  void* staged_mem = nullptr;
+  Staged staged;
 };
 
 // Prepared weights of one layer (W [K][cin][cout]): the MFMA fragment order
@@ -83,6 +117,30 @@ struct Weights {
   uint32_t flags = 0;
   _Float16* buf = nullptr;  // K * cin * cout elements, library-owned
 };
+
+// Build of the staged plan, in two passes around one host wait: the count
+// pass splits the tiles into units and scans their sizes (totals[0] units,
+// totals[1] staged rows); the fill pass, once the plan is allocated, writes it.
+struct StagedTemps {
+  int64_t n_tiles = 0;     // tiles of kStageUnitRows rows
+  int4* tile_units = nullptr;  // [n_tiles][16] {row in tile, rows, staged rows, 0}
+  int32_t* tile_nu = nullptr;  // [n_tiles] units of each tile
+  int32_t* tile_ns = nullptr;  // [n_tiles] staged rows of each tile
+  int64_t* unit_off = nullptr;   // [n_tiles] first unit of each tile
+  int64_t* staged_off = nullptr; // [n_tiles] first staged row of each tile
+  int64_t* totals = nullptr;     // [2]
+};
+int staged_count(const int32_t* nbr, int64_t n, const StagedTemps& tp, hipStream_t stream);
+int staged_fill(const int32_t* nbr, int64_t n, const StagedTemps& tp, const Staged& plan,
+                hipStream_t stream);
+
+// The staged forward takes a 3x3x3 forward of cin in {32, 64} and cout in
+// {32, 64} channels on a map with a staged plan (weights in MFMA fragment
+// order).
+bool staged_shape(int cin, int cout);
+bool staged_takes(const Map& m, int ksize, int cin, int cout);
+int forward_staged(const Map& m, int cin, int cout, bool bf16, const _Float16* feats,
+                   const _Float16* wp, const float* bias, _Float16* out, hipStream_t stream);
 
 // Allocates the device's staging buffer for weights passed as the caller
 // holds them (once per device; every map build calls it).

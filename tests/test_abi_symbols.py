@@ -73,7 +73,8 @@ def test_host_only_entry_points(lib):
     g0 = (ctypes.c_int32 * 3)(0, 4, 4)
     assert lib.submconv_build_map(None, 0, 1, g0, 0, None, ctypes.byref(h)) == -1  # grid[0] < 1
     assert lib.submconv_build_map(None, 0, 1, g, 4 | 8, None, ctypes.byref(h)) == -1  # two tile sizes
-    assert lib.submconv_build_map(None, 0, 1, g, 16, None, ctypes.byref(h)) == -1  # unknown flag
+    assert lib.submconv_build_map(None, 0, 1, g, 16 | 32, None, ctypes.byref(h)) == -1  # staged and not
+    assert lib.submconv_build_map(None, 0, 1, g, 64, None, ctypes.byref(h)) == -1  # unknown flag
     lib.submconv_forward.restype = ctypes.c_int
     assert lib.submconv_forward(None, None, None, None, None, 8, 8, 3, None) == -1  # map NULL
     lib.submconv_map_free.restype = ctypes.c_int
@@ -84,12 +85,17 @@ def test_forward_kernel_choice_and_buffer_limit(lib):
     """Which kernel a forward takes, decided on the host: the MFMA gather-GEMM
     for its channel counts while features and lists stay below 2 GiB (its
     32-bit buffer offsets), an explicit SUBMCONV_ERR_UNSUPPORTED_SHAPE above,
-    the VALU kernel for other channel counts (64-bit addressing, no limit)."""
+    the VALU kernel for other channel counts (64-bit addressing, no limit);
+    on dense maps (12 or more neighbours per row) the staged kernel for
+    32 -> 32, 64 -> 32 and 32 -> 64 channels."""
     f = lib.submconv_forward_kernel
     f.restype = ctypes.c_int
     f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     assert f(209715, 744981, 128, 128, 3) == 1
-    assert f(1495574, 31_200_000, 64, 32, 3) == 1
+    assert f(1495574, 31_200_000, 64, 32, 3) == 2   # dense: the staged kernel
+    assert f(1495574, 31_200_000, 64, 64, 3) == 1   # (not for 64 -> 64)
+    assert f(1495574, 5_000_000, 64, 32, 3) == 1    # under 12 neighbours per row
+    assert f(1495574, 31_200_000, 64, 32, 1) == 1   # a 1x1x1 layer
     assert f(1000, 4000, 256, 256, 1) == 1
     assert f(1000, 4000, 96, 96, 3) == 0        # no MFMA tile for 96 channels
     assert f(1000, 4000, 256, 64, 3) == 0       # Cin 256 needs Cout a multiple of 128

@@ -1,0 +1,155 @@
+"""GPU parity of the staged forward (dense maps, 32 or 64 channels) against the
+CPU oracle, through the C ABI.
+
+On a dense map the build also makes the staged plan (units of up to 128 rows
+whose distinct neighbour rows fit in LDS), and forwards of 32 -> 32, 64 -> 32
+and 32 -> 64 channels take it. The tolerance is the forward's:
+|gpu - oracle| <= 1e-3 + 1e-2 |oracle| per element. A row's result is summed
+in the same order whatever unit it falls in, so maps in raster and Morton
+order give the same bits.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import cpu as oc
+from oracle import oracle as op
+
+from test_gpu_parity import (_assert_close, _bf16_tensor, _bf16_values, _say, _sc, _to, dev,  # noqa: F401
+                             gpu)
+
+STAGED_SHAPES = [(32, 32), (64, 32), (32, 64)]
+
+
+def _dense_cube(G, batch=1):
+    c = np.stack(np.meshgrid(np.arange(G), np.arange(G), np.arange(G), indexing="ij"), -1).reshape(-1, 3)
+    parts = [np.concatenate([np.full((c.shape[0], 1), b, np.int32), c.astype(np.int32)], 1)
+             for b in range(batch)]
+    return np.concatenate(parts, 0)
+
+
+def _layer(rng, cin, cout, bias=True):
+    W = (rng.standard_normal((27, cin, cout)) / np.sqrt(27 * cin)).astype(np.float16)
+    b = (rng.standard_normal(cout) * 0.1).astype(np.float32) if bias else None
+    return W, b
+
+
+@gpu
+def test_kernel_choice_reports_the_staged_forward(dev):
+    sc = _sc()
+    # 20 neighbours per row: dense; 3.5: sparse
+    assert sc.forward_kernel(1000, 20000, 64, 32) == 2
+    assert sc.forward_kernel(1000, 20000, 32, 64) == 2
+    assert sc.forward_kernel(1000, 20000, 32, 32) == 2
+    assert sc.forward_kernel(1000, 20000, 64, 64) == 1
+    assert sc.forward_kernel(1000, 20000, 128, 32) == 1
+    assert sc.forward_kernel(1000, 3500, 64, 32) == 1
+    assert sc.forward_kernel(1000, 20000, 64, 32, ksize=1) == 1
+
+
+@gpu
+@pytest.mark.slow
+@pytest.mark.parametrize("morton", [False, True])
+def test_c5_layers_staged(dev, morton):
+    # the 512^3 shell: both 3x3x3 layers and the first layer's input gradient
+    # against the oracle on sampled rows, against the compacted-list kernel
+    # on every row, and raster against Morton order bit for bit
+    sc = _sc()
+    wl = workloads.make("c5_512_chain")
+    coords = _to(dev, wl.coords)
+    _say(f"[staged c5] N={wl.n} morton={morton}")
+    km = sc.build_map(coords, wl.grid, wl.batch, morton=morton)
+    kp = sc.build_map(coords, wl.grid, wl.batch, morton=morton, staged=False)
+    ko = sc.build_map(coords, wl.grid, wl.batch, morton=not morton)
+    kmap = oc.kernel_map(wl.coords, wl.grid, wl.batch, 3)
+    rows = np.random.default_rng(11).choice(wl.n, 3000, replace=False)
+    rows_t = torch.from_numpy(rows).to(dev)
+    x = _to(dev, wl.feats)
+    for li, L in enumerate(wl.layers[:2]):
+        _say(f"[staged c5] layer {li} {L.cin}->{L.cout}")
+        W = _to(dev, L.W)
+        y = sc.forward(km, x, W)
+        ref = oc.submconv_rows(kmap, x.cpu().numpy(), L.W, None, rows)
+        _assert_close(y[rows_t].float().cpu().numpy(), ref, f"staged c5 layer {li}")
+        yp = sc.forward(kp, x, W)
+        _assert_close(y.float().cpu().numpy(), yp.float().cpu().numpy().astype(np.float64),
+                      f"staged vs compacted, layer {li}")
+        assert torch.equal(y, sc.forward(ko, x, W)), "raster and Morton order differ"
+        assert torch.equal(y, sc.forward(km, x, W)), "not reproducible"
+        x = y
+    L = wl.layers[0]
+    g = torch.from_numpy(workloads.normal_f16(np.random.default_rng(12), (wl.n, L.cout))).to(dev)
+    _say("[staged c5] input gradient 32->64")
+    dx = sc.backward_input(km, g, _to(dev, L.W))
+    ref = oc.backward_input_rows(wl.coords, wl.grid, wl.batch, 3, g.cpu().numpy(), L.W, rows)
+    _assert_close(dx[rows_t].float().cpu().numpy(), ref, "staged c5 input gradient")
+    for k in (km, kp, ko):
+        k.free()
+
+
+@gpu
+@pytest.mark.parametrize("cin,cout", STAGED_SHAPES)
+@pytest.mark.parametrize("morton", [False, True])
+def test_dense_cube_splits_units(dev, cin, cout, morton):
+    # a fully occupied 24^3 cube in raster order: a 128-row tile touches
+    # ~3 x 7 x 24 rows, more than a unit stages, so tiles split into halves
+    # (and quarters); every row against the oracle
+    sc = _sc()
+    coords = _dense_cube(24)
+    rng = np.random.default_rng(cin * 7 + cout)
+    W, b = _layer(rng, cin, cout)
+    feats = workloads.normal_f16(rng, (coords.shape[0], cin))
+    _say(f"[staged cube] {cin}->{cout} morton={morton}")
+    km = sc.build_map(_to(dev, coords), (24, 24, 24), 1, morton=morton)
+    out = sc.forward(km, _to(dev, feats), _to(dev, W), _to(dev, b)).float().cpu().numpy()
+    kmap = oc.kernel_map(coords, (24, 24, 24), 1, 3)
+    _assert_close(out, oc.submconv_rows(kmap, feats, W, b), f"staged cube {cin}->{cout}")
+    km.free()
+
+
+@gpu
+@pytest.mark.parametrize("n", [1, 2, 3, 31, 127, 128, 129, 257, 1001])
+@pytest.mark.parametrize("cin,cout", STAGED_SHAPES)
+def test_forced_staged_ragged(dev, n, cin, cout):
+    # the plan forced on small sparse maps: row counts around the unit size,
+    # odd counts (the table's padded stride), isolated sites (only the centre)
+    sc = _sc()
+    rng = np.random.default_rng(n * 13 + cin + cout)
+    G = 12
+    flat = rng.choice(G ** 3, n, replace=False)
+    coords = np.stack([np.zeros(n, np.int64), flat // (G * G), (flat // G) % G, flat % G], 1).astype(np.int32)
+    W, b = _layer(rng, cin, cout, bias=bool(n % 2))
+    feats = workloads.normal_f16(rng, (n, cin))
+    km = sc.build_map(_to(dev, coords), (G, G, G), 1, staged=True)
+    out = sc.forward(km, _to(dev, feats), _to(dev, W), _to(dev, b)).float().cpu().numpy()
+    kmap = oc.kernel_map(coords, (G, G, G), 1, 3)
+    _assert_close(out, oc.submconv_rows(kmap, feats, W, b), f"forced staged n={n} {cin}->{cout}")
+    kp = sc.build_map(_to(dev, coords), (G, G, G), 1, staged=False)
+    outp = sc.forward(kp, _to(dev, feats), _to(dev, W), _to(dev, b)).float().cpu().numpy()
+    _assert_close(out, outp.astype(np.float64), "staged vs compacted")
+    km.free()
+    kp.free()
+
+
+@gpu
+@pytest.mark.parametrize("cin,cout", STAGED_SHAPES)
+def test_staged_bf16_and_input_grad(dev, cin, cout):
+    # bf16 features and weights on a dense two-item map; the forward and the
+    # input gradient (cout -> cin channels: staged when that shape is)
+    sc = _sc()
+    wl = workloads.random_small(500 + cin + cout, G=14, occ=0.9, cin=cin, cout=cout, batch=2, ksize=3)
+    rng = np.random.default_rng(cin + 3 * cout)
+    fb = workloads.normal_bf16_bits(rng, (wl.n, cin))
+    Wb = workloads.normal_bf16_bits(rng, wl.layers[0].W.shape, std=1.0 / np.sqrt(27 * cin))
+    gb = workloads.normal_bf16_bits(rng, (wl.n, cout))
+    _say(f"[staged bf16] {cin}->{cout} N={wl.n}")
+    km = sc.build_map(_to(dev, wl.coords), wl.grid, wl.batch)
+    kmap = oc.kernel_map(wl.coords, wl.grid, wl.batch, 3)
+    F, Wd, G = (op.bf16_bits_to_float64(v) for v in (fb, Wb, gb))
+    out = sc.forward(km, _bf16_tensor(dev, fb), _bf16_tensor(dev, Wb), _to(dev, wl.layers[0].bias))
+    _assert_close(_bf16_values(out), oc.submconv_rows(kmap, F, Wd, wl.layers[0].bias), "bf16 forward")
+    dx = sc.backward_input(km, _bf16_tensor(dev, gb), _bf16_tensor(dev, Wb))
+    _assert_close(_bf16_values(dx), oc.backward_input_rows(wl.coords, wl.grid, wl.batch, 3, G, Wd),
+                  "bf16 input gradient")
+    km.free()
