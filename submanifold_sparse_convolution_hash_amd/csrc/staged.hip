@@ -304,26 +304,32 @@ struct CfgSt {
   static constexpr int KS = CIN / 16;        // MFMA K steps per row
   static constexpr int RC = CIN / 8;         // 16-byte chunks per row
   static constexpr int NCB = COUT / 32;      // 32-column blocks
-  static constexpr int STG = (kStageCap + 1) * RC;  // staged rows and the zero row, in chunks
-  static constexpr int MAXJ = kStageCap * RC / NT;  // staging chunks per thread
-  static constexpr int IW = kTaps3 * kStageUnitRows / 2;  // the staged-row table, in words
-  static constexpr int IPT = (IW + NT - 1) / NT;          // its words per thread
-  static constexpr int SPT = kStageCap / NT;              // staged-row indices per thread
   static constexpr int RED = 3 * 4 * 64;            // float4s of one row block's partial sums
+  // staged rows and the zero row, in chunks; with one column pass the space
+  // also takes the four row blocks' partial sums at once (the zero row is
+  // written again with every unit)
+  static constexpr int STG0 = (kStageCap + 1) * RC;
+  static constexpr int STG = NCB > 1 || STG0 > 4 * RED ? STG0 : 4 * RED;
+  static constexpr int MAXJ = kStageCap * RC / NT;  // staging loads per thread
+  static constexpr int IW = kTaps3 * kStageUnitRows / 2;  // the staged-row table, in words
+  static constexpr int IJ = (IW + NT - 1) / NT;           // its loads per thread
+  static constexpr int SPT = kStageCap / NT;              // staged-row indices per thread
   static constexpr int RPR = STG / RED < 4 ? STG / RED : 4;  // row blocks per round
   // with two column passes, the first pass's partial sums go to a space of
   // their own (the second pass still reads the staged rows)
-  static constexpr int RPRX = RPR < 2 ? RPR : 2;
+  static constexpr int RPRX = 1;
   static constexpr int REDX = NCB > 1 ? RPRX * RED : 1;
   // a wave keeps its first NRES taps' weights in registers for all its
   // units (as many as fit two waves per SIMD without spilling), and loads
   // each other tap's two taps ahead of its multiply; 64 columns run as two
   // passes of 32 over the staged rows
-  static constexpr int NRES = NCB == 2 ? 0 : (CIN == 32 ? 7 : 1);
+  static constexpr int NRES = NCB == 2 ? 0 : (CIN == 32 ? 7 : 0);
   static_assert((CIN == 32 || CIN == 64) && (COUT == 32 || COUT == 64) && CIN * COUT < 64 * 64,
                 "shape");
-  static_assert(RPR >= 1 && kStageCap % NT == 0, "layout");
+  static_assert(kStageCap % NT == 0 && IW % 64 == 0 && (kStageCap * RC) % NT == 0, "layout");
 };
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 // Chunk c of staged row s sits at s*RC + (c ^ swz(s)): rows that follow each
 // other fill the 16 bank groups of a 256-byte line, so that the 16 lanes of
@@ -389,28 +395,9 @@ __global__ __launch_bounds__(256, 2) void k_fwd_staged(
       SR[q] = sr < d.w ? srows[d.z + sr] : -1;
     }
   };
-  // word q of the table: tap e / 64, rows 2 (e % 64) and + 1 (units start on
-  // even rows, and the table's stride is even)
-  auto fetch_table = [&](const int4& d, uint32_t (&X)[C::IPT]) {
-#pragma unroll
-    for (int q = 0; q < C::IPT; ++q) {
-      const int e = tid + C::NT * q;
-      const int k = e >> 6, p = e & 63;
-      X[q] = (e < C::IW && 2 * p < d.y)
-                 ? sidx2[static_cast<int64_t>(k) * istride2 + (d.x >> 1) + p]
-                 : 0xFFFFFFFFu;
-    }
-  };
   auto put_rows = [&](const int (&SR)[C::SPT]) {
 #pragma unroll
     for (int q = 0; q < C::SPT; ++q) sbuf[tid + C::NT * q] = SR[q];
-  };
-  auto put_table = [&](const uint32_t (&X)[C::IPT]) {
-#pragma unroll
-    for (int q = 0; q < C::IPT; ++q) {
-      const int e = tid + C::NT * q;
-      if (e < C::IW) itab[e] = X[q];
-    }
   };
 
   int ju = j0;
@@ -440,39 +427,42 @@ __global__ __launch_bounds__(256, 2) void k_fwd_staged(
     const int s32 = tid_u & 31, h = (tid_u >> 5) & 1;
 
     // ---- stage the unit's distinct neighbour rows, the zero row and its table ----
-    // thread tid moves chunks i = tid + 256 j: chunk i % RC of staged row
-    // i / RC, in two halves of j (fewer registers in flight)
-    // the table goes out with the rows (neither waits for the other)
-    uint32_t X[C::IPT];
-    fetch_table(d, X);
+    // straight from memory into LDS (global_load_lds: lane l of a wave's load
+    // writes the 16 bytes at the load's LDS base + 16 l), every load in
+    // flight at once. Slot i of the staging space holds chunk (i % RC) ^
+    // swz(s) of staged row s = i / RC; slots past the unit's staged rows
+    // load row 0's chunk and are never read.
     if constexpr (NRES < 7) {
       load_a(tap(NRES), 0, AT[0]);
       if constexpr (NRES + 1 < 7) load_a(tap(NRES + 1), 0, AT[1]);
     }
-    if (tid_u < RC) stg[kStageCap * RC + tid_u] = half8{};  // the zero row
-    constexpr int HJ = C::MAXJ / 2;
-#pragma unroll
-    for (int hj = 0; hj < C::MAXJ; hj += HJ) {
-      half8 D[HJ];
-#pragma unroll
-      for (int j = 0; j < HJ; ++j) {
-        const int i = tid_u + C::NT * (hj + j);
-        const int sr = i / RC;
-        D[j] = half8{};
-        if ((C::NT * (hj + j) + 64 * w) / RC < cnt) {  // whole waves past the staged rows skip
-          const int row = sbuf[sr < cnt ? sr : 0];
-          D[j] = bload_h8(rf, sr < cnt ? static_cast<uint32_t>(row) * (CIN * 2) + (i % RC) * 16
-                                       : kOob);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < HJ; ++j) {
-        const int i = tid_u + C::NT * (hj + j);
-        const int sr = i / RC;
-        if (sr < cnt) stg[sr * RC + ((i % RC) ^ swz<RC>(sr))] = D[j];
+#pragma unroll 2
+    for (int j = 0; j < C::MAXJ; ++j) {
+      const int base = (j * (C::NT / 64) + w) * 64;
+      if (base / RC < cnt) {  // whole waves past the staged rows skip
+        const int i = base + lane, sr = i / RC;
+        const int row = sbuf[sr < cnt ? sr : 0];
+        const _Float16* g = feats + static_cast<int64_t>(row) * CIN + ((i % RC) ^ swz<RC>(sr)) * 8;
+        __builtin_amdgcn_global_load_lds(g, (lds_void*)(stg + base), 16, 0, 0);
       }
     }
-    put_table(X);
+    // table word e: tap e / 64, rows 2 (e % 64) and + 1 of the unit (units
+    // start on even rows, the table's stride is even; words past the unit's
+    // rows repeat its last word)
+    {
+      const int pw = (rows + 1) >> 1;
+#pragma unroll 2
+      for (int j = 0; j < C::IJ; ++j) {
+        const int base = (j * (C::NT / 64) + w) * 64;
+        if (base < C::IW) {
+          const int e = base + lane, k = e >> 6, p = e & 63;
+          const uint32_t* g = sidx2 + k * istride2 + (t0 >> 1) + (p < pw ? p : pw - 1);
+          __builtin_amdgcn_global_load_lds(g, (lds_void*)(itab + base), 4, 0, 0);
+        }
+      }
+    }
+    if (tid_u < RC) stg[kStageCap * RC + tid_u] = half8{};  // the zero row
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     // ---- the next unit's staged-row indices, on their way during the multiplies ----
@@ -489,37 +479,60 @@ __global__ __launch_bounds__(256, 2) void k_fwd_staged(
         float16v acc[NRB];
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) acc[rb] = float16v{};
-        auto multiply = [&](const half8 (&Aw)[KS], int k) {
+        // the staged row of this lane's row in each block at tap k (the zero
+        // row when it has none, or past the unit's rows)
+        auto load_e = [&](int k, int (&E)[NRB]) {
 #pragma unroll
           for (int rb = 0; rb < NRB; ++rb) {
             const int r = 32 * rb + s32;
             const int e = r < rows ? it16[k * kStageUnitRows + r] : kStageNone;
-            const int sr = e == kStageNone ? kStageCap : e;
-            const int sw = swz<RC>(sr);
-            half8 B[KS];
+            E[rb] = e == kStageNone ? kStageCap : e;
+          }
+        };
+        // one tap, two row blocks at a time: both blocks' operands requested
+        // first (and the next tap's staged rows behind the first pair), then
+        // the MFMAs alternating between the two blocks' accumulators
+        auto multiply = [&](const half8 (&Aw)[KS], const int (&E)[NRB], int k_next, int (&En)[NRB]) {
 #pragma unroll
-            for (int st = 0; st < KS; ++st) B[st] = stg[sr * RC + ((h * KS + st) ^ sw)];
+          for (int rp = 0; rp < NRB; rp += 2) {
+            const int nb = rp + 1 < NRB ? 2 : 1;
+            half8 B[2][KS];
 #pragma unroll
-            for (int st = 0; st < KS; ++st) {
-              if constexpr (IS_BF16)
-                acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, Aw[st]), __builtin_bit_cast(bf16x8, B[st]), acc[rb],
-                    0, 0, 0);
-              else
-                acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Aw[st], B[st], acc[rb], 0, 0, 0);
-            }
+            for (int q = 0; q < 2; ++q)
+              if (q < nb) {
+                const int sw = swz<RC>(E[rp + q]);
+#pragma unroll
+                for (int st = 0; st < KS; ++st)
+                  B[q][st] = stg[E[rp + q] * RC + ((h * KS + st) ^ sw)];
+              }
+            if (rp == 0) load_e(k_next, En);
+#pragma unroll
+            for (int st = 0; st < KS; ++st)
+#pragma unroll
+              for (int q = 0; q < 2; ++q)
+                if (q < nb) {
+                  if constexpr (IS_BF16)
+                    acc[rp + q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, Aw[st]), __builtin_bit_cast(bf16x8, B[q][st]),
+                        acc[rp + q], 0, 0, 0);
+                  else
+                    acc[rp + q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Aw[st], B[q][st],
+                                                                         acc[rp + q], 0, 0, 0);
+                }
           }
         };
         if (cb > 0) {  // the ring's first taps of this column pass
           load_a(tap(NRES), cb, AT[0]);
           load_a(tap(NRES + 1), cb, AT[1]);
         }
+        int E[2][NRB];
+        load_e(tap(0), E[0]);
 #pragma unroll
         for (int i = 0; i < 7; ++i) {
           if (i < NRES) {
-            if (i < ntaps) multiply(AR[i < NRES ? i : 0], tap(i));
+            if (i < ntaps) multiply(AR[i < NRES ? i : 0], E[i % 2], tap(i + 1), E[(i + 1) % 2]);
           } else {
-            if (i < ntaps) multiply(AT[(i - NRES) % 2], tap(i));
+            if (i < ntaps) multiply(AT[(i - NRES) % 2], E[i % 2], tap(i + 1), E[(i + 1) % 2]);
             if (i + 2 < 7) load_a(tap(i + 2), cb, AT[(i - NRES) % 2]);
           }
         }
