@@ -58,8 +58,8 @@ CSRC = os.path.join(ROOT, "submanifold_sparse_convolution_hash_amd", "csrc")
 MEASURED_TRAFFIC = {
     ("c3_128_128", "forward"): {
         "src": ["forward.hip", "map_build.hip"],  # the kernel, and the map's tile size
-        "sha256": "3301a64e8b95e0107de52b5aa5dc6625d7a998281683df76fc5bb4b3800cc0de",
-        "fetch_kib": 38858.97, "write_kib": 52429.77,
+        "sha256": "b27f659b5e5bbff7988ee07711d38eae4200cb0269a8f1fc9190f16fd7d8e779",
+        "fetch_kib": 38906.19, "write_kib": 52429.85,
         "fetch_factor": 524288.0 / 262156.0, "write_factor": 524288.0 / 524288.0},
 }
 
@@ -76,20 +76,25 @@ KERNELS = {"forward": "k_fwd_pp", "backward_input": "k_fwd_pp", "backward_weight
            "downsample": "k_down_max", "subdivide": "k_subdivide"}
 
 
-def algorithmic_bytes(op, n, cin, cout, ksize, has_order, has_bias, pairs, tile_rows):
+def algorithmic_bytes(op, n, cin, cout, ksize, has_order, has_bias, pairs, tile_rows, staged=None):
     """Compulsory HBM bytes of one launch of the op's dominant kernel: its row
     inputs read once and its output written once; for a 3x3x3 forward (or
     input gradient) the per-tile lists it streams (8 bytes per active pair,
     plus the terminating entry) with the tiles' counts (27 x 2 bytes) and
-    offsets (4 bytes), for the weight gradient the same lists; the processing
-    order when there is one; the weights (fp16 in, or the fp32 weight
-    gradient out) and the bias."""
+    offsets (4 bytes), or with the staged kernel (staged = (units, staged
+    rows)) the staged plan it reads (16 bytes per unit, 4 per staged row, a
+    2-byte table entry per (tap, row)); for the weight gradient the lists;
+    the processing order when there is one; the weights (fp16 in, or the
+    fp32 weight gradient out) and the bias."""
     K = 27 if ksize == 3 else 1
     b = n * cin * 2 + n * cout * 2
     b += K * cin * cout * (4 if op == "backward_weight" else 2)
     if ksize == 3:
-        n_tiles = -(-n // tile_rows)
-        b += (pairs + 1) * 8 + n_tiles * (27 * 2 + 4) + 4
+        if staged:
+            b += staged[0] * 16 + staged[1] * 4 + 27 * 2 * (n + (n & 1))
+        else:
+            n_tiles = -(-n // tile_rows)
+            b += (pairs + 1) * 8 + n_tiles * (27 * 2 + 4) + 4
         if has_order:
             b += n * 4
     if has_bias and op in ("forward", "forward_masked"):
@@ -353,6 +358,13 @@ def main():
         build_ms.append((time.perf_counter() - t) * 1e3)
     pairs = km.active_pairs(L.ksize)
     flops = 2.0 * pairs * L.cin * L.cout
+    # the kernel the op's forward takes: the staged one on a map with a plan
+    cin_t, cout_t = (L.cout, L.cin) if op == "backward_input" else (L.cin, L.cout)
+    staged = None
+    if op in ("forward", "backward_input") and L.ksize == 3 and km.staged()[0] > 0 and \
+            sc.forward_kernel(wl.n, pairs, cin_t, cout_t, 3) == 2:
+        staged = km.staged()
+    kname = "k_fwd_staged" if staged else KERNELS[op]
 
     # Steps and kernels call the C ABI directly (ctypes, arguments built
     # once): the Python binding's checks would add host time to every launch.
@@ -437,7 +449,7 @@ def main():
         kernel()
     k_us = timed(kernel, args.steps)
     alg_bytes = algorithmic_bytes(op, wl.n, L.cin, L.cout, L.ksize, args.morton, bias is not None,
-                                  pairs, km.tile_rows)
+                                  pairs, km.tile_rows, staged)
     achieved_gbs = alg_bytes / (k_us * 1e-6) / 1e9
     print(f"[bench] {op} kernels {k_us:.1f} us, {achieved_gbs:.0f} GB/s algorithmic", file=sys.stderr, flush=True)
 
@@ -532,7 +544,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(args.config, op, args.morton),
-                     "kernel": KERNELS[op], "kernel_us": round(k_us, 2),
+                     "kernel": kname, "kernel_us": round(k_us, 2),
                      "algorithmic_bytes": alg_bytes,
                      "mfma_effective_frac": round(flops / (k_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
                      "measured_ceilings": dict(ceil, **{

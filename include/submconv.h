@@ -155,6 +155,13 @@ int32_t submconv_map_tile_rows(submconv_map_t map);
  * 2 * active_pairs * Cin * Cout flops. Negative on a bad argument. */
 int64_t submconv_map_active_pairs(submconv_map_t map, int32_t ksize);
 
+/* Size of the map's staged plan (see SUBMCONV_FLAG_STAGED): out[0] = units,
+ * out[1] = staged rows over all units; both 0 when the map has none. The
+ * plan's device memory is 16 bytes per unit, 4 per staged row and 54 per
+ * row (n rounded up to even). Returns 0, or a negative status for a NULL
+ * argument. */
+int submconv_map_staged(submconv_map_t map, int64_t out[2]);
+
 /*
  * submconv_map_export -- write the neighbour map in the caller's row order
  * (the indice map the README's "What's in it" SparseTensor row caches; the

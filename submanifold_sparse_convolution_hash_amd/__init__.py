@@ -18,7 +18,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Optional, Sequence
+from typing import Optional, Sequence, Tuple
 
 import torch
 
@@ -70,6 +70,7 @@ def load_library():
         "submconv_map_num_rows": ([P], I64),
         "submconv_map_tile_rows": ([P], I32),
         "submconv_map_active_pairs": ([P, I32], I64),
+        "submconv_map_staged": ([P, P], I32),
         "submconv_map_export": ([P, P, P], ctypes.c_int),
         "submconv_map_order": ([P, P, P], ctypes.c_int),
         "submconv_map_free": ([P], ctypes.c_int),
@@ -177,6 +178,12 @@ class KernelMap:
         if v < 0:
             _check(v)
         return v
+
+    def staged(self) -> Tuple[int, int]:
+        """(units, staged rows) of the map's staged plan; (0, 0) without one."""
+        v = (ctypes.c_int64 * 2)()
+        _check(load_library().submconv_map_staged(self.handle, v))
+        return int(v[0]), int(v[1])
 
     def export(self) -> torch.Tensor:
         """[N,27] int32 neighbour rows in the caller's order, -1 for none."""

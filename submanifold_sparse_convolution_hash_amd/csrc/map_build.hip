@@ -948,6 +948,14 @@ extern "C" int64_t submconv_map_active_pairs(submconv_map_t map, int32_t ksize) 
   return set_error(SUBMCONV_ERR_INVALID_ARG, "ksize = %d is not 1 or 3", ksize);
 }
 
+extern "C" int submconv_map_staged(submconv_map_t map, int64_t out[2]) {
+  clear_error();
+  if (!map || !out) return set_error(SUBMCONV_ERR_INVALID_ARG, "map or out is NULL");
+  out[0] = map->m.staged.n_units;
+  out[1] = map->m.staged.n_rows;
+  return SUBMCONV_OK;
+}
+
 extern "C" int submconv_map_export(submconv_map_t map, int32_t* kmap, hipStream_t stream) {
   clear_error();
   if (!map) return set_error(SUBMCONV_ERR_INVALID_ARG, "map is NULL");

@@ -55,12 +55,24 @@ __device__ __forceinline__ int hash_slot(int32_t key) {
 }
 static_assert(kHashSlots == 1 << 10, "hash bits");
 
+// A part's neighbour rows usually lie within a narrow range of row indices
+// (in raster order a few planes of the grid, in Morton order most often
+// within 64k rows): a bitmap over [kmin, kmin + kBitmapBits) then lists them
+// distinct and sorted at once, a row's rank among them being the set bits
+// before its own. Wider parts take the hash table and a rank count.
+constexpr int kBitmapBits = 1 << 16;
+constexpr int kBitmapWords = kBitmapBits / 32;
+constexpr int kWordsPerThread = kBitmapWords / kPlanThreads;
+
 struct PlanLds {
   int32_t H[kHashSlots];   // hash table of neighbour rows, -1 empty
-  int32_t L[kStageCap];    // the distinct rows, then sorted
+  alignas(16) int32_t L[kStageCap];  // the distinct rows
   uint16_t V[kHashSlots];  // slot -> position in the sorted rows
   int count;               // rows inserted into H
   int wsum[kPlanThreads / 64];
+  uint32_t BM[kBitmapWords];   // bit i: row kmin + i is a neighbour
+  uint16_t WP[kBitmapWords];   // set bits in the words before each word
+  int kmin, kmax;
 };
 
 __device__ __forceinline__ int find_slot(const PlanLds& P, int32_t key) {
@@ -133,6 +145,100 @@ __device__ int collect(const int32_t (&key)[kCandsPerThread], PlanLds& P) {
   return U;
 }
 
+// The bitmap path: the range of the candidates, and when it is narrower than
+// kBitmapBits, their bitmap and its word prefix; returns the number of
+// distinct rows, or -1 for a wider range (the same in every thread).
+__device__ int collect_bitmap(const int32_t (&key)[kCandsPerThread], PlanLds& P) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int mn = INT_MAX, mx = -1;
+#pragma unroll
+  for (int q = 0; q < kCandsPerThread; ++q)
+    if (key[q] >= 0) {
+      mn = key[q] < mn ? key[q] : mn;
+      mx = key[q] > mx ? key[q] : mx;
+    }
+  for (int off = 32; off > 0; off >>= 1) {
+    const int a = __shfl_xor(mn, off, 64), b = __shfl_xor(mx, off, 64);
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+  }
+  if (tid == 0) {
+    P.kmin = INT_MAX;
+    P.kmax = -1;
+  }
+  __syncthreads();
+  if (lane == 0) {
+    atomicMin(&P.kmin, mn);
+    atomicMax(&P.kmax, mx);
+  }
+  __syncthreads();
+  mn = P.kmin;
+  mx = P.kmax;
+  if (mx < 0) return 0;
+  if (mx - mn >= kBitmapBits) return -1;
+  // only the words the range covers
+  const int nw = ((mx - mn) >> 5) + 1;
+  for (int i = tid; i < nw; i += kPlanThreads) P.BM[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kCandsPerThread; ++q)
+    if (key[q] >= 0) {
+      const int b = key[q] - mn;
+      atomicOr(&P.BM[b >> 5], 1u << (b & 31));
+    }
+  __syncthreads();
+  // thread tid's words tid*W .. tid*W + W - 1 (of the nw in use), then a
+  // block scan of their counts
+  const int wpt = (nw + kPlanThreads - 1) / kPlanThreads;
+  int cnt = 0;
+  for (int i = 0; i < wpt; ++i) {
+    const int wd = tid * wpt + i;
+    cnt += wd < nw ? __popc(P.BM[wd]) : 0;
+  }
+  int incl = cnt;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) P.wsum[w] = incl;
+  __syncthreads();
+  int pos = incl - cnt, total = 0;
+  for (int ww = 0; ww < kPlanThreads / 64; ++ww) {
+    pos += ww < w ? P.wsum[ww] : 0;
+    total += P.wsum[ww];
+  }
+  for (int i = 0; i < wpt; ++i) {
+    const int wd = tid * wpt + i;
+    if (wd < nw) {
+      P.WP[wd] = static_cast<uint16_t>(pos);
+      pos += __popc(P.BM[wd]);
+    }
+  }
+  if (tid == 0) P.count = nw;  // (the words in use, for bitmap_rows)
+  __syncthreads();
+  return total;
+}
+
+// rank of candidate row r among the bitmap's rows
+__device__ __forceinline__ int bitmap_rank(const PlanLds& P, int32_t r) {
+  const int b = r - P.kmin;
+  return P.WP[b >> 5] + __popc(P.BM[b >> 5] & ((1u << (b & 31)) - 1u));
+}
+
+// the bitmap's rows in order to srows
+__device__ void bitmap_rows(const PlanLds& P, int32_t* __restrict__ srows) {
+  const int mn = P.kmin, nw = P.count;
+  for (int wd = threadIdx.x; wd < nw; wd += kPlanThreads) {
+    uint32_t m = P.BM[wd];
+    int pos = P.WP[wd];
+    while (m) {
+      const int b = __ffs(m) - 1;
+      m &= m - 1;
+      srows[pos++] = mn + 32 * wd + b;
+    }
+  }
+}
+
 // Places each distinct row at its rank among them (rows ascending): V[slot]
 // = rank for the row's hash slot, and the sorted rows go to srows. The rows
 // are distinct, so a row's rank is the number of smaller ones.
@@ -171,7 +277,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_stage_count(const int32_t* __r
     }
     int32_t key[kCandsPerThread];
     load_cands(nbr, n, t0 + a, b - a, key);
-    const int U = collect(key, P);
+    int U = collect_bitmap(key, P);
+    if (U < 0) U = collect(key, P);
     if (U <= kStageCap || b - a <= kStageMinRows) {
       if (threadIdx.x == 0) tile_units[tile * kMaxUnitsPerTile + nu] = make_int4(a, b - a, U, 0);
       ++nu;
@@ -258,8 +365,14 @@ __global__ __launch_bounds__(kPlanThreads) void k_stage_fill(
     const int64_t u0 = t0 + d.x;
     int32_t key[kCandsPerThread];
     load_cands(nbr, n, u0, d.y, key);
-    const int U = collect(key, P);
-    rank_rows(P, U, srows + so);
+    int U = collect_bitmap(key, P);
+    const bool bitmap = U >= 0;
+    if (bitmap) {
+      bitmap_rows(P, srows + so);
+    } else {
+      U = collect(key, P);
+      rank_rows(P, U, srows + so);
+    }
     const int cands = kTaps3 * d.y;
 #pragma unroll
     for (int q = 0; q < kCandsPerThread; ++q) {
@@ -267,7 +380,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_stage_fill(
       if (c < cands) {
         const int k = c / d.y;
         sidx[static_cast<int64_t>(k) * stride + u0 + (c - k * d.y)] =
-            key[q] >= 0 ? P.V[find_slot(P, key[q])] : kStageNone;
+            key[q] < 0 ? kStageNone
+                       : (bitmap ? bitmap_rank(P, key[q]) : P.V[find_slot(P, key[q])]);
       }
     }
     if (threadIdx.x == 0)
@@ -580,7 +694,10 @@ __global__ __launch_bounds__(256, 2) void k_fwd_staged(
                   typedef _Float16 half4 __attribute__((ext_vector_type(4)));
                   const half4 o = {round16<IS_BF16>(t[0] + b4[0]), round16<IS_BF16>(t[1] + b4[1]),
                                    round16<IS_BF16>(t[2] + b4[2]), round16<IS_BF16>(t[3] + b4[3])};
-                  __builtin_nontemporal_store(o, reinterpret_cast<half4*>(out + orow * COUT + col));
+                  // (an ordinary store: the L2 merges a row's 8-byte pieces into whole
+                  // lines, where non-temporal stores reached memory as partial lines,
+                  // 2.9x the output's bytes)
+                  *reinterpret_cast<half4*>(out + orow * COUT + col) = o;
                 }
               }
             }

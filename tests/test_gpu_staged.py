@@ -62,6 +62,9 @@ def test_c5_layers_staged(dev, morton):
     km = sc.build_map(coords, wl.grid, wl.batch, morton=morton)
     kp = sc.build_map(coords, wl.grid, wl.batch, morton=morton, staged=False)
     ko = sc.build_map(coords, wl.grid, wl.batch, morton=not morton)
+    # dense: the plan is built by default; every row staged at least once
+    units, srows = km.staged()
+    assert units >= -(-wl.n // 128) and srows >= wl.n, (units, srows)
     kmap = oc.kernel_map(wl.coords, wl.grid, wl.batch, 3)
     rows = np.random.default_rng(11).choice(wl.n, 3000, replace=False)
     rows_t = torch.from_numpy(rows).to(dev)
@@ -126,6 +129,9 @@ def test_forced_staged_ragged(dev, n, cin, cout):
     kmap = oc.kernel_map(coords, (G, G, G), 1, 3)
     _assert_close(out, oc.submconv_rows(kmap, feats, W, b), f"forced staged n={n} {cin}->{cout}")
     kp = sc.build_map(_to(dev, coords), (G, G, G), 1, staged=False)
+    units, srows = km.staged()
+    assert 1 <= units <= -(-n // 16) and n <= srows <= 27 * n, (units, srows)
+    assert kp.staged() == (0, 0)
     outp = sc.forward(kp, _to(dev, feats), _to(dev, W), _to(dev, b)).float().cpu().numpy()
     _assert_close(out, outp.astype(np.float64), "staged vs compacted")
     km.free()
