@@ -61,6 +61,11 @@ MEASURED_TRAFFIC = {
         "sha256": "b27f659b5e5bbff7988ee07711d38eae4200cb0269a8f1fc9190f16fd7d8e779",
         "fetch_kib": 38906.19, "write_kib": 52429.85,
         "fetch_factor": 524288.0 / 262156.0, "write_factor": 524288.0 / 524288.0},
+    ("c5_512_chain", "forward"): {
+        "src": ["staged.hip", "map_build.hip"],  # the staged kernel (64 -> 32), and its plan
+        "sha256": "b70e037b0eaa2134462905fc66000df6ceea6b3ba4642c678da35c54ee960456",
+        "fetch_kib": 182132.80, "write_kib": 93584.43,
+        "fetch_factor": 524288.0 / 262168.0, "write_factor": 524288.0 / 524288.0},
 }
 
 METRICS = {
