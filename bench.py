@@ -63,8 +63,8 @@ MEASURED_TRAFFIC = {
         "fetch_factor": 524288.0 / 262156.0, "write_factor": 524288.0 / 524288.0},
     ("c5_512_chain", "forward"): {
         "src": ["staged.hip", "map_build.hip"],  # the staged kernel (64 -> 32), and its plan
-        "sha256": "b70e037b0eaa2134462905fc66000df6ceea6b3ba4642c678da35c54ee960456",
-        "fetch_kib": 182132.80, "write_kib": 93584.43,
+        "sha256": "ecf66e112f3c5ef6284cd9ddf832c4b6ec20fe53140c97c40a27b36299ab1727",
+        "fetch_kib": 171773.78, "write_kib": 95631.12,
         "fetch_factor": 524288.0 / 262168.0, "write_factor": 524288.0 / 524288.0},
 }
 

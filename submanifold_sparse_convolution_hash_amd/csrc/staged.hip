@@ -433,11 +433,13 @@ struct CfgSt {
   // their own (the second pass still reads the staged rows)
   static constexpr int RPRX = 1;
   static constexpr int REDX = NCB > 1 ? RPRX * RED : 1;
-  // a wave keeps its first NRES taps' weights in registers for all its
-  // units (as many as fit two waves per SIMD without spilling), and loads
-  // each other tap's two taps ahead of its multiply; 64 columns run as two
-  // passes of 32 over the staged rows
-  static constexpr int NRES = NCB == 2 ? 0 : (CIN == 32 ? 7 : 0);
+  // with 32 output columns a wave keeps all 7 of its taps' weights in
+  // registers for all its units (at 64 input channels that spills a few
+  // registers, saved and restored outside the multiply loop: still faster
+  // than reloading 108 KiB of weights per unit); 64 columns run as two
+  // passes of 32 over the staged rows and load each tap's weights two taps
+  // ahead of its multiply
+  static constexpr int NRES = NCB == 2 ? 0 : 7;
   static_assert((CIN == 32 || CIN == 64) && (COUT == 32 || COUT == 64) && CIN * COUT < 64 * 64,
                 "shape");
   static_assert(kStageCap % NT == 0 && IW % 64 == 0 && (kStageCap * RC) % NT == 0, "layout");
