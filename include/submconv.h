@@ -77,8 +77,10 @@ extern "C" {
 /* the staged plan: on a dense map (at least 12 neighbours per row on
  * average, centre included, as on a surface) the build also cuts the rows
  * into units of up to 128 whose distinct neighbour rows (at most 512) a
- * forward of 32 or 64 channels in and out stages once in LDS, instead of
- * gathering each (row, tap) pair; it costs 54 bytes per row plus 4 per staged
+ * forward of 32 -> 32, 64 -> 32, 32 -> 64, 128 -> 256 or 256 -> 256 channels
+ * stages once in LDS, instead of gathering each (row, tap) pair (the input
+ * gradient of such a shape too, when its transposed shape is one of them);
+ * it costs 54 bytes per row plus 4 per staged
  * row. SUBMCONV_FLAG_STAGED builds it on any map, SUBMCONV_FLAG_NO_STAGED on
  * none (such forwards then take the compacted lists) */
 #define SUBMCONV_FLAG_STAGED 16u
@@ -289,9 +291,10 @@ int submconv_forward_prepared(submconv_map_t map, const uint16_t* feats, submcon
 /*
  * submconv_forward_kernel -- which kernel a forward of this shape takes on a
  * map built with default flags, on the host, without a device: 2 the staged
- * gather-GEMM (a 3x3x3 forward of 32 -> 32, 64 -> 32 or 32 -> 64 channels on
- * a dense map, see SUBMCONV_FLAG_STAGED), 1 the MFMA gather-GEMM on the
- * per-tile lists, 0 the VALU kernel, or a negative status:
+ * gather-GEMM (a 3x3x3 forward of 32 -> 32, 64 -> 32, 32 -> 64, 128 -> 256
+ * or 256 -> 256 channels on a dense map, see SUBMCONV_FLAG_STAGED), 1 the
+ * MFMA gather-GEMM on the per-tile lists, 0 the VALU kernel, or a negative
+ * status:
  * SUBMCONV_ERR_UNSUPPORTED_SHAPE for an MFMA shape whose features or lists
  * reach 2 GiB (submconv_forward's limit), or a shape error. n rows,
  * active_pairs as submconv_map_active_pairs reports them.

@@ -301,7 +301,8 @@ def prepare_weights(W: torch.Tensor, input_grad: bool = False) -> Weights:
 def forward_kernel(n: int, active_pairs: int, cin: int, cout: int, ksize: int = 3) -> int:
     """The kernel a forward of this shape takes on a map built with default
     flags (host only): 2 the staged MFMA kernel (dense maps, 32 -> 32,
-    64 -> 32 or 32 -> 64 channels), 1 the MFMA kernel on the per-tile lists,
+    64 -> 32, 32 -> 64, 128 -> 256 or 256 -> 256 channels), 1 the MFMA kernel
+    on the per-tile lists,
     0 VALU; raises :class:`SubmconvError` for a shape the library rejects
     (e.g. MFMA features of 2 GiB or more)."""
     v = int(load_library().submconv_forward_kernel(int(n), int(active_pairs), int(cin), int(cout),

@@ -13,20 +13,25 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsubmconv.so")
 SOURCES = ["map_build.hip", "forward.hip", "backward.hip", "coord_ops.hip", "masked.hip",
-           "staged.hip"]
+           "staged.hip", "staged_wide.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++20", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         # keep MFMA accumulators in VGPRs: the kernels read and write them
-         # through LDS every step, which AGPRs would cost extra moves for
-         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", os.path.join(os.path.dirname(HERE), "include")]
+# keep MFMA accumulators in VGPRs: most kernels read and write them through
+# LDS every step, which AGPRs would cost extra moves for
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+# sources whose MFMA accumulators stay in registers for a whole unit (128 per
+# lane) are built without it: the accumulators take the AGPRs, the operands
+# the VGPRs
+AGPR_SOURCES = {"staged_wide.hip"}
 
 
 def _compile(src, verbose):
     obj = os.path.join(CSRC, "_build", os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    flags = FLAGS + ([] if src in AGPR_SOURCES else VGPR_FORM)
+    cmd = [HIPCC] + flags + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

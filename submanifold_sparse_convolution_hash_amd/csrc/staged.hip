@@ -758,6 +758,7 @@ int launch_staged(const Map& m, const _Float16* feats, const _Float16* wp, const
 template <bool IS_BF16>
 int staged_typed(const Map& m, int cin, int cout, const _Float16* feats, const _Float16* wp,
                  const float* bias, _Float16* out, hipStream_t stream) {
+  if (cout == 256) return forward_staged_wide(m, cin, IS_BF16, feats, wp, bias, out, stream);
   if (cin == 64) return launch_staged<64, 32, IS_BF16>(m, feats, wp, bias, out, stream);
   if (cout == 64) return launch_staged<32, 64, IS_BF16>(m, feats, wp, bias, out, stream);
   return launch_staged<32, 32, IS_BF16>(m, feats, wp, bias, out, stream);
@@ -789,7 +790,8 @@ int staged_fill(const int32_t* nbr, int64_t n, const StagedTemps& tp, const Stag
 
 bool staged_shape(int cin, int cout) {
   // (64 -> 64 needs more registers than two waves per SIMD have)
-  return (cin == 32 && (cout == 32 || cout == 64)) || (cin == 64 && cout == 32);
+  return (cin == 32 && (cout == 32 || cout == 64)) || (cin == 64 && cout == 32) ||
+         ((cin == 128 || cin == 256) && cout == 256);
 }
 
 bool staged_takes(const Map& m, int ksize, int cin, int cout) {

@@ -134,13 +134,16 @@ int staged_count(const int32_t* nbr, int64_t n, const StagedTemps& tp, hipStream
 int staged_fill(const int32_t* nbr, int64_t n, const StagedTemps& tp, const Staged& plan,
                 hipStream_t stream);
 
-// The staged forward takes a 3x3x3 forward of cin in {32, 64} and cout in
-// {32, 64} channels on a map with a staged plan (weights in MFMA fragment
-// order).
+// The staged forward takes a 3x3x3 forward of 32 -> 32, 32 -> 64, 64 -> 32,
+// 128 -> 256 or 256 -> 256 channels on a map with a staged plan (weights in
+// MFMA fragment order); forward_staged_wide runs the 256-column shapes.
 bool staged_shape(int cin, int cout);
 bool staged_takes(const Map& m, int ksize, int cin, int cout);
 int forward_staged(const Map& m, int cin, int cout, bool bf16, const _Float16* feats,
                    const _Float16* wp, const float* bias, _Float16* out, hipStream_t stream);
+int forward_staged_wide(const Map& m, int cin, bool bf16, const _Float16* feats,
+                        const _Float16* wp, const float* bias, _Float16* out,
+                        hipStream_t stream);
 
 // Allocates the device's staging buffer for weights passed as the caller
 // holds them (once per device; every map build calls it).

@@ -86,8 +86,8 @@ def test_forward_kernel_choice_and_buffer_limit(lib):
     for its channel counts while features and lists stay below 2 GiB (its
     32-bit buffer offsets), an explicit SUBMCONV_ERR_UNSUPPORTED_SHAPE above,
     the VALU kernel for other channel counts (64-bit addressing, no limit);
-    on dense maps (12 or more neighbours per row) the staged kernel for
-    32 -> 32, 64 -> 32 and 32 -> 64 channels."""
+    on dense maps (12 or more neighbours per row) the staged kernels for
+    32 -> 32, 64 -> 32, 32 -> 64, 128 -> 256 and 256 -> 256 channels."""
     f = lib.submconv_forward_kernel
     f.restype = ctypes.c_int
     f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
@@ -96,6 +96,10 @@ def test_forward_kernel_choice_and_buffer_limit(lib):
     assert f(1495574, 31_200_000, 64, 64, 3) == 1   # (not for 64 -> 64)
     assert f(1495574, 5_000_000, 64, 32, 3) == 1    # under 12 neighbours per row
     assert f(1495574, 31_200_000, 64, 32, 1) == 1   # a 1x1x1 layer
+    assert f(744643, 15_556_763, 256, 256, 3) == 2  # the 256^3 shells
+    assert f(744643, 15_556_763, 128, 256, 3) == 2
+    assert f(744643, 15_556_763, 256, 128, 3) == 1
+    assert f(744643, 15_556_763, 128, 128, 3) == 1
     assert f(1000, 4000, 256, 256, 1) == 1
     assert f(1000, 4000, 96, 96, 3) == 0        # no MFMA tile for 96 channels
     assert f(1000, 4000, 256, 64, 3) == 0       # Cin 256 needs Cout a multiple of 128

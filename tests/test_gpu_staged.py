@@ -1,12 +1,13 @@
-"""GPU parity of the staged forward (dense maps, 32 or 64 channels) against the
-CPU oracle, through the C ABI.
+"""GPU parity of the staged forwards (dense maps) against the CPU oracle,
+through the C ABI.
 
 On a dense map the build also makes the staged plan (units of up to 128 rows
 whose distinct neighbour rows fit in LDS), and forwards of 32 -> 32, 64 -> 32
-and 32 -> 64 channels take it. The tolerance is the forward's:
-|gpu - oracle| <= 1e-3 + 1e-2 |oracle| per element. A row's result is summed
-in the same order whatever unit it falls in, so maps in raster and Morton
-order give the same bits.
+and 32 -> 64 channels (k_fwd_staged) and of 128 -> 256 and 256 -> 256
+channels (k_fwd_staged_wide, the rows staged in 64-channel slices) take it.
+The tolerance is the forward's: |gpu - oracle| <= 1e-3 + 1e-2 |oracle| per
+element. A row's result is summed in the same order whatever unit it falls
+in, so maps in raster and Morton order give the same bits.
 """
 import numpy as np
 import pytest
@@ -19,7 +20,7 @@ from oracle import oracle as op
 from test_gpu_parity import (_assert_close, _bf16_tensor, _bf16_values, _say, _sc, _to, dev,  # noqa: F401
                              gpu)
 
-STAGED_SHAPES = [(32, 32), (64, 32), (32, 64)]
+STAGED_SHAPES = [(32, 32), (64, 32), (32, 64), (128, 256), (256, 256)]
 
 
 def _dense_cube(G, batch=1):
@@ -46,6 +47,11 @@ def test_kernel_choice_reports_the_staged_forward(dev):
     assert sc.forward_kernel(1000, 20000, 128, 32) == 1
     assert sc.forward_kernel(1000, 3500, 64, 32) == 1
     assert sc.forward_kernel(1000, 20000, 64, 32, ksize=1) == 1
+    assert sc.forward_kernel(1000, 20000, 256, 256) == 2
+    assert sc.forward_kernel(1000, 20000, 128, 256) == 2
+    assert sc.forward_kernel(1000, 20000, 256, 128) == 1
+    assert sc.forward_kernel(1000, 20000, 128, 128) == 1
+    assert sc.forward_kernel(1000, 3500, 256, 256) == 1
 
 
 @gpu
@@ -87,6 +93,46 @@ def test_c5_layers_staged(dev, morton):
     dx = sc.backward_input(km, g, _to(dev, L.W))
     ref = oc.backward_input_rows(wl.coords, wl.grid, wl.batch, 3, g.cpu().numpy(), L.W, rows)
     _assert_close(dx[rows_t].float().cpu().numpy(), ref, "staged c5 input gradient")
+    for k in (km, kp, ko):
+        k.free()
+
+
+@gpu
+@pytest.mark.slow
+def test_c4_layer_staged_wide(dev):
+    # the 256^3 shells (two items, 256 -> 256): the forward against the oracle
+    # on sampled rows and against the compacted-list kernel on every row,
+    # raster against Morton order bit for bit; the input gradient (also
+    # 256 -> 256, so staged too) on sampled rows
+    sc = _sc()
+    wl = workloads.make("c4_256_shell")
+    L = wl.layers[0]
+    coords = _to(dev, wl.coords)
+    _say(f"[staged c4] N={wl.n} {L.cin}->{L.cout}")
+    km = sc.build_map(coords, wl.grid, wl.batch)
+    kp = sc.build_map(coords, wl.grid, wl.batch, staged=False)
+    ko = sc.build_map(coords, wl.grid, wl.batch, morton=True)
+    units, srows = km.staged()
+    assert units >= -(-wl.n // 128) and srows >= wl.n, (units, srows)
+    assert sc.forward_kernel(wl.n, km.active_pairs(3), L.cin, L.cout) == 2
+    kmap = oc.kernel_map(wl.coords, wl.grid, wl.batch, 3)
+    rows = np.concatenate([np.random.default_rng(21).choice(wl.n, 1500, replace=False), [0, wl.n - 1]])
+    rows_t = torch.from_numpy(rows).to(dev)
+    x, W = _to(dev, wl.feats), _to(dev, L.W)
+    b = _to(dev, (np.random.default_rng(22).standard_normal(L.cout) * 0.1).astype(np.float32))
+    y = sc.forward(km, x, W, b)
+    ref = oc.submconv_rows(kmap, wl.feats, L.W, b.cpu().numpy(), rows)
+    _assert_close(y[rows_t].float().cpu().numpy(), ref, "staged c4 forward")
+    yp = sc.forward(kp, x, W, b)
+    _assert_close(y.float().cpu().numpy(), yp.float().cpu().numpy().astype(np.float64),
+                  "staged vs compacted, c4")
+    assert torch.equal(y, sc.forward(ko, x, W, b)), "raster and Morton order differ"
+    assert torch.equal(y, sc.forward(km, x, W, b)), "not reproducible"
+    g = torch.from_numpy(workloads.normal_f16(np.random.default_rng(23), (wl.n, L.cout))).to(dev)
+    _say("[staged c4] input gradient")
+    dx = sc.backward_input(km, g, W)
+    ref = oc.backward_input_rows(wl.coords, wl.grid, wl.batch, 3, g.cpu().numpy(), L.W, rows)
+    _assert_close(dx[rows_t].float().cpu().numpy(), ref, "staged c4 input gradient")
     for k in (km, kp, ko):
         k.free()
 
