@@ -66,6 +66,12 @@ MEASURED_TRAFFIC = {
         "sha256": "ecf66e112f3c5ef6284cd9ddf832c4b6ec20fe53140c97c40a27b36299ab1727",
         "fetch_kib": 171773.78, "write_kib": 95631.12,
         "fetch_factor": 524288.0 / 262168.0, "write_factor": 524288.0 / 524288.0},
+    ("c5_512_chain", "backward_weight"): {
+        # the staged weight gradient (64 -> 32) and its reduce: the call bench.py times
+        "src": ["staged_bwd.hip", "map_build.hip"],
+        "sha256": "6abc658d79adc8f4928d6be89051478f2c634bd97be4e335b81311d9d6cc7ac5",
+        "fetch_kib": 195407.1 + 27656.5, "write_kib": 55296.0 + 216.0,
+        "fetch_factor": 524288.0 / 262155.9, "write_factor": 524288.0 / 524288.0},
     ("c4_256_shell", "forward"): {
         "src": ["staged_wide.hip", "map_build.hip"],  # the staged kernel (256 -> 256), and its plan
         "sha256": "03b56b3fe31da67445cd61435f51401a8c74183c0487837a54f0dffc55309d06",
@@ -375,6 +381,11 @@ def main():
             sc.forward_kernel(wl.n, pairs, cin_t, cout_t, 3) == 2:
         staged = km.staged()
     kname = ("k_fwd_staged_wide" if cout_t == 256 else "k_fwd_staged") if staged else KERNELS[op]
+    # the weight gradient on the staged plan (dense maps, these shapes)
+    if op == "backward_weight" and L.ksize == 3 and km.staged()[0] > 0 and \
+            (L.cin, L.cout) in ((32, 32), (64, 32), (32, 64)):
+        staged = km.staged()
+        kname = "k_bwd_weight_staged"
 
     # Steps and kernels call the C ABI directly (ctypes, arguments built
     # once): the Python binding's checks would add host time to every launch.

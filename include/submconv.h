@@ -338,8 +338,12 @@ int submconv_backward_input_prepared(submconv_map_t map, const uint16_t* grad_ou
 
 /*
  * submconv_backward_weight_workspace_bytes -- device workspace that
- * submconv_backward_weight needs for this map and shape (0 is possible).
- * Negative on a bad argument.
+ * submconv_backward_weight needs for this map and shape (0 is possible):
+ * fp32 partial sums of dW per workgroup. On a map with a staged plan (see
+ * SUBMCONV_FLAG_STAGED) a 3x3x3 weight gradient of 32 -> 32, 64 -> 32 or
+ * 32 -> 64 channels works per staged unit, with partials of all 27 taps per
+ * workgroup (about 54 MiB at 64 -> 32 on 256 compute units). Negative on a
+ * bad argument.
  */
 int64_t submconv_backward_weight_workspace_bytes(submconv_map_t map, int32_t cin, int32_t cout,
                                                  int32_t ksize);

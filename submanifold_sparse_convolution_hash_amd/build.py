@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsubmconv.so")
 SOURCES = ["map_build.hip", "forward.hip", "backward.hip", "coord_ops.hip", "masked.hip",
-           "staged.hip", "staged_wide.hip"]
+           "staged.hip", "staged_wide.hip", "staged_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++20", "-fPIC", "-Wall",
@@ -25,7 +25,7 @@ VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 # sources whose MFMA accumulators stay in registers for a whole unit (128 per
 # lane) are built without it: the accumulators take the AGPRs, the operands
 # the VGPRs
-AGPR_SOURCES = {"staged_wide.hip"}
+AGPR_SOURCES = {"staged_wide.hip", "staged_bwd.hip"}
 
 
 def _compile(src, verbose):

@@ -727,6 +727,10 @@ int dispatch_w(const Map& m, int K, int cout, const _Float16* feats, const _Floa
 int64_t workspace_bytes(const Map& m, int cin, int cout, int ksize, int64_t max_blocks) {
   if (!use_mfma_w(cin, cout) || m.n == 0) return 0;
   const int K = ksize == 3 ? kTaps3 : 1;
+  // the staged kernel on a dense map, when its partials (all 27 taps per
+  // workgroup) fit
+  if (const int64_t sb = staged_wgrad_blocks(m, ksize, cin, cout); sb > 0 && sb * K <= max_blocks)
+    return sb * K * cin * cout * static_cast<int64_t>(sizeof(float));
   const int64_t blocks = use_pp_w(cin, cout)
                              ? split_for(m, K, cin, cout, max_blocks).blocks()
                              : static_cast<int64_t>(runs_for(m, K, max_blocks).runs) * K;
@@ -776,6 +780,8 @@ int backward_weight_impl(const Map& m, const uint16_t* feats, const uint16_t* gr
                        static_cast<long long>(m.n), cin, cout,
                        static_cast<long long>(m.active_pairs));
     const int64_t mb = max_blocks;
+    if (const int64_t sb = staged_wgrad_blocks(m, ksize, cin, cout); sb > 0 && sb * K <= mb)
+      return backward_weight_staged(m, cin, cout, f, g, part, grad_w, stream);
     switch (cin) {
       case 32: return dispatch_w<32>(m, K, cout, f, g, part, grad_w, mb, stream);
       case 64: return dispatch_w<64>(m, K, cout, f, g, part, grad_w, mb, stream);

@@ -145,6 +145,15 @@ int forward_staged_wide(const Map& m, int cin, bool bf16, const _Float16* feats,
                         const _Float16* wp, const float* bias, _Float16* out,
                         hipStream_t stream);
 
+// The staged weight gradient (3x3x3, fp16; 32 -> 32, 64 -> 32 or 32 -> 64
+// channels on a map with a staged plan): its workgroups, each writing
+// 27 x cin x cout fp32 partials (0 when it does not apply), and the call,
+// which adds the partials into dw.
+int64_t staged_wgrad_blocks(const Map& m, int ksize, int cin, int cout);
+int backward_weight_staged(const Map& m, int cin, int cout, const _Float16* feats,
+                           const _Float16* grad_out, float* partial, float* dw,
+                           hipStream_t stream);
+
 // Allocates the device's staging buffer for weights passed as the caller
 // holds them (once per device; every map build calls it).
 int ensure_weight_stage(int device);
