@@ -62,7 +62,6 @@ static_assert(kHashSlots == 1 << 10, "hash bits");
 // before its own. Wider parts take the hash table and a rank count.
 constexpr int kBitmapBits = 1 << 16;
 constexpr int kBitmapWords = kBitmapBits / 32;
-constexpr int kWordsPerThread = kBitmapWords / kPlanThreads;
 
 struct PlanLds {
   int32_t H[kHashSlots];   // hash table of neighbour rows, -1 empty
@@ -399,7 +398,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
                                            static_cast<int>(bytes), 0x00020000);
 }
-constexpr uint32_t kOob = 0x80000000u;
 __device__ __forceinline__ half8 bload_h8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
@@ -419,9 +417,9 @@ struct CfgSt {
   static constexpr int RC = CIN / 8;         // 16-byte chunks per row
   static constexpr int NCB = COUT / 32;      // 32-column blocks
   static constexpr int RED = 3 * 4 * 64;            // float4s of one row block's partial sums
-  // staged rows and the zero row, in chunks; with one column pass the space
-  // also takes the four row blocks' partial sums at once (the zero row is
-  // written again with every unit)
+  // staged rows and the zero row, in chunks; with 32 output columns the
+  // space also takes the four row blocks' partial sums at once (the zero row
+  // is written again with every unit)
   static constexpr int STG0 = (kStageCap + 1) * RC;
   static constexpr int STG = NCB > 1 || STG0 > 4 * RED ? STG0 : 4 * RED;
   static constexpr int MAXJ = kStageCap * RC / NT;  // staging loads per thread
@@ -429,17 +427,14 @@ struct CfgSt {
   static constexpr int IJ = (IW + NT - 1) / NT;           // its loads per thread
   static constexpr int SPT = kStageCap / NT;              // staged-row indices per thread
   static constexpr int RPR = STG / RED < 4 ? STG / RED : 4;  // row blocks per round
-  // with two column passes, the first pass's partial sums go to a space of
-  // their own (the second pass still reads the staged rows)
-  static constexpr int RPRX = 1;
-  static constexpr int REDX = NCB > 1 ? RPRX * RED : 1;
-  // with 32 output columns a wave keeps all 7 of its taps' weights in
-  // registers for all its units (at 64 input channels that spills a few
-  // registers, saved and restored outside the multiply loop: still faster
-  // than reloading 108 KiB of weights per unit); 64 columns run as two
-  // passes of 32 over the staged rows and load each tap's weights two taps
-  // ahead of its multiply
-  static constexpr int NRES = NCB == 2 ? 0 : 7;
+  // k_fwd_staged (32 output columns): a wave keeps all 7 of its taps'
+  // weights in registers for all its units (at 64 input channels that spills
+  // a few registers, saved and restored outside the multiply loop: still
+  // faster than reloading 108 KiB of weights per unit); with fewer resident
+  // taps the others are loaded two taps ahead of their multiply.
+  // k_fwd_staged_c64 (64 output columns) loads every tap's weights two taps
+  // ahead.
+  static constexpr int NRES = 7;
   static_assert((CIN == 32 || CIN == 64) && (COUT == 32 || COUT == 64) && CIN * COUT < 64 * 64,
                 "shape");
   static_assert(kStageCap % NT == 0 && IW % 64 == 0 && (kStageCap * RC) % NT == 0, "layout");
@@ -469,10 +464,10 @@ __global__ __launch_bounds__(256, 2) void k_fwd_staged(
     const _Float16* __restrict__ wp, const float* __restrict__ bias, _Float16* __restrict__ out) {
   using C = CfgSt<CIN, COUT>;
   constexpr int KS = C::KS, RC = C::RC, NCB = C::NCB, NRES = C::NRES;
+  static_assert(NCB == 1, "32 output columns (64: k_fwd_staged_c64)");
   __shared__ half8 stg[C::STG];
   __shared__ uint32_t itab[C::IW];      // [27][128] staged rows of the unit's rows, two per word
   __shared__ int32_t sbuf[kStageCap];   // the unit's staged rows (caller rows)
-  __shared__ float4v redx[C::REDX];
 
   const int bid = blockIdx.x;
   const int xcd = bid & 7, j0 = bid >> 3;
@@ -483,7 +478,6 @@ __global__ __launch_bounds__(256, 2) void k_fwd_staged(
   // assume the fewest in flight after the branch)
   auto tap = [&](int i) { return w + 4 * i < kTaps3 ? w + 4 * i : kTaps3 - 1; };
 
-  const __amdgpu_buffer_rsrc_t rf = make_rsrc(feats, static_cast<uint32_t>(n * CIN * 2));
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(wp, static_cast<uint32_t>(kTaps3 * CIN * COUT * 2));
   // the weights of tap k, columns 32 cb.. (1 KiB per K step, in fragment order)
   auto load_a = [&](int k, int cb, half8 (&A)[KS]) {
@@ -590,8 +584,8 @@ __global__ __launch_bounds__(256, 2) void k_fwd_staged(
     auto body = [&](auto nrbc) {
       constexpr int NRB = decltype(nrbc)::value;
       const uint16_t* it16 = reinterpret_cast<const uint16_t*>(itab);
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
+      {
+        constexpr int cb = 0;  // the one 32-column block
         float16v acc[NRB];
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) acc[rb] = float16v{};
@@ -637,10 +631,6 @@ __global__ __launch_bounds__(256, 2) void k_fwd_staged(
                 }
           }
         };
-        if (cb > 0) {  // the ring's first taps of this column pass
-          load_a(tap(NRES), cb, AT[0]);
-          load_a(tap(NRES + 1), cb, AT[1]);
-        }
         int E[2][NRB];
         load_e(tap(0), E[0]);
 #pragma unroll
@@ -652,12 +642,12 @@ __global__ __launch_bounds__(256, 2) void k_fwd_staged(
             if (i + 2 < 7) load_a(tap(i + 2), cb, AT[(i - NRES) % 2]);
           }
         }
-        __syncthreads();  // every wave is done with the staged rows (of the last pass) and sbuf
-        if (cb + 1 == NCB) put_rows(SR_n);  // read by the next unit's staging, after the barriers below
+        __syncthreads();  // every wave is done with the staged rows and sbuf
+        put_rows(SR_n);   // read by the next unit's staging, after the barriers below
 
         // ---- partial sums of the four waves, in wave order, then the epilogue ----
-        constexpr int RPR = NCB > 1 ? C::RPRX : C::RPR;
-        float4v* red = cb + 1 < NCB ? redx : reinterpret_cast<float4v*>(stg);
+        constexpr int RPR = C::RPR;
+        float4v* red = reinterpret_cast<float4v*>(stg);
 #pragma unroll
         for (int rr = 0; rr < NRB; rr += RPR) {
 #pragma unroll
@@ -719,6 +709,288 @@ __global__ __launch_bounds__(256, 2) void k_fwd_staged(
   }
 }
 
+// 32 -> 64 channels (the input gradient of a 64 -> 32 layer): both 32-column
+// blocks accumulate in one pass over the staged rows, so each staged-row
+// fragment read feeds two MFMAs and every tap's weights of both blocks are
+// loaded once per unit; the four waves' partial sums meet in the staging
+// space one row block (both column blocks) at a time, added in wave order as
+// in k_fwd_staged (the same sums, the same bits).
+template <bool IS_BF16>
+__global__ __launch_bounds__(256, 2) void k_fwd_staged_c64(
+    const int4* __restrict__ units, int n_units, int per_xcd, int wpx,
+    const int32_t* __restrict__ srows, const uint32_t* __restrict__ sidx2, int64_t istride2,
+    const int32_t* __restrict__ order, int64_t n, const _Float16* __restrict__ feats,
+    const _Float16* __restrict__ wp, const float* __restrict__ bias, _Float16* __restrict__ out) {
+  constexpr int CIN = 32, COUT = 64;
+  using C = CfgSt<CIN, COUT>;
+  constexpr int KS = C::KS, RC = C::RC, NCB = C::NCB;
+  static_assert(NCB == 2 && 2 * C::RED <= C::STG * 1, "a row block's partial sums fit the staging space");
+  __shared__ half8 stg[C::STG];
+  __shared__ uint32_t itab[C::IW];      // [27][128] staged rows of the unit's rows, two per word
+  __shared__ int32_t sbuf[kStageCap];   // the unit's staged rows (caller rows)
+
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, j0 = bid >> 3;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int ntaps = (kTaps3 - w + 3) / 4;  // this wave's taps k = w + 4 i
+  // taps past the wave's last load tap 26 again and go unused, so that no
+  // load sits in a branch (the compiler's waits for loads would otherwise
+  // assume the fewest in flight after the branch)
+  auto tap = [&](int i) { return w + 4 * i < kTaps3 ? w + 4 * i : kTaps3 - 1; };
+
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wp, static_cast<uint32_t>(kTaps3 * CIN * COUT * 2));
+  // the weights of tap k, both column blocks (1 KiB per K step, in fragment order)
+  auto load_a = [&](int k, half8 (&A)[NCB][KS]) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const uint32_t base = static_cast<uint32_t>(((k * NCB + cb) * KS) * 1024 + lane * 16);
+#pragma unroll
+      for (int st = 0; st < KS; ++st) A[cb][st] = bload_h8(rw, base + st * 1024);
+    }
+  };
+  // v_mfma_f32_32x32x16: A = weights (lane: column lane%32, K steps st of
+  // lane half h = lane/32: channels h CIN/2 + 8 st + 0..7), B = staged rows
+  // (lane: row lane%32 of the block, the same channels); D: lane holds row
+  // lane%32 and columns 8 a + 4 h + b in register 4 a + b.
+  // AT: a two-slot ring of taps' weights, loaded two taps ahead
+  half8 AT[2][NCB][KS];
+
+  // a unit's descriptor, staged-row indices (to sbuf) and table words (to
+  // itab): requested by fetch_*, stored by put_*
+  auto unit_of = [&](int ju) { return ju < per_xcd ? xcd * per_xcd + ju : n_units; };
+  auto fetch_rows = [&](const int4& d, int (&SR)[C::SPT]) {
+#pragma unroll
+    for (int q = 0; q < C::SPT; ++q) {
+      const int sr = tid + C::NT * q;
+      SR[q] = sr < d.w ? srows[d.z + sr] : -1;
+    }
+  };
+  auto put_rows = [&](const int (&SR)[C::SPT]) {
+#pragma unroll
+    for (int q = 0; q < C::SPT; ++q) sbuf[tid + C::NT * q] = SR[q];
+  };
+
+  int ju = j0;
+  int u = unit_of(ju);
+  if (u >= n_units) return;
+  int4 d = units[u];
+  {
+    int SR[C::SPT];
+    fetch_rows(d, SR);
+    put_rows(SR);
+  }
+  __syncthreads();
+
+  while (true) {
+    const int64_t t0 = d.x;
+    const int rows = d.y, cnt = d.w;
+    const int ju_n = ju + wpx;
+    const int u_n = unit_of(ju_n);
+    const bool has_next = u_n < n_units;
+    const int4 d_n = has_next ? units[u_n] : make_int4(0, 0, 0, 0);
+    // the thread index, made opaque per unit: the LDS addresses of the
+    // unit's staging stores and of its 7 x 4 (tap, row block) reads derive
+    // from it, and computed once before the unit loop they would hold ~60
+    // registers throughout
+    int tid_u = tid;
+    asm volatile("" : "+v"(tid_u));
+    const int s32 = tid_u & 31, h = (tid_u >> 5) & 1;
+
+    // ---- stage the unit's distinct neighbour rows, the zero row and its table ----
+    // straight from memory into LDS (global_load_lds: lane l of a wave's load
+    // writes the 16 bytes at the load's LDS base + 16 l), every load in
+    // flight at once. Slot i of the staging space holds chunk (i % RC) ^
+    // swz(s) of staged row s = i / RC; slots past the unit's staged rows
+    // load row 0's chunk and are never read.
+    load_a(tap(0), AT[0]);
+    load_a(tap(1), AT[1]);
+#pragma unroll 2
+    for (int j = 0; j < C::MAXJ; ++j) {
+      const int base = (j * (C::NT / 64) + w) * 64;
+      if (base / RC < cnt) {  // whole waves past the staged rows skip
+        const int i = base + lane, sr = i / RC;
+        const int row = sbuf[sr < cnt ? sr : 0];
+        const _Float16* g = feats + static_cast<int64_t>(row) * CIN + ((i % RC) ^ swz<RC>(sr)) * 8;
+        __builtin_amdgcn_global_load_lds(g, (lds_void*)(stg + base), 16, 0, 0);
+      }
+    }
+    // table word e: tap e / 64, rows 2 (e % 64) and + 1 of the unit (units
+    // start on even rows, the table's stride is even; words past the unit's
+    // rows repeat its last word)
+    {
+      const int pw = (rows + 1) >> 1;
+#pragma unroll 2
+      for (int j = 0; j < C::IJ; ++j) {
+        const int base = (j * (C::NT / 64) + w) * 64;
+        if (base < C::IW) {
+          const int e = base + lane, k = e >> 6, p = e & 63;
+          const uint32_t* g = sidx2 + k * istride2 + (t0 >> 1) + (p < pw ? p : pw - 1);
+          __builtin_amdgcn_global_load_lds(g, (lds_void*)(itab + base), 4, 0, 0);
+        }
+      }
+    }
+    if (tid_u < RC) stg[kStageCap * RC + tid_u] = half8{};  // the zero row
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // ---- the next unit's staged-row indices, on their way during the multiplies ----
+    int SR_n[C::SPT];
+    fetch_rows(d_n, SR_n);
+
+    // ---- this wave's taps over the unit's row blocks; the four waves'
+    // partial sums of block rb meet in wave rb, which writes its outputs ----
+    auto body = [&](auto nrbc) {
+      constexpr int NRB = decltype(nrbc)::value;
+      const uint16_t* it16 = reinterpret_cast<const uint16_t*>(itab);
+      float16v acc[NRB][NCB];
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = float16v{};
+      // the staged row of this lane's row in each block at tap k (the zero
+      // row when it has none, or past the unit's rows)
+      auto load_e = [&](int k, int (&E)[NRB]) {
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          const int r = 32 * rb + s32;
+          const int e = r < rows ? it16[k * kStageUnitRows + r] : kStageNone;
+          E[rb] = e == kStageNone ? kStageCap : e;
+        }
+      };
+      // one tap, two row blocks at a time: both blocks' operands requested
+      // first (and the next tap's staged rows behind the first pair), then
+      // the MFMAs of both column blocks, alternating over four accumulators
+      auto multiply = [&](const half8 (&Aw)[NCB][KS], const int (&E)[NRB], int k_next,
+                          int (&En)[NRB]) {
+#pragma unroll
+        for (int rp = 0; rp < NRB; rp += 2) {
+          const int nb = rp + 1 < NRB ? 2 : 1;
+          half8 B[2][KS];
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+            if (q < nb) {
+              const int sw = swz<RC>(E[rp + q]);
+#pragma unroll
+              for (int st = 0; st < KS; ++st) B[q][st] = stg[E[rp + q] * RC + ((h * KS + st) ^ sw)];
+            }
+          if (rp == 0) load_e(k_next, En);
+#pragma unroll
+          for (int st = 0; st < KS; ++st)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+              for (int cb = 0; cb < NCB; ++cb)
+                if (q < nb) {
+                  if constexpr (IS_BF16)
+                    acc[rp + q][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, Aw[cb][st]), __builtin_bit_cast(bf16x8, B[q][st]),
+                        acc[rp + q][cb], 0, 0, 0);
+                  else
+                    acc[rp + q][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Aw[cb][st], B[q][st],
+                                                                             acc[rp + q][cb], 0, 0, 0);
+                }
+        }
+      };
+      int E[2][NRB];
+      load_e(tap(0), E[0]);
+#pragma unroll
+      for (int i = 0; i < 7; ++i) {
+        if (i < ntaps) multiply(AT[i % 2], E[i % 2], tap(i + 1), E[(i + 1) % 2]);
+        if (i + 2 < 7) load_a(tap(i + 2), AT[i % 2]);
+      }
+      __syncthreads();  // every wave is done with the staged rows and sbuf
+      put_rows(SR_n);   // read by the next unit's staging, after the barriers below
+
+      // ---- partial sums of the four waves, one row block (both column
+      // blocks) at a time, in wave order, then the epilogue ----
+      float4v* red = reinterpret_cast<float4v*>(stg);
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        if (w != rb) {
+          const int slot = w < rb ? w : w - 1;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+              const float16v& v = acc[rb][cb];
+              red[(((cb * 3 + slot) * 4 + a) * 64) + lane] =
+                  float4v{v[4 * a], v[4 * a + 1], v[4 * a + 2], v[4 * a + 3]};
+            }
+        }
+        __syncthreads();
+        if (w == rb) {
+          const int r = 32 * rb + s32;
+          const bool live = r < rows;
+          const int64_t orow = live ? (order ? order[t0 + r] : t0 + r) : 0;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+              const float16v& v = acc[rb][cb];
+              const float4v own = float4v{v[4 * a], v[4 * a + 1], v[4 * a + 2], v[4 * a + 3]};
+              // partial sums in wave order: ((p0 + p1) + p2) + p3
+              float4v t = rb == 0 ? own : red[((cb * 3 + 0) * 4 + a) * 64 + lane];
+#pragma unroll
+              for (int ww = 1; ww < 4; ++ww) {
+                const int slot = ww < rb ? ww : ww - 1;
+                t += ww == rb ? own : red[((cb * 3 + slot) * 4 + a) * 64 + lane];
+              }
+              if (live) {
+                const int col = 32 * cb + 8 * a + 4 * h;
+                float4v b4 = {0.f, 0.f, 0.f, 0.f};
+                if (bias) b4 = *reinterpret_cast<const float4v*>(bias + col);
+                typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+                const half4 o = {round16<IS_BF16>(t[0] + b4[0]), round16<IS_BF16>(t[1] + b4[1]),
+                                 round16<IS_BF16>(t[2] + b4[2]), round16<IS_BF16>(t[3] + b4[3])};
+                *reinterpret_cast<half4*>(out + orow * COUT + col) = o;
+              }
+            }
+        }
+        __syncthreads();  // the partial sums' space (and then stg, itab, sbuf) is free again
+      }
+    };
+    switch ((rows + 31) / 32) {
+      case 1: body(std::integral_constant<int, 1>{}); break;
+      case 2: body(std::integral_constant<int, 2>{}); break;
+      case 3: body(std::integral_constant<int, 3>{}); break;
+      default: body(std::integral_constant<int, 4>{}); break;
+    }
+    if (!has_next) break;
+    ju = ju_n;
+    d = d_n;
+  }
+}
+
+// workgroups of one instance that a CU holds at once (cached)
+
+template <bool IS_BF16>
+int launch_staged_c64(const Map& m, const _Float16* feats, const _Float16* wp, const float* bias,
+                      _Float16* out, hipStream_t stream) {
+  static const int per_cu = [] {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &nb, reinterpret_cast<const void*>(k_fwd_staged_c64<IS_BF16>), CfgSt<32, 64>::NT, 0) !=
+        hipSuccess)
+      nb = 1;
+    return nb < 1 ? 1 : nb;
+  }();
+  const Staged& S = m.staged;
+  if (S.n_units > (int64_t{1} << 28))
+    return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "too many staged units");
+  int dev = 0, cus = 256;
+  SUBMCONV_HIP_CHECK(hipGetDevice(&dev));
+  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int per_xcd = static_cast<int>((S.n_units + 7) / 8);
+  const int slots = (cus < 8 ? 1 : cus / 8) * per_cu;
+  const int wpx = per_xcd < slots ? per_xcd : slots;
+  k_fwd_staged_c64<IS_BF16><<<static_cast<unsigned>(8 * wpx), CfgSt<32, 64>::NT, 0, stream>>>(
+      S.units, static_cast<int>(S.n_units), per_xcd, wpx, S.rows,
+      reinterpret_cast<const uint32_t*>(S.idx), staged_idx_stride(m.n) / 2, m.order, m.n, feats,
+      wp, bias, out);
+  SUBMCONV_HIP_CHECK(hipGetLastError());
+  return SUBMCONV_OK;
+}
+
 // workgroups of one instance that a CU holds at once (cached)
 template <int CIN, int COUT, bool IS_BF16>
 int staged_per_cu() {
@@ -760,7 +1032,7 @@ int staged_typed(const Map& m, int cin, int cout, const _Float16* feats, const _
                  const float* bias, _Float16* out, hipStream_t stream) {
   if (cout == 256) return forward_staged_wide(m, cin, IS_BF16, feats, wp, bias, out, stream);
   if (cin == 64) return launch_staged<64, 32, IS_BF16>(m, feats, wp, bias, out, stream);
-  if (cout == 64) return launch_staged<32, 64, IS_BF16>(m, feats, wp, bias, out, stream);
+  if (cout == 64) return launch_staged_c64<IS_BF16>(m, feats, wp, bias, out, stream);
   return launch_staged<32, 32, IS_BF16>(m, feats, wp, bias, out, stream);
 }
 
