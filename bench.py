@@ -63,9 +63,9 @@ MEASURED_TRAFFIC = {
         "fetch_factor": 524288.0 / 262156.0, "write_factor": 524288.0 / 524288.0},
     ("c5_512_chain", "forward"): {
         "src": ["staged.hip", "map_build.hip"],  # the staged kernel (64 -> 32), and its plan
-        "sha256": "ecf66e112f3c5ef6284cd9ddf832c4b6ec20fe53140c97c40a27b36299ab1727",
-        "fetch_kib": 171773.78, "write_kib": 95631.12,
-        "fetch_factor": 524288.0 / 262168.0, "write_factor": 524288.0 / 524288.0},
+        "sha256": "e619e2cd48f2ce2cbcc039929127659a344eea2cec442a9fe50c76e3fbb1a156",
+        "fetch_kib": 170177.18, "write_kib": 95630.8,
+        "fetch_factor": 524288.0 / 262155.9, "write_factor": 524288.0 / 524288.0},
     ("c5_512_chain", "backward_weight"): {
         # the staged weight gradient (64 -> 32) and its reduce: the call bench.py times
         "src": ["staged_bwd.hip", "map_build.hip"],

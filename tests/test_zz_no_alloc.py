@@ -102,3 +102,36 @@ def test_noalloc_split_that_does_not_fit(dev):
     scale = oc.backward_weight(km_t, np.abs(wl.feats.astype(np.float64)), np.abs(g.astype(np.float64)))[taps]
     _close(out.cpu().numpy()[taps], ref, scale, "noalloc 256->256, longer runs")
     km.free()
+
+
+@gpu
+@pytest.mark.parametrize("cin,cout", [(32, 32), (64, 32)])
+def test_noalloc_on_a_staged_map(dev, cin, cout):
+    # a dense map (a fully occupied 20^3 cube) has a staged plan: at 32 -> 32
+    # the staged kernel's partials fit the static workspace and the call takes
+    # it, as the allocating entry point does (the same bits); at 64 -> 32 they
+    # do not, and the call keeps the pair-by-pair kernel (the oracle's bound)
+    sc = _sc()
+    G = 20
+    c = np.stack(np.meshgrid(np.arange(G), np.arange(G), np.arange(G), indexing="ij"), -1).reshape(-1, 3)
+    coords = np.concatenate([np.zeros((c.shape[0], 1), np.int32), c.astype(np.int32)], 1)
+    rng = np.random.default_rng(cin + cout)
+    feats = rng.standard_normal((coords.shape[0], cin)).astype(np.float16)
+    g = rng.standard_normal((coords.shape[0], cout)).astype(np.float16)
+    km = sc.build_map(_to(dev, coords), (G, G, G), 1)
+    assert km.staged()[0] > 0
+    f, gd = _to(dev, feats), _to(dev, g)
+    out = torch.empty((27, cin, cout), dtype=torch.float32, device=dev)
+    print(f"[noalloc staged map] {cin}->{cout} N={coords.shape[0]}", flush=True)
+    assert _noalloc(sc, km, f, gd, out, cin, cout) == 0
+    ref_ws = sc.backward_weight(km, f, gd, 3)
+    kmap = oc.kernel_map(coords, (G, G, G), 1, 3)
+    ref = oc.backward_weight(kmap, feats, g)
+    scale = oc.backward_weight(kmap, np.abs(feats.astype(np.float64)), np.abs(g.astype(np.float64)))
+    _close(out.cpu().numpy(), ref, scale, f"noalloc on a staged map {cin}->{cout}")
+    if (cin, cout) == (32, 32):
+        assert torch.equal(out, ref_ws), "the same kernel and partials: the same bits"
+    else:
+        _close(out.cpu().numpy(), ref_ws.cpu().numpy().astype(np.float64), scale,
+               "noalloc vs workspace entry on a staged map")
+    km.free()
