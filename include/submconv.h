@@ -455,8 +455,10 @@ typedef struct submconv_down_s* submconv_down_t;
  * ... (a repeated site is simply one more child). The parents are the
  * distinct parent sites in ascending lexicographic (b,x,y,z) order; the
  * parent grid is ceil(grid/2). Builds on `stream`, then waits for it once (to
- * learn the parent count and report SUBMCONV_ERR_COORD_OUT_OF_RANGE). Allocates
- * device memory (about 24 bytes per site, plus temporaries freed on return).
+ * learn the parent count and report SUBMCONV_ERR_COORD_OUT_OF_RANGE). Makes one
+ * device allocation, held until submconv_downsample_free: the plan's arrays (28
+ * bytes per site) and the build's temporaries (16 bytes per site, 24 when
+ * batch * ceil(grid/2) products exceed 2^32, plus the radix sort's scratch).
  */
 int submconv_downsample_plan(const int32_t* coords, int64_t n, int32_t batch, const int32_t grid[3],
                              hipStream_t stream, submconv_down_t* out_plan);

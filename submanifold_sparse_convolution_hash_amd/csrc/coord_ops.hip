@@ -22,19 +22,25 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 
+// All of a plan's device arrays, and the temporaries its build uses, live in
+// one allocation (blob): a build costs one hipMalloc and a release one hipFree.
 struct DownPlan {
   int device = 0;
   int64_t n = 0, m = 0;
   int32_t pgrid[3] = {0, 0, 0};
+  void* blob = nullptr;
   int32_t* sorted_child = nullptr;  // [n] site indices in parent-key order
   int32_t* seg = nullptr;           // [m+1] run of parent p: sorted_child[seg[p] .. seg[p+1])
-  int32_t* inverse = nullptr;       // [n] parent row of each site
+  int32_t* inverse = nullptr;       // [n] parent row of each site (the sort's index input first)
   int32_t* pcoords = nullptr;       // [m][4]
 };
 
+// K is uint32_t when batch * P0 * P1 * P2 fits in 32 bits (the radix sort then
+// moves half the key bytes), else uint64_t.
+template <typename K>
 __global__ void k_parent_keys(const int32_t* __restrict__ coords, int64_t n, int32_t batch,
                               int32_t g0, int32_t g1, int32_t g2, int32_t p0, int32_t p1,
-                              int32_t p2, uint64_t* __restrict__ keys, int32_t* __restrict__ idx,
+                              int32_t p2, K* __restrict__ keys, int32_t* __restrict__ idx,
                               uint32_t* __restrict__ err) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= n) return;
@@ -43,43 +49,50 @@ __global__ void k_parent_keys(const int32_t* __restrict__ coords, int64_t n, int
     atomicOr(err, 1u);
     keys[i] = 0;
   } else {
-    keys[i] = ((static_cast<uint64_t>(b) * p0 + static_cast<uint64_t>(x >> 1)) * p1 +
-               static_cast<uint64_t>(y >> 1)) * p2 + static_cast<uint64_t>(z >> 1);
+    keys[i] = ((static_cast<K>(b) * static_cast<K>(p0) + static_cast<K>(x >> 1)) * static_cast<K>(p1) +
+               static_cast<K>(y >> 1)) * static_cast<K>(p2) + static_cast<K>(z >> 1);
   }
   idx[i] = static_cast<int32_t>(i);
 }
 
 // 1 where a new parent key starts in the sorted order
-__global__ void k_run_heads(const uint64_t* __restrict__ skeys, int64_t n, int32_t* __restrict__ head) {
+template <typename K>
+__global__ void k_run_heads(const K* __restrict__ skeys, int64_t n, int32_t* __restrict__ head) {
   const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (t < n) head[t] = (t == 0 || skeys[t] != skeys[t - 1]) ? 1 : 0;
 }
 
 // pos[t] = exclusive scan of head: parent row of sorted position t is
-// pos[t] + head[t] - 1
-__global__ void k_runs(const uint64_t* __restrict__ skeys, const int32_t* __restrict__ schild,
+// pos[t] + head[t] - 1. The last position also writes the parent count M to
+// *count, so the host reads M and the range flag in one copy.
+template <typename K>
+__global__ void k_runs(const K* __restrict__ skeys, const int32_t* __restrict__ schild,
                        const int32_t* __restrict__ head, const int32_t* __restrict__ pos, int64_t n,
                        int32_t p0, int32_t p1, int32_t p2, int32_t* __restrict__ seg,
-                       int32_t* __restrict__ inverse, int32_t* __restrict__ pcoords) {
+                       int32_t* __restrict__ inverse, int32_t* __restrict__ pcoords,
+                       uint32_t* __restrict__ count) {
   const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (t >= n) return;
   const int32_t p = pos[t] + head[t] - 1;
   inverse[schild[t]] = p;
   if (head[t]) {
     seg[p] = static_cast<int32_t>(t);
-    uint64_t k = skeys[t];
-    const int32_t z = static_cast<int32_t>(k % static_cast<uint64_t>(p2));
-    k /= static_cast<uint64_t>(p2);
-    const int32_t y = static_cast<int32_t>(k % static_cast<uint64_t>(p1));
-    k /= static_cast<uint64_t>(p1);
-    const int32_t x = static_cast<int32_t>(k % static_cast<uint64_t>(p0));
-    const int32_t b = static_cast<int32_t>(k / static_cast<uint64_t>(p0));
+    K k = skeys[t];
+    const int32_t z = static_cast<int32_t>(k % static_cast<K>(p2));
+    k /= static_cast<K>(p2);
+    const int32_t y = static_cast<int32_t>(k % static_cast<K>(p1));
+    k /= static_cast<K>(p1);
+    const int32_t x = static_cast<int32_t>(k % static_cast<K>(p0));
+    const int32_t b = static_cast<int32_t>(k / static_cast<K>(p0));
     pcoords[4 * p] = b;
     pcoords[4 * p + 1] = x;
     pcoords[4 * p + 2] = y;
     pcoords[4 * p + 3] = z;
   }
-  if (t == n - 1) seg[p + 1] = static_cast<int32_t>(n);
+  if (t == n - 1) {
+    seg[p + 1] = static_cast<int32_t>(n);
+    *count = static_cast<uint32_t>(p + 1);
+  }
 }
 
 // parent p, 8-channel chunk c8: max over the run of p (fp16 max is exact)
@@ -126,13 +139,6 @@ __global__ void k_subdivide(const int32_t* __restrict__ coords, int64_t n,
   }
 }
 
-struct Tmp {
-  void* p = nullptr;
-  ~Tmp() {
-    if (p) (void)hipFree(p);
-  }
-};
-
 int bits_of(uint64_t v) {  // bits to hold values < v
   int b = 1;
   while (b < 64 && (uint64_t{1} << b) < v) ++b;
@@ -141,11 +147,74 @@ int bits_of(uint64_t v) {  // bits to hold values < v
 
 void free_plan(DownPlan* d) {
   if (!d) return;
-  if (d->sorted_child) (void)hipFree(d->sorted_child);
-  if (d->seg) (void)hipFree(d->seg);
-  if (d->inverse) (void)hipFree(d->inverse);
-  if (d->pcoords) (void)hipFree(d->pcoords);
+  if (d->blob) (void)hipFree(d->blob);
   delete d;
+}
+
+size_t up256(size_t v) { return (v + 255) & ~size_t{255}; }
+
+// Carves the plan's arrays and the build's temporaries out of one
+// allocation, sorts the parent keys, and marks the runs. Returns the HIP
+// error of the first failing call; *flags receives {range flag, M}.
+template <typename K>
+hipError_t build_plan(DownPlan* d, const int32_t* coords, int32_t batch, const int32_t grid[3],
+                      uint64_t span, hipStream_t stream, uint32_t flags[2]) {
+  const int64_t n = d->n;
+  const size_t nn = static_cast<size_t>(n);
+  const int end_bit = bits_of(span);
+  size_t sort_bytes = 0, scan_bytes = 0;
+  hipError_t e = rocprim::radix_sort_pairs(nullptr, sort_bytes, static_cast<K*>(nullptr),
+                                           static_cast<K*>(nullptr), static_cast<int32_t*>(nullptr),
+                                           static_cast<int32_t*>(nullptr), nn, 0, end_bit, stream);
+  if (e != hipSuccess) return e;
+  e = rocprim::exclusive_scan(nullptr, scan_bytes, static_cast<int32_t*>(nullptr),
+                              static_cast<int32_t*>(nullptr), 0, nn, rocprim::plus<int32_t>(), stream);
+  if (e != hipSuccess) return e;
+  // offsets: plan arrays first, then the temporaries
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += up256(bytes > 0 ? bytes : 1);
+    return o;
+  };
+  const size_t o_child = take(4 * nn), o_inv = take(4 * nn), o_seg = take(4 * (nn + 1));
+  const size_t o_pc = take(16 * nn), o_keys = take(sizeof(K) * nn), o_skeys = take(sizeof(K) * nn);
+  const size_t o_head = take(4 * nn), o_pos = take(4 * nn), o_small = take(16);
+  const size_t o_sort = take(sort_bytes), o_scan = take(scan_bytes);
+  e = hipMalloc(&d->blob, off);
+  if (e != hipSuccess) return e;
+  char* base = static_cast<char*>(d->blob);
+  d->sorted_child = reinterpret_cast<int32_t*>(base + o_child);
+  d->inverse = reinterpret_cast<int32_t*>(base + o_inv);
+  d->seg = reinterpret_cast<int32_t*>(base + o_seg);
+  d->pcoords = reinterpret_cast<int32_t*>(base + o_pc);
+  K* keys = reinterpret_cast<K*>(base + o_keys);
+  K* skeys = reinterpret_cast<K*>(base + o_skeys);
+  int32_t* head = reinterpret_cast<int32_t*>(base + o_head);
+  int32_t* pos = reinterpret_cast<int32_t*>(base + o_pos);
+  uint32_t* small = reinterpret_cast<uint32_t*>(base + o_small);
+  // the sort's index input lives in inverse: it is dead once the sort has run
+  int32_t* idx = d->inverse;
+  e = hipMemsetAsync(small, 0, 16, stream);
+  if (e != hipSuccess) return e;
+  const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
+  k_parent_keys<K><<<blocks, 256, 0, stream>>>(coords, n, batch, grid[0], grid[1], grid[2], d->pgrid[0],
+                                               d->pgrid[1], d->pgrid[2], keys, idx, small);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  e = rocprim::radix_sort_pairs(base + o_sort, sort_bytes, keys, skeys, idx, d->sorted_child, nn, 0,
+                                end_bit, stream);
+  if (e != hipSuccess) return e;
+  k_run_heads<K><<<blocks, 256, 0, stream>>>(skeys, n, head);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  e = rocprim::exclusive_scan(base + o_scan, scan_bytes, head, pos, 0, nn, rocprim::plus<int32_t>(),
+                              stream);
+  if (e != hipSuccess) return e;
+  k_runs<K><<<blocks, 256, 0, stream>>>(skeys, d->sorted_child, head, pos, n, d->pgrid[0], d->pgrid[1],
+                                        d->pgrid[2], d->seg, d->inverse, d->pcoords, small + 1);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  e = hipMemcpyAsync(flags, small, 8, hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) return e;
+  return hipStreamSynchronize(stream);
 }
 
 }  // namespace
@@ -156,16 +225,6 @@ struct submconv_down_s {
 };
 
 using namespace submconv;
-
-#define PLAN_CHECK(expr)                                                                     \
-  do {                                                                                       \
-    hipError_t e_ = (expr);                                                                  \
-    if (e_ != hipSuccess) {                                                                  \
-      free_plan(d);                                                                          \
-      return set_error(e_ == hipErrorOutOfMemory ? SUBMCONV_ERR_OUT_OF_MEMORY : SUBMCONV_ERR_HIP, \
-                       "%s failed: %s", #expr, hipGetErrorString(e_));                       \
-    }                                                                                        \
-  } while (0)
 
 extern "C" int submconv_downsample_plan(const int32_t* coords, int64_t n, int32_t batch,
                                         const int32_t grid[3], hipStream_t stream,
@@ -179,69 +238,25 @@ extern "C" int submconv_downsample_plan(const int32_t* coords, int64_t n, int32_
     return set_error(SUBMCONV_ERR_INVALID_ARG, "grid extents must be positive");
   if (n >= INT32_MAX) return set_error(SUBMCONV_ERR_UNSUPPORTED_SHAPE, "too many sites");
   DownPlan* d = new DownPlan;
-  PLAN_CHECK(hipGetDevice(&d->device));
+  hipError_t e = hipGetDevice(&d->device);
   d->n = n;
   for (int a = 0; a < 3; ++a) d->pgrid[a] = (grid[a] + 1) / 2;
   const uint64_t span = static_cast<uint64_t>(batch) * d->pgrid[0] * d->pgrid[1] * d->pgrid[2];
-  if (n == 0) {
-    *out_plan = new submconv_down_s{*d};
-    delete d;
-    return SUBMCONV_OK;
+  uint32_t flags[2] = {0, 0};
+  if (e == hipSuccess && n > 0)
+    e = span <= (uint64_t{1} << 32) ? build_plan<uint32_t>(d, coords, batch, grid, span, stream, flags)
+                                    : build_plan<uint64_t>(d, coords, batch, grid, span, stream, flags);
+  if (e != hipSuccess) {
+    free_plan(d);
+    return set_error(e == hipErrorOutOfMemory ? SUBMCONV_ERR_OUT_OF_MEMORY : SUBMCONV_ERR_HIP,
+                     "downsample plan: %s", hipGetErrorString(e));
   }
-  Tmp keys, skeys, idx, head, pos, small, sort_tmp, scan_tmp;
-  PLAN_CHECK(hipMalloc(&keys.p, sizeof(uint64_t) * n));
-  PLAN_CHECK(hipMalloc(&skeys.p, sizeof(uint64_t) * n));
-  PLAN_CHECK(hipMalloc(&idx.p, sizeof(int32_t) * n));
-  PLAN_CHECK(hipMalloc(&head.p, sizeof(int32_t) * n));
-  PLAN_CHECK(hipMalloc(&pos.p, sizeof(int32_t) * n));
-  PLAN_CHECK(hipMalloc(&small.p, 16));
-  PLAN_CHECK(hipMalloc(reinterpret_cast<void**>(&d->sorted_child), sizeof(int32_t) * n));
-  PLAN_CHECK(hipMalloc(reinterpret_cast<void**>(&d->inverse), sizeof(int32_t) * n));
-  PLAN_CHECK(hipMalloc(reinterpret_cast<void**>(&d->seg), sizeof(int32_t) * (n + 1)));
-  PLAN_CHECK(hipMalloc(reinterpret_cast<void**>(&d->pcoords), sizeof(int32_t) * 4 * n));
-  PLAN_CHECK(hipMemsetAsync(small.p, 0, 16, stream));
-  const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
-  k_parent_keys<<<blocks, 256, 0, stream>>>(coords, n, batch, grid[0], grid[1], grid[2], d->pgrid[0],
-                                            d->pgrid[1], d->pgrid[2], static_cast<uint64_t*>(keys.p),
-                                            static_cast<int32_t*>(idx.p), static_cast<uint32_t*>(small.p));
-  PLAN_CHECK(hipGetLastError());
-  size_t tmp_bytes = 0;
-  const int end_bit = bits_of(span);
-  PLAN_CHECK(rocprim::radix_sort_pairs(nullptr, tmp_bytes, static_cast<uint64_t*>(keys.p),
-                                       static_cast<uint64_t*>(skeys.p), static_cast<int32_t*>(idx.p),
-                                       d->sorted_child, static_cast<size_t>(n), 0, end_bit, stream));
-  PLAN_CHECK(hipMalloc(&sort_tmp.p, tmp_bytes > 0 ? tmp_bytes : 1));
-  PLAN_CHECK(rocprim::radix_sort_pairs(sort_tmp.p, tmp_bytes, static_cast<uint64_t*>(keys.p),
-                                       static_cast<uint64_t*>(skeys.p), static_cast<int32_t*>(idx.p),
-                                       d->sorted_child, static_cast<size_t>(n), 0, end_bit, stream));
-  k_run_heads<<<blocks, 256, 0, stream>>>(static_cast<uint64_t*>(skeys.p), n,
-                                          static_cast<int32_t*>(head.p));
-  PLAN_CHECK(hipGetLastError());
-  tmp_bytes = 0;
-  PLAN_CHECK(rocprim::exclusive_scan(nullptr, tmp_bytes, static_cast<int32_t*>(head.p),
-                                     static_cast<int32_t*>(pos.p), 0, static_cast<size_t>(n),
-                                     rocprim::plus<int32_t>(), stream));
-  PLAN_CHECK(hipMalloc(&scan_tmp.p, tmp_bytes > 0 ? tmp_bytes : 1));
-  PLAN_CHECK(rocprim::exclusive_scan(scan_tmp.p, tmp_bytes, static_cast<int32_t*>(head.p),
-                                     static_cast<int32_t*>(pos.p), 0, static_cast<size_t>(n),
-                                     rocprim::plus<int32_t>(), stream));
-  k_runs<<<blocks, 256, 0, stream>>>(static_cast<uint64_t*>(skeys.p), d->sorted_child,
-                                     static_cast<int32_t*>(head.p), static_cast<int32_t*>(pos.p), n,
-                                     d->pgrid[0], d->pgrid[1], d->pgrid[2], d->seg, d->inverse,
-                                     d->pcoords);
-  PLAN_CHECK(hipGetLastError());
-  int32_t last[2] = {0, 0};
-  uint32_t err = 0;
-  PLAN_CHECK(hipMemcpyAsync(&last[0], static_cast<int32_t*>(pos.p) + (n - 1), 4, hipMemcpyDeviceToHost, stream));
-  PLAN_CHECK(hipMemcpyAsync(&last[1], static_cast<int32_t*>(head.p) + (n - 1), 4, hipMemcpyDeviceToHost, stream));
-  PLAN_CHECK(hipMemcpyAsync(&err, small.p, 4, hipMemcpyDeviceToHost, stream));
-  PLAN_CHECK(hipStreamSynchronize(stream));
-  if (err) {
+  if (flags[0]) {
     free_plan(d);
     return set_error(SUBMCONV_ERR_COORD_OUT_OF_RANGE, "a site lies outside [0,%d) x [0,%d) x [0,%d) x [0,%d)",
                      batch, grid[0], grid[1], grid[2]);
   }
-  d->m = static_cast<int64_t>(last[0]) + last[1];
+  d->m = n > 0 ? static_cast<int64_t>(flags[1]) : 0;
   *out_plan = new submconv_down_s{*d};
   delete d;
   return SUBMCONV_OK;

@@ -49,6 +49,36 @@ def test_downsample_small(dev, seed, G, occ, batch, c):
     _check_down(sc, dev, wl.coords, wl.feats, wl.grid, batch, O.downsample)
 
 
+def _clustered_sites(rng, batch, grid, parents):
+    """Distinct sites in the 2x2x2 blocks of `parents` random parent sites (1 to 8
+    children each), plus the grid's two extreme corners."""
+    pg = [(g + 1) // 2 for g in grid]
+    pb = rng.integers(0, batch, parents)
+    px = [rng.integers(0, pg[a], parents) for a in range(3)]
+    rows = [[0, 0, 0, 0], [batch - 1, grid[0] - 1, grid[1] - 1, grid[2] - 1]]
+    for i in range(parents):
+        for c in rng.choice(8, size=int(rng.integers(1, 9)), replace=False):
+            s = [int(pb[i])] + [2 * int(px[a][i]) + ((int(c) >> (2 - a)) & 1) for a in range(3)]
+            if all(s[1 + a] < grid[a] for a in range(3)):
+                rows.append(s)
+    return np.unique(np.array(rows, dtype=np.int32), axis=0)
+
+
+@gpu
+@pytest.mark.parametrize("batch,grid", [(1, (4096, 4096, 2048)), (3, (4096, 4096, 4095)),
+                                        (2, (2, 1 << 20, 1 << 20))])
+def test_downsample_wide_keys(dev, batch, grid):
+    # parent-key spans of exactly 2^32 (largest key 2^32 - 1, 32-bit sort keys)
+    # and beyond 2^32 (64-bit sort keys), odd extents included
+    sc = _sc()
+    rng = np.random.default_rng(sum(grid) + batch)
+    coords = _clustered_sites(rng, batch, grid, 3000)
+    coords = coords[rng.permutation(len(coords))]
+    feats = rng.standard_normal((len(coords), 16)).astype(np.float16)
+    print(f"[coordops] downsample wide keys batch={batch} grid={grid} N={len(coords)}", flush=True)
+    _check_down(sc, dev, coords, feats, grid, batch, O.downsample)
+
+
 @gpu
 @pytest.mark.parametrize("name", ["c2_64_64", "c3_128_128", "c5_512_chain"])
 def test_downsample_configs(dev, name):
