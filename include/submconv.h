@@ -416,8 +416,11 @@ typedef struct submconv_masked_s* submconv_masked_t;
 /*
  * submconv_masked_plan -- sort the map's rows by neighbour mask and build the
  * per-block tap lists and neighbour tables (about 4 bytes per (block row, run
- * tap)). Builds on `stream` and waits for it twice; allocates device memory.
- * The plan refers to `map`'s buffers: free it before the map.
+ * tap)). Builds on `stream` and waits for it twice; makes two device
+ * allocations, held until submconv_masked_free: the block arrays with the
+ * build's temporaries (about 28 bytes per row, plus the radix sort's scratch),
+ * then the tap lists and neighbour tables. The plan refers to `map`'s buffers:
+ * free it before the map.
  */
 int submconv_masked_plan(submconv_map_t map, hipStream_t stream, submconv_masked_t* out_plan);
 

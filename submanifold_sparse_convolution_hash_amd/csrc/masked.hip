@@ -32,11 +32,15 @@ typedef float float16v __attribute__((ext_vector_type(16)));
 
 constexpr int kBlockRows = 64;
 
+// Two allocations: `head` holds rows, slot_off and the build's temporaries
+// (sized before the build), `tail` the slot arrays (sized by the scan).
 struct MaskedPlan {
   int device = 0;
   int64_t n = 0;
   int64_t n_blocks = 0;
   int64_t n_slots = 0;         // sum over blocks of the taps they run
+  void* head = nullptr;
+  void* tail = nullptr;
   int32_t* rows = nullptr;     // [n_blocks * 64] caller row of each sorted row (-1 past n)
   int32_t* slot_off = nullptr; // [n_blocks + 1] first tap slot of each block
   int32_t* slot_tap = nullptr; // [n_slots] tap of each slot
@@ -228,21 +232,14 @@ __global__ __launch_bounds__(2 * COUT_T) void k_fwd_masked(
   }
 }
 
-struct Tmp {
-  void* p = nullptr;
-  ~Tmp() {
-    if (p) (void)hipFree(p);
-  }
-};
-
 void free_masked(MaskedPlan* d) {
   if (!d) return;
-  if (d->rows) (void)hipFree(d->rows);
-  if (d->slot_off) (void)hipFree(d->slot_off);
-  if (d->slot_tap) (void)hipFree(d->slot_tap);
-  if (d->slot_nbr) (void)hipFree(d->slot_nbr);
+  if (d->head) (void)hipFree(d->head);
+  if (d->tail) (void)hipFree(d->tail);
   delete d;
 }
+
+size_t up256(size_t v) { return (v + 255) & ~size_t{255}; }
 
 template <int CIN, int COUT_T>
 int launch_masked(const MaskedPlan& p, const _Float16* feats, const _Float16* wp, const float* bias,
@@ -299,50 +296,56 @@ extern "C" int submconv_masked_plan(submconv_map_t map, hipStream_t stream,
   }
   const int64_t n = m.n;
   d->n_blocks = (n + kBlockRows - 1) / kBlockRows;
-  Tmp mask, smask, idx, sidx, umask, cnt, sort_tmp, scan_tmp;
-  MPLAN_CHECK(hipMalloc(&mask.p, 4 * n));
-  MPLAN_CHECK(hipMalloc(&smask.p, 4 * n));
-  MPLAN_CHECK(hipMalloc(&idx.p, 4 * n));
-  MPLAN_CHECK(hipMalloc(&sidx.p, 4 * n));
-  MPLAN_CHECK(hipMalloc(&umask.p, 4 * d->n_blocks));
-  MPLAN_CHECK(hipMalloc(&cnt.p, 4 * (d->n_blocks + 1)));
-  MPLAN_CHECK(hipMalloc(reinterpret_cast<void**>(&d->rows), 4 * d->n_blocks * kBlockRows));
-  MPLAN_CHECK(hipMalloc(reinterpret_cast<void**>(&d->slot_off), 4 * (d->n_blocks + 1)));
+  const size_t nn = static_cast<size_t>(n), nb = static_cast<size_t>(d->n_blocks);
+  size_t sort_bytes = 0, scan_bytes = 0;
+  MPLAN_CHECK(rocprim::radix_sort_pairs(nullptr, sort_bytes, static_cast<uint32_t*>(nullptr),
+                                        static_cast<uint32_t*>(nullptr), static_cast<int32_t*>(nullptr),
+                                        static_cast<int32_t*>(nullptr), nn, 0u,
+                                        static_cast<unsigned>(kTaps3), stream));
+  MPLAN_CHECK(rocprim::exclusive_scan(nullptr, scan_bytes, static_cast<int32_t*>(nullptr),
+                                      static_cast<int32_t*>(nullptr), 0, nb + 1, rocprim::plus<int32_t>(),
+                                      stream));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += up256(bytes > 0 ? bytes : 1);
+    return o;
+  };
+  const size_t o_rows = take(4 * nb * kBlockRows), o_soff = take(4 * (nb + 1));
+  const size_t o_mask = take(4 * nn), o_smask = take(4 * nn), o_idx = take(4 * nn), o_sidx = take(4 * nn);
+  const size_t o_umask = take(4 * nb), o_cnt = take(4 * (nb + 1));
+  const size_t o_sort = take(sort_bytes), o_scan = take(scan_bytes);
+  MPLAN_CHECK(hipMalloc(&d->head, off));
+  char* base = static_cast<char*>(d->head);
+  d->rows = reinterpret_cast<int32_t*>(base + o_rows);
+  d->slot_off = reinterpret_cast<int32_t*>(base + o_soff);
+  uint32_t* mask = reinterpret_cast<uint32_t*>(base + o_mask);
+  uint32_t* smask = reinterpret_cast<uint32_t*>(base + o_smask);
+  int32_t* idx = reinterpret_cast<int32_t*>(base + o_idx);
+  int32_t* sidx = reinterpret_cast<int32_t*>(base + o_sidx);
+  uint32_t* umask = reinterpret_cast<uint32_t*>(base + o_umask);
+  int32_t* cnt = reinterpret_cast<int32_t*>(base + o_cnt);
   const unsigned gb = static_cast<unsigned>((n + 255) / 256);
-  k_masks<<<gb, 256, 0, stream>>>(m.nbr, n, static_cast<uint32_t*>(mask.p), static_cast<int32_t*>(idx.p));
+  k_masks<<<gb, 256, 0, stream>>>(m.nbr, n, mask, idx);
   MPLAN_CHECK(hipGetLastError());
-  size_t tmp_bytes = 0;
-  MPLAN_CHECK(rocprim::radix_sort_pairs(nullptr, tmp_bytes, static_cast<uint32_t*>(mask.p),
-                                        static_cast<uint32_t*>(smask.p), static_cast<int32_t*>(idx.p),
-                                        static_cast<int32_t*>(sidx.p), static_cast<size_t>(n), 0u,
+  MPLAN_CHECK(rocprim::radix_sort_pairs(base + o_sort, sort_bytes, mask, smask, idx, sidx, nn, 0u,
                                         static_cast<unsigned>(kTaps3), stream));
-  MPLAN_CHECK(hipMalloc(&sort_tmp.p, tmp_bytes > 0 ? tmp_bytes : 1));
-  MPLAN_CHECK(rocprim::radix_sort_pairs(sort_tmp.p, tmp_bytes, static_cast<uint32_t*>(mask.p),
-                                        static_cast<uint32_t*>(smask.p), static_cast<int32_t*>(idx.p),
-                                        static_cast<int32_t*>(sidx.p), static_cast<size_t>(n), 0u,
-                                        static_cast<unsigned>(kTaps3), stream));
-  MPLAN_CHECK(hipMemsetAsync(cnt.p, 0, 4 * (d->n_blocks + 1), stream));
+  MPLAN_CHECK(hipMemsetAsync(cnt, 0, 4 * (nb + 1), stream));
   const unsigned gbb = static_cast<unsigned>((d->n_blocks + 3) / 4);
-  k_block_union<<<gbb, 256, 0, stream>>>(static_cast<uint32_t*>(smask.p), static_cast<int32_t*>(sidx.p),
-                                         m.order, n, d->n_blocks, static_cast<uint32_t*>(umask.p),
-                                         static_cast<int32_t*>(cnt.p), d->rows);
+  k_block_union<<<gbb, 256, 0, stream>>>(smask, sidx, m.order, n, d->n_blocks, umask, cnt, d->rows);
   MPLAN_CHECK(hipGetLastError());
-  tmp_bytes = 0;
-  MPLAN_CHECK(rocprim::exclusive_scan(nullptr, tmp_bytes, static_cast<int32_t*>(cnt.p), d->slot_off, 0,
-                                      static_cast<size_t>(d->n_blocks + 1), rocprim::plus<int32_t>(),
-                                      stream));
-  MPLAN_CHECK(hipMalloc(&scan_tmp.p, tmp_bytes > 0 ? tmp_bytes : 1));
-  MPLAN_CHECK(rocprim::exclusive_scan(scan_tmp.p, tmp_bytes, static_cast<int32_t*>(cnt.p), d->slot_off, 0,
-                                      static_cast<size_t>(d->n_blocks + 1), rocprim::plus<int32_t>(),
-                                      stream));
+  MPLAN_CHECK(rocprim::exclusive_scan(base + o_scan, scan_bytes, cnt, d->slot_off, 0, nb + 1,
+                                      rocprim::plus<int32_t>(), stream));
   int32_t total = 0;
   MPLAN_CHECK(hipMemcpyAsync(&total, d->slot_off + d->n_blocks, 4, hipMemcpyDeviceToHost, stream));
   MPLAN_CHECK(hipStreamSynchronize(stream));
   d->n_slots = total;
-  MPLAN_CHECK(hipMalloc(reinterpret_cast<void**>(&d->slot_tap), 4 * (total > 0 ? total : 1)));
-  MPLAN_CHECK(hipMalloc(reinterpret_cast<void**>(&d->slot_nbr), 4 * kBlockRows * (total > 0 ? total : 1)));
-  k_slots<<<gbb, 256, 0, stream>>>(static_cast<uint32_t*>(umask.p), d->slot_off,
-                                   static_cast<int32_t*>(sidx.p), m.nbr, n, d->n_blocks, d->slot_tap,
+  const size_t ns = static_cast<size_t>(total > 0 ? total : 1);
+  const size_t t_nbr = up256(4 * ns);
+  MPLAN_CHECK(hipMalloc(&d->tail, t_nbr + 4 * kBlockRows * ns));
+  d->slot_tap = static_cast<int32_t*>(d->tail);
+  d->slot_nbr = reinterpret_cast<int32_t*>(static_cast<char*>(d->tail) + t_nbr);
+  k_slots<<<gbb, 256, 0, stream>>>(umask, d->slot_off, sidx, m.nbr, n, d->n_blocks, d->slot_tap,
                                    d->slot_nbr);
   MPLAN_CHECK(hipGetLastError());
   MPLAN_CHECK(hipStreamSynchronize(stream));
