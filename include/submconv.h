@@ -129,8 +129,9 @@ typedef struct submconv_map_s* submconv_map_t;
  * or 12 when packed keys exceed 32 bits; 8 bytes of key per site; sort space
  * with SUBMCONV_FLAG_MORTON or SUBMCONV_FLAG_SORTED_KEYS) stays with the
  * device after the call, up to 256 MiB, for the next build, until the
- * process ends; so does a 14 MiB buffer that forwards on W stage the weights
- * in (see submconv_forward), allocated by the first build on the device.
+ * process ends; so do the four 14 MiB buffers that forwards on W stage the
+ * weights in (see submconv_forward), allocated by the first build on the
+ * device.
  * Builds on one device run one at a time.
  */
 int submconv_build_map(const int32_t* coords, int64_t n, int32_t batch, const int32_t grid[3],
@@ -140,7 +141,7 @@ int submconv_build_map(const int32_t* coords, int64_t n, int32_t batch, const in
  * submconv_release_scratch -- free the build scratch that the current device
  * keeps for its next map build (see submconv_build_map); waits for a build in
  * progress on the device and for the device itself. Maps, prepared weights
- * and the 14 MiB weight stage are not affected; the next build allocates its
+ * and the weight stage (4 x 14 MiB) are not affected; the next build allocates its
  * scratch again. Host call, safe at any time.
  */
 int submconv_release_scratch(void);
@@ -253,13 +254,17 @@ int submconv_weights_free(submconv_weights_t w);
  * run a VALU kernel with 64-bit addressing.
  *
  * Allocation: none. For the MFMA kernels W is rearranged first into a
- * per-device buffer of the library (14 MiB, the largest MFMA layer; the
- * first map build on a device allocates it, and it stays until the process
- * ends, like the build's scratch); forwards that take W on different streams of one
- * device are ordered after one another through an event on that buffer
- * (none is recorded while `stream` is being captured into a graph: a
- * captured forward must not run at the same time as another forward that
- * takes W on its device). Forwards with prepared weights
+ * staging buffer of the library (14 MiB each, the largest MFMA layer; the
+ * first map build on a device allocates four, and they stay until the
+ * process ends, like the build's scratch). The first three streams that
+ * forward on W on a device each own one buffer, which the stream's own order
+ * protects; forwards from any further streams share the fourth and are
+ * ordered after one another through an event on it (none is recorded while
+ * `stream` is being captured into a graph). A captured forward must not run
+ * at the same time as another forward on W from the stream it was captured
+ * on, nor, if that stream shares the fourth buffer, from any stream that
+ * shares it; a stream handle that is destroyed and created again counts as
+ * the same stream. Forwards with prepared weights
  * (submconv_forward_prepared) run concurrently on any streams.
  */
 int submconv_forward(submconv_map_t map, const uint16_t* feats, const uint16_t* W,

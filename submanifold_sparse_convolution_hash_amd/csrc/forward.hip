@@ -919,10 +919,16 @@ int prepare_into(const _Float16* W, int K, int cin, int cout, bool grad, _Float1
 // input gradient) 16-bit elements.
 constexpr size_t kStageBytes = size_t{kTaps3} * 256 * 1024 * 2;
 
+// Buffers per device: the first kStageSlots - 1 streams that forward on W
+// each own one for good, so their forwards need no ordering against other
+// streams; any further streams share the last, ordered by an event.
+constexpr int kStageSlots = 4;
 struct Stage {
   std::mutex mu;
-  _Float16* ptr = nullptr;       // this device's staging buffer
-  hipEvent_t done = nullptr;     // recorded after the last forward that read it
+  _Float16* ptr[kStageSlots] = {};            // this device's staging buffers
+  hipStream_t owner[kStageSlots - 1] = {};    // the stream owning each private buffer
+  int owned = 0;                              // private buffers taken (in order)
+  hipEvent_t done = nullptr;     // shared buffer: recorded after the last forward that read it
   hipStream_t last = nullptr;    // the stream of that forward
   bool recorded = false;
 };
@@ -930,10 +936,12 @@ constexpr int kMaxDevices = 64;
 Stage g_stages[kMaxDevices];
 
 // A forward with weights as the caller holds them: for the MFMA kernels they
-// are rearranged into this device's staging buffer first. Forwards on other
-// streams are ordered around the buffer by an event (the stream waits for
-// the previous user's event, and records its own after its launches); while
-// the stream is being captured into a graph no event is used.
+// are rearranged into a staging buffer of the device first: the stream's own
+// buffer (the stream's order alone protects it), or, past the first
+// kStageSlots - 1 streams, the shared one. Forwards on different streams are
+// ordered around the shared buffer by an event (the stream waits for the
+// previous user's event, and records its own after its launches); while the
+// stream is being captured into a graph no event is used.
 template <bool IS_BF16>
 int forward_raw(const Map& m, int ksize, int cin, int cout, const _Float16* feats,
                 const _Float16* W, bool grad, const float* bias, _Float16* out,
@@ -950,20 +958,33 @@ int forward_raw(const Map& m, int ksize, int cin, int cout, const _Float16* feat
                      cin, cout);
   Stage& sg = g_stages[m.device];
   std::lock_guard<std::mutex> lock(sg.mu);
-  if (!sg.ptr || !sg.done)  // a map build on the device sets both up
+  if (!sg.ptr[0] || !sg.done)  // a map build on the device sets both up
     return set_error(SUBMCONV_ERR_INVALID_ARG, "internal: no weight stage on device %d", m.device);
+  // the stream's own buffer, a free one it takes, or the shared one
+  int slot = kStageSlots - 1;
+  for (int i = 0; i < sg.owned; ++i)
+    if (sg.owner[i] == stream) slot = i;
+  if (slot == kStageSlots - 1 && sg.owned < kStageSlots - 1) {
+    slot = sg.owned++;
+    sg.owner[slot] = stream;
+  }
+  _Float16* const buf = sg.ptr[slot];
+  const bool shared = slot == kStageSlots - 1;
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  const bool capturing =
-      hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone;
-  (void)hipGetLastError();  // a failed query is not this call's error
-  if (!capturing && sg.recorded && sg.last != stream)
-    SUBMCONV_HIP_CHECK(hipStreamWaitEvent(stream, sg.done, 0));
+  bool capturing = false;
+  if (shared) {
+    capturing =
+        hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone;
+    (void)hipGetLastError();  // a failed query is not this call's error
+    if (!capturing && sg.recorded && sg.last != stream)
+      SUBMCONV_HIP_CHECK(hipStreamWaitEvent(stream, sg.done, 0));
+  }
   // the layer's W is [K][cin][cout], or [K][cout][cin] for an input gradient
-  const int st = prepare_into(W, K, grad ? cout : cin, grad ? cin : cout, grad, sg.ptr, stream);
+  const int st = prepare_into(W, K, grad ? cout : cin, grad ? cin : cout, grad, buf, stream);
   if (st != SUBMCONV_OK) return st;
-  const int fs = forward_typed<IS_BF16>(m, ksize, cin, cout, feats, sg.ptr, false, bias, out,
+  const int fs = forward_typed<IS_BF16>(m, ksize, cin, cout, feats, buf, false, bias, out,
                                         stream);
-  if (!capturing) {
+  if (shared && !capturing) {
     SUBMCONV_HIP_CHECK(hipEventRecord(sg.done, stream));
     sg.recorded = true;
     sg.last = stream;
@@ -990,18 +1011,20 @@ int check_call(const Map& m, const void* feats, const void* w, const void* out, 
 
 }  // namespace
 
-// Sets up the device's weight stage (one allocation and one event per device,
-// kept until the process ends); every map build calls it, so that a forward,
-// which always has a map, finds it and allocates nothing.
+// Sets up the device's weight stage (one allocation of kStageSlots buffers
+// and one event per device, kept until the process ends); every map build
+// calls it, so that a forward, which always has a map, finds it and
+// allocates nothing.
 int ensure_weight_stage(int device) {
   if (device < 0 || device >= kMaxDevices)
     return set_error(SUBMCONV_ERR_INVALID_ARG, "device %d out of range", device);
   Stage& sg = g_stages[device];
   std::lock_guard<std::mutex> lock(sg.mu);
-  if (!sg.ptr) {
+  if (!sg.ptr[0]) {
     void* p = nullptr;
-    SUBMCONV_HIP_CHECK(hipMalloc(&p, kStageBytes));
-    sg.ptr = static_cast<_Float16*>(p);
+    SUBMCONV_HIP_CHECK(hipMalloc(&p, kStageSlots * kStageBytes));
+    for (int i = 0; i < kStageSlots; ++i)
+      sg.ptr[i] = static_cast<_Float16*>(p) + i * (kStageBytes / 2);
   }
   // the event only orders forwards on other streams of this device behind
   // the buffer's last user (hipStreamWaitEvent), so it needs no system-scope

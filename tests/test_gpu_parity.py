@@ -884,10 +884,10 @@ def test_features_at_the_2gib_limit(dev):
 
 @gpu
 def test_two_streams_raw_weights(dev):
-    """Forwards on weights as the caller holds them share the device's
-    staging buffer: on two side streams at once, each with its own W, every
-    output equals the same forward run alone (the streams are ordered around
-    the buffer by an event)."""
+    """Forwards on weights as the caller holds them on two side streams at
+    once, each with its own W: every output equals the same forward run
+    alone (each stream stages W in its own buffer, or, once three streams
+    own one, in the shared buffer ordered by an event)."""
     sc = _sc()
     wl = workloads.uniform_workload(48, 11000, [(3, 64, 64)], seed=1211, bias_kind="normal", name="rw")
     L = wl.layers[0]
@@ -918,6 +918,43 @@ def test_two_streams_raw_weights(dev):
     ref = oc.submconv_rows(oc.kernel_map(wl.coords, wl.grid, wl.batch, 3), fb.cpu().numpy(),
                            Wb.cpu().numpy(), L.bias)
     _assert_close(ob.float().cpu().numpy(), ref, "stream b")
+    km.free()
+
+
+@gpu
+def test_many_streams_raw_weights(dev):
+    """Six side streams forwarding on their own W at once: at most three
+    streams of a device own a staging buffer, so at least three of these
+    share the fourth, ordered by its event. Every output equals the same
+    forward run alone, and one matches the oracle."""
+    sc = _sc()
+    wl = workloads.uniform_workload(40, 7000, [(3, 128, 128)], seed=1215, bias_kind="normal", name="ms")
+    L = wl.layers[0]
+    km = sc.build_map(_to(dev, wl.coords), wl.grid, wl.batch)
+    rng = np.random.default_rng(1216)
+    b = _to(dev, L.bias)
+    fs, ws, refs = [], [], []
+    for i in range(6):
+        fs.append(_to(dev, rng.standard_normal((wl.n, 128)).astype(np.float16)))
+        ws.append(_to(dev, (rng.standard_normal(L.W.shape) / 60).astype(np.float16)))
+        refs.append(sc.forward(km, fs[i], ws[i], b))
+    torch.cuda.synchronize(dev)
+    outs = [torch.empty_like(r) for r in refs]
+    streams = [torch.cuda.Stream(device=dev) for _ in range(6)]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream(dev))
+    for _ in range(4):
+        for i, s in enumerate(streams):
+            with torch.cuda.stream(s):
+                sc.forward(km, fs[i], ws[i], b, out=outs[i])
+    for s in streams:
+        torch.cuda.current_stream(dev).wait_stream(s)
+    torch.cuda.synchronize(dev)
+    for i in range(6):
+        assert torch.equal(outs[i], refs[i]), f"stream {i}"
+    ref = oc.submconv_rows(oc.kernel_map(wl.coords, wl.grid, wl.batch, 3), fs[5].cpu().numpy(),
+                           ws[5].cpu().numpy(), L.bias)
+    _assert_close(outs[5].float().cpu().numpy(), ref, "stream 5")
     km.free()
 
 
