@@ -58,9 +58,9 @@ CSRC = os.path.join(ROOT, "submanifold_sparse_convolution_hash_amd", "csrc")
 MEASURED_TRAFFIC = {
     ("c3_128_128", "forward"): {
         "src": ["forward.hip", "map_build.hip"],  # the kernel, and the map's tile size
-        "sha256": "43ab4ef81df78d08eb6f352b02b797f5f51f465da0d71709f9062e4d187d8869",
-        "fetch_kib": 38908.32, "write_kib": 52429.93,
-        "fetch_factor": 524288.0 / 262155.9, "write_factor": 524288.0 / 524288.0},
+        "sha256": "e92f7fe41a046f320df2a14c59052cc5baef392380f9690e33af2430da88db21",
+        "fetch_kib": 38898.9, "write_kib": 52434.6,
+        "fetch_factor": 524288.0 / 262155.5, "write_factor": 524288.0 / 524288.0},
     ("c5_512_chain", "forward"): {
         "src": ["staged.hip", "map_build.hip"],  # the staged kernel (64 -> 32), and its plan
         "sha256": "e619e2cd48f2ce2cbcc039929127659a344eea2cec442a9fe50c76e3fbb1a156",
@@ -444,31 +444,29 @@ def main():
 
         kernel = step
 
-    def timed(fn, steps):
-        """Average µs of `steps` back-to-back calls inside one event pair on
-        the launch stream (torch's current stream), after a synchronisation."""
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps * 1e3
-
     for _ in range(args.warmup):
         step()
+    # The K timed steps, then K launches of the op's dominant kernel alone,
+    # each run back to back inside one event pair on the launch stream
+    # (torch's current stream), with a synchronisation before the steps and
+    # after the kernels and no idle time between the two runs.
+    torch.cuda.synchronize()
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
     t = time.perf_counter()
-    step_us = timed(step, args.steps)
-    wall_ms = (time.perf_counter() - t) * 1e3 / args.steps
-    ms_step = step_us / 1e3
-    print(f"[bench] step {step_us:.1f} us (wall {wall_ms * 1e3:.1f} us)", file=sys.stderr, flush=True)
-
-    # the op's dominant kernel alone, timed as the steps are: back to back in
-    # one event pair
-    for _ in range(args.warmup):
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    for _ in range(args.steps):
         kernel()
-    k_us = timed(kernel, args.steps)
+    e2.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t) * 1e3 / args.steps
+    step_us = e0.elapsed_time(e1) / args.steps * 1e3
+    k_us = e1.elapsed_time(e2) / args.steps * 1e3
+    ms_step = step_us / 1e3
+    print(f"[bench] step {step_us:.1f} us (wall of steps and kernels {wall_ms * 1e3:.1f} us)",
+          file=sys.stderr, flush=True)
     alg_bytes = algorithmic_bytes(op, wl.n, L.cin, L.cout, L.ksize, args.morton, bias is not None,
                                   pairs, km.tile_rows, staged)
     achieved_gbs = alg_bytes / (k_us * 1e-6) / 1e9
