@@ -959,6 +959,45 @@ def test_many_streams_raw_weights(dev):
 
 
 @gpu
+def test_many_streams_forward_and_input_grad(dev):
+    """Five side streams, each alternating a forward and an input gradient
+    on its own W (the input gradient stages the flipped, transposed W in the
+    same buffers), fp16 and bf16 mixed: every output equals the same call
+    run alone."""
+    sc = _sc()
+    wl = workloads.uniform_workload(36, 5000, [(3, 64, 64)], seed=1217, bias_kind=None, name="mi")
+    L = wl.layers[0]
+    km = sc.build_map(_to(dev, wl.coords), wl.grid, wl.batch)
+    rng = np.random.default_rng(1218)
+    args, refs = [], []
+    for i in range(5):
+        dt = torch.bfloat16 if i % 2 else torch.float16
+        f = _to(dev, rng.standard_normal((wl.n, 64)).astype(np.float16)).to(dt)
+        g = _to(dev, rng.standard_normal((wl.n, 64)).astype(np.float16)).to(dt)
+        W = _to(dev, (rng.standard_normal(L.W.shape) / 40).astype(np.float16)).to(dt)
+        args.append((f, g, W))
+        refs.append((sc.forward(km, f, W), sc.backward_input(km, g, W)))
+    torch.cuda.synchronize(dev)
+    outs = [(torch.empty_like(a), torch.empty_like(b)) for a, b in refs]
+    streams = [torch.cuda.Stream(device=dev) for _ in range(5)]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream(dev))
+    for _ in range(3):
+        for i, st in enumerate(streams):
+            f, g, W = args[i]
+            with torch.cuda.stream(st):
+                sc.forward(km, f, W, out=outs[i][0])
+                sc.backward_input(km, g, W, out=outs[i][1])
+    for st in streams:
+        torch.cuda.current_stream(dev).wait_stream(st)
+    torch.cuda.synchronize(dev)
+    for i in range(5):
+        assert torch.equal(outs[i][0], refs[i][0]), f"forward, stream {i}"
+        assert torch.equal(outs[i][1], refs[i][1]), f"input gradient, stream {i}"
+    km.free()
+
+
+@gpu
 def test_raw_weights_forward_in_a_captured_graph(dev):
     """submconv_forward on W inside a captured graph (the weight
     rearrangement and the gather-GEMM are both captured): every replay, with
