@@ -219,11 +219,13 @@ struct CfgPP {
 template <int CIN, int COUT_T, bool K3, bool IS_BF16, int GR_, int NP = 1, int M_ = kTileRows>
 __global__ __launch_bounds__((CfgPP<CIN, COUT_T, K3, GR_, M_>::NT)) void k_fwd_pp(
     const int2* __restrict__ ent, const int32_t* __restrict__ tile_off,
-    const uint16_t* __restrict__ tile_cnt, const int32_t* __restrict__ order, int64_t n,
-    const _Float16* __restrict__ feats, const _Float16* __restrict__ wp,
-    const float* __restrict__ bias, _Float16* __restrict__ out, int cout, int n_tiles, int n_ct,
-    int tiles_per_xcd, int n_pairs, int tile_rows) {
-  // tile_rows: the map's rows per tile, at most M (the LDS accumulator's rows)
+    const uint16_t* __restrict__ tile_cnt, const int32_t* __restrict__ walk,
+    const int32_t* __restrict__ order, int64_t n, const _Float16* __restrict__ feats,
+    const _Float16* __restrict__ wp, const float* __restrict__ bias, _Float16* __restrict__ out,
+    int cout, int n_tiles, int n_ct, int tiles_per_xcd, int n_pairs, int tile_rows) {
+  // tile_rows: the map's rows per tile, at most M (the LDS accumulator's
+  // rows); walk: the tile at each position of an XCD's run, or nullptr for
+  // tile i at position i
   using C = CfgPP<CIN, COUT_T, K3, GR_, M_>;
   constexpr int M = C::M, GR = C::GR, NRBW = C::NRBW, KS = C::KS, RC = C::RC;
   constexpr int LB = C::LB, LE = C::LE, CPT = C::CPT, NCG = C::NCG, BR = C::BR;
@@ -261,8 +263,9 @@ __global__ __launch_bounds__((CfgPP<CIN, COUT_T, K3, GR_, M_>::NT)) void k_fwd_p
     Raw r{0, 0, -1, 0, s % NP};
     const int u = j0 + (s / NP) * wpx;
     const int tl = u / n_ct;
-    const int tile = xcd * tiles_per_xcd + tl;
-    if (u < units && tl < tiles_per_xcd && tile < n_tiles) {
+    const int pos = xcd * tiles_per_xcd + tl;
+    if (u < units && tl < tiles_per_xcd && pos < n_tiles) {
+      const int tile = walk ? walk[pos] : pos;
       r.tile = tile;
       r.ct = u - tl * n_ct;
       if (K3) {
@@ -791,8 +794,9 @@ int launch_pp(const Map& m, const Tiles& T, const _Float16* feats, const _Float1
   const int64_t wpx = std::min<int64_t>(units_per_xcd, int64_t{cus_per_xcd()} * per_cu);
   k_fwd_pp<CIN, COUT_T, K3, IS_BF16, GR, NP, M><<<static_cast<unsigned>(8 * wpx), C::NT, 0,
                                                  stream>>>(
-      K3 ? T.ent : nullptr, K3 ? T.off : nullptr, K3 ? T.cnt : nullptr, K3 ? m.order : nullptr,
-      m.n, feats, wp, bias, out, cout, n_tiles, n_ct, tiles_per_xcd, n_pairs, T.rows);
+      K3 ? T.ent : nullptr, K3 ? T.off : nullptr, K3 ? T.cnt : nullptr, K3 ? T.walk : nullptr,
+      K3 ? m.order : nullptr, m.n, feats, wp, bias, out, cout, n_tiles, n_ct, tiles_per_xcd,
+      n_pairs, T.rows);
   SUBMCONV_HIP_CHECK(hipGetLastError());
   return SUBMCONV_OK;
 }

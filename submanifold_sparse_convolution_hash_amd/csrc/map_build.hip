@@ -508,6 +508,56 @@ int wide_tile_rows(int64_t n, int cus) {
   return tr > kTileRows ? tr : 0;
 }
 
+// The order of the wide tiles in each XCD's run. A forward with one
+// workgroup per CU deals the tiles of XCD x, [x tpx, (x+1) tpx), to its wpx
+// workgroups by run position: workgroup j takes positions j, j + wpx, ...
+// A tile's cost is the steps the forward gives it (the centre's steps, then
+// one per 32 entries of each other position, the off-centre part padded to
+// a multiple of 4) plus about an epilogue's worth; the costliest tiles go
+// first, each to the workgroup with the least cost so far that still has a
+// position, so that the workgroups finish together. Tiles stay in their
+// XCD's run (the neighbouring rows that share its L2).
+void balance_walk(const uint16_t* cnt, int64_t nt, int wpx, int32_t* walk) {
+  constexpr int kGroup = 32, kCentre = kTileRowsWide / kGroup;
+  constexpr int kRound = (4 - kCentre % 4) % 4, kEpilogue = 3;
+  const int64_t tpx = (nt + 7) / 8;
+  std::vector<int> cost(static_cast<size_t>(nt));
+  for (int64_t t = 0; t < nt; ++t) {
+    int f = kCentre;
+    for (int p = 1; p < kTaps3; ++p) f += (cnt[t * kTaps3 + p] + kGroup - 1) / kGroup;
+    const int off = std::max(f - kCentre - kRound, 0);
+    cost[static_cast<size_t>(t)] = std::max(kCentre + kRound + ((off + 3) & ~3), 8) + kEpilogue;
+  }
+  std::vector<int32_t> tiles;
+  std::vector<int64_t> load;
+  std::vector<int> used;
+  for (int64_t x = 0; x < 8; ++x) {
+    const int64_t lo = x * tpx, hi = std::min(nt, lo + tpx);
+    if (hi <= lo) break;
+    const int64_t count = hi - lo;
+    const int w = static_cast<int>(std::min<int64_t>(wpx, count));
+    tiles.resize(static_cast<size_t>(count));
+    for (int64_t i = 0; i < count; ++i) tiles[static_cast<size_t>(i)] = static_cast<int32_t>(lo + i);
+    std::stable_sort(tiles.begin(), tiles.end(), [&](int32_t a, int32_t b) {
+      return cost[static_cast<size_t>(a)] > cost[static_cast<size_t>(b)];
+    });
+    load.assign(static_cast<size_t>(w), 0);
+    used.assign(static_cast<size_t>(w), 0);
+    for (const int32_t tile : tiles) {
+      int best = -1;
+      for (int j = 0; j < w; ++j) {
+        const int64_t pos = j + static_cast<int64_t>(used[static_cast<size_t>(j)]) * w;
+        if (pos < count && (best < 0 || load[static_cast<size_t>(j)] < load[static_cast<size_t>(best)]))
+          best = j;
+      }
+      const int64_t pos = best + static_cast<int64_t>(used[static_cast<size_t>(best)]) * w;
+      walk[lo + pos] = tile;
+      ++used[static_cast<size_t>(best)];
+      load[static_cast<size_t>(best)] += cost[static_cast<size_t>(tile)];
+    }
+  }
+}
+
 // Hands out 256-byte aligned pieces of one allocation: a first pass with no
 // base sizes it, a second pass over the same requests gives the pointers.
 struct Carve {
@@ -698,6 +748,7 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
     if (nt_wide > 0) {
       wide.cnt = c.take<uint16_t>(kTaps3 * nt_wide);
       wide.off = c.take<int32_t>(nt_wide + 1);
+      wide.walk = c.take<int32_t>(nt_wide);
     }
   };
 
@@ -863,10 +914,14 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   }
   if (const int st = fill_tiles(base); st != SUBMCONV_OK) return st;
   uint64_t host_groups[kTaps3] = {};
+  std::vector<uint16_t> wide_cnt;
   if (use_wide) {
     if (const int st = fill_tiles(wide); st != SUBMCONV_OK) return st;
     BUILD_CHECK(hipMemcpyAsync(host_groups, groups_wide, sizeof(host_groups), hipMemcpyDeviceToHost,
                                stream));
+    wide_cnt.resize(static_cast<size_t>(kTaps3 * wide.n));
+    BUILD_CHECK(hipMemcpyAsync(wide_cnt.data(), wide.cnt, sizeof(uint16_t) * wide_cnt.size(),
+                               hipMemcpyDeviceToHost, stream));
   }
   // the staged plan of a dense map (or of any map, when asked for): its
   // units are counted before the wait, and written after it
@@ -881,8 +936,18 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   }
   // the forward may run on another stream: the map is complete on return
   BUILD_CHECK(hipStreamSynchronize(stream));
-  if (use_wide)
+  std::vector<int32_t> wide_walk;
+  if (use_wide) {
     for (int q = 0; q < kTaps3; ++q) wide.pos_groups[q] = static_cast<int64_t>(host_groups[q]);
+    // the forward's workgroups per XCD at one per CU
+    wide_walk.resize(static_cast<size_t>(wide.n));
+    balance_walk(wide_cnt.data(), wide.n, std::max(1, cus / 8), wide_walk.data());
+    BUILD_CHECK(hipMemcpyAsync(wide.walk, wide_walk.data(), sizeof(int32_t) * wide_walk.size(),
+                               hipMemcpyHostToDevice, stream));
+    BUILD_CHECK(hipStreamSynchronize(stream));
+  } else {
+    wide.walk = nullptr;
+  }
   Staged staged;
   // (the kernel's staged-row offsets are 32-bit)
   if (want_staged && host_staged[0] > 0 && host_staged[1] < INT32_MAX) {

@@ -53,6 +53,10 @@ struct Tiles {
   uint16_t* cnt = nullptr;
   int32_t* off = nullptr;
   int2* ent = nullptr;
+  // [n] int32 or nullptr: the order in which each XCD's run of tiles is
+  // walked (position i of the run -> tile), balanced across the workgroups
+  // of a forward with one workgroup per CU; nullptr: tile i at position i
+  int32_t* walk = nullptr;
   // groups of kGroupRows entries per processing position, over all tiles
   int64_t pos_groups[kTaps3] = {};
 };
