@@ -58,25 +58,25 @@ CSRC = os.path.join(ROOT, "submanifold_sparse_convolution_hash_amd", "csrc")
 MEASURED_TRAFFIC = {
     ("c3_128_128", "forward"): {
         "src": ["forward.hip", "map_build.hip"],  # the kernel, and the map's tile size
-        "sha256": "e92f7fe41a046f320df2a14c59052cc5baef392380f9690e33af2430da88db21",
-        "fetch_kib": 38898.9, "write_kib": 52434.6,
-        "fetch_factor": 524288.0 / 262155.5, "write_factor": 524288.0 / 524288.0},
+        "sha256": "7119ce66efeda5ea5b943086472a0abbea7dfc2508e6787a55ca3e4802e7b855",
+        "fetch_kib": 49387.7, "write_kib": 52431.9,
+        "fetch_factor": 524288.0 / 262171.9, "write_factor": 524288.0 / 524288.0},
     ("c5_512_chain", "forward"): {
         "src": ["staged.hip", "map_build.hip"],  # the staged kernel (64 -> 32), and its plan
-        "sha256": "e619e2cd48f2ce2cbcc039929127659a344eea2cec442a9fe50c76e3fbb1a156",
-        "fetch_kib": 170177.18, "write_kib": 95630.8,
-        "fetch_factor": 524288.0 / 262155.9, "write_factor": 524288.0 / 524288.0},
+        "sha256": "528fba85ec7bbbb55da1f095cc687615d03942bc25d5ca20af5c7bba9855303f",
+        "fetch_kib": 168074.3, "write_kib": 95630.2,
+        "fetch_factor": 524288.0 / 262169.6, "write_factor": 524288.0 / 524288.0},
     ("c5_512_chain", "backward_weight"): {
         # the staged weight gradient (64 -> 32) and its reduce: the call bench.py times
         "src": ["staged_bwd.hip", "map_build.hip"],
-        "sha256": "6abc658d79adc8f4928d6be89051478f2c634bd97be4e335b81311d9d6cc7ac5",
-        "fetch_kib": 195407.1 + 27656.5, "write_kib": 55296.0 + 216.0,
-        "fetch_factor": 524288.0 / 262155.9, "write_factor": 524288.0 / 524288.0},
+        "sha256": "646fac0bd6d7330d4fe08ba295ba0f8bc637109d54428dea6d5f2010e0b42a08",
+        "fetch_kib": 195540.0 + 27656.5, "write_kib": 55296.0 + 216.0,
+        "fetch_factor": 524288.0 / 262166.6, "write_factor": 524288.0 / 524288.0},
     ("c4_256_shell", "forward"): {
         "src": ["staged_wide.hip", "map_build.hip"],  # the staged kernel (256 -> 256), and its plan
-        "sha256": "03b56b3fe31da67445cd61435f51401a8c74183c0487837a54f0dffc55309d06",
-        "fetch_kib": 2068079.3, "write_kib": 372321.9,
-        "fetch_factor": 524288.0 / 262155.9, "write_factor": 524288.0 / 524288.0},
+        "sha256": "e413a3eaf46b8d85735aa0a76c447fec9209636778959f08b2724cec098fdad6",
+        "fetch_kib": 2072867.3, "write_kib": 372321.9,
+        "fetch_factor": 524288.0 / 262171.1, "write_factor": 524288.0 / 524288.0},
 }
 
 METRICS = {
