@@ -415,6 +415,84 @@ __global__ void k_order_out(const int32_t* __restrict__ order, int64_t n, int32_
   if (t < n) out[t] = order ? order[t] : static_cast<int32_t>(t);
 }
 
+// The order of the wide tiles in each XCD's run (one workgroup per XCD). A
+// forward with one workgroup per CU deals the tiles of XCD x, [x tpx,
+// (x+1) tpx), to its wpx workgroups by run position: workgroup j takes
+// positions j, j + wpx, ... A tile's cost is the steps the forward gives it
+// (the centre's, then one per 32 entries of each other position, the
+// off-centre part padded to a multiple of 4) plus about an epilogue's worth.
+// The costliest tiles go first (ties: the lower tile), each to the workgroup
+// with the least cost so far that still has a position (ties: the lower
+// workgroup), so that the workgroups finish together; tiles stay in their
+// XCD's run, whose neighbouring rows share its L2. Runs of more than
+// kWalkMax tiles (many units per workgroup, which even out by themselves)
+// keep their order.
+constexpr int kWalkMax = 256;
+__global__ __launch_bounds__(kWalkMax) void k_tile_walk(const uint16_t* __restrict__ cnt,
+                                                         int64_t nt, int64_t tpx, int wpx,
+                                                         int32_t* __restrict__ walk) {
+  constexpr int kGroup = 32, kCentre = kTileRowsWide / kGroup;
+  constexpr int kRound = (4 - kCentre % 4) % 4, kEpilogue = 3;
+  __shared__ uint32_t key[kWalkMax];  // cost << 16 | (0xffff - index): descending = costliest, lowest
+  const int64_t lo = static_cast<int64_t>(blockIdx.x) * tpx;
+  const int64_t hi = lo + tpx < nt ? lo + tpx : nt;
+  if (hi <= lo) return;
+  const int count = static_cast<int>(hi - lo);
+  const int tid = threadIdx.x;
+  if (count > kWalkMax) {
+    for (int64_t i = lo + tid; i < hi; i += blockDim.x) walk[i] = static_cast<int32_t>(i);
+    return;
+  }
+  uint32_t k = 0;
+  if (tid < count) {
+    int f = kCentre;
+    for (int p = 1; p < kTaps3; ++p) f += (cnt[(lo + tid) * kTaps3 + p] + kGroup - 1) / kGroup;
+    const int off = f - kCentre - kRound > 0 ? f - kCentre - kRound : 0;
+    const int steps = kCentre + kRound + ((off + 3) & ~3);
+    const uint32_t c = static_cast<uint32_t>((steps > 8 ? steps : 8) + kEpilogue);
+    k = (c << 16) | static_cast<uint32_t>(0xffff - tid);
+  }
+  key[tid] = k;
+  __syncthreads();
+  // bitonic sort, descending
+  for (int size = 2; size <= kWalkMax; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const int partner = tid ^ stride;
+      if (partner > tid) {
+        const uint32_t a = key[tid], b = key[partner];
+        const bool desc = (tid & size) == 0;
+        if (desc ? a < b : a > b) {
+          key[tid] = b;
+          key[partner] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // greedy placement by the first wave: lane j is workgroup j
+  if (tid >= 64) return;
+  const int w = wpx < count ? wpx : count;
+  int64_t load = 0;
+  int used = 0;
+  for (int i = 0; i < count; ++i) {
+    const uint32_t ki = key[i];
+    const int tile = 0xffff - static_cast<int>(ki & 0xffff);
+    const int c = static_cast<int>(ki >> 16);
+    const bool open = tid < w && tid + used * w < count;
+    // the least-loaded open workgroup, the lowest on a tie (loads stay far below 2^40)
+    int64_t v = open ? (load << 6) | tid : INT64_MAX;
+    for (int sh = 1; sh < 64; sh <<= 1) {
+      const int64_t o = __shfl_xor(v, sh, 64);
+      v = o < v ? o : v;
+    }
+    if (open && (v & 63) == tid) {
+      walk[lo + tid + static_cast<int64_t>(used) * w] = static_cast<int32_t>(lo + tile);
+      load += c;
+      ++used;
+    }
+  }
+}
+
 inline unsigned grid_for(int64_t n, int block) {
   return static_cast<unsigned>((n + block - 1) / block);
 }
@@ -506,56 +584,6 @@ int wide_tile_rows(int64_t n, int cus) {
   const int64_t slots = r288 * cus;
   const int tr = static_cast<int>(std::min<int64_t>((n + slots - 1) / slots, kTileRowsWide));
   return tr > kTileRows ? tr : 0;
-}
-
-// The order of the wide tiles in each XCD's run. A forward with one
-// workgroup per CU deals the tiles of XCD x, [x tpx, (x+1) tpx), to its wpx
-// workgroups by run position: workgroup j takes positions j, j + wpx, ...
-// A tile's cost is the steps the forward gives it (the centre's steps, then
-// one per 32 entries of each other position, the off-centre part padded to
-// a multiple of 4) plus about an epilogue's worth; the costliest tiles go
-// first, each to the workgroup with the least cost so far that still has a
-// position, so that the workgroups finish together. Tiles stay in their
-// XCD's run (the neighbouring rows that share its L2).
-void balance_walk(const uint16_t* cnt, int64_t nt, int wpx, int32_t* walk) {
-  constexpr int kGroup = 32, kCentre = kTileRowsWide / kGroup;
-  constexpr int kRound = (4 - kCentre % 4) % 4, kEpilogue = 3;
-  const int64_t tpx = (nt + 7) / 8;
-  std::vector<int> cost(static_cast<size_t>(nt));
-  for (int64_t t = 0; t < nt; ++t) {
-    int f = kCentre;
-    for (int p = 1; p < kTaps3; ++p) f += (cnt[t * kTaps3 + p] + kGroup - 1) / kGroup;
-    const int off = std::max(f - kCentre - kRound, 0);
-    cost[static_cast<size_t>(t)] = std::max(kCentre + kRound + ((off + 3) & ~3), 8) + kEpilogue;
-  }
-  std::vector<int32_t> tiles;
-  std::vector<int64_t> load;
-  std::vector<int> used;
-  for (int64_t x = 0; x < 8; ++x) {
-    const int64_t lo = x * tpx, hi = std::min(nt, lo + tpx);
-    if (hi <= lo) break;
-    const int64_t count = hi - lo;
-    const int w = static_cast<int>(std::min<int64_t>(wpx, count));
-    tiles.resize(static_cast<size_t>(count));
-    for (int64_t i = 0; i < count; ++i) tiles[static_cast<size_t>(i)] = static_cast<int32_t>(lo + i);
-    std::stable_sort(tiles.begin(), tiles.end(), [&](int32_t a, int32_t b) {
-      return cost[static_cast<size_t>(a)] > cost[static_cast<size_t>(b)];
-    });
-    load.assign(static_cast<size_t>(w), 0);
-    used.assign(static_cast<size_t>(w), 0);
-    for (const int32_t tile : tiles) {
-      int best = -1;
-      for (int j = 0; j < w; ++j) {
-        const int64_t pos = j + static_cast<int64_t>(used[static_cast<size_t>(j)]) * w;
-        if (pos < count && (best < 0 || load[static_cast<size_t>(j)] < load[static_cast<size_t>(best)]))
-          best = j;
-      }
-      const int64_t pos = best + static_cast<int64_t>(used[static_cast<size_t>(best)]) * w;
-      walk[lo + pos] = tile;
-      ++used[static_cast<size_t>(best)];
-      load[static_cast<size_t>(best)] += cost[static_cast<size_t>(tile)];
-    }
-  }
 }
 
 // Hands out 256-byte aligned pieces of one allocation: a first pass with no
@@ -914,14 +942,14 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   }
   if (const int st = fill_tiles(base); st != SUBMCONV_OK) return st;
   uint64_t host_groups[kTaps3] = {};
-  std::vector<uint16_t> wide_cnt;
   if (use_wide) {
     if (const int st = fill_tiles(wide); st != SUBMCONV_OK) return st;
+    // the walk order for a forward with one workgroup per CU (cus / 8 per XCD)
+    k_tile_walk<<<8, kWalkMax, 0, stream>>>(wide.cnt, wide.n, (wide.n + 7) / 8,
+                                            std::max(1, cus / 8), wide.walk);
+    BUILD_CHECK(hipGetLastError());
     BUILD_CHECK(hipMemcpyAsync(host_groups, groups_wide, sizeof(host_groups), hipMemcpyDeviceToHost,
                                stream));
-    wide_cnt.resize(static_cast<size_t>(kTaps3 * wide.n));
-    BUILD_CHECK(hipMemcpyAsync(wide_cnt.data(), wide.cnt, sizeof(uint16_t) * wide_cnt.size(),
-                               hipMemcpyDeviceToHost, stream));
   }
   // the staged plan of a dense map (or of any map, when asked for): its
   // units are counted before the wait, and written after it
@@ -936,18 +964,8 @@ extern "C" int submconv_build_map(const int32_t* coords, int64_t n, int32_t batc
   }
   // the forward may run on another stream: the map is complete on return
   BUILD_CHECK(hipStreamSynchronize(stream));
-  std::vector<int32_t> wide_walk;
-  if (use_wide) {
+  if (use_wide)
     for (int q = 0; q < kTaps3; ++q) wide.pos_groups[q] = static_cast<int64_t>(host_groups[q]);
-    // the forward's workgroups per XCD at one per CU
-    wide_walk.resize(static_cast<size_t>(wide.n));
-    balance_walk(wide_cnt.data(), wide.n, std::max(1, cus / 8), wide_walk.data());
-    BUILD_CHECK(hipMemcpyAsync(wide.walk, wide_walk.data(), sizeof(int32_t) * wide_walk.size(),
-                               hipMemcpyHostToDevice, stream));
-    BUILD_CHECK(hipStreamSynchronize(stream));
-  } else {
-    wide.walk = nullptr;
-  }
   Staged staged;
   // (the kernel's staged-row offsets are 32-bit)
   if (want_staged && host_staged[0] > 0 && host_staged[1] < INT32_MAX) {
