@@ -58,25 +58,25 @@ CSRC = os.path.join(ROOT, "submanifold_sparse_convolution_hash_amd", "csrc")
 MEASURED_TRAFFIC = {
     ("c3_128_128", "forward"): {
         "src": ["forward.hip", "map_build.hip"],  # the kernel, and the map's tile size
-        "sha256": "7119ce66efeda5ea5b943086472a0abbea7dfc2508e6787a55ca3e4802e7b855",
-        "fetch_kib": 49387.7, "write_kib": 52431.9,
-        "fetch_factor": 524288.0 / 262171.9, "write_factor": 524288.0 / 524288.0},
+        "sha256": "0f4b360452b448220799c64650ddf23d7cc734f49374a2e3bd6513d03029610c",
+        "fetch_kib": 49379.4, "write_kib": 52429.3,
+        "fetch_factor": 524288.0 / 262169.8, "write_factor": 524288.0 / 524288.0},
     ("c5_512_chain", "forward"): {
         "src": ["staged.hip", "map_build.hip"],  # the staged kernel (64 -> 32), and its plan
-        "sha256": "528fba85ec7bbbb55da1f095cc687615d03942bc25d5ca20af5c7bba9855303f",
-        "fetch_kib": 168074.3, "write_kib": 95630.2,
-        "fetch_factor": 524288.0 / 262169.6, "write_factor": 524288.0 / 524288.0},
+        "sha256": "b0f2dd13d41743a4c842b45551fa9e0d86616936b0a3ffc58188395d4ec91023",
+        "fetch_kib": 169595.7, "write_kib": 95630.9,
+        "fetch_factor": 524288.0 / 262170.3, "write_factor": 524288.0 / 524288.0},
     ("c5_512_chain", "backward_weight"): {
         # the staged weight gradient (64 -> 32) and its reduce: the call bench.py times
         "src": ["staged_bwd.hip", "map_build.hip"],
-        "sha256": "646fac0bd6d7330d4fe08ba295ba0f8bc637109d54428dea6d5f2010e0b42a08",
-        "fetch_kib": 195540.0 + 27656.5, "write_kib": 55296.0 + 216.0,
-        "fetch_factor": 524288.0 / 262166.6, "write_factor": 524288.0 / 524288.0},
+        "sha256": "fd19916f07e24285ebdc5de4e9420c49b01a8050eddf442384dfdb0aff3cd83a",
+        "fetch_kib": 195473.9 + 27656.5, "write_kib": 55296.0 + 216.0,
+        "fetch_factor": 524288.0 / 262167.2, "write_factor": 524288.0 / 524288.0},
     ("c4_256_shell", "forward"): {
         "src": ["staged_wide.hip", "map_build.hip"],  # the staged kernel (256 -> 256), and its plan
-        "sha256": "e413a3eaf46b8d85735aa0a76c447fec9209636778959f08b2724cec098fdad6",
-        "fetch_kib": 2072867.3, "write_kib": 372321.9,
-        "fetch_factor": 524288.0 / 262171.1, "write_factor": 524288.0 / 524288.0},
+        "sha256": "25a69e8d4c70100ced58223810cd4fc13e281b93f7ce8924f6852efab20bda43",
+        "fetch_kib": 2076727.6, "write_kib": 372321.9,
+        "fetch_factor": 524288.0 / 262170.0, "write_factor": 524288.0 / 524288.0},
 }
 
 METRICS = {
