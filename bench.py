@@ -58,25 +58,25 @@ CSRC = os.path.join(ROOT, "submanifold_sparse_convolution_hash_amd", "csrc")
 MEASURED_TRAFFIC = {
     ("c3_128_128", "forward"): {
         "src": ["forward.hip", "map_build.hip"],  # the kernel, and the map's tile size
-        "sha256": "0f4b360452b448220799c64650ddf23d7cc734f49374a2e3bd6513d03029610c",
-        "fetch_kib": 49379.4, "write_kib": 52429.3,
-        "fetch_factor": 524288.0 / 262169.8, "write_factor": 524288.0 / 524288.0},
+        "sha256": "58379b2e89bb43ddf2c4f318803e671165dc532190e1195c6cd804526e716e00",
+        "fetch_kib": 49377.4, "write_kib": 52430.7,
+        "fetch_factor": 524288.0 / 262170.9, "write_factor": 524288.0 / 524288.0},
     ("c5_512_chain", "forward"): {
         "src": ["staged.hip", "map_build.hip"],  # the staged kernel (64 -> 32), and its plan
-        "sha256": "b0f2dd13d41743a4c842b45551fa9e0d86616936b0a3ffc58188395d4ec91023",
-        "fetch_kib": 169595.7, "write_kib": 95630.9,
-        "fetch_factor": 524288.0 / 262170.3, "write_factor": 524288.0 / 524288.0},
+        "sha256": "59d85ecd7a57ae395b215df26e4b960f1191677160ce4c408c1fd486515174df",
+        "fetch_kib": 168751.0, "write_kib": 95630.5,
+        "fetch_factor": 524288.0 / 262170.0, "write_factor": 524288.0 / 524288.0},
     ("c5_512_chain", "backward_weight"): {
         # the staged weight gradient (64 -> 32) and its reduce: the call bench.py times
         "src": ["staged_bwd.hip", "map_build.hip"],
-        "sha256": "fd19916f07e24285ebdc5de4e9420c49b01a8050eddf442384dfdb0aff3cd83a",
-        "fetch_kib": 195473.9 + 27656.5, "write_kib": 55296.0 + 216.0,
-        "fetch_factor": 524288.0 / 262167.2, "write_factor": 524288.0 / 524288.0},
+        "sha256": "ee68c00cb7a9fa3ce43ce3c826da56166e4d758d23e519adef566fae22430577",
+        "fetch_kib": 195501.9 + 27656.5, "write_kib": 55296.0 + 216.0,
+        "fetch_factor": 524288.0 / 262159.1, "write_factor": 524288.0 / 524288.0},
     ("c4_256_shell", "forward"): {
         "src": ["staged_wide.hip", "map_build.hip"],  # the staged kernel (256 -> 256), and its plan
-        "sha256": "25a69e8d4c70100ced58223810cd4fc13e281b93f7ce8924f6852efab20bda43",
-        "fetch_kib": 2076727.6, "write_kib": 372321.9,
-        "fetch_factor": 524288.0 / 262170.0, "write_factor": 524288.0 / 524288.0},
+        "sha256": "057d7490056cdcf9fa2e8abef00a7b3dd37286e31b8181b3325c9bef842de8b5",
+        "fetch_kib": 2059962.6, "write_kib": 372321.9,
+        "fetch_factor": 524288.0 / 262160.9, "write_factor": 524288.0 / 524288.0},
 }
 
 METRICS = {

@@ -425,8 +425,9 @@ __global__ void k_order_out(const int32_t* __restrict__ order, int64_t n, int32_
 // with the least cost so far that still has a position (ties: the lower
 // workgroup), so that the workgroups finish together; tiles stay in their
 // XCD's run, whose neighbouring rows share its L2. Runs of more than
-// kWalkMax tiles (many units per workgroup, which even out by themselves)
-// keep their order.
+// kWalkMax tiles (many units per workgroup, which even out by themselves),
+// and more than 64 workgroups per XCD (one wave places the tiles), keep
+// their order.
 constexpr int kWalkMax = 256;
 __global__ __launch_bounds__(kWalkMax) void k_tile_walk(const uint16_t* __restrict__ cnt,
                                                          int64_t nt, int64_t tpx, int wpx,
@@ -439,7 +440,7 @@ __global__ __launch_bounds__(kWalkMax) void k_tile_walk(const uint16_t* __restri
   if (hi <= lo) return;
   const int count = static_cast<int>(hi - lo);
   const int tid = threadIdx.x;
-  if (count > kWalkMax) {
+  if (count > kWalkMax || wpx > 64) {
     for (int64_t i = lo + tid; i < hi; i += blockDim.x) walk[i] = static_cast<int32_t>(i);
     return;
   }

@@ -726,6 +726,35 @@ def test_tiles_288_same_results(dev, cin, cout, dtype, morton, bias):
 
 
 @gpu
+@pytest.mark.parametrize("n_tiles", [1, 9, 263])
+def test_wide_tile_walk_sizes(dev, n_tiles):
+    """288-row tiles walked in the balanced order the map build writes, with
+    tile counts that leave XCDs empty (1), uneven (9) and one workgroup with
+    fewer tiles than the rest (263): the 128 -> 128 forward (one workgroup
+    per CU) equals the 256-row tiles' bit for bit and the oracle on every
+    row."""
+    sc = _sc()
+    n = 288 * n_tiles - 7
+    G = max(16, int(round((n / 0.1) ** (1 / 3))))
+    wl = workloads.uniform_workload(G, n, [(3, 128, 128)], seed=1300 + n_tiles, bias_kind=None,
+                                    name="walk")
+    L = wl.layers[0]
+    _say(f"[wide walk] n_tiles={n_tiles} N={wl.n} G={G}")
+    coords = _to(dev, wl.coords)
+    km256 = sc.build_map(coords, wl.grid, wl.batch, tile_rows=256)
+    km288 = sc.build_map(coords, wl.grid, wl.batch, tile_rows=288)
+    assert km288.tile_rows == 288
+    feats = _to(dev, wl.feats)
+    W = _to(dev, L.W)
+    o288 = sc.forward(km288, feats, W)
+    assert torch.equal(sc.forward(km256, feats, W), o288)
+    ref = oc.submconv_rows(oc.kernel_map(wl.coords, wl.grid, wl.batch, 3), wl.feats, L.W, None)
+    _assert_close(o288.float().cpu().numpy(), ref, f"wide walk {n_tiles} tiles")
+    km256.free()
+    km288.free()
+
+
+@gpu
 def test_c3_map_takes_wider_tiles(dev):
     # 128^3 at 10 %: under one 32-entry group per off-centre position and
     # 256-row tile, and tiles of up to 288 rows fill three rounds of 256 CUs
