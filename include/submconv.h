@@ -125,7 +125,8 @@ typedef struct submconv_map_s* submconv_map_t;
  * with no handle, for invalid sites; and once at the end, so that the map
  * is complete on return. The map's device memory is 27*n*4 bytes for the
  * neighbour table plus the per-tile lists (8 bytes per active pair and tile
- * set). The build's scratch (the hash table: at least 2n slots of 8 bytes,
+ * set; a sparse map's wider tiles also keep the order, 4 bytes per tile, in
+ * which a forward's workgroups walk them). The build's scratch (the hash table: at least 2n slots of 8 bytes,
  * or 12 when packed keys exceed 32 bits; 8 bytes of key per site; sort space
  * with SUBMCONV_FLAG_MORTON or SUBMCONV_FLAG_SORTED_KEYS) stays with the
  * device after the call, up to 256 MiB, for the next build, until the
